@@ -1,0 +1,250 @@
+"""Seeded synthetic inputs for the differential-attention workloads.
+
+This module is shared by the CPU oracle tests, the GPU parity tests and the
+benchmark.  It holds no attention arithmetic: only random draws, the
+sequence-length draw for packed batches, and rounding to the storage dtype.
+
+Every tensor is drawn on the CPU with ``torch.Generator`` so that the same seed
+gives the same values on any machine.  Large tensors are drawn one leading
+index (batch entry or token block) at a time, each from its own derived seed,
+so that a test can regenerate a single slice without materialising the whole
+tensor on the host.
+
+Workload shapes follow the models the method's pages discuss: a 12-head,
+d_model 3072 V1 model whose value heads are twice as wide as its query/key
+heads, and V2 GQA models with 64 query heads (32 even/odd pairs) over 8 KV
+heads at sequence length 8192.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+INV_SQRT_128 = 1.0 / math.sqrt(128.0)
+
+
+def slice_seed(seed: int, index: int) -> int:
+    """Seed of slice ``index`` of a tensor drawn with base seed ``seed``."""
+    return (int(seed) * 1_000_003 + int(index)) % (2**63 - 1)
+
+
+def normal_slice(shape, seed: int, index: int, std: float = 1.0, mean: float = 0.0,
+                 dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """One slice: fp32 N(0,1) draw, times ``std`` plus ``mean`` in fp32, rounded to ``dtype``."""
+    g = torch.Generator(device="cpu").manual_seed(slice_seed(seed, index))
+    x = torch.randn(tuple(shape), generator=g, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    if mean != 0.0:
+        x.add_(mean)
+    return x if dtype == torch.float32 else x.to(dtype)
+
+
+def normal(shape, seed: int, std: float = 1.0, mean: float = 0.0,
+           dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """A tensor drawn slice by slice along its first axis (see :func:`normal_slice`)."""
+    shape = tuple(int(s) for s in shape)
+    out = torch.empty(shape, dtype=dtype)
+    for i in range(shape[0]):
+        out[i] = normal_slice(shape[1:], seed, i, std, mean, dtype)
+    return out
+
+
+def varlen_lengths(total: int, lo: int, hi: int, seed: int) -> list[int]:
+    """Sequence lengths for a packed batch.
+
+    Lengths are drawn uniformly from [lo, hi] with ``numpy.random.default_rng(seed)``
+    and appended (the last one cut short) until they sum to ``total``; so the
+    last sequence may be shorter than ``lo``.
+    """
+    rng = np.random.default_rng(seed)
+    lens: list[int] = []
+    acc = 0
+    while acc < total:
+        x = int(rng.integers(lo, hi + 1))
+        x = min(x, total - acc)
+        lens.append(x)
+        acc += x
+    return lens
+
+
+def cu_seqlens_of(lengths) -> list[int]:
+    out = [0]
+    for n in lengths:
+        out.append(out[-1] + int(n))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Workload recipes
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class V1Workload:
+    """V1 differential attention prefill: Q1,K1,Q2,K2 [B,T,H,d], V [B,T,H,dv]."""
+    name: str
+    B: int
+    T: int
+    H: int
+    d: int
+    dv: int
+    dtype: torch.dtype
+    std: float
+    layers: tuple
+    seeds: tuple  # q1, k1, q2, k2, v
+    eps: float = 1e-12
+    causal: bool = True
+
+    def with_shape(self, **kw) -> "V1Workload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return V1Workload(**d)
+
+
+@dataclass(frozen=True)
+class V2Workload:
+    """V2 GQA prefill, padded [B,T,*] or packed varlen [total,*] when ``lengths`` is set."""
+    name: str
+    B: int
+    T: int
+    Hq: int
+    Hkv: int
+    d: int
+    std: float
+    seeds: tuple  # q, k, v, logit
+    logit_mean: float = 0.0
+    logit_std: float = 1.0
+    lengths: tuple | None = None
+    causal: bool = True
+
+    def with_shape(self, **kw) -> "V2Workload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return V2Workload(**d)
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """V2 decode step: q [B,Hq,d], caches [B,S,Hkv,d], logits [B,Hq/2]."""
+    name: str
+    B: int
+    S: int
+    Hq: int
+    Hkv: int
+    d: int
+    std: float
+    seeds: tuple  # q, k_cache, v_cache, logit
+    cache_lens: tuple | None = None
+
+    def with_shape(self, **kw) -> "DecodeWorkload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return DecodeWorkload(**d)
+
+
+V1_FP32_SMALL = V1Workload(
+    name="v1_fp32_causal_b1_h1_t128_d64_dv128", B=1, T=128, H=1, d=64, dv=128,
+    dtype=torch.float32, std=1.0, layers=(1,), seeds=(101, 102, 103, 104, 105))
+
+V1_BF16 = V1Workload(
+    name="v1_bf16_causal_b4_h12_t4096_d128_dv256", B=4, T=4096, H=12, d=128, dv=256,
+    dtype=torch.bfloat16, std=INV_SQRT_128, layers=tuple(range(1, 29)),
+    seeds=(201, 202, 203, 204, 205))
+
+V2_PREFILL = V2Workload(
+    name="v2_prefill_bf16_causal_b2_t8192_hq64_hkv8_d128", B=2, T=8192, Hq=64, Hkv=8, d=128,
+    std=INV_SQRT_128, seeds=(301, 302, 303, 304))
+
+V2_DECODE = DecodeWorkload(
+    name="v2_decode_bf16_b64_s32768_hq64_hkv8_d128", B=64, S=32768, Hq=64, Hkv=8, d=128,
+    std=INV_SQRT_128, seeds=(401, 402, 403, 404))
+
+VARLEN_SEED = 501
+VARLEN_TOTAL = 65536
+VARLEN_LO, VARLEN_HI = 512, 16384
+
+V2_VARLEN = V2Workload(
+    name="v2_varlen_bf16_causal_total65536_hq64_hkv8_d128", B=1, T=VARLEN_TOTAL, Hq=64, Hkv=8,
+    d=128, std=INV_SQRT_128, seeds=(502, 503, 504, 505), logit_mean=2.0, logit_std=1.0,
+    lengths=tuple(varlen_lengths(VARLEN_TOTAL, VARLEN_LO, VARLEN_HI, VARLEN_SEED)))
+
+WORKLOADS = {w.name: w for w in (V1_FP32_SMALL, V1_BF16, V2_PREFILL, V2_DECODE, V2_VARLEN)}
+
+
+# ---------------------------------------------------------------------------
+# Generators (CPU tensors; callers move them to a device)
+# ---------------------------------------------------------------------------
+
+def v1_inputs(w: V1Workload) -> dict:
+    sq, sk, sq2, sk2, sv = w.seeds
+    qk_shape = (w.B, w.T, w.H, w.d)
+    return dict(
+        q1=normal(qk_shape, sq, w.std, dtype=w.dtype),
+        k1=normal(qk_shape, sk, w.std, dtype=w.dtype),
+        q2=normal(qk_shape, sq2, w.std, dtype=w.dtype),
+        k2=normal(qk_shape, sk2, w.std, dtype=w.dtype),
+        v=normal((w.B, w.T, w.H, w.dv), sv, w.std, dtype=w.dtype),
+    )
+
+
+def v2_inputs(w: V2Workload) -> dict:
+    """Padded: q [B,T,Hq,d] ...; packed (``w.lengths`` set): q [total,Hq,d], plus cu_seqlens."""
+    sq, sk, sv, sl = w.seeds
+    h = w.Hq // 2
+    if w.lengths is None:
+        lead = (w.B, w.T)
+        return dict(
+            q=normal(lead + (w.Hq, w.d), sq, w.std),
+            k=normal(lead + (w.Hkv, w.d), sk, w.std),
+            v=normal(lead + (w.Hkv, w.d), sv, w.std),
+            logit=normal(lead + (h,), sl, w.logit_std, w.logit_mean, dtype=torch.float32),
+            cu_seqlens=None,
+        )
+    total = int(sum(w.lengths))
+    # packed tensors are drawn in blocks of 1024 tokens (one derived seed per block)
+    def packed(width, seed, std, mean=0.0, dtype=torch.bfloat16):
+        blk = 1024
+        nb = (total + blk - 1) // blk
+        t = normal((nb, blk) + width, seed, std, mean, dtype)
+        return t.reshape((nb * blk,) + width)[:total].contiguous()
+    return dict(
+        q=packed((w.Hq, w.d), sq, w.std),
+        k=packed((w.Hkv, w.d), sk, w.std),
+        v=packed((w.Hkv, w.d), sv, w.std),
+        logit=packed((h,), sl, w.logit_std, w.logit_mean, dtype=torch.float32),
+        cu_seqlens=torch.tensor(cu_seqlens_of(w.lengths), dtype=torch.int32),
+    )
+
+
+def decode_small_inputs(w: DecodeWorkload) -> dict:
+    """Decode inputs for the query, logits and lengths (the caches come from :func:`decode_cache_slice`)."""
+    sq, sk, sv, sl = w.seeds
+    h = w.Hq // 2
+    lens = None if w.cache_lens is None else torch.tensor(w.cache_lens, dtype=torch.int32)
+    return dict(
+        q=normal((w.B, w.Hq, w.d), sq, w.std),
+        logit=normal((w.B, h), sl, 1.0, dtype=torch.float32),
+        cache_len=lens,
+    )
+
+
+def decode_cache_slice(w: DecodeWorkload, b: int, which: str) -> torch.Tensor:
+    """Cache slice [S, Hkv, d] of batch entry ``b``; ``which`` is 'k' or 'v'."""
+    seed = w.seeds[1] if which == "k" else w.seeds[2]
+    return normal_slice((w.S, w.Hkv, w.d), seed, b, w.std)
+
+
+def decode_inputs(w: DecodeWorkload, device=None) -> dict:
+    """All decode inputs; caches are filled one batch entry at a time (on ``device`` if given)."""
+    out = decode_small_inputs(w)
+    dev = torch.device("cpu") if device is None else torch.device(device)
+    kc = torch.empty((w.B, w.S, w.Hkv, w.d), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    for b in range(w.B):
+        kc[b].copy_(decode_cache_slice(w, b, "k"))
+        vc[b].copy_(decode_cache_slice(w, b, "v"))
+    out["k_cache"], out["v_cache"] = kc, vc
+    return out

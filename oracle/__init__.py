@@ -1,0 +1,21 @@
+"""fp64 CPU oracle for differential attention -- test infrastructure only.
+
+Imported by the tests, the smoke check and the benchmark's CPU-baseline leg;
+never by the library itself.
+"""
+from .diffattn_oracle import (  # noqa: F401
+    gqa_kv_head,
+    lambda_init,
+    sigmoid,
+    softmax_rows,
+    v1_attention,
+    v1_forward,
+    v1_head,
+    v1_norm,
+    v2_combine,
+    v2_decode,
+    v2_forward,
+    v2_heads,
+    v2_sequence,
+    v2_varlen_forward,
+)

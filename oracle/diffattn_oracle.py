@@ -1,0 +1,272 @@
+"""fp64 CPU oracle for differential attention (V1 and V2) -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this module.  The library (HIP kernels, C ABI and its Python binding)
+never imports, links or calls it, and this module imports nothing from the
+library: the two share no code.  Inputs come in as arrays (numpy or anything
+``numpy.asarray`` accepts) and are promoted exactly to float64.
+
+What is computed, and where it is stated
+-----------------------------------------
+* V1 differential attention -- "Differential Transformer | ICLR 2025 Oral" blog
+  (dainus.ai), section "Differential Attention: 빼기의 힘": the output is
+  (softmax(Q1 K1^T / sqrt d) - lambda * softmax(Q2 K2^T / sqrt d)) V, with the
+  two maps from independent query/key halves.  The value head is twice as wide
+  as the query/key head ("파라미터 효율성" on the same page; V2 summary §1).
+* lambda_init(l) = 0.8 - 0.6 exp(-0.3 (l - 1)) -- same blog, section "λ의 역할과 학습".
+* V1 post-processing -- "Differential Transformer V2" summary (pogovet.com),
+  상세 정리 §1: after the subtraction each head is RMS-normalised and then
+  multiplied by a factor set by the layer's initial lambda; that factor is
+  (1 - lambda_init).
+* V2 -- same summary, §1 and §4: one attention call over 2h query heads whose
+  key/value heads are shared within GQA groups; the outputs are split into
+  even/odd heads and the odd one, scaled by sigmoid of a per-token, per-head
+  coefficient, is subtracted from the even one, leaving h*d columns.  No norm
+  and no scale follow.
+* V2 decode -- same summary, §2: the KV heads and cache are those of a
+  standard GQA model; a decode step is the V2 formula for one new query row
+  against every cached position.
+
+Readings where the pages are silent (each one is an argument, not a constant)
+----------------------------------------------------------------------------
+* sqrt(d) uses the query/key head dim d, not the value width.
+* Causal masking keeps keys j <= i (diagonal included); a packed (varlen)
+  batch never attends across sequence boundaries.
+* The RMS norm runs over the value channels of one (token, head):
+  y = (1 - lambda_init) * w * z / sqrt(mean(z^2) + eps); w defaults to ones.
+* Pairs are (2p, 2p+1); query head j reads KV head j // (Hq / Hkv).
+* sigmoid(x) = 1 / (1 + e^-x), evaluated in its overflow-free form.
+* A decode sequence with no cached positions gives a zero output.
+
+Parity status: every public function here is pinned by tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+_ROW_BLOCK = 256
+
+
+def _f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # a torch tensor: go through float32 (exact for bf16/fp32)
+        x = x.detach().cpu()
+        if str(x.dtype) in ("torch.bfloat16", "torch.float16"):
+            x = x.float()
+        x = x.numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def lambda_init(layer: int) -> float:
+    """Initial lambda of (1-based) layer ``layer``: 0.8 - 0.6 * exp(-0.3 * (layer - 1)).
+
+    Blog "Differential Transformer | ICLR 2025 Oral", section "λ의 역할과 학습".
+    """
+    if int(layer) != layer or layer < 1:
+        raise ValueError("layer is 1-based")
+    return 0.8 - 0.6 * math.exp(-0.3 * (layer - 1))
+
+
+def sigmoid(x) -> np.ndarray:
+    """Logistic function 1 / (1 + e^-x) without overflow for large |x|."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    e = np.exp(x[~pos])
+    out[~pos] = e / (1.0 + e)
+    return out
+
+
+def softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Softmax along the last axis, with the row maximum subtracted first.
+
+    Entries equal to -inf (masked keys) get weight exactly 0.
+    """
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def _attention_map(q_rows: np.ndarray, k: np.ndarray, rows: np.ndarray, scale: float,
+                   causal: bool) -> np.ndarray:
+    """softmax(q k^T * scale) for the query positions ``rows`` against keys 0..n-1."""
+    s = (q_rows @ k.T) * scale
+    if causal:
+        keys = np.arange(k.shape[0])
+        s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
+    return softmax_rows(s)
+
+
+# ---------------------------------------------------------------------------
+# V1
+# ---------------------------------------------------------------------------
+
+def v1_head(q1, k1, q2, k2, v, lam: float, rows=None, causal: bool = True) -> np.ndarray:
+    """Differential attention z for one (batch, head) slice.
+
+    q1, k1, q2, k2: [T, d]; v: [T, dv].  Returns z[rows] = (P1 - lam * P2) v, [R, dv],
+    where P1, P2 are the two softmax maps (blog, "Differential Attention: 빼기의 힘").
+    The difference map is formed first, literally as written on the page.
+    """
+    q1, k1, q2, k2, v = (_f64(a) for a in (q1, k1, q2, k2, v))
+    T, d = q1.shape
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    scale = 1.0 / math.sqrt(d)
+    out = np.empty((rows.size, v.shape[1]))
+    for r0 in range(0, rows.size, _ROW_BLOCK):
+        rr = rows[r0:r0 + _ROW_BLOCK]
+        p1 = _attention_map(q1[rr], k1, rr, scale, causal)
+        p2 = _attention_map(q2[rr], k2, rr, scale, causal)
+        diff_map = p1 - lam * p2
+        out[r0:r0 + rr.size] = diff_map @ v
+    return out
+
+
+def v1_norm(z, lam_init: float, eps: float, weight=None) -> np.ndarray:
+    """Per-head RMS norm over the value channels, then the (1 - lambda_init) factor.
+
+    V2 summary §1 (the V1 recap): normalise each head, then multiply by a factor
+    set by the layer's initial lambda.  z: [..., dv]; weight: [dv] or None (ones).
+    """
+    z = _f64(z)
+    ms = np.mean(z * z, axis=-1, keepdims=True)
+    y = z / np.sqrt(ms + eps)
+    if weight is not None:
+        y = y * _f64(weight)
+    return (1.0 - lam_init) * y
+
+
+def v1_attention(q1, k1, q2, k2, v, lam: float, causal: bool = True, rows=None) -> np.ndarray:
+    """z for every (batch, head): inputs [B, T, H, d] / [B, T, H, dv] -> [B, R, H, dv]."""
+    q1, k1, q2, k2, v = (_f64(a) for a in (q1, k1, q2, k2, v))
+    B, T, H, _ = q1.shape
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.empty((B, rows.size, H, v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            out[b, :, h] = v1_head(q1[b, :, h], k1[b, :, h], q2[b, :, h], k2[b, :, h],
+                                   v[b, :, h], lam, rows, causal)
+    return out
+
+
+def v1_forward(q1, k1, q2, k2, v, lam: float, lam_init: float, eps: float, weight=None,
+               causal: bool = True, rows=None) -> np.ndarray:
+    """Full V1 attention output y = (1 - lam_init) * w * z / rms(z): [B, R, H, dv]."""
+    z = v1_attention(q1, k1, q2, k2, v, lam, causal, rows)
+    return v1_norm(z, lam_init, eps, weight)
+
+
+# ---------------------------------------------------------------------------
+# V2
+# ---------------------------------------------------------------------------
+
+def gqa_kv_head(j: int, Hq: int, Hkv: int) -> int:
+    """KV head read by query head j: contiguous groups of Hq / Hkv query heads."""
+    return j // (Hq // Hkv)
+
+
+def v2_heads(q, k, v, rows=None, causal: bool = True, scale: float | None = None) -> np.ndarray:
+    """Plain softmax attention of every query head over its GQA KV head, one sequence.
+
+    q: [T, Hq, d]; k, v: [T, Hkv, d].  Returns O: [R, Hq, d].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = np.empty((rows.size, Hq, v.shape[-1]))
+    for j in range(Hq):
+        kv = gqa_kv_head(j, Hq, Hkv)
+        for r0 in range(0, rows.size, _ROW_BLOCK):
+            rr = rows[r0:r0 + _ROW_BLOCK]
+            p = _attention_map(q[rr, j], k[:, kv], rr, scale, causal)
+            out[r0:r0 + rr.size, j] = p @ v[:, kv]
+    return out
+
+
+def v2_combine(O, logit) -> np.ndarray:
+    """out[:, p] = O[:, 2p] - sigmoid(logit[:, p]) * O[:, 2p+1]  (V2 summary §1, §4).
+
+    O: [R, 2h, d]; logit: [R, h].  Returns [R, h, d].
+    """
+    O, logit = _f64(O), _f64(logit)
+    if O.shape[1] % 2:
+        raise ValueError("an even number of query heads is required")
+    sig = sigmoid(logit)
+    return O[:, 0::2] - sig[..., None] * O[:, 1::2]
+
+
+def v2_sequence(q, k, v, logit, rows=None, causal: bool = True,
+                scale: float | None = None) -> np.ndarray:
+    """V2 output for one sequence: q [T, 2h, d], k/v [T, Hkv, d], logit [T, h] -> [R, h, d]."""
+    logit = _f64(logit)
+    T = logit.shape[0]
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    O = v2_heads(q, k, v, rows, causal, scale)
+    return v2_combine(O, logit[rows])
+
+
+def v2_forward(q, k, v, logit, causal: bool = True, scale: float | None = None,
+               rows=None) -> np.ndarray:
+    """Padded batch: q [B, T, 2h, d], k/v [B, T, Hkv, d], logit [B, T, h] -> [B, R, h, d]."""
+    q, k, v, logit = _f64(q), _f64(k), _f64(v), _f64(logit)
+    B, T = q.shape[:2]
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.empty((B, rows.size, q.shape[2] // 2, v.shape[-1]))
+    for b in range(B):
+        out[b] = v2_sequence(q[b], k[b], v[b], logit[b], rows, causal, scale)
+    return out
+
+
+def v2_varlen_forward(q, k, v, logit, cu_seqlens, causal: bool = True,
+                      scale: float | None = None, tokens=None) -> np.ndarray:
+    """Packed batch: q [N, 2h, d], k/v [N, Hkv, d], logit [N, h], cu_seqlens [nseq+1].
+
+    Each sequence s owns tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 and attends only
+    within itself.  ``tokens`` (global indices) selects output rows; default all.
+    Returns [len(tokens), h, d].
+    """
+    q, k, v, logit = _f64(q), _f64(k), _f64(v), _f64(logit)
+    cu = [int(c) for c in np.asarray(cu_seqlens).tolist()]
+    N = q.shape[0]
+    tokens = np.arange(N) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    out = np.zeros((tokens.size, q.shape[1] // 2, v.shape[-1]))
+    for s in range(len(cu) - 1):
+        a, e = cu[s], cu[s + 1]
+        sel = np.nonzero((tokens >= a) & (tokens < e))[0]
+        if sel.size == 0:
+            continue
+        out[sel] = v2_sequence(q[a:e], k[a:e], v[a:e], logit[a:e], tokens[sel] - a, causal, scale)
+    return out
+
+
+def v2_decode(q, k_cache, v_cache, logit, cache_len=None, scale: float | None = None,
+              batch=None) -> np.ndarray:
+    """One decode step: q [B, 2h, d], caches [B, S, Hkv, d], logit [B, h] -> [B', h, d].
+
+    Entry b attends (non-causally) to cache positions 0 .. cache_len[b]-1 (all S when
+    ``cache_len`` is None); an entry with no cached positions gives zeros.  ``batch``
+    selects entries (default all); the caches may then hold only those entries
+    (``k_cache.shape[0] == len(batch)``) to bound host memory.
+    """
+    q, logit = _f64(q), _f64(logit)
+    B = q.shape[0]
+    batch = list(range(B)) if batch is None else [int(b) for b in batch]
+    h = q.shape[1] // 2
+    S = k_cache.shape[1]
+    out = np.zeros((len(batch), h, v_cache.shape[-1]))
+    sliced = k_cache.shape[0] == len(batch) and len(batch) != B
+    for i, b in enumerate(batch):
+        n = S if cache_len is None else int(np.asarray(cache_len)[b])
+        if n <= 0:
+            continue
+        cb = i if sliced else b
+        kb, vb = _f64(k_cache[cb, :n]), _f64(v_cache[cb, :n])
+        O = v2_heads(q[b][None], kb, vb, rows=np.array([0]), causal=False, scale=scale)
+        out[i] = v2_combine(O, logit[b][None])[0]
+    return out

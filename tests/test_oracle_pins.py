@@ -1,0 +1,367 @@
+"""Pins for the fp64 oracle: each test checks it against something other than itself.
+
+The pins come from what the pages and the mathematics fix: the lambda_init
+schedule, the figure 90.5 printed for uniform attention at length 8192, the
+reduction to ordinary softmax attention (checked against torch's
+scaled_dot_product_attention in float64, an independent library routine),
+exact zeros for identical streams, closed forms for uniform and one-hot
+attention, structural properties (causality, shift invariance, no leakage
+across packed sequences), and scalar brute force on tiny inputs.  Each pin is
+chosen so that a plausible slip in the oracle (a dropped term, a wrong sign,
+index or axis, a transposed operand) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from scipy.special import expit
+
+import oracle
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def sdpa(q, k, v, causal, gqa=False):
+    """torch SDPA in float64 on [T, H, d] arrays (one sequence) -> [T, H, dv]."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(np.swapaxes(a, 0, 1)))[None]
+    o = F.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=causal, enable_gqa=gqa)
+    return np.swapaxes(o[0].numpy(), 0, 1)
+
+
+# ---------------------------------------------------------------------------
+# lambda_init
+# ---------------------------------------------------------------------------
+
+def test_lambda_init_first_layer_is_page_value():
+    assert oracle.lambda_init(1) == pytest.approx(GOLDEN["lambda_init_layer1"]["value"], abs=1e-15)
+
+
+def test_lambda_init_grows_geometrically_to_limit():
+    lim = GOLDEN["lambda_init_limit"]["value"]
+    vals = [oracle.lambda_init(l) for l in range(1, 31)]
+    assert all(b > a for a, b in zip(vals, vals[1:])), "must grow with depth"
+    assert all(v < lim for v in vals)
+    # the gap to the limit shrinks by the same factor every layer
+    ratios = [(lim - b) / (lim - a) for a, b in zip(vals, vals[1:])]
+    assert max(ratios) - min(ratios) < 1e-10
+    assert ratios[0] == pytest.approx(math.exp(-0.3), rel=1e-12)
+    assert oracle.lambda_init(300) == pytest.approx(lim, abs=1e-15)
+    with pytest.raises(ValueError):
+        oracle.lambda_init(0)
+
+
+# ---------------------------------------------------------------------------
+# V1
+# ---------------------------------------------------------------------------
+
+def v1_rand(seed, T=24, H=1, d=8, dv=16):
+    r = rng(seed)
+    qk = lambda: r.standard_normal((1, T, H, d))
+    return qk(), qk(), qk(), qk(), r.standard_normal((1, T, H, dv))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_v1_lambda_zero_is_softmax_attention(causal):
+    q1, k1, q2, k2, v = v1_rand(1, T=37, H=3, d=8, dv=16)
+    z = oracle.v1_attention(q1, k1, q2, k2, v, lam=0.0, causal=causal)
+    ref = sdpa(q1[0], k1[0], v[0], causal)
+    np.testing.assert_allclose(z[0], ref, rtol=0, atol=1e-13)
+
+
+def test_v1_second_stream_enters_with_minus_lambda():
+    # one stream alone is plain attention; the difference is linear in lambda
+    q1, k1, q2, k2, v = v1_rand(2, T=19, H=2, d=8, dv=16)
+    a1 = sdpa(q1[0], k1[0], v[0], True)
+    a2 = sdpa(q2[0], k2[0], v[0], True)
+    for lam in (-0.5, 0.2, 0.8, 1.7):
+        z = oracle.v1_attention(q1, k1, q2, k2, v, lam)
+        np.testing.assert_allclose(z[0], a1 - lam * a2, rtol=0, atol=1e-13)
+
+
+def test_v1_identical_streams_give_exact_zero():
+    q1, k1, _, _, v = v1_rand(3, T=33, H=2, d=16, dv=32)
+    z = oracle.v1_attention(q1, k1, q1.copy(), k1.copy(), v, lam=1.0)
+    assert np.all(z == 0.0)
+    y = oracle.v1_forward(q1, k1, q1.copy(), k1.copy(), v, lam=1.0, lam_init=0.2, eps=1e-12)
+    assert np.all(y == 0.0)
+
+
+@pytest.mark.parametrize("lam", [0.2, 0.7])
+def test_v1_uniform_attention_is_prefix_mean(lam):
+    # zero keys make every logit 0, so each causal row averages v_0..v_i
+    q1, _, q2, _, v = v1_rand(4, T=40, H=2, d=8, dv=16)
+    zk = np.zeros_like(q1)
+    z = oracle.v1_attention(q1, zk, q2, zk, v, lam)
+    n = np.arange(1, 41, dtype=np.float64)[None, :, None, None]
+    prefix_mean = np.cumsum(v, axis=1) / n
+    np.testing.assert_allclose(z, (1 - lam) * prefix_mean, rtol=0, atol=1e-13)
+    lam_init, eps = 0.47, 1e-12
+    y = oracle.v1_forward(q1, zk, q2, zk, v, lam, lam_init, eps)
+    zz = (1 - lam) * prefix_mean
+    expect = (1 - lam_init) * zz / np.sqrt((zz ** 2).mean(-1, keepdims=True) + eps)
+    np.testing.assert_allclose(y, expect, rtol=1e-12, atol=1e-13)
+
+
+def test_v1_uniform_attention_gain_matches_page_figure():
+    # V2 summary §3: uncorrelated RMS-1 values averaged uniformly over n = 8192
+    # tokens have context RMS ~ 1/sqrt(n): the norm multiplies by ~90.5.
+    fig = GOLDEN["uniform_attention_norm_gain_n8192"]
+    n, dv, heads = fig["n"], 64, 256
+    r = rng(5)
+    ms = []
+    zq = np.zeros((n, 4))
+    for _ in range(heads):
+        v = r.standard_normal((n, dv))
+        z = oracle.v1_head(zq, zq, zq, zq, v, lam=0.0, rows=[n - 1])
+        ms.append(np.mean(z ** 2))
+    gain = 1.0 / math.sqrt(np.mean(ms))
+    assert abs(gain - fig["value"]) / fig["value"] < fig["tolerance_rel"]
+    assert 1.0 / math.sqrt(n) < math.sqrt(np.mean(ms)) * 1.05  # lower end of [1/sqrt(n), 1)
+
+
+def test_v1_one_hot_maps_select_values():
+    # make stream 1 of row i look only at key a, stream 2 only at key b
+    T, d, dv, i, a, b = 12, 8, 16, 9, 2, 6
+    r = rng(6)
+    q1 = np.zeros((1, T, 1, d)); k1 = np.zeros_like(q1)
+    q2 = np.zeros_like(q1); k2 = np.zeros_like(q1)
+    q1[0, i, 0, 0] = 40.0; k1[0, a, 0, 0] = 40.0
+    q2[0, i, 0, 1] = 40.0; k2[0, b, 0, 1] = 40.0
+    v = r.standard_normal((1, T, 1, dv))
+    lam = 0.35
+    z = oracle.v1_attention(q1, k1, q2, k2, v, lam, rows=[i])
+    np.testing.assert_allclose(z[0, 0, 0], v[0, a, 0] - lam * v[0, b, 0], rtol=0, atol=1e-12)
+
+
+def test_v1_first_row_closed_form():
+    q1, k1, q2, k2, v = v1_rand(7, T=10, H=3, d=8, dv=16)
+    lam, lam_init, eps = 0.6, 0.3555, 1e-6
+    w = rng(8).uniform(0.5, 1.5, 16)
+    y = oracle.v1_forward(q1, k1, q2, k2, v, lam, lam_init, eps, weight=w, rows=[0])
+    z0 = (1 - lam) * v[0, 0]  # one visible key: both maps are exactly 1
+    expect = (1 - lam_init) * w * z0 / np.sqrt((z0 ** 2).mean(-1, keepdims=True) + eps)
+    np.testing.assert_allclose(y[0, 0], expect, rtol=1e-13, atol=0)
+
+
+def test_v1_norm_gives_rms_of_scale_per_row_and_head():
+    q1, k1, q2, k2, v = v1_rand(9, T=21, H=4, d=8, dv=32)
+    lam_init = 0.7008
+    y = oracle.v1_forward(q1, k1, q2, k2, v, 0.5, lam_init, eps=0.0)
+    rms = np.sqrt((y ** 2).mean(-1))
+    np.testing.assert_allclose(rms, 1 - lam_init, rtol=1e-12)
+
+
+def test_v1_causal_rows_ignore_future_tokens():
+    q1, k1, q2, k2, v = v1_rand(10, T=30, H=2, d=8, dv=16)
+    y = oracle.v1_forward(q1, k1, q2, k2, v, 0.4, 0.2, 1e-12)
+    cut = 17
+    k1b, k2b, vb = k1.copy(), k2.copy(), v.copy()
+    r = rng(11)
+    k1b[:, cut:] = r.standard_normal(k1b[:, cut:].shape)
+    k2b[:, cut:] = r.standard_normal(k2b[:, cut:].shape)
+    vb[:, cut:] = r.standard_normal(vb[:, cut:].shape)
+    yb = oracle.v1_forward(q1, k1b, q2, k2b, vb, 0.4, 0.2, 1e-12)
+    assert np.array_equal(y[:, :cut], yb[:, :cut])
+    assert not np.allclose(y[:, cut:], yb[:, cut:])
+
+
+def test_v1_softmax_is_over_keys_shift_invariant():
+    # adding one vector to every key shifts each row's logits by a constant
+    q1, k1, q2, k2, v = v1_rand(12, T=25, H=1, d=8, dv=16)
+    c1, c2 = rng(13).standard_normal(8), rng(14).standard_normal(8)
+    z = oracle.v1_attention(q1, k1, q2, k2, v, 0.3)
+    zs = oracle.v1_attention(q1, k1 + c1, q2, k2 + c2, v, 0.3)
+    np.testing.assert_allclose(z, zs, rtol=0, atol=1e-12)
+
+
+def brute_v1(q1, k1, q2, k2, v, lam, lam_init, eps):
+    """Scalar loops over one (batch, head): the page formula, element by element."""
+    T, d = len(q1), len(q1[0])
+    dv = len(v[0])
+    out = []
+    for i in range(T):
+        s1 = [sum(q1[i][c] * k1[j][c] for c in range(d)) / math.sqrt(d) for j in range(i + 1)]
+        s2 = [sum(q2[i][c] * k2[j][c] for c in range(d)) / math.sqrt(d) for j in range(i + 1)]
+        e1 = [math.exp(x - max(s1)) for x in s1]
+        e2 = [math.exp(x - max(s2)) for x in s2]
+        z = [sum((e1[j] / sum(e1) - lam * e2[j] / sum(e2)) * v[j][c] for j in range(i + 1))
+             for c in range(dv)]
+        r = math.sqrt(sum(x * x for x in z) / dv + eps)
+        out.append([(1 - lam_init) * x / r for x in z])
+    return out
+
+
+@pytest.mark.parametrize("lam", [-0.5, 0.0, 0.2, 1.0, 1.5])
+def test_v1_brute_force_tiny(lam):
+    r = rng(15)
+    T, d, dv = 6, 4, 8
+    q1, k1, q2, k2 = (r.standard_normal((1, T, 1, d)) for _ in range(4))
+    v = r.standard_normal((1, T, 1, dv))
+    y = oracle.v1_forward(q1, k1, q2, k2, v, lam, 0.4, 1e-9)
+    ref = brute_v1(q1[0, :, 0].tolist(), k1[0, :, 0].tolist(), q2[0, :, 0].tolist(),
+                   k2[0, :, 0].tolist(), v[0, :, 0].tolist(), lam, 0.4, 1e-9)
+    np.testing.assert_allclose(y[0, :, 0], np.array(ref), rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# V2
+# ---------------------------------------------------------------------------
+
+def v2_rand(seed, T=20, Hq=8, Hkv=2, d=8, B=1):
+    r = rng(seed)
+    return (r.standard_normal((B, T, Hq, d)), r.standard_normal((B, T, Hkv, d)),
+            r.standard_normal((B, T, Hkv, d)), r.standard_normal((B, T, Hq // 2)))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_v2_zero_sigmoid_is_gqa_attention_of_even_heads(causal):
+    q, k, v, _ = v2_rand(20, T=23, Hq=8, Hkv=2)
+    logit = np.full((1, 23, 4), -200.0)  # sigmoid(-200) ~ 1e-87
+    out = oracle.v2_forward(q, k, v, logit, causal=causal)
+    ref = sdpa(q[0], k[0], v[0], causal, gqa=True)
+    np.testing.assert_allclose(out[0], ref[:, 0::2], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (16, 2), (4, 4), (8, 1)])
+def test_v2_matches_library_attention_and_logistic(Hq, Hkv):
+    q, k, v, logit = v2_rand(21, T=17, Hq=Hq, Hkv=Hkv)
+    out = oracle.v2_forward(q, k, v, logit)
+    o = sdpa(q[0], k[0], v[0], True, gqa=True)
+    ref = o[:, 0::2] - expit(logit[0])[..., None] * o[:, 1::2]
+    np.testing.assert_allclose(out[0], ref, rtol=0, atol=1e-13)
+
+
+def test_v2_identical_pair_with_unit_sigmoid_is_exact_zero():
+    # Pairs share their GQA group's K and V (V2 summary §1), so two equal query heads
+    # in a pair give equal outputs; sigmoid(40) is exactly 1.0 in float64.
+    q, k, v, _ = v2_rand(22, T=26, Hq=16, Hkv=4)
+    q[..., 1::2, :] = q[..., 0::2, :]
+    logit = np.full((1, 26, 8), 40.0)
+    assert oracle.sigmoid(np.array([40.0]))[0] == 1.0
+    out = oracle.v2_forward(q, k, v, logit)
+    assert np.all(out == 0.0)
+
+
+def test_v2_one_hot_difference_and_rms_range():
+    # V2 summary §4: the difference of two maps spans context RMS in (0, sqrt 2).
+    T, d, Hq, Hkv, i, a, b = 10, 8, 2, 1, 8, 1, 5
+    r = rng(23)
+    q = np.zeros((1, T, Hq, d)); k = np.zeros((1, T, Hkv, d))
+    q[0, i, 0, 0] = 40.0; k[0, a, 0, 0] = 40.0
+    q[0, i, 1, 1] = 40.0; k[0, b, 0, 1] = 40.0
+    v = r.standard_normal((1, T, Hkv, 4096))
+    v /= np.sqrt((v ** 2).mean(-1, keepdims=True))  # RMS exactly 1 per token
+    for x in (-3.0, 0.0, 2.5):
+        logit = np.full((1, T, 1), x)
+        out = oracle.v2_forward(q, k, v, logit, rows=[i])[0, 0, 0]
+        s = expit(x)
+        np.testing.assert_allclose(out, v[0, a, 0] - s * v[0, b, 0], rtol=0, atol=1e-12)
+        rms = math.sqrt((out ** 2).mean())
+        assert 0.0 < rms < math.sqrt(GOLDEN["context_rms_range_v2"]["upper_sq"])
+    # uniform maps in both heads and sigmoid -> 1 drive the output to zero (lower end 0)
+    kz = np.zeros_like(k)
+    out = oracle.v2_forward(q, kz, v, np.full((1, T, 1), 30.0), rows=[i])
+    assert math.sqrt((out ** 2).mean()) < 1e-12
+
+
+def test_v2_causal_rows_ignore_future_tokens():
+    q, k, v, logit = v2_rand(24, T=30)
+    out = oracle.v2_forward(q, k, v, logit)
+    r = rng(25)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 12:] = r.standard_normal(k2[:, 12:].shape)
+    v2[:, 12:] = r.standard_normal(v2[:, 12:].shape)
+    out2 = oracle.v2_forward(q, k2, v2, logit)
+    assert np.array_equal(out[:, :12], out2[:, :12])
+
+
+def test_v2_varlen_is_per_sequence_attention():
+    lens = [5, 1, 9, 0, 14]
+    cu = np.cumsum([0] + lens)
+    N = cu[-1]
+    q, k, v, logit = (a[0] for a in v2_rand(26, T=N, Hq=8, Hkv=2))
+    out = oracle.v2_varlen_forward(q, k, v, logit, cu)
+    for s in range(len(lens)):
+        a, e = cu[s], cu[s + 1]
+        if a == e:
+            continue
+        o = sdpa(q[a:e], k[a:e], v[a:e], True, gqa=True)
+        ref = o[:, 0::2] - expit(logit[a:e])[..., None] * o[:, 1::2]
+        np.testing.assert_allclose(out[a:e], ref, rtol=0, atol=1e-13)
+    # no leakage: rewriting the third sequence leaves the others bit-identical
+    k2 = k.copy()
+    k2[cu[2]:cu[3]] += 1.0
+    out2 = oracle.v2_varlen_forward(q, k2, v, logit, cu)
+    keep = np.r_[0:cu[2], cu[3]:N]
+    assert np.array_equal(out[keep], out2[keep])
+    # a token subset gives the same rows
+    sub = np.array([0, 6, 13, 20, N - 1])
+    np.testing.assert_array_equal(oracle.v2_varlen_forward(q, k, v, logit, cu, tokens=sub), out[sub])
+
+
+def test_v2_decode_is_single_query_attention_over_cache():
+    B, S, Hq, Hkv, d = 3, 29, 8, 2, 8
+    r = rng(27)
+    q = r.standard_normal((B, Hq, d))
+    kc = r.standard_normal((B, S, Hkv, d)); vc = r.standard_normal((B, S, Hkv, d))
+    logit = r.standard_normal((B, Hq // 2))
+    lens = np.array([29, 7, 0])
+    out = oracle.v2_decode(q, kc, vc, logit, cache_len=lens)
+    for b in range(B):
+        n = lens[b]
+        if n == 0:
+            assert np.all(out[b] == 0.0)
+            continue
+        o = sdpa(q[b][None], kc[b, :n], vc[b, :n], False, gqa=True)[0]
+        ref = o[0::2] - expit(logit[b])[:, None] * o[1::2]
+        np.testing.assert_allclose(out[b], ref, rtol=0, atol=1e-13)
+    # decoding the last token equals the last row of causal prefill over the cache
+    qs = r.standard_normal((1, S, Hq, d))
+    qs[0, -1] = q[0]
+    ls = np.zeros((1, S, Hq // 2)); ls[0, -1] = logit[0]
+    pre = oracle.v2_forward(qs, kc[:1], vc[:1], ls, rows=[S - 1])
+    np.testing.assert_allclose(out[0], pre[0, 0], rtol=0, atol=1e-13)
+    # a batch subset with sliced caches
+    sub = oracle.v2_decode(q, kc[1:2], vc[1:2], logit, cache_len=lens, batch=[1])
+    np.testing.assert_allclose(sub[0], out[1], rtol=0, atol=0)
+
+
+def brute_v2_row(q, k, v, logit, i, g):
+    """Scalar loops for one query row of one sequence."""
+    Hq, d = len(q[0]), len(q[0][0])
+    dvv = len(v[0][0])
+    O = []
+    for j in range(Hq):
+        kv = j // g
+        s = [sum(q[i][j][c] * k[t][kv][c] for c in range(d)) / math.sqrt(d) for t in range(i + 1)]
+        e = [math.exp(x - max(s)) for x in s]
+        O.append([sum(e[t] / sum(e) * v[t][kv][c] for t in range(i + 1)) for c in range(dvv)])
+    res = []
+    for p in range(Hq // 2):
+        sg = 1.0 / (1.0 + math.exp(-logit[i][p]))
+        res.append([O[2 * p][c] - sg * O[2 * p + 1][c] for c in range(dvv)])
+    return res
+
+
+def test_v2_brute_force_tiny():
+    q, k, v, logit = v2_rand(28, T=6, Hq=4, Hkv=2, d=4)
+    out = oracle.v2_forward(q, k, v, logit)
+    for i in range(6):
+        ref = brute_v2_row(q[0].tolist(), k[0].tolist(), v[0].tolist(), logit[0].tolist(), i, 2)
+        np.testing.assert_allclose(out[0, i], np.array(ref), rtol=1e-11, atol=1e-12)
+
+
+def test_sigmoid_is_overflow_free_and_symmetric():
+    x = np.array([-800.0, -40.0, -1.0, 0.0, 1.0, 40.0, 800.0])
+    s = oracle.sigmoid(x)
+    assert np.all(np.isfinite(s))
+    np.testing.assert_allclose(s, expit(x), rtol=1e-15, atol=0)
+    np.testing.assert_allclose(s + oracle.sigmoid(-x), 1.0, rtol=0, atol=1e-15)
