@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Throughput benchmark for the differential-attention hot path on one MI355X.
+
+Headline workload: DIFF V1 causal prefill, bf16 inputs / fp32 accumulation,
+batch 4 x 12 heads x 4096 tokens, q/k head dim 128, v head dim 256
+(d_model 3072), evaluated for layers l = 1..28 with lambda = lambda_init(l).
+One step = the 28 layer calls on one synthetic batch; the metric is
+algorithmic TFLOP/s (causal lower triangle, diagonal included).
+
+The other hot-path kernels are timed in the same run (``secondary``):
+V2 GQA causal prefill (B2, Hq64/Hkv8, T8192, d128), V2 packed varlen prefill
+(65536 tokens), and the V2 decode step (B64, 32768-entry cache, Hq64/Hkv8,
+d128, metric HBM GB/s).  Inputs are synthetic, seeded, already resident in HBM
+when timing starts.  The fp64 CPU oracle is timed on a bounded sample of the
+headline workload on this host (``cpu_baseline``).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
+       [--no-cpu-baseline] [--only v1|v2|varlen|decode]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def v1_flops(B, T, H, d, dv):
+    return 2.0 * (d + dv) * T * (T + 1) * B * H
+
+
+def v2_flops_seq(n, Hq, d):
+    return 2.0 * d * n * (n + 1) * Hq
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def time_calls(fn, iters, stream):
+    """Average milliseconds per call of ``fn`` with HIP events on ``stream``."""
+    import torch
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["v1", "v2", "varlen", "decode"], default=None)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the kernels would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import differential_softmax_attention_diffattn_amd as da
+    from differential_softmax_attention_diffattn_amd import inputs as inp
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    result = {}
+    secondary = {}
+
+    # ------------------------------------------------------------------ V1 (headline)
+    if args.only in (None, "v1"):
+        w = inp.V1_BF16
+        log(f"[bench] generating {w.name}")
+        x = inp.v1_inputs(w, device=dev)
+        out = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device=dev)
+        ws = torch.empty(da.v1_workspace_bytes(w.B, w.T, w.H, w.d, w.dv, torch.bfloat16),
+                         dtype=torch.uint8, device=dev)
+        lams = [da.lambda_init(l) for l in w.layers]
+
+        def v1_call(li):
+            da.v1_fwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], li, li, w.eps, out=out,
+                      workspace=ws)
+
+        def step():
+            for li in lams:
+                v1_call(li)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        log(f"[bench] timing {args.steps} steps x {len(lams)} layer calls")
+        t0 = time.perf_counter()
+        ms_step = time_calls(step, args.steps, stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        flop_call = v1_flops(w.B, w.T, w.H, w.d, w.dv)
+        flop_step = flop_call * len(lams)
+        tflops = flop_step / (ms_step * 1e-3) / 1e12
+        ms_call = ms_step / len(lams)
+        result = {
+            "metric": "diff-attn prefill TFLOP/s (% bf16 MFMA peak); V2 decode HBM GB/s (% peak)",
+            "value": round(tflops, 2),
+            "unit": "TFLOP/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(ms_step, 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1)/sqrt(128) bf16 inputs, generated on the GPU)",
+            "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "d": w.d, "dv": w.dv,
+                       "layers": f"{w.layers[0]}..{w.layers[-1]}", "calls_per_step": len(lams),
+                       "causal": True, "parallelism": "single GPU"},
+            "roofline": {"bound": "mfma", "achieved": round(flop_call / (ms_call * 1e-3) / 1e12, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(flop_call / (ms_call * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None,
+                         "kernel": "diffattn_v1_fwd (V pack + fused prefill), HIP events per call",
+                         "ms_per_launch": round(ms_call, 4),
+                         "flop_per_launch": flop_call},
+            "wall_s_timed": round(wall, 3),
+        }
+        del x, out, ws
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------ secondary kernels
+    if not args.no_secondary:
+        iters = max(3, args.steps)
+        if args.only in (None, "v2"):
+            w = inp.V2_PREFILL
+            log(f"[bench] {w.name}")
+            x = inp.v2_inputs(w, device=dev)
+            o = torch.empty((w.B, w.T, w.Hq // 2, w.d), dtype=torch.bfloat16, device=dev)
+            f = lambda: da.v2_fwd(x["q"], x["k"], x["v"], x["logit"], out=o)
+            for _ in range(args.warmup):
+                f()
+            ms = time_calls(f, iters, stream)
+            flop = w.B * v2_flops_seq(w.T, w.Hq, w.d)
+            tf = flop / (ms * 1e-3) / 1e12
+            secondary["v2_prefill"] = {"workload": w.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
+                                       "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flop": flop}
+            del x, o
+            torch.cuda.empty_cache()
+        if args.only in (None, "varlen"):
+            w = inp.V2_VARLEN
+            log(f"[bench] {w.name} lengths={w.lengths}")
+            x = inp.v2_inputs(w, device=dev)
+            N = sum(w.lengths)
+            o = torch.empty((N, w.Hq // 2, w.d), dtype=torch.bfloat16, device=dev)
+            mx = max(w.lengths)
+            f = lambda: da.v2_fwd(x["q"], x["k"], x["v"], x["logit"], cu_seqlens=x["cu_seqlens"],
+                                  max_seqlen=mx, out=o)
+            for _ in range(args.warmup):
+                f()
+            ms = time_calls(f, iters, stream)
+            flop = sum(v2_flops_seq(n, w.Hq, w.d) for n in w.lengths)
+            tf = flop / (ms * 1e-3) / 1e12
+            secondary["v2_varlen"] = {"workload": w.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
+                                      "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flop": flop,
+                                      "lengths": list(w.lengths)}
+            del x, o
+            torch.cuda.empty_cache()
+        if args.only in (None, "decode"):
+            w = inp.V2_DECODE
+            log(f"[bench] {w.name}")
+            x = inp.decode_inputs(w, device=dev)
+            o = torch.empty((w.B, w.Hq // 2, w.d), dtype=torch.bfloat16, device=dev)
+            wsd = torch.empty(da.v2_decode_workspace_bytes(w.B, w.S, w.Hq, w.Hkv, w.d),
+                              dtype=torch.uint8, device=dev)
+            f = lambda: da.v2_decode(x["q"], x["k_cache"], x["v_cache"], x["logit"], out=o,
+                                     workspace=wsd)
+            for _ in range(args.warmup):
+                f()
+            ms = time_calls(f, iters, stream)
+            byts = 2.0 * w.B * w.S * w.Hkv * w.d * 2
+            gbs = byts / (ms * 1e-3) / 1e9
+            secondary["v2_decode"] = {"workload": w.name, "ms": round(ms, 4), "GB/s": round(gbs, 1),
+                                      "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": byts}
+            del x, o, wsd
+            torch.cuda.empty_cache()
+    if secondary:
+        result["secondary"] = secondary
+
+    # ------------------------------------------------------------------ CPU oracle baseline
+    if not args.no_cpu_baseline and args.only in (None, "v1"):
+        result["cpu_baseline"] = cpu_baseline()
+
+    if "metric" not in result:
+        result = {"metric": "partial run (--only)", "secondary": secondary}
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(budget_s: float = 12.0) -> dict:
+    """Time the fp64 oracle on (batch, head) slices of the headline workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from differential_softmax_attention_diffattn_amd import inputs as inp
+
+    w = inp.V1_BF16
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    # one (b, h) slice at a time, all 4096 rows, layer 1
+    x = inp.v1_inputs(w.with_shape(B=1, H=4))
+    lam = oracle.lambda_init(1)
+    done = 0
+    flop = 0.0
+    t0 = time.perf_counter()
+    for h in range(4):
+        sl = [x[k][:, :, h:h + 1] for k in ("q1", "k1", "q2", "k2", "v")]
+        oracle.v1_forward(*sl, lam, lam, w.eps)
+        done += 1
+        flop += v1_flops(1, w.T, 1, w.d, w.dv)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{done} of 48 (batch, head) slices of {w.name}, all 4096 rows, layer 1, fp64 numpy"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,221 @@
+"""Differential attention (DIFF V1 / V2) on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/diffattn.h``: every function
+here only checks and marshals torch tensors (device, dtype, shape,
+contiguity), allocates outputs/workspaces with torch when the caller does not
+pass them, and calls the HIP library on torch's current stream.  All of the
+arithmetic runs in the library's kernels; there is no fallback path.
+
+    v1_fwd      V1: (softmax(Q1K1^T/sqrt d) - lambda softmax(Q2K2^T/sqrt d)) V,
+                per-head RMS norm, (1 - lambda_init) factor
+    v2_fwd      V2: GQA attention over 2h query heads, O_even - sigmoid(logit) O_odd
+                (padded or packed/varlen batches)
+    v2_decode   V2 decode step against a KV cache
+    lambda_init 0.8 - 0.6 exp(-0.3 (l - 1))
+"""
+from __future__ import annotations
+
+from . import _lib
+from ._lib import DIFFATTN_BF16, DIFFATTN_F32, DiffAttnError  # noqa: F401
+
+__all__ = [
+    "v1_fwd",
+    "v2_fwd",
+    "v2_decode",
+    "lambda_init",
+    "v1_workspace_bytes",
+    "v2_decode_workspace_bytes",
+    "DiffAttnError",
+]
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return DIFFATTN_F32
+    if t.dtype == torch.bfloat16:
+        return DIFFATTN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check_tensor(name, t, dtype=None, dim=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims (got shape {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device):
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def lambda_init(layer: int) -> float:
+    """Initial lambda of 1-based layer ``layer`` (computed by the library, fp32)."""
+    v = _lib.load().diffattn_lambda_init(int(layer))
+    if v != v:  # NaN
+        _lib.check("diffattn_lambda_init", -1)
+    return v
+
+
+def v1_workspace_bytes(B, T, H, d, dv, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(_torch().empty(0, dtype=dtype))
+    return int(_lib.load().diffattn_v1_workspace_bytes(B, T, H, d, dv, code))
+
+
+def v1_fwd(q1, k1, q2, k2, v, lam: float, lambda_init: float, eps: float = 1e-12, weight=None,
+           causal: bool = True, out=None, workspace=None):
+    """DIFF V1 forward.  q1,k1,q2,k2: [B,T,H,d]; v: [B,T,H,dv] (fp32 or bf16) -> out [B,T,H,dv] fp32."""
+    torch = _torch()
+    dev = q1.device
+    _check_tensor("q1", q1, dim=4)
+    for n, t in (("k1", k1), ("q2", q2), ("k2", k2)):
+        _check_tensor(n, t, dtype=q1.dtype, dim=4, device=dev)
+        if t.shape != q1.shape:
+            raise ValueError(f"{n} shape {tuple(t.shape)} != q1 shape {tuple(q1.shape)}")
+    _check_tensor("v", v, dtype=q1.dtype, dim=4, device=dev)
+    B, T, H, d = q1.shape
+    if tuple(v.shape[:3]) != (B, T, H):
+        raise ValueError(f"v shape {tuple(v.shape)} does not match q1 {tuple(q1.shape)}")
+    dv = v.shape[3]
+    if weight is not None:
+        _check_tensor("weight", weight, dtype=torch.float32, dim=1, device=dev)
+        if weight.shape[0] != dv:
+            raise ValueError("weight must have dv entries")
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _check_tensor("out", out, dtype=torch.float32, dim=4, device=dev)
+    if tuple(out.shape) != (B, T, H, dv):
+        raise ValueError("out has the wrong shape")
+    code = _dtype_code(q1)
+    lib = _lib.load()
+    need = int(lib.diffattn_v1_workspace_bytes(B, T, H, d, dv, code))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _check_tensor("workspace", workspace, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        rc = lib.diffattn_v1_fwd(
+            _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(weight), _ptr(out), B, T, H, d,
+            dv, float(lam), float(lambda_init), float(eps), 1 if causal else 0, code,
+            _ptr(workspace), ws_bytes, _stream(dev))
+    _lib.check("diffattn_v1_fwd", rc)
+    return out
+
+
+def v2_fwd(q, k, v, logit, cu_seqlens=None, max_seqlen=None, causal: bool = True,
+           scale: float | None = None, out=None):
+    """DIFF V2 forward.
+
+    Padded: q [B,T,Hq,d], k/v [B,T,Hkv,d] bf16, logit [B,T,Hq/2] fp32 -> out [B,T,Hq/2,d] bf16.
+    Packed: q [N,Hq,d], k/v [N,Hkv,d], logit [N,Hq/2], cu_seqlens int32 [nseq+1] on the GPU and
+    ``max_seqlen`` (host int, >= every sequence length) -> out [N,Hq/2,d].
+    """
+    torch = _torch()
+    dev = q.device
+    packed = cu_seqlens is not None
+    nd = 3 if packed else 4
+    _check_tensor("q", q, dtype=torch.bfloat16, dim=nd)
+    _check_tensor("k", k, dtype=torch.bfloat16, dim=nd, device=dev)
+    _check_tensor("v", v, dtype=torch.bfloat16, dim=nd, device=dev)
+    _check_tensor("logit", logit, dtype=torch.float32, dim=nd - 1, device=dev)
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    lead = tuple(q.shape[:nd - 2])
+    Hq, d = q.shape[-2], q.shape[-1]
+    Hkv = k.shape[-2]
+    if tuple(k.shape[:nd - 2]) != lead or k.shape[-1] != d:
+        raise ValueError("k/v shape does not match q")
+    if Hq % 2:
+        raise ValueError("Hq must be even")
+    if tuple(logit.shape) != lead + (Hq // 2,):
+        raise ValueError(f"logit must have shape {lead + (Hq // 2,)}")
+    if out is None:
+        out = torch.empty(lead + (Hq // 2, d), dtype=torch.bfloat16, device=dev)
+    _check_tensor("out", out, dtype=torch.bfloat16, dim=nd, device=dev)
+    if tuple(out.shape) != lead + (Hq // 2, d):
+        raise ValueError("out has the wrong shape")
+    if packed:
+        _check_tensor("cu_seqlens", cu_seqlens, dtype=torch.int32, dim=1, device=dev)
+        if max_seqlen is None:
+            raise ValueError("max_seqlen (a host int) is required with cu_seqlens")
+        nseq = cu_seqlens.shape[0] - 1
+        B, T = 0, 0
+    else:
+        nseq, max_seqlen = 0, 0
+        B, T = lead
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        rc = lib.diffattn_v2_fwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(logit), _ptr(out), _ptr(cu_seqlens), nseq,
+            int(max_seqlen), B, T, Hq, Hkv, d, float(scale or 0.0), 1 if causal else 0,
+            DIFFATTN_BF16, _stream(dev))
+    _lib.check("diffattn_v2_fwd", rc)
+    return out
+
+
+def v2_decode_workspace_bytes(B, S_max, Hq, Hkv, d) -> int:
+    return int(_lib.load().diffattn_v2_decode_workspace_bytes(B, S_max, Hq, Hkv, d))
+
+
+def v2_decode(q, k_cache, v_cache, logit, cache_len=None, scale: float | None = None, out=None,
+              workspace=None):
+    """DIFF V2 decode step.  q [B,Hq,d], caches [B,S_max,Hkv,d] bf16, logit [B,Hq/2] fp32,
+    cache_len int32 [B] on the GPU or None -> out [B,Hq/2,d] bf16."""
+    torch = _torch()
+    dev = q.device
+    _check_tensor("q", q, dtype=torch.bfloat16, dim=3)
+    _check_tensor("k_cache", k_cache, dtype=torch.bfloat16, dim=4, device=dev)
+    _check_tensor("v_cache", v_cache, dtype=torch.bfloat16, dim=4, device=dev)
+    _check_tensor("logit", logit, dtype=torch.float32, dim=2, device=dev)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    B, Hq, d = q.shape
+    _, S_max, Hkv, dk = k_cache.shape
+    if k_cache.shape[0] != B or dk != d:
+        raise ValueError("cache shape does not match q")
+    if Hq % 2:
+        raise ValueError("Hq must be even")
+    if tuple(logit.shape) != (B, Hq // 2):
+        raise ValueError("logit must have shape [B, Hq/2]")
+    if cache_len is not None:
+        _check_tensor("cache_len", cache_len, dtype=torch.int32, dim=1, device=dev)
+        if cache_len.shape[0] != B:
+            raise ValueError("cache_len must have B entries")
+    if out is None:
+        out = torch.empty((B, Hq // 2, d), dtype=torch.bfloat16, device=dev)
+    _check_tensor("out", out, dtype=torch.bfloat16, dim=3, device=dev)
+    lib = _lib.load()
+    need = int(lib.diffattn_v2_decode_workspace_bytes(B, S_max, Hq, Hkv, d))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _check_tensor("workspace", workspace, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        rc = lib.diffattn_v2_decode(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(logit), _ptr(out),
+            _ptr(workspace), ws_bytes, B, S_max, Hq, Hkv, d, float(scale or 0.0), DIFFATTN_BF16,
+            _stream(dev))
+    _lib.check("diffattn_v2_decode", rc)
+    return out

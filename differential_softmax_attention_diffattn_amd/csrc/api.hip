@@ -1,0 +1,249 @@
+// C ABI of the differential-attention library: argument validation, workspace
+// queries and kernel dispatch.  Every check runs before any launch, so an
+// error return leaves the outputs untouched.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/diffattn.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return DIFFATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DIFFATTN_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Product of non-negative ints, or -1 on overflow past int64.
+long long prod(std::initializer_list<long long> xs) {
+  long long r = 1;
+  for (long long x : xs) {
+    if (x < 0) return -1;
+    if (x != 0 && r > (long long)(INT64_MAX / x)) return -1;
+    r *= x;
+  }
+  return r;
+}
+
+bool v1_shape_supported(int d, int dv, diffattn_dtype dt) {
+  if (dt == DIFFATTN_F32) return d >= 16 && d <= 128 && d % 16 == 0 && dv >= 16 && dv <= 256 && dv % 16 == 0;
+  if (dt == DIFFATTN_BF16) return (d == 128 && dv == 256) || (d == 64 && dv == 128);
+  return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+int diffattn_version(void) { return 100; }
+
+const char* diffattn_last_error(void) { return g_last_error.c_str(); }
+
+float diffattn_lambda_init(int layer) {
+  if (layer < 1) {
+    fail(DIFFATTN_E_INVALID, "diffattn_lambda_init: layer must be >= 1 (got %d)", layer);
+    return NAN;
+  }
+  g_last_error.clear();
+  return 0.8f - 0.6f * expf(-0.3f * (float)(layer - 1));
+}
+
+size_t diffattn_v1_workspace_bytes(int B, int T, int H, int d, int dv, diffattn_dtype in_dtype) {
+  if (B < 0 || T < 0 || H < 0 || !v1_shape_supported(d, dv, in_dtype)) return 0;
+  if (in_dtype != DIFFATTN_BF16 || prod({B, T, H}) == 0) return 0;
+  return diffattn::v1_bf16_workspace_bytes(B, T, H, d, dv);
+}
+
+int diffattn_v1_fwd(const void* q1, const void* k1, const void* q2, const void* k2,
+                    const void* v, const float* norm_weight, float* out, int B, int T, int H,
+                    int d, int dv, float lambda, float lambda_init, float eps, int causal,
+                    diffattn_dtype in_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  const char* fn = "diffattn_v1_fwd";
+  if (!q1 || !k1 || !q2 || !k2 || !v || !out)
+    return fail(DIFFATTN_E_INVALID, "%s: null tensor pointer", fn);
+  if (B < 0 || T < 0 || H < 0 || d <= 0 || dv <= 0)
+    return fail(DIFFATTN_E_INVALID, "%s: bad sizes B=%d T=%d H=%d d=%d dv=%d", fn, B, T, H, d, dv);
+  if (in_dtype != DIFFATTN_F32 && in_dtype != DIFFATTN_BF16)
+    return fail(DIFFATTN_E_INVALID, "%s: unknown dtype %d", fn, (int)in_dtype);
+  if (causal != 0 && causal != 1) return fail(DIFFATTN_E_INVALID, "%s: causal must be 0 or 1", fn);
+  if (!isfinite(lambda) || !isfinite(lambda_init) || !isfinite(eps) || eps < 0.f)
+    return fail(DIFFATTN_E_INVALID, "%s: lambda, lambda_init must be finite and eps finite >= 0", fn);
+  if (!v1_shape_supported(d, dv, in_dtype))
+    return fail(DIFFATTN_E_UNSUPPORTED,
+                "%s: (d=%d, dv=%d) not supported for %s inputs (fp32: multiples of 16, d<=128, "
+                "dv<=256; bf16: (128,256) or (64,128))",
+                fn, d, dv, in_dtype == DIFFATTN_F32 ? "fp32" : "bf16");
+  const long long nout = prod({B, T, H, dv});
+  if (nout < 0 || prod({B, T, H, d}) < 0 || nout > (1LL << 40))
+    return fail(DIFFATTN_E_INVALID, "%s: problem too large", fn);
+  const void* ptrs[] = {q1, k1, q2, k2, v, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(DIFFATTN_E_ALIGN, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (norm_weight && !aligned4(norm_weight))
+    return fail(DIFFATTN_E_ALIGN, "%s: norm_weight must be 4-byte aligned", fn);
+  if (nout == 0) return ok();
+  const size_t need = diffattn_v1_workspace_bytes(B, T, H, d, dv, in_dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(DIFFATTN_E_WORKSPACE, "%s: workspace of %zu bytes required (got %zu%s)", fn, need,
+                workspace_bytes, workspace ? "" : ", NULL");
+  if (need > 0 && !aligned16(workspace))
+    return fail(DIFFATTN_E_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+
+  diffattn::V1Args a{q1, k1, q2, k2, v, norm_weight, out, B, T, H, d, dv,
+                     lambda, lambda_init, eps, causal};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (in_dtype == DIFFATTN_F32) return from_hip(diffattn::launch_v1_f32(a, s), fn);
+  return from_hip(diffattn::launch_v1_bf16(a, workspace, s), fn);
+}
+
+int diffattn_v2_fwd(const void* q, const void* k, const void* v, const float* lambda_logit,
+                    void* out, const int* cu_seqlens, int nseq, int max_seqlen, int B, int T,
+                    int Hq, int Hkv, int d, float scale, int causal, diffattn_dtype dtype,
+                    void* stream) {
+  const char* fn = "diffattn_v2_fwd";
+  if (!q || !k || !v || !lambda_logit || !out)
+    return fail(DIFFATTN_E_INVALID, "%s: null tensor pointer", fn);
+  if (Hq <= 0 || Hkv <= 0 || d <= 0)
+    return fail(DIFFATTN_E_INVALID, "%s: bad head sizes Hq=%d Hkv=%d d=%d", fn, Hq, Hkv, d);
+  if (Hq % 2) return fail(DIFFATTN_E_INVALID, "%s: Hq=%d must be even (pairs of heads)", fn, Hq);
+  if (Hq % Hkv)
+    return fail(DIFFATTN_E_INVALID, "%s: Hq=%d must be a multiple of Hkv=%d", fn, Hq, Hkv);
+  if ((Hq / Hkv) % 2)
+    return fail(DIFFATTN_E_INVALID,
+                "%s: Hq/Hkv=%d must be even so both heads of a pair share one KV head", fn,
+                Hq / Hkv);
+  if (causal != 0 && causal != 1) return fail(DIFFATTN_E_INVALID, "%s: causal must be 0 or 1", fn);
+  if (!isfinite(scale)) return fail(DIFFATTN_E_INVALID, "%s: scale must be finite", fn);
+  if (dtype != DIFFATTN_BF16)
+    return fail(dtype == DIFFATTN_F32 ? DIFFATTN_E_UNSUPPORTED : DIFFATTN_E_INVALID,
+                "%s: only bf16 is supported", fn);
+  if (d != 64 && d != 128) return fail(DIFFATTN_E_UNSUPPORTED, "%s: d=%d not in {64, 128}", fn, d);
+  int nseq_eff, maxlen;
+  if (cu_seqlens) {
+    if (nseq < 0 || max_seqlen < 0)
+      return fail(DIFFATTN_E_INVALID, "%s: nseq=%d max_seqlen=%d must be >= 0", fn, nseq, max_seqlen);
+    nseq_eff = nseq;
+    maxlen = max_seqlen;
+  } else {
+    if (B < 0 || T < 0) return fail(DIFFATTN_E_INVALID, "%s: B=%d T=%d must be >= 0", fn, B, T);
+    if (prod({B, T, Hq, d}) > (1LL << 40)) return fail(DIFFATTN_E_INVALID, "%s: problem too large", fn);
+    nseq_eff = B;
+    maxlen = T;
+  }
+  const void* ptrs[] = {q, k, v, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(DIFFATTN_E_ALIGN, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (!aligned4(lambda_logit) || (cu_seqlens && !aligned4(cu_seqlens)))
+    return fail(DIFFATTN_E_ALIGN, "%s: lambda_logit and cu_seqlens must be 4-byte aligned", fn);
+  if (nseq_eff == 0 || maxlen == 0) return ok();
+  diffattn::V2Args a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.logit = lambda_logit;
+  a.out = static_cast<uint16_t*>(out);
+  a.cu_seqlens = cu_seqlens;
+  a.nseq = nseq_eff;
+  a.max_seqlen = maxlen;
+  a.T = T;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+  a.causal = causal;
+  return from_hip(diffattn::launch_v2_prefill(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+size_t diffattn_v2_decode_workspace_bytes(int B, int S_max, int Hq, int Hkv, int d) {
+  if (B < 0 || S_max < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || (Hq / Hkv) % 2 || Hq / Hkv > 16)
+    return 0;
+  if (d != 64 && d != 128) return 0;
+  int split_len, nsplit;
+  diffattn::decode_split(B, S_max, Hkv, &split_len, &nsplit);
+  const long long n = prod({B, Hq, nsplit, d + 2});
+  return n < 0 ? 0 : (size_t)n * sizeof(float);
+}
+
+int diffattn_v2_decode(const void* q, const void* k_cache, const void* v_cache,
+                       const int* cache_len, const float* lambda_logit, void* out,
+                       void* workspace, size_t workspace_bytes, int B, int S_max, int Hq,
+                       int Hkv, int d, float scale, diffattn_dtype dtype, void* stream) {
+  const char* fn = "diffattn_v2_decode";
+  if (!q || !k_cache || !v_cache || !lambda_logit || !out)
+    return fail(DIFFATTN_E_INVALID, "%s: null tensor pointer", fn);
+  if (B < 0 || S_max < 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
+    return fail(DIFFATTN_E_INVALID, "%s: bad sizes B=%d S_max=%d Hq=%d Hkv=%d d=%d", fn, B, S_max,
+                Hq, Hkv, d);
+  if (Hq % 2) return fail(DIFFATTN_E_INVALID, "%s: Hq=%d must be even (pairs of heads)", fn, Hq);
+  if (Hq % Hkv)
+    return fail(DIFFATTN_E_INVALID, "%s: Hq=%d must be a multiple of Hkv=%d", fn, Hq, Hkv);
+  if ((Hq / Hkv) % 2)
+    return fail(DIFFATTN_E_INVALID,
+                "%s: Hq/Hkv=%d must be even so both heads of a pair share one KV head", fn,
+                Hq / Hkv);
+  if (!isfinite(scale)) return fail(DIFFATTN_E_INVALID, "%s: scale must be finite", fn);
+  if (dtype != DIFFATTN_BF16)
+    return fail(dtype == DIFFATTN_F32 ? DIFFATTN_E_UNSUPPORTED : DIFFATTN_E_INVALID,
+                "%s: only bf16 is supported", fn);
+  if (d != 64 && d != 128) return fail(DIFFATTN_E_UNSUPPORTED, "%s: d=%d not in {64, 128}", fn, d);
+  if (Hq / Hkv > 16)
+    return fail(DIFFATTN_E_UNSUPPORTED, "%s: Hq/Hkv=%d above 16 query heads per KV head", fn,
+                Hq / Hkv);
+  if (prod({B, S_max, Hkv, d}) > (1LL << 40)) return fail(DIFFATTN_E_INVALID, "%s: problem too large", fn);
+  const void* ptrs[] = {q, k_cache, v_cache, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(DIFFATTN_E_ALIGN, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (!aligned4(lambda_logit) || (cache_len && !aligned4(cache_len)))
+    return fail(DIFFATTN_E_ALIGN, "%s: lambda_logit and cache_len must be 4-byte aligned", fn);
+  if (B == 0) return ok();
+  const size_t need = diffattn_v2_decode_workspace_bytes(B, S_max, Hq, Hkv, d);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DIFFATTN_E_WORKSPACE, "%s: workspace of %zu bytes required (got %zu%s)", fn, need,
+                workspace_bytes, workspace ? "" : ", NULL");
+  if (!aligned16(workspace)) return fail(DIFFATTN_E_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  diffattn::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.cache_len = cache_len;
+  a.logit = lambda_logit;
+  a.out = static_cast<uint16_t*>(out);
+  a.partial = static_cast<float*>(workspace);
+  a.B = B;
+  a.S_max = S_max;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  diffattn::decode_split(B, S_max, Hkv, &a.split_len, &a.nsplit);
+  a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+  return from_hip(diffattn::launch_v2_decode(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"

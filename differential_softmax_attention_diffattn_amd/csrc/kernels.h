@@ -1,0 +1,63 @@
+// Host-side launch interface between the C ABI (api.cpp) and the HIP kernels.
+// Argument validation happens in api.cpp before any of these is called; the
+// launchers only pick a kernel instance and a grid, and enqueue on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace diffattn {
+
+struct V1Args {
+  const void* q1;
+  const void* k1;
+  const void* q2;
+  const void* k2;
+  const void* v;
+  const float* norm_weight;  // [dv] or nullptr
+  float* out;                // [B,T,H,dv]
+  int B, T, H, d, dv;
+  float lambda, lambda_init, eps;
+  int causal;
+};
+
+struct V2Args {
+  const uint16_t* q;        // bf16 [tokens, Hq, d]
+  const uint16_t* k;        // bf16 [tokens, Hkv, d]
+  const uint16_t* v;        // bf16 [tokens, Hkv, d]
+  const float* logit;       // fp32 [tokens, Hq/2]
+  uint16_t* out;            // bf16 [tokens, Hq/2, d]
+  const int* cu_seqlens;    // device [nseq+1] or nullptr (padded: sequence s = tokens s*T .. s*T+T-1)
+  int nseq;                 // number of sequences (B when padded)
+  int max_seqlen;           // longest sequence (T when padded)
+  int T;                    // padded sequence length (unused when cu_seqlens != nullptr)
+  int Hq, Hkv, d;
+  float scale;              // softmax scale (> 0)
+  int causal;
+};
+
+struct DecodeArgs {
+  const uint16_t* q;        // bf16 [B, Hq, d]
+  const uint16_t* k_cache;  // bf16 [B, S_max, Hkv, d]
+  const uint16_t* v_cache;  // bf16 [B, S_max, Hkv, d]
+  const int* cache_len;     // device [B] or nullptr
+  const float* logit;       // fp32 [B, Hq/2]
+  uint16_t* out;            // bf16 [B, Hq/2, d]
+  float* partial;           // fp32 workspace [B, Hq, nsplit, d + 2]
+  int B, S_max, Hq, Hkv, d;
+  int split_len, nsplit;
+  float scale;
+};
+
+// Decode split rule shared by the workspace query and the launcher.
+void decode_split(int B, int S_max, int Hkv, int* split_len, int* nsplit);
+
+hipError_t launch_v1_f32(const V1Args& a, hipStream_t stream);
+// bf16 V1 needs a workspace for V packed as fp16 tiles (see v1_prefill.hip).
+size_t v1_bf16_workspace_bytes(int B, int T, int H, int d, int dv);
+hipError_t launch_v1_bf16(const V1Args& a, void* workspace, hipStream_t stream);
+hipError_t launch_v2_prefill(const V2Args& a, hipStream_t stream);
+hipError_t launch_v2_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace diffattn

@@ -1,0 +1,443 @@
+// DIFF V1 fused prefill on gfx950, bf16 inputs.
+//
+// Per (batch, head) and query row t, with the two query/key halves (Q1,K1) and
+// (Q2,K2) and values V whose head dim is twice the query/key dim:
+//     z_t = sum_k (softmax_k(q1_t.k1_k/sqrt d) - lambda softmax_k(q2_t.k2_k/sqrt d)) v_k
+//     y_t = (1 - lambda_init) * w * z_t / sqrt(mean(z_t^2) + eps)
+// ("Differential Transformer | ICLR 2025 Oral" blog, section "Differential
+// Attention: 빼기의 힘"; the per-head RMS norm and the lambda_init factor are
+// from the V1 recap in the "Differential Transformer V2" summary, 상세 정리 §1).
+//
+// A workgroup of 4 waves owns 128 query rows of one (batch, head); each wave
+// owns 32 rows = two 16-column blocks, and runs two online-softmax streams over
+// the same staged K1/K2/V tiles.  Scores are formed transposed, S^T = K Q^T on
+// 16x16x32 bf16 MFMA, so one lane holds one query column per block.  P is
+// rounded to fp16 (11-bit significand) and P.V runs on 16x16x32 fp16 MFMA:
+// bf16 P would put the RMS-normalised output outside a 2e-2 RMS(V) error
+// budget, because the norm divides by |z|, which is small when both maps are
+// near-uniform.  A pre-pass converts V bf16->fp16 (exact for normal-range
+// values) into a workspace laid out tile by tile as Vt[d][key] with padded
+// rows, exactly the LDS image the main kernel needs, so V tiles reach LDS by
+// direct-to-LDS loads with no register staging or per-tile conversion.  One V^T fragment read from LDS feeds four MFMAs (two
+// streams x two column blocks).  The subtraction, RMS norm and scale run on
+// the accumulators in registers; the output is fp32.
+#include <math.h>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace diffattn {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kRows = 32;
+constexpr int kQTile = kWaves * kRows;  // 128 query rows per workgroup
+constexpr int kKeys = 64;
+constexpr float kRescaleLog2 = 8.0f;  // P <= 2^8, well inside fp16 range
+
+template <int D, int DV>
+struct Tile {
+  static constexpr int kChunks = D / 8;
+  static constexpr int kKBytes = kKeys * D * 2;       // one of K1 / K2
+  static constexpr int kVtStride = kKeys + 8;         // fp16 elements per Vt row (144 B)
+  static constexpr int kVtBytes = DV * kVtStride * 2;
+  static constexpr int kStage = 2 * kKBytes + kVtBytes;
+  static constexpr int kKInstrPerWave = kKBytes / 1024 / kWaves;
+  static constexpr int kVKeysPerThread = DV / 32;  // 8 for DV = 256, 4 for DV = 128
+  static constexpr int kVInstr = kVtBytes / 1024;   // 1 KiB direct loads per V tile
+};
+
+// Pre-pass: V [B,T,H,DV] bf16 -> per (b, h, key tile) an fp16 block Vt[DV][kVtStride]
+// (keys 0..63 of the tile, then zero padding; keys past T are zero).
+template <int D, int DV>
+__global__ __launch_bounds__(kThreads) void v1_pack_v_kernel(V1Args a, uint16_t* vp) {
+  using TL = Tile<D, DV>;
+  constexpr int NKT = TL::kVKeysPerThread;
+  const int n_kt = (a.T + kKeys - 1) / kKeys;
+  const int kt = blockIdx.x % n_kt;
+  const int bh = blockIdx.x / n_kt;
+  const int b = bh / a.H;
+  const int h = bh - b * a.H;
+  const uint16_t* vsrc = static_cast<const uint16_t*>(a.v);
+  const int dc = threadIdx.x % (DV / 8);
+  const int kg = threadIdx.x / (DV / 8);
+  u32x4 hv[NKT];
+#pragma unroll
+  for (int k = 0; k < NKT; ++k) {
+    const int key = kt * kKeys + kg * NKT + k;
+    u32x4 w = u32x4{0, 0, 0, 0};
+    if (key < a.T) w = ldg128(vsrc + (((size_t)b * a.T + key) * a.H + h) * DV + dc * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hv[k][j] = bf16x2_to_f16x2(w[j]);
+  }
+  uint16_t* vt = vp + (size_t)blockIdx.x * (DV * TL::kVtStride);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint16_t* r0 = vt + (dc * 8 + 2 * j) * TL::kVtStride + kg * NKT;
+    uint16_t* r1 = r0 + TL::kVtStride;
+    if constexpr (NKT == 8) {
+      *reinterpret_cast<u32x4*>(r0) =
+          u32x4{pack_lo16(hv[0][j], hv[1][j]), pack_lo16(hv[2][j], hv[3][j]),
+                pack_lo16(hv[4][j], hv[5][j]), pack_lo16(hv[6][j], hv[7][j])};
+      *reinterpret_cast<u32x4*>(r1) =
+          u32x4{pack_hi16(hv[0][j], hv[1][j]), pack_hi16(hv[2][j], hv[3][j]),
+                pack_hi16(hv[4][j], hv[5][j]), pack_hi16(hv[6][j], hv[7][j])};
+    } else {
+      *reinterpret_cast<u32x2*>(r0) =
+          u32x2{pack_lo16(hv[0][j], hv[1][j]), pack_lo16(hv[2][j], hv[3][j])};
+      *reinterpret_cast<u32x2*>(r1) =
+          u32x2{pack_hi16(hv[0][j], hv[1][j]), pack_hi16(hv[2][j], hv[3][j])};
+    }
+  }
+  if (kg == 0) {  // zero the padding columns of this thread's 8 rows
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      *reinterpret_cast<u32x4*>(vt + (dc * 8 + r) * TL::kVtStride + kKeys) = u32x4{0, 0, 0, 0};
+  }
+}
+
+__device__ __forceinline__ int k_swizzled(int row, int chunk, int nchunks) {
+  return row * nchunks * 16 + ((chunk ^ (row & (nchunks - 1))) << 4);
+}
+
+template <int D, int DV, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const uint16_t* vp) {
+  using TL = Tile<D, DV>;
+  constexpr int NC = D / 32;
+  constexpr int NDB = DV / 16;
+  constexpr int NKT = TL::kVKeysPerThread;
+
+  __shared__ __align__(16) uint8_t smem[2 * TL::kStage];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+
+  const int BH = a.B * a.H;
+  const int n_qt = (a.T + kQTile - 1) / kQTile;
+  const int jr = blockIdx.x / BH;
+  const int bh = blockIdx.x - jr * BH;
+  const int qt = n_qt - 1 - jr;
+  const int b = bh / a.H;
+  const int h = bh - b * a.H;
+  const int T = a.T;
+  const size_t tok_base = (size_t)b * T;
+
+  const int q_lo = qt * kQTile + wave * kRows;
+  const bool wave_active = q_lo < T;
+  const int q_end_block = min(qt * kQTile + kQTile, T);
+  const int n_kt_all = (T + kKeys - 1) / kKeys;
+  const int n_kt = CAUSAL ? (q_end_block - 1) / kKeys + 1 : n_kt_all;
+  const int wave_key_end = CAUSAL ? min(q_lo + kRows, T) : T;
+
+  const uint16_t* q1 = static_cast<const uint16_t*>(a.q1);
+  const uint16_t* q2 = static_cast<const uint16_t*>(a.q2);
+  const uint16_t* k1 = static_cast<const uint16_t*>(a.k1);
+  const uint16_t* k2 = static_cast<const uint16_t*>(a.k2);
+
+  // Q^T fragments of both streams
+  u32x4 qf[2][2][NC];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int row = q_lo + nb * 16 + c16;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (row < T) {
+        const size_t off = ((tok_base + row) * a.H + h) * D + c * 32 + g * 8;
+        qf[0][nb][c] = ldg128(q1 + off);
+        qf[1][nb][c] = ldg128(q2 + off);
+      } else {
+        qf[0][nb][c] = u32x4{0, 0, 0, 0};
+        qf[1][nb][c] = u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+
+  auto load_k_tiles = [&](int kt, int stage) {
+    uint8_t* base = smem + stage * TL::kStage;
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx) {
+      const uint16_t* ksrc = sidx == 0 ? k1 : k2;
+#pragma unroll
+      for (int j = 0; j < TL::kKInstrPerWave; ++j) {
+        const int blk = wave * TL::kKInstrPerWave + j;
+        const int off = blk * 1024 + lane * 16;
+        const int row = off / (D * 2);
+        const int pos = (off % (D * 2)) >> 4;
+        const int chunk = pos ^ (row & (TL::kChunks - 1));
+        const int key = min(kt * kKeys + row, T - 1);
+        const uint16_t* src = ksrc + ((tok_base + key) * a.H + h) * D + chunk * 8;
+        __builtin_amdgcn_global_load_lds(
+            src,
+            (__attribute__((address_space(3))) void*)(base + sidx * TL::kKBytes + blk * 1024),
+            16, 0, 0);
+      }
+    }
+  };
+  // V tiles: direct-to-LDS copies of the pre-packed fp16 blocks
+  const uint8_t* vp_bh = reinterpret_cast<const uint8_t*>(vp) + (size_t)bh * n_kt_all * TL::kVtBytes;
+  auto load_v_tile = [&](int kt, int stage) {
+    uint8_t* base = smem + stage * TL::kStage + 2 * TL::kKBytes;
+    const uint8_t* src = vp_bh + (size_t)kt * TL::kVtBytes + lane * 16;
+#pragma unroll
+    for (int j = 0; j < (TL::kVInstr + kWaves - 1) / kWaves; ++j) {
+      const int blk = wave + j * kWaves;
+      if (blk < TL::kVInstr)
+        __builtin_amdgcn_global_load_lds(
+            src + blk * 1024, (__attribute__((address_space(3))) void*)(base + blk * 1024), 16, 0,
+            0);
+    }
+  };
+
+  load_k_tiles(0, 0);
+  load_v_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
+
+  f32x4 o[2][NDB][2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) o[s][db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref[2][2], l_part[2][2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      m_ref[s][nb] = -INFINITY;
+      l_part[s][nb] = 0.f;
+    }
+  const float cs = kLog2e / sqrtf((float)D);
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int stage = kt & 1;
+    const bool has_next = kt + 1 < n_kt;
+    if (has_next) {
+      load_k_tiles(kt + 1, stage ^ 1);
+      load_v_tile(kt + 1, stage ^ 1);
+    }
+    if (wave_active) {
+      const uint8_t* kbase = smem + stage * TL::kStage;
+      const uint16_t* vt = reinterpret_cast<const uint16_t*>(kbase + 2 * TL::kKBytes);
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int k0 = kt * kKeys + cc * 32;
+        if (k0 < wave_key_end) {
+          f32x4 sacc[2][2][2];  // [stream][key block][column block]
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int nb = 0; nb < 2; ++nb) sacc[s][kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          // K fragments are fetched one k-chunk ahead of the MFMAs that use them
+          u32x4 kf[2][2], kn[2][2];
+          auto fetch_k = [&](int c, u32x4 (&dst)[2][2]) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+              const int koff = k_swizzled(cc * 32 + kb * 16 + c16, c * 4 + g, TL::kChunks);
+              dst[0][kb] = *reinterpret_cast<const u32x4*>(kbase + koff);
+              dst[1][kb] = *reinterpret_cast<const u32x4*>(kbase + TL::kKBytes + koff);
+            }
+          };
+          fetch_k(0, kn);
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+              for (int kb = 0; kb < 2; ++kb) kf[s][kb] = kn[s][kb];
+            if (c + 1 < NC) fetch_k(c + 1, kn);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int nb = 0; nb < 2; ++nb) {
+                sacc[0][kb][nb] = mfma_bf16(kf[0][kb], qf[0][nb][c], sacc[0][kb][nb]);
+                sacc[1][kb][nb] = mfma_bf16(kf[1][kb], qf[1][nb][c], sacc[1][kb][nb]);
+              }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          const bool need_mask = (k0 + 32 > T) || (CAUSAL && k0 + 31 > q_lo);
+          if (need_mask) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+              for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) {
+                    const int key = k0 + kb * 16 + 4 * g + i;
+                    const int row = q_lo + nb * 16 + c16;
+                    if (key >= T || (CAUSAL && key > row)) sacc[s][kb][nb][i] = -INFINITY;
+                  }
+          }
+          float mt[2][2];
+          bool grow = false;
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+              float x = sacc[s][0][nb][0];
+#pragma unroll
+              for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x = fmaxf(x, sacc[s][kb][nb][i]);
+              mt[s][nb] = max_across_rows(x) * cs;
+              grow |= mt[s][nb] > m_ref[s][nb] + kRescaleLog2;
+            }
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+              for (int nb = 0; nb < 2; ++nb) pin_agpr(o[s][db][nb]);
+          if (wave_any(grow)) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+              for (int nb = 0; nb < 2; ++nb) {
+                const float mn = fmaxf(m_ref[s][nb], mt[s][nb]);
+                const float alpha = (mn == m_ref[s][nb]) ? 1.f : fast_exp2(m_ref[s][nb] - mn);
+                m_ref[s][nb] = mn;
+                l_part[s][nb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                  // one accumulator at a time: read, scale, write back
+                  o[s][db][nb] *= alpha;
+                  pin_agpr(o[s][db][nb]);
+                  __builtin_amdgcn_sched_barrier(0);
+                }
+              }
+          }
+          u32x4 pf[2][2];
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+              const float mb = (m_ref[s][nb] == -INFINITY) ? 0.f : m_ref[s][nb];
+              float pv[8];
+#pragma unroll
+              for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const float e = fast_exp2(fmaf(sacc[s][kb][nb][i], cs, -mb));
+                  pv[kb * 4 + i] = e;
+                  l_part[s][nb] += e;
+                }
+              pf[s][nb] = u32x4{pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]),
+                                pack_f16x2(pv[4], pv[5]), pack_f16x2(pv[6], pv[7])};
+            }
+          // V^T fragments are fetched two blocks ahead of their MFMAs
+          const uint16_t* vbase = vt + c16 * TL::kVtStride + cc * 32 + g * 4;
+          auto fetch_v = [&](int db) {
+            const uint16_t* vr = vbase + db * 16 * TL::kVtStride;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 16);
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+          };
+          u32x4 vq0 = fetch_v(0), vq1 = fetch_v(1);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const u32x4 vf = vq0;
+            vq0 = vq1;
+            if (db + 2 < NDB) vq1 = fetch_v(db + 2);
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+              for (int nb = 0; nb < 2; ++nb) o[s][db][nb] = mfma_f16(vf, pf[s][nb], o[s][db][nb]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) pin_agpr(o[s][db][nb]);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+  }
+
+  if (!wave_active) return;
+
+  // ---- epilogue: z = O1/l1 - lambda O2/l2, RMS norm over DV, scale, fp32 store ----
+  const float post = 1.0f - a.lambda_init;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const float inv1 = 1.0f / sum_across_rows(l_part[0][nb]);
+    const float inv2 = 1.0f / sum_across_rows(l_part[1][nb]);
+    float ss = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float z = fmaf(-a.lambda, __fmul_rn(o[1][db][nb][i], inv2),
+                             __fmul_rn(o[0][db][nb][i], inv1));
+        o[0][db][nb][i] = z;
+        ss = fmaf(z, z, ss);
+      }
+    ss = sum_across_rows(ss);
+    const float r = post / sqrtf(ss * (1.0f / DV) + a.eps);
+    const int row = q_lo + nb * 16 + c16;
+    if (row < T) {
+      float* dst = a.out + ((tok_base + row) * a.H + h) * DV + g * 4;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        f32x4 y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float w = a.norm_weight ? a.norm_weight[db * 16 + g * 4 + i] : 1.0f;
+          y[i] = o[0][db][nb][i] * r * w;
+        }
+        *reinterpret_cast<f32x4*>(dst + db * 16) = y;
+      }
+    }
+  }
+}
+
+template <int D, int DV>
+size_t packed_v_bytes(int B, int T, int H) {
+  return (size_t)B * H * ((T + kKeys - 1) / kKeys) * Tile<D, DV>::kVtBytes;
+}
+
+template <int D, int DV>
+hipError_t launch_typed(const V1Args& a, void* workspace, hipStream_t stream) {
+  const long long n_kt = (a.T + kKeys - 1) / kKeys;
+  const long long pack_blocks = n_kt * a.B * a.H;
+  const long long blocks = (long long)((a.T + kQTile - 1) / kQTile) * a.B * a.H;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL || pack_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  uint16_t* vp = static_cast<uint16_t*>(workspace);
+  hipLaunchKernelGGL((v1_pack_v_kernel<D, DV>), dim3((unsigned)pack_blocks), dim3(kThreads), 0,
+                     stream, a, vp);
+  if (a.causal)
+    hipLaunchKernelGGL((v1_prefill_kernel<D, DV, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, a, vp);
+  else
+    hipLaunchKernelGGL((v1_prefill_kernel<D, DV, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, a, vp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t v1_bf16_workspace_bytes(int B, int T, int H, int d, int dv) {
+  if (d == 128 && dv == 256) return packed_v_bytes<128, 256>(B, T, H);
+  if (d == 64 && dv == 128) return packed_v_bytes<64, 128>(B, T, H);
+  return 0;
+}
+
+hipError_t launch_v1_bf16(const V1Args& a, void* workspace, hipStream_t stream) {
+  if (a.d == 128 && a.dv == 256) return launch_typed<128, 256>(a, workspace, stream);
+  if (a.d == 64 && a.dv == 128) return launch_typed<64, 128>(a, workspace, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace diffattn

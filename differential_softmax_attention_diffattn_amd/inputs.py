@@ -4,11 +4,13 @@ This module is shared by the CPU oracle tests, the GPU parity tests and the
 benchmark.  It holds no attention arithmetic: only random draws, the
 sequence-length draw for packed batches, and rounding to the storage dtype.
 
-Every tensor is drawn on the CPU with ``torch.Generator`` so that the same seed
-gives the same values on any machine.  Large tensors are drawn one leading
-index (batch entry or token block) at a time, each from its own derived seed,
-so that a test can regenerate a single slice without materialising the whole
-tensor on the host.
+By default every tensor is drawn on the CPU with ``torch.Generator`` so that
+the same seed gives the same values on any machine.  Large tensors are drawn
+one leading index (batch entry or token block) at a time, each from its own
+derived seed, so that a slice can be regenerated without materialising the
+whole tensor on the host.  With ``device=`` a GPU, the same recipe runs on that
+device's generator instead (same seeds, different but equally deterministic
+values); callers that check such inputs read them back from the device.
 
 Workload shapes follow the models the method's pages discuss: a 12-head,
 d_model 3072 V1 model whose value heads are twice as wide as its query/key
@@ -32,10 +34,11 @@ def slice_seed(seed: int, index: int) -> int:
 
 
 def normal_slice(shape, seed: int, index: int, std: float = 1.0, mean: float = 0.0,
-                 dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+                 dtype: torch.dtype = torch.bfloat16, device=None) -> torch.Tensor:
     """One slice: fp32 N(0,1) draw, times ``std`` plus ``mean`` in fp32, rounded to ``dtype``."""
-    g = torch.Generator(device="cpu").manual_seed(slice_seed(seed, index))
-    x = torch.randn(tuple(shape), generator=g, dtype=torch.float32)
+    dev = torch.device("cpu") if device is None else torch.device(device)
+    g = torch.Generator(device=dev).manual_seed(slice_seed(seed, index))
+    x = torch.randn(tuple(shape), generator=g, dtype=torch.float32, device=dev)
     if std != 1.0:
         x.mul_(std)
     if mean != 0.0:
@@ -44,12 +47,12 @@ def normal_slice(shape, seed: int, index: int, std: float = 1.0, mean: float = 0
 
 
 def normal(shape, seed: int, std: float = 1.0, mean: float = 0.0,
-           dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+           dtype: torch.dtype = torch.bfloat16, device=None) -> torch.Tensor:
     """A tensor drawn slice by slice along its first axis (see :func:`normal_slice`)."""
     shape = tuple(int(s) for s in shape)
-    out = torch.empty(shape, dtype=dtype)
+    out = torch.empty(shape, dtype=dtype, device=device)
     for i in range(shape[0]):
-        out[i] = normal_slice(shape[1:], seed, i, std, mean, dtype)
+        out[i] = normal_slice(shape[1:], seed, i, std, mean, dtype, device)
     return out
 
 
@@ -178,29 +181,30 @@ WORKLOADS = {w.name: w for w in (V1_FP32_SMALL, V1_BF16, V2_PREFILL, V2_DECODE, 
 # Generators (CPU tensors; callers move them to a device)
 # ---------------------------------------------------------------------------
 
-def v1_inputs(w: V1Workload) -> dict:
+def v1_inputs(w: V1Workload, device=None) -> dict:
     sq, sk, sq2, sk2, sv = w.seeds
     qk_shape = (w.B, w.T, w.H, w.d)
     return dict(
-        q1=normal(qk_shape, sq, w.std, dtype=w.dtype),
-        k1=normal(qk_shape, sk, w.std, dtype=w.dtype),
-        q2=normal(qk_shape, sq2, w.std, dtype=w.dtype),
-        k2=normal(qk_shape, sk2, w.std, dtype=w.dtype),
-        v=normal((w.B, w.T, w.H, w.dv), sv, w.std, dtype=w.dtype),
+        q1=normal(qk_shape, sq, w.std, dtype=w.dtype, device=device),
+        k1=normal(qk_shape, sk, w.std, dtype=w.dtype, device=device),
+        q2=normal(qk_shape, sq2, w.std, dtype=w.dtype, device=device),
+        k2=normal(qk_shape, sk2, w.std, dtype=w.dtype, device=device),
+        v=normal((w.B, w.T, w.H, w.dv), sv, w.std, dtype=w.dtype, device=device),
     )
 
 
-def v2_inputs(w: V2Workload) -> dict:
+def v2_inputs(w: V2Workload, device=None) -> dict:
     """Padded: q [B,T,Hq,d] ...; packed (``w.lengths`` set): q [total,Hq,d], plus cu_seqlens."""
     sq, sk, sv, sl = w.seeds
     h = w.Hq // 2
     if w.lengths is None:
         lead = (w.B, w.T)
         return dict(
-            q=normal(lead + (w.Hq, w.d), sq, w.std),
-            k=normal(lead + (w.Hkv, w.d), sk, w.std),
-            v=normal(lead + (w.Hkv, w.d), sv, w.std),
-            logit=normal(lead + (h,), sl, w.logit_std, w.logit_mean, dtype=torch.float32),
+            q=normal(lead + (w.Hq, w.d), sq, w.std, device=device),
+            k=normal(lead + (w.Hkv, w.d), sk, w.std, device=device),
+            v=normal(lead + (w.Hkv, w.d), sv, w.std, device=device),
+            logit=normal(lead + (h,), sl, w.logit_std, w.logit_mean, dtype=torch.float32,
+                         device=device),
             cu_seqlens=None,
         )
     total = int(sum(w.lengths))
@@ -208,43 +212,44 @@ def v2_inputs(w: V2Workload) -> dict:
     def packed(width, seed, std, mean=0.0, dtype=torch.bfloat16):
         blk = 1024
         nb = (total + blk - 1) // blk
-        t = normal((nb, blk) + width, seed, std, mean, dtype)
+        t = normal((nb, blk) + width, seed, std, mean, dtype, device)
         return t.reshape((nb * blk,) + width)[:total].contiguous()
     return dict(
         q=packed((w.Hq, w.d), sq, w.std),
         k=packed((w.Hkv, w.d), sk, w.std),
         v=packed((w.Hkv, w.d), sv, w.std),
         logit=packed((h,), sl, w.logit_std, w.logit_mean, dtype=torch.float32),
-        cu_seqlens=torch.tensor(cu_seqlens_of(w.lengths), dtype=torch.int32),
+        cu_seqlens=torch.tensor(cu_seqlens_of(w.lengths), dtype=torch.int32, device=device),
     )
 
 
-def decode_small_inputs(w: DecodeWorkload) -> dict:
+def decode_small_inputs(w: DecodeWorkload, device=None) -> dict:
     """Decode inputs for the query, logits and lengths (the caches come from :func:`decode_cache_slice`)."""
     sq, sk, sv, sl = w.seeds
     h = w.Hq // 2
-    lens = None if w.cache_lens is None else torch.tensor(w.cache_lens, dtype=torch.int32)
+    lens = None if w.cache_lens is None else torch.tensor(w.cache_lens, dtype=torch.int32,
+                                                          device=device)
     return dict(
-        q=normal((w.B, w.Hq, w.d), sq, w.std),
-        logit=normal((w.B, h), sl, 1.0, dtype=torch.float32),
+        q=normal((w.B, w.Hq, w.d), sq, w.std, device=device),
+        logit=normal((w.B, h), sl, 1.0, dtype=torch.float32, device=device),
         cache_len=lens,
     )
 
 
-def decode_cache_slice(w: DecodeWorkload, b: int, which: str) -> torch.Tensor:
+def decode_cache_slice(w: DecodeWorkload, b: int, which: str, device=None) -> torch.Tensor:
     """Cache slice [S, Hkv, d] of batch entry ``b``; ``which`` is 'k' or 'v'."""
     seed = w.seeds[1] if which == "k" else w.seeds[2]
-    return normal_slice((w.S, w.Hkv, w.d), seed, b, w.std)
+    return normal_slice((w.S, w.Hkv, w.d), seed, b, w.std, device=device)
 
 
 def decode_inputs(w: DecodeWorkload, device=None) -> dict:
-    """All decode inputs; caches are filled one batch entry at a time (on ``device`` if given)."""
-    out = decode_small_inputs(w)
+    """All decode inputs, drawn on ``device`` (CPU when None), caches one batch entry at a time."""
+    out = decode_small_inputs(w, device)
     dev = torch.device("cpu") if device is None else torch.device(device)
     kc = torch.empty((w.B, w.S, w.Hkv, w.d), dtype=torch.bfloat16, device=dev)
     vc = torch.empty_like(kc)
     for b in range(w.B):
-        kc[b].copy_(decode_cache_slice(w, b, "k"))
-        vc[b].copy_(decode_cache_slice(w, b, "v"))
+        kc[b].copy_(decode_cache_slice(w, b, "k", device))
+        vc[b].copy_(decode_cache_slice(w, b, "v", device))
     out["k_cache"], out["v_cache"] = kc, vc
     return out

@@ -1,0 +1,164 @@
+/*
+ * diffattn.h -- C ABI of the MI355X (gfx950) differential-attention library.
+ *
+ * The library computes the forward pass of differential attention as described
+ * on two web pages:
+ *   [P1] "Differential Transformer | ICLR 2025 Oral" (dainus.ai blog),
+ *        sections "Differential Attention: 빼기의 힘", "λ의 역할과 학습",
+ *        "파라미터 효율성";
+ *   [P2] "Differential Transformer V2" (pogovet.com summary), 상세 정리 §1-§4.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Return value: DIFFATTN_OK (0) on success, a negative DIFFATTN_E_* code on
+ *    error.  Nothing throws.  diffattn_last_error() returns a message for the
+ *    last nonzero code returned on the calling thread.
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    keeps no pointer after a call returns, allocates nothing and does not
+ *    synchronise: work is enqueued asynchronously on `stream`, a hipStream_t
+ *    passed as void* (NULL = the default stream).
+ *  - Tensors are dense and row-major in the index order given.  Pointers to
+ *    bf16/fp32 activation tensors (q, k, v, caches, out) and to workspaces
+ *    must be 16-byte aligned; pointers to per-token/per-head scalars
+ *    (lambda_logit, norm_weight, cu_seqlens, cache_len) 4-byte aligned
+ *    (DIFFATTN_E_ALIGN otherwise).
+ *  - Arguments are validated before anything is launched, so a call that
+ *    returns an error has not touched any output.  DIFFATTN_E_HIP reports a
+ *    failed launch (message from the HIP runtime).
+ *  - "bf16" is bfloat16 stored as 16-bit words; "fp32" is IEEE binary32.
+ *  - Empty problems (a zero batch or length) return DIFFATTN_OK and launch
+ *    nothing.
+ */
+#ifndef DIFFATTN_H_
+#define DIFFATTN_H_
+
+#include <stddef.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define DIFFATTN_API __attribute__((visibility("default")))
+#else
+#define DIFFATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DIFFATTN_F32 = 0, DIFFATTN_BF16 = 1 } diffattn_dtype;
+
+enum {
+  DIFFATTN_OK = 0,
+  DIFFATTN_E_INVALID = -1,     /* bad shape, null pointer, non-finite scalar */
+  DIFFATTN_E_UNSUPPORTED = -2, /* well-formed, but not a shape/dtype this build runs */
+  DIFFATTN_E_ALIGN = -3,       /* a pointer is not 16-byte aligned */
+  DIFFATTN_E_WORKSPACE = -4,   /* workspace missing or smaller than the query says */
+  DIFFATTN_E_HIP = -5          /* the HIP runtime reported an error at launch */
+};
+
+/*
+ * V1 differential attention forward (prefill) [P1 "Differential Attention:
+ * 빼기의 힘"; norm and factor: P2 §1].  For every batch b, head h and query row i:
+ *
+ *   P1 = softmax_j(q1_i . k1_j / sqrt(d)),  P2 = softmax_j(q2_i . k2_j / sqrt(d)),
+ *   z_i = sum_j (P1_ij - lambda * P2_ij) v_j,
+ *   y_i = (1 - lambda_init) * w * z_i / sqrt(mean_c(z_ic^2) + eps),
+ *
+ * with j <= i when causal != 0 and j over all T keys otherwise.  The mean runs
+ * over the dv value channels of the (row, head); w = norm_weight (NULL = ones).
+ *
+ *   q1, k1, q2, k2 : [B, T, H, d]   in_dtype
+ *   v              : [B, T, H, dv]  in_dtype (the pages' V1 uses dv = 2d)
+ *   norm_weight    : [dv] fp32 or NULL
+ *   out            : [B, T, H, dv] fp32
+ *   lambda         : any finite value (the pages allow lambda > 1)
+ *   lambda_init    : the layer's initial lambda (see diffattn_lambda_init)
+ *   eps            : finite, >= 0
+ *   workspace      : device scratch of at least diffattn_v1_workspace_bytes()
+ *                    bytes (may be NULL when that is 0); caller-owned, its
+ *                    contents on entry are ignored and on exit unspecified.
+ *
+ * Supported: in_dtype DIFFATTN_F32 with d in 16..128 and dv in 16..256, both
+ * multiples of 16; in_dtype DIFFATTN_BF16 with (d, dv) = (128, 256) or
+ * (64, 128).  The bf16 path forms P.V in fp16 (11-bit significand), so V
+ * entries must lie within the fp16 range (|v| <= 65504).
+ */
+DIFFATTN_API int diffattn_v1_fwd(const void* q1, const void* k1, const void* q2, const void* k2,
+                    const void* v, const float* norm_weight, float* out, int B, int T, int H,
+                    int d, int dv, float lambda, float lambda_init, float eps, int causal,
+                    diffattn_dtype in_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Workspace bytes diffattn_v1_fwd needs for these sizes (0 for fp32 inputs).
+ * Returns 0 for sizes the call would reject. */
+DIFFATTN_API size_t diffattn_v1_workspace_bytes(int B, int T, int H, int d, int dv, diffattn_dtype in_dtype);
+
+/*
+ * V2 differential attention forward (prefill) [P2 §1, §4].  Hq = 2h query heads
+ * attend over Hkv shared key/value heads; query head j reads KV head
+ * j / (Hq / Hkv).  For every sequence, query row i and pair p:
+ *
+ *   O_j[i]   = sum_t softmax_t(q_{i,j} . k_{t,kv(j)} * scale) v_{t,kv(j)},
+ *   out[i,p] = O_{2p}[i] - sigmoid(lambda_logit[i,p]) * O_{2p+1}[i],
+ *
+ * with t <= i when causal != 0.  No norm or scale follows (P2 §4).  Both heads
+ * of a pair must sit in one GQA group, so Hq / Hkv must be even (P2 §1).
+ *
+ * Padded batch (cu_seqlens == NULL): sequences of length T,
+ *   q : [B, T, Hq, d] bf16;  k, v : [B, T, Hkv, d] bf16;
+ *   lambda_logit : [B, T, Hq/2] fp32;  out : [B, T, Hq/2, d] bf16.
+ *   nseq and max_seqlen are ignored.
+ * Packed batch (cu_seqlens != NULL): nseq sequences; sequence s owns tokens
+ *   cu_seqlens[s] .. cu_seqlens[s+1]-1 of the packed tensors and attends only
+ *   within itself.  cu_seqlens is a DEVICE int32 array [nseq + 1], non-
+ *   decreasing, starting at 0; max_seqlen must be >= every sequence length
+ *   (rows beyond it are not computed).  Shapes as above with [B, T] replaced
+ *   by [total tokens]; B and T are ignored.
+ *
+ *   scale : softmax scale; <= 0 selects 1/sqrt(d).
+ * Supported: dtype DIFFATTN_BF16, d in {64, 128}.
+ */
+DIFFATTN_API int diffattn_v2_fwd(const void* q, const void* k, const void* v, const float* lambda_logit,
+                    void* out, const int* cu_seqlens, int nseq, int max_seqlen, int B, int T,
+                    int Hq, int Hkv, int d, float scale, int causal, diffattn_dtype dtype,
+                    void* stream);
+
+/*
+ * V2 decode step [P2 §1, §2]: one new query row per sequence against its KV
+ * cache.  The cache already holds the new token's K and V; entry b attends to
+ * positions 0 .. cache_len[b]-1 (all S_max when cache_len == NULL).  An entry
+ * with no cached position gives zeros; lengths are clamped to [0, S_max].
+ *
+ *   q            : [B, Hq, d] bf16
+ *   k_cache      : [B, S_max, Hkv, d] bf16;  v_cache: same
+ *   cache_len    : DEVICE int32 [B] or NULL
+ *   lambda_logit : [B, Hq/2] fp32
+ *   out          : [B, Hq/2, d] bf16
+ *   workspace    : device scratch of at least diffattn_v2_decode_workspace_bytes()
+ *                  bytes for per-slice partial results; caller-owned.
+ *   scale        : <= 0 selects 1/sqrt(d).
+ * Supported: dtype DIFFATTN_BF16, d in {64, 128}, Hq / Hkv even and <= 16.
+ */
+DIFFATTN_API int diffattn_v2_decode(const void* q, const void* k_cache, const void* v_cache,
+                       const int* cache_len, const float* lambda_logit, void* out,
+                       void* workspace, size_t workspace_bytes, int B, int S_max, int Hq,
+                       int Hkv, int d, float scale, diffattn_dtype dtype, void* stream);
+
+/* Workspace bytes diffattn_v2_decode needs (0 for sizes it would reject). */
+DIFFATTN_API size_t diffattn_v2_decode_workspace_bytes(int B, int S_max, int Hq, int Hkv, int d);
+
+/* Initial lambda of 1-based layer `layer` [P1 "λ의 역할과 학습"]:
+ * 0.8 - 0.6 * exp(-0.3 * (layer - 1)) in fp32.  Returns NaN (and sets the last
+ * error) for layer < 1. */
+DIFFATTN_API float diffattn_lambda_init(int layer);
+
+/* Message for the last nonzero code returned on this thread ("" if none). */
+DIFFATTN_API const char* diffattn_last_error(void);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+DIFFATTN_API int diffattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIFFATTN_H_ */
