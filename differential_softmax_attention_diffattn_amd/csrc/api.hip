@@ -185,9 +185,9 @@ size_t diffattn_v2_decode_workspace_bytes(int B, int S_max, int Hq, int Hkv, int
   if (B < 0 || S_max < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || (Hq / Hkv) % 2 || Hq / Hkv > 16)
     return 0;
   if (d != 64 && d != 128) return 0;
-  int split_len, nsplit;
-  diffattn::decode_split(B, S_max, Hkv, &split_len, &nsplit);
-  const long long n = prod({B, Hq, nsplit, d + 2});
+  int split_len, nsplit, nparts;
+  diffattn::decode_split(B, S_max, Hkv, &split_len, &nsplit, &nparts);
+  const long long n = prod({B, Hq, nparts, d + 4});
   return n < 0 ? 0 : (size_t)n * sizeof(float);
 }
 
@@ -241,7 +241,8 @@ int diffattn_v2_decode(const void* q, const void* k_cache, const void* v_cache,
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.d = d;
-  diffattn::decode_split(B, S_max, Hkv, &a.split_len, &a.nsplit);
+  int nparts;
+  diffattn::decode_split(B, S_max, Hkv, &a.split_len, &a.nsplit, &nparts);
   a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
   return from_hip(diffattn::launch_v2_decode(a, static_cast<hipStream_t>(stream)), fn);
 }

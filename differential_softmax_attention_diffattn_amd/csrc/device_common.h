@@ -71,16 +71,22 @@ __device__ __forceinline__ f32x4 mfma_f16(const u32x4& a, const u32x4& b, const 
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// Reductions across the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
+// Reductions across the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48),
+// with the gfx950 row-swap permutes.  permlane32_swap(x, x) returns
+// {x[l mod 32], x[l mod 32 + 32]} in every lane l, and permlane16_swap(x, x)
+// returns {x[l'], x[l' + 16]} with l' = l with bit 4 cleared, so each step
+// combines a lane with its partner one row-pair (or one row) away.
 __device__ __forceinline__ float max_across_rows(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float sum_across_rows(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 __device__ __forceinline__ float sum_within_row16(float x) {
   x += __shfl_xor(x, 1);
@@ -109,6 +115,28 @@ __device__ __forceinline__ u32x4 ldg128(const void* p) {
 }
 __device__ __forceinline__ void stg128(void* p, const u32x4& v) {
   *reinterpret_cast<u32x4*>(p) = v;
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each 16-lane row
+// of the wave, lane j supplies the address of an 8-byte chunk; the 16 chunks
+// form a 4 x 16 matrix of 16-bit values whose row r is the chunks of lanes
+// 4r..4r+3 in order.  Lane c receives column c: {M[0][c], M[1][c], M[2][c], M[3][c]}.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_addr) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<void*>(lds_addr)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Direct global->LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
+// lane l's bytes land at lds_base + 16 * l.  `base` is wave-uniform and `byte_off`
+// a per-lane 32-bit offset, so the load can use a scalar base address.
+__device__ __forceinline__ void dma16(const void* base, uint32_t byte_off, void* lds_base) {
+  const __attribute__((address_space(1))) char* g =
+      (const __attribute__((address_space(1))) char*)(base) + byte_off;
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds_base), 16, 0,
+                                   0);
 }
 
 // Register-allocation hint: the value lives in accumulation registers here.

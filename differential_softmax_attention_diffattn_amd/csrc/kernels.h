@@ -44,14 +44,14 @@ struct DecodeArgs {
   const int* cache_len;     // device [B] or nullptr
   const float* logit;       // fp32 [B, Hq/2]
   uint16_t* out;            // bf16 [B, Hq/2, d]
-  float* partial;           // fp32 workspace [B, Hq, nsplit, d + 2]
+  float* partial;           // fp32 workspace [B, Hq, nparts, d + 4]
   int B, S_max, Hq, Hkv, d;
-  int split_len, nsplit;
+  int split_len, nsplit;    // cache slices of split_len keys; nparts = partials per head
   float scale;
 };
 
 // Decode split rule shared by the workspace query and the launcher.
-void decode_split(int B, int S_max, int Hkv, int* split_len, int* nsplit);
+void decode_split(int B, int S_max, int Hkv, int* split_len, int* nsplit, int* nparts);
 
 hipError_t launch_v1_f32(const V1Args& a, hipStream_t stream);
 // bf16 V1 needs a workspace for V packed as fp16 tiles (see v1_prefill.hip).

@@ -29,10 +29,11 @@
 namespace diffattn {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kRowGroups = 4;                 // 32-row groups per workgroup
+constexpr int kWaves = 2 * kRowGroups;          // one wave per (stream, row group)
 constexpr int kThreads = kWaves * kWave;
 constexpr int kRows = 32;
-constexpr int kQTile = kWaves * kRows;  // 128 query rows per workgroup
+constexpr int kQTile = kRowGroups * kRows;      // 128 query rows per workgroup
 constexpr int kKeys = 64;
 constexpr float kRescaleLog2 = 8.0f;  // P <= 2^8, well inside fp16 range
 
@@ -43,17 +44,30 @@ struct Tile {
   static constexpr int kVtStride = kKeys + 8;         // fp16 elements per Vt row (144 B)
   static constexpr int kVtBytes = DV * kVtStride * 2;
   static constexpr int kStage = 2 * kKBytes + kVtBytes;
-  static constexpr int kKInstrPerWave = kKBytes / 1024 / kWaves;
+  static constexpr int kKInstrPerWave = kKBytes / 1024 / kRowGroups;  // per wave of a stream
   static constexpr int kVKeysPerThread = DV / 32;  // 8 for DV = 256, 4 for DV = 128
   static constexpr int kVInstr = kVtBytes / 1024;   // 1 KiB direct loads per V tile
 };
 
+constexpr int kPackThreads = 256;
+
+// Position of key k (0..63) inside a packed Vt row.  Within each 32-key half,
+// the eight keys one MFMA lane needs (4g..4g+3 and 16+4g..16+4g+3 for lane row
+// group g) are stored next to each other, so the V^T operand is one 16-byte
+// LDS read: half*32 + 8*g + j holds key half*32 + 4g + j (j < 4) or
+// half*32 + 16 + 4g + (j - 4) (j >= 4).
+__device__ __forceinline__ int vt_pos(int k) {
+  const int half = k >> 5, kl = k & 31;
+  const int hi = kl >> 4, g = (kl >> 2) & 3, j = kl & 3;
+  return half * 32 + 8 * g + 4 * hi + j;
+}
+
 // Pre-pass: V [B,T,H,DV] bf16 -> per (b, h, key tile) an fp16 block Vt[DV][kVtStride]
-// (keys 0..63 of the tile, then zero padding; keys past T are zero).
+// (keys of the tile in vt_pos order, then zero padding; keys past T are zero).
 template <int D, int DV>
-__global__ __launch_bounds__(kThreads) void v1_pack_v_kernel(V1Args a, uint16_t* vp) {
+__global__ __launch_bounds__(kPackThreads) void v1_pack_v_kernel(V1Args a, uint16_t* vp) {
   using TL = Tile<D, DV>;
-  constexpr int NKT = TL::kVKeysPerThread;
+  constexpr int NKT = TL::kVKeysPerThread;  // consecutive keys per thread (8 or 4)
   const int n_kt = (a.T + kKeys - 1) / kKeys;
   const int kt = blockIdx.x % n_kt;
   const int bh = blockIdx.x / n_kt;
@@ -72,22 +86,19 @@ __global__ __launch_bounds__(kThreads) void v1_pack_v_kernel(V1Args a, uint16_t*
     for (int j = 0; j < 4; ++j) hv[k][j] = bf16x2_to_f16x2(w[j]);
   }
   uint16_t* vt = vp + (size_t)blockIdx.x * (DV * TL::kVtStride);
+  // runs of 4 consecutive keys stay contiguous under vt_pos
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint16_t* r0 = vt + (dc * 8 + 2 * j) * TL::kVtStride + kg * NKT;
-    uint16_t* r1 = r0 + TL::kVtStride;
-    if constexpr (NKT == 8) {
-      *reinterpret_cast<u32x4*>(r0) =
-          u32x4{pack_lo16(hv[0][j], hv[1][j]), pack_lo16(hv[2][j], hv[3][j]),
-                pack_lo16(hv[4][j], hv[5][j]), pack_lo16(hv[6][j], hv[7][j])};
-      *reinterpret_cast<u32x4*>(r1) =
-          u32x4{pack_hi16(hv[0][j], hv[1][j]), pack_hi16(hv[2][j], hv[3][j]),
-                pack_hi16(hv[4][j], hv[5][j]), pack_hi16(hv[6][j], hv[7][j])};
-    } else {
+  for (int run = 0; run < NKT / 4; ++run) {
+    const int pos = vt_pos(kg * NKT + run * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint16_t* r0 = vt + (dc * 8 + 2 * j) * TL::kVtStride + pos;
+      uint16_t* r1 = r0 + TL::kVtStride;
+      const u32x4* src = hv + run * 4;
       *reinterpret_cast<u32x2*>(r0) =
-          u32x2{pack_lo16(hv[0][j], hv[1][j]), pack_lo16(hv[2][j], hv[3][j])};
+          u32x2{pack_lo16(src[0][j], src[1][j]), pack_lo16(src[2][j], src[3][j])};
       *reinterpret_cast<u32x2*>(r1) =
-          u32x2{pack_hi16(hv[0][j], hv[1][j]), pack_hi16(hv[2][j], hv[3][j])};
+          u32x2{pack_hi16(src[0][j], src[1][j]), pack_hi16(src[2][j], src[3][j])};
     }
   }
   if (kg == 0) {  // zero the padding columns of this thread's 8 rows
@@ -106,12 +117,15 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
   using TL = Tile<D, DV>;
   constexpr int NC = D / 32;
   constexpr int NDB = DV / 16;
-  constexpr int NKT = TL::kVKeysPerThread;
+  constexpr int XSTRIDE = DV + 4;  // fp32 row stride of the epilogue exchange (banks)
+  static_assert(kQTile * XSTRIDE * 4 <= 2 * TL::kStage, "exchange must fit in the stages");
 
   __shared__ __align__(16) uint8_t smem[2 * TL::kStage];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int stream = wave / kRowGroups;  // 0: (Q1, K1), 1: (Q2, K2)
+  const int rg = wave % kRowGroups;
   const int g = lane >> 4;
   const int c16 = lane & 15;
 
@@ -125,264 +139,223 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
   const int T = a.T;
   const size_t tok_base = (size_t)b * T;
 
-  const int q_lo = qt * kQTile + wave * kRows;
+  const int q_lo = qt * kQTile + rg * kRows;
   const bool wave_active = q_lo < T;
   const int q_end_block = min(qt * kQTile + kQTile, T);
   const int n_kt_all = (T + kKeys - 1) / kKeys;
   const int n_kt = CAUSAL ? (q_end_block - 1) / kKeys + 1 : n_kt_all;
   const int wave_key_end = CAUSAL ? min(q_lo + kRows, T) : T;
 
-  const uint16_t* q1 = static_cast<const uint16_t*>(a.q1);
-  const uint16_t* q2 = static_cast<const uint16_t*>(a.q2);
-  const uint16_t* k1 = static_cast<const uint16_t*>(a.k1);
-  const uint16_t* k2 = static_cast<const uint16_t*>(a.k2);
+  const uint16_t* qsrc = static_cast<const uint16_t*>(stream == 0 ? a.q1 : a.q2);
+  const uint16_t* ksrc = static_cast<const uint16_t*>(stream == 0 ? a.k1 : a.k2);
 
-  // Q^T fragments of both streams
-  u32x4 qf[2][2][NC];
+  // Q^T fragments (B operand) of this wave's stream
+  u32x4 qf[2][NC];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int row = q_lo + nb * 16 + c16;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (row < T) {
-        const size_t off = ((tok_base + row) * a.H + h) * D + c * 32 + g * 8;
-        qf[0][nb][c] = ldg128(q1 + off);
-        qf[1][nb][c] = ldg128(q2 + off);
-      } else {
-        qf[0][nb][c] = u32x4{0, 0, 0, 0};
-        qf[1][nb][c] = u32x4{0, 0, 0, 0};
-      }
-    }
+    for (int c = 0; c < NC; ++c)
+      qf[nb][c] = row < T ? ldg128(qsrc + ((tok_base + row) * a.H + h) * D + c * 32 + g * 8)
+                          : u32x4{0, 0, 0, 0};
   }
 
-  auto load_k_tiles = [&](int kt, int stage) {
-    uint8_t* base = smem + stage * TL::kStage;
+  // K tile of this wave's stream: the four waves of a stream share its 1 KiB loads
+  // Each lane's K chunks inside a tile are fixed; only the tile's first key
+  // changes.  Keep the lane part as a 32-bit element offset and move the tile
+  // base in scalar registers; clamp rows past T only on the ragged last tile.
+  const size_t krow_stride = (size_t)a.H * D;  // elements between consecutive tokens
+  uint32_t k_lane_off[TL::kKInstrPerWave];  // bytes
 #pragma unroll
-    for (int sidx = 0; sidx < 2; ++sidx) {
-      const uint16_t* ksrc = sidx == 0 ? k1 : k2;
+  for (int j = 0; j < TL::kKInstrPerWave; ++j) {
+    const int off = (rg * TL::kKInstrPerWave + j) * 1024 + lane * 16;
+    const int row = off / (D * 2);
+    const int chunk = ((off % (D * 2)) >> 4) ^ (row & (TL::kChunks - 1));
+    k_lane_off[j] = (uint32_t)((row * krow_stride + chunk * 8) * 2);
+  }
+  const uint16_t* k_head = ksrc + (tok_base * a.H + h) * D;
+  auto load_k_tile = [&](int kt, int stage) {
+    uint8_t* base = smem + stage * TL::kStage + stream * TL::kKBytes;
+    const uint16_t* tile = k_head + (size_t)kt * kKeys * krow_stride;
+    if ((kt + 1) * kKeys <= T) {
+#pragma unroll
+      for (int j = 0; j < TL::kKInstrPerWave; ++j)
+        dma16(tile, k_lane_off[j], base + (rg * TL::kKInstrPerWave + j) * 1024);
+    } else {  // ragged last tile: clamp rows past T (they are masked)
 #pragma unroll
       for (int j = 0; j < TL::kKInstrPerWave; ++j) {
-        const int blk = wave * TL::kKInstrPerWave + j;
+        const int blk = rg * TL::kKInstrPerWave + j;
         const int off = blk * 1024 + lane * 16;
         const int row = off / (D * 2);
-        const int pos = (off % (D * 2)) >> 4;
-        const int chunk = pos ^ (row & (TL::kChunks - 1));
-        const int key = min(kt * kKeys + row, T - 1);
-        const uint16_t* src = ksrc + ((tok_base + key) * a.H + h) * D + chunk * 8;
-        __builtin_amdgcn_global_load_lds(
-            src,
-            (__attribute__((address_space(3))) void*)(base + sidx * TL::kKBytes + blk * 1024),
-            16, 0, 0);
+        const int chunk = ((off % (D * 2)) >> 4) ^ (row & (TL::kChunks - 1));
+        const size_t e = (size_t)min(kt * kKeys + row, T - 1) * krow_stride + chunk * 8;
+        dma16(k_head, (uint32_t)(e * 2), base + blk * 1024);
       }
     }
   };
-  // V tiles: direct-to-LDS copies of the pre-packed fp16 blocks
+  // V tiles: direct-to-LDS copies of the pre-packed fp16 blocks, spread over all waves
   const uint8_t* vp_bh = reinterpret_cast<const uint8_t*>(vp) + (size_t)bh * n_kt_all * TL::kVtBytes;
   auto load_v_tile = [&](int kt, int stage) {
     uint8_t* base = smem + stage * TL::kStage + 2 * TL::kKBytes;
-    const uint8_t* src = vp_bh + (size_t)kt * TL::kVtBytes + lane * 16;
+    const uint8_t* src = vp_bh + (size_t)kt * TL::kVtBytes;
 #pragma unroll
     for (int j = 0; j < (TL::kVInstr + kWaves - 1) / kWaves; ++j) {
       const int blk = wave + j * kWaves;
-      if (blk < TL::kVInstr)
-        __builtin_amdgcn_global_load_lds(
-            src + blk * 1024, (__attribute__((address_space(3))) void*)(base + blk * 1024), 16, 0,
-            0);
+      if (blk < TL::kVInstr) dma16(src, blk * 1024 + lane * 16, base + blk * 1024);
     }
   };
 
-  load_k_tiles(0, 0);
+  load_k_tile(0, 0);
   load_v_tile(0, 0);
   __builtin_amdgcn_s_waitcnt(0x0f70);
   __syncthreads();
 
-  f32x4 o[2][NDB][2];
+  f32x4 o[NDB][2];
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) o[s][db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref[2][2], l_part[2][2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      m_ref[s][nb] = -INFINITY;
-      l_part[s][nb] = 0.f;
-    }
+    for (int nb = 0; nb < 2; ++nb) o[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
   const float cs = kLog2e / sqrtf((float)D);
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int stage = kt & 1;
     const bool has_next = kt + 1 < n_kt;
     if (has_next) {
-      load_k_tiles(kt + 1, stage ^ 1);
+      load_k_tile(kt + 1, stage ^ 1);
       load_v_tile(kt + 1, stage ^ 1);
     }
     if (wave_active) {
-      const uint8_t* kbase = smem + stage * TL::kStage;
-      const uint16_t* vt = reinterpret_cast<const uint16_t*>(kbase + 2 * TL::kKBytes);
+      const uint8_t* kbase = smem + stage * TL::kStage + stream * TL::kKBytes;
+      const uint16_t* vt =
+          reinterpret_cast<const uint16_t*>(smem + stage * TL::kStage + 2 * TL::kKBytes);
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         const int k0 = kt * kKeys + cc * 32;
         if (k0 < wave_key_end) {
-          f32x4 sacc[2][2][2];  // [stream][key block][column block]
+          // S^T = K Q^T: 2 key blocks x 2 column blocks
+          f32x4 sacc[2][2];
 #pragma unroll
-          for (int s = 0; s < 2; ++s)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int nb = 0; nb < 2; ++nb) sacc[s][kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          // K fragments are fetched one k-chunk ahead of the MFMAs that use them
-          u32x4 kf[2][2], kn[2][2];
-          auto fetch_k = [&](int c, u32x4 (&dst)[2][2]) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-              const int koff = k_swizzled(cc * 32 + kb * 16 + c16, c * 4 + g, TL::kChunks);
-              dst[0][kb] = *reinterpret_cast<const u32x4*>(kbase + koff);
-              dst[1][kb] = *reinterpret_cast<const u32x4*>(kbase + TL::kKBytes + koff);
-            }
-          };
-          fetch_k(0, kn);
+            for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+            for (int kb = 0; kb < 2; ++kb) {
+              const u32x4 kf = *reinterpret_cast<const u32x4*>(
+                  kbase + k_swizzled(cc * 32 + kb * 16 + c16, c * 4 + g, TL::kChunks));
 #pragma unroll
-              for (int kb = 0; kb < 2; ++kb) kf[s][kb] = kn[s][kb];
-            if (c + 1 < NC) fetch_k(c + 1, kn);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int nb = 0; nb < 2; ++nb) {
-                sacc[0][kb][nb] = mfma_bf16(kf[0][kb], qf[0][nb][c], sacc[0][kb][nb]);
-                sacc[1][kb][nb] = mfma_bf16(kf[1][kb], qf[1][nb][c], sacc[1][kb][nb]);
-              }
-            __builtin_amdgcn_sched_barrier(0);
+              for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = mfma_bf16(kf, qf[nb][c], sacc[kb][nb]);
+            }
           }
           const bool need_mask = (k0 + 32 > T) || (CAUSAL && k0 + 31 > q_lo);
           if (need_mask) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-              for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                  for (int i = 0; i < 4; ++i) {
-                    const int key = k0 + kb * 16 + 4 * g + i;
-                    const int row = q_lo + nb * 16 + c16;
-                    if (key >= T || (CAUSAL && key > row)) sacc[s][kb][nb][i] = -INFINITY;
-                  }
-          }
-          float mt[2][2];
-          bool grow = false;
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-              float x = sacc[s][0][nb][0];
-#pragma unroll
-              for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) x = fmaxf(x, sacc[s][kb][nb][i]);
-              mt[s][nb] = max_across_rows(x) * cs;
-              grow |= mt[s][nb] > m_ref[s][nb] + kRescaleLog2;
-            }
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-              for (int nb = 0; nb < 2; ++nb) pin_agpr(o[s][db][nb]);
-          if (wave_any(grow)) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-              for (int nb = 0; nb < 2; ++nb) {
-                const float mn = fmaxf(m_ref[s][nb], mt[s][nb]);
-                const float alpha = (mn == m_ref[s][nb]) ? 1.f : fast_exp2(m_ref[s][nb] - mn);
-                m_ref[s][nb] = mn;
-                l_part[s][nb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                  // one accumulator at a time: read, scale, write back
-                  o[s][db][nb] *= alpha;
-                  pin_agpr(o[s][db][nb]);
-                  __builtin_amdgcn_sched_barrier(0);
-                }
-              }
-          }
-          u32x4 pf[2][2];
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-              const float mb = (m_ref[s][nb] == -INFINITY) ? 0.f : m_ref[s][nb];
-              float pv[8];
-#pragma unroll
-              for (int kb = 0; kb < 2; ++kb)
+              for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                  const float e = fast_exp2(fmaf(sacc[s][kb][nb][i], cs, -mb));
-                  pv[kb * 4 + i] = e;
-                  l_part[s][nb] += e;
+                  const int key = k0 + kb * 16 + 4 * g + i;
+                  const int row = q_lo + nb * 16 + c16;
+                  if (key >= T || (CAUSAL && key > row)) sacc[kb][nb][i] = -INFINITY;
                 }
-              pf[s][nb] = u32x4{pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]),
-                                pack_f16x2(pv[4], pv[5]), pack_f16x2(pv[6], pv[7])};
+          }
+          float mt[2];
+          bool grow = false;
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            float x = sacc[0][nb][0];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) x = fmaxf(x, sacc[kb][nb][i]);
+            mt[nb] = max_across_rows(x) * cs;
+            grow |= mt[nb] > m_ref[nb] + kRescaleLog2;
+          }
+          if (wave_any(grow)) {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+              const float mn = fmaxf(m_ref[nb], mt[nb]);
+              const float alpha = (mn == m_ref[nb]) ? 1.f : fast_exp2(m_ref[nb] - mn);
+              m_ref[nb] = mn;
+              l_part[nb] *= alpha;
+#pragma unroll
+              for (int db = 0; db < NDB; ++db) o[db][nb] *= alpha;
             }
-          // V^T fragments are fetched two blocks ahead of their MFMAs
-          const uint16_t* vbase = vt + c16 * TL::kVtStride + cc * 32 + g * 4;
+          }
+          u32x4 pf[2];
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const float mb = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
+            float pv[8];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float e = fast_exp2(fmaf(sacc[kb][nb][i], cs, -mb));
+                pv[kb * 4 + i] = e;
+                l_part[nb] += e;
+              }
+            pf[nb] = u32x4{pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]),
+                           pack_f16x2(pv[4], pv[5]), pack_f16x2(pv[6], pv[7])};
+          }
+          // O^T += V^T P^T, V^T fragments (one 16-byte read each) fetched one block ahead
+          const uint16_t* vbase = vt + c16 * TL::kVtStride + cc * 32 + g * 8;
           auto fetch_v = [&](int db) {
-            const uint16_t* vr = vbase + db * 16 * TL::kVtStride;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 16);
-            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+            return *reinterpret_cast<const u32x4*>(vbase + db * 16 * TL::kVtStride);
           };
-          u32x4 vq0 = fetch_v(0), vq1 = fetch_v(1);
+          u32x4 vnext = fetch_v(0);
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const u32x4 vf = vq0;
-            vq0 = vq1;
-            if (db + 2 < NDB) vq1 = fetch_v(db + 2);
+            const u32x4 vf = vnext;
+            if (db + 1 < NDB) vnext = fetch_v(db + 1);
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-              for (int nb = 0; nb < 2; ++nb) o[s][db][nb] = mfma_f16(vf, pf[s][nb], o[s][db][nb]);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int nb = 0; nb < 2; ++nb) o[db][nb] = mfma_f16(vf, pf[nb], o[db][nb]);
           }
         }
       }
     }
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) pin_agpr(o[s][db][nb]);
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
   }
 
-  if (!wave_active) return;
-
-  // ---- epilogue: z = O1/l1 - lambda O2/l2, RMS norm over DV, scale, fp32 store ----
+  // ---- epilogue: stream-2 waves publish O2 / l2 through LDS; stream-1 waves combine ----
+  float* xch = reinterpret_cast<float*>(smem);  // [128 rows][XSTRIDE]
+  float inv[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) inv[nb] = 1.0f / sum_across_rows(l_part[nb]);
+  if (stream == 1 && wave_active) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float* dst = xch + (rg * kRows + nb * 16 + c16) * XSTRIDE + g * 4;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        f32x4 t;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] = __fmul_rn(o[db][nb][i], inv[nb]);
+        *reinterpret_cast<f32x4*>(dst + db * 16) = t;
+      }
+    }
+  }
+  __syncthreads();
+  if (stream != 0 || !wave_active) return;
   const float post = 1.0f - a.lambda_init;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const float inv1 = 1.0f / sum_across_rows(l_part[0][nb]);
-    const float inv2 = 1.0f / sum_across_rows(l_part[1][nb]);
+    const float* src = xch + (rg * kRows + nb * 16 + c16) * XSTRIDE + g * 4;
     float ss = 0.f;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(src + db * 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float z = fmaf(-a.lambda, __fmul_rn(o[1][db][nb][i], inv2),
-                             __fmul_rn(o[0][db][nb][i], inv1));
-        o[0][db][nb][i] = z;
+        const float z = fmaf(-a.lambda, t[i], __fmul_rn(o[db][nb][i], inv[nb]));
+        o[db][nb][i] = z;
         ss = fmaf(z, z, ss);
       }
+    }
     ss = sum_across_rows(ss);
     const float r = post / sqrtf(ss * (1.0f / DV) + a.eps);
     const int row = q_lo + nb * 16 + c16;
@@ -394,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float w = a.norm_weight ? a.norm_weight[db * 16 + g * 4 + i] : 1.0f;
-          y[i] = o[0][db][nb][i] * r * w;
+          y[i] = o[db][nb][i] * r * w;
         }
         *reinterpret_cast<f32x4*>(dst + db * 16) = y;
       }
@@ -415,7 +388,7 @@ hipError_t launch_typed(const V1Args& a, void* workspace, hipStream_t stream) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL || pack_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   uint16_t* vp = static_cast<uint16_t*>(workspace);
-  hipLaunchKernelGGL((v1_pack_v_kernel<D, DV>), dim3((unsigned)pack_blocks), dim3(kThreads), 0,
+  hipLaunchKernelGGL((v1_pack_v_kernel<D, DV>), dim3((unsigned)pack_blocks), dim3(kPackThreads), 0,
                      stream, a, vp);
   if (a.causal)
     hipLaunchKernelGGL((v1_prefill_kernel<D, DV, true>), dim3((unsigned)blocks), dim3(kThreads), 0,

@@ -6,14 +6,16 @@
 // each cached K/V row once per KV head ("Differential Transformer V2" summary,
 // 상세 정리 §2: decoding is memory-bound and V2 does not grow the KV cache).
 //
-// Split-K: a workgroup owns (batch entry, KV head, slice of the cache).  Its 4
-// waves walk the slice in 32-key chunks.  All query heads of the KV group
-// (up to 16) ride in one MFMA column block, so every K/V byte is read once:
-// S^T = K Q^T on 16x16x32 bf16 MFMA with K fragments loaded straight from
-// global memory (16-byte loads), then P^T V via a per-wave LDS transpose of V.
-// Each workgroup leaves a partial (O, m, l) per query head; a second kernel
-// merges the partials with log-sum-exp weights and applies the pair
-// subtraction.
+// Split-K.  A workgroup of 8 waves owns (batch entry, cache slice, KVW KV
+// heads); wave w takes KV head w % KVW and the (w / KVW)-th part of the slice,
+// so with 8 KV heads the workgroup streams whole 2 KiB cache rows (all heads
+// of a token) at once.  Each wave walks 32-key chunks: K fragments are loaded
+// straight into registers one chunk ahead, V chunks go global->LDS with
+// direct-to-LDS loads into a per-wave double buffer and are read back as the
+// V^T MFMA operand with the transposing LDS load.  All query heads of the KV
+// group (up to 16) share one MFMA column block, so each K/V byte is read once.
+// Each wave leaves a partial (O, m, l) per query head; a second kernel merges
+// the partials with log-sum-exp weights and applies the pair subtraction.
 #include <math.h>
 
 #include "device_common.h"
@@ -22,79 +24,134 @@
 namespace diffattn {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kChunk = 32;            // keys per wave iteration
-constexpr int kVtStride = kChunk + 8;  // bf16 elements per transposed V row (80 B)
+constexpr int kChunk = 32;  // keys per wave step
 constexpr float kRescaleLog2 = 8.0f;
 
+// Partial record per (batch, query head, part): O[0..D), m at D, l at D+1, padded
+// to a 16-byte multiple so the O stores are aligned.
 template <int D>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
+constexpr int kPartStride = D + 4;
+
+template <int D>
+struct DecTile {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kBytes = kChunk * kRowBytes;  // one V chunk
+  static constexpr int kInstr = kBytes / 1024;       // 1 KiB direct loads per chunk
+};
+
+// V rows: 32-byte chunk c of row r at 32-byte position c ^ (r mod n32).
+template <int D>
+__device__ __forceinline__ int dec_v_offset(int row, int byte_in_row) {
+  constexpr int n32 = D / 16;
+  const int c32 = byte_in_row >> 5;
+  return row * DecTile<D>::kRowBytes + ((c32 ^ (row & (n32 - 1))) << 5) + (byte_in_row & 31);
+}
+
+int kv_heads_per_block(int Hkv) {
+  if (Hkv % 8 == 0) return 8;
+  if (Hkv % 4 == 0) return 4;
+  if (Hkv % 2 == 0) return 2;
+  return 1;
+}
+
+template <int D, int KVW>
+__global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a) {
+  using TL = DecTile<D>;
+  constexpr int SUB = kWaves / KVW;  // waves sharing one KV head
   constexpr int NC = D / 32;
   constexpr int NDB = D / 16;
-  __shared__ __align__(16) uint16_t vts[kWaves][D * kVtStride];
-  __shared__ float mrg_m[kWaves][16];
-  __shared__ float mrg_l[kWaves][16];
+  __shared__ __align__(16) uint8_t vbuf[kWaves][2][TL::kBytes];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int c16 = lane & 15;
 
+  const int n_kvg = a.Hkv / KVW;
   const int split = blockIdx.x % a.nsplit;
-  const int bkv = blockIdx.x / a.nsplit;
-  const int kv = bkv % a.Hkv;
-  const int b = bkv / a.Hkv;
+  const int rest = blockIdx.x / a.nsplit;
+  const int kvg = rest % n_kvg;
+  const int b = rest / n_kvg;
+  const int kv = kvg * KVW + wave % KVW;
+  const int sub = wave / KVW;
   const int grp = a.Hq / a.Hkv;
   int n = a.S_max;
   if (a.cache_len != nullptr) n = min(max(a.cache_len[b], 0), a.S_max);
-  const int t0 = split * a.split_len;
-  const int t1 = min(t0 + a.split_len, n);
+  // this wave's key range: part `sub` of the slice, in whole chunks
+  const int s0 = split * a.split_len;
+  const int s1 = min(s0 + a.split_len, n);
+  const int chunks = s1 > s0 ? (s1 - s0 + kChunk - 1) / kChunk : 0;
+  const int per = (chunks + SUB - 1) / SUB;
+  const int c_begin = min(sub * per, chunks);
+  const int c_end = min(c_begin + per, chunks);
 
   // Q^T fragment: column c16 = query head kv*grp + c16 (zeros beyond the group)
   u32x4 qf[NC];
   const bool col_valid = c16 < grp;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    if (col_valid)
-      qf[c] = ldg128(a.q + ((size_t)b * a.Hq + kv * grp + c16) * D + c * 32 + g * 8);
-    else
-      qf[c] = u32x4{0, 0, 0, 0};
-  }
+  for (int c = 0; c < NC; ++c)
+    qf[c] = col_valid ? ldg128(a.q + ((size_t)b * a.Hq + kv * grp + c16) * D + c * 32 + g * 8)
+                      : u32x4{0, 0, 0, 0};
 
   const size_t row_stride = (size_t)a.Hkv * D;  // elements between consecutive keys
   const uint16_t* kbase = a.k_cache + ((size_t)b * a.S_max * a.Hkv + kv) * D;
   const uint16_t* vbase = a.v_cache + ((size_t)b * a.S_max * a.Hkv + kv) * D;
+
+  auto load_k = [&](int chunk, u32x4 (&kf)[2][NC]) {
+    const int base = s0 + chunk * kChunk;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = base + kb * 16 + c16;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        kf[kb][c] = key < s1 ? ldg128(kbase + (size_t)key * row_stride + c * 32 + g * 8)
+                             : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto load_v = [&](int chunk, int buf) {
+    const int base = s0 + chunk * kChunk;
+    uint8_t* dst = vbuf[wave][buf];
+#pragma unroll
+    for (int j = 0; j < TL::kInstr; ++j) {
+      const int off = j * 1024 + lane * 16;
+      const int r = off / TL::kRowBytes;
+      const int pos = (off % TL::kRowBytes) >> 4;
+      constexpr int n32 = D / 16;
+      const int vc = (((pos >> 1) ^ (r & (n32 - 1))) << 1) | (pos & 1);
+      const int key = min(base + r, s1 - 1);  // rows past the end are masked (P = 0)
+      __builtin_amdgcn_global_load_lds(vbase + (size_t)key * row_stride + vc * 8,
+                                       (__attribute__((address_space(3))) void*)(dst + j * 1024),
+                                       16, 0, 0);
+    }
+  };
 
   f32x4 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_part = 0.f;
   const float cs = a.scale * kLog2e;
-  uint16_t* vt = vts[wave];
+  const int tr_key = 4 * g + (c16 >> 2);
+  const int tr_byte = 8 * (c16 & 3);
 
-  // V staging: lane -> keys 8*(lane/16) .. +7 (for D = 128) of the chunk, d-chunk lane % 16
-  const int vdc = lane % (D / 8);
-  const int vkg = lane / (D / 8);
-  constexpr int VKEYS = kChunk / (kWave / (D / 8));  // keys per lane: 8 (D=128) or 4 (D=64)
-
-  for (int base = t0 + wave * kChunk; base < t1; base += kWaves * kChunk) {
-    // K fragments straight from global memory
-    u32x4 kf[2][NC];
+  u32x4 kf[2][NC], kn[2][NC];
+  if (c_begin < c_end) {
+    load_k(c_begin, kn);
+    load_v(c_begin, 0);
+  }
+  for (int ci = c_begin; ci < c_end; ++ci) {
+    const int buf = (ci - c_begin) & 1;
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this chunk's K registers and V buffer landed
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = base + kb * 16 + c16;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        kf[kb][c] = key < t1 ? ldg128(kbase + (size_t)key * row_stride + c * 32 + g * 8)
-                             : u32x4{0, 0, 0, 0};
+      for (int c = 0; c < NC; ++c) kf[kb][c] = kn[kb][c];
+    if (ci + 1 < c_end) {  // next chunk in flight while this one is computed
+      load_k(ci + 1, kn);
+      load_v(ci + 1, buf ^ 1);
     }
-    u32x4 vs[VKEYS];
-#pragma unroll
-    for (int k = 0; k < VKEYS; ++k) {
-      const int key = base + vkg * VKEYS + k;
-      vs[k] = key < t1 ? ldg128(vbase + (size_t)key * row_stride + vdc * 8) : u32x4{0, 0, 0, 0};
-    }
+    const int base = s0 + ci * kChunk;
 
     f32x4 sacc[2];
 #pragma unroll
@@ -103,12 +160,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) sacc[kb] = mfma_bf16(kf[kb][c], qf[c], sacc[kb]);
     }
-    if (base + kChunk > t1) {
+    if (base + kChunk > s1) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (base + kb * 16 + 4 * g + i >= t1) sacc[kb][i] = -INFINITY;
+          if (base + kb * 16 + 4 * g + i >= s1) sacc[kb][i] = -INFINITY;
     }
     float x = sacc[0][0];
 #pragma unroll
@@ -136,131 +193,125 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       }
     const u32x4 pf = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                            pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
-
-    // transpose the V chunk into this wave's LDS region: vt[d][key]
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint16_t* r0 = vt + (vdc * 8 + 2 * j) * kVtStride + vkg * VKEYS;
-      uint16_t* r1 = r0 + kVtStride;
-      if constexpr (VKEYS == 8) {
-        *reinterpret_cast<u32x4*>(r0) =
-            u32x4{pack_lo16(vs[0][j], vs[1][j]), pack_lo16(vs[2][j], vs[3][j]),
-                  pack_lo16(vs[4][j], vs[5][j]), pack_lo16(vs[6][j], vs[7][j])};
-        *reinterpret_cast<u32x4*>(r1) =
-            u32x4{pack_hi16(vs[0][j], vs[1][j]), pack_hi16(vs[2][j], vs[3][j]),
-                  pack_hi16(vs[4][j], vs[5][j]), pack_hi16(vs[6][j], vs[7][j])};
-      } else {
-        *reinterpret_cast<u32x2*>(r0) =
-            u32x2{pack_lo16(vs[0][j], vs[1][j]), pack_lo16(vs[2][j], vs[3][j])};
-        *reinterpret_cast<u32x2*>(r1) =
-            u32x2{pack_hi16(vs[0][j], vs[1][j]), pack_hi16(vs[2][j], vs[3][j])};
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): LDS writes done (vmcnt/expcnt unconstrained)
+    const uint8_t* vb = vbuf[wave][buf];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const uint16_t* vr = vt + (db * 16 + c16) * kVtStride + g * 4;
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 16);
+      const u32x2 lo = lds_read_tr16(vb + dec_v_offset<D>(tr_key, db * 32 + tr_byte));
+      const u32x2 hi = lds_read_tr16(vb + dec_v_offset<D>(tr_key + 16, db * 32 + tr_byte));
       o[db] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, o[db]);
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next chunk overwrites vt
+    // the next iteration's loads overwrite the other buffer only; this buffer is
+    // rewritten two iterations later, after the reads above have returned
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   }
 
-  // ---- merge the four waves' partial states through LDS ----
+  // ---- this wave's partial (O unnormalised, m in scaled log2 units, l) ----
   const float l_tot = sum_across_rows(l_part);
-  __syncthreads();  // all waves finished with their V regions: reuse them as fp32 O storage
-  float* osh = reinterpret_cast<float*>(&vts[0][0]);  // [wave][col 16][D]
-  if (g == 0) {
-    mrg_m[wave][c16] = m_ref;
-    mrg_l[wave][c16] = l_tot;
-  }
+  if (col_valid) {
+    const int part = split * SUB + sub;
+    const int nparts = a.nsplit * SUB;
+    float* dst = a.partial + (((size_t)b * a.Hq + kv * grp + c16) * nparts + part) * kPartStride<D>;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) osh[(wave * 16 + c16) * D + db * 16 + 4 * g + i] = o[db][i];
-  __syncthreads();
-
-  for (int idx = threadIdx.x; idx < grp * D; idx += kThreads) {
-    const int col = idx / D;
-    const int d = idx - col * D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mrg_m[w][col]);
-    float O = 0.f, Lsum = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = mrg_m[w][col];
-        const float wt = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-        O = fmaf(osh[(w * 16 + col) * D + d], wt, O);
-        Lsum = fmaf(mrg_l[w][col], wt, Lsum);
-      }
-    }
-    float* dst = a.partial + (((size_t)b * a.Hq + kv * grp + col) * a.nsplit + split) * (D + 2);
-    dst[d] = O;
-    if (d == 0) {
-      dst[D] = M;
-      dst[D + 1] = Lsum;
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<f32x4*>(dst + db * 16 + 4 * g) = o[db];
+    if (g == 0) {
+      dst[D] = m_ref;
+      dst[D + 1] = l_tot;
     }
   }
 }
 
-// Merge split partials with log-sum-exp weights, then out_p = O_2p - sigmoid(logit) O_2p+1.
+// Merge the partials of both heads of a pair with log-sum-exp weights, then
+// out_p = O_2p - sigmoid(logit_p) * O_2p+1.
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, int nparts) {
+  __shared__ float wts[2][512];
+  __shared__ float inv_l[2];
   const int hp = a.Hq / 2;
   const int p = blockIdx.x % hp;
   const int b = blockIdx.x / hp;
-  const int d = threadIdx.x;
+  const int t = threadIdx.x;
+  const float* src[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    src[e] = a.partial + (((size_t)b * a.Hq + 2 * p + e) * nparts) * kPartStride<D>;
+  // weights 2^(m_s - M) / L per part, computed once per head by one wave each
+  if (t < 2 * kWave) {
+    const int e = t / kWave, ln = t % kWave;
+    float M = -INFINITY;
+    for (int s = ln; s < nparts; s += kWave) M = fmaxf(M, src[e][s * kPartStride<D> + D]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float L = 0.f;
+    for (int s = ln; s < nparts; s += kWave) {
+      const float ms = src[e][s * kPartStride<D> + D];
+      const float w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
+      wts[e][s] = w;
+      L = fmaf(src[e][s * kPartStride<D> + D + 1], w, L);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
+    if (ln == 0) inv_l[e] = L > 0.f ? 1.0f / L : 0.f;
+  }
+  __syncthreads();
+  if (t >= D) return;
   float res[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const float* src = a.partial + (((size_t)b * a.Hq + 2 * p + e) * a.nsplit) * (D + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, src[s * (D + 2) + D]);
-    float O = 0.f, L = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < a.nsplit; ++s) {
-        const float ms = src[s * (D + 2) + D];
-        const float wt = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
-        O = fmaf(src[s * (D + 2) + d], wt, O);
-        L = fmaf(src[s * (D + 2) + D + 1], wt, L);
-      }
-    }
-    res[e] = (L > 0.f) ? __fdiv_rn(O, L) : 0.f;
+    float O = 0.f;
+    for (int s = 0; s < nparts; ++s) O = fmaf(src[e][s * kPartStride<D> + t], wts[e][s], O);
+    res[e] = __fmul_rn(O, inv_l[e]);
   }
   const float sg = sigmoid_f32(a.logit[(size_t)b * hp + p]);
-  a.out[((size_t)b * hp + p) * D + d] = f32_to_bf16(fmaf(-sg, res[1], res[0]));
+  a.out[((size_t)b * hp + p) * D + t] = f32_to_bf16(fmaf(-sg, res[1], res[0]));
+}
+
+template <int D, int KVW>
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  const long long blocks = (long long)a.B * (a.Hkv / KVW) * a.nsplit;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((decode_split_kernel<D, KVW>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                     stream, a);
+  const int nparts = a.nsplit * (kWaves / KVW);
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.B * (a.Hq / 2))), dim3(256), 0,
+                     stream, a, nparts);
+  return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-  const long long blocks = (long long)a.B * a.Hkv * a.nsplit;
-  if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.B * (a.Hq / 2))), dim3(D), 0,
-                     stream, a);
-  return hipGetLastError();
+hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
+  switch (kv_heads_per_block(a.Hkv)) {
+    case 8: return launch_typed<D, 8>(a, stream);
+    case 4: return launch_typed<D, 4>(a, stream);
+    case 2: return launch_typed<D, 2>(a, stream);
+    default: return launch_typed<D, 1>(a, stream);
+  }
 }
 
 }  // namespace
 
-void decode_split(int B, int S_max, int Hkv, int* split_len, int* nsplit) {
-  // aim for >= 1024 workgroups (4 per CU on 256 CUs), slices of 256..2048 keys
+// Slices of 256..2048 keys, aiming for >= 2048 workgroups; the partial count per
+// (batch, query head) is nsplit * (8 / KV heads per workgroup) and stays <= 512.
+void decode_split(int B, int S_max, int Hkv, int* split_len, int* nsplit, int* nparts) {
+  const int kvw = kv_heads_per_block(Hkv);
+  const long long units = (long long)B * (Hkv / kvw);
   int len = 2048;
-  const long long units = (long long)B * Hkv;
-  while (len > 256 && units * ((S_max + len - 1) / len) < 1024) len /= 2;
+  while (len > 256 && units * ((S_max + len - 1) / len) < 2048) len /= 2;
+  int ns = S_max > 0 ? (S_max + len - 1) / len : 1;
+  const int sub = kWaves / kvw;
+  while (ns * sub > 512) {  // bound the partial count (combine kernel weight table)
+    len *= 2;
+    ns = (S_max + len - 1) / len;
+  }
   *split_len = len;
-  *nsplit = S_max > 0 ? (S_max + len - 1) / len : 1;
+  *nsplit = ns;
+  *nparts = ns * sub;
 }
 
 hipError_t launch_v2_decode(const DecodeArgs& a, hipStream_t stream) {
-  if (a.d == 128) return launch_typed<128>(a, stream);
-  if (a.d == 64) return launch_typed<64>(a, stream);
+  if (a.d == 128) return launch_d<128>(a, stream);
+  if (a.d == 64) return launch_d<64>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -8,20 +8,22 @@
 // 상세 정리 §1 and §4: one attention over 2h query heads, even/odd split,
 // sigmoid-weighted subtraction, no norm afterwards, h*d output columns.
 //
-// Work decomposition: a workgroup of 4 waves owns a tile of query rows and PW
-// consecutive head pairs of one KV head.  Each wave owns one pair and 32 rows,
-// i.e. four 16-column blocks (even/odd head x two row halves).  Every K/V tile
-// staged in LDS therefore serves all 2*PW query heads of the workgroup.
+// Work decomposition: a workgroup of 8 waves (two per SIMD) owns a tile of
+// query rows and PW consecutive head pairs of one KV head.  Each wave owns one
+// pair and 16 rows, i.e. two 16-column MFMA blocks (even head, odd head) that
+// share every K and V fragment it reads.  Every K/V tile staged in LDS serves
+// all 2*PW query heads of the workgroup.
 //
-// Per 64-key tile a wave computes S^T = K Q^T on 16x16x32 bf16 MFMA (keys on
-// the M side, query columns on N), so each lane ends up holding one query
-// column; the softmax row statistics are then per lane, P^T feeds the second
-// MFMA directly as its B operand, and O^T = V^T P^T accumulates with the head
-// dim on M.  V is written to LDS transposed (Vt[d][key]) by the loader so the
-// A operand reads are two 8-byte LDS loads.  K tiles go global->LDS with
-// direct-to-LDS loads into an XOR-swizzled layout.  Rescaling of O is lazy:
-// the reference maximum only moves when a column's maximum grows by more than
-// 2^8, which keeps P <= 256 (exact in the final O / l quotient).
+// Per 32-key step a wave computes S^T = K Q^T on 16x16x32 bf16 MFMA (keys on
+// the M side, query columns on N), so each lane holds one query column: the
+// softmax statistics are per lane, P^T feeds the second MFMA directly as its B
+// operand, and O^T = V^T P^T accumulates with the head dim on M.  K and V
+// tiles arrive by direct-to-LDS loads, both row-major with XOR-swizzled
+// chunks; the V^T operand is read with the transposing LDS load.  Both heads of
+// a pair sit in the same lane (same row, same d), so the sigmoid-weighted
+// subtraction happens in registers and only h*d bf16 columns are written.
+// Rescaling of O is lazy: the reference maximum only moves when a column's
+// maximum grows by more than 2^8, which keeps P <= 256 (exact in O / l).
 #include <math.h>
 
 #include "device_common.h"
@@ -30,62 +32,82 @@
 namespace diffattn {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kRows = 32;   // query rows per wave
-constexpr int kKeys = 64;   // keys per KV tile
+constexpr int kRows = 16;   // query rows per wave
+constexpr int kKeys = 64;   // keys per staged KV tile
 constexpr float kRescaleLog2 = 8.0f;
 
 template <int D>
 struct Tile {
-  static constexpr int kChunks = D / 8;               // 16-byte chunks per K row
-  static constexpr int kKBytes = kKeys * D * 2;       // K tile bytes
-  static constexpr int kVtStride = kKeys + 4;         // Vt row length in elements (padded)
-  static constexpr int kVtBytes = D * kVtStride * 2;  // Vt tile bytes
-  static constexpr int kStage = kKBytes + kVtBytes;
-  static constexpr int kKInstr = kKBytes / 1024;      // 1 KiB direct loads per K tile
-  static constexpr int kKInstrPerWave = kKInstr / kWaves;
-  static constexpr int kVKeysPerThread = D / 32;      // V keys staged per thread
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;             // 16-byte chunks per row
+  static constexpr int kTileBytes = kKeys * kRowBytes;
+  static constexpr int kStage = 2 * kTileBytes;     // K then V
+  static constexpr int kInstr = kTileBytes / 1024;  // 1 KiB direct loads per tile
 };
 
-__device__ __forceinline__ int k_swizzled(int row, int chunk, int nchunks) {
-  return row * nchunks * 16 + ((chunk ^ (row & (nchunks - 1))) << 4);
+// K rows: 16-byte chunk c of row r sits at chunk position c ^ (r mod nchunks).
+template <int D>
+__device__ __forceinline__ int k_offset(int row, int chunk) {
+  return row * Tile<D>::kRowBytes + ((chunk ^ (row & (Tile<D>::kChunks - 1))) << 4);
+}
+// V rows: 32-byte chunk c of row r sits at 32-byte position c ^ (r mod n32), so
+// the 16 rows one transposing read touches spread over the LDS banks.
+template <int D>
+__device__ __forceinline__ int v_offset(int row, int byte_in_row) {
+  constexpr int n32 = D / 16;
+  const int c32 = byte_in_row >> 5;
+  return row * Tile<D>::kRowBytes + ((c32 ^ (row & (n32 - 1))) << 5) + (byte_in_row & 31);
 }
 
 template <int D, int PW, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   using TL = Tile<D>;
-  constexpr int QSUB = kWaves / PW;
+  constexpr int QSUB = kWaves / PW;  // 16-row groups per workgroup
   constexpr int QTILE = kRows * QSUB;
   constexpr int NC = D / 32;   // k-chunks of Q K^T
   constexpr int NDB = D / 16;  // 16-row blocks of O^T
-  constexpr int NKT = TL::kVKeysPerThread;
+  static_assert(TL::kInstr % kWaves == 0, "tile loads must split evenly over the waves");
 
   __shared__ __align__(16) uint8_t smem[2 * TL::kStage];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int c16 = lane & 15;
 
-  // ---- block -> (query tile, sequence, pair group); longest tiles first ----
+  // ---- block -> (sequence, query tile, pair group) ----
+  // Sequence-major: the query tiles of a sequence are numbered consecutively,
+  // longest (last) tile first, and the pair groups of a tile are adjacent.  With
+  // one pair group per KV head and 8 of them, blocks of one KV head land on one
+  // XCD and that XCD's CUs work through the tiles of one sequence together,
+  // sharing its K/V tiles in L2.  Blocks past the last tile exit.
   const int n_hg = a.Hq / (2 * PW);
-  const int per_qt = a.nseq * n_hg;
-  const int jr = blockIdx.x / per_qt;
-  const int rem = blockIdx.x - jr * per_qt;
-  const int seq = rem / n_hg;
-  const int hg = rem - seq * n_hg;
-  const int n_qt_max = (a.max_seqlen + QTILE - 1) / QTILE;
-  const int qt = n_qt_max - 1 - jr;
-  int tok0, L;
+  const int hg = blockIdx.x % n_hg;
+  int t = blockIdx.x / n_hg;
+  int tok0, L, qt;
   if (a.cu_seqlens != nullptr) {
+    int seq = 0;
+    for (; seq < a.nseq; ++seq) {
+      const int len = a.cu_seqlens[seq + 1] - a.cu_seqlens[seq];
+      const int nt = (len + QTILE - 1) / QTILE;
+      if (t < nt) {
+        qt = nt - 1 - t;
+        break;
+      }
+      t -= nt;
+    }
+    if (seq == a.nseq) return;  // uniform over the block
     tok0 = a.cu_seqlens[seq];
     L = a.cu_seqlens[seq + 1] - tok0;
   } else {
+    const int nt = (a.T + QTILE - 1) / QTILE;
+    const int seq = t / nt;
+    qt = nt - 1 - (t - seq * nt);
     tok0 = seq * a.T;
     L = a.T;
   }
-  if (qt < 0 || qt * QTILE >= L) return;  // uniform over the block
 
   const int hpairs = a.Hq / 2;
   const int group = a.Hq / a.Hkv;
@@ -96,144 +118,129 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
 
   const int q_end_block = min(qt * QTILE + QTILE, L);
   const int n_kt = CAUSAL ? (q_end_block - 1) / kKeys + 1 : (L + kKeys - 1) / kKeys;
-  const int wave_n_kt =
-      !wave_active ? 0 : (CAUSAL ? (min(q_lo + kRows, L) - 1) / kKeys + 1 : n_kt);
+  const int wave_key_end = CAUSAL ? min(q_lo + kRows, L) : L;
 
-  // ---- Q^T fragments (B operand), resident for the whole key loop ----
-  u32x4 qf[4][NC];
+  // ---- Q^T fragments (B operand): block 0 = even head, block 1 = odd head ----
+  const int row = q_lo + c16;
+  u32x4 qf[2][NC];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int head = 2 * p + (nb >> 1);
-    const int row = q_lo + (nb & 1) * 16 + c16;
+  for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if (row < L)
-        qf[nb][c] = ldg128(a.q + ((size_t)(tok0 + row) * a.Hq + head) * D + c * 32 + g * 8);
-      else
-        qf[nb][c] = u32x4{0, 0, 0, 0};
-    }
+    for (int c = 0; c < NC; ++c)
+      qf[nb][c] = row < L ? ldg128(a.q + ((size_t)(tok0 + row) * a.Hq + 2 * p + nb) * D +
+                                   c * 32 + g * 8)
+                          : u32x4{0, 0, 0, 0};
+
+  // ---- direct-to-LDS tile loads (K and V rows, swizzled) ----
+  // Each lane's chunks inside a tile are fixed; keep them as 32-bit element
+  // offsets from the tile's first key and move the tile base in scalar
+  // registers.  Rows past the sequence end are clamped on the ragged last tile.
+  const size_t kv_stride = (size_t)a.Hkv * D;  // elements between consecutive tokens
+  const uint16_t* kbase_g = a.k + ((size_t)tok0 * a.Hkv + kv) * D;
+  const uint16_t* vbase_g = a.v + ((size_t)tok0 * a.Hkv + kv) * D;
+  constexpr int NJ = TL::kInstr / kWaves;
+  uint32_t k_lane_off[NJ], v_lane_off[NJ];  // bytes
+  auto lane_chunks = [&](int j, int& r, int& kc, int& vc) {
+    const int off = (wave + j * kWaves) * 1024 + lane * 16;  // LDS byte offset this lane fills
+    r = off / TL::kRowBytes;
+    const int pos = (off % TL::kRowBytes) >> 4;
+    kc = pos ^ (r & (TL::kChunks - 1));  // K: position pos holds chunk pos ^ (r mod nchunks)
+    constexpr int n32 = D / 16;          // V: 32-byte position pos/2 holds (pos/2) ^ (r mod n32)
+    vc = (((pos >> 1) ^ (r & (n32 - 1))) << 1) | (pos & 1);
+  };
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    int r, kc, vc;
+    lane_chunks(j, r, kc, vc);
+    k_lane_off[j] = (uint32_t)((r * kv_stride + kc * 8) * 2);
+    v_lane_off[j] = (uint32_t)((r * kv_stride + vc * 8) * 2);
   }
-
-  // ---- loaders ----
-  auto load_k_tile = [&](int kt, int stage) {
+  auto load_tiles = [&](int kt, int stage) {
     uint8_t* base = smem + stage * TL::kStage;
+    const size_t tile = (size_t)kt * kKeys * kv_stride;
+    if ((kt + 1) * kKeys <= L) {
 #pragma unroll
-    for (int j = 0; j < TL::kKInstrPerWave; ++j) {
-      const int blk = wave * TL::kKInstrPerWave + j;
-      const int off = blk * 1024 + lane * 16;
-      const int row = off / (D * 2);
-      const int pos = (off % (D * 2)) >> 4;
-      const int chunk = pos ^ (row & (TL::kChunks - 1));
-      const int key = min(kt * kKeys + row, L - 1);
-      const uint16_t* src = a.k + ((size_t)(tok0 + key) * a.Hkv + kv) * D + chunk * 8;
-      __builtin_amdgcn_global_load_lds(
-          src, (__attribute__((address_space(3))) void*)(base + blk * 1024), 16, 0, 0);
-    }
-  };
-  const int vdc = threadIdx.x % (D / 8);
-  const int vkg = threadIdx.x / (D / 8);
-  u32x4 vst[NKT];
-  auto load_v_tile = [&](int kt) {
+      for (int j = 0; j < NJ; ++j) {
+        const int blk = wave + j * kWaves;
+        dma16(kbase_g + tile, k_lane_off[j], base + blk * 1024);
+        dma16(vbase_g + tile, v_lane_off[j], base + TL::kTileBytes + blk * 1024);
+      }
+    } else {  // ragged last tile: clamp rows past the sequence end (they are masked)
 #pragma unroll
-    for (int k = 0; k < NKT; ++k) {
-      const int key = kt * kKeys + vkg * NKT + k;
-      if (key < L)
-        vst[k] = ldg128(a.v + ((size_t)(tok0 + key) * a.Hkv + kv) * D + vdc * 8);
-      else
-        vst[k] = u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_v_tile = [&](int stage) {
-    uint16_t* vt = reinterpret_cast<uint16_t*>(smem + stage * TL::kStage + TL::kKBytes);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint16_t* r0 = vt + (vdc * 8 + 2 * j) * TL::kVtStride + vkg * NKT;
-      uint16_t* r1 = r0 + TL::kVtStride;
-      if constexpr (NKT == 4) {
-        *reinterpret_cast<u32x2*>(r0) =
-            u32x2{pack_lo16(vst[0][j], vst[1][j]), pack_lo16(vst[2][j], vst[3][j])};
-        *reinterpret_cast<u32x2*>(r1) =
-            u32x2{pack_hi16(vst[0][j], vst[1][j]), pack_hi16(vst[2][j], vst[3][j])};
-      } else {
-        *reinterpret_cast<uint32_t*>(r0) = pack_lo16(vst[0][j], vst[1][j]);
-        *reinterpret_cast<uint32_t*>(r1) = pack_hi16(vst[0][j], vst[1][j]);
+      for (int j = 0; j < NJ; ++j) {
+        const int blk = wave + j * kWaves;
+        int r, kc, vc;
+        lane_chunks(j, r, kc, vc);
+        const size_t key = (size_t)min(kt * kKeys + r, L - 1);
+        dma16(kbase_g, (uint32_t)((key * kv_stride + kc * 8) * 2), base + blk * 1024);
+        dma16(vbase_g, (uint32_t)((key * kv_stride + vc * 8) * 2), base + TL::kTileBytes + blk * 1024);
       }
     }
   };
 
-  // ---- prologue: tile 0 ----
-  load_k_tile(0, 0);
-  load_v_tile(0);
-  store_v_tile(0);
+  load_tiles(0, 0);
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): direct-to-LDS loads landed
   __syncthreads();
 
-  f32x4 o[NDB][4];
+  f32x4 o[NDB][2];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) o[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref[4], l_part[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    m_ref[nb] = -INFINITY;
-    l_part[nb] = 0.f;
-  }
+    for (int nb = 0; nb < 2; ++nb) o[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
   const float cs = a.scale * kLog2e;
+
+  // transposing-read address pieces: lane j of a row supplies key 4g + j/4, d 4(j%4)
+  const int tr_key = 4 * g + (c16 >> 2);
+  const int tr_byte = 8 * (c16 & 3);
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int stage = kt & 1;
-    const bool has_next = kt + 1 < n_kt;
-    if (has_next) {
-      load_k_tile(kt + 1, stage ^ 1);
-      load_v_tile(kt + 1);
-    }
-    if (kt < wave_n_kt) {
-      const uint8_t* kbase = smem + stage * TL::kStage;
-      const uint16_t* vt = reinterpret_cast<const uint16_t*>(kbase + TL::kKBytes);
-      const int wave_key_end = CAUSAL ? min(q_lo + kRows, L) : L;
-      // two 32-key halves per staged tile keep the score registers small
+    if (kt + 1 < n_kt) load_tiles(kt + 1, stage ^ 1);
+    if (wave_active) {
+      const uint8_t* k_lds = smem + stage * TL::kStage;
+      const uint8_t* v_lds = k_lds + TL::kTileBytes;
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         const int k0 = kt * kKeys + cc * 32;
         if (k0 < wave_key_end) {
-          // S^T = K Q^T: 2 key blocks x 4 column blocks
-          f32x4 sacc[2][4];
+          // S^T = K Q^T: 2 key blocks x 2 column blocks
+          f32x4 sacc[2][2];
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) sacc[kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
               const u32x4 kf = *reinterpret_cast<const u32x4*>(
-                  kbase + k_swizzled(cc * 32 + kb * 16 + c16, c * 4 + g, TL::kChunks));
+                  k_lds + k_offset<D>(cc * 32 + kb * 16 + c16, c * 4 + g));
 #pragma unroll
-              for (int nb = 0; nb < 4; ++nb) sacc[kb][nb] = mfma_bf16(kf, qf[nb][c], sacc[kb][nb]);
+              for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = mfma_bf16(kf, qf[nb][c], sacc[kb][nb]);
             }
           }
 
-          // causal / ragged mask
+          // causal / ragged mask (same rows for both heads of the pair)
           const bool need_mask = (k0 + 32 > L) || (CAUSAL && k0 + 31 > q_lo);
           if (need_mask) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-              for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const int key = k0 + kb * 16 + 4 * g + i;
-                  const int row = q_lo + (nb & 1) * 16 + c16;
-                  if (key >= L || (CAUSAL && key > row)) sacc[kb][nb][i] = -INFINITY;
+              for (int i = 0; i < 4; ++i) {
+                const int key = k0 + kb * 16 + 4 * g + i;
+                if (key >= L || (CAUSAL && key > row)) {
+                  sacc[kb][0][i] = -INFINITY;
+                  sacc[kb][1][i] = -INFINITY;
                 }
+              }
           }
 
           // online softmax, one query column per lane and column block
-          float mt[4];
+          float mt[2];
           bool grow = false;
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) {
+          for (int nb = 0; nb < 2; ++nb) {
             float x = sacc[0][nb][0];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -242,29 +249,20 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
             mt[nb] = max_across_rows(x) * cs;
             grow |= mt[nb] > m_ref[nb] + kRescaleLog2;
           }
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) pin_agpr(o[db][nb]);
           if (wave_any(grow)) {
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
+            for (int nb = 0; nb < 2; ++nb) {
               const float mn = fmaxf(m_ref[nb], mt[nb]);
               const float alpha = (mn == m_ref[nb]) ? 1.f : fast_exp2(m_ref[nb] - mn);
               m_ref[nb] = mn;
               l_part[nb] *= alpha;
 #pragma unroll
-              for (int db = 0; db < NDB; ++db) {
-                // one accumulator at a time: read, scale, write back
-                o[db][nb] *= alpha;
-                pin_agpr(o[db][nb]);
-                __builtin_amdgcn_sched_barrier(0);
-              }
+              for (int db = 0; db < NDB; ++db) o[db][nb] *= alpha;
             }
           }
-          u32x4 pf[4];
+          u32x4 pf[2];
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) {
+          for (int nb = 0; nb < 2; ++nb) {
             const float mb = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
             float pv[8];
 #pragma unroll
@@ -279,25 +277,19 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
                            pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
           }
 
-          // O^T += V^T P^T
+          // O^T += V^T P^T; V^T fragments by transposing reads of the row-major V tile
+          const int r0 = cc * 32 + tr_key;  // key row for slots 0..3; +16 for slots 4..7
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const uint16_t* vr = vt + (db * 16 + c16) * TL::kVtStride + cc * 32 + g * 4;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 16);
+            const u32x2 lo = lds_read_tr16(v_lds + v_offset<D>(r0, db * 32 + tr_byte));
+            const u32x2 hi = lds_read_tr16(v_lds + v_offset<D>(r0 + 16, db * 32 + tr_byte));
             const u32x4 vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) o[db][nb] = mfma_bf16(vf, pf[nb], o[db][nb]);
+            for (int nb = 0; nb < 2; ++nb) o[db][nb] = mfma_bf16(vf, pf[nb], o[db][nb]);
           }
         }
       }
     }
-    // keep the accumulators in AGPRs across the loop back-edge
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) pin_agpr(o[db][nb]);
-    if (has_next) store_v_tile(stage ^ 1);
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
   }
@@ -305,28 +297,23 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   if (!wave_active) return;
 
   // ---- epilogue: normalise, pair subtraction, bf16 store ----
-  float inv[4];
+  const float inv_e = 1.0f / sum_across_rows(l_part[0]);
+  const float inv_o = 1.0f / sum_across_rows(l_part[1]);
+  if (row < L) {
+    const size_t tok = (size_t)(tok0 + row);
+    const float sg = sigmoid_f32(a.logit[tok * hpairs + p]);
+    uint16_t* dst = a.out + (tok * hpairs + p) * D + g * 4;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) inv[nb] = 1.0f / sum_across_rows(l_part[nb]);
+    for (int db = 0; db < NDB; ++db) {
+      float r[4];
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const int row = q_lo + hf * 16 + c16;
-    if (row < L) {
-      const size_t tok = (size_t)(tok0 + row);
-      const float sg = sigmoid_f32(a.logit[tok * hpairs + p]);
-      uint16_t* dst = a.out + (tok * hpairs + p) * D + g * 4;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        float r[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float ev = __fmul_rn(o[db][hf][i], inv[hf]);
-          const float od = __fmul_rn(o[db][hf + 2][i], inv[hf + 2]);
-          r[i] = fmaf(-sg, od, ev);
-        }
-        *reinterpret_cast<u32x2*>(dst + db * 16) =
-            u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+      for (int i = 0; i < 4; ++i) {
+        const float ev = __fmul_rn(o[db][0][i], inv_e);
+        const float od = __fmul_rn(o[db][1][i], inv_o);
+        r[i] = fmaf(-sg, od, ev);
       }
+      *reinterpret_cast<u32x2*>(dst + db * 16) =
+          u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
     }
   }
 }
@@ -334,6 +321,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
 template <int D, int PW>
 hipError_t launch_typed(const V2Args& a, hipStream_t stream) {
   constexpr int QTILE = kRows * (kWaves / PW);
+  // an upper bound on the query tiles of all sequences (exact for padded batches)
   const int n_qt_max = (a.max_seqlen + QTILE - 1) / QTILE;
   const long long blocks = (long long)n_qt_max * a.nseq * (a.Hq / (2 * PW));
   if (blocks <= 0) return hipSuccess;
