@@ -41,33 +41,28 @@ template <int D, int DV>
 struct Tile {
   static constexpr int kChunks = D / 8;
   static constexpr int kKBytes = kKeys * D * 2;       // one of K1 / K2
-  static constexpr int kVtStride = kKeys + 8;         // fp16 elements per Vt row (144 B)
-  static constexpr int kVtBytes = DV * kVtStride * 2;
+  static constexpr int kVtRowBytes = kKeys * 2;       // one fp16 Vt row: 64 keys, 128 B
+  static constexpr int kVtBytes = DV * kVtRowBytes;
   static constexpr int kStage = 2 * kKBytes + kVtBytes;
   static constexpr int kKInstrPerWave = kKBytes / 1024 / kRowGroups;  // per wave of a stream
-  static constexpr int kVKeysPerThread = DV / 32;  // 8 for DV = 256, 4 for DV = 128
   static constexpr int kVInstr = kVtBytes / 1024;   // 1 KiB direct loads per V tile
 };
 
-constexpr int kPackThreads = 256;
-
-// Position of key k (0..63) inside a packed Vt row.  Within each 32-key half,
-// the eight keys one MFMA lane needs (4g..4g+3 and 16+4g..16+4g+3 for lane row
-// group g) are stored next to each other, so the V^T operand is one 16-byte
-// LDS read: half*32 + 8*g + j holds key half*32 + 4g + j (j < 4) or
-// half*32 + 16 + 4g + (j - 4) (j >= 4).
-__device__ __forceinline__ int vt_pos(int k) {
-  const int half = k >> 5, kl = k & 31;
-  const int hi = kl >> 4, g = (kl >> 2) & 3, j = kl & 3;
-  return half * 32 + 8 * g + 4 * hi + j;
+// Packed V tile layout (one per batch, head and 64-key tile): Vt[d][64 keys] in
+// fp16, 128 bytes per row, split into eight 16-byte chunks.  Logical chunk c
+// (0..7) holds the eight keys one MFMA lane needs for one 32-key half: with
+// half = c / 4 and g = c % 4, keys half*32 + 4g + j then half*32 + 16 + 4g + j
+// for j = 0..3, so the V^T operand is a single 16-byte LDS read.  Chunk c of
+// row d is stored at position c ^ ((d / 2) mod 8), which spreads the 16 rows
+// one read instruction touches over all LDS banks.
+__device__ __forceinline__ int vt_chunk_offset(int d, int c) {
+  return d * 128 + ((c ^ ((d >> 1) & 7)) << 4);
 }
 
-// Pre-pass: V [B,T,H,DV] bf16 -> per (b, h, key tile) an fp16 block Vt[DV][kVtStride]
-// (keys of the tile in vt_pos order, then zero padding; keys past T are zero).
+// Pre-pass: V [B,T,H,DV] bf16 -> the packed fp16 tiles above (keys past T are zero).
+// Thread (dc, c): the 8 rows d = 8 dc .. 8 dc + 7 and logical chunk c.
 template <int D, int DV>
-__global__ __launch_bounds__(kPackThreads) void v1_pack_v_kernel(V1Args a, uint16_t* vp) {
-  using TL = Tile<D, DV>;
-  constexpr int NKT = TL::kVKeysPerThread;  // consecutive keys per thread (8 or 4)
+__global__ __launch_bounds__(DV) void v1_pack_v_kernel(V1Args a, uint16_t* vp) {
   const int n_kt = (a.T + kKeys - 1) / kKeys;
   const int kt = blockIdx.x % n_kt;
   const int bh = blockIdx.x / n_kt;
@@ -75,36 +70,27 @@ __global__ __launch_bounds__(kPackThreads) void v1_pack_v_kernel(V1Args a, uint1
   const int h = bh - b * a.H;
   const uint16_t* vsrc = static_cast<const uint16_t*>(a.v);
   const int dc = threadIdx.x % (DV / 8);
-  const int kg = threadIdx.x / (DV / 8);
-  u32x4 hv[NKT];
+  const int c = threadIdx.x / (DV / 8);
+  const int key0 = kt * kKeys + (c >> 2) * 32 + 4 * (c & 3);
+  u32x4 hv[8];
 #pragma unroll
-  for (int k = 0; k < NKT; ++k) {
-    const int key = kt * kKeys + kg * NKT + k;
+  for (int k = 0; k < 8; ++k) {
+    const int key = key0 + (k & 3) + (k >> 2) * 16;
     u32x4 w = u32x4{0, 0, 0, 0};
     if (key < a.T) w = ldg128(vsrc + (((size_t)b * a.T + key) * a.H + h) * DV + dc * 8);
 #pragma unroll
     for (int j = 0; j < 4; ++j) hv[k][j] = bf16x2_to_f16x2(w[j]);
   }
-  uint16_t* vt = vp + (size_t)blockIdx.x * (DV * TL::kVtStride);
-  // runs of 4 consecutive keys stay contiguous under vt_pos
+  uint8_t* vt = reinterpret_cast<uint8_t*>(vp) + (size_t)blockIdx.x * (DV * 128);
 #pragma unroll
-  for (int run = 0; run < NKT / 4; ++run) {
-    const int pos = vt_pos(kg * NKT + run * 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint16_t* r0 = vt + (dc * 8 + 2 * j) * TL::kVtStride + pos;
-      uint16_t* r1 = r0 + TL::kVtStride;
-      const u32x4* src = hv + run * 4;
-      *reinterpret_cast<u32x2*>(r0) =
-          u32x2{pack_lo16(src[0][j], src[1][j]), pack_lo16(src[2][j], src[3][j])};
-      *reinterpret_cast<u32x2*>(r1) =
-          u32x2{pack_hi16(src[0][j], src[1][j]), pack_hi16(src[2][j], src[3][j])};
-    }
-  }
-  if (kg == 0) {  // zero the padding columns of this thread's 8 rows
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-      *reinterpret_cast<u32x4*>(vt + (dc * 8 + r) * TL::kVtStride + kKeys) = u32x4{0, 0, 0, 0};
+  for (int j = 0; j < 4; ++j) {  // rows 8 dc + 2j (low halves) and 8 dc + 2j + 1 (high halves)
+    const int d0 = dc * 8 + 2 * j;
+    *reinterpret_cast<u32x4*>(vt + vt_chunk_offset(d0, c)) =
+        u32x4{pack_lo16(hv[0][j], hv[1][j]), pack_lo16(hv[2][j], hv[3][j]),
+              pack_lo16(hv[4][j], hv[5][j]), pack_lo16(hv[6][j], hv[7][j])};
+    *reinterpret_cast<u32x4*>(vt + vt_chunk_offset(d0 + 1, c)) =
+        u32x4{pack_hi16(hv[0][j], hv[1][j]), pack_hi16(hv[2][j], hv[3][j]),
+              pack_hi16(hv[4][j], hv[5][j]), pack_hi16(hv[6][j], hv[7][j])};
   }
 }
 
@@ -118,9 +104,10 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
   constexpr int NC = D / 32;
   constexpr int NDB = DV / 16;
   constexpr int XSTRIDE = DV + 4;  // fp32 row stride of the epilogue exchange (banks)
-  static_assert(kQTile * XSTRIDE * 4 <= 2 * TL::kStage, "exchange must fit in the stages");
-
-  __shared__ __align__(16) uint8_t smem[2 * TL::kStage];
+  // two K/V stages during the key loop; the epilogue reuses the space for the exchange
+  constexpr int kSmem = 2 * TL::kStage > kQTile * XSTRIDE * 4 ? 2 * TL::kStage
+                                                               : kQTile * XSTRIDE * 4;
+  __shared__ __align__(16) uint8_t smem[kSmem];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -129,6 +116,10 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
   const int g = lane >> 4;
   const int c16 = lane & 15;
 
+  // Block order: query tiles longest first over all (batch, head) pairs, so the
+  // short tiles of the causal triangle fill the tail of the launch.  (Grouping
+  // one head's tiles per XCD for L2 reuse measured slower: it breaks this
+  // longest-first order inside each XCD.)
   const int BH = a.B * a.H;
   const int n_qt = (a.T + kQTile - 1) / kQTile;
   const int jr = blockIdx.x / BH;
@@ -227,92 +218,114 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
     }
     if (wave_active) {
       const uint8_t* kbase = smem + stage * TL::kStage + stream * TL::kKBytes;
-      const uint16_t* vt =
-          reinterpret_cast<const uint16_t*>(smem + stage * TL::kStage + 2 * TL::kKBytes);
+      const uint8_t* vbytes = smem + stage * TL::kStage + 2 * TL::kKBytes;
+
+      // S^T = K Q^T for one 32-key half: 2 key blocks x 2 column blocks
+      auto scores = [&](int cc, f32x4 (&sacc)[2][2]) {
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int k0 = kt * kKeys + cc * 32;
-        if (k0 < wave_key_end) {
-          // S^T = K Q^T: 2 key blocks x 2 column blocks
-          f32x4 sacc[2][2];
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const u32x4 kf = *reinterpret_cast<const u32x4*>(
+                kbase + k_swizzled(cc * 32 + kb * 16 + c16, c * 4 + g, TL::kChunks));
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = mfma_bf16(kf, qf[nb][c], sacc[kb][nb]);
+          }
+        }
+      };
+      auto mask = [&](int k0, f32x4 (&sacc)[2][2]) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = k0 + kb * 16 + 4 * g + i;
+              const int row = q_lo + nb * 16 + c16;
+              if (key >= T || (CAUSAL && key > row)) sacc[kb][nb][i] = -INFINITY;
+            }
+      };
+      // column maxima (scaled to log2 units); true if any column outgrew m_ref by 2^8
+      auto col_max = [&](const f32x4 (&sacc)[2][2], float (&mt)[2]) {
+        bool grow = false;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          float x = sacc[0][nb][0];
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < 4; ++i) x = fmaxf(x, sacc[kb][nb][i]);
+          mt[nb] = max_across_rows(x) * cs;
+          grow |= mt[nb] > m_ref[nb] + kRescaleLog2;
+        }
+        return wave_any(grow);
+      };
+      auto rescale = [&](const float (&mt)[2]) {
 #pragma unroll
-          for (int c = 0; c < NC; ++c) {
+        for (int nb = 0; nb < 2; ++nb) {
+          const float mn = fmaxf(m_ref[nb], mt[nb]);
+          const float alpha = (mn == m_ref[nb]) ? 1.f : fast_exp2(m_ref[nb] - mn);
+          m_ref[nb] = mn;
+          l_part[nb] *= alpha;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-              const u32x4 kf = *reinterpret_cast<const u32x4*>(
-                  kbase + k_swizzled(cc * 32 + kb * 16 + c16, c * 4 + g, TL::kChunks));
+          for (int db = 0; db < NDB; ++db) o[db][nb] *= alpha;
+        }
+      };
+      // P = 2^(S cs - m_ref) rounded to fp16, and its per-lane column sums
+      auto probs = [&](const f32x4 (&sacc)[2][2], u32x4 (&pf)[2], float (&ps)[2]) {
 #pragma unroll
-              for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = mfma_bf16(kf, qf[nb][c], sacc[kb][nb]);
+        for (int nb = 0; nb < 2; ++nb) {
+          const float mb = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
+          float pv[8];
+          float sum = 0.f;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float e = fast_exp2(fmaf(sacc[kb][nb][i], cs, -mb));
+              pv[kb * 4 + i] = e;
+              sum += e;
             }
-          }
-          const bool need_mask = (k0 + 32 > T) || (CAUSAL && k0 + 31 > q_lo);
-          if (need_mask) {
+          ps[nb] = sum;
+          pf[nb] = u32x4{pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]),
+                         pack_f16x2(pv[4], pv[5]), pack_f16x2(pv[6], pv[7])};
+        }
+      };
+      // O^T += V^T P^T, V^T fragments (one 16-byte read each) fetched one block ahead
+      auto pv_update = [&](int cc, const u32x4 (&pf)[2]) {
+        auto fetch_v = [&](int db) {
+          return *reinterpret_cast<const u32x4*>(vbytes + vt_chunk_offset(db * 16 + c16, cc * 4 + g));
+        };
+        u32x4 vnext = fetch_v(0);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int db = 0; db < NDB; ++db) {
+          const u32x4 vf = vnext;
+          if (db + 1 < NDB) vnext = fetch_v(db + 1);
 #pragma unroll
-              for (int nb = 0; nb < 2; ++nb)
+          for (int nb = 0; nb < 2; ++nb) o[db][nb] = mfma_f16(vf, pf[nb], o[db][nb]);
+        }
+      };
+
+      const int kbase_key = kt * kKeys;
+      {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const int key = k0 + kb * 16 + 4 * g + i;
-                  const int row = q_lo + nb * 16 + c16;
-                  if (key >= T || (CAUSAL && key > row)) sacc[kb][nb][i] = -INFINITY;
-                }
-          }
-          float mt[2];
-          bool grow = false;
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            float x = sacc[0][nb][0];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) x = fmaxf(x, sacc[kb][nb][i]);
-            mt[nb] = max_across_rows(x) * cs;
-            grow |= mt[nb] > m_ref[nb] + kRescaleLog2;
-          }
-          if (wave_any(grow)) {
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-              const float mn = fmaxf(m_ref[nb], mt[nb]);
-              const float alpha = (mn == m_ref[nb]) ? 1.f : fast_exp2(m_ref[nb] - mn);
-              m_ref[nb] = mn;
-              l_part[nb] *= alpha;
-#pragma unroll
-              for (int db = 0; db < NDB; ++db) o[db][nb] *= alpha;
-            }
-          }
-          u32x4 pf[2];
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const float mb = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
-            float pv[8];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const float e = fast_exp2(fmaf(sacc[kb][nb][i], cs, -mb));
-                pv[kb * 4 + i] = e;
-                l_part[nb] += e;
-              }
-            pf[nb] = u32x4{pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]),
-                           pack_f16x2(pv[4], pv[5]), pack_f16x2(pv[6], pv[7])};
-          }
-          // O^T += V^T P^T, V^T fragments (one 16-byte read each) fetched one block ahead
-          const uint16_t* vbase = vt + c16 * TL::kVtStride + cc * 32 + g * 8;
-          auto fetch_v = [&](int db) {
-            return *reinterpret_cast<const u32x4*>(vbase + db * 16 * TL::kVtStride);
-          };
-          u32x4 vnext = fetch_v(0);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const u32x4 vf = vnext;
-            if (db + 1 < NDB) vnext = fetch_v(db + 1);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) o[db][nb] = mfma_f16(vf, pf[nb], o[db][nb]);
+        for (int cc = 0; cc < 2; ++cc) {
+          const int k0 = kbase_key + cc * 32;
+          if (k0 < wave_key_end) {
+            f32x4 sacc[2][2];
+            float mt[2], ps[2];
+            u32x4 pf[2];
+            scores(cc, sacc);
+            if ((k0 + 32 > T) || (CAUSAL && k0 + 31 > q_lo)) mask(k0, sacc);
+            if (col_max(sacc, mt)) rescale(mt);
+            probs(sacc, pf, ps);
+            l_part[0] += ps[0];
+            l_part[1] += ps[1];
+            pv_update(cc, pf);
           }
         }
       }
@@ -388,7 +401,7 @@ hipError_t launch_typed(const V1Args& a, void* workspace, hipStream_t stream) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL || pack_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   uint16_t* vp = static_cast<uint16_t*>(workspace);
-  hipLaunchKernelGGL((v1_pack_v_kernel<D, DV>), dim3((unsigned)pack_blocks), dim3(kPackThreads), 0,
+  hipLaunchKernelGGL((v1_pack_v_kernel<D, DV>), dim3((unsigned)pack_blocks), dim3(DV), 0,
                      stream, a, vp);
   if (a.causal)
     hipLaunchKernelGGL((v1_prefill_kernel<D, DV, true>), dim3((unsigned)blocks), dim3(kThreads), 0,

@@ -88,8 +88,8 @@ def test_v1_empty_problem_is_a_no_op(lib):
 def test_v1_workspace_query(lib):
     assert lib.diffattn_v1_workspace_bytes(4, 4096, 12, 128, 256, F32) == 0
     need = lib.diffattn_v1_workspace_bytes(4, 4096, 12, 128, 256, BF16)
-    # one fp16 block [256][72] per (batch, head, 64-key tile)
-    assert need == 4 * 12 * 64 * 256 * 72 * 2
+    # one fp16 block [256 rows][64 keys] per (batch, head, 64-key tile)
+    assert need == 4 * 12 * 64 * 256 * 64 * 2
     assert lib.diffattn_v1_workspace_bytes(4, 4096, 12, 96, 192, BF16) == 0
 
 
