@@ -62,7 +62,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   constexpr int SUB = kWaves / KVW;  // waves sharing one KV head
   constexpr int NC = D / 32;
   constexpr int NDB = D / 16;
-  __shared__ __align__(16) uint8_t vbuf[kWaves][2][TL::kBytes];
+  // The two halves of each wave's V double buffer are separate LDS objects, so
+  // the compiler sees that reads of one cannot alias the direct-to-LDS loads in
+  // flight into the other and waits only for the loads of the chunk it reads.
+  __shared__ __align__(16) uint8_t vbuf0[kWaves][TL::kBytes];
+  __shared__ __align__(16) uint8_t vbuf1[kWaves][TL::kBytes];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -103,16 +107,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
     const int base = s0 + chunk * kChunk;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int key = base + kb * 16 + c16;
+      // rows past the end are clamped (their scores are masked), so every load is
+      // issued unconditionally and the wait counts stay exact
+      const int key = min(base + kb * 16 + c16, s1 - 1);
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        kf[kb][c] = key < s1 ? ldg128(kbase + (size_t)key * row_stride + c * 32 + g * 8)
-                             : u32x4{0, 0, 0, 0};
+      for (int c = 0; c < NC; ++c) kf[kb][c] = ldg128(kbase + (size_t)key * row_stride + c * 32 + g * 8);
     }
   };
-  auto load_v = [&](int chunk, int buf) {
+  auto load_v = [&](int chunk, uint8_t* dst) {
     const int base = s0 + chunk * kChunk;
-    uint8_t* dst = vbuf[wave][buf];
 #pragma unroll
     for (int j = 0; j < TL::kInstr; ++j) {
       const int off = j * 1024 + lane * 16;
@@ -130,27 +133,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   f32x4 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY, l_part = 0.f;
+  float m_ref = -INFINITY, mb = 0.f, l_part = 0.f;  // mb: m_ref, or 0 while it is -inf
   const float cs = a.scale * kLog2e;
   const int tr_key = 4 * g + (c16 >> 2);
   const int tr_byte = 8 * (c16 & 3);
 
-  u32x4 kf[2][NC], kn[2][NC];
-  if (c_begin < c_end) {
-    load_k(c_begin, kn);
-    load_v(c_begin, 0);
-  }
-  for (int ci = c_begin; ci < c_end; ++ci) {
-    const int buf = (ci - c_begin) & 1;
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this chunk's K registers and V buffer landed
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) kf[kb][c] = kn[kb][c];
-    if (ci + 1 < c_end) {  // next chunk in flight while this one is computed
-      load_k(ci + 1, kn);
-      load_v(ci + 1, buf ^ 1);
-    }
+  // One 32-key chunk: start the next chunk's loads (K into the other register
+  // set, V into the other buffer), then consume this one.  The loads are issued
+  // unconditionally (past the wave's last chunk they fetch clamped, valid rows
+  // that are never used), so the compiler can count them and waits for exactly
+  // the loads each use depends on.
+  auto chunk_step = [&](int ci, const u32x4 (&kf)[2][NC], u32x4 (&kn)[2][NC], const uint8_t* vb,
+                        uint8_t* vnext) {
+    load_k(ci + 1, kn);
+    load_v(ci + 1, vnext);
     const int base = s0 + ci * kChunk;
 
     f32x4 sacc[2];
@@ -177,11 +173,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
       const float mn = fmaxf(m_ref, mt);
       const float alpha = (mn == m_ref) ? 1.f : fast_exp2(m_ref - mn);
       m_ref = mn;
+      mb = (mn == -INFINITY) ? 0.f : mn;
       l_part *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] *= alpha;
     }
-    const float mb = (m_ref == -INFINITY) ? 0.f : m_ref;
     float pv[8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -193,17 +189,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
       }
     const u32x4 pf = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                            pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
-    const uint8_t* vb = vbuf[wave][buf];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const u32x2 lo = lds_read_tr16(vb + dec_v_offset<D>(tr_key, db * 32 + tr_byte));
       const u32x2 hi = lds_read_tr16(vb + dec_v_offset<D>(tr_key + 16, db * 32 + tr_byte));
       o[db] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, o[db]);
     }
-    // the next iteration's loads overwrite the other buffer only; this buffer is
-    // rewritten two iterations later, after the reads above have returned
+    // the buffer read here is refilled by the next step's loads: make sure the
+    // reads above have returned first
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  };
+
+  u32x4 ka[2][NC], kb2[2][NC];
+  if (c_begin < c_end) {
+    load_k(c_begin, ka);
+    load_v(c_begin, vbuf0[wave]);
   }
+  for (int ci = c_begin; ci < c_end; ci += 2) {
+    chunk_step(ci, ka, kb2, vbuf0[wave], vbuf1[wave]);
+    if (ci + 1 < c_end) chunk_step(ci + 1, kb2, ka, vbuf1[wave], vbuf0[wave]);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the unused last prefetch has landed
 
   // ---- this wave's partial (O unnormalised, m in scaled log2 units, l) ----
   const float l_tot = sum_across_rows(l_part);

@@ -38,6 +38,11 @@ constexpr int kRows = 16;   // query rows per wave
 constexpr int kKeys = 64;   // keys per staged KV tile
 constexpr float kRescaleLog2 = 8.0f;
 
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
 template <int D>
 struct Tile {
   static constexpr int kRowBytes = D * 2;
@@ -70,7 +75,11 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   constexpr int NDB = D / 16;  // 16-row blocks of O^T
   static_assert(TL::kInstr % kWaves == 0, "tile loads must split evenly over the waves");
 
-  __shared__ __align__(16) uint8_t smem[2 * TL::kStage];
+  // Two pipeline stages as two separate LDS objects: the compiler then knows
+  // the transposing reads of one stage cannot alias the direct-to-LDS loads in
+  // flight into the other, and does not wait for those loads before each read.
+  __shared__ __align__(16) uint8_t smem0[TL::kStage];
+  __shared__ __align__(16) uint8_t smem1[TL::kStage];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -139,7 +148,12 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   const uint16_t* kbase_g = a.k + ((size_t)tok0 * a.Hkv + kv) * D;
   const uint16_t* vbase_g = a.v + ((size_t)tok0 * a.Hkv + kv) * D;
   constexpr int NJ = TL::kInstr / kWaves;
-  uint32_t k_lane_off[NJ], v_lane_off[NJ];  // bytes
+  // A lane's LDS bytes in its j-th load of a tile lie kJRows rows below those of
+  // its first load; kJRows is a multiple of both swizzle periods, so the chunk
+  // it fetches is the same and the j-th global offset differs by a uniform
+  // kJRows rows (added to the scalar base).
+  constexpr int kJRows = kWaves * 1024 / TL::kRowBytes;
+  static_assert(kJRows % TL::kChunks == 0 && kJRows % (D / 16) == 0, "loads must repeat the swizzle");
   auto lane_chunks = [&](int j, int& r, int& kc, int& vc) {
     const int off = (wave + j * kWaves) * 1024 + lane * 16;  // LDS byte offset this lane fills
     r = off / TL::kRowBytes;
@@ -148,22 +162,22 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
     constexpr int n32 = D / 16;          // V: 32-byte position pos/2 holds (pos/2) ^ (r mod n32)
     vc = (((pos >> 1) ^ (r & (n32 - 1))) << 1) | (pos & 1);
   };
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
+  uint32_t k_lane_off, v_lane_off;  // bytes, first load of a tile
+  {
     int r, kc, vc;
-    lane_chunks(j, r, kc, vc);
-    k_lane_off[j] = (uint32_t)((r * kv_stride + kc * 8) * 2);
-    v_lane_off[j] = (uint32_t)((r * kv_stride + vc * 8) * 2);
+    lane_chunks(0, r, kc, vc);
+    k_lane_off = (uint32_t)((r * kv_stride + kc * 8) * 2);
+    v_lane_off = (uint32_t)((r * kv_stride + vc * 8) * 2);
   }
-  auto load_tiles = [&](int kt, int stage) {
-    uint8_t* base = smem + stage * TL::kStage;
+  auto load_tiles = [&](int kt, uint8_t* base) {
     const size_t tile = (size_t)kt * kKeys * kv_stride;
     if ((kt + 1) * kKeys <= L) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int blk = wave + j * kWaves;
-        dma16(kbase_g + tile, k_lane_off[j], base + blk * 1024);
-        dma16(vbase_g + tile, v_lane_off[j], base + TL::kTileBytes + blk * 1024);
+        const size_t jrow = tile + (size_t)j * kJRows * kv_stride;
+        dma16(kbase_g + jrow, k_lane_off, base + blk * 1024);
+        dma16(vbase_g + jrow, v_lane_off, base + TL::kTileBytes + blk * 1024);
       }
     } else {  // ragged last tile: clamp rows past the sequence end (they are masked)
 #pragma unroll
@@ -178,7 +192,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
     }
   };
 
-  load_tiles(0, 0);
+  load_tiles(0, smem0);
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): direct-to-LDS loads landed
   __syncthreads();
 
@@ -187,108 +201,146 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) o[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
+  // m_ref: reference maximum (log2 units) per column block; mb is m_ref with
+  // -inf replaced by 0, the value subtracted before exp2.
+  float m_ref[2] = {-INFINITY, -INFINITY}, mb[2] = {0.f, 0.f}, l_part[2] = {0.f, 0.f};
   const float cs = a.scale * kLog2e;
 
-  // transposing-read address pieces: lane j of a row supplies key 4g + j/4, d 4(j%4)
+  // Per-lane LDS offsets, fixed for the whole key loop.  K operand: row c16 of
+  // a 16-key block, chunk 4c + g.  V^T operand (transposing read): lane j of a
+  // 16-lane row supplies key 4g + j/4 and d 4(j%4) of 32-byte column block db.
+  // Offsets of the 32-key step and the upper 16 keys are added as immediates.
   const int tr_key = 4 * g + (c16 >> 2);
   const int tr_byte = 8 * (c16 & 3);
+  int k_ofs[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) k_ofs[c] = k_offset<D>(c16, c * 4 + g);
+  // v_offset(tr_key + 16 m, 32 db + tr_byte) = v_tr ^ (32 db) + 16 m rows: the row
+  // swizzle only touches bits 5.. of the in-row offset, which v_tr's row and
+  // tr_byte parts leave clear.
+  static_assert(TL::kRowBytes % (32 * (D / 16)) == 0, "row offsets must keep the swizzle bits clear");
+  const int v_tr = v_offset<D>(tr_key, tr_byte);
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int stage = kt & 1;
-    if (kt + 1 < n_kt) load_tiles(kt + 1, stage ^ 1);
-    if (wave_active) {
-      const uint8_t* k_lds = smem + stage * TL::kStage;
-      const uint8_t* v_lds = k_lds + TL::kTileBytes;
+  // One 32-key step; MASKED adds the causal / ragged mask (only the key tiles
+  // on the diagonal or at the sequence end need it).
+  auto step = [&](auto masked, const uint8_t* k_lds, const uint8_t* v_lds, int cc, int k0) {
+    constexpr bool MASKED = decltype(masked)::value;
+    // S^T = K Q^T: 2 key blocks x 2 column blocks
+    f32x4 sacc[2][2];
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int k0 = kt * kKeys + cc * 32;
-        if (k0 < wave_key_end) {
-          // S^T = K Q^T: 2 key blocks x 2 column blocks
-          f32x4 sacc[2][2];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+      for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NC; ++c) {
 #pragma unroll
-          for (int c = 0; c < NC; ++c) {
+      for (int kb = 0; kb < 2; ++kb) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(
+            k_lds + k_ofs[c] + (cc * 32 + kb * 16) * TL::kRowBytes);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-              const u32x4 kf = *reinterpret_cast<const u32x4*>(
-                  k_lds + k_offset<D>(cc * 32 + kb * 16 + c16, c * 4 + g));
+        for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = mfma_bf16(kf, qf[nb][c], sacc[kb][nb]);
+      }
+    }
+    if constexpr (MASKED) {  // same rows for both heads of the pair
 #pragma unroll
-              for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = mfma_bf16(kf, qf[nb][c], sacc[kb][nb]);
-            }
-          }
-
-          // causal / ragged mask (same rows for both heads of the pair)
-          const bool need_mask = (k0 + 32 > L) || (CAUSAL && k0 + 31 > q_lo);
-          if (need_mask) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int key = k0 + kb * 16 + 4 * g + i;
-                if (key >= L || (CAUSAL && key > row)) {
-                  sacc[kb][0][i] = -INFINITY;
-                  sacc[kb][1][i] = -INFINITY;
-                }
-              }
-          }
-
-          // online softmax, one query column per lane and column block
-          float mt[2];
-          bool grow = false;
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            float x = sacc[0][nb][0];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) x = fmaxf(x, sacc[kb][nb][i]);
-            mt[nb] = max_across_rows(x) * cs;
-            grow |= mt[nb] > m_ref[nb] + kRescaleLog2;
-          }
-          if (wave_any(grow)) {
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-              const float mn = fmaxf(m_ref[nb], mt[nb]);
-              const float alpha = (mn == m_ref[nb]) ? 1.f : fast_exp2(m_ref[nb] - mn);
-              m_ref[nb] = mn;
-              l_part[nb] *= alpha;
-#pragma unroll
-              for (int db = 0; db < NDB; ++db) o[db][nb] *= alpha;
-            }
-          }
-          u32x4 pf[2];
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const float mb = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
-            float pv[8];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const float e = fast_exp2(fmaf(sacc[kb][nb][i], cs, -mb));
-                pv[kb * 4 + i] = e;
-                l_part[nb] += e;
-              }
-            pf[nb] = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                           pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
-          }
-
-          // O^T += V^T P^T; V^T fragments by transposing reads of the row-major V tile
-          const int r0 = cc * 32 + tr_key;  // key row for slots 0..3; +16 for slots 4..7
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const u32x2 lo = lds_read_tr16(v_lds + v_offset<D>(r0, db * 32 + tr_byte));
-            const u32x2 hi = lds_read_tr16(v_lds + v_offset<D>(r0 + 16, db * 32 + tr_byte));
-            const u32x4 vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) o[db][nb] = mfma_bf16(vf, pf[nb], o[db][nb]);
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + kb * 16 + 4 * g + i;
+          if (key >= L || (CAUSAL && key > row)) {
+            sacc[kb][0][i] = -INFINITY;
+            sacc[kb][1][i] = -INFINITY;
           }
         }
+    }
+
+    // online softmax, one query column per lane and column block
+    float mt[2];
+    bool grow = false;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float x = sacc[0][nb][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x = fmaxf(x, sacc[kb][nb][i]);
+      mt[nb] = max_across_rows(x) * cs;
+      grow |= mt[nb] > m_ref[nb] + kRescaleLog2;
+    }
+    if (wave_any(grow)) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const float mn = fmaxf(m_ref[nb], mt[nb]);
+        const float alpha = (mn == m_ref[nb]) ? 1.f : fast_exp2(m_ref[nb] - mn);
+        m_ref[nb] = mn;
+        mb[nb] = (mn == -INFINITY) ? 0.f : mn;
+        l_part[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db][nb] *= alpha;
       }
+    }
+    u32x4 pf[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float pv[8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = fast_exp2(fmaf(sacc[kb][nb][i], cs, -mb[nb]));
+          pv[kb * 4 + i] = e;
+          l_part[nb] += e;
+        }
+      pf[nb] = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                     pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+    }
+
+    // O^T += V^T P^T; V^T fragments by transposing reads of the row-major V tile
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const uint8_t* vp = v_lds + (v_tr ^ (db * 32)) + cc * 32 * TL::kRowBytes;
+      const u32x2 lo = lds_read_tr16(vp);
+      const u32x2 hi = lds_read_tr16(vp + 16 * TL::kRowBytes);
+      const u32x4 vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) o[db][nb] = mfma_bf16(vf, pf[nb], o[db][nb]);
+    }
+  };
+
+  // Key tiles [0, n_int) are fully valid and visible to every row of the
+  // workgroup: they take the unmasked step in a branch-free loop, unrolled by
+  // two so each stage is a fixed LDS object.  The remaining (diagonal and
+  // ragged) tiles take the masked step with the stage chosen at run time.
+  const int q_lo_block = qt * QTILE;
+  const int n_int = CAUSAL ? min((q_lo_block + 1) / kKeys, L / kKeys) : L / kKeys;
+  auto interior_tile = [&](int kt, const uint8_t* k_lds, uint8_t* next) {
+    if (kt + 1 < n_kt) load_tiles(kt + 1, next);
+    if (wave_active) {
+      const uint8_t* v_lds = k_lds + TL::kTileBytes;
+      step(BoolTag<false>{}, k_lds, v_lds, 0, kt * kKeys);
+      step(BoolTag<false>{}, k_lds, v_lds, 1, kt * kKeys + 32);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile landed
+    __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + 2 <= n_int; kt += 2) {
+    interior_tile(kt, smem0, smem1);
+    interior_tile(kt + 1, smem1, smem0);
+  }
+  if (kt < n_int) {
+    interior_tile(kt, smem0, smem1);
+    ++kt;
+  }
+  for (; kt < n_kt; ++kt) {
+    uint8_t* cur = (kt & 1) ? smem1 : smem0;
+    uint8_t* next = (kt & 1) ? smem0 : smem1;
+    if (kt + 1 < n_kt) load_tiles(kt + 1, next);
+    if (wave_active) {
+      const uint8_t* v_lds = cur + TL::kTileBytes;
+      const int t0 = kt * kKeys;
+      if (t0 < wave_key_end) step(BoolTag<true>{}, cur, v_lds, 0, t0);
+      if (t0 + 32 < wave_key_end) step(BoolTag<true>{}, cur, v_lds, 1, t0 + 32);
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
