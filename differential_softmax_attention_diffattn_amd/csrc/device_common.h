@@ -105,6 +105,40 @@ __device__ __forceinline__ float max_within_row16(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Sum of the eight bf16 values of a packed 16-byte fragment, added to acc, with
+// the dot-product unit (v_dot2c_f32_bf16 against {1, 1}).
+__device__ __forceinline__ float sum_bf16x8(const u32x4& p, float acc) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  const s16x2 ones = __builtin_bit_cast(s16x2, 0x3f803f80u);
+  // (each word goes through a scalar copy: bit-casting a vector element
+  // directly would reinterpret the vector's first word)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = p[j];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(s16x2, w), ones, acc, false);
+  }
+  return acc;
+}
+// Sum of the eight fp16 values of a packed 16-byte fragment, added to acc.
+__device__ __forceinline__ float sum_f16x8(const u32x4& p, float acc) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 ones = __builtin_bit_cast(f16x2, 0x3c003c00u);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = p[j];
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), ones, acc, false);
+  }
+  return acc;
+}
+// Eight packed bf16 values times s, rounded back to bf16 (nearest even).
+__device__ __forceinline__ u32x4 scale_bf16x8(const u32x4& q, float s) {
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    r[j] = pack_bf16x2(bf16lo_to_f32(q[j]) * s, bf16hi_to_f32(q[j]) * s);
+  return r;
+}
+
 // Logistic function in fp32: 1 / (1 + 2^(-x log2 e)).  For x >= 40 it is exactly 1.0f.
 __device__ __forceinline__ float sigmoid_f32(float x) {
   return 1.0f / (1.0f + exp2f(-x * kLog2e));

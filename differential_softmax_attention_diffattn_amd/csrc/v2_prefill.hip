@@ -130,14 +130,18 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   const int wave_key_end = CAUSAL ? min(q_lo + kRows, L) : L;
 
   // ---- Q^T fragments (B operand): block 0 = even head, block 1 = odd head ----
+  // Q is pre-multiplied by scale * log2(e) (rounded to bf16), so the score MFMA
+  // yields log2-domain logits directly.
+  const float cs = a.scale * kLog2e;
   const int row = q_lo + c16;
   u32x4 qf[2][NC];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      qf[nb][c] = row < L ? ldg128(a.q + ((size_t)(tok0 + row) * a.Hq + 2 * p + nb) * D +
-                                   c * 32 + g * 8)
+      qf[nb][c] = row < L ? scale_bf16x8(ldg128(a.q + ((size_t)(tok0 + row) * a.Hq + 2 * p + nb) * D +
+                                                c * 32 + g * 8),
+                                         cs)
                           : u32x4{0, 0, 0, 0};
 
   // ---- direct-to-LDS tile loads (K and V rows, swizzled) ----
@@ -201,10 +205,12 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) o[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // m_ref: reference maximum (log2 units) per column block; mb is m_ref with
-  // -inf replaced by 0, the value subtracted before exp2.
+  // Softmax state per column block (log2 units): m_ref is the reference
+  // maximum, -inf until the first key; mb is m_ref with -inf replaced by 0, the
+  // value subtracted before exp2; sinit = {-mb x 4} starts every score MFMA
+  // chain, so the accumulators come out as S*scale*log2(e) - mb.
   float m_ref[2] = {-INFINITY, -INFINITY}, mb[2] = {0.f, 0.f}, l_part[2] = {0.f, 0.f};
-  const float cs = a.scale * kLog2e;
+  f32x4 sinit[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 
   // Per-lane LDS offsets, fixed for the whole key loop.  K operand: row c16 of
   // a 16-key block, chunk 4c + g.  V^T operand (transposing read): lane j of a
@@ -212,25 +218,42 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   // Offsets of the 32-key step and the upper 16 keys are added as immediates.
   const int tr_key = 4 * g + (c16 >> 2);
   const int tr_byte = 8 * (c16 & 3);
-  int k_ofs[NC];
+  int k_ofs[NC], v_ofs[NDB];
 #pragma unroll
   for (int c = 0; c < NC; ++c) k_ofs[c] = k_offset<D>(c16, c * 4 + g);
-  // v_offset(tr_key + 16 m, 32 db + tr_byte) = v_tr ^ (32 db) + 16 m rows: the row
-  // swizzle only touches bits 5.. of the in-row offset, which v_tr's row and
-  // tr_byte parts leave clear.
-  static_assert(TL::kRowBytes % (32 * (D / 16)) == 0, "row offsets must keep the swizzle bits clear");
-  const int v_tr = v_offset<D>(tr_key, tr_byte);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) v_ofs[db] = v_offset<D>(tr_key, db * 32 + tr_byte);
+
+  // P for one column block from its two score accumulators, minus `shift`:
+  // packed bf16 fragment plus the per-lane sum of the rounded values.
+  auto probs = [&](const f32x4 (&sacc)[2][2], int nb, float shift, u32x4& pf, float& st) {
+    float pv[8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[kb * 4 + i] = fast_exp2(sacc[kb][nb][i] - shift);
+    pf = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
+               pack_bf16x2(pv[6], pv[7])};
+    st = sum_bf16x8(pf, 0.f);
+  };
 
   // One 32-key step; MASKED adds the causal / ragged mask (only the key tiles
   // on the diagonal or at the sequence end need it).
+  //
+  // Lazy rescaling, checked after the fact: P = 2^(s - mb) is computed with the
+  // current reference; if some lane's eight values sum past 2^8 (so some P may
+  // exceed 2^8) or no reference exists yet, the wave takes the rare path: the
+  // column maxima are computed, the reference moves up to them, O and l are
+  // rescaled and P is recomputed (now <= 1).  Otherwise every P <= 2^8, which
+  // bf16 P and the fp32 O / l accumulators carry without loss of range.
   auto step = [&](auto masked, const uint8_t* k_lds, const uint8_t* v_lds, int cc, int k0) {
     constexpr bool MASKED = decltype(masked)::value;
-    // S^T = K Q^T: 2 key blocks x 2 column blocks
+    // S^T = K Q^T - mb: 2 key blocks x 2 column blocks
     f32x4 sacc[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = sinit[nb];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
 #pragma unroll
@@ -254,51 +277,41 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
         }
     }
 
-    // online softmax, one query column per lane and column block
-    float mt[2];
-    bool grow = false;
+    u32x4 pf[2];
+    float st[2];
+    bool redo = false;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      float x = sacc[0][nb][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x = fmaxf(x, sacc[kb][nb][i]);
-      mt[nb] = max_across_rows(x) * cs;
-      grow |= mt[nb] > m_ref[nb] + kRescaleLog2;
+      probs(sacc, nb, 0.f, pf[nb], st[nb]);
+      redo |= !(st[nb] <= 256.f) || m_ref[nb] == -INFINITY;
     }
-    if (wave_any(grow)) {
+    if (wave_any(redo)) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const float mn = fmaxf(m_ref[nb], mt[nb]);
+        float x = sacc[0][nb][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x = fmaxf(x, sacc[kb][nb][i]);
+        const float mn = fmaxf(m_ref[nb], max_across_rows(x) + mb[nb]);
         const float alpha = (mn == m_ref[nb]) ? 1.f : fast_exp2(m_ref[nb] - mn);
+        const float mb_new = (mn == -INFINITY) ? 0.f : mn;
+        probs(sacc, nb, mb_new - mb[nb], pf[nb], st[nb]);
         m_ref[nb] = mn;
-        mb[nb] = (mn == -INFINITY) ? 0.f : mn;
+        mb[nb] = mb_new;
+        sinit[nb] = f32x4{-mb_new, -mb_new, -mb_new, -mb_new};
         l_part[nb] *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[db][nb] *= alpha;
       }
     }
-    u32x4 pf[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float pv[8];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = fast_exp2(fmaf(sacc[kb][nb][i], cs, -mb[nb]));
-          pv[kb * 4 + i] = e;
-          l_part[nb] += e;
-        }
-      pf[nb] = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                     pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
-    }
+    l_part[0] += st[0];
+    l_part[1] += st[1];
 
     // O^T += V^T P^T; V^T fragments by transposing reads of the row-major V tile
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const uint8_t* vp = v_lds + (v_tr ^ (db * 32)) + cc * 32 * TL::kRowBytes;
+      const uint8_t* vp = v_lds + v_ofs[db] + cc * 32 * TL::kRowBytes;
       const u32x2 lo = lds_read_tr16(vp);
       const u32x2 hi = lds_read_tr16(vp + 16 * TL::kRowBytes);
       const u32x4 vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
