@@ -37,6 +37,11 @@ constexpr int kQTile = kRowGroups * kRows;      // 128 query rows per workgroup
 constexpr int kKeys = 64;
 constexpr float kRescaleLog2 = 8.0f;  // P <= 2^8, well inside fp16 range
 
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
 template <int D, int DV>
 struct Tile {
   static constexpr int kChunks = D / 8;
@@ -140,7 +145,10 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
   const uint16_t* qsrc = static_cast<const uint16_t*>(stream == 0 ? a.q1 : a.q2);
   const uint16_t* ksrc = static_cast<const uint16_t*>(stream == 0 ? a.k1 : a.k2);
 
-  // Q^T fragments (B operand) of this wave's stream
+  // Q^T fragments (B operand) of this wave's stream.  (Q is not pre-scaled by
+  // log2(e)/sqrt(d): rounding that product to bf16 perturbs the logits enough to
+  // show through the difference of two maps and the RMS norm.)
+  const float cs = kLog2e / sqrtf((float)D);
   u32x4 qf[2][NC];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
@@ -151,18 +159,25 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
                           : u32x4{0, 0, 0, 0};
   }
 
-  // K tile of this wave's stream: the four waves of a stream share its 1 KiB loads
-  // Each lane's K chunks inside a tile are fixed; only the tile's first key
-  // changes.  Keep the lane part as a 32-bit element offset and move the tile
-  // base in scalar registers; clamp rows past T only on the ragged last tile.
+  // K tile of this wave's stream: the four waves of a stream share its 1 KiB
+  // loads, wave rg taking blocks rg, rg + 4, ...  Consecutive blocks of a wave
+  // lie kJRows rows apart, a multiple of the swizzle period, so a lane fetches
+  // the same chunk of each: one 32-bit lane offset serves every load and the
+  // tile and block bases move in scalar registers.  Rows past T are clamped on
+  // the ragged last tile only (they are masked).
+  constexpr int kJRows = kRowGroups * 1024 / (D * 2);
+  static_assert(kJRows % TL::kChunks == 0, "K loads must repeat the swizzle");
   const size_t krow_stride = (size_t)a.H * D;  // elements between consecutive tokens
-  uint32_t k_lane_off[TL::kKInstrPerWave];  // bytes
-#pragma unroll
-  for (int j = 0; j < TL::kKInstrPerWave; ++j) {
-    const int off = (rg * TL::kKInstrPerWave + j) * 1024 + lane * 16;
-    const int row = off / (D * 2);
-    const int chunk = ((off % (D * 2)) >> 4) ^ (row & (TL::kChunks - 1));
-    k_lane_off[j] = (uint32_t)((row * krow_stride + chunk * 8) * 2);
+  auto k_lane_chunk = [&](int blk, int& row, int& chunk) {
+    const int off = blk * 1024 + lane * 16;
+    row = off / (D * 2);
+    chunk = ((off % (D * 2)) >> 4) ^ (row & (TL::kChunks - 1));
+  };
+  uint32_t k_lane_off;  // bytes, first block of a tile
+  {
+    int row, chunk;
+    k_lane_chunk(rg, row, chunk);
+    k_lane_off = (uint32_t)((row * krow_stride + chunk * 8) * 2);
   }
   const uint16_t* k_head = ksrc + (tok_base * a.H + h) * D;
   auto load_k_tile = [&](int kt, int stage) {
@@ -171,14 +186,14 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
     if ((kt + 1) * kKeys <= T) {
 #pragma unroll
       for (int j = 0; j < TL::kKInstrPerWave; ++j)
-        dma16(tile, k_lane_off[j], base + (rg * TL::kKInstrPerWave + j) * 1024);
+        dma16(tile + (size_t)j * kJRows * krow_stride, k_lane_off,
+              base + (rg + kRowGroups * j) * 1024);
     } else {  // ragged last tile: clamp rows past T (they are masked)
 #pragma unroll
       for (int j = 0; j < TL::kKInstrPerWave; ++j) {
-        const int blk = rg * TL::kKInstrPerWave + j;
-        const int off = blk * 1024 + lane * 16;
-        const int row = off / (D * 2);
-        const int chunk = ((off % (D * 2)) >> 4) ^ (row & (TL::kChunks - 1));
+        const int blk = rg + kRowGroups * j;
+        int row, chunk;
+        k_lane_chunk(blk, row, chunk);
         const size_t e = (size_t)min(kt * kKeys + row, T - 1) * krow_stride + chunk * 8;
         dma16(k_head, (uint32_t)(e * 2), base + blk * 1024);
       }
@@ -206,129 +221,147 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) o[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
-  const float cs = kLog2e / sqrtf((float)D);
+  // Softmax state per column block (log2 units): m_ref is the reference
+  // maximum, -inf until the first key; mb is m_ref with -inf replaced by 0, the
+  // value subtracted before exp2.
+  float m_ref[2] = {-INFINITY, -INFINITY}, mb[2] = {0.f, 0.f}, l_part[2] = {0.f, 0.f};
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int stage = kt & 1;
-    const bool has_next = kt + 1 < n_kt;
-    if (has_next) {
+  // P = 2^(S cs - ref) for one column block from its two score accumulators:
+  // packed fp16 fragment plus the per-lane sum of the rounded values.
+  auto probs = [&](const f32x4 (&sacc)[2][2], int nb, float ref, u32x4& pf, float& st)
+                   __attribute__((always_inline)) {
+    float pv[8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[kb * 4 + i] = fast_exp2(fmaf(sacc[kb][nb][i], cs, -ref));
+    pf = u32x4{pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]), pack_f16x2(pv[4], pv[5]),
+               pack_f16x2(pv[6], pv[7])};
+    st = sum_f16x8(pf, 0.f);
+  };
+
+  // One 32-key step of this wave's stream over the staged tile at `stage_base`;
+  // MASKED adds the causal / ragged mask (only diagonal and ragged tiles need it).
+  //
+  // Lazy rescaling, checked after the fact: P = 2^(s - mb) is computed with the
+  // current reference; if some lane's eight values sum past 2^8 (so some P may
+  // exceed 2^8) or no reference exists yet, the wave takes the rare path: the
+  // column maxima are computed, the reference moves up to them, O and l are
+  // rescaled and P is recomputed (now <= 1).  Otherwise every P <= 2^8, well
+  // inside the fp16 range of P and the fp32 O / l accumulators.
+  auto step = [&](auto masked, const uint8_t* stage_base, int cc, int k0) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    const uint8_t* kbase = stage_base + stream * TL::kKBytes;
+    const uint8_t* vbytes = stage_base + 2 * TL::kKBytes;
+    // S^T = K Q^T for one 32-key half: 2 key blocks x 2 column blocks
+    f32x4 sacc[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(
+            kbase + k_swizzled(cc * 32 + kb * 16 + c16, c * 4 + g, TL::kChunks));
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = mfma_bf16(kf, qf[nb][c], sacc[kb][nb]);
+      }
+    }
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = k0 + kb * 16 + 4 * g + i;
+            const int row = q_lo + nb * 16 + c16;
+            if (key >= T || (CAUSAL && key > row)) sacc[kb][nb][i] = -INFINITY;
+          }
+    }
+
+    u32x4 pf[2];
+    float st[2];
+    bool redo = false;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      probs(sacc, nb, mb[nb], pf[nb], st[nb]);
+      redo |= !(st[nb] <= 256.f) || m_ref[nb] == -INFINITY;
+    }
+    if (wave_any(redo)) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float x = sacc[0][nb][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x = fmaxf(x, sacc[kb][nb][i]);
+        const float mn = fmaxf(m_ref[nb], max_across_rows(x) * cs);
+        const float alpha = (mn == m_ref[nb]) ? 1.f : fast_exp2(m_ref[nb] - mn);
+        const float mb_new = (mn == -INFINITY) ? 0.f : mn;
+        probs(sacc, nb, mb_new, pf[nb], st[nb]);
+        m_ref[nb] = mn;
+        mb[nb] = mb_new;
+        l_part[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db][nb] *= alpha;
+      }
+    }
+    l_part[0] += st[0];
+    l_part[1] += st[1];
+
+    // O^T += V^T P^T, V^T fragments (one 16-byte read each) fetched one block ahead
+    auto fetch_v = [&](int db) {
+      return *reinterpret_cast<const u32x4*>(vbytes + vt_chunk_offset(db * 16 + c16, cc * 4 + g));
+    };
+    u32x4 vnext = fetch_v(0);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const u32x4 vf = vnext;
+      if (db + 1 < NDB) vnext = fetch_v(db + 1);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) o[db][nb] = mfma_f16(vf, pf[nb], o[db][nb]);
+    }
+  };
+
+  // Key tiles [0, n_int) are fully valid and visible to every row of the
+  // workgroup: they take the unmasked step in a branch-free loop, unrolled by
+  // two so each stage's LDS offsets are constants.  The remaining (diagonal and
+  // ragged) tiles take the masked step.
+  const int n_int = CAUSAL ? min((qt * kQTile + 1) / kKeys, T / kKeys) : T / kKeys;
+  auto interior_tile = [&](int kt, int stage) __attribute__((always_inline)) {
+    if (kt + 1 < n_kt) {
       load_k_tile(kt + 1, stage ^ 1);
       load_v_tile(kt + 1, stage ^ 1);
     }
     if (wave_active) {
-      const uint8_t* kbase = smem + stage * TL::kStage + stream * TL::kKBytes;
-      const uint8_t* vbytes = smem + stage * TL::kStage + 2 * TL::kKBytes;
-
-      // S^T = K Q^T for one 32-key half: 2 key blocks x 2 column blocks
-      auto scores = [&](int cc, f32x4 (&sacc)[2][2]) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const u32x4 kf = *reinterpret_cast<const u32x4*>(
-                kbase + k_swizzled(cc * 32 + kb * 16 + c16, c * 4 + g, TL::kChunks));
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = mfma_bf16(kf, qf[nb][c], sacc[kb][nb]);
-          }
-        }
-      };
-      auto mask = [&](int k0, f32x4 (&sacc)[2][2]) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = k0 + kb * 16 + 4 * g + i;
-              const int row = q_lo + nb * 16 + c16;
-              if (key >= T || (CAUSAL && key > row)) sacc[kb][nb][i] = -INFINITY;
-            }
-      };
-      // column maxima (scaled to log2 units); true if any column outgrew m_ref by 2^8
-      auto col_max = [&](const f32x4 (&sacc)[2][2], float (&mt)[2]) {
-        bool grow = false;
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          float x = sacc[0][nb][0];
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x = fmaxf(x, sacc[kb][nb][i]);
-          mt[nb] = max_across_rows(x) * cs;
-          grow |= mt[nb] > m_ref[nb] + kRescaleLog2;
-        }
-        return wave_any(grow);
-      };
-      auto rescale = [&](const float (&mt)[2]) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const float mn = fmaxf(m_ref[nb], mt[nb]);
-          const float alpha = (mn == m_ref[nb]) ? 1.f : fast_exp2(m_ref[nb] - mn);
-          m_ref[nb] = mn;
-          l_part[nb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) o[db][nb] *= alpha;
-        }
-      };
-      // P = 2^(S cs - m_ref) rounded to fp16, and its per-lane column sums
-      auto probs = [&](const f32x4 (&sacc)[2][2], u32x4 (&pf)[2], float (&ps)[2]) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const float mb = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
-          float pv[8];
-          float sum = 0.f;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float e = fast_exp2(fmaf(sacc[kb][nb][i], cs, -mb));
-              pv[kb * 4 + i] = e;
-              sum += e;
-            }
-          ps[nb] = sum;
-          pf[nb] = u32x4{pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]),
-                         pack_f16x2(pv[4], pv[5]), pack_f16x2(pv[6], pv[7])};
-        }
-      };
-      // O^T += V^T P^T, V^T fragments (one 16-byte read each) fetched one block ahead
-      auto pv_update = [&](int cc, const u32x4 (&pf)[2]) {
-        auto fetch_v = [&](int db) {
-          return *reinterpret_cast<const u32x4*>(vbytes + vt_chunk_offset(db * 16 + c16, cc * 4 + g));
-        };
-        u32x4 vnext = fetch_v(0);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const u32x4 vf = vnext;
-          if (db + 1 < NDB) vnext = fetch_v(db + 1);
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) o[db][nb] = mfma_f16(vf, pf[nb], o[db][nb]);
-        }
-      };
-
-      const int kbase_key = kt * kKeys;
-      {
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const int k0 = kbase_key + cc * 32;
-          if (k0 < wave_key_end) {
-            f32x4 sacc[2][2];
-            float mt[2], ps[2];
-            u32x4 pf[2];
-            scores(cc, sacc);
-            if ((k0 + 32 > T) || (CAUSAL && k0 + 31 > q_lo)) mask(k0, sacc);
-            if (col_max(sacc, mt)) rescale(mt);
-            probs(sacc, pf, ps);
-            l_part[0] += ps[0];
-            l_part[1] += ps[1];
-            pv_update(cc, pf);
-          }
-        }
-      }
+      step(BoolTag<false>{}, smem + stage * TL::kStage, 0, kt * kKeys);
+      step(BoolTag<false>{}, smem + stage * TL::kStage, 1, kt * kKeys + 32);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile landed
+    __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + 2 <= n_int; kt += 2) {
+    interior_tile(kt, 0);
+    interior_tile(kt + 1, 1);
+  }
+  if (kt < n_int) {
+    interior_tile(kt, 0);
+    ++kt;
+  }
+  for (; kt < n_kt; ++kt) {
+    const int stage = kt & 1;
+    if (kt + 1 < n_kt) {
+      load_k_tile(kt + 1, stage ^ 1);
+      load_v_tile(kt + 1, stage ^ 1);
+    }
+    if (wave_active) {
+      const int t0 = kt * kKeys;
+      if (t0 < wave_key_end) step(BoolTag<true>{}, smem + stage * TL::kStage, 0, t0);
+      if (t0 + 32 < wave_key_end) step(BoolTag<true>{}, smem + stage * TL::kStage, 1, t0 + 32);
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
