@@ -29,6 +29,53 @@ import time
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "differential_softmax_attention_diffattn_amd", "csrc")
+# kernel sources behind each timed workload (the HBM-traffic record is void once they change)
+SOURCES = {
+    "v1": ("v1_prefill.hip", "device_common.h", "kernels.h"),
+    "v2": ("v2_prefill.hip", "device_common.h", "kernels.h"),
+    "varlen": ("v2_prefill.hip", "device_common.h", "kernels.h"),
+    "decode": ("v2_decode.hip", "device_common.h", "kernels.h"),
+}
+
+
+def kernel_digest(which: str) -> str:
+    """sha256 over the kernel sources of one workload (file order fixed)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in SOURCES[which]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def hbm_traffic(which: str, workload: str):
+    """HBM bytes per call from the committed counter record, or None.
+
+    profiles/<workload>_hbm_traffic.txt holds FETCH_SIZE / WRITE_SIZE per
+    dispatch (rocprofv3 --pmc, KiB) for the call's kernels, scaled by the
+    factors a plain copy of known size gives, and the digest of the kernel
+    sources they were taken with.  A record taken with other sources is not
+    used (the kernels have changed since).
+    """
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("kernel_sources_sha256") != kernel_digest(which):
+        return None
+    try:
+        return int(float(rec["hbm_bytes_per_call"]))
+    except (KeyError, ValueError):
+        return None
+
 
 def v1_flops(B, T, H, d, dv):
     return 2.0 * (d + dv) * T * (T + 1) * B * H
@@ -132,8 +179,8 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(flop_call / (ms_call * 1e-3) / 1e12, 2),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(flop_call / (ms_call * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                         "traffic": None,
-                         "kernel": "diffattn_v1_fwd (V pack + fused prefill), HIP events per call",
+                         "traffic": hbm_traffic("v1", w.name),
+                         "kernel": "diffattn_v1_fwd = v1_pack_v + v1_prefill launches, HIP events per call",
                          "ms_per_launch": round(ms_call, 4),
                          "flop_per_launch": flop_call},
             "wall_s_timed": round(wall, 3),
@@ -156,7 +203,8 @@ def main():
             flop = w.B * v2_flops_seq(w.T, w.Hq, w.d)
             tf = flop / (ms * 1e-3) / 1e12
             secondary["v2_prefill"] = {"workload": w.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
-                                       "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flop": flop}
+                                       "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flop": flop,
+                                       "traffic": hbm_traffic("v2", w.name)}
             del x, o
             torch.cuda.empty_cache()
         if args.only in (None, "varlen"):
@@ -175,7 +223,8 @@ def main():
             tf = flop / (ms * 1e-3) / 1e12
             secondary["v2_varlen"] = {"workload": w.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
                                       "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flop": flop,
-                                      "lengths": list(w.lengths)}
+                                      "lengths": list(w.lengths),
+                                      "traffic": hbm_traffic("varlen", w.name)}
             del x, o
             torch.cuda.empty_cache()
         if args.only in (None, "decode"):
@@ -193,7 +242,8 @@ def main():
             byts = 2.0 * w.B * w.S * w.Hkv * w.d * 2
             gbs = byts / (ms * 1e-3) / 1e9
             secondary["v2_decode"] = {"workload": w.name, "ms": round(ms, 4), "GB/s": round(gbs, 1),
-                                      "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": byts}
+                                      "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": byts,
+                                      "traffic": hbm_traffic("decode", w.name)}
             del x, o, wsd
             torch.cuda.empty_cache()
     if secondary:
