@@ -211,6 +211,30 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
     }
   };
 
+  // Halves of a full tile's loads, for spreading them through a tile's compute.
+  // (All eight waves issuing a whole tile at once stalls each of them for
+  // hundreds of cycles at the issue of its direct-to-LDS loads.)
+  constexpr int kKHalf = (TL::kKInstrPerWave + 1) / 2;
+  constexpr int kVPerWave = (TL::kVInstr + kWaves - 1) / kWaves;
+  constexpr int kVHalf = (kVPerWave + 1) / 2;
+  auto load_k_half = [&](int kt, int stage, int half) __attribute__((always_inline)) {
+    uint8_t* base = smem + stage * TL::kStage + stream * TL::kKBytes;
+    const uint16_t* tile = k_head + (size_t)kt * kKeys * krow_stride;
+#pragma unroll
+    for (int j = half * kKHalf; j < min((half + 1) * kKHalf, TL::kKInstrPerWave); ++j)
+      dma16(tile + (size_t)j * kJRows * krow_stride, k_lane_off, base + (rg + kRowGroups * j) * 1024);
+  };
+  auto load_v_half = [&](int kt, int stage, int half) __attribute__((always_inline)) {
+    uint8_t* base = smem + stage * TL::kStage + 2 * TL::kKBytes;
+    const uint8_t* src = vp_bh + (size_t)kt * TL::kVtBytes;
+#pragma unroll
+    for (int j = half * kVHalf; j < min((half + 1) * kVHalf, kVPerWave); ++j) {
+      const int blk = wave + j * kWaves;
+      if (TL::kVInstr % kWaves == 0 || blk < TL::kVInstr)  // (no branch when the loads split evenly)
+        dma16(src, blk * 1024 + lane * 16, base + blk * 1024);
+    }
+  };
+
   load_k_tile(0, 0);
   load_v_tile(0, 0);
   __builtin_amdgcn_s_waitcnt(0x0f70);
@@ -249,7 +273,8 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
   // column maxima are computed, the reference moves up to them, O and l are
   // rescaled and P is recomputed (now <= 1).  Otherwise every P <= 2^8, well
   // inside the fp16 range of P and the fp32 O / l accumulators.
-  auto step = [&](auto masked, const uint8_t* stage_base, int cc, int k0) __attribute__((always_inline)) {
+  auto step = [&](auto masked, const uint8_t* stage_base, int cc, int k0, auto mid)
+                  __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
     const uint8_t* kbase = stage_base + stream * TL::kKBytes;
     const uint8_t* vbytes = stage_base + 2 * TL::kKBytes;
@@ -269,6 +294,7 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
         for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = mfma_bf16(kf, qf[nb][c], sacc[kb][nb]);
       }
     }
+    mid();  // work to issue between the score MFMAs and the softmax
     if constexpr (MASKED) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -330,15 +356,26 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
   // workgroup: they take the unmasked step in a branch-free loop, unrolled by
   // two so each stage's LDS offsets are constants.  The remaining (diagonal and
   // ragged) tiles take the masked step.
-  const int n_int = CAUSAL ? min((qt * kQTile + 1) / kKeys, T / kKeys) : T / kKeys;
+  // (An interior tile is never the last tile, and its successor is a full
+  // tile: the last full tile before a ragged end goes to the tail loop.)
+  const int n_int = max(0, CAUSAL ? min((qt * kQTile + 1) / kKeys, T / kKeys - 1) : T / kKeys - 1);
   auto interior_tile = [&](int kt, int stage) __attribute__((always_inline)) {
-    if (kt + 1 < n_kt) {
+    // The next tile's loads go out in quarters: before and after each step's
+    // score MFMAs.  Stream-1 waves run the first step at raised issue
+    // priority: at equal priority the older (stream-0) wave of each SIMD wins
+    // most issue slots and then idles at the barrier while the other finishes.
+    if (wave_active) {
+      load_k_half(kt + 1, stage ^ 1, 0);
+      if (stream == 1) __builtin_amdgcn_s_setprio(1);
+      step(BoolTag<false>{}, smem + stage * TL::kStage, 0, kt * kKeys,
+           [&] { load_k_half(kt + 1, stage ^ 1, 1); });
+      if (stream == 1) __builtin_amdgcn_s_setprio(0);
+      load_v_half(kt + 1, stage ^ 1, 0);
+      step(BoolTag<false>{}, smem + stage * TL::kStage, 1, kt * kKeys + 32,
+           [&] { load_v_half(kt + 1, stage ^ 1, 1); });
+    } else {
       load_k_tile(kt + 1, stage ^ 1);
       load_v_tile(kt + 1, stage ^ 1);
-    }
-    if (wave_active) {
-      step(BoolTag<false>{}, smem + stage * TL::kStage, 0, kt * kKeys);
-      step(BoolTag<false>{}, smem + stage * TL::kStage, 1, kt * kKeys + 32);
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile landed
     __syncthreads();
@@ -360,8 +397,8 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
     }
     if (wave_active) {
       const int t0 = kt * kKeys;
-      if (t0 < wave_key_end) step(BoolTag<true>{}, smem + stage * TL::kStage, 0, t0);
-      if (t0 + 32 < wave_key_end) step(BoolTag<true>{}, smem + stage * TL::kStage, 1, t0 + 32);
+      if (t0 < wave_key_end) step(BoolTag<true>{}, smem + stage * TL::kStage, 0, t0, [] {});
+      if (t0 + 32 < wave_key_end) step(BoolTag<true>{}, smem + stage * TL::kStage, 1, t0 + 32, [] {});
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
