@@ -246,7 +246,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   // column maxima are computed, the reference moves up to them, O and l are
   // rescaled and P is recomputed (now <= 1).  Otherwise every P <= 2^8, which
   // bf16 P and the fp32 O / l accumulators carry without loss of range.
-  auto step = [&](auto masked, const uint8_t* k_lds, const uint8_t* v_lds, int cc, int k0) {
+  auto step = [&](auto masked, const uint8_t* k_lds, const uint8_t* v_lds, int cc, int k0, auto mid) {
     constexpr bool MASKED = decltype(masked)::value;
     // S^T = K Q^T - mb: 2 key blocks x 2 column blocks
     f32x4 sacc[2][2];
@@ -264,6 +264,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
         for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = mfma_bf16(kf, qf[nb][c], sacc[kb][nb]);
       }
     }
+    mid();  // work to issue between the score MFMAs and the softmax
     if constexpr (MASKED) {  // same rows for both heads of the pair
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -325,13 +326,39 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   // two so each stage is a fixed LDS object.  The remaining (diagonal and
   // ragged) tiles take the masked step with the stage chosen at run time.
   const int q_lo_block = qt * QTILE;
-  const int n_int = CAUSAL ? min((q_lo_block + 1) / kKeys, L / kKeys) : L / kKeys;
+  const int n_int = max(0, CAUSAL ? min((q_lo_block + 1) / kKeys, L / kKeys - 1) : L / kKeys - 1);
+  // Quarters of a full tile's loads (K or V, first or second half of this
+  // wave's share), spread through a tile's compute: all eight waves issuing a
+  // whole tile at once stall for hundreds of cycles at the load issue.
+  constexpr int kHalf = (NJ + 1) / 2;
+  auto load_quarter = [&](int kt, uint8_t* base, int which, int half) __attribute__((always_inline)) {
+    const size_t tile = (size_t)kt * kKeys * kv_stride;
+#pragma unroll
+    for (int j = half * kHalf; j < min((half + 1) * kHalf, NJ); ++j) {
+      const int blk = wave + j * kWaves;
+      const size_t jrow = tile + (size_t)j * kJRows * kv_stride;
+      if (which == 0)
+        dma16(kbase_g + jrow, k_lane_off, base + blk * 1024);
+      else
+        dma16(vbase_g + jrow, v_lane_off, base + TL::kTileBytes + blk * 1024);
+    }
+  };
+  // An interior tile is never the last one and its successor is full (the last
+  // full tile before a ragged end goes to the tail loop).  The younger wave of
+  // each SIMD (waves 4..7) runs the first step at raised issue priority: at
+  // equal priority the older wave wins most issue slots and then idles at the
+  // barrier while the other finishes alone.
   auto interior_tile = [&](int kt, const uint8_t* k_lds, uint8_t* next) {
-    if (kt + 1 < n_kt) load_tiles(kt + 1, next);
     if (wave_active) {
       const uint8_t* v_lds = k_lds + TL::kTileBytes;
-      step(BoolTag<false>{}, k_lds, v_lds, 0, kt * kKeys);
-      step(BoolTag<false>{}, k_lds, v_lds, 1, kt * kKeys + 32);
+      load_quarter(kt + 1, next, 0, 0);
+      if (wave >= kWaves / 2) __builtin_amdgcn_s_setprio(1);
+      step(BoolTag<false>{}, k_lds, v_lds, 0, kt * kKeys, [&] { load_quarter(kt + 1, next, 0, 1); });
+      if (wave >= kWaves / 2) __builtin_amdgcn_s_setprio(0);
+      load_quarter(kt + 1, next, 1, 0);
+      step(BoolTag<false>{}, k_lds, v_lds, 1, kt * kKeys + 32, [&] { load_quarter(kt + 1, next, 1, 1); });
+    } else {
+      load_tiles(kt + 1, next);
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the next tile landed
     __syncthreads();
@@ -352,8 +379,8 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
     if (wave_active) {
       const uint8_t* v_lds = cur + TL::kTileBytes;
       const int t0 = kt * kKeys;
-      if (t0 < wave_key_end) step(BoolTag<true>{}, cur, v_lds, 0, t0);
-      if (t0 + 32 < wave_key_end) step(BoolTag<true>{}, cur, v_lds, 1, t0 + 32);
+      if (t0 < wave_key_end) step(BoolTag<true>{}, cur, v_lds, 0, t0, [] {});
+      if (t0 + 32 < wave_key_end) step(BoolTag<true>{}, cur, v_lds, 1, t0 + 32, [] {});
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
