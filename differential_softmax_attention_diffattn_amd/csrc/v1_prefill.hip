@@ -65,7 +65,9 @@ __device__ __forceinline__ int vt_chunk_offset(int d, int c) {
 }
 
 // Pre-pass: V [B,T,H,DV] bf16 -> the packed fp16 tiles above (keys past T are zero).
-// Thread (dc, c): the 8 rows d = 8 dc .. 8 dc + 7 and logical chunk c.
+// Thread (dc, c): the 8 rows d = 8 dc .. 8 dc + 7 and logical chunk c.  The
+// eight threads of one dc are adjacent, so each store instruction of a wave
+// fills whole 128-byte rows.
 template <int D, int DV>
 __global__ __launch_bounds__(DV) void v1_pack_v_kernel(V1Args a, uint16_t* vp) {
   const int n_kt = (a.T + kKeys - 1) / kKeys;
@@ -74,8 +76,8 @@ __global__ __launch_bounds__(DV) void v1_pack_v_kernel(V1Args a, uint16_t* vp) {
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const uint16_t* vsrc = static_cast<const uint16_t*>(a.v);
-  const int dc = threadIdx.x % (DV / 8);
-  const int c = threadIdx.x / (DV / 8);
+  const int c = threadIdx.x % 8;
+  const int dc = threadIdx.x / 8;
   const int key0 = kt * kKeys + (c >> 2) * 32 + 4 * (c & 3);
   u32x4 hv[8];
 #pragma unroll
