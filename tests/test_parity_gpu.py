@@ -107,6 +107,21 @@ def test_v1_bf16_small_all_rows(gpu, d, dv, layer):
             what=f"v1 bf16 T=300 d={d} layer={layer}")
 
 
+@pytest.mark.parametrize("T", [1, 63, 64, 128, 129, 256])
+@pytest.mark.parametrize("causal", [True, False])
+def test_v1_bf16_tile_boundaries(gpu, T, causal):
+    # lengths at and around the 64-key tile and 128-row query tile edges: the
+    # unmasked interior-tile loop, its successor tile and the masked tail meet here
+    w = inp.V1_BF16.with_shape(B=2, T=T, H=2)
+    x = inp.v1_inputs(w)
+    lam = li = oracle.lambda_init(5)
+    ref = oracle.v1_forward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, li, w.eps,
+                            causal=causal)
+    out = run_v1(cuda(x, gpu), lam, li, w.eps, causal=causal)
+    compare(out.cpu().numpy(), ref, rms(x["v"]), TOL_BF16, REL_L2_BF16,
+            what=f"v1 bf16 T={T} causal={causal}")
+
+
 def test_v1_bf16_non_causal_and_weight(gpu):
     w = inp.V1_BF16.with_shape(B=1, T=200, H=2)
     x = inp.v1_inputs(w)
@@ -190,6 +205,27 @@ def test_v2_small_all_rows(gpu, Hq, Hkv, d, T, causal):
     out = run_v2(cuda(x, gpu), causal)
     compare(out.float().cpu().numpy(), ref, rms(x["v"]), TOL_BF16, REL_L2_BF16,
             what=f"v2 Hq={Hq} Hkv={Hkv} d={d} T={T} causal={causal}")
+
+
+@pytest.mark.parametrize("T,causal", [(64, True), (128, False), (192, False), (256, True)])
+def test_v2_tile_boundaries(gpu, T, causal):
+    # lengths that are whole 64-key tiles (the interior loop's last successor is full)
+    w = inp.V2_PREFILL.with_shape(B=2, T=T, Hq=16, Hkv=2, causal=causal)
+    x = inp.v2_inputs(w)
+    ref = oracle.v2_forward(x["q"], x["k"], x["v"], x["logit"], causal=causal)
+    out = run_v2(cuda(x, gpu), causal)
+    compare(out.float().cpu().numpy(), ref, rms(x["v"]), TOL_BF16, REL_L2_BF16,
+            what=f"v2 T={T} causal={causal}")
+
+
+def test_v2_varlen_whole_tiles(gpu):
+    lens = (64, 128, 192, 63, 65)
+    w = inp.V2_VARLEN.with_shape(lengths=lens, Hq=16, Hkv=2)
+    x = inp.v2_inputs(w)
+    ref = oracle.v2_varlen_forward(x["q"], x["k"], x["v"], x["logit"], x["cu_seqlens"])
+    out = run_v2(cuda(x, gpu), max_seqlen=max(lens))
+    compare(out.float().cpu().numpy(), ref, rms(x["v"]), TOL_BF16, REL_L2_BF16,
+            what="v2 varlen whole tiles")
 
 
 def test_v2_unit_logits(gpu):
