@@ -163,14 +163,20 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_addr) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Direct global->LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
-// lane l's bytes land at lds_base + 16 * l.  `base` is wave-uniform and `byte_off`
-// a per-lane 32-bit offset, so the load can use a scalar base address.
+// Direct global->LDS copy of 16 bytes per lane (gfx950 buffer_load_dwordx4 ...
+// lds): lane l's bytes land at lds_base + 16 * l.  `base` is wave-uniform and
+// becomes a raw buffer resource (scalar registers, no range limit); `byte_off`
+// is the per-lane 32-bit offset.  The buffer form rather than
+// global_load_lds: the compiler counts a pending global (flat-encoded) LDS
+// load against the LDS wait counter as well, and then makes every later LDS
+// read wait for all outstanding LDS reads, so no read can be kept in flight
+// behind the MFMAs while a tile is loading.
+constexpr int kBufferRsrcWord3 = 0x00020000;
 __device__ __forceinline__ void dma16(const void* base, uint32_t byte_off, void* lds_base) {
-  const __attribute__((address_space(1))) char* g =
-      (const __attribute__((address_space(1))) char*)(base) + byte_off;
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds_base), 16, 0,
-                                   0);
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0xffffffff, kBufferRsrcWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)(lds_base), 16, (int)byte_off, 0, 0, 0);
 }
 
 // Register-allocation hint: the value lives in accumulation registers here.

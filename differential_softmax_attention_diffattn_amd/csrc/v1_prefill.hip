@@ -8,19 +8,21 @@
 // Attention: 빼기의 힘"; the per-head RMS norm and the lambda_init factor are
 // from the V1 recap in the "Differential Transformer V2" summary, 상세 정리 §1).
 //
-// A workgroup of 4 waves owns 128 query rows of one (batch, head); each wave
-// owns 32 rows = two 16-column blocks, and runs two online-softmax streams over
-// the same staged K1/K2/V tiles.  Scores are formed transposed, S^T = K Q^T on
-// 16x16x32 bf16 MFMA, so one lane holds one query column per block.  P is
-// rounded to fp16 (11-bit significand) and P.V runs on 16x16x32 fp16 MFMA:
-// bf16 P would put the RMS-normalised output outside a 2e-2 RMS(V) error
-// budget, because the norm divides by |z|, which is small when both maps are
-// near-uniform.  A pre-pass converts V bf16->fp16 (exact for normal-range
-// values) into a workspace laid out tile by tile as Vt[d][key] with padded
-// rows, exactly the LDS image the main kernel needs, so V tiles reach LDS by
-// direct-to-LDS loads with no register staging or per-tile conversion.  One V^T fragment read from LDS feeds four MFMAs (two
-// streams x two column blocks).  The subtraction, RMS norm and scale run on
-// the accumulators in registers; the output is fp32.
+// A workgroup of 8 waves owns 128 query rows of one (batch, head): four row
+// groups of 32 rows (two 16-column blocks) times the two streams, so each
+// wave runs one online softmax, (Q1, K1) or (Q2, K2), over the staged K1/K2/V
+// tiles.  Scores are formed transposed, S^T = K Q^T on 16x16x32 bf16 MFMA, so
+// one lane holds one query column per block.  P is rounded to fp16 (11-bit
+// significand) and P.V runs on 16x16x32 fp16 MFMA: bf16 P would put the
+// RMS-normalised output outside a 2e-2 RMS(V) error budget, because the norm
+// divides by |z|, which is small when both maps are near-uniform.  A pre-pass
+// converts V bf16->fp16 (exact for normal-range values) into a workspace laid
+// out tile by tile as Vt[d][key] with padded rows, exactly the LDS image the
+// main kernel needs, so V tiles reach LDS by direct-to-LDS loads with no
+// register staging or per-tile conversion.  One V^T fragment read from LDS
+// feeds two MFMAs (the wave's two column blocks).  At the end the stream-2
+// waves hand O2 / l2 to their stream-1 partners through LDS, which apply the
+// subtraction, RMS norm and scale in registers; the output is fp32.
 #include <math.h>
 
 #include "device_common.h"
@@ -36,6 +38,7 @@ constexpr int kRows = 32;
 constexpr int kQTile = kRowGroups * kRows;      // 128 query rows per workgroup
 constexpr int kKeys = 64;
 constexpr float kRescaleLog2 = 8.0f;  // P <= 2^8, well inside fp16 range
+constexpr int kVDepth = 2;            // V^T fragments in flight during P.V
 
 template <bool B>
 struct BoolTag {
@@ -297,6 +300,14 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
       }
     }
     mid();  // work to issue between the score MFMAs and the softmax
+    // the first V^T fragments of the P.V product go out before the softmax
+    auto fetch_v = [&](int db) {
+      return *reinterpret_cast<const u32x4*>(vbytes + vt_chunk_offset(db * 16 + c16, cc * 4 + g));
+    };
+    u32x4 vbuf[kVDepth];
+#pragma unroll
+    for (int i = 0; i < kVDepth; ++i) vbuf[i] = fetch_v(i);
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (MASKED) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -340,17 +351,17 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
     l_part[0] += st[0];
     l_part[1] += st[1];
 
-    // O^T += V^T P^T, V^T fragments (one 16-byte read each) fetched one block ahead
-    auto fetch_v = [&](int db) {
-      return *reinterpret_cast<const u32x4*>(vbytes + vt_chunk_offset(db * 16 + c16, cc * 4 + g));
-    };
-    u32x4 vnext = fetch_v(0);
+    // O^T += V^T P^T.  V^T fragments (one 16-byte read each) are read kVDepth
+    // blocks ahead; the scheduling fences keep each read where it is issued
+    // (left alone, the compiler sinks every read to just before its MFMAs and
+    // exposes the full LDS latency on each of them).
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const u32x4 vf = vnext;
-      if (db + 1 < NDB) vnext = fetch_v(db + 1);
+      const u32x4 vf = vbuf[db % kVDepth];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) o[db][nb] = mfma_f16(vf, pf[nb], o[db][nb]);
+      if (db + kVDepth < NDB) vbuf[db % kVDepth] = fetch_v(db + kVDepth);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 

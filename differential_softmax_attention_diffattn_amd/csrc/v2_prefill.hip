@@ -36,6 +36,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kRows = 16;   // query rows per wave
 constexpr int kKeys = 64;   // keys per staged KV tile
+constexpr int kVDepth = 2;  // V^T fragments in flight during P.V
 constexpr float kRescaleLog2 = 8.0f;
 
 template <bool B>
@@ -265,6 +266,18 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
       }
     }
     mid();  // work to issue between the score MFMAs and the softmax
+    // the first V^T fragments (transposing reads of the row-major V tile) go
+    // out before the softmax
+    auto fetch_v = [&](int db) {
+      const uint8_t* vp = v_lds + v_ofs[db] + cc * 32 * TL::kRowBytes;
+      const u32x2 lo = lds_read_tr16(vp);
+      const u32x2 hi = lds_read_tr16(vp + 16 * TL::kRowBytes);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 vbuf[kVDepth];
+#pragma unroll
+    for (int i = 0; i < kVDepth; ++i) vbuf[i] = fetch_v(i);
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (MASKED) {  // same rows for both heads of the pair
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -309,15 +322,17 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
     l_part[0] += st[0];
     l_part[1] += st[1];
 
-    // O^T += V^T P^T; V^T fragments by transposing reads of the row-major V tile
+    // O^T += V^T P^T.  V^T fragments are read kVDepth blocks ahead; the
+    // scheduling fences keep each read where it is issued (left alone, the
+    // compiler sinks every read to just before its MFMAs and exposes the full
+    // LDS latency on each of them).
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const uint8_t* vp = v_lds + v_ofs[db] + cc * 32 * TL::kRowBytes;
-      const u32x2 lo = lds_read_tr16(vp);
-      const u32x2 hi = lds_read_tr16(vp + 16 * TL::kRowBytes);
-      const u32x4 vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      const u32x4 vf = vbuf[db % kVDepth];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) o[db][nb] = mfma_bf16(vf, pf[nb], o[db][nb]);
+      if (db + kVDepth < NDB) vbuf[db % kVDepth] = fetch_v(db + kVDepth);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
