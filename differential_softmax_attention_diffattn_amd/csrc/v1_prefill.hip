@@ -283,7 +283,10 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
     constexpr bool MASKED = decltype(masked)::value;
     const uint8_t* kbase = stage_base + stream * TL::kKBytes;
     const uint8_t* vbytes = stage_base + 2 * TL::kKBytes;
-    // S^T = K Q^T for one 32-key half: 2 key blocks x 2 column blocks
+    // S^T = K Q^T for one 32-key half: 2 key blocks x 2 column blocks.  The
+    // wave issues them at raised priority, so the score MFMAs of one wave go
+    // ahead of the softmax and P.V work of the other wave on its SIMD.
+    __builtin_amdgcn_s_setprio(1);
     f32x4 sacc[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -299,6 +302,7 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
         for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = mfma_bf16(kf, qf[nb][c], sacc[kb][nb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     mid();  // work to issue between the score MFMAs and the softmax
     // the first V^T fragments of the P.V product go out before the softmax
     auto fetch_v = [&](int db) {
@@ -374,15 +378,11 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
   const int n_int = max(0, CAUSAL ? min((qt * kQTile + 1) / kKeys, T / kKeys - 1) : T / kKeys - 1);
   auto interior_tile = [&](int kt, int stage) __attribute__((always_inline)) {
     // The next tile's loads go out in quarters: before and after each step's
-    // score MFMAs.  Stream-1 waves run the first step at raised issue
-    // priority: at equal priority the older (stream-0) wave of each SIMD wins
-    // most issue slots and then idles at the barrier while the other finishes.
+    // score MFMAs.
     if (wave_active) {
       load_k_half(kt + 1, stage ^ 1, 0);
-      if (stream == 1) __builtin_amdgcn_s_setprio(1);
       step(BoolTag<false>{}, smem + stage * TL::kStage, 0, kt * kKeys,
            [&] { load_k_half(kt + 1, stage ^ 1, 1); });
-      if (stream == 1) __builtin_amdgcn_s_setprio(0);
       load_v_half(kt + 1, stage ^ 1, 0);
       step(BoolTag<false>{}, smem + stage * TL::kStage, 1, kt * kKeys + 32,
            [&] { load_v_half(kt + 1, stage ^ 1, 1); });

@@ -359,17 +359,12 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
     }
   };
   // An interior tile is never the last one and its successor is full (the last
-  // full tile before a ragged end goes to the tail loop).  The younger wave of
-  // each SIMD (waves 4..7) runs the first step at raised issue priority: at
-  // equal priority the older wave wins most issue slots and then idles at the
-  // barrier while the other finishes alone.
+  // full tile before a ragged end goes to the tail loop).
   auto interior_tile = [&](int kt, const uint8_t* k_lds, uint8_t* next) {
     if (wave_active) {
       const uint8_t* v_lds = k_lds + TL::kTileBytes;
       load_quarter(kt + 1, next, 0, 0);
-      if (wave >= kWaves / 2) __builtin_amdgcn_s_setprio(1);
       step(BoolTag<false>{}, k_lds, v_lds, 0, kt * kKeys, [&] { load_quarter(kt + 1, next, 0, 1); });
-      if (wave >= kWaves / 2) __builtin_amdgcn_s_setprio(0);
       load_quarter(kt + 1, next, 1, 0);
       step(BoolTag<false>{}, k_lds, v_lds, 1, kt * kKeys + 32, [&] { load_quarter(kt + 1, next, 1, 1); });
     } else {
