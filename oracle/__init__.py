@@ -12,10 +12,13 @@ from .diffattn_oracle import (  # noqa: F401
     v1_forward,
     v1_head,
     v1_norm,
+    v2_backward,
     v2_combine,
     v2_decode,
     v2_forward,
+    v2_forward_stats,
     v2_heads,
     v2_sequence,
+    v2_sequence_backward,
     v2_varlen_forward,
 )

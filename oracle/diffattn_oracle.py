@@ -38,6 +38,18 @@ Readings where the pages are silent (each one is an argument, not a constant)
 * sigmoid(x) = 1 / (1 + e^-x), evaluated in its overflow-free form.
 * A decode sequence with no cached positions gives a zero output.
 
+V2 backward (training)
+----------------------
+The pages quote V2's throughput for pretraining but print no gradient.  The
+backward functions below are the chain rule through the V2 forward above,
+written term by term: with sigma = sigmoid(logit), the even head of pair p
+receives dO_2p = dOut_p and the odd head dO_2p+1 = -sigma * dOut_p;
+dlogit_p = -sigma (1 - sigma) <dOut_p, O_2p+1>; each head then takes the usual
+softmax-attention backward (dP = dO V^T, dS = P o (dP - rowsum(dO o O)),
+dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO), and the gradients of the
+query heads sharing a KV head add up.  Pinned against central finite
+differences of ``v2_forward``.
+
 Parity status: every public function here is pinned by tests/test_oracle_pins.py.
 """
 from __future__ import annotations
@@ -270,3 +282,82 @@ def v2_decode(q, k_cache, v_cache, logit, cache_len=None, scale: float | None = 
         O = v2_heads(q[b][None], kb, vb, rows=np.array([0]), causal=False, scale=scale)
         out[i] = v2_combine(O, logit[b][None])[0]
     return out
+
+
+# ---------------------------------------------------------------------------
+# V2 backward (the chain rule through v2_forward; see the module docstring)
+# ---------------------------------------------------------------------------
+
+def v2_sequence_backward(q, k, v, logit, dout, causal: bool = True, scale: float | None = None):
+    """Gradients of sum(dout * v2_sequence(q, k, v, logit)) for one sequence.
+
+    q [T, 2h, d], k/v [T, Hkv, d], logit [T, h], dout [T, h, d].
+    Returns (dq [T, 2h, d], dk [T, Hkv, d], dv [T, Hkv, d], dlogit [T, h]).
+    """
+    q, k, v, logit, dout = (_f64(a) for a in (q, k, v, logit, dout))
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv or Hq % 2:
+        raise ValueError("Hq must be even and a multiple of Hkv")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rows = np.arange(T)
+    sig = sigmoid(logit)                                   # [T, h]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dlogit = np.zeros_like(logit)
+    for j in range(Hq):
+        kv = gqa_kv_head(j, Hq, Hkv)
+        p = _attention_map(q[:, j], k[:, kv], rows, scale, causal)   # P_j  [T, T]
+        o = p @ v[:, kv]                                             # O_j  [T, d]
+        if j % 2 == 0:
+            do = dout[:, j // 2]                                     # dO of the even head
+        else:
+            do = -sig[:, j // 2, None] * dout[:, j // 2]             # dO of the odd head
+            dlogit[:, j // 2] = -sig[:, j // 2] * (1.0 - sig[:, j // 2]) * np.sum(
+                dout[:, j // 2] * o, axis=-1)
+        dp = do @ v[:, kv].T                                         # dL/dP
+        dsum = np.sum(do * o, axis=-1, keepdims=True)                # rowsum(dO o O)
+        ds = p * (dp - dsum)                                         # dL/dS (softmax backward)
+        dq[:, j] = scale * (ds @ k[:, kv])
+        dk[:, kv] += scale * (ds.T @ q[:, j])
+        dv[:, kv] += p.T @ do
+    return dq, dk, dv, dlogit
+
+
+def v2_backward(q, k, v, logit, dout, causal: bool = True, scale: float | None = None):
+    """Padded batch: q [B, T, 2h, d], k/v [B, T, Hkv, d], logit [B, T, h], dout [B, T, h, d].
+
+    Returns (dq, dk, dv, dlogit) shaped like (q, k, v, logit).
+    """
+    q, k, v, logit, dout = (_f64(a) for a in (q, k, v, logit, dout))
+    outs = [v2_sequence_backward(q[b], k[b], v[b], logit[b], dout[b], causal, scale)
+            for b in range(q.shape[0])]
+    return tuple(np.stack([o[i] for o in outs]) for i in range(4))
+
+
+def v2_forward_stats(q, k, v, causal: bool = True, scale: float | None = None):
+    """Per-head outputs and log-sum-exp of one padded batch, as a training forward keeps them.
+
+    Returns (O [B, T, 2h, d], lse [B, T, 2h]) with lse = log sum_k exp(q.k * scale) over
+    the visible keys (natural log).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    O = np.empty((B, T, Hq, v.shape[-1]))
+    lse = np.empty((B, T, Hq))
+    rows = np.arange(T)
+    for b in range(B):
+        for j in range(Hq):
+            kv = gqa_kv_head(j, Hq, Hkv)
+            s = (q[b, :, j] @ k[b, :, kv].T) * scale
+            if causal:
+                s = np.where(rows[None, :] > rows[:, None], -np.inf, s)
+            m = np.max(s, axis=-1, keepdims=True)
+            e = np.exp(s - m)
+            l = np.sum(e, axis=-1, keepdims=True)
+            O[b, :, j] = (e / l) @ v[b, :, kv]
+            lse[b, :, j] = (m + np.log(l))[:, 0]
+    return O, lse

@@ -365,3 +365,86 @@ def test_sigmoid_is_overflow_free_and_symmetric():
     assert np.all(np.isfinite(s))
     np.testing.assert_allclose(s, expit(x), rtol=1e-15, atol=0)
     np.testing.assert_allclose(s + oracle.sigmoid(-x), 1.0, rtol=0, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# V2 backward (chain rule through the forward; pinned by finite differences)
+# ---------------------------------------------------------------------------
+
+def _v2_loss_and_grads(seed, T, Hq, Hkv, d, causal):
+    r = rng(seed)
+    q = r.normal(size=(1, T, Hq, d))
+    k = r.normal(size=(1, T, Hkv, d))
+    v = r.normal(size=(1, T, Hkv, d))
+    logit = r.normal(size=(1, T, Hq // 2))
+    dout = r.normal(size=(1, T, Hq // 2, d))
+    loss = lambda *a: float(np.sum(dout * oracle.v2_forward(*a, causal=causal)))
+    return (q, k, v, logit, dout), loss
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (8, 2), (4, 1)])
+def test_v2_backward_matches_central_differences_everywhere(causal, Hq, Hkv):
+    # Every element of every gradient against a central difference of the forward
+    # oracle (step 1e-5: truncation ~1e-10, rounding ~1e-11 at these magnitudes).
+    (q, k, v, logit, dout), loss = _v2_loss_and_grads(30 + Hq + Hkv, 5, Hq, Hkv, 3, causal)
+    grads = oracle.v2_backward(q, k, v, logit, dout, causal=causal)
+    args = [q, k, v, logit]
+    h = 1e-5
+    for which, g in enumerate(grads):
+        fd = np.empty_like(g)
+        for idx in np.ndindex(*g.shape):
+            plus = [a.copy() for a in args]
+            minus = [a.copy() for a in args]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            fd[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        np.testing.assert_allclose(g, fd, rtol=0, atol=2e-8)
+
+
+def test_v2_backward_key_gradient_sums_to_zero_over_keys():
+    # Adding one vector to every key shifts a query's scores by a constant, which the
+    # softmax ignores; so for each KV head the key gradients sum to zero.
+    (q, k, v, logit, dout), _ = _v2_loss_and_grads(40, 19, 8, 2, 6, True)
+    _, dk, _, _ = oracle.v2_backward(q, k, v, logit, dout)
+    np.testing.assert_allclose(dk.sum(axis=1), 0.0, atol=1e-12)
+    assert np.abs(dk).max() > 1e-2
+
+
+def test_v2_backward_single_token_closed_form():
+    # One token: every map is the single weight 1, so S has no influence (dq = dk = 0),
+    # out_p = v_kv(p) (1 - sigmoid), and dv sums dout_p (1 - sigmoid(logit_p)) over the
+    # pairs of each KV head; dlogit_p = -sigmoid'(logit_p) <dout_p, v_kv>.
+    (q, k, v, logit, dout), _ = _v2_loss_and_grads(41, 1, 8, 2, 4, True)
+    dq, dk, dv, dlogit = oracle.v2_backward(q, k, v, logit, dout)
+    # (zero up to the rounding of dO.v against rowsum(dO o O))
+    np.testing.assert_allclose(dq, 0.0, atol=1e-15)
+    np.testing.assert_allclose(dk, 0.0, atol=1e-15)
+    s = expit(logit[0, 0])
+    for g in range(2):
+        pairs = range(2 * g, 2 * g + 2)  # Hq/Hkv = 4 query heads = 2 pairs per KV head
+        ref = sum(dout[0, 0, p] * (1 - s[p]) for p in pairs)
+        np.testing.assert_allclose(dv[0, 0, g], ref, rtol=1e-14, atol=1e-14)
+    for p in range(4):
+        ref = -s[p] * (1 - s[p]) * np.dot(dout[0, 0, p], v[0, 0, p // 2])
+        np.testing.assert_allclose(dlogit[0, 0, p], ref, rtol=1e-14, atol=1e-15)
+
+
+def test_v2_backward_zero_upstream_gives_zero():
+    (q, k, v, logit, dout), _ = _v2_loss_and_grads(42, 9, 4, 2, 4, True)
+    for g in oracle.v2_backward(q, k, v, logit, np.zeros_like(dout)):
+        np.testing.assert_array_equal(g, 0.0)
+
+
+def test_v2_forward_stats_match_library_attention_and_logsumexp():
+    # Per-head O against torch SDPA (float64), lse against torch.logsumexp of the
+    # masked, scaled scores.
+    q, k, v, _ = v2_rand(43, T=21, Hq=8, Hkv=2)
+    O, lse = oracle.v2_forward_stats(q, k, v)
+    np.testing.assert_allclose(O[0], sdpa(q[0], k[0], v[0], True, gqa=True), rtol=0, atol=1e-13)
+    tq = torch.from_numpy(q[0]).permute(1, 0, 2)                       # [Hq, T, d]
+    tk = torch.from_numpy(np.repeat(k[0], 4, axis=1)).permute(1, 0, 2)  # GQA groups of 4
+    s = tq @ tk.transpose(1, 2) / math.sqrt(q.shape[-1])
+    s = s.masked_fill(torch.ones(21, 21, dtype=torch.bool).triu(1), float("-inf"))
+    ref = torch.logsumexp(s, dim=-1).T.numpy()
+    np.testing.assert_allclose(lse[0], ref, rtol=0, atol=1e-13)
