@@ -11,6 +11,9 @@ arithmetic runs in the library's kernels; there is no fallback path.
     v2_fwd      V2: GQA attention over 2h query heads, O_even - sigmoid(logit) O_odd
                 (padded or packed/varlen batches)
     v2_decode   V2 decode step against a KV cache
+    v2_fwd_train / v2_bwd
+                V2 training forward (also keeps per-head O and log-sum-exp) and
+                the backward: gradients of q, k, v and the lambda logits
     lambda_init 0.8 - 0.6 exp(-0.3 (l - 1))
 """
 from __future__ import annotations
@@ -22,9 +25,12 @@ __all__ = [
     "v1_fwd",
     "v2_fwd",
     "v2_decode",
+    "v2_fwd_train",
+    "v2_bwd",
     "lambda_init",
     "v1_workspace_bytes",
     "v2_decode_workspace_bytes",
+    "v2_bwd_workspace_bytes",
     "DiffAttnError",
 ]
 
@@ -219,3 +225,84 @@ def v2_decode(q, k_cache, v_cache, logit, cache_len=None, scale: float | None = 
             _stream(dev))
     _lib.check("diffattn_v2_decode", rc)
     return out
+
+
+def _v2_padded_check(q, k, v, logit):
+    torch = _torch()
+    dev = q.device
+    _check_tensor("q", q, dtype=torch.bfloat16, dim=4)
+    _check_tensor("k", k, dtype=torch.bfloat16, dim=4, device=dev)
+    _check_tensor("v", v, dtype=torch.bfloat16, dim=4, device=dev)
+    _check_tensor("logit", logit, dtype=torch.float32, dim=3, device=dev)
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    B, T, Hq, d = q.shape
+    if tuple(k.shape[:2]) != (B, T) or k.shape[3] != d:
+        raise ValueError("k/v shape does not match q")
+    if Hq % 2:
+        raise ValueError("Hq must be even")
+    if tuple(logit.shape) != (B, T, Hq // 2):
+        raise ValueError(f"logit must have shape {(B, T, Hq // 2)}")
+    return B, T, Hq, k.shape[2], d
+
+
+def v2_fwd_train(q, k, v, logit, causal: bool = True, scale: float | None = None):
+    """DIFF V2 training forward (padded batch).
+
+    q [B,T,Hq,d], k/v [B,T,Hkv,d] bf16, logit [B,T,Hq/2] fp32 ->
+    (out [B,T,Hq/2,d] bf16, o_heads [B,T,Hq,d] bf16, lse [B,T,Hq] fp32).
+    """
+    torch = _torch()
+    dev = q.device
+    B, T, Hq, Hkv, d = _v2_padded_check(q, k, v, logit)
+    out = torch.empty((B, T, Hq // 2, d), dtype=torch.bfloat16, device=dev)
+    o_heads = torch.empty((B, T, Hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        rc = lib.diffattn_v2_fwd_train(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(logit), _ptr(out), _ptr(o_heads), _ptr(lse), B, T, Hq,
+            Hkv, d, float(scale or 0.0), 1 if causal else 0, DIFFATTN_BF16, _stream(dev))
+    _lib.check("diffattn_v2_fwd_train", rc)
+    return out, o_heads, lse
+
+
+def v2_bwd_workspace_bytes(B, T, Hq, Hkv, d) -> int:
+    return int(_lib.load().diffattn_v2_bwd_workspace_bytes(B, T, Hq, Hkv, d))
+
+
+def v2_bwd(q, k, v, logit, o_heads, lse, dout, causal: bool = True, scale: float | None = None,
+           workspace=None):
+    """DIFF V2 backward (padded batch): gradients of sum(dout * out).
+
+    o_heads, lse from v2_fwd_train on the same inputs; dout [B,T,Hq/2,d] bf16 ->
+    (dq [B,T,Hq,d], dk [B,T,Hkv,d], dv [B,T,Hkv,d], dlogit [B,T,Hq/2]), all fp32.
+    """
+    torch = _torch()
+    dev = q.device
+    B, T, Hq, Hkv, d = _v2_padded_check(q, k, v, logit)
+    _check_tensor("o_heads", o_heads, dtype=torch.bfloat16, dim=4, device=dev)
+    _check_tensor("lse", lse, dtype=torch.float32, dim=3, device=dev)
+    _check_tensor("dout", dout, dtype=torch.bfloat16, dim=4, device=dev)
+    if tuple(o_heads.shape) != (B, T, Hq, d) or tuple(lse.shape) != (B, T, Hq):
+        raise ValueError("o_heads / lse shapes do not match q")
+    if tuple(dout.shape) != (B, T, Hq // 2, d):
+        raise ValueError("dout must have shape [B, T, Hq/2, d]")
+    dq = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
+    dk = torch.empty((B, T, Hkv, d), dtype=torch.float32, device=dev)
+    dv = torch.empty((B, T, Hkv, d), dtype=torch.float32, device=dev)
+    dlogit = torch.empty((B, T, Hq // 2), dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    need = int(lib.diffattn_v2_bwd_workspace_bytes(B, T, Hq, Hkv, d))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _check_tensor("workspace", workspace, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        rc = lib.diffattn_v2_bwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(logit), _ptr(o_heads), _ptr(lse), _ptr(dout), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(dlogit), _ptr(workspace), ws_bytes, B, T, Hq, Hkv, d,
+            float(scale or 0.0), 1 if causal else 0, DIFFATTN_BF16, _stream(dev))
+    _lib.check("diffattn_v2_bwd", rc)
+    return dq, dk, dv, dlogit

@@ -51,6 +51,28 @@ long long prod(std::initializer_list<long long> xs) {
   return r;
 }
 
+// Head-layout and dtype checks shared by the V2 prefill, training-forward and
+// backward entry points; returns DIFFATTN_OK or a failure code.
+int v2_heads_check(const char* fn, int Hq, int Hkv, int d, float scale, int causal,
+                   diffattn_dtype dtype) {
+  if (Hq <= 0 || Hkv <= 0 || d <= 0)
+    return fail(DIFFATTN_E_INVALID, "%s: bad head sizes Hq=%d Hkv=%d d=%d", fn, Hq, Hkv, d);
+  if (Hq % 2) return fail(DIFFATTN_E_INVALID, "%s: Hq=%d must be even (pairs of heads)", fn, Hq);
+  if (Hq % Hkv)
+    return fail(DIFFATTN_E_INVALID, "%s: Hq=%d must be a multiple of Hkv=%d", fn, Hq, Hkv);
+  if ((Hq / Hkv) % 2)
+    return fail(DIFFATTN_E_INVALID,
+                "%s: Hq/Hkv=%d must be even so both heads of a pair share one KV head", fn,
+                Hq / Hkv);
+  if (causal != 0 && causal != 1) return fail(DIFFATTN_E_INVALID, "%s: causal must be 0 or 1", fn);
+  if (!isfinite(scale)) return fail(DIFFATTN_E_INVALID, "%s: scale must be finite", fn);
+  if (dtype != DIFFATTN_BF16)
+    return fail(dtype == DIFFATTN_F32 ? DIFFATTN_E_UNSUPPORTED : DIFFATTN_E_INVALID,
+                "%s: only bf16 is supported", fn);
+  if (d != 64 && d != 128) return fail(DIFFATTN_E_UNSUPPORTED, "%s: d=%d not in {64, 128}", fn, d);
+  return DIFFATTN_OK;
+}
+
 bool v1_shape_supported(int d, int dv, diffattn_dtype dt) {
   if (dt == DIFFATTN_F32) return d >= 16 && d <= 128 && d % 16 == 0 && dv >= 16 && dv <= 256 && dv % 16 == 0;
   if (dt == DIFFATTN_BF16) return (d == 128 && dv == 256) || (d == 64 && dv == 128);
@@ -130,21 +152,8 @@ int diffattn_v2_fwd(const void* q, const void* k, const void* v, const float* la
   const char* fn = "diffattn_v2_fwd";
   if (!q || !k || !v || !lambda_logit || !out)
     return fail(DIFFATTN_E_INVALID, "%s: null tensor pointer", fn);
-  if (Hq <= 0 || Hkv <= 0 || d <= 0)
-    return fail(DIFFATTN_E_INVALID, "%s: bad head sizes Hq=%d Hkv=%d d=%d", fn, Hq, Hkv, d);
-  if (Hq % 2) return fail(DIFFATTN_E_INVALID, "%s: Hq=%d must be even (pairs of heads)", fn, Hq);
-  if (Hq % Hkv)
-    return fail(DIFFATTN_E_INVALID, "%s: Hq=%d must be a multiple of Hkv=%d", fn, Hq, Hkv);
-  if ((Hq / Hkv) % 2)
-    return fail(DIFFATTN_E_INVALID,
-                "%s: Hq/Hkv=%d must be even so both heads of a pair share one KV head", fn,
-                Hq / Hkv);
-  if (causal != 0 && causal != 1) return fail(DIFFATTN_E_INVALID, "%s: causal must be 0 or 1", fn);
-  if (!isfinite(scale)) return fail(DIFFATTN_E_INVALID, "%s: scale must be finite", fn);
-  if (dtype != DIFFATTN_BF16)
-    return fail(dtype == DIFFATTN_F32 ? DIFFATTN_E_UNSUPPORTED : DIFFATTN_E_INVALID,
-                "%s: only bf16 is supported", fn);
-  if (d != 64 && d != 128) return fail(DIFFATTN_E_UNSUPPORTED, "%s: d=%d not in {64, 128}", fn, d);
+  const int rc = v2_heads_check(fn, Hq, Hkv, d, scale, causal, dtype);
+  if (rc != DIFFATTN_OK) return rc;
   int nseq_eff, maxlen;
   if (cu_seqlens) {
     if (nseq < 0 || max_seqlen < 0)
@@ -179,6 +188,96 @@ int diffattn_v2_fwd(const void* q, const void* k, const void* v, const float* la
   a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
   a.causal = causal;
   return from_hip(diffattn::launch_v2_prefill(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int diffattn_v2_fwd_train(const void* q, const void* k, const void* v, const float* lambda_logit,
+                          void* out, void* o_heads, float* lse, int B, int T, int Hq, int Hkv,
+                          int d, float scale, int causal, diffattn_dtype dtype, void* stream) {
+  const char* fn = "diffattn_v2_fwd_train";
+  if (!q || !k || !v || !lambda_logit || !out || !o_heads || !lse)
+    return fail(DIFFATTN_E_INVALID, "%s: null tensor pointer", fn);
+  const int rc = v2_heads_check(fn, Hq, Hkv, d, scale, causal, dtype);
+  if (rc != DIFFATTN_OK) return rc;
+  if (B < 0 || T < 0) return fail(DIFFATTN_E_INVALID, "%s: B=%d T=%d must be >= 0", fn, B, T);
+  if (prod({B, T, Hq, d}) > (1LL << 40)) return fail(DIFFATTN_E_INVALID, "%s: problem too large", fn);
+  const void* ptrs[] = {q, k, v, out, o_heads};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(DIFFATTN_E_ALIGN, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (!aligned4(lambda_logit) || !aligned4(lse))
+    return fail(DIFFATTN_E_ALIGN, "%s: lambda_logit and lse must be 4-byte aligned", fn);
+  if (B == 0 || T == 0) return ok();
+  diffattn::V2Args a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.logit = lambda_logit;
+  a.out = static_cast<uint16_t*>(out);
+  a.cu_seqlens = nullptr;
+  a.nseq = B;
+  a.max_seqlen = T;
+  a.T = T;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+  a.causal = causal;
+  a.o_heads = static_cast<uint16_t*>(o_heads);
+  a.lse = lse;
+  return from_hip(diffattn::launch_v2_prefill(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+size_t diffattn_v2_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d) {
+  if (B < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || Hq % 2 || Hq % Hkv || (Hq / Hkv) % 2) return 0;
+  if (d != 64 && d != 128) return 0;
+  if (prod({B, T, Hq, d}) < 0) return 0;
+  return diffattn::v2_bwd_workspace_bytes(B, T, Hq);
+}
+
+int diffattn_v2_bwd(const void* q, const void* k, const void* v, const float* lambda_logit,
+                    const void* o_heads, const float* lse, const void* dout, float* dq, float* dk,
+                    float* dv, float* dlambda_logit, void* workspace, size_t workspace_bytes,
+                    int B, int T, int Hq, int Hkv, int d, float scale, int causal,
+                    diffattn_dtype dtype, void* stream) {
+  const char* fn = "diffattn_v2_bwd";
+  if (!q || !k || !v || !lambda_logit || !o_heads || !lse || !dout || !dq || !dk || !dv ||
+      !dlambda_logit)
+    return fail(DIFFATTN_E_INVALID, "%s: null tensor pointer", fn);
+  const int rc = v2_heads_check(fn, Hq, Hkv, d, scale, causal, dtype);
+  if (rc != DIFFATTN_OK) return rc;
+  if (B < 0 || T < 0) return fail(DIFFATTN_E_INVALID, "%s: B=%d T=%d must be >= 0", fn, B, T);
+  if (prod({B, T, Hq, d}) > (1LL << 40)) return fail(DIFFATTN_E_INVALID, "%s: problem too large", fn);
+  const void* ptrs[] = {q, k, v, o_heads, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(DIFFATTN_E_ALIGN, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (!aligned4(lambda_logit) || !aligned4(lse) || !aligned4(dlambda_logit))
+    return fail(DIFFATTN_E_ALIGN, "%s: lambda_logit, lse and dlambda_logit must be 4-byte aligned", fn);
+  if (B == 0 || T == 0) return ok();
+  const size_t need = diffattn_v2_bwd_workspace_bytes(B, T, Hq, Hkv, d);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DIFFATTN_E_WORKSPACE, "%s: workspace of %zu bytes required (got %zu%s)", fn, need,
+                workspace_bytes, workspace ? "" : ", NULL");
+  if (!aligned16(workspace)) return fail(DIFFATTN_E_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  diffattn::V2BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.logit = lambda_logit;
+  a.o_heads = static_cast<const uint16_t*>(o_heads);
+  a.lse = lse;
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dlogit = dlambda_logit;
+  a.delta = static_cast<float*>(workspace);
+  a.B = B;
+  a.T = T;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+  a.causal = causal;
+  return from_hip(diffattn::launch_v2_backward(a, static_cast<hipStream_t>(stream)), fn);
 }
 
 size_t diffattn_v2_decode_workspace_bytes(int B, int S_max, int Hq, int Hkv, int d) {

@@ -35,6 +35,27 @@ struct V2Args {
   int Hq, Hkv, d;
   float scale;              // softmax scale (> 0)
   int causal;
+  uint16_t* o_heads;        // bf16 [tokens, Hq, d] per-head outputs, or nullptr (training forward)
+  float* lse;               // fp32 [tokens, Hq] natural-log log-sum-exp, or nullptr
+};
+
+// V2 backward (padded batches).  Gradients of sum(dout * out) of the V2 forward.
+struct V2BwdArgs {
+  const uint16_t* q;        // bf16 [B, T, Hq, d]
+  const uint16_t* k;        // bf16 [B, T, Hkv, d]
+  const uint16_t* v;        // bf16 [B, T, Hkv, d]
+  const float* logit;       // fp32 [B, T, Hq/2]
+  const uint16_t* o_heads;  // bf16 [B, T, Hq, d]  (from the training forward)
+  const float* lse;         // fp32 [B, T, Hq]     (from the training forward)
+  const uint16_t* dout;     // bf16 [B, T, Hq/2, d]
+  float* dq;                // fp32 [B, T, Hq, d]
+  float* dk;                // fp32 [B, T, Hkv, d]
+  float* dv;                // fp32 [B, T, Hkv, d]
+  float* dlogit;            // fp32 [B, T, Hq/2]
+  float* delta;             // fp32 workspace [B, T, Hq]: rowsum(dO_j o O_j)
+  int B, T, Hq, Hkv, d;
+  float scale;
+  int causal;
 };
 
 struct DecodeArgs {
@@ -58,6 +79,9 @@ hipError_t launch_v1_f32(const V1Args& a, hipStream_t stream);
 size_t v1_bf16_workspace_bytes(int B, int T, int H, int d, int dv);
 hipError_t launch_v1_bf16(const V1Args& a, void* workspace, hipStream_t stream);
 hipError_t launch_v2_prefill(const V2Args& a, hipStream_t stream);
+// V2 backward workspace: per-row delta, log2 lse and sigmoid (see v2_backward.hip).
+size_t v2_bwd_workspace_bytes(int B, int T, int Hq);
+hipError_t launch_v2_backward(const V2BwdArgs& a, hipStream_t stream);
 hipError_t launch_v2_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace diffattn

@@ -1,0 +1,577 @@
+// DIFF V2 backward on gfx950 (padded batches): gradients of sum(dout * out) of
+// the V2 forward
+//     O_j[t]   = softmax_k(q_{t,j} . k_{k,kv(j)} * scale) v_{k,kv(j)}    (causal: k <= t)
+//     out[t,p] = O_2p[t] - sigmoid(logit[t,p]) * O_2p+1[t]
+// ("Differential Transformer V2" summary (pogovet.com), 상세 정리 §1 and §4).
+// The pages print no gradient; this is the chain rule through that forward.
+// With s = sigmoid(logit):
+//     dO_2p = dout_p,   dO_2p+1 = -s dout_p,   dlogit_p = -s (1 - s) <dout_p, O_2p+1>,
+// and per query head j the softmax-attention backward
+//     D_j = rowsum(dO_j o O_j),  dP = dO_j V^T,  dS = P o (dP - D_j),
+//     dQ_j = scale dS K,  dK += scale dS^T Q_j,  dV += P^T dO_j,
+// with P recomputed from the forward's log-sum-exp.  Both heads of a pair
+// share dout_p, so dout_p V^T is formed once per pair.
+//
+// Three kernels:
+//  * v2_bwd_pre_kernel: per (token, pair) D_2p, D_2p+1, s, dlogit, and the
+//    log-sum-exp in log2 units, stored [B][head][T rounded up to 64] so that a
+//    query tile's row values are contiguous;
+//  * v2_bwd_dq_kernel: the forward's decomposition (a wave owns one pair and
+//    16 query rows, lanes own query columns; K and V tiles stream through LDS):
+//    S^T = K Q^T, dP^T = V dout^T, dS^T, dQ^T += K^T dS^T;
+//  * v2_bwd_dkdv_kernel: a workgroup owns 64 keys of one KV head; wave
+//    (key block, even/odd) keeps its 16 keys' K and V fragments in registers,
+//    lanes own key columns, and the Q and dout tiles of every pair and query
+//    tile stream through LDS: S = Q K^T, dP = dout V^T, dS, dV += P'^T dout
+//    (P' = P or -s P), dK += dS^T Q; the even and odd waves' sums are added at
+//    the end.
+// All MFMA work is 16x16x32 bf16 with fp32 accumulation; P and dS are rounded
+// to bf16 for the second product of each pair, as in the forward.
+#include <math.h>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace diffattn {
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kKeys = 64;   // keys per staged tile (dq) / keys per workgroup (dkdv)
+constexpr int kQRows = 64;  // query rows per staged tile (dkdv)
+constexpr int kRows = 16;   // query rows per wave (dq)
+
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
+template <int D>
+struct BTile {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;  // 16-byte chunks per row
+  static constexpr int kBytes = 64 * kRowBytes;
+  static constexpr int kInstr = kBytes / 1024;
+};
+
+// Two LDS layouts of a 64-row bf16 tile (row-major, swizzled):
+//  * rows: 16-byte chunk c of row r at position c ^ (r mod nchunks), for
+//    16-byte row reads (an MFMA operand whose k index runs along a row);
+//  * trans: 32-byte chunk c of row r at position c ^ (r mod D/16), for the
+//    transposing read (an operand whose k index runs down the rows).
+template <int D>
+__device__ __forceinline__ int rows_offset(int row, int chunk) {
+  return row * BTile<D>::kRowBytes + ((chunk ^ (row & (BTile<D>::kChunks - 1))) << 4);
+}
+template <int D>
+__device__ __forceinline__ int trans_offset(int row, int byte_in_row) {
+  constexpr int n32 = D / 16;
+  const int c32 = byte_in_row >> 5;
+  return row * BTile<D>::kRowBytes + ((c32 ^ (row & (n32 - 1))) << 5) + (byte_in_row & 31);
+}
+
+// Direct-to-LDS load of a 64-row tile: rows r0 .. r0+63 of a bf16 matrix whose
+// consecutive rows are `stride` elements apart, rows >= n_valid clamped to the
+// last valid row (their values are masked by the caller).  TRANS selects the
+// layout.  Each wave issues kInstr / kWaves loads of 1 KiB.
+template <int D, bool TRANS>
+__device__ __forceinline__ void load_tile(const uint16_t* base, size_t stride, int n_valid,
+                                          uint8_t* lds, int wave, int lane) {
+  using TL = BTile<D>;
+#pragma unroll
+  for (int j = 0; j < (TL::kInstr + kWaves - 1) / kWaves; ++j) {
+    const int blk = wave + j * kWaves;
+    if (TL::kInstr % kWaves != 0 && blk >= TL::kInstr) break;
+    const int off = blk * 1024 + lane * 16;  // LDS byte this lane fills
+    const int r = off / TL::kRowBytes;
+    const int pos = (off % TL::kRowBytes) >> 4;
+    int lc;  // logical 16-byte chunk stored at that position
+    if (TRANS) {
+      constexpr int n32 = D / 16;
+      lc = (((pos >> 1) ^ (r & (n32 - 1))) << 1) | (pos & 1);
+    } else {
+      lc = pos ^ (r & (TL::kChunks - 1));
+    }
+    const size_t row = (size_t)min(r, n_valid - 1);
+    dma16(base, (uint32_t)((row * stride + lc * 8) * 2), lds + blk * 1024);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Preprocessing: one wave per (token, pair).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void v2_bwd_pre_kernel(V2BwdArgs a, int Tp, float* lse2,
+                                                         float* sig) {
+  const int h = a.Hq / 2;
+  const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const long long n_items = (long long)a.B * Tp * h;
+  if (item >= n_items) return;
+  const int p = (int)(item % h);
+  const long long bt = item / h;
+  const int t = (int)(bt % Tp);
+  const int b = (int)(bt / Tp);
+  const size_t ws = ((size_t)b * a.Hq + 2 * p) * Tp + t;  // [b][2p][t]
+  const size_t wsig = ((size_t)b * h + p) * Tp + t;
+  if (t >= a.T) {  // padding rows: finite zeros (the tiles read them and mask them)
+    if (lane == 0) {
+      a.delta[ws] = 0.f;
+      a.delta[ws + Tp] = 0.f;
+      lse2[ws] = 0.f;
+      lse2[ws + Tp] = 0.f;
+      sig[wsig] = 0.f;
+    }
+    return;
+  }
+  const size_t tok = (size_t)b * a.T + t;
+  constexpr int E = D / 64;  // elements per lane
+  float de = 0.f, dod = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int c = lane * E + e;
+    const float g = bf16_to_f32(a.dout[(tok * h + p) * D + c]);
+    de = fmaf(g, bf16_to_f32(a.o_heads[(tok * a.Hq + 2 * p) * D + c]), de);
+    dod = fmaf(g, bf16_to_f32(a.o_heads[(tok * a.Hq + 2 * p + 1) * D + c]), dod);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    de += __shfl_xor(de, m);
+    dod += __shfl_xor(dod, m);
+  }
+  if (lane == 0) {
+    const float s = sigmoid_f32(a.logit[tok * h + p]);
+    a.delta[ws] = de;             // <dO_2p, O_2p> with dO_2p = dout_p
+    a.delta[ws + Tp] = -s * dod;  // <dO_2p+1, O_2p+1> with dO_2p+1 = -s dout_p
+    a.dlogit[tok * h + p] = -s * (1.f - s) * dod;
+    lse2[ws] = a.lse[tok * a.Hq + 2 * p] * kLog2e;
+    lse2[ws + Tp] = a.lse[tok * a.Hq + 2 * p + 1] * kLog2e;
+    sig[wsig] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: a wave owns one pair and 16 query rows; K and V tiles of 64 keys stream
+// through LDS (K in the transposing layout: it is read both ways).
+// ---------------------------------------------------------------------------
+template <int D, int PW, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, int Tp,
+                                                                const float* lse2,
+                                                                const float* sig) {
+  using TL = BTile<D>;
+  constexpr int QSUB = kWaves / PW;
+  constexpr int QTILE = kRows * QSUB;
+  constexpr int NC = D / 32;
+  constexpr int NDB = D / 16;
+  __shared__ __align__(16) uint8_t kbuf0[TL::kBytes];
+  __shared__ __align__(16) uint8_t kbuf1[TL::kBytes];
+  __shared__ __align__(16) uint8_t vbuf0[TL::kBytes];
+  __shared__ __align__(16) uint8_t vbuf1[TL::kBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+
+  const int n_hg = a.Hq / (2 * PW);
+  const int hg = blockIdx.x % n_hg;
+  const int t = blockIdx.x / n_hg;
+  const int nt = (a.T + QTILE - 1) / QTILE;
+  const int b = t / nt;
+  const int qt = nt - 1 - (t - b * nt);  // longest first
+  const int T = a.T;
+  const int hpairs = a.Hq / 2;
+  const int group = a.Hq / a.Hkv;
+  const int p = hg * PW + (wave % PW);
+  const int kv = (hg * PW * 2) / group;
+  const int q_lo = qt * QTILE + (wave / PW) * kRows;
+  const bool wave_active = q_lo < T;
+  const int q_end_block = min(qt * QTILE + QTILE, T);
+  const int n_kt = CAUSAL ? (q_end_block - 1) / kKeys + 1 : (T + kKeys - 1) / kKeys;
+  const int wave_key_end = CAUSAL ? min(q_lo + kRows, T) : T;
+
+  const float cs = a.scale * kLog2e;
+  const int row = q_lo + c16;  // this lane's query column
+  const int rowc = min(row, T - 1);
+  const size_t tok = (size_t)b * T + rowc;
+  // B operands: Q^T of both heads and dout^T of the pair
+  u32x4 qf[2][NC], of[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      qf[nb][c] = ldg128(a.q + (tok * a.Hq + 2 * p + nb) * D + c * 32 + g * 8);
+    of[c] = ldg128(a.dout + (tok * hpairs + p) * D + c * 32 + g * 8);
+  }
+  float l2[2], dl[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const size_t w = ((size_t)b * a.Hq + 2 * p + nb) * Tp + rowc;
+    l2[nb] = lse2[w];
+    dl[nb] = a.delta[w];
+  }
+  const float sg = sig[((size_t)b * hpairs + p) * Tp + rowc];
+
+  const size_t kv_stride = (size_t)a.Hkv * D;
+  const uint16_t* kbase_g = a.k + ((size_t)b * T * a.Hkv + kv) * D;
+  const uint16_t* vbase_g = a.v + ((size_t)b * T * a.Hkv + kv) * D;
+  auto load = [&](int kt, uint8_t* kl, uint8_t* vl) {
+    const int r0 = kt * kKeys;
+    load_tile<D, true>(kbase_g + (size_t)r0 * kv_stride, kv_stride, T - r0, kl, wave, lane);
+    load_tile<D, false>(vbase_g + (size_t)r0 * kv_stride, kv_stride, T - r0, vl, wave, lane);
+  };
+
+  f32x4 dq[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) dq[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // transposing-read offsets of the K^T operand (as the forward's V^T)
+  const int tr_key = 4 * g + (c16 >> 2);
+  const int tr_byte = 8 * (c16 & 3);
+
+  // one 32-key step over the staged tile
+  auto step = [&](const uint8_t* kl, const uint8_t* vl, int cc, int k0, bool masked) {
+    f32x4 sacc[2][2], dpa[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      dpa[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key = cc * 32 + kb * 16 + c16;
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(kl + trans_offset<D>(key, (c * 4 + g) * 16));
+        const u32x4 vf = *reinterpret_cast<const u32x4*>(vl + rows_offset<D>(key, c * 4 + g));
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = mfma_bf16(kf, qf[nb][c], sacc[kb][nb]);
+        dpa[kb] = mfma_bf16(vf, of[c], dpa[kb]);
+      }
+    // dS^T per head, packed as the B operand of dQ^T += K^T dS^T
+    u32x4 dsf[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float v8[8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + kb * 16 + 4 * g + i;
+          float pr = fast_exp2(fmaf(sacc[kb][nb][i], cs, -l2[nb]));
+          if (masked && (key >= T || (CAUSAL && key > row))) pr = 0.f;
+          const float dpv = nb ? -sg * dpa[kb][i] : dpa[kb][i];
+          v8[kb * 4 + i] = pr * (dpv - dl[nb]);
+        }
+      dsf[nb] = u32x4{pack_bf16x2(v8[0], v8[1]), pack_bf16x2(v8[2], v8[3]),
+                      pack_bf16x2(v8[4], v8[5]), pack_bf16x2(v8[6], v8[7])};
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const uint8_t* kp = kl + trans_offset<D>(cc * 32 + tr_key, db * 32 + tr_byte);
+      const u32x2 lo = lds_read_tr16(kp);
+      const u32x2 hi = lds_read_tr16(kp + 16 * TL::kRowBytes);
+      const u32x4 kt_f = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) dq[db][nb] = mfma_bf16(kt_f, dsf[nb], dq[db][nb]);
+    }
+  };
+
+  load(0, kbuf0, vbuf0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const bool odd = kt & 1;
+    if (kt + 1 < n_kt) {
+      if (odd)
+        load(kt + 1, kbuf0, vbuf0);
+      else
+        load(kt + 1, kbuf1, vbuf1);
+    }
+    if (wave_active) {
+      const int t0 = kt * kKeys;
+      const bool masked = (t0 + kKeys > T) || (CAUSAL && t0 + kKeys - 1 > q_lo);
+      if (t0 < wave_key_end) {
+        if (odd)
+          step(kbuf1, vbuf1, 0, t0, masked);
+        else
+          step(kbuf0, vbuf0, 0, t0, masked);
+      }
+      if (t0 + 32 < wave_key_end) {
+        if (odd)
+          step(kbuf1, vbuf1, 1, t0 + 32, masked);
+        else
+          step(kbuf0, vbuf0, 1, t0 + 32, masked);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+  }
+  if (!wave_active || row >= T) return;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    float* dst = a.dq + (((size_t)b * T + row) * a.Hq + 2 * p + nb) * D + g * 4;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      f32x4 r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = dq[db][nb][i] * a.scale;
+      *reinterpret_cast<f32x4*>(dst + db * 16) = r;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV: a workgroup owns 64 keys of one KV head.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, int Tp,
+                                                                  const float* lse2,
+                                                                  const float* sig) {
+  using TL = BTile<D>;
+  constexpr int NC = D / 32;
+  constexpr int NDB = D / 16;
+  // per stage: Q of the even and odd head, dout of the pair (transposing layout,
+  // read both ways), then the rows' lse2 / delta of both heads and s (fp32 x 64)
+  constexpr int kVec = 5 * kQRows * 4;
+  constexpr int kStage = 3 * TL::kBytes + kVec;
+  __shared__ __align__(16) uint8_t st0[kStage];
+  __shared__ __align__(16) uint8_t st1[kStage];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+  const int kb = wave & 3;   // 16-key block of the workgroup's 64 keys
+  const int hh = wave >> 2;  // 0: even heads, 1: odd heads
+
+  const int T = a.T;
+  const int n_kt = (T + kKeys - 1) / kKeys;
+  const int n_qt = (T + kQRows - 1) / kQRows;
+  // blocks: key tiles with the most query tiles first, then (batch, KV head)
+  const int nbg = a.B * a.Hkv;
+  const int kt = blockIdx.x / nbg;
+  const int bg = blockIdx.x - kt * nbg;
+  const int b = bg / a.Hkv;
+  const int kvh = bg - b * a.Hkv;
+  const int group = a.Hq / a.Hkv;
+  const int npairs = group / 2;
+  const int hpairs = a.Hq / 2;
+  const int key0 = kt * kKeys;
+  const int qt0 = CAUSAL ? key0 / kQRows : 0;
+  const int n_items = npairs * (n_qt - qt0);  // (pair, query tile) items
+
+  // this wave's 16 keys: K^T and V^T B operands (lane column = key)
+  const int key = key0 + kb * 16 + c16;
+  const int keyc = min(key, T - 1);
+  const size_t kvrow = ((size_t)b * T + keyc) * a.Hkv + kvh;
+  u32x4 kf[NC], vf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    kf[c] = ldg128(a.k + kvrow * D + c * 32 + g * 8);
+    vf[c] = ldg128(a.v + kvrow * D + c * 32 + g * 8);
+  }
+  const float cs = a.scale * kLog2e;
+
+  auto load = [&](int item, uint8_t* st) {
+    const int pp = item % npairs;
+    const int qt = qt0 + item / npairs;
+    const int r0 = qt * kQRows;
+    const int je = kvh * group + 2 * pp;  // even head of the pair
+    const int pair = je / 2;
+    const size_t q_stride = (size_t)a.Hq * D;
+    const uint16_t* qe = a.q + (((size_t)b * T + r0) * a.Hq + je) * D;
+    load_tile<D, true>(qe, q_stride, T - r0, st, wave, lane);
+    load_tile<D, true>(qe + D, q_stride, T - r0, st + TL::kBytes, wave, lane);
+    const uint16_t* dsrc = a.dout + (((size_t)b * T + r0) * hpairs + pair) * D;
+    load_tile<D, true>(dsrc, (size_t)hpairs * D, T - r0, st + 2 * TL::kBytes, wave, lane);
+    // row vectors (64 floats each, padded rows included): 5 x 256 bytes
+    if (wave < 5 && lane < 16) {
+      const float* src;
+      if (wave < 2)
+        src = lse2 + ((size_t)b * a.Hq + je + wave) * Tp + r0;
+      else if (wave < 4)
+        src = a.delta + ((size_t)b * a.Hq + je + wave - 2) * Tp + r0;
+      else
+        src = sig + ((size_t)b * hpairs + pair) * Tp + r0;
+      dma16(src, (uint32_t)(lane * 16), st + 3 * TL::kBytes + wave * 256);
+    }
+  };
+
+  f32x4 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int tr_row = 4 * g + (c16 >> 2);
+  const int tr_byte = 8 * (c16 & 3);
+
+  auto work = [&](int item, const uint8_t* st) {
+    const int qt = qt0 + item / npairs;
+    const int r0 = qt * kQRows;
+    const uint8_t* ql = st + hh * TL::kBytes;  // this wave's head
+    const uint8_t* dl = st + 2 * TL::kBytes;
+    const float* vec = reinterpret_cast<const float*>(st + 3 * TL::kBytes);
+    const float* l2v = vec + hh * kQRows;
+    const float* dlv = vec + (2 + hh) * kQRows;
+    const float* sgv = vec + 4 * kQRows;
+    // S = Q K^T and dP = dout V^T: 4 query blocks x this wave's 16 keys
+    f32x4 sacc[4], dpa[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      sacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dpa[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int r = qb * 16 + c16;
+        const u32x4 qa = *reinterpret_cast<const u32x4*>(ql + trans_offset<D>(r, (c * 4 + g) * 16));
+        const u32x4 da = *reinterpret_cast<const u32x4*>(dl + trans_offset<D>(r, (c * 4 + g) * 16));
+        sacc[qb] = mfma_bf16(qa, kf[c], sacc[qb]);
+        dpa[qb] = mfma_bf16(da, vf[c], dpa[qb]);
+      }
+    }
+    // P, P' (= P, or -s P for the odd head) and dS; rows are queries 16 qb + 4 g + i
+    float pp_[4][4], ds_[4][4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(l2v + qb * 16 + 4 * g);
+      const f32x4 dlt = *reinterpret_cast<const f32x4*>(dlv + qb * 16 + 4 * g);
+      const f32x4 sg = *reinterpret_cast<const f32x4*>(sgv + qb * 16 + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = r0 + qb * 16 + 4 * g + i;
+        float pr = fast_exp2(fmaf(sacc[qb][i], cs, -l2[i]));
+        if (q >= T || key >= T || (CAUSAL && key > q)) pr = 0.f;
+        const float f = hh ? -sg[i] : 1.f;
+        pp_[qb][i] = f * pr;
+        ds_[qb][i] = pr * (f * dpa[qb][i] - dlt[i]);
+      }
+    }
+    // dV += P'^T dout and dK += dS^T Q over two 32-query k-steps; A operands
+    // from the registers above (key = row, queries 32 s + {4 g + i, 16 + 4 g + i}),
+    // B operands by transposing reads of the dout and Q tiles.
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const u32x4 pa = u32x4{pack_bf16x2(pp_[2 * s][0], pp_[2 * s][1]),
+                             pack_bf16x2(pp_[2 * s][2], pp_[2 * s][3]),
+                             pack_bf16x2(pp_[2 * s + 1][0], pp_[2 * s + 1][1]),
+                             pack_bf16x2(pp_[2 * s + 1][2], pp_[2 * s + 1][3])};
+      const u32x4 sa = u32x4{pack_bf16x2(ds_[2 * s][0], ds_[2 * s][1]),
+                             pack_bf16x2(ds_[2 * s][2], ds_[2 * s][3]),
+                             pack_bf16x2(ds_[2 * s + 1][0], ds_[2 * s + 1][1]),
+                             pack_bf16x2(ds_[2 * s + 1][2], ds_[2 * s + 1][3])};
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int off = trans_offset<D>(s * 32 + tr_row, db * 32 + tr_byte);
+        const u32x2 dlo = lds_read_tr16(dl + off);
+        const u32x2 dhi = lds_read_tr16(dl + off + 16 * TL::kRowBytes);
+        const u32x2 qlo = lds_read_tr16(ql + off);
+        const u32x2 qhi = lds_read_tr16(ql + off + 16 * TL::kRowBytes);
+        dv[db] = mfma_bf16(pa, u32x4{dlo[0], dlo[1], dhi[0], dhi[1]}, dv[db]);
+        dk[db] = mfma_bf16(sa, u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, dk[db]);
+      }
+    }
+  };
+
+  if (n_items > 0) {
+    load(0, st0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+  }
+  for (int it = 0; it < n_items; ++it) {
+    const bool odd = it & 1;
+    if (it + 1 < n_items) load(it + 1, odd ? st0 : st1);
+    if (odd)
+      work(it, st1);
+    else
+      work(it, st0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+  }
+
+  // even + odd waves' sums: the odd waves publish theirs through LDS (dK in
+  // the first stage buffer, dV in the second: [4 key blocks][NDB][64 lanes][4])
+  static_assert(4 * NDB * 64 * 16 <= kStage, "exchange must fit one stage");
+  float* xk = reinterpret_cast<float*>(st0);
+  float* xv = reinterpret_cast<float*>(st1);
+  if (hh == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      *reinterpret_cast<f32x4*>(xk + ((kb * NDB + db) * 64 + lane) * 4) = dk[db];
+      *reinterpret_cast<f32x4*>(xv + ((kb * NDB + db) * 64 + lane) * 4) = dv[db];
+    }
+  }
+  __syncthreads();
+  if (hh == 1) return;
+  // C layout: lane column = d (16 db + c16), rows = keys 4 g + i of the block
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const f32x4 ok = *reinterpret_cast<const f32x4*>(xk + ((kb * NDB + db) * 64 + lane) * 4);
+    const f32x4 ov = *reinterpret_cast<const f32x4*>(xv + ((kb * NDB + db) * 64 + lane) * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kk = key0 + kb * 16 + 4 * g + i;
+      if (kk < T) {
+        const size_t o = (((size_t)b * T + kk) * a.Hkv + kvh) * D + db * 16 + c16;
+        a.dk[o] = (dk[db][i] + ok[i]) * a.scale;
+        a.dv[o] = dv[db][i] + ov[i];
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const V2BwdArgs& a, hipStream_t stream) {
+  const int Tp = (a.T + 63) / 64 * 64;
+  float* lse2 = a.delta + (size_t)a.B * a.Hq * Tp;
+  float* sig = lse2 + (size_t)a.B * a.Hq * Tp;
+  const long long pre_items = (long long)a.B * Tp * (a.Hq / 2);
+  const long long pre_blocks = (pre_items + 3) / 4;
+  if (pre_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((v2_bwd_pre_kernel<D>), dim3((unsigned)pre_blocks), dim3(256), 0, stream, a,
+                     Tp, lse2, sig);
+  const int pairs_per_group = (a.Hq / a.Hkv) / 2;
+  const int PW = pairs_per_group % 4 == 0 ? 4 : pairs_per_group % 2 == 0 ? 2 : 1;
+  const int qtile = kRows * (kWaves / PW);
+  const long long dq_blocks = (long long)((a.T + qtile - 1) / qtile) * a.B * (a.Hq / (2 * PW));
+  const long long kv_blocks = (long long)((a.T + kKeys - 1) / kKeys) * a.B * a.Hkv;
+  if (dq_blocks > 0x7fffffffLL || kv_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+#define DQ(PWV, C)                                                                               \
+  hipLaunchKernelGGL((v2_bwd_dq_kernel<D, PWV, C>), dim3((unsigned)dq_blocks), dim3(kThreads), 0, \
+                     stream, a, Tp, (const float*)lse2, (const float*)sig)
+  if (a.causal) {
+    if (PW == 4) DQ(4, true);
+    else if (PW == 2) DQ(2, true);
+    else DQ(1, true);
+    hipLaunchKernelGGL((v2_bwd_dkdv_kernel<D, true>), dim3((unsigned)kv_blocks), dim3(kThreads), 0,
+                       stream, a, Tp, (const float*)lse2, (const float*)sig);
+  } else {
+    if (PW == 4) DQ(4, false);
+    else if (PW == 2) DQ(2, false);
+    else DQ(1, false);
+    hipLaunchKernelGGL((v2_bwd_dkdv_kernel<D, false>), dim3((unsigned)kv_blocks), dim3(kThreads),
+                       0, stream, a, Tp, (const float*)lse2, (const float*)sig);
+  }
+#undef DQ
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t v2_bwd_workspace_bytes(int B, int T, int Hq) {
+  const size_t Tp = (size_t)(T + 63) / 64 * 64;
+  // delta and lse2 [B][Hq][Tp], sigmoid [B][Hq/2][Tp], fp32
+  return ((size_t)B * Hq * Tp * 2 + (size_t)B * (Hq / 2) * Tp) * sizeof(float);
+}
+
+hipError_t launch_v2_backward(const V2BwdArgs& a, hipStream_t stream) {
+  if (a.d == 128) return launch_d<128>(a, stream);
+  if (a.d == 64) return launch_d<64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace diffattn

@@ -399,8 +399,29 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   if (!wave_active) return;
 
   // ---- epilogue: normalise, pair subtraction, bf16 store ----
-  const float inv_e = 1.0f / sum_across_rows(l_part[0]);
-  const float inv_o = 1.0f / sum_across_rows(l_part[1]);
+  const float l_e = sum_across_rows(l_part[0]);
+  const float l_o = sum_across_rows(l_part[1]);
+  const float inv_e = 1.0f / l_e;
+  const float inv_o = 1.0f / l_o;
+  if (row < L && a.o_heads != nullptr) {
+    // training forward: per-head outputs and natural-log log-sum-exp of the
+    // scaled scores (the accumulators hold log2-domain values minus mb)
+    const size_t tok = (size_t)(tok0 + row);
+    if (g == 0) {
+      a.lse[tok * a.Hq + 2 * p] = (mb[0] + log2f(l_e)) * 0.69314718055994531f;
+      a.lse[tok * a.Hq + 2 * p + 1] = (mb[1] + log2f(l_o)) * 0.69314718055994531f;
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float inv = nb ? inv_o : inv_e;
+      uint16_t* dst = a.o_heads + (tok * a.Hq + 2 * p + nb) * D + g * 4;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<u32x2*>(dst + db * 16) =
+            u32x2{pack_bf16x2(o[db][nb][0] * inv, o[db][nb][1] * inv),
+                  pack_bf16x2(o[db][nb][2] * inv, o[db][nb][3] * inv)};
+    }
+  }
   if (row < L) {
     const size_t tok = (size_t)(tok0 + row);
     const float sg = sigmoid_f32(a.logit[tok * hpairs + p]);

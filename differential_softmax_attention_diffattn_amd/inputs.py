@@ -223,6 +223,14 @@ def v2_inputs(w: V2Workload, device=None) -> dict:
     )
 
 
+DOUT_SEED = 305  # upstream gradient of the V2 backward workload (B2 T8192 Hq64 Hkv8 d128)
+
+
+def v2_dout(w: V2Workload, seed: int = DOUT_SEED, device=None) -> torch.Tensor:
+    """Upstream gradient dL/dout [B,T,Hq/2,d] bf16, iid N(0,1) (padded batches)."""
+    return normal((w.B, w.T, w.Hq // 2, w.d), seed, 1.0, device=device)
+
+
 def decode_small_inputs(w: DecodeWorkload, device=None) -> dict:
     """Decode inputs for the query, logits and lengths (the caches come from :func:`decode_cache_slice`)."""
     sq, sk, sv, sl = w.seeds

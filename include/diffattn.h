@@ -1,8 +1,8 @@
 /*
  * diffattn.h -- C ABI of the MI355X (gfx950) differential-attention library.
  *
- * The library computes the forward pass of differential attention as described
- * on two web pages:
+ * The library computes differential attention (the forward pass, and the V2
+ * backward for training) as described on two web pages:
  *   [P1] "Differential Transformer | ICLR 2025 Oral" (dainus.ai blog),
  *        sections "Differential Attention: 빼기의 힘", "λ의 역할과 학습",
  *        "파라미터 효율성";
@@ -121,6 +121,57 @@ DIFFATTN_API int diffattn_v2_fwd(const void* q, const void* k, const void* v, co
                     void* out, const int* cu_seqlens, int nseq, int max_seqlen, int B, int T,
                     int Hq, int Hkv, int d, float scale, int causal, diffattn_dtype dtype,
                     void* stream);
+
+/*
+ * V2 training forward (padded batches) [P2 §1, §4]: diffattn_v2_fwd's output,
+ * plus what diffattn_v2_bwd needs from the forward:
+ *
+ *   out          : [B, T, Hq/2, d] bf16, as diffattn_v2_fwd
+ *   o_heads      : [B, T, Hq, d] bf16, O_j of every query head before the pair
+ *                  subtraction
+ *   lse          : [B, T, Hq] fp32, log sum_t exp(q_{i,j} . k_{t,kv(j)} * scale)
+ *                  over the visible keys (natural log)
+ *
+ * Other arguments, layouts and support as diffattn_v2_fwd with cu_seqlens ==
+ * NULL.  (For speed the kernel rounds q * scale * log2(e) to bf16 before the
+ * score product; lse and o_heads carry that rounding.)
+ */
+DIFFATTN_API int diffattn_v2_fwd_train(const void* q, const void* k, const void* v,
+                          const float* lambda_logit, void* out, void* o_heads, float* lse, int B,
+                          int T, int Hq, int Hkv, int d, float scale, int causal,
+                          diffattn_dtype dtype, void* stream);
+
+/*
+ * V2 backward (padded batches).  The pages give the forward [P2 §1, §4] and
+ * quote its training throughput, but no gradient; this is the chain rule
+ * through that forward.  For the loss L = sum(dout * out), with s =
+ * sigmoid(lambda_logit):
+ *
+ *   dO_2p = dout_p,  dO_2p+1 = -s * dout_p,
+ *   dlambda_logit[i,p] = -s (1 - s) <dout[i,p], O_2p+1[i]>,
+ *   per query head j: P = softmax rows (recomputed from lse), dP = dO_j V^T,
+ *     dS = P o (dP - rowsum(dO_j o O_j)), dq_j = scale dS K,
+ *     dk_kv(j) += scale dS^T q_j,  dv_kv(j) += P^T dO_j.
+ *
+ *   q, k, v, lambda_logit : as diffattn_v2_fwd (padded)
+ *   o_heads, lse          : from diffattn_v2_fwd_train on the same inputs
+ *   dout                  : [B, T, Hq/2, d] bf16, dL/dout
+ *   dq                    : [B, T, Hq, d] fp32 (written)
+ *   dk, dv                : [B, T, Hkv, d] fp32 (written; the query heads of a
+ *                           GQA group are summed)
+ *   dlambda_logit         : [B, T, Hq/2] fp32 (written)
+ *   workspace             : device scratch of at least
+ *                           diffattn_v2_bwd_workspace_bytes() bytes; caller-owned.
+ * Supported: dtype DIFFATTN_BF16, d in {64, 128}, Hq / Hkv even.
+ */
+DIFFATTN_API int diffattn_v2_bwd(const void* q, const void* k, const void* v,
+                    const float* lambda_logit, const void* o_heads, const float* lse,
+                    const void* dout, float* dq, float* dk, float* dv, float* dlambda_logit,
+                    void* workspace, size_t workspace_bytes, int B, int T, int Hq, int Hkv, int d,
+                    float scale, int causal, diffattn_dtype dtype, void* stream);
+
+/* Workspace bytes diffattn_v2_bwd needs (0 for sizes it would reject). */
+DIFFATTN_API size_t diffattn_v2_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d);
 
 /*
  * V2 decode step [P2 §1, §2]: one new query row per sequence against its KV

@@ -13,6 +13,7 @@ from .diffattn_oracle import (  # noqa: F401
     v1_head,
     v1_norm,
     v2_backward,
+    v2_backward_query_rows,
     v2_combine,
     v2_decode,
     v2_forward,

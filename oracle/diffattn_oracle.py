@@ -361,3 +361,36 @@ def v2_forward_stats(q, k, v, causal: bool = True, scale: float | None = None):
             O[b, :, j] = (e / l) @ v[b, :, kv]
             lse[b, :, j] = (m + np.log(l))[:, 0]
     return O, lse
+
+
+def v2_backward_query_rows(q, k, v, logit, dout, rows, causal: bool = True,
+                           scale: float | None = None):
+    """dq and dlogit of one sequence at the query positions ``rows`` only.
+
+    Same chain rule as ``v2_sequence_backward``, restricted to the rows: a row's
+    dq and dlogit need only its own attention row, so this runs at any length.
+    q [T, 2h, d], k/v [T, Hkv, d], logit [T, h], dout [T, h, d] ->
+    (dq [R, 2h, d], dlogit [R, h]).
+    """
+    q, k, v, logit, dout = (_f64(a) for a in (q, k, v, logit, dout))
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rows = np.asarray(rows, dtype=np.int64)
+    sig = sigmoid(logit[rows])                               # [R, h]
+    dq = np.empty((rows.size, Hq, d))
+    dlogit = np.empty((rows.size, Hq // 2))
+    for j in range(Hq):
+        kv = gqa_kv_head(j, Hq, Hkv)
+        p = _attention_map(q[rows, j], k[:, kv], rows, scale, causal)   # [R, T]
+        o = p @ v[:, kv]
+        if j % 2 == 0:
+            do = dout[rows, j // 2]
+        else:
+            do = -sig[:, j // 2, None] * dout[rows, j // 2]
+            dlogit[:, j // 2] = -sig[:, j // 2] * (1.0 - sig[:, j // 2]) * np.sum(
+                dout[rows, j // 2] * o, axis=-1)
+        dp = do @ v[:, kv].T
+        ds = p * (dp - np.sum(do * o, axis=-1, keepdims=True))
+        dq[:, j] = scale * (ds @ k[:, kv])
+    return dq, dlogit

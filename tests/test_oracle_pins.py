@@ -448,3 +448,22 @@ def test_v2_forward_stats_match_library_attention_and_logsumexp():
     s = s.masked_fill(torch.ones(21, 21, dtype=torch.bool).triu(1), float("-inf"))
     ref = torch.logsumexp(s, dim=-1).T.numpy()
     np.testing.assert_allclose(lse[0], ref, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_v2_backward_query_rows_matches_central_differences(causal):
+    # dq and dlogit of selected rows against central differences of the forward oracle
+    (q, k, v, logit, dout), loss = _v2_loss_and_grads(44, 6, 8, 2, 3, causal)
+    rows = np.array([0, 3, 5])
+    dq, dlogit = oracle.v2_backward_query_rows(q[0], k[0], v[0], logit[0], dout[0], rows, causal)
+    h = 1e-5
+    for which, g in ((0, dq), (3, dlogit)):
+        for ridx, r in enumerate(rows):
+            for idx in np.ndindex(*g.shape[1:]):
+                args = [q, k, v, logit]
+                plus = [a.copy() for a in args]
+                minus = [a.copy() for a in args]
+                plus[which][(0, r) + idx] += h
+                minus[which][(0, r) + idx] -= h
+                fd = (loss(*plus) - loss(*minus)) / (2 * h)
+                assert abs(g[(ridx,) + idx] - fd) <= 2e-8, (which, r, idx)
