@@ -9,13 +9,14 @@ algorithmic TFLOP/s (causal lower triangle, diagonal included).
 
 The other hot-path kernels are timed in the same run (``secondary``):
 V2 GQA causal prefill (B2, Hq64/Hkv8, T8192, d128), V2 packed varlen prefill
-(65536 tokens), and the V2 decode step (B64, 32768-entry cache, Hq64/Hkv8,
-d128, metric HBM GB/s).  Inputs are synthetic, seeded, already resident in HBM
-when timing starts.  The fp64 CPU oracle is timed on a bounded sample of the
+(65536 tokens), the V2 decode step (B64, 32768-entry cache, Hq64/Hkv8,
+d128, metric HBM GB/s) and the V2 backward on the prefill workload (2.5x the
+forward's FLOP).  Inputs are synthetic, seeded, already resident in HBM when
+timing starts.  The fp64 CPU oracle is timed on a bounded sample of the
 headline workload on this host (``cpu_baseline``).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
-       [--no-cpu-baseline] [--only v1|v2|varlen|decode]
+       [--no-cpu-baseline] [--only v1|v2|varlen|decode|bwd]
 """
 from __future__ import annotations
 
@@ -37,6 +38,7 @@ SOURCES = {
     "v2": ("v2_prefill.hip", "device_common.h", "kernels.h"),
     "varlen": ("v2_prefill.hip", "device_common.h", "kernels.h"),
     "decode": ("v2_decode.hip", "device_common.h", "kernels.h"),
+    "bwd": ("v2_backward.hip", "device_common.h", "kernels.h"),
 }
 
 
@@ -110,7 +112,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["v1", "v2", "varlen", "decode"], default=None)
+    ap.add_argument("--only", choices=["v1", "v2", "varlen", "decode", "bwd"], default=None)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -245,6 +247,30 @@ def main():
                                       "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": byts,
                                       "traffic": hbm_traffic("decode", w.name)}
             del x, o, wsd
+            torch.cuda.empty_cache()
+        if args.only in (None, "bwd"):
+            # V2 backward on the prefill workload: the preprocessing, dQ and dK/dV
+            # kernels of one diffattn_v2_bwd call; the training forward that
+            # produces o_heads / lse runs once, outside the timed region
+            w = inp.V2_PREFILL
+            name = w.name.replace("v2_prefill", "v2_backward")
+            log(f"[bench] {name}")
+            x = inp.v2_inputs(w, device=dev)
+            dout = inp.v2_dout(w, device=dev)
+            _, oh, lse = da.v2_fwd_train(x["q"], x["k"], x["v"], x["logit"])
+            wsb = torch.empty(da.v2_bwd_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.d),
+                              dtype=torch.uint8, device=dev)
+            f = lambda: da.v2_bwd(x["q"], x["k"], x["v"], x["logit"], oh, lse, dout, workspace=wsb)
+            for _ in range(args.warmup):
+                f()
+            ms = time_calls(f, iters, stream)
+            # five products per (query, key) pair and head against the forward's two
+            flop = 2.5 * w.B * v2_flops_seq(w.T, w.Hq, w.d)
+            tf = flop / (ms * 1e-3) / 1e12
+            secondary["v2_backward"] = {"workload": name, "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
+                                        "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flop": flop,
+                                        "traffic": hbm_traffic("bwd", name)}
+            del x, dout, oh, lse, wsb
             torch.cuda.empty_cache()
     if secondary:
         result["secondary"] = secondary

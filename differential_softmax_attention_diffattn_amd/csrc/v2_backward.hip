@@ -19,12 +19,11 @@
 //  * v2_bwd_dq_kernel: the forward's decomposition (a wave owns one pair and
 //    16 query rows, lanes own query columns; K and V tiles stream through LDS):
 //    S^T = K Q^T, dP^T = V dout^T, dS^T, dQ^T += K^T dS^T;
-//  * v2_bwd_dkdv_kernel: a workgroup owns 64 keys of one KV head; wave
-//    (key block, even/odd) keeps its 16 keys' K and V fragments in registers,
-//    lanes own key columns, and the Q and dout tiles of every pair and query
-//    tile stream through LDS: S = Q K^T, dP = dout V^T, dS, dV += P'^T dout
-//    (P' = P or -s P), dK += dS^T Q; the even and odd waves' sums are added at
-//    the end.
+//  * v2_bwd_dkdv_kernel: a workgroup owns 128 keys of one KV head; a wave
+//    keeps its 16 keys' K and V fragments in registers (lanes own key
+//    columns) and handles both heads of every pair, so dout V^T and the dV
+//    product are formed once per pair; the Q and dout tiles of every pair and
+//    query tile stream through LDS.
 // All MFMA work is 16x16x32 bf16 with fp32 accumulation; P and dS are rounded
 // to bf16 for the second product of each pair, as in the forward.
 #include <math.h>
@@ -37,7 +36,7 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kKeys = 64;   // keys per staged tile (dq) / keys per workgroup (dkdv)
+constexpr int kKeys = 64;   // keys per staged tile (dq)
 constexpr int kQRows = 64;  // query rows per staged tile (dkdv)
 constexpr int kRows = 16;   // query rows per wave (dq)
 
@@ -325,8 +324,14 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, int
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV: a workgroup owns 64 keys of one KV head.
+// dK and dV: a workgroup owns 128 keys of one KV head, a wave 16 of them and
+// both heads of every pair.  Per (pair, query tile of 64 rows):
+//   S_e, S_o = Q_{e,o} K^T, dP = dout V^T (shared: dP_o = -s dP),
+//   dS_e = P_e o (dP - D_e), dS_o = P_o o (-s dP - D_o),
+//   dV += (P_e - s P_o)^T dout,  dK += dS_e^T Q_e + dS_o^T Q_o.
 // ---------------------------------------------------------------------------
+constexpr int kDkvKeys = kWaves * 16;
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, int Tp,
                                                                   const float* lse2,
@@ -334,8 +339,8 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
   using TL = BTile<D>;
   constexpr int NC = D / 32;
   constexpr int NDB = D / 16;
-  // per stage: Q of the even and odd head, dout of the pair (transposing layout,
-  // read both ways), then the rows' lse2 / delta of both heads and s (fp32 x 64)
+  // per stage: Q of the even and odd head and dout of the pair (transposing
+  // layout, read both ways), then the rows' lse2 and delta of both heads and s
   constexpr int kVec = 5 * kQRows * 4;
   constexpr int kStage = 3 * TL::kBytes + kVec;
   __shared__ __align__(16) uint8_t st0[kStage];
@@ -345,11 +350,8 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int c16 = lane & 15;
-  const int kb = wave & 3;   // 16-key block of the workgroup's 64 keys
-  const int hh = wave >> 2;  // 0: even heads, 1: odd heads
 
   const int T = a.T;
-  const int n_kt = (T + kKeys - 1) / kKeys;
   const int n_qt = (T + kQRows - 1) / kQRows;
   // blocks: key tiles with the most query tiles first, then (batch, KV head)
   const int nbg = a.B * a.Hkv;
@@ -360,12 +362,12 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
   const int group = a.Hq / a.Hkv;
   const int npairs = group / 2;
   const int hpairs = a.Hq / 2;
-  const int key0 = kt * kKeys;
+  const int key0 = kt * kDkvKeys;
   const int qt0 = CAUSAL ? key0 / kQRows : 0;
   const int n_items = npairs * (n_qt - qt0);  // (pair, query tile) items
 
   // this wave's 16 keys: K^T and V^T B operands (lane column = key)
-  const int key = key0 + kb * 16 + c16;
+  const int key = key0 + wave * 16 + c16;
   const int keyc = min(key, T - 1);
   const size_t kvrow = ((size_t)b * T + keyc) * a.Hkv + kvh;
   u32x4 kf[NC], vf[NC];
@@ -375,6 +377,8 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
     vf[c] = ldg128(a.v + kvrow * D + c * 32 + g * 8);
   }
   const float cs = a.scale * kLog2e;
+  // the last query row this wave's keys can see is below the tile start: skip
+  const int wave_key_lo = key0 + wave * 16;
 
   auto load = [&](int item, uint8_t* st) {
     const int pp = item % npairs;
@@ -410,69 +414,80 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
   const int tr_row = 4 * g + (c16 >> 2);
   const int tr_byte = 8 * (c16 & 3);
 
-  auto work = [&](int item, const uint8_t* st) {
+  auto work = [&](int item, const uint8_t* st) __attribute__((always_inline)) {
     const int qt = qt0 + item / npairs;
     const int r0 = qt * kQRows;
-    const uint8_t* ql = st + hh * TL::kBytes;  // this wave's head
+    if (CAUSAL && r0 + kQRows <= wave_key_lo) return;  // every key of the wave is above the rows
+    const uint8_t* qle = st;
+    const uint8_t* qlo = st + TL::kBytes;
     const uint8_t* dl = st + 2 * TL::kBytes;
     const float* vec = reinterpret_cast<const float*>(st + 3 * TL::kBytes);
-    const float* l2v = vec + hh * kQRows;
-    const float* dlv = vec + (2 + hh) * kQRows;
-    const float* sgv = vec + 4 * kQRows;
-    // S = Q K^T and dP = dout V^T: 4 query blocks x this wave's 16 keys
-    f32x4 sacc[4], dpa[4];
+    // S_e, S_o = Q K^T and dP = dout V^T: 4 query blocks x this wave's 16 keys
+    f32x4 se[4], so[4], dpa[4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
-      sacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      se[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      so[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
       dpa[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const int r = qb * 16 + c16;
-        const u32x4 qa = *reinterpret_cast<const u32x4*>(ql + trans_offset<D>(r, (c * 4 + g) * 16));
-        const u32x4 da = *reinterpret_cast<const u32x4*>(dl + trans_offset<D>(r, (c * 4 + g) * 16));
-        sacc[qb] = mfma_bf16(qa, kf[c], sacc[qb]);
+        const int off = trans_offset<D>(qb * 16 + c16, (c * 4 + g) * 16);
+        const u32x4 qa = *reinterpret_cast<const u32x4*>(qle + off);
+        const u32x4 qb_ = *reinterpret_cast<const u32x4*>(qlo + off);
+        const u32x4 da = *reinterpret_cast<const u32x4*>(dl + off);
+        se[qb] = mfma_bf16(qa, kf[c], se[qb]);
+        so[qb] = mfma_bf16(qb_, kf[c], so[qb]);
         dpa[qb] = mfma_bf16(da, vf[c], dpa[qb]);
       }
     }
-    // P, P' (= P, or -s P for the odd head) and dS; rows are queries 16 qb + 4 g + i
-    float pp_[4][4], ds_[4][4];
+    // P, dS of both heads and P'' = P_e - s P_o; rows are queries 16 qb + 4 g + i
+    float pv[4][4], dse[4][4], dso[4][4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
-      const f32x4 l2 = *reinterpret_cast<const f32x4*>(l2v + qb * 16 + 4 * g);
-      const f32x4 dlt = *reinterpret_cast<const f32x4*>(dlv + qb * 16 + 4 * g);
-      const f32x4 sg = *reinterpret_cast<const f32x4*>(sgv + qb * 16 + 4 * g);
+      const f32x4 l2e = *reinterpret_cast<const f32x4*>(vec + qb * 16 + 4 * g);
+      const f32x4 l2o = *reinterpret_cast<const f32x4*>(vec + kQRows + qb * 16 + 4 * g);
+      const f32x4 dle = *reinterpret_cast<const f32x4*>(vec + 2 * kQRows + qb * 16 + 4 * g);
+      const f32x4 dlo = *reinterpret_cast<const f32x4*>(vec + 3 * kQRows + qb * 16 + 4 * g);
+      const f32x4 sg = *reinterpret_cast<const f32x4*>(vec + 4 * kQRows + qb * 16 + 4 * g);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int q = r0 + qb * 16 + 4 * g + i;
-        float pr = fast_exp2(fmaf(sacc[qb][i], cs, -l2[i]));
-        if (q >= T || key >= T || (CAUSAL && key > q)) pr = 0.f;
-        const float f = hh ? -sg[i] : 1.f;
-        pp_[qb][i] = f * pr;
-        ds_[qb][i] = pr * (f * dpa[qb][i] - dlt[i]);
+        float pe = fast_exp2(fmaf(se[qb][i], cs, -l2e[i]));
+        float po = fast_exp2(fmaf(so[qb][i], cs, -l2o[i]));
+        if (q >= T || key >= T || (CAUSAL && key > q)) {
+          pe = 0.f;
+          po = 0.f;
+        }
+        pv[qb][i] = fmaf(-sg[i], po, pe);
+        dse[qb][i] = pe * (dpa[qb][i] - dle[i]);
+        dso[qb][i] = po * fmaf(-sg[i], dpa[qb][i], -dlo[i]);
       }
     }
-    // dV += P'^T dout and dK += dS^T Q over two 32-query k-steps; A operands
-    // from the registers above (key = row, queries 32 s + {4 g + i, 16 + 4 g + i}),
-    // B operands by transposing reads of the dout and Q tiles.
+    // dV += P''^T dout and dK += dS_e^T Q_e + dS_o^T Q_o over two 32-query
+    // k-steps; A operands from the registers above (key = row, queries
+    // 32 s + {4 g + i, 16 + 4 g + i}), B operands by transposing reads.
+    auto pack8 = [&](const float (&x)[4][4], int s) {
+      return u32x4{pack_bf16x2(x[2 * s][0], x[2 * s][1]), pack_bf16x2(x[2 * s][2], x[2 * s][3]),
+                   pack_bf16x2(x[2 * s + 1][0], x[2 * s + 1][1]),
+                   pack_bf16x2(x[2 * s + 1][2], x[2 * s + 1][3])};
+    };
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const u32x4 pa = u32x4{pack_bf16x2(pp_[2 * s][0], pp_[2 * s][1]),
-                             pack_bf16x2(pp_[2 * s][2], pp_[2 * s][3]),
-                             pack_bf16x2(pp_[2 * s + 1][0], pp_[2 * s + 1][1]),
-                             pack_bf16x2(pp_[2 * s + 1][2], pp_[2 * s + 1][3])};
-      const u32x4 sa = u32x4{pack_bf16x2(ds_[2 * s][0], ds_[2 * s][1]),
-                             pack_bf16x2(ds_[2 * s][2], ds_[2 * s][3]),
-                             pack_bf16x2(ds_[2 * s + 1][0], ds_[2 * s + 1][1]),
-                             pack_bf16x2(ds_[2 * s + 1][2], ds_[2 * s + 1][3])};
+      const u32x4 pa = pack8(pv, s);
+      const u32x4 sae = pack8(dse, s);
+      const u32x4 sao = pack8(dso, s);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int off = trans_offset<D>(s * 32 + tr_row, db * 32 + tr_byte);
-        const u32x2 dlo = lds_read_tr16(dl + off);
-        const u32x2 dhi = lds_read_tr16(dl + off + 16 * TL::kRowBytes);
-        const u32x2 qlo = lds_read_tr16(ql + off);
-        const u32x2 qhi = lds_read_tr16(ql + off + 16 * TL::kRowBytes);
-        dv[db] = mfma_bf16(pa, u32x4{dlo[0], dlo[1], dhi[0], dhi[1]}, dv[db]);
-        dk[db] = mfma_bf16(sa, u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, dk[db]);
+        const u32x2 dlo_ = lds_read_tr16(dl + off);
+        const u32x2 dhi_ = lds_read_tr16(dl + off + 16 * TL::kRowBytes);
+        const u32x2 elo = lds_read_tr16(qle + off);
+        const u32x2 ehi = lds_read_tr16(qle + off + 16 * TL::kRowBytes);
+        const u32x2 olo = lds_read_tr16(qlo + off);
+        const u32x2 ohi = lds_read_tr16(qlo + off + 16 * TL::kRowBytes);
+        dv[db] = mfma_bf16(pa, u32x4{dlo_[0], dlo_[1], dhi_[0], dhi_[1]}, dv[db]);
+        dk[db] = mfma_bf16(sae, u32x4{elo[0], elo[1], ehi[0], ehi[1]}, dk[db]);
+        dk[db] = mfma_bf16(sao, u32x4{olo[0], olo[1], ohi[0], ohi[1]}, dk[db]);
       }
     }
   };
@@ -482,46 +497,31 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
   }
-  for (int it = 0; it < n_items; ++it) {
-    const bool odd = it & 1;
-    if (it + 1 < n_items) load(it + 1, odd ? st0 : st1);
-    if (odd)
-      work(it, st1);
-    else
-      work(it, st0);
+  int it = 0;
+  for (; it + 2 <= n_items; it += 2) {  // unrolled by two: each stage a fixed LDS object
+    if (it + 1 < n_items) load(it + 1, st1);
+    work(it, st0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+    if (it + 2 < n_items) load(it + 2, st0);
+    work(it + 1, st1);
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
   }
+  if (it < n_items) work(it, st0);
 
-  // even + odd waves' sums: the odd waves publish theirs through LDS (dK in
-  // the first stage buffer, dV in the second: [4 key blocks][NDB][64 lanes][4])
-  static_assert(4 * NDB * 64 * 16 <= kStage, "exchange must fit one stage");
-  float* xk = reinterpret_cast<float*>(st0);
-  float* xv = reinterpret_cast<float*>(st1);
-  if (hh == 1) {
+  // C layout: lane column = d (16 db + c16), rows = keys 4 g + i of the wave's 16
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      *reinterpret_cast<f32x4*>(xk + ((kb * NDB + db) * 64 + lane) * 4) = dk[db];
-      *reinterpret_cast<f32x4*>(xv + ((kb * NDB + db) * 64 + lane) * 4) = dv[db];
-    }
-  }
-  __syncthreads();
-  if (hh == 1) return;
-  // C layout: lane column = d (16 db + c16), rows = keys 4 g + i of the block
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const f32x4 ok = *reinterpret_cast<const f32x4*>(xk + ((kb * NDB + db) * 64 + lane) * 4);
-    const f32x4 ov = *reinterpret_cast<const f32x4*>(xv + ((kb * NDB + db) * 64 + lane) * 4);
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int kk = key0 + kb * 16 + 4 * g + i;
+      const int kk = key0 + wave * 16 + 4 * g + i;
       if (kk < T) {
         const size_t o = (((size_t)b * T + kk) * a.Hkv + kvh) * D + db * 16 + c16;
-        a.dk[o] = (dk[db][i] + ok[i]) * a.scale;
-        a.dv[o] = dv[db][i] + ov[i];
+        a.dk[o] = dk[db][i] * a.scale;
+        a.dv[o] = dv[db][i];
       }
     }
-  }
 }
 
 template <int D>
@@ -538,7 +538,7 @@ hipError_t launch_d(const V2BwdArgs& a, hipStream_t stream) {
   const int PW = pairs_per_group % 4 == 0 ? 4 : pairs_per_group % 2 == 0 ? 2 : 1;
   const int qtile = kRows * (kWaves / PW);
   const long long dq_blocks = (long long)((a.T + qtile - 1) / qtile) * a.B * (a.Hq / (2 * PW));
-  const long long kv_blocks = (long long)((a.T + kKeys - 1) / kKeys) * a.B * a.Hkv;
+  const long long kv_blocks = (long long)((a.T + kDkvKeys - 1) / kDkvKeys) * a.B * a.Hkv;
   if (dq_blocks > 0x7fffffffLL || kv_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
 #define DQ(PWV, C)                                                                               \
   hipLaunchKernelGGL((v2_bwd_dq_kernel<D, PWV, C>), dim3((unsigned)dq_blocks), dim3(kThreads), 0, \

@@ -150,3 +150,57 @@ def test_decode_workspace_query(lib):
     nparts = n // (4 * 132 * 64 * 64)
     assert 1 <= nparts <= 512
     assert lib.diffattn_v2_decode_workspace_bytes(64, 32768, 64, 3, 128) == 0
+
+
+def v2t(lib, **kw):
+    a = dict(q=P, k=P, v=P, lg=P, out=P, oh=P, lse=P, B=2, T=64, Hq=16, Hkv=2, d=128, scale=0.0,
+             causal=1, dt=BF16, stream=None)
+    a.update(kw)
+    return lib.diffattn_v2_fwd_train(a["q"], a["k"], a["v"], a["lg"], a["out"], a["oh"], a["lse"],
+                                     a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], a["scale"],
+                                     a["causal"], a["dt"], a["stream"])
+
+
+def test_v2_train_forward_rejects_bad_arguments(lib):
+    assert v2t(lib, oh=None) == E_INVALID
+    assert v2t(lib, lse=None) == E_INVALID
+    assert v2t(lib, Hq=6, Hkv=2) == E_INVALID
+    assert v2t(lib, d=96) == E_UNSUPPORTED
+    assert v2t(lib, T=-3) == E_INVALID
+    assert v2t(lib, oh=P + 8) == E_ALIGN
+    assert v2t(lib, lse=P + 2) == E_ALIGN
+    assert v2t(lib, B=0) == 0
+
+
+def bwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, lg=P, oh=P, lse=P, dout=P, dq=P, dk=P, dv=P, dlg=P, ws=P, wsb=1 << 30,
+             B=2, T=64, Hq=16, Hkv=2, d=128, scale=0.0, causal=1, dt=BF16, stream=None)
+    a.update(kw)
+    return lib.diffattn_v2_bwd(a["q"], a["k"], a["v"], a["lg"], a["oh"], a["lse"], a["dout"],
+                               a["dq"], a["dk"], a["dv"], a["dlg"], a["ws"], a["wsb"], a["B"],
+                               a["T"], a["Hq"], a["Hkv"], a["d"], a["scale"], a["causal"],
+                               a["dt"], a["stream"])
+
+
+def test_v2_backward_rejects_bad_arguments(lib):
+    assert bwd(lib, dout=None) == E_INVALID
+    assert bwd(lib, dlg=None) == E_INVALID
+    assert bwd(lib, Hq=16, Hkv=3) == E_INVALID
+    assert bwd(lib, Hq=6, Hkv=2) == E_INVALID
+    assert bwd(lib, causal=3) == E_INVALID
+    assert bwd(lib, d=80) == E_UNSUPPORTED
+    assert bwd(lib, dt=F32) == E_UNSUPPORTED
+    assert bwd(lib, dq=P + 4) == E_ALIGN
+    assert bwd(lib, dlg=P + 1) == E_ALIGN
+    assert bwd(lib, ws=None) == E_WORKSPACE
+    assert bwd(lib, wsb=64) == E_WORKSPACE
+    assert b"workspace" in lib.diffattn_last_error()
+    assert bwd(lib, T=0, ws=None, wsb=0) == 0
+
+
+def test_v2_backward_workspace_query(lib):
+    # fp32 delta and log2-lse [B][Hq][T rounded up to 64], sigmoid [B][Hq/2][same]
+    assert lib.diffattn_v2_bwd_workspace_bytes(2, 8192, 64, 8, 128) == 4 * 2 * 8192 * (64 * 2 + 32)
+    assert lib.diffattn_v2_bwd_workspace_bytes(1, 65, 16, 2, 128) == 4 * 128 * (16 * 2 + 8)
+    assert lib.diffattn_v2_bwd_workspace_bytes(1, 64, 6, 2, 128) == 0
+    assert lib.diffattn_v2_bwd_workspace_bytes(1, 64, 16, 2, 96) == 0
