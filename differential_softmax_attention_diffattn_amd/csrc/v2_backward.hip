@@ -214,9 +214,12 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, int
   const size_t kv_stride = (size_t)a.Hkv * D;
   const uint16_t* kbase_g = a.k + ((size_t)b * T * a.Hkv + kv) * D;
   const uint16_t* vbase_g = a.v + ((size_t)b * T * a.Hkv + kv) * D;
-  auto load = [&](int kt, uint8_t* kl, uint8_t* vl) {
+  auto load_k = [&](int kt, uint8_t* kl) {
     const int r0 = kt * kKeys;
     load_tile<D, true>(kbase_g + (size_t)r0 * kv_stride, kv_stride, T - r0, kl, wave, lane);
+  };
+  auto load_v = [&](int kt, uint8_t* vl) {
+    const int r0 = kt * kKeys;
     load_tile<D, false>(vbase_g + (size_t)r0 * kv_stride, kv_stride, T - r0, vl, wave, lane);
   };
 
@@ -230,8 +233,11 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, int
   const int tr_key = 4 * g + (c16 >> 2);
   const int tr_byte = 8 * (c16 & 3);
 
-  // one 32-key step over the staged tile
-  auto step = [&](const uint8_t* kl, const uint8_t* vl, int cc, int k0, bool masked) {
+  // one 32-key step over the staged tile; MASKED applies the causal / ragged
+  // mask (only diagonal and ragged tiles need it)
+  auto step = [&](auto masked, const uint8_t* kl, const uint8_t* vl, int cc, int k0)
+                  __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
     f32x4 sacc[2][2], dpa[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -261,7 +267,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, int
         for (int i = 0; i < 4; ++i) {
           const int key = k0 + kb * 16 + 4 * g + i;
           float pr = fast_exp2(fmaf(sacc[kb][nb][i], cs, -l2[nb]));
-          if (masked && (key >= T || (CAUSAL && key > row))) pr = 0.f;
+          if (MASKED && (key >= T || (CAUSAL && key > row))) pr = 0.f;
           const float dpv = nb ? -sg * dpa[kb][i] : dpa[kb][i];
           v8[kb * 4 + i] = pr * (dpv - dl[nb]);
         }
@@ -279,31 +285,54 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, int
     }
   };
 
-  load(0, kbuf0, vbuf0);
+  // Key tiles [0, n_int) are fully valid and visible to every row of the
+  // workgroup (and each has a full successor): unmasked steps, unrolled by two
+  // so each stage is a fixed LDS object, the next tile's K loads before the
+  // first step and its V loads before the second.  The rest take the masked step.
+  const int n_int = max(0, CAUSAL ? min((qt * QTILE + 1) / kKeys, T / kKeys - 1) : T / kKeys - 1);
+  auto interior_tile = [&](int kt, const uint8_t* kl, const uint8_t* vl, uint8_t* kn,
+                           uint8_t* vn) __attribute__((always_inline)) {
+    load_k(kt + 1, kn);
+    if (wave_active) step(BoolTag<false>{}, kl, vl, 0, kt * kKeys);
+    load_v(kt + 1, vn);
+    if (wave_active) step(BoolTag<false>{}, kl, vl, 1, kt * kKeys + 32);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+  };
+  load_k(0, kbuf0);
+  load_v(0, vbuf0);
   __builtin_amdgcn_s_waitcnt(0x0f70);
   __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
+  int kt = 0;
+  for (; kt + 2 <= n_int; kt += 2) {
+    interior_tile(kt, kbuf0, vbuf0, kbuf1, vbuf1);
+    interior_tile(kt + 1, kbuf1, vbuf1, kbuf0, vbuf0);
+  }
+  if (kt < n_int) {
+    interior_tile(kt, kbuf0, vbuf0, kbuf1, vbuf1);
+    ++kt;
+  }
+  for (; kt < n_kt; ++kt) {
     const bool odd = kt & 1;
     if (kt + 1 < n_kt) {
-      if (odd)
-        load(kt + 1, kbuf0, vbuf0);
-      else
-        load(kt + 1, kbuf1, vbuf1);
+      if (odd) {
+        load_k(kt + 1, kbuf0);
+        load_v(kt + 1, vbuf0);
+      } else {
+        load_k(kt + 1, kbuf1);
+        load_v(kt + 1, vbuf1);
+      }
     }
     if (wave_active) {
       const int t0 = kt * kKeys;
-      const bool masked = (t0 + kKeys > T) || (CAUSAL && t0 + kKeys - 1 > q_lo);
-      if (t0 < wave_key_end) {
-        if (odd)
-          step(kbuf1, vbuf1, 0, t0, masked);
-        else
-          step(kbuf0, vbuf0, 0, t0, masked);
-      }
-      if (t0 + 32 < wave_key_end) {
-        if (odd)
-          step(kbuf1, vbuf1, 1, t0 + 32, masked);
-        else
-          step(kbuf0, vbuf0, 1, t0 + 32, masked);
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        if (t0 + 32 * cc < wave_key_end) {
+          if (odd)
+            step(BoolTag<true>{}, kbuf1, vbuf1, cc, t0 + 32 * cc);
+          else
+            step(BoolTag<true>{}, kbuf0, vbuf0, cc, t0 + 32 * cc);
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);
@@ -414,7 +443,9 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
   const int tr_row = 4 * g + (c16 >> 2);
   const int tr_byte = 8 * (c16 & 3);
 
-  auto work = [&](int item, const uint8_t* st) __attribute__((always_inline)) {
+  // MASKED: the item's query tile touches the diagonal or a ragged end
+  auto work = [&](auto masked, int item, const uint8_t* st) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int qt = qt0 + item / npairs;
     const int r0 = qt * kQRows;
     if (CAUSAL && r0 + kQRows <= wave_key_lo) return;  // every key of the wave is above the rows
@@ -454,7 +485,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
         const int q = r0 + qb * 16 + 4 * g + i;
         float pe = fast_exp2(fmaf(se[qb][i], cs, -l2e[i]));
         float po = fast_exp2(fmaf(so[qb][i], cs, -l2o[i]));
-        if (q >= T || key >= T || (CAUSAL && key > q)) {
+        if (MASKED && (q >= T || key >= T || (CAUSAL && key > q))) {
           pe = 0.f;
           po = 0.f;
         }
@@ -497,18 +528,30 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
   }
+  auto item_masked = [&](int item) {
+    const int r0 = (qt0 + item / npairs) * kQRows;
+    return (CAUSAL && r0 < key0 + kDkvKeys) || r0 + kQRows > T || key0 + kDkvKeys > T;
+  };
+  auto run = [&](int item, const uint8_t* st) __attribute__((always_inline)) {
+    // (without the causal mask a single instance is kept: two of them make the
+    // register allocator spill)
+    if (!CAUSAL || item_masked(item))
+      work(BoolTag<true>{}, item, st);
+    else
+      work(BoolTag<false>{}, item, st);
+  };
   int it = 0;
   for (; it + 2 <= n_items; it += 2) {  // unrolled by two: each stage a fixed LDS object
-    if (it + 1 < n_items) load(it + 1, st1);
-    work(it, st0);
+    load(it + 1, st1);
+    run(it, st0);
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
     if (it + 2 < n_items) load(it + 2, st0);
-    work(it + 1, st1);
+    run(it + 1, st1);
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
   }
-  if (it < n_items) work(it, st0);
+  if (it < n_items) run(it, st0);
 
   // C layout: lane column = d (16 db + c16), rows = keys 4 g + i of the wave's 16
 #pragma unroll
