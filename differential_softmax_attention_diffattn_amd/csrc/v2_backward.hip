@@ -393,7 +393,10 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
   const int hpairs = a.Hq / 2;
   const int key0 = kt * kDkvKeys;
   const int qt0 = CAUSAL ? key0 / kQRows : 0;
-  const int n_items = npairs * (n_qt - qt0);  // (pair, query tile) items
+  // (pair, query tile) items, last query tile first: the workgroups of one KV
+  // head (on one XCD) then walk the same Q / dout tiles at the same time and
+  // share them in L2
+  const int n_items = npairs * (n_qt - qt0);
 
   // this wave's 16 keys: K^T and V^T B operands (lane column = key)
   const int key = key0 + wave * 16 + c16;
@@ -411,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
 
   auto load = [&](int item, uint8_t* st) {
     const int pp = item % npairs;
-    const int qt = qt0 + item / npairs;
+    const int qt = n_qt - 1 - item / npairs;
     const int r0 = qt * kQRows;
     const int je = kvh * group + 2 * pp;  // even head of the pair
     const int pair = je / 2;
@@ -446,7 +449,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
   // MASKED: the item's query tile touches the diagonal or a ragged end
   auto work = [&](auto masked, int item, const uint8_t* st) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
-    const int qt = qt0 + item / npairs;
+    const int qt = n_qt - 1 - item / npairs;
     const int r0 = qt * kQRows;
     if (CAUSAL && r0 + kQRows <= wave_key_lo) return;  // every key of the wave is above the rows
     const uint8_t* qle = st;
@@ -529,7 +532,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
     __syncthreads();
   }
   auto item_masked = [&](int item) {
-    const int r0 = (qt0 + item / npairs) * kQRows;
+    const int r0 = (n_qt - 1 - item / npairs) * kQRows;
     return (CAUSAL && r0 < key0 + kDkvKeys) || r0 + kQRows > T || key0 + kDkvKeys > T;
   };
   auto run = [&](int item, const uint8_t* st) __attribute__((always_inline)) {
