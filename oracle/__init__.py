@@ -9,6 +9,7 @@ from .diffattn_oracle import (  # noqa: F401
     sigmoid,
     softmax_rows,
     v1_attention,
+    v1_decode,
     v1_forward,
     v1_head,
     v1_norm,

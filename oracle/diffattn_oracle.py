@@ -25,7 +25,8 @@ What is computed, and where it is stated
   and no scale follow.
 * V2 decode -- same summary, §2: the KV heads and cache are those of a
   standard GQA model; a decode step is the V2 formula for one new query row
-  against every cached position.
+  against every cached position.  V1 decode is the V1 formula (with its norm)
+  for one new query row against the cached K1, K2 and V.
 
 Readings where the pages are silent (each one is an argument, not a constant)
 ----------------------------------------------------------------------------
@@ -168,6 +169,36 @@ def v1_forward(q1, k1, q2, k2, v, lam: float, lam_init: float, eps: float, weigh
     """Full V1 attention output y = (1 - lam_init) * w * z / rms(z): [B, R, H, dv]."""
     z = v1_attention(q1, k1, q2, k2, v, lam, causal, rows)
     return v1_norm(z, lam_init, eps, weight)
+
+
+def v1_decode(q1, q2, k1_cache, k2_cache, v_cache, lam: float, lam_init: float, eps: float,
+              weight=None, cache_len=None, batch=None) -> np.ndarray:
+    """One V1 decode step: q1, q2 [B, H, d]; caches k1/k2 [B, S, H, d], v [B, S, H, dv].
+
+    Entry b's query attends (non-causally) to cache positions 0 .. cache_len[b]-1 (all
+    S when ``cache_len`` is None) with both maps, then the V1 norm and factor: the V1
+    formula for a single query row (blog section "Differential Attention: 빼기의 힘";
+    V2 summary §1 for the norm).  An entry with no cached positions gives zeros.
+    ``batch`` selects entries; the caches may then hold only those entries.
+    Returns [B', H, dv].
+    """
+    q1, q2 = _f64(q1), _f64(q2)
+    B, H, d = q1.shape
+    batch = list(range(B)) if batch is None else [int(b) for b in batch]
+    S = k1_cache.shape[1]
+    out = np.zeros((len(batch), H, v_cache.shape[-1]))
+    sliced = k1_cache.shape[0] == len(batch) and len(batch) != B
+    for i, b in enumerate(batch):
+        n = S if cache_len is None else int(np.asarray(cache_len)[b])
+        if n <= 0:
+            continue
+        cb = i if sliced else b
+        k1b, k2b, vb = _f64(k1_cache[cb, :n]), _f64(k2_cache[cb, :n]), _f64(v_cache[cb, :n])
+        for h in range(H):
+            z = v1_head(q1[b, h][None], k1b[:, h], q2[b, h][None], k2b[:, h], vb[:, h], lam,
+                        rows=np.array([0]), causal=False)
+            out[i, h] = v1_norm(z, lam_init, eps, weight)[0]
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -467,3 +467,58 @@ def test_v2_backward_query_rows_matches_central_differences(causal):
                 minus[which][(0, r) + idx] -= h
                 fd = (loss(*plus) - loss(*minus)) / (2 * h)
                 assert abs(g[(ridx,) + idx] - fd) <= 2e-8, (which, r, idx)
+
+
+
+# ---------------------------------------------------------------------------
+# V1 decode
+# ---------------------------------------------------------------------------
+
+def test_v1_decode_lambda_zero_is_normalised_single_query_attention():
+    # lambda = 0: z is plain attention of the query over the cache (torch SDPA, float64,
+    # no mask), then the per-head RMS norm and factor
+    r = rng(50)
+    B, S, H, d, dv = 2, 37, 3, 8, 16
+    q1, q2 = r.normal(size=(B, H, d)), r.normal(size=(B, H, d))
+    k1, k2 = r.normal(size=(B, S, H, d)), r.normal(size=(B, S, H, d))
+    v = r.normal(size=(B, S, H, dv))
+    out = oracle.v1_decode(q1, q2, k1, k2, v, 0.0, 0.3, 0.0)
+    for b in range(B):
+        z = sdpa(q1[b][None], k1[b], v[b], False)[0]                     # [H, dv]
+        ref = 0.7 * z / np.sqrt(np.mean(z * z, axis=-1, keepdims=True))
+        np.testing.assert_allclose(out[b], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_v1_decode_brute_force_tiny():
+    # scalar loops with math.exp: both maps, the difference, the norm and the weight
+    r = rng(51)
+    B, S, H, d, dv = 2, 5, 2, 3, 4
+    q1, q2 = r.normal(size=(B, H, d)), r.normal(size=(B, H, d))
+    k1, k2 = r.normal(size=(B, S, H, d)), r.normal(size=(B, S, H, d))
+    v = r.normal(size=(B, S, H, dv))
+    w = r.normal(size=dv)
+    lens = np.array([5, 3])
+    lam, li, eps = 0.6, 0.2, 1e-3
+    out = oracle.v1_decode(q1, q2, k1, k2, v, lam, li, eps, weight=w, cache_len=lens)
+    for b in range(B):
+        n = int(lens[b])
+        for h in range(H):
+            def smax(q, k):
+                s = [sum(q[t] * k[j, t] for t in range(d)) / math.sqrt(d) for j in range(n)]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                return [x / sum(e) for x in e]
+            p1, p2 = smax(q1[b, h], k1[b, :, h]), smax(q2[b, h], k2[b, :, h])
+            z = [sum((p1[j] - lam * p2[j]) * v[b, j, h, c] for j in range(n)) for c in range(dv)]
+            rr = math.sqrt(sum(x * x for x in z) / dv + eps)
+            for c in range(dv):
+                assert abs(out[b, h, c] - (1 - li) * w[c] * z[c] / rr) < 1e-12
+
+
+def test_v1_decode_empty_cache_gives_zeros():
+    r = rng(52)
+    q = r.normal(size=(1, 2, 4))
+    k = r.normal(size=(1, 6, 2, 4))
+    v = r.normal(size=(1, 6, 2, 8))
+    out = oracle.v1_decode(q, q, k, k, v, 0.2, 0.2, 1e-12, cache_len=np.array([0]))
+    np.testing.assert_array_equal(out, 0.0)
