@@ -10,13 +10,14 @@ algorithmic TFLOP/s (causal lower triangle, diagonal included).
 The other hot-path kernels are timed in the same run (``secondary``):
 V2 GQA causal prefill (B2, Hq64/Hkv8, T8192, d128), V2 packed varlen prefill
 (65536 tokens), the V2 decode step (B64, 32768-entry cache, Hq64/Hkv8,
-d128, metric HBM GB/s) and the V2 backward on the prefill workload (2.5x the
+d128, metric HBM GB/s), the V1 decode step (B32, 32768-entry cache, H12,
+d128/dv256, GB/s) and the V2 backward on the prefill workload (2.5x the
 forward's FLOP).  Inputs are synthetic, seeded, already resident in HBM when
 timing starts.  The fp64 CPU oracle is timed on a bounded sample of the
 headline workload on this host (``cpu_baseline``).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
-       [--no-cpu-baseline] [--only v1|v2|varlen|decode|bwd]
+       [--no-cpu-baseline] [--only v1|v2|varlen|decode|v1dec|bwd]
 """
 from __future__ import annotations
 
@@ -39,6 +40,7 @@ SOURCES = {
     "varlen": ("v2_prefill.hip", "device_common.h", "kernels.h"),
     "decode": ("v2_decode.hip", "device_common.h", "kernels.h"),
     "bwd": ("v2_backward.hip", "device_common.h", "kernels.h"),
+    "v1dec": ("v1_decode.hip", "device_common.h", "kernels.h"),
 }
 
 
@@ -112,7 +114,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["v1", "v2", "varlen", "decode", "bwd"], default=None)
+    ap.add_argument("--only", choices=["v1", "v2", "varlen", "decode", "v1dec", "bwd"],
+                    default=None)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -246,6 +249,26 @@ def main():
             secondary["v2_decode"] = {"workload": w.name, "ms": round(ms, 4), "GB/s": round(gbs, 1),
                                       "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": byts,
                                       "traffic": hbm_traffic("decode", w.name)}
+            del x, o, wsd
+            torch.cuda.empty_cache()
+        if args.only in (None, "v1dec"):
+            w = inp.V1_DECODE
+            log(f"[bench] {w.name}")
+            x = inp.v1_decode_inputs(w, device=dev)
+            o = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=dev)
+            wsd = torch.empty(da.v1_decode_workspace_bytes(w.B, w.S, w.H, w.d, w.dv),
+                              dtype=torch.uint8, device=dev)
+            li = da.lambda_init(w.layer)
+            f = lambda: da.v1_decode(x["q1"], x["q2"], x["k1_cache"], x["k2_cache"], x["v_cache"],
+                                     li, li, w.eps, out=o, workspace=wsd)
+            for _ in range(args.warmup):
+                f()
+            ms = time_calls(f, iters, stream)
+            byts = 2.0 * w.B * w.S * w.H * (2 * w.d + w.dv)  # K1, K2 and V once, bf16
+            gbs = byts / (ms * 1e-3) / 1e9
+            secondary["v1_decode"] = {"workload": w.name, "ms": round(ms, 4), "GB/s": round(gbs, 1),
+                                      "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": byts,
+                                      "traffic": hbm_traffic("v1dec", w.name)}
             del x, o, wsd
             torch.cuda.empty_cache()
         if args.only in (None, "bwd"):

@@ -11,6 +11,7 @@ arithmetic runs in the library's kernels; there is no fallback path.
     v2_fwd      V2: GQA attention over 2h query heads, O_even - sigmoid(logit) O_odd
                 (padded or packed/varlen batches)
     v2_decode   V2 decode step against a KV cache
+    v1_decode   V1 decode step against cached K1, K2 and V (with the norm)
     v2_fwd_train / v2_bwd
                 V2 training forward (also keeps per-head O and log-sum-exp) and
                 the backward: gradients of q, k, v and the lambda logits
@@ -25,11 +26,13 @@ __all__ = [
     "v1_fwd",
     "v2_fwd",
     "v2_decode",
+    "v1_decode",
     "v2_fwd_train",
     "v2_bwd",
     "lambda_init",
     "v1_workspace_bytes",
     "v2_decode_workspace_bytes",
+    "v1_decode_workspace_bytes",
     "v2_bwd_workspace_bytes",
     "DiffAttnError",
 ]
@@ -306,3 +309,55 @@ def v2_bwd(q, k, v, logit, o_heads, lse, dout, causal: bool = True, scale: float
             float(scale or 0.0), 1 if causal else 0, DIFFATTN_BF16, _stream(dev))
     _lib.check("diffattn_v2_bwd", rc)
     return dq, dk, dv, dlogit
+
+
+def v1_decode_workspace_bytes(B, S_max, H, d, dv) -> int:
+    return int(_lib.load().diffattn_v1_decode_workspace_bytes(B, S_max, H, d, dv))
+
+
+def v1_decode(q1, q2, k1_cache, k2_cache, v_cache, lam: float, lambda_init: float,
+              eps: float = 1e-12, weight=None, cache_len=None, out=None, workspace=None):
+    """DIFF V1 decode step.  q1, q2 [B,H,d]; k1/k2 caches [B,S_max,H,d]; v cache
+    [B,S_max,H,dv] bf16; cache_len int32 [B] on the GPU or None -> out [B,H,dv] fp32."""
+    torch = _torch()
+    dev = q1.device
+    _check_tensor("q1", q1, dtype=torch.bfloat16, dim=3)
+    _check_tensor("q2", q2, dtype=torch.bfloat16, dim=3, device=dev)
+    for n, t in (("k1_cache", k1_cache), ("k2_cache", k2_cache), ("v_cache", v_cache)):
+        _check_tensor(n, t, dtype=torch.bfloat16, dim=4, device=dev)
+    if q2.shape != q1.shape or k2_cache.shape != k1_cache.shape:
+        raise ValueError("q2 / k2_cache must match q1 / k1_cache")
+    B, H, d = q1.shape
+    _, S_max, Hk, dk = k1_cache.shape
+    if k1_cache.shape[0] != B or Hk != H or dk != d:
+        raise ValueError("k caches do not match q1")
+    if tuple(v_cache.shape[:3]) != (B, S_max, H):
+        raise ValueError("v_cache does not match the k caches")
+    dv = v_cache.shape[3]
+    if weight is not None:
+        _check_tensor("weight", weight, dtype=torch.float32, dim=1, device=dev)
+        if weight.shape[0] != dv:
+            raise ValueError("weight must have dv entries")
+    if cache_len is not None:
+        _check_tensor("cache_len", cache_len, dtype=torch.int32, dim=1, device=dev)
+        if cache_len.shape[0] != B:
+            raise ValueError("cache_len must have B entries")
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=torch.float32, device=dev)
+    _check_tensor("out", out, dtype=torch.float32, dim=3, device=dev)
+    if tuple(out.shape) != (B, H, dv):
+        raise ValueError("out has the wrong shape")
+    lib = _lib.load()
+    need = int(lib.diffattn_v1_decode_workspace_bytes(B, S_max, H, d, dv))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _check_tensor("workspace", workspace, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        rc = lib.diffattn_v1_decode(
+            _ptr(q1), _ptr(q2), _ptr(k1_cache), _ptr(k2_cache), _ptr(v_cache), _ptr(cache_len),
+            _ptr(weight), _ptr(out), _ptr(workspace), ws_bytes, B, S_max, H, d, dv, float(lam),
+            float(lambda_init), float(eps), DIFFATTN_BF16, _stream(dev))
+    _lib.check("diffattn_v1_decode", rc)
+    return out

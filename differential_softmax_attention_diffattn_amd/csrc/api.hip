@@ -280,6 +280,69 @@ int diffattn_v2_bwd(const void* q, const void* k, const void* v, const float* la
   return from_hip(diffattn::launch_v2_backward(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+size_t diffattn_v1_decode_workspace_bytes(int B, int S_max, int H, int d, int dv) {
+  if (B < 0 || S_max < 0 || H <= 0) return 0;
+  if (!((d == 128 && dv == 256) || (d == 64 && dv == 128))) return 0;
+  int split_len, nsplit;
+  diffattn::v1_decode_split(B, S_max, H, &split_len, &nsplit);
+  const long long n = prod({B, H, 2, nsplit, dv + 4});
+  return n < 0 ? 0 : (size_t)n * sizeof(float);
+}
+
+int diffattn_v1_decode(const void* q1, const void* q2, const void* k1_cache, const void* k2_cache,
+                       const void* v_cache, const int* cache_len, const float* norm_weight,
+                       float* out, void* workspace, size_t workspace_bytes, int B, int S_max,
+                       int H, int d, int dv, float lambda, float lambda_init, float eps,
+                       diffattn_dtype dtype, void* stream) {
+  const char* fn = "diffattn_v1_decode";
+  if (!q1 || !q2 || !k1_cache || !k2_cache || !v_cache || !out)
+    return fail(DIFFATTN_E_INVALID, "%s: null tensor pointer", fn);
+  if (B < 0 || S_max < 0 || H <= 0 || d <= 0 || dv <= 0)
+    return fail(DIFFATTN_E_INVALID, "%s: bad sizes B=%d S_max=%d H=%d d=%d dv=%d", fn, B, S_max, H,
+                d, dv);
+  if (!isfinite(lambda) || !isfinite(lambda_init) || !isfinite(eps) || eps < 0.f)
+    return fail(DIFFATTN_E_INVALID, "%s: lambda, lambda_init must be finite and eps finite >= 0", fn);
+  if (dtype != DIFFATTN_BF16)
+    return fail(dtype == DIFFATTN_F32 ? DIFFATTN_E_UNSUPPORTED : DIFFATTN_E_INVALID,
+                "%s: only bf16 is supported", fn);
+  if (!((d == 128 && dv == 256) || (d == 64 && dv == 128)))
+    return fail(DIFFATTN_E_UNSUPPORTED, "%s: (d=%d, dv=%d) not (128, 256) or (64, 128)", fn, d, dv);
+  if (prod({B, S_max, H, dv}) < 0 || prod({B, S_max, H, dv}) > (1LL << 40))
+    return fail(DIFFATTN_E_INVALID, "%s: problem too large", fn);
+  const void* ptrs[] = {q1, q2, k1_cache, k2_cache, v_cache, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(DIFFATTN_E_ALIGN, "%s: tensor pointers must be 16-byte aligned", fn);
+  if ((cache_len && !aligned4(cache_len)) || (norm_weight && !aligned4(norm_weight)))
+    return fail(DIFFATTN_E_ALIGN, "%s: cache_len and norm_weight must be 4-byte aligned", fn);
+  if (B == 0) return ok();
+  const size_t need = diffattn_v1_decode_workspace_bytes(B, S_max, H, d, dv);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DIFFATTN_E_WORKSPACE, "%s: workspace of %zu bytes required (got %zu%s)", fn, need,
+                workspace_bytes, workspace ? "" : ", NULL");
+  if (!aligned16(workspace)) return fail(DIFFATTN_E_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  diffattn::V1DecodeArgs a{};
+  a.q1 = static_cast<const uint16_t*>(q1);
+  a.q2 = static_cast<const uint16_t*>(q2);
+  a.k1 = static_cast<const uint16_t*>(k1_cache);
+  a.k2 = static_cast<const uint16_t*>(k2_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.cache_len = cache_len;
+  a.norm_weight = norm_weight;
+  a.out = out;
+  a.partial = static_cast<float*>(workspace);
+  a.B = B;
+  a.S_max = S_max;
+  a.H = H;
+  a.d = d;
+  a.dv = dv;
+  diffattn::v1_decode_split(B, S_max, H, &a.split_len, &a.nsplit);
+  a.lambda = lambda;
+  a.lambda_init = lambda_init;
+  a.eps = eps;
+  a.scale = 1.0f / sqrtf((float)d);
+  return from_hip(diffattn::launch_v1_decode(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 size_t diffattn_v2_decode_workspace_bytes(int B, int S_max, int Hq, int Hkv, int d) {
   if (B < 0 || S_max < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || (Hq / Hkv) % 2 || Hq / Hkv > 16)
     return 0;

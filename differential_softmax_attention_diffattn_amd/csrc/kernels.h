@@ -71,6 +71,25 @@ struct DecodeArgs {
   float scale;
 };
 
+struct V1DecodeArgs {
+  const uint16_t* q1;        // bf16 [B, H, d]
+  const uint16_t* q2;        // bf16 [B, H, d]
+  const uint16_t* k1;        // bf16 [B, S_max, H, d]
+  const uint16_t* k2;        // bf16 [B, S_max, H, d]
+  const uint16_t* v;         // bf16 [B, S_max, H, dv]
+  const int* cache_len;      // device [B] or nullptr
+  const float* norm_weight;  // [dv] or nullptr
+  float* out;                // fp32 [B, H, dv]
+  float* partial;            // fp32 workspace [B, H, 2 maps, nsplit, dv + 4]
+  int B, S_max, H, d, dv;
+  int split_len, nsplit;     // cache slices of split_len keys
+  float lambda, lambda_init, eps, scale;
+};
+
+// V1 decode split rule shared by the workspace query and the launcher.
+void v1_decode_split(int B, int S_max, int H, int* split_len, int* nsplit);
+hipError_t launch_v1_decode(const V1DecodeArgs& a, hipStream_t stream);
+
 // Decode split rule shared by the workspace query and the launcher.
 void decode_split(int B, int S_max, int Hkv, int* split_len, int* nsplit, int* nparts);
 

@@ -165,6 +165,33 @@ V2_DECODE = DecodeWorkload(
     name="v2_decode_bf16_b64_s32768_hq64_hkv8_d128", B=64, S=32768, Hq=64, Hkv=8, d=128,
     std=INV_SQRT_128, seeds=(401, 402, 403, 404))
 
+@dataclass(frozen=True)
+class V1DecodeWorkload:
+    """V1 decode step: q1, q2 [B,H,d], caches k1, k2 [B,S,H,d] and v [B,S,H,dv]."""
+    name: str
+    B: int
+    S: int
+    H: int
+    d: int
+    dv: int
+    std: float
+    seeds: tuple  # q1, q2, k1_cache, k2_cache, v_cache
+    layer: int = 1
+    eps: float = 1e-12
+    cache_lens: tuple | None = None
+
+    def with_shape(self, **kw) -> "V1DecodeWorkload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return V1DecodeWorkload(**d)
+
+
+# The V1 model of the headline prefill (12 heads, d 128, dv 256) decoding against a
+# 32768-entry cache, batch 32: 12.9 GB of K1, K2 and V.
+V1_DECODE = V1DecodeWorkload(
+    name="v1_decode_bf16_b32_s32768_h12_d128_dv256", B=32, S=32768, H=12, d=128, dv=256,
+    std=INV_SQRT_128, seeds=(601, 602, 603, 604, 605))
+
 VARLEN_SEED = 501
 VARLEN_TOTAL = 65536
 VARLEN_LO, VARLEN_HI = 512, 16384
@@ -174,7 +201,8 @@ V2_VARLEN = V2Workload(
     d=128, std=INV_SQRT_128, seeds=(502, 503, 504, 505), logit_mean=2.0, logit_std=1.0,
     lengths=tuple(varlen_lengths(VARLEN_TOTAL, VARLEN_LO, VARLEN_HI, VARLEN_SEED)))
 
-WORKLOADS = {w.name: w for w in (V1_FP32_SMALL, V1_BF16, V2_PREFILL, V2_DECODE, V2_VARLEN)}
+WORKLOADS = {w.name: w for w in (V1_FP32_SMALL, V1_BF16, V2_PREFILL, V2_DECODE, V2_VARLEN,
+                                  V1_DECODE)}
 
 
 # ---------------------------------------------------------------------------
@@ -260,4 +288,22 @@ def decode_inputs(w: DecodeWorkload, device=None) -> dict:
         kc[b].copy_(decode_cache_slice(w, b, "k", device))
         vc[b].copy_(decode_cache_slice(w, b, "v", device))
     out["k_cache"], out["v_cache"] = kc, vc
+    return out
+
+
+def v1_decode_inputs(w: V1DecodeWorkload, device=None) -> dict:
+    """All V1 decode inputs on ``device`` (CPU when None); caches drawn one batch entry at a time."""
+    sq1, sq2, sk1, sk2, sv = w.seeds
+    dev = torch.device("cpu") if device is None else torch.device(device)
+    out = dict(
+        q1=normal((w.B, w.H, w.d), sq1, w.std, device=device),
+        q2=normal((w.B, w.H, w.d), sq2, w.std, device=device),
+        cache_len=None if w.cache_lens is None else torch.tensor(w.cache_lens, dtype=torch.int32,
+                                                                 device=device),
+    )
+    for name, seed, width in (("k1_cache", sk1, w.d), ("k2_cache", sk2, w.d), ("v_cache", sv, w.dv)):
+        t = torch.empty((w.B, w.S, w.H, width), dtype=torch.bfloat16, device=dev)
+        for b in range(w.B):
+            t[b].copy_(normal_slice((w.S, w.H, width), seed, b, w.std, device=device))
+        out[name] = t
     return out

@@ -174,6 +174,38 @@ DIFFATTN_API int diffattn_v2_bwd(const void* q, const void* k, const void* v,
 DIFFATTN_API size_t diffattn_v2_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d);
 
 /*
+ * V1 decode step [P1 "Differential Attention: 빼기의 힘"; norm and factor: P2
+ * §1]: one new query row per (batch entry, head) against the cached K1, K2
+ * and V.  The cache already holds the new token; entry b attends to positions
+ * 0 .. cache_len[b]-1 (all S_max when cache_len == NULL), lengths clamped to
+ * [0, S_max]:
+ *
+ *   z = sum_k (softmax_k(q1 . k1_k / sqrt(d)) - lambda softmax_k(q2 . k2_k / sqrt(d))) v_k,
+ *   y = (1 - lambda_init) * w * z / sqrt(mean_c(z_c^2) + eps).
+ *
+ * An entry with no cached position gives zeros.
+ *
+ *   q1, q2            : [B, H, d] bf16
+ *   k1_cache, k2_cache: [B, S_max, H, d] bf16
+ *   v_cache           : [B, S_max, H, dv] bf16
+ *   cache_len         : DEVICE int32 [B] or NULL
+ *   norm_weight       : [dv] fp32 or NULL (ones)
+ *   out               : [B, H, dv] fp32
+ *   workspace         : device scratch of at least diffattn_v1_decode_workspace_bytes()
+ *                       bytes for per-slice partial results; caller-owned.
+ * Supported: dtype DIFFATTN_BF16, (d, dv) = (128, 256) or (64, 128).
+ */
+DIFFATTN_API int diffattn_v1_decode(const void* q1, const void* q2, const void* k1_cache,
+                       const void* k2_cache, const void* v_cache, const int* cache_len,
+                       const float* norm_weight, float* out, void* workspace,
+                       size_t workspace_bytes, int B, int S_max, int H, int d, int dv,
+                       float lambda, float lambda_init, float eps, diffattn_dtype dtype,
+                       void* stream);
+
+/* Workspace bytes diffattn_v1_decode needs (0 for sizes it would reject). */
+DIFFATTN_API size_t diffattn_v1_decode_workspace_bytes(int B, int S_max, int H, int d, int dv);
+
+/*
  * V2 decode step [P2 §1, §2]: one new query row per sequence against its KV
  * cache.  The cache already holds the new token's K and V; entry b attends to
  * positions 0 .. cache_len[b]-1 (all S_max when cache_len == NULL).  An entry

@@ -460,3 +460,66 @@ def test_v2_backward_full_workload_sampled(gpu):
     note(f"v2 bwd full dk zero-sum: max |sum| / sum|.| = {rel:.3e}")
     assert rel <= 1e-2
     assert torch.isfinite(dv).all()
+
+
+
+# ---------------------------------------------------------------------------
+# V1 decode
+# ---------------------------------------------------------------------------
+
+def run_v1_decode(x, lam, li, eps, weight=None):
+    out = da.v1_decode(x["q1"], x["q2"], x["k1_cache"], x["k2_cache"], x["v_cache"], lam, li, eps,
+                       weight=weight, cache_len=x["cache_len"])
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("B,S,H,d,dv,lens,layer", [(3, 1000, 12, 128, 256, (1000, 1, 517), 1),
+                                                   (2, 777, 4, 128, 256, None, 5),
+                                                   (4, 300, 2, 64, 128, (300, 0, 33, 129), 28),
+                                                   (2, 5000, 6, 128, 256, (4999, 2048), 2),
+                                                   (1, 96, 1, 64, 128, (65,), 1)])
+def test_v1_decode_small(gpu, B, S, H, d, dv, lens, layer):
+    w = inp.V1_DECODE.with_shape(B=B, S=S, H=H, d=d, dv=dv, cache_lens=lens, layer=layer)
+    x = inp.v1_decode_inputs(w)
+    lam = li = oracle.lambda_init(layer)
+    ref = oracle.v1_decode(x["q1"], x["q2"], x["k1_cache"], x["k2_cache"], x["v_cache"], lam, li,
+                           w.eps, cache_len=None if lens is None else np.array(lens))
+    out = run_v1_decode(cuda(x, gpu), lam, li, w.eps)
+    got = out.cpu().numpy()
+    compare(got, ref, rms(x["v_cache"]), TOL_BF16, REL_L2_BF16,
+            what=f"v1 decode B={B} S={S} H={H} d={d} layer={layer}")
+    if lens is not None:
+        for b, n in enumerate(lens):
+            if n == 0:
+                assert np.all(got[b] == 0.0)
+
+
+def test_v1_decode_weight_and_identical_maps(gpu):
+    # a norm weight, and identical maps with lambda = 1: z = 0 exactly, so y = 0
+    w = inp.V1_DECODE.with_shape(B=2, S=400, H=4, cache_lens=(400, 123))
+    x = inp.v1_decode_inputs(w)
+    wt = torch.linspace(0.5, 1.5, 256, dtype=torch.float32)
+    ref = oracle.v1_decode(x["q1"], x["q2"], x["k1_cache"], x["k2_cache"], x["v_cache"], 0.35, 0.4,
+                           1e-6, weight=wt, cache_len=np.array(w.cache_lens))
+    out = run_v1_decode(cuda(x, gpu), 0.35, 0.4, 1e-6, weight=wt.to(gpu))
+    compare(out.cpu().numpy(), ref, rms(x["v_cache"]), TOL_BF16, REL_L2_BF16, what="v1 decode weight")
+    xs = cuda(x, gpu)
+    xs["q2"], xs["k2_cache"] = xs["q1"], xs["k1_cache"]
+    out = run_v1_decode(xs, 1.0, 0.2, 1e-12)
+    assert torch.count_nonzero(out).item() == 0
+
+
+def test_v1_decode_full_workload_sampled_batches(gpu):
+    w = inp.V1_DECODE
+    note(f"generating {w.name} on the GPU (12.9 GB of cache)")
+    x = inp.v1_decode_inputs(w, device=gpu)
+    lam = li = oracle.lambda_init(w.layer)
+    out = run_v1_decode(x, lam, li, w.eps)
+    sel = [0, 17, 31]
+    ref = oracle.v1_decode(x["q1"].cpu(), x["q2"].cpu(), x["k1_cache"][sel].cpu(),
+                           x["k2_cache"][sel].cpu(), x["v_cache"][sel].cpu(), lam, li, w.eps,
+                           batch=sel)
+    got = out[sel].cpu().numpy()
+    ratio = compare(got, ref, rms(x["v_cache"][:1]), TOL_BF16, REL_L2_BF16, what="v1 decode full")
+    note(f"v1 decode full: error ratio {ratio:.3f}")
