@@ -11,7 +11,7 @@
 // so with 8 KV heads the workgroup streams whole 2 KiB cache rows (all heads
 // of a token) at once.  Each wave walks 32-key chunks: K fragments are loaded
 // straight into registers one chunk ahead, V chunks go global->LDS with
-// direct-to-LDS loads into a per-wave double buffer and are read back as the
+// direct-to-LDS buffer loads into a per-wave double buffer and are read back as the
 // V^T MFMA operand with the transposing LDS load.  All query heads of the KV
 // group (up to 16) share one MFMA column block, so each K/V byte is read once.
 // Each wave leaves a partial (O, m, l) per query head; a second kernel merges
@@ -101,7 +101,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
 
   const size_t row_stride = (size_t)a.Hkv * D;  // elements between consecutive keys
   const uint16_t* kbase = a.k_cache + ((size_t)b * a.S_max * a.Hkv + kv) * D;
-  const uint16_t* vbase = a.v_cache + ((size_t)b * a.S_max * a.Hkv + kv) * D;
+  // V: 32-bit byte offsets from the slice start (bounded by one slice)
+  const uint16_t* vslice = a.v_cache + (((size_t)b * a.S_max + s0) * a.Hkv + kv) * D;
 
   auto load_k = [&](int chunk, u32x4 (&kf)[2][NC]) {
     const int base = s0 + chunk * kChunk;
@@ -124,9 +125,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
       constexpr int n32 = D / 16;
       const int vc = (((pos >> 1) ^ (r & (n32 - 1))) << 1) | (pos & 1);
       const int key = min(base + r, s1 - 1);  // rows past the end are masked (P = 0)
-      __builtin_amdgcn_global_load_lds(vbase + (size_t)key * row_stride + vc * 8,
-                                       (__attribute__((address_space(3))) void*)(dst + j * 1024),
-                                       16, 0, 0);
+      dma16(vslice, (uint32_t)(((size_t)(key - s0) * row_stride + vc * 8) * 2), dst + j * 1024);
     }
   };
 
