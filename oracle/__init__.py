@@ -9,9 +9,11 @@ from .diffattn_oracle import (  # noqa: F401
     sigmoid,
     softmax_rows,
     v1_attention,
+    v1_backward,
     v1_decode,
     v1_forward,
     v1_head,
+    v1_head_backward,
     v1_norm,
     v2_backward,
     v2_backward_query_rows,

@@ -51,6 +51,9 @@ dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO), and the gradients of the
 query heads sharing a KV head add up.  Pinned against central finite
 differences of ``v2_forward``.
 
+V1 backward (training): the chain rule through the V1 forward and its norm
+(``v1_head_backward``), likewise pinned by finite differences.
+
 Parity status: every public function here is pinned by tests/test_oracle_pins.py.
 """
 from __future__ import annotations
@@ -169,6 +172,69 @@ def v1_forward(q1, k1, q2, k2, v, lam: float, lam_init: float, eps: float, weigh
     """Full V1 attention output y = (1 - lam_init) * w * z / rms(z): [B, R, H, dv]."""
     z = v1_attention(q1, k1, q2, k2, v, lam, causal, rows)
     return v1_norm(z, lam_init, eps, weight)
+
+
+def v1_head_backward(q1, k1, q2, k2, v, lam: float, lam_init: float, eps: float, dy, weight=None,
+                     causal: bool = True):
+    """Gradients of sum(dy * y) for one (batch, head) slice of the V1 forward.
+
+    The chain rule through ``v1_head`` and ``v1_norm`` (the pages print no gradient):
+    with y = s w z / r, s = 1 - lam_init, r = sqrt(mean(z^2) + eps), g = s w dy,
+        dz = g / r - z <g, z> / (dv r^3),      dw += s dy z / r,
+        dO1 = dz,  dO2 = -lam dz,  dlam = -sum <dz, O2>,
+    and for each map k the softmax-attention backward
+        dP = dO_k v^T,  dS = P_k o (dP - rowsum(dO_k o O_k)),
+        dq_k = dS k_k / sqrt(d),  dk_k = dS^T q_k / sqrt(d),  dv += P_k^T dO_k.
+    q1, k1, q2, k2 [T, d]; v, dy [T, dv].
+    Returns (dq1, dk1, dq2, dk2, dv, dlam, dw).
+    """
+    q1, k1, q2, k2, v, dy = (_f64(a) for a in (q1, k1, q2, k2, v, dy))
+    T, d = q1.shape
+    dvw = v.shape[1]
+    w = np.ones(dvw) if weight is None else _f64(weight)
+    rows = np.arange(T)
+    scale = 1.0 / math.sqrt(d)
+    p1 = _attention_map(q1, k1, rows, scale, causal)
+    p2 = _attention_map(q2, k2, rows, scale, causal)
+    o1, o2 = p1 @ v, p2 @ v
+    z = o1 - lam * o2
+    r = np.sqrt(np.mean(z * z, axis=-1, keepdims=True) + eps)
+    s = 1.0 - lam_init
+    g = s * w * dy
+    dz = g / r - z * np.sum(g * z, axis=-1, keepdims=True) / (dvw * r ** 3)
+    dw = np.sum(s * dy * z / r, axis=0)
+    dlam = -float(np.sum(dz * o2))
+    grads = []
+    dv = np.zeros_like(v)
+    for p, o, q, k, do in ((p1, o1, q1, k1, dz), (p2, o2, q2, k2, -lam * dz)):
+        dp = do @ v.T
+        ds = p * (dp - np.sum(do * o, axis=-1, keepdims=True))
+        grads.append((scale * (ds @ k), scale * (ds.T @ q)))
+        dv += p.T @ do
+    (dq1, dk1), (dq2, dk2) = grads
+    return dq1, dk1, dq2, dk2, dv, dlam, dw
+
+
+def v1_backward(q1, k1, q2, k2, v, lam: float, lam_init: float, eps: float, dy, weight=None,
+                causal: bool = True):
+    """Batch version of ``v1_head_backward``: inputs [B, T, H, d] / [B, T, H, dv], dy like v.
+
+    Returns (dq1, dk1, dq2, dk2, dv, dlam, dw); dlam and dw sum over every (b, t, h).
+    """
+    q1, k1, q2, k2, v, dy = (_f64(a) for a in (q1, k1, q2, k2, v, dy))
+    B, T, H, _ = q1.shape
+    out = [np.zeros_like(q1), np.zeros_like(k1), np.zeros_like(q2), np.zeros_like(k2),
+           np.zeros_like(v)]
+    dlam, dw = 0.0, np.zeros(v.shape[-1])
+    for b in range(B):
+        for h in range(H):
+            g = v1_head_backward(q1[b, :, h], k1[b, :, h], q2[b, :, h], k2[b, :, h], v[b, :, h],
+                                 lam, lam_init, eps, dy[b, :, h], weight, causal)
+            for i in range(5):
+                out[i][b, :, h] = g[i]
+            dlam += g[5]
+            dw += g[6]
+    return (*out, dlam, dw)
 
 
 def v1_decode(q1, q2, k1_cache, k2_cache, v_cache, lam: float, lam_init: float, eps: float,

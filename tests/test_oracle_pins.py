@@ -522,3 +522,63 @@ def test_v1_decode_empty_cache_gives_zeros():
     v = r.normal(size=(1, 6, 2, 8))
     out = oracle.v1_decode(q, q, k, k, v, 0.2, 0.2, 1e-12, cache_len=np.array([0]))
     np.testing.assert_array_equal(out, 0.0)
+
+
+
+# ---------------------------------------------------------------------------
+# V1 backward (chain rule through the forward and the norm; finite differences)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_v1_backward_matches_central_differences_everywhere(causal):
+    r = rng(60)
+    B, T, H, d, dv = 1, 5, 2, 3, 6
+    q1, k1, q2, k2 = (r.normal(size=(B, T, H, d)) for _ in range(4))
+    v = r.normal(size=(B, T, H, dv))
+    dy = r.normal(size=(B, T, H, dv))
+    w = r.normal(size=dv)
+    lam, li, eps = 0.45, 0.2, 1e-3
+    grads = oracle.v1_backward(q1, k1, q2, k2, v, lam, li, eps, dy, weight=w, causal=causal)
+
+    def loss(q1_, k1_, q2_, k2_, v_, lam_, w_):
+        return float(np.sum(dy * oracle.v1_forward(q1_, k1_, q2_, k2_, v_, lam_, li, eps, weight=w_,
+                                                   causal=causal)))
+    args = [q1, k1, q2, k2, v, lam, w]
+    h = 1e-5
+    for which in (0, 1, 2, 3, 4, 6):
+        g = grads[which if which < 5 else 6]
+        fd = np.empty_like(g)
+        for idx in np.ndindex(*g.shape):
+            plus = [a.copy() if isinstance(a, np.ndarray) else a for a in args]
+            minus = [a.copy() if isinstance(a, np.ndarray) else a for a in args]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            fd[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        np.testing.assert_allclose(g, fd, rtol=0, atol=5e-8)
+    lp = args.copy(); lp[5] = lam + h
+    lm = args.copy(); lm[5] = lam - h
+    assert abs(grads[5] - (loss(*lp) - loss(*lm)) / (2 * h)) < 5e-8
+
+
+def test_v1_backward_key_gradients_sum_to_zero_and_norm_is_scale_free():
+    # each map's key gradients sum to zero over keys (softmax shift invariance); the norm
+    # makes y invariant to scaling V (eps = 0), so <dv, v> = 0 over each (b, h)
+    r = rng(61)
+    B, T, H, d, dv = 1, 17, 2, 4, 8
+    q1, k1, q2, k2 = (r.normal(size=(B, T, H, d)) for _ in range(4))
+    v = r.normal(size=(B, T, H, dv))
+    dy = r.normal(size=(B, T, H, dv))
+    dq1, dk1, dq2, dk2, dvv, dlam, dw = oracle.v1_backward(q1, k1, q2, k2, v, 0.3, 0.2, 0.0, dy)
+    np.testing.assert_allclose(dk1.sum(axis=1), 0.0, atol=1e-11)
+    np.testing.assert_allclose(dk2.sum(axis=1), 0.0, atol=1e-11)
+    for h in range(H):
+        assert abs(np.sum(dvv[0, :, h] * v[0, :, h])) < 1e-9 * np.sum(np.abs(dvv[0, :, h] * v[0, :, h]))
+
+
+def test_v1_backward_zero_upstream_gives_zero():
+    r = rng(62)
+    q = r.normal(size=(1, 6, 1, 4))
+    v = r.normal(size=(1, 6, 1, 8))
+    g = oracle.v1_backward(q, q, q, q, v, 0.2, 0.2, 1e-6, np.zeros_like(v))
+    for x in g:
+        np.testing.assert_array_equal(x, 0.0)
