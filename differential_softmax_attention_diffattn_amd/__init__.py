@@ -15,6 +15,10 @@ arithmetic runs in the library's kernels; there is no fallback path.
     v2_fwd_train / v2_bwd
                 V2 training forward (also keeps per-head O and log-sum-exp) and
                 the backward: gradients of q, k, v and the lambda logits
+    v1_fwd_train / v1_bwd
+                V1 training forward (also keeps per-map O and log-sum-exp) and
+                the backward through the norm: gradients of q1, k1, q2, k2, v,
+                lambda and the norm weight
     lambda_init 0.8 - 0.6 exp(-0.3 (l - 1))
 """
 from __future__ import annotations
@@ -29,11 +33,14 @@ __all__ = [
     "v1_decode",
     "v2_fwd_train",
     "v2_bwd",
+    "v1_fwd_train",
+    "v1_bwd",
     "lambda_init",
     "v1_workspace_bytes",
     "v2_decode_workspace_bytes",
     "v1_decode_workspace_bytes",
     "v2_bwd_workspace_bytes",
+    "v1_bwd_workspace_bytes",
     "DiffAttnError",
 ]
 
@@ -130,6 +137,102 @@ def v1_fwd(q1, k1, q2, k2, v, lam: float, lambda_init: float, eps: float = 1e-12
             _ptr(workspace), ws_bytes, _stream(dev))
     _lib.check("diffattn_v1_fwd", rc)
     return out
+
+
+def _v1_bf16_check(q1, k1, q2, k2, v, weight):
+    torch = _torch()
+    dev = q1.device
+    _check_tensor("q1", q1, dtype=torch.bfloat16, dim=4)
+    for n, t in (("k1", k1), ("q2", q2), ("k2", k2)):
+        _check_tensor(n, t, dtype=torch.bfloat16, dim=4, device=dev)
+        if t.shape != q1.shape:
+            raise ValueError(f"{n} shape {tuple(t.shape)} != q1 shape {tuple(q1.shape)}")
+    _check_tensor("v", v, dtype=torch.bfloat16, dim=4, device=dev)
+    B, T, H, d = q1.shape
+    if tuple(v.shape[:3]) != (B, T, H):
+        raise ValueError(f"v shape {tuple(v.shape)} does not match q1 {tuple(q1.shape)}")
+    dv = v.shape[3]
+    if weight is not None:
+        _check_tensor("weight", weight, dtype=torch.float32, dim=1, device=dev)
+        if weight.shape[0] != dv:
+            raise ValueError("weight must have dv entries")
+    return B, T, H, d, dv
+
+
+def v1_fwd_train(q1, k1, q2, k2, v, lam: float, lambda_init: float, eps: float = 1e-12,
+                 weight=None, causal: bool = True, workspace=None):
+    """DIFF V1 training forward (bf16 inputs).
+
+    Returns (out [B,T,H,dv], o1 [B,T,H,dv], o2 [B,T,H,dv], lse [B,T,H,2]), all
+    fp32: o1, o2 are the per-map normalised outputs, lse their log-sum-exp.
+    """
+    torch = _torch()
+    dev = q1.device
+    B, T, H, d, dv = _v1_bf16_check(q1, k1, q2, k2, v, weight)
+    out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    o1 = torch.empty_like(out)
+    o2 = torch.empty_like(out)
+    lse = torch.empty((B, T, H, 2), dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    need = int(lib.diffattn_v1_workspace_bytes(B, T, H, d, dv, DIFFATTN_BF16))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _check_tensor("workspace", workspace, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        rc = lib.diffattn_v1_fwd_train(
+            _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(weight), _ptr(out), _ptr(o1),
+            _ptr(o2), _ptr(lse), B, T, H, d, dv, float(lam), float(lambda_init), float(eps),
+            1 if causal else 0, DIFFATTN_BF16, _ptr(workspace), ws_bytes, _stream(dev))
+    _lib.check("diffattn_v1_fwd_train", rc)
+    return out, o1, o2, lse
+
+
+def v1_bwd_workspace_bytes(B, T, H, d, dv) -> int:
+    return int(_lib.load().diffattn_v1_bwd_workspace_bytes(B, T, H, d, dv))
+
+
+def v1_bwd(q1, k1, q2, k2, v, o1, o2, lse, dy, lam: float, lambda_init: float,
+           eps: float = 1e-12, weight=None, causal: bool = True, workspace=None):
+    """DIFF V1 backward (bf16 inputs): gradients of sum(dy * y).
+
+    o1, o2, lse from v1_fwd_train on the same inputs; dy [B,T,H,dv] fp32 ->
+    (dq1, dk1, dq2, dk2 [B,T,H,d], dv [B,T,H,dv], dlambda [1], dweight [dv]),
+    all fp32.  dweight is the gradient of the norm weight (ones when weight is None).
+    """
+    torch = _torch()
+    dev = q1.device
+    B, T, H, d, dv = _v1_bf16_check(q1, k1, q2, k2, v, weight)
+    for n, t in (("o1", o1), ("o2", o2), ("dy", dy)):
+        _check_tensor(n, t, dtype=torch.float32, dim=4, device=dev)
+        if tuple(t.shape) != (B, T, H, dv):
+            raise ValueError(f"{n} must have shape {(B, T, H, dv)}")
+    _check_tensor("lse", lse, dtype=torch.float32, dim=4, device=dev)
+    if tuple(lse.shape) != (B, T, H, 2):
+        raise ValueError(f"lse must have shape {(B, T, H, 2)}")
+    dq1 = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
+    dk1 = torch.empty_like(dq1)
+    dq2 = torch.empty_like(dq1)
+    dk2 = torch.empty_like(dq1)
+    dvv = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    dlam = torch.empty(1, dtype=torch.float32, device=dev)
+    dw = torch.empty(dv, dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    need = int(lib.diffattn_v1_bwd_workspace_bytes(B, T, H, d, dv))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _check_tensor("workspace", workspace, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        rc = lib.diffattn_v1_bwd(
+            _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(weight), _ptr(o1), _ptr(o2),
+            _ptr(lse), _ptr(dy), _ptr(dq1), _ptr(dk1), _ptr(dq2), _ptr(dk2), _ptr(dvv), _ptr(dlam),
+            _ptr(dw), B, T, H, d, dv, float(lam), float(lambda_init), float(eps),
+            1 if causal else 0, DIFFATTN_BF16, _ptr(workspace), ws_bytes, _stream(dev))
+    _lib.check("diffattn_v1_bwd", rc)
+    return dq1, dk1, dq2, dk2, dvv, dlam, dw
 
 
 def v2_fwd(q, k, v, logit, cu_seqlens=None, max_seqlen=None, causal: bool = True,

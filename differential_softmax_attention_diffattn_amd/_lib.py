@@ -33,6 +33,12 @@ SIGNATURES = {
     "diffattn_v1_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _f, _i,
                              _i, _vp, _sz, _vp]),
     "diffattn_v1_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "diffattn_v1_fwd_train": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
+                                   _i, _f, _f, _f, _i, _i, _vp, _sz, _vp]),
+    "diffattn_v1_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _f, _i, _i, _vp, _sz,
+                             _vp]),
+    "diffattn_v1_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "diffattn_v2_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i,
                              _vp]),
     "diffattn_v2_fwd_train": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,

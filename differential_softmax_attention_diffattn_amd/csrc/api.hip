@@ -79,6 +79,44 @@ bool v1_shape_supported(int d, int dv, diffattn_dtype dt) {
   return false;
 }
 
+// Checks shared by the V1 forward and training-forward entry points: sizes,
+// dtype, flags, shape support, alignment and workspace; DIFFATTN_OK or a code.
+int v1_fwd_check(const char* fn, const void* const* ptrs, int nptrs,
+                        const float* norm_weight, int B, int T, int H, int d, int dv,
+                        float lambda, float lambda_init, float eps, int causal,
+                        diffattn_dtype in_dtype, void* workspace, size_t workspace_bytes) {
+  for (int i = 0; i < nptrs; ++i)
+    if (!ptrs[i]) return fail(DIFFATTN_E_INVALID, "%s: null tensor pointer", fn);
+  if (B < 0 || T < 0 || H < 0 || d <= 0 || dv <= 0)
+    return fail(DIFFATTN_E_INVALID, "%s: bad sizes B=%d T=%d H=%d d=%d dv=%d", fn, B, T, H, d, dv);
+  if (in_dtype != DIFFATTN_F32 && in_dtype != DIFFATTN_BF16)
+    return fail(DIFFATTN_E_INVALID, "%s: unknown dtype %d", fn, (int)in_dtype);
+  if (causal != 0 && causal != 1) return fail(DIFFATTN_E_INVALID, "%s: causal must be 0 or 1", fn);
+  if (!isfinite(lambda) || !isfinite(lambda_init) || !isfinite(eps) || eps < 0.f)
+    return fail(DIFFATTN_E_INVALID, "%s: lambda, lambda_init must be finite and eps finite >= 0", fn);
+  if (!v1_shape_supported(d, dv, in_dtype))
+    return fail(DIFFATTN_E_UNSUPPORTED,
+                "%s: (d=%d, dv=%d) not supported for %s inputs (fp32: multiples of 16, d<=128, "
+                "dv<=256; bf16: (128,256) or (64,128))",
+                fn, d, dv, in_dtype == DIFFATTN_F32 ? "fp32" : "bf16");
+  const long long nout = prod({B, T, H, dv});
+  if (nout < 0 || prod({B, T, H, d}) < 0 || nout > (1LL << 40))
+    return fail(DIFFATTN_E_INVALID, "%s: problem too large", fn);
+  for (int i = 0; i < nptrs; ++i)
+    if (!aligned16(ptrs[i]))
+      return fail(DIFFATTN_E_ALIGN, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (norm_weight && !aligned4(norm_weight))
+    return fail(DIFFATTN_E_ALIGN, "%s: norm_weight must be 4-byte aligned", fn);
+  if (nout == 0) return DIFFATTN_OK;
+  const size_t need = diffattn_v1_workspace_bytes(B, T, H, d, dv, in_dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(DIFFATTN_E_WORKSPACE, "%s: workspace of %zu bytes required (got %zu%s)", fn, need,
+                workspace_bytes, workspace ? "" : ", NULL");
+  if (need > 0 && !aligned16(workspace))
+    return fail(DIFFATTN_E_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  return DIFFATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -108,41 +146,114 @@ int diffattn_v1_fwd(const void* q1, const void* k1, const void* q2, const void* 
                     diffattn_dtype in_dtype, void* workspace, size_t workspace_bytes,
                     void* stream) {
   const char* fn = "diffattn_v1_fwd";
-  if (!q1 || !k1 || !q2 || !k2 || !v || !out)
-    return fail(DIFFATTN_E_INVALID, "%s: null tensor pointer", fn);
-  if (B < 0 || T < 0 || H < 0 || d <= 0 || dv <= 0)
-    return fail(DIFFATTN_E_INVALID, "%s: bad sizes B=%d T=%d H=%d d=%d dv=%d", fn, B, T, H, d, dv);
-  if (in_dtype != DIFFATTN_F32 && in_dtype != DIFFATTN_BF16)
-    return fail(DIFFATTN_E_INVALID, "%s: unknown dtype %d", fn, (int)in_dtype);
-  if (causal != 0 && causal != 1) return fail(DIFFATTN_E_INVALID, "%s: causal must be 0 or 1", fn);
-  if (!isfinite(lambda) || !isfinite(lambda_init) || !isfinite(eps) || eps < 0.f)
-    return fail(DIFFATTN_E_INVALID, "%s: lambda, lambda_init must be finite and eps finite >= 0", fn);
-  if (!v1_shape_supported(d, dv, in_dtype))
-    return fail(DIFFATTN_E_UNSUPPORTED,
-                "%s: (d=%d, dv=%d) not supported for %s inputs (fp32: multiples of 16, d<=128, "
-                "dv<=256; bf16: (128,256) or (64,128))",
-                fn, d, dv, in_dtype == DIFFATTN_F32 ? "fp32" : "bf16");
-  const long long nout = prod({B, T, H, dv});
-  if (nout < 0 || prod({B, T, H, d}) < 0 || nout > (1LL << 40))
-    return fail(DIFFATTN_E_INVALID, "%s: problem too large", fn);
   const void* ptrs[] = {q1, k1, q2, k2, v, out};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return fail(DIFFATTN_E_ALIGN, "%s: tensor pointers must be 16-byte aligned", fn);
-  if (norm_weight && !aligned4(norm_weight))
-    return fail(DIFFATTN_E_ALIGN, "%s: norm_weight must be 4-byte aligned", fn);
-  if (nout == 0) return ok();
-  const size_t need = diffattn_v1_workspace_bytes(B, T, H, d, dv, in_dtype);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(DIFFATTN_E_WORKSPACE, "%s: workspace of %zu bytes required (got %zu%s)", fn, need,
-                workspace_bytes, workspace ? "" : ", NULL");
-  if (need > 0 && !aligned16(workspace))
-    return fail(DIFFATTN_E_ALIGN, "%s: workspace must be 16-byte aligned", fn);
-
+  const int rc = v1_fwd_check(fn, ptrs, 6, norm_weight, B, T, H, d, dv, lambda, lambda_init, eps,
+                              causal, in_dtype, workspace, workspace_bytes);
+  if (rc != DIFFATTN_OK) return rc;
+  if (prod({B, T, H}) == 0) return ok();
   diffattn::V1Args a{q1, k1, q2, k2, v, norm_weight, out, B, T, H, d, dv,
                      lambda, lambda_init, eps, causal};
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (in_dtype == DIFFATTN_F32) return from_hip(diffattn::launch_v1_f32(a, s), fn);
   return from_hip(diffattn::launch_v1_bf16(a, workspace, s), fn);
+}
+
+int diffattn_v1_fwd_train(const void* q1, const void* k1, const void* q2, const void* k2,
+                          const void* v, const float* norm_weight, float* out, float* o1,
+                          float* o2, float* lse, int B, int T, int H, int d, int dv, float lambda,
+                          float lambda_init, float eps, int causal, diffattn_dtype in_dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "diffattn_v1_fwd_train";
+  if (in_dtype != DIFFATTN_BF16)
+    return fail(in_dtype == DIFFATTN_F32 ? DIFFATTN_E_UNSUPPORTED : DIFFATTN_E_INVALID,
+                "%s: only bf16 inputs are supported", fn);
+  const void* ptrs[] = {q1, k1, q2, k2, v, out, o1, o2, lse};
+  const int rc = v1_fwd_check(fn, ptrs, 9, norm_weight, B, T, H, d, dv, lambda, lambda_init, eps,
+                              causal, in_dtype, workspace, workspace_bytes);
+  if (rc != DIFFATTN_OK) return rc;
+  if (prod({B, T, H}) == 0) return ok();
+  diffattn::V1Args a{q1, k1, q2, k2, v, norm_weight, out, B, T, H, d, dv,
+                     lambda, lambda_init, eps, causal, o1, o2, lse};
+  return from_hip(diffattn::launch_v1_bf16(a, workspace, static_cast<hipStream_t>(stream)), fn);
+}
+
+size_t diffattn_v1_bwd_workspace_bytes(int B, int T, int H, int d, int dv) {
+  if (B < 0 || T < 0 || H < 0 || !v1_shape_supported(d, dv, DIFFATTN_BF16)) return 0;
+  if (prod({B, T, H, dv}) <= 0) return 0;
+  return diffattn::v1_bwd_workspace_bytes(B, T, H, d, dv);
+}
+
+int diffattn_v1_bwd(const void* q1, const void* k1, const void* q2, const void* k2,
+                    const void* v, const float* norm_weight, const float* o1, const float* o2,
+                    const float* lse, const float* dy, float* dq1, float* dk1, float* dq2,
+                    float* dk2, float* dv_out, float* dlambda, float* dnorm_weight, int B, int T,
+                    int H, int d, int dv, float lambda, float lambda_init, float eps, int causal,
+                    diffattn_dtype in_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  const char* fn = "diffattn_v1_bwd";
+  if (in_dtype != DIFFATTN_BF16)
+    return fail(in_dtype == DIFFATTN_F32 ? DIFFATTN_E_UNSUPPORTED : DIFFATTN_E_INVALID,
+                "%s: only bf16 inputs are supported", fn);
+  if (!dlambda || !dnorm_weight) return fail(DIFFATTN_E_INVALID, "%s: null dlambda or dnorm_weight", fn);
+  if (B < 0 || T < 0 || H < 0 || d <= 0 || dv <= 0)
+    return fail(DIFFATTN_E_INVALID, "%s: bad sizes B=%d T=%d H=%d d=%d dv=%d", fn, B, T, H, d, dv);
+  if (causal != 0 && causal != 1) return fail(DIFFATTN_E_INVALID, "%s: causal must be 0 or 1", fn);
+  if (!isfinite(lambda) || !isfinite(lambda_init) || !isfinite(eps) || eps < 0.f)
+    return fail(DIFFATTN_E_INVALID, "%s: lambda, lambda_init must be finite and eps finite >= 0", fn);
+  if (!v1_shape_supported(d, dv, in_dtype))
+    return fail(DIFFATTN_E_UNSUPPORTED, "%s: (d=%d, dv=%d) not in {(128, 256), (64, 128)}", fn, d,
+                dv);
+  const long long nout = prod({B, T, H, dv});
+  if (nout < 0 || nout > (1LL << 40)) return fail(DIFFATTN_E_INVALID, "%s: problem too large", fn);
+  // with no rows the tensors are not read: only dlambda and dnorm_weight must be valid
+  const void* ptrs[] = {q1, k1, q2, k2, v, o1, o2, dy, dq1, dk1, dq2, dk2, dv_out};
+  if (nout != 0) {
+    for (const void* p : ptrs)
+      if (!p) return fail(DIFFATTN_E_INVALID, "%s: null tensor pointer", fn);
+    if (!lse) return fail(DIFFATTN_E_INVALID, "%s: null lse", fn);
+    for (const void* p : ptrs)
+      if (!aligned16(p))
+        return fail(DIFFATTN_E_ALIGN, "%s: tensor pointers must be 16-byte aligned", fn);
+  }
+  if (!aligned4(lse) || !aligned4(dlambda) || !aligned4(dnorm_weight) ||
+      (norm_weight && !aligned4(norm_weight)))
+    return fail(DIFFATTN_E_ALIGN, "%s: lse, norm_weight, dlambda and dnorm_weight must be 4-byte aligned", fn);
+  // with no rows only the parameter gradients (sums over nothing) are written
+  const size_t need = diffattn_v1_bwd_workspace_bytes(B, T, H, d, dv);
+  if (nout != 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(DIFFATTN_E_WORKSPACE, "%s: workspace of %zu bytes required (got %zu%s)", fn, need,
+                workspace_bytes, workspace ? "" : ", NULL");
+  if (nout != 0 && !aligned16(workspace))
+    return fail(DIFFATTN_E_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  diffattn::V1BwdArgs a{};
+  a.q1 = static_cast<const uint16_t*>(q1);
+  a.k1 = static_cast<const uint16_t*>(k1);
+  a.q2 = static_cast<const uint16_t*>(q2);
+  a.k2 = static_cast<const uint16_t*>(k2);
+  a.v = static_cast<const uint16_t*>(v);
+  a.norm_weight = norm_weight;
+  a.o1 = o1;
+  a.o2 = o2;
+  a.lse = lse;
+  a.dy = dy;
+  a.dq1 = dq1;
+  a.dk1 = dk1;
+  a.dq2 = dq2;
+  a.dk2 = dk2;
+  a.dvg = dv_out;
+  a.dlambda = dlambda;
+  a.dnorm_weight = dnorm_weight;
+  a.workspace = workspace;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.d = d;
+  a.dv = dv;
+  a.lambda = lambda;
+  a.lambda_init = lambda_init;
+  a.eps = eps;
+  a.causal = causal;
+  return from_hip(diffattn::launch_v1_backward(a, static_cast<hipStream_t>(stream)), fn);
 }
 
 int diffattn_v2_fwd(const void* q, const void* k, const void* v, const float* lambda_logit,

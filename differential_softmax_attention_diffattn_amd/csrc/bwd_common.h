@@ -1,0 +1,64 @@
+// Tile helpers shared by the backward kernels (V1 and V2): swizzled LDS
+// layouts of 64-row bf16 tiles and their direct-to-LDS loader.
+#pragma once
+
+#include "device_common.h"
+
+namespace diffattn {
+namespace bwd {
+
+constexpr int kWaves = 8;  // waves of the 512-thread backward workgroups
+
+template <int D>
+struct BTile {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;  // 16-byte chunks per row
+  static constexpr int kBytes = 64 * kRowBytes;
+  static constexpr int kInstr = kBytes / 1024;
+};
+
+// Two LDS layouts of a 64-row bf16 tile (row-major, swizzled):
+//  * rows: 16-byte chunk c of row r at position c ^ (r mod nchunks), for
+//    16-byte row reads (an MFMA operand whose k index runs along a row);
+//  * trans: 32-byte chunk c of row r at position c ^ (r mod D/16), for the
+//    transposing read (an operand whose k index runs down the rows).
+template <int D>
+__device__ __forceinline__ int rows_offset(int row, int chunk) {
+  return row * BTile<D>::kRowBytes + ((chunk ^ (row & (BTile<D>::kChunks - 1))) << 4);
+}
+template <int D>
+__device__ __forceinline__ int trans_offset(int row, int byte_in_row) {
+  constexpr int n32 = D / 16;
+  const int c32 = byte_in_row >> 5;
+  return row * BTile<D>::kRowBytes + ((c32 ^ (row & (n32 - 1))) << 5) + (byte_in_row & 31);
+}
+
+// Direct-to-LDS load of a 64-row tile: rows r0 .. r0+63 of a bf16 matrix whose
+// consecutive rows are `stride` elements apart, rows >= n_valid clamped to the
+// last valid row (their values are masked by the caller).  TRANS selects the
+// layout.  Each wave issues kInstr / NW loads of 1 KiB.
+template <int D, bool TRANS, int NW = kWaves>
+__device__ __forceinline__ void load_tile(const uint16_t* base, size_t stride, int n_valid,
+                                          uint8_t* lds, int wave, int lane) {
+  using TL = BTile<D>;
+#pragma unroll
+  for (int j = 0; j < (TL::kInstr + NW - 1) / NW; ++j) {
+    const int blk = wave + j * NW;
+    if (TL::kInstr % NW != 0 && blk >= TL::kInstr) break;
+    const int off = blk * 1024 + lane * 16;  // LDS byte this lane fills
+    const int r = off / TL::kRowBytes;
+    const int pos = (off % TL::kRowBytes) >> 4;
+    int lc;  // logical 16-byte chunk stored at that position
+    if (TRANS) {
+      constexpr int n32 = D / 16;
+      lc = (((pos >> 1) ^ (r & (n32 - 1))) << 1) | (pos & 1);
+    } else {
+      lc = pos ^ (r & (TL::kChunks - 1));
+    }
+    const size_t row = (size_t)min(r, n_valid - 1);
+    dma16(base, (uint32_t)((row * stride + lc * 8) * 2), lds + blk * 1024);
+  }
+}
+
+}  // namespace bwd
+}  // namespace diffattn

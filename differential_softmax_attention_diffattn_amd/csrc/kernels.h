@@ -20,6 +20,34 @@ struct V1Args {
   int B, T, H, d, dv;
   float lambda, lambda_init, eps;
   int causal;
+  float* o1;                 // fp32 [B,T,H,dv] normalised O of map 1, or nullptr (training forward)
+  float* o2;                 // fp32 [B,T,H,dv] normalised O of map 2
+  float* lse;                // fp32 [B,T,H,2] natural-log log-sum-exp of both maps
+};
+
+// V1 backward.  Gradients of sum(dy * y) of the V1 forward and its norm.
+struct V1BwdArgs {
+  const uint16_t* q1;        // bf16 [B,T,H,d]
+  const uint16_t* k1;
+  const uint16_t* q2;
+  const uint16_t* k2;
+  const uint16_t* v;         // bf16 [B,T,H,dv]
+  const float* norm_weight;  // [dv] or nullptr
+  const float* o1;           // fp32 [B,T,H,dv] (training forward)
+  const float* o2;
+  const float* lse;          // fp32 [B,T,H,2]
+  const float* dy;           // fp32 [B,T,H,dv]
+  float* dq1;                // fp32 [B,T,H,d]
+  float* dk1;
+  float* dq2;
+  float* dk2;
+  float* dvg;                // fp32 [B,T,H,dv] (gradient of v)
+  float* dlambda;            // fp32 [1]
+  float* dnorm_weight;       // fp32 [dv]
+  void* workspace;
+  int B, T, H, d, dv;
+  float lambda, lambda_init, eps;
+  int causal;
 };
 
 struct V2Args {
@@ -97,6 +125,9 @@ hipError_t launch_v1_f32(const V1Args& a, hipStream_t stream);
 // bf16 V1 needs a workspace for V packed as fp16 tiles (see v1_prefill.hip).
 size_t v1_bf16_workspace_bytes(int B, int T, int H, int d, int dv);
 hipError_t launch_v1_bf16(const V1Args& a, void* workspace, hipStream_t stream);
+// V1 backward workspace: dz (bf16), per-row stats and reduction partials (see v1_backward.hip).
+size_t v1_bwd_workspace_bytes(int B, int T, int H, int d, int dv);
+hipError_t launch_v1_backward(const V1BwdArgs& a, hipStream_t stream);
 hipError_t launch_v2_prefill(const V2Args& a, hipStream_t stream);
 // V2 backward workspace: per-row delta, log2 lse and sigmoid (see v2_backward.hip).
 size_t v2_bwd_workspace_bytes(int B, int T, int Hq);

@@ -1,0 +1,626 @@
+// DIFF V1 backward on gfx950: gradients of sum(dy * y) of the V1 forward
+//     z = (softmax(Q1 K1^T / sqrt d) - lambda softmax(Q2 K2^T / sqrt d)) V,
+//     y = (1 - lambda_init) * w * z / sqrt(mean(z^2) + eps)
+// ("Differential Transformer | ICLR 2025 Oral" blog, section "Differential
+// Attention: 빼기의 힘"; the norm and factor from the V1 recap of the
+// "Differential Transformer V2" summary, 상세 정리 §1).  The pages print no
+// gradient; this is the chain rule through that forward.  Per (row, head),
+// with s = 1 - lambda_init, r = sqrt(mean(z^2) + eps) and g = s w dy:
+//     dz = g / r - z <g, z> / (dv r^3),   dw += s dy z / r,   dlambda -= <dz, O2>,
+//     dO1 = dz,  dO2 = -lambda dz,
+// and for each map the softmax-attention backward with P recomputed from the
+// forward's log-sum-exp; both maps read the same V, so dP2 = -lambda dP1 and
+// dV = (P1 - lambda P2)^T dz are formed once.
+//
+// Kernels:
+//  * v1_bwd_pre_kernel (one wave per row): z from the forward's per-map O, dz
+//    (stored bf16 as the MFMA operand), D_k = rowsum(dO_k o O_k) from the
+//    rounded dz, log2-unit log-sum-exp, per-block partial sums of dlambda and
+//    dw; stats stored [B][H][4][T rounded up to 64] so a tile's row values
+//    are contiguous.  v1_bwd_reduce_kernel sums the partials in a fixed order.
+//  * v1_bwd_dq_kernel: a wave owns 16 query rows of one (batch, head) and both
+//    maps, lanes own query columns; K1, K2 and V tiles of 64 keys stream
+//    through LDS: S1^T, S2^T, dP^T = V dz^T, dS^T, dQ_k^T += K_k^T dS_k^T.
+//  * v1_bwd_dkdv_kernel: a workgroup of 4 waves owns 64 keys of one (batch,
+//    head), a wave 16 keys with their K1, K2 and V fragments in registers
+//    (lanes own key columns); Q1, Q2 and dz tiles of 64 rows stream through
+//    LDS: S1, S2, dP = dz V^T, dS, dV += (P1 - lambda P2)^T dz,
+//    dK_k += dS_k^T Q_k.
+// MFMA work is 16x16x32 bf16 with fp32 accumulation; P, dS and dz are rounded
+// to bf16 as operands.
+#include <math.h>
+
+#include "bwd_common.h"
+#include "device_common.h"
+#include "kernels.h"
+
+namespace diffattn {
+namespace {
+
+using bwd::BTile;
+using bwd::load_tile;
+using bwd::rows_offset;
+using bwd::trans_offset;
+
+constexpr int kKeys = 64;     // keys per staged tile (dq)
+constexpr int kQRows = 64;    // query rows per staged tile (dkdv)
+constexpr int kRows = 16;     // query rows per wave (dq)
+constexpr int kDqWaves = 8;   // dq: 128 query rows per workgroup
+constexpr int kKvWaves = 4;   // dkdv: 64 keys per workgroup, one wave per SIMD
+constexpr int kPreBlocks = 1024;
+
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
+int pad64(int T) { return (T + 63) / 64 * 64; }
+
+// ---------------------------------------------------------------------------
+// Preprocessing: one wave per (row, head), grid-stride; per-block partials.
+// ---------------------------------------------------------------------------
+template <int DV>
+__global__ __launch_bounds__(256) void v1_bwd_pre_kernel(V1BwdArgs a, int Tp, uint16_t* dz,
+                                                         float* stats, float* part) {
+  constexpr int E = DV / 64;  // channels per lane
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const float s = 1.0f - a.lambda_init;
+  float w[E], dw_acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    w[e] = a.norm_weight ? a.norm_weight[lane * E + e] : 1.0f;
+    dw_acc[e] = 0.f;
+  }
+  float dl_acc = 0.f;
+  const long long n_items = (long long)a.B * a.H * Tp;
+  for (long long item = (long long)blockIdx.x * 4 + wave; item < n_items;
+       item += (long long)gridDim.x * 4) {
+    const int t = (int)(item % Tp);
+    const long long bh = item / Tp;
+    const int h = (int)(bh % a.H);
+    const int b = (int)(bh / a.H);
+    float* st = stats + (size_t)bh * 4 * Tp + t;  // [b][h][k][t] at st[k * Tp]
+    if (t >= a.T) {  // padding rows: finite zeros (tiles read and mask them)
+      if (lane == 0) st[0] = st[Tp] = st[2 * Tp] = st[3 * Tp] = 0.f;
+      continue;
+    }
+    const size_t r = ((size_t)b * a.T + t) * a.H + h;
+    float dy[E], o1[E], o2[E], z[E];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const size_t c = r * DV + lane * E + e;
+      dy[e] = a.dy[c];
+      o1[e] = a.o1[c];
+      o2[e] = a.o2[c];
+      z[e] = fmaf(-a.lambda, o2[e], o1[e]);  // as the forward forms it
+      ss = fmaf(z[e], z[e], ss);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+    const float rr = sqrtf(ss * (1.0f / DV) + a.eps);
+    const float ir = 1.0f / rr;
+    float g[E], gz = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      g[e] = s * w[e] * dy[e];
+      gz = fmaf(g[e], z[e], gz);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) gz += __shfl_xor(gz, m);
+    const float cz = gz * ir * ir * ir * (1.0f / DV);
+    float d1 = 0.f, d2 = 0.f, dl = 0.f;
+    uint16_t zb[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float dzv = fmaf(g[e], ir, -z[e] * cz);
+      zb[e] = f32_to_bf16(dzv);
+      const float dzr = bf16_to_f32(zb[e]);  // the operand the MFMAs see
+      d1 = fmaf(dzr, o1[e], d1);
+      d2 = fmaf(dzr, o2[e], d2);
+      dl = fmaf(-dzv, o2[e], dl);
+      dw_acc[e] = fmaf(s * dy[e] * z[e], ir, dw_acc[e]);
+    }
+    dl_acc += dl;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      d1 += __shfl_xor(d1, m);
+      d2 += __shfl_xor(d2, m);
+    }
+    uint16_t* dzr = dz + r * DV + lane * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) dzr[e] = zb[e];
+    if (lane == 0) {
+      st[0] = a.lse[r * 2] * kLog2e;
+      st[Tp] = a.lse[r * 2 + 1] * kLog2e;
+      st[2 * Tp] = d1;
+      st[3 * Tp] = -a.lambda * d2;
+    }
+  }
+  // block partials: [dlambda, pad x3, dw[DV]]
+  __shared__ float red[4][DV];
+  __shared__ float redl[4];
+#pragma unroll
+  for (int e = 0; e < E; ++e) red[wave][lane * E + e] = dw_acc[e];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) dl_acc += __shfl_xor(dl_acc, m);
+  if (lane == 0) redl[wave] = dl_acc;
+  __syncthreads();
+  float* pb = part + (size_t)blockIdx.x * (DV + 4);
+  for (int c = threadIdx.x; c < DV; c += blockDim.x)
+    pb[4 + c] = red[0][c] + red[1][c] + red[2][c] + red[3][c];
+  if (threadIdx.x == 0) pb[0] = redl[0] + redl[1] + redl[2] + redl[3];
+}
+
+// Fixed-order sums of the per-block partials into dlambda and dw.
+template <int DV>
+__global__ __launch_bounds__(256) void v1_bwd_reduce_kernel(V1BwdArgs a, const float* part,
+                                                            int nblk) {
+  if (a.dnorm_weight != nullptr) {
+    for (int c = threadIdx.x; c < DV; c += blockDim.x) {
+      float acc = 0.f;
+      for (int k = 0; k < nblk; ++k) acc += part[(size_t)k * (DV + 4) + 4 + c];
+      a.dnorm_weight[c] = acc;
+    }
+  }
+  if (a.dlambda != nullptr && threadIdx.x < kWave) {
+    float acc = 0.f;
+    for (int k = threadIdx.x; k < nblk; k += kWave) acc += part[(size_t)k * (DV + 4)];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (threadIdx.x == 0) a.dlambda[0] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ1 and dQ2: a wave owns 16 query rows of one (batch, head).
+// ---------------------------------------------------------------------------
+template <int D, int DV, bool CAUSAL>
+__global__ __launch_bounds__(kDqWaves * kWave, 1) void v1_bwd_dq_kernel(V1BwdArgs a, int Tp,
+                                                                       const uint16_t* dz,
+                                                                       const float* stats) {
+  using TK = BTile<D>;
+  using TV = BTile<DV>;
+  constexpr int NC = D / 32;
+  constexpr int NCV = DV / 32;
+  constexpr int NDB = D / 16;
+  constexpr int QTILE = kDqWaves * kRows;
+  __shared__ __align__(16) uint8_t k1b0[TK::kBytes];
+  __shared__ __align__(16) uint8_t k1b1[TK::kBytes];
+  __shared__ __align__(16) uint8_t k2b0[TK::kBytes];
+  __shared__ __align__(16) uint8_t k2b1[TK::kBytes];
+  __shared__ __align__(16) uint8_t vb0[TV::kBytes];
+  __shared__ __align__(16) uint8_t vb1[TV::kBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+  const int T = a.T;
+  const int BH = a.B * a.H;
+  const int n_qt = (T + QTILE - 1) / QTILE;
+  const int jr = blockIdx.x / BH;  // longest query tiles first over all (batch, head)
+  const int bh = blockIdx.x - jr * BH;
+  const int qt = n_qt - 1 - jr;
+  const int b = bh / a.H;
+  const int h = bh - b * a.H;
+  const int q_lo = qt * QTILE + wave * kRows;
+  const bool wave_active = q_lo < T;
+  const int q_end_block = min(qt * QTILE + QTILE, T);
+  const int n_kt = CAUSAL ? (q_end_block - 1) / kKeys + 1 : (T + kKeys - 1) / kKeys;
+  const int wave_key_end = CAUSAL ? min(q_lo + kRows, T) : T;
+
+  const float cs = kLog2e / sqrtf((float)D);
+  const int row = q_lo + c16;  // this lane's query column
+  const int rowc = min(row, T - 1);
+  const size_t rq = ((size_t)b * T + rowc) * a.H + h;
+  u32x4 q1f[NC], q2f[NC], dzf[NCV];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    q1f[c] = ldg128(a.q1 + rq * D + c * 32 + g * 8);
+    q2f[c] = ldg128(a.q2 + rq * D + c * 32 + g * 8);
+  }
+#pragma unroll
+  for (int c = 0; c < NCV; ++c) dzf[c] = ldg128(dz + rq * DV + c * 32 + g * 8);
+  const float* st = stats + (size_t)bh * 4 * Tp + rowc;
+  const float l21 = st[0], l22 = st[Tp], dd1 = st[2 * Tp], dd2 = st[3 * Tp];
+
+  const size_t kstr = (size_t)a.H * D, vstr = (size_t)a.H * DV;
+  const uint16_t* k1g = a.k1 + ((size_t)b * T * a.H + h) * D;
+  const uint16_t* k2g = a.k2 + ((size_t)b * T * a.H + h) * D;
+  const uint16_t* vg = a.v + ((size_t)b * T * a.H + h) * DV;
+  auto load_k = [&](int kt, uint8_t* l1, uint8_t* l2) {
+    const int r0 = kt * kKeys;
+    load_tile<D, true>(k1g + (size_t)r0 * kstr, kstr, T - r0, l1, wave, lane);
+    load_tile<D, true>(k2g + (size_t)r0 * kstr, kstr, T - r0, l2, wave, lane);
+  };
+  auto load_v = [&](int kt, uint8_t* lv) {
+    const int r0 = kt * kKeys;
+    load_tile<DV, false>(vg + (size_t)r0 * vstr, vstr, T - r0, lv, wave, lane);
+  };
+
+  f32x4 dq1[NDB], dq2[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dq1[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dq2[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int tr_key = 4 * g + (c16 >> 2);
+  const int tr_byte = 8 * (c16 & 3);
+
+  auto pack8 = [](const float (&x)[8]) {
+    return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                 pack_bf16x2(x[6], x[7])};
+  };
+  // one 32-key step over the staged tiles
+  auto step = [&](auto masked, const uint8_t* l1, const uint8_t* l2, const uint8_t* lv, int cc,
+                  int k0) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    f32x4 s1[2], s2[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s1[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s2[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int key = cc * 32 + kb * 16 + c16;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int off = trans_offset<D>(key, (c * 4 + g) * 16);
+        s1[kb] = mfma_bf16(*reinterpret_cast<const u32x4*>(l1 + off), q1f[c], s1[kb]);
+        s2[kb] = mfma_bf16(*reinterpret_cast<const u32x4*>(l2 + off), q2f[c], s2[kb]);
+      }
+#pragma unroll
+      for (int c = 0; c < NCV; ++c)
+        dp[kb] = mfma_bf16(*reinterpret_cast<const u32x4*>(lv + rows_offset<DV>(key, c * 4 + g)),
+                           dzf[c], dp[kb]);
+    }
+    float x1[8], x2[8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = k0 + kb * 16 + 4 * g + i;
+        float p1 = fast_exp2(fmaf(s1[kb][i], cs, -l21));
+        float p2 = fast_exp2(fmaf(s2[kb][i], cs, -l22));
+        if (MASKED && (key >= T || (CAUSAL && key > row))) {
+          p1 = 0.f;
+          p2 = 0.f;
+        }
+        x1[kb * 4 + i] = p1 * (dp[kb][i] - dd1);
+        x2[kb * 4 + i] = p2 * fmaf(-a.lambda, dp[kb][i], -dd2);
+      }
+    const u32x4 ds1 = pack8(x1), ds2 = pack8(x2);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int off = trans_offset<D>(cc * 32 + tr_key, db * 32 + tr_byte);
+      const u32x2 a1 = lds_read_tr16(l1 + off), b1 = lds_read_tr16(l1 + off + 16 * TK::kRowBytes);
+      const u32x2 a2 = lds_read_tr16(l2 + off), b2 = lds_read_tr16(l2 + off + 16 * TK::kRowBytes);
+      dq1[db] = mfma_bf16(u32x4{a1[0], a1[1], b1[0], b1[1]}, ds1, dq1[db]);
+      dq2[db] = mfma_bf16(u32x4{a2[0], a2[1], b2[0], b2[1]}, ds2, dq2[db]);
+    }
+  };
+
+  // key tiles [0, n_int) are fully valid and visible to every row: unmasked,
+  // unrolled by two over fixed LDS objects; the rest take the masked step
+  const int n_int = max(0, CAUSAL ? min((qt * QTILE + 1) / kKeys, T / kKeys - 1) : T / kKeys - 1);
+  auto interior = [&](int kt, const uint8_t* l1, const uint8_t* l2, const uint8_t* lv, uint8_t* n1,
+                      uint8_t* n2, uint8_t* nv) __attribute__((always_inline)) {
+    load_k(kt + 1, n1, n2);
+    if (wave_active) step(BoolTag<false>{}, l1, l2, lv, 0, kt * kKeys);
+    load_v(kt + 1, nv);
+    if (wave_active) step(BoolTag<false>{}, l1, l2, lv, 1, kt * kKeys + 32);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+  };
+  load_k(0, k1b0, k2b0);
+  load_v(0, vb0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 2 <= n_int; kt += 2) {
+    interior(kt, k1b0, k2b0, vb0, k1b1, k2b1, vb1);
+    interior(kt + 1, k1b1, k2b1, vb1, k1b0, k2b0, vb0);
+  }
+  if (kt < n_int) {
+    interior(kt, k1b0, k2b0, vb0, k1b1, k2b1, vb1);
+    ++kt;
+  }
+  for (; kt < n_kt; ++kt) {
+    const bool odd = kt & 1;
+    if (kt + 1 < n_kt) {
+      if (odd) {
+        load_k(kt + 1, k1b0, k2b0);
+        load_v(kt + 1, vb0);
+      } else {
+        load_k(kt + 1, k1b1, k2b1);
+        load_v(kt + 1, vb1);
+      }
+    }
+    if (wave_active) {
+      const int t0 = kt * kKeys;
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        if (t0 + 32 * cc < wave_key_end) {
+          if (odd)
+            step(BoolTag<true>{}, k1b1, k2b1, vb1, cc, t0 + 32 * cc);
+          else
+            step(BoolTag<true>{}, k1b0, k2b0, vb0, cc, t0 + 32 * cc);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+  }
+  if (!wave_active || row >= T) return;
+  const float scale = 1.0f / sqrtf((float)D);
+  const size_t ro = (((size_t)b * T + row) * a.H + h) * D + g * 4;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    f32x4 r1, r2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r1[i] = dq1[db][i] * scale;
+      r2[i] = dq2[db][i] * scale;
+    }
+    *reinterpret_cast<f32x4*>(a.dq1 + ro + db * 16) = r1;
+    *reinterpret_cast<f32x4*>(a.dq2 + ro + db * 16) = r2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK1, dK2 and dV: a workgroup of 4 waves owns 64 keys of one (batch, head).
+// ---------------------------------------------------------------------------
+template <int D, int DV, bool CAUSAL>
+__global__ __launch_bounds__(kKvWaves * kWave, 1) void v1_bwd_dkdv_kernel(V1BwdArgs a, int Tp,
+                                                                         const uint16_t* dz,
+                                                                         const float* stats) {
+  using TK = BTile<D>;
+  using TV = BTile<DV>;
+  constexpr int NC = D / 32;
+  constexpr int NCV = DV / 32;
+  constexpr int NDB = D / 16;
+  constexpr int NDBV = DV / 16;
+  constexpr int kKvKeys = kKvWaves * 16;
+  // per stage: Q1, Q2 (transposing layout, read both ways), dz (same), then the
+  // rows' log2 lse of both maps and D1, D2 (fp32 x 64 each)
+  constexpr int kVec = 4 * kQRows * 4;
+  constexpr int kStage = 2 * TK::kBytes + TV::kBytes + kVec;
+  __shared__ __align__(16) uint8_t st0[kStage];
+  __shared__ __align__(16) uint8_t st1[kStage];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+  const int T = a.T;
+  const int BH = a.B * a.H;
+  const int n_qt = (T + kQRows - 1) / kQRows;
+  const int kt = blockIdx.x / BH;  // key tiles with the most query tiles first
+  const int bh = blockIdx.x - kt * BH;
+  const int b = bh / a.H;
+  const int h = bh - b * a.H;
+  const int key0 = kt * kKvKeys;
+  const int qt0 = CAUSAL ? key0 / kQRows : 0;
+  const int n_items = n_qt - qt0;  // query tiles, last first
+
+  const int key = key0 + wave * 16 + c16;  // this lane's key column
+  const int keyc = min(key, T - 1);
+  const size_t rk = ((size_t)b * T + keyc) * a.H + h;
+  u32x4 k1f[NC], k2f[NC], vf[NCV];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    k1f[c] = ldg128(a.k1 + rk * D + c * 32 + g * 8);
+    k2f[c] = ldg128(a.k2 + rk * D + c * 32 + g * 8);
+  }
+#pragma unroll
+  for (int c = 0; c < NCV; ++c) vf[c] = ldg128(a.v + rk * DV + c * 32 + g * 8);
+  const float cs = kLog2e / sqrtf((float)D);
+  const int wave_key_lo = key0 + wave * 16;
+
+  const size_t qstr = (size_t)a.H * D, zstr = (size_t)a.H * DV;
+  auto load = [&](int item, uint8_t* st) {
+    const int r0 = (n_qt - 1 - item) * kQRows;
+    const size_t rr = ((size_t)b * T + r0) * a.H + h;
+    load_tile<D, true, kKvWaves>(a.q1 + rr * D, qstr, T - r0, st, wave, lane);
+    load_tile<D, true, kKvWaves>(a.q2 + rr * D, qstr, T - r0, st + TK::kBytes, wave, lane);
+    load_tile<DV, true, kKvWaves>(dz + rr * DV, zstr, T - r0, st + 2 * TK::kBytes, wave, lane);
+    if (lane < 16)  // wave k loads row vector k (256 bytes)
+      dma16(stats + ((size_t)bh * 4 + wave) * Tp + r0, (uint32_t)(lane * 16),
+            st + 2 * TK::kBytes + TV::kBytes + wave * 256);
+  };
+
+  f32x4 dk1[NDB], dk2[NDB], dvv[NDBV];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dk1[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dk2[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int db = 0; db < NDBV; ++db) dvv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int tr_row = 4 * g + (c16 >> 2);
+  const int tr_byte = 8 * (c16 & 3);
+
+  auto work = [&](auto masked, int item, const uint8_t* st) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    const int r0 = (n_qt - 1 - item) * kQRows;
+    if (CAUSAL && r0 + kQRows <= wave_key_lo) return;  // every key of the wave is above the rows
+    const uint8_t* q1l = st;
+    const uint8_t* q2l = st + TK::kBytes;
+    const uint8_t* zl = st + 2 * TK::kBytes;
+    const float* vec = reinterpret_cast<const float*>(st + 2 * TK::kBytes + TV::kBytes);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {  // 32-query halves: one k-step of the dV / dK products
+      float pc[2][4], d1[2][4], d2[2][4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int qb = 2 * s + j;
+        f32x4 s1 = f32x4{0.f, 0.f, 0.f, 0.f}, s2 = s1, dp = s1;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int off = trans_offset<D>(qb * 16 + c16, (c * 4 + g) * 16);
+          s1 = mfma_bf16(*reinterpret_cast<const u32x4*>(q1l + off), k1f[c], s1);
+          s2 = mfma_bf16(*reinterpret_cast<const u32x4*>(q2l + off), k2f[c], s2);
+        }
+#pragma unroll
+        for (int c = 0; c < NCV; ++c)
+          dp = mfma_bf16(*reinterpret_cast<const u32x4*>(zl + trans_offset<DV>(qb * 16 + c16, (c * 4 + g) * 16)),
+                         vf[c], dp);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(vec + qb * 16 + 4 * g);
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(vec + kQRows + qb * 16 + 4 * g);
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(vec + 2 * kQRows + qb * 16 + 4 * g);
+        const f32x4 e2 = *reinterpret_cast<const f32x4*>(vec + 3 * kQRows + qb * 16 + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int q = r0 + qb * 16 + 4 * g + i;
+          float p1 = fast_exp2(fmaf(s1[i], cs, -l1[i]));
+          float p2 = fast_exp2(fmaf(s2[i], cs, -l2[i]));
+          if (MASKED && (q >= T || key >= T || (CAUSAL && key > q))) {
+            p1 = 0.f;
+            p2 = 0.f;
+          }
+          pc[j][i] = fmaf(-a.lambda, p2, p1);
+          d1[j][i] = p1 * (dp[i] - e1[i]);
+          d2[j][i] = p2 * fmaf(-a.lambda, dp[i], -e2[i]);
+        }
+      }
+      auto pack = [](const float (&x)[2][4]) {
+        return u32x4{pack_bf16x2(x[0][0], x[0][1]), pack_bf16x2(x[0][2], x[0][3]),
+                     pack_bf16x2(x[1][0], x[1][1]), pack_bf16x2(x[1][2], x[1][3])};
+      };
+      const u32x4 pa = pack(pc), sa1 = pack(d1), sa2 = pack(d2);
+#pragma unroll
+      for (int db = 0; db < NDBV; ++db) {
+        const int off = trans_offset<DV>(s * 32 + tr_row, db * 32 + tr_byte);
+        const u32x2 lo = lds_read_tr16(zl + off), hi = lds_read_tr16(zl + off + 16 * TV::kRowBytes);
+        dvv[db] = mfma_bf16(pa, u32x4{lo[0], lo[1], hi[0], hi[1]}, dvv[db]);
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int off = trans_offset<D>(s * 32 + tr_row, db * 32 + tr_byte);
+        const u32x2 a1 = lds_read_tr16(q1l + off), b1 = lds_read_tr16(q1l + off + 16 * TK::kRowBytes);
+        const u32x2 a2 = lds_read_tr16(q2l + off), b2 = lds_read_tr16(q2l + off + 16 * TK::kRowBytes);
+        dk1[db] = mfma_bf16(sa1, u32x4{a1[0], a1[1], b1[0], b1[1]}, dk1[db]);
+        dk2[db] = mfma_bf16(sa2, u32x4{a2[0], a2[1], b2[0], b2[1]}, dk2[db]);
+      }
+    }
+  };
+  auto item_masked = [&](int item) {
+    const int r0 = (n_qt - 1 - item) * kQRows;
+    return (CAUSAL && r0 < key0 + kKvKeys) || r0 + kQRows > T || key0 + kKvKeys > T;
+  };
+  auto run = [&](int item, const uint8_t* st) __attribute__((always_inline)) {
+    if (!CAUSAL || item_masked(item))
+      work(BoolTag<true>{}, item, st);
+    else
+      work(BoolTag<false>{}, item, st);
+  };
+
+  if (n_items > 0) {
+    load(0, st0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+  }
+  int it = 0;
+  for (; it + 2 <= n_items; it += 2) {  // unrolled by two: each stage a fixed LDS object
+    load(it + 1, st1);
+    run(it, st0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+    if (it + 2 < n_items) load(it + 2, st0);
+    run(it + 1, st1);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+  }
+  if (it < n_items) run(it, st0);
+
+  // C layout: lane column = channel (16 db + c16), rows = keys 4 g + i of the wave's 16
+  const float scale = 1.0f / sqrtf((float)D);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int kk = key0 + wave * 16 + 4 * g + i;
+    if (kk >= T) continue;
+    const size_t r = ((size_t)b * T + kk) * a.H + h;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      a.dk1[r * D + db * 16 + c16] = dk1[db][i] * scale;
+      a.dk2[r * D + db * 16 + c16] = dk2[db][i] * scale;
+    }
+#pragma unroll
+    for (int db = 0; db < NDBV; ++db) a.dvg[r * DV + db * 16 + c16] = dvv[db][i];
+  }
+}
+
+template <int D, int DV>
+struct Layout {
+  size_t dz, stats, part;  // byte offsets in the workspace
+  size_t total;
+  int Tp, nblk;
+};
+
+template <int D, int DV>
+Layout<D, DV> layout(int B, int T, int H) {
+  Layout<D, DV> L;
+  L.Tp = pad64(T);
+  const long long items = (long long)B * H * L.Tp;
+  L.nblk = (int)std::min<long long>(kPreBlocks, (items + 3) / 4);
+  L.dz = 0;
+  L.stats = ((size_t)B * T * H * DV * 2 + 255) / 256 * 256;
+  L.part = L.stats + ((size_t)B * H * 4 * L.Tp * 4 + 255) / 256 * 256;
+  L.total = L.part + (size_t)L.nblk * (DV + 4) * 4;
+  return L;
+}
+
+template <int D, int DV>
+hipError_t launch_typed(const V1BwdArgs& a, hipStream_t stream) {
+  if ((long long)a.B * a.T * a.H == 0) {  // no rows: dlambda and dw are empty sums
+    hipLaunchKernelGGL((v1_bwd_reduce_kernel<DV>), dim3(1), dim3(256), 0, stream, a,
+                       (const float*)nullptr, 0);
+    return hipGetLastError();
+  }
+  const auto L = layout<D, DV>(a.B, a.T, a.H);
+  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+  uint16_t* dz = reinterpret_cast<uint16_t*>(ws + L.dz);
+  float* stats = reinterpret_cast<float*>(ws + L.stats);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  hipLaunchKernelGGL((v1_bwd_pre_kernel<DV>), dim3(L.nblk), dim3(256), 0, stream, a, L.Tp, dz,
+                     stats, part);
+  hipLaunchKernelGGL((v1_bwd_reduce_kernel<DV>), dim3(1), dim3(256), 0, stream, a,
+                     (const float*)part, L.nblk);
+  const long long BH = (long long)a.B * a.H;
+  const long long dq_blocks = (long long)((a.T + kDqWaves * kRows - 1) / (kDqWaves * kRows)) * BH;
+  const long long kv_blocks = (long long)((a.T + kKvWaves * 16 - 1) / (kKvWaves * 16)) * BH;
+  if (dq_blocks > 0x7fffffffLL || kv_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (a.causal) {
+    hipLaunchKernelGGL((v1_bwd_dq_kernel<D, DV, true>), dim3((unsigned)dq_blocks),
+                       dim3(kDqWaves * kWave), 0, stream, a, L.Tp, (const uint16_t*)dz,
+                       (const float*)stats);
+    hipLaunchKernelGGL((v1_bwd_dkdv_kernel<D, DV, true>), dim3((unsigned)kv_blocks),
+                       dim3(kKvWaves * kWave), 0, stream, a, L.Tp, (const uint16_t*)dz,
+                       (const float*)stats);
+  } else {
+    hipLaunchKernelGGL((v1_bwd_dq_kernel<D, DV, false>), dim3((unsigned)dq_blocks),
+                       dim3(kDqWaves * kWave), 0, stream, a, L.Tp, (const uint16_t*)dz,
+                       (const float*)stats);
+    hipLaunchKernelGGL((v1_bwd_dkdv_kernel<D, DV, false>), dim3((unsigned)kv_blocks),
+                       dim3(kKvWaves * kWave), 0, stream, a, L.Tp, (const uint16_t*)dz,
+                       (const float*)stats);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t v1_bwd_workspace_bytes(int B, int T, int H, int d, int dv) {
+  if (d == 128 && dv == 256) return layout<128, 256>(B, T, H).total;
+  if (d == 64 && dv == 128) return layout<64, 128>(B, T, H).total;
+  return 0;
+}
+
+hipError_t launch_v1_backward(const V1BwdArgs& a, hipStream_t stream) {
+  if (a.d == 128 && a.dv == 256) return launch_typed<128, 256>(a, stream);
+  if (a.d == 64 && a.dv == 128) return launch_typed<64, 128>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace diffattn

@@ -419,9 +419,32 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
 
   // ---- epilogue: stream-2 waves publish O2 / l2 through LDS; stream-1 waves combine ----
   float* xch = reinterpret_cast<float*>(smem);  // [128 rows][XSTRIDE]
-  float inv[2];
+  float inv[2], lsum[2];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) inv[nb] = 1.0f / sum_across_rows(l_part[nb]);
+  for (int nb = 0; nb < 2; ++nb) {
+    lsum[nb] = sum_across_rows(l_part[nb]);
+    inv[nb] = 1.0f / lsum[nb];
+  }
+  if (a.o1 != nullptr && wave_active) {
+    // training forward: this stream's normalised O (fp32) and its log-sum-exp
+    // (natural log of the scaled scores; m_ref is in log2 units of s / sqrt(d))
+    float* ost = stream == 0 ? a.o1 : a.o2;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int row = q_lo + nb * 16 + c16;
+      if (row >= T) continue;
+      const size_t r = (tok_base + row) * a.H + h;
+      if (g == 0) a.lse[r * 2 + stream] = (m_ref[nb] + log2f(lsum[nb])) * 0.69314718055994531f;
+      float* dst = ost + r * DV + g * 4;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        f32x4 t;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] = __fmul_rn(o[db][nb][i], inv[nb]);
+        *reinterpret_cast<f32x4*>(dst + db * 16) = t;
+      }
+    }
+  }
   if (stream == 1 && wave_active) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {

@@ -221,6 +221,14 @@ def v1_inputs(w: V1Workload, device=None) -> dict:
     )
 
 
+V1_DY_SEED = 206  # upstream gradient of the V1 backward workload (B4 T4096 H12 d128 dv256)
+
+
+def v1_dy(w: V1Workload, seed: int = V1_DY_SEED, device=None) -> torch.Tensor:
+    """Upstream gradient dL/dy [B,T,H,dv] fp32, iid N(0,1)."""
+    return normal((w.B, w.T, w.H, w.dv), seed, 1.0, dtype=torch.float32, device=device)
+
+
 def v2_inputs(w: V2Workload, device=None) -> dict:
     """Padded: q [B,T,Hq,d] ...; packed (``w.lengths`` set): q [total,Hq,d], plus cu_seqlens."""
     sq, sk, sv, sl = w.seeds

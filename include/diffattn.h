@@ -93,6 +93,67 @@ DIFFATTN_API int diffattn_v1_fwd(const void* q1, const void* k1, const void* q2,
 DIFFATTN_API size_t diffattn_v1_workspace_bytes(int B, int T, int H, int d, int dv, diffattn_dtype in_dtype);
 
 /*
+ * V1 forward for training: diffattn_v1_fwd (bf16 inputs) that also writes
+ * what diffattn_v1_bwd needs from the forward:
+ *
+ *   o1, o2 : [B, T, H, dv] fp32, the normalised per-map outputs
+ *            O_k[i] = sum_j P_k,ij v_j (so z = o1 - lambda * o2)
+ *   lse    : [B, T, H, 2] fp32, natural-log log-sum-exp of each map's scaled
+ *            scores, map 1 first (P_k,ij = exp(q_k,i . k_k,j / sqrt(d) - lse))
+ *
+ * Other arguments, the workspace and the supported shapes are those of
+ * diffattn_v1_fwd with in_dtype DIFFATTN_BF16 (DIFFATTN_F32 is rejected with
+ * DIFFATTN_E_UNSUPPORTED).  o1, o2 and lse are caller-owned and 16-byte aligned.
+ */
+DIFFATTN_API int diffattn_v1_fwd_train(const void* q1, const void* k1, const void* q2,
+                          const void* k2, const void* v, const float* norm_weight, float* out,
+                          float* o1, float* o2, float* lse, int B, int T, int H, int d, int dv,
+                          float lambda, float lambda_init, float eps, int causal,
+                          diffattn_dtype in_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * V1 backward [P1 "Differential Attention: 빼기의 힘"; norm and factor: P2 §1].
+ * The pages give the forward only; this is the chain rule through it.  For
+ * the loss L = sum(dy * y), with s = 1 - lambda_init, r_i = sqrt(mean(z_i^2) +
+ * eps) and g_i = s * w * dy_i:
+ *
+ *   dz_i = g_i / r_i - z_i <g_i, z_i> / (dv r_i^3),
+ *   dnorm_weight = sum_i s dy_i z_i / r_i,   dlambda = -sum_i <dz_i, O2_i>,
+ *   map 1 with dO1 = dz and map 2 with dO2 = -lambda dz, each:
+ *     P = softmax rows (recomputed from lse), dP = dO V^T,
+ *     dS = P o (dP - rowsum(dO o O)),
+ *     dq_k = dS K_k / sqrt(d),  dk_k = dS^T Q_k / sqrt(d),
+ *   dv = (P1 - lambda P2)^T dz.
+ * Sums over i run over every batch, row and head.
+ *
+ *   q1, k1, q2, k2, v, norm_weight : as diffattn_v1_fwd (bf16)
+ *   o1, o2, lse        : from diffattn_v1_fwd_train on the same inputs
+ *   dy                 : [B, T, H, dv] fp32, dL/dy
+ *   dq1, dk1, dq2, dk2 : [B, T, H, d] fp32 (written)
+ *   dv_out             : [B, T, H, dv] fp32 (written)
+ *   dlambda            : [1] fp32 (written)
+ *   dnorm_weight       : [dv] fp32 (written; the gradient of the norm weight,
+ *                        also when norm_weight is NULL, i.e. all ones)
+ *   workspace          : device scratch of at least diffattn_v1_bwd_workspace_bytes()
+ *                        bytes (may be NULL when that is 0); caller-owned.
+ * All reductions run in a fixed order: results are deterministic.  With no
+ * rows (B, T or H zero) only dlambda and dnorm_weight are written, as zeros;
+ * the other tensor pointers are then not read and may be NULL.
+ * Supported: in_dtype DIFFATTN_BF16 with (d, dv) = (128, 256) or (64, 128).
+ */
+DIFFATTN_API int diffattn_v1_bwd(const void* q1, const void* k1, const void* q2, const void* k2,
+                    const void* v, const float* norm_weight, const float* o1, const float* o2,
+                    const float* lse, const float* dy, float* dq1, float* dk1, float* dq2,
+                    float* dk2, float* dv_out, float* dlambda, float* dnorm_weight, int B,
+                    int T, int H, int d, int dv, float lambda, float lambda_init, float eps,
+                    int causal, diffattn_dtype in_dtype, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Workspace bytes diffattn_v1_bwd needs (0 for sizes it would reject or with no rows). */
+DIFFATTN_API size_t diffattn_v1_bwd_workspace_bytes(int B, int T, int H, int d, int dv);
+
+/*
  * V2 differential attention forward (prefill) [P2 §1, §4].  Hq = 2h query heads
  * attend over Hkv shared key/value heads; query head j reads KV head
  * j / (Hq / Hkv).  For every sequence, query row i and pair p:

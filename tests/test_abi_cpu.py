@@ -204,3 +204,65 @@ def test_v2_backward_workspace_query(lib):
     assert lib.diffattn_v2_bwd_workspace_bytes(1, 65, 16, 2, 128) == 4 * 128 * (16 * 2 + 8)
     assert lib.diffattn_v2_bwd_workspace_bytes(1, 64, 6, 2, 128) == 0
     assert lib.diffattn_v2_bwd_workspace_bytes(1, 64, 16, 2, 96) == 0
+
+
+def v1t(lib, **kw):
+    a = dict(q1=P, k1=P, q2=P, k2=P, v=P, w=None, out=P, o1=P, o2=P, lse=P, B=1, T=16, H=1, d=128,
+             dv=256, lam=0.2, li=0.2, eps=1e-12, causal=1, dt=BF16, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.diffattn_v1_fwd_train(a["q1"], a["k1"], a["q2"], a["k2"], a["v"], a["w"], a["out"],
+                                     a["o1"], a["o2"], a["lse"], a["B"], a["T"], a["H"], a["d"],
+                                     a["dv"], a["lam"], a["li"], a["eps"], a["causal"], a["dt"],
+                                     a["ws"], a["wsb"], a["stream"])
+
+
+def test_v1_train_forward_rejects_bad_arguments(lib):
+    assert v1t(lib, o1=None) == E_INVALID
+    assert v1t(lib, lse=None) == E_INVALID
+    assert v1t(lib, dt=F32) == E_UNSUPPORTED
+    assert v1t(lib, d=96, dv=192) == E_UNSUPPORTED
+    assert v1t(lib, o2=P + 8) == E_ALIGN
+    assert v1t(lib, ws=None) == E_WORKSPACE
+    assert v1t(lib, T=0, ws=None, wsb=0) == 0
+
+
+def v1b(lib, **kw):
+    a = dict(q1=P, k1=P, q2=P, k2=P, v=P, w=None, o1=P, o2=P, lse=P, dy=P, dq1=P, dk1=P, dq2=P,
+             dk2=P, dv=P, dlam=P, dw=P, B=1, T=16, H=1, d=128, dvd=256, lam=0.2, li=0.2,
+             eps=1e-12, causal=1, dt=BF16, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.diffattn_v1_bwd(a["q1"], a["k1"], a["q2"], a["k2"], a["v"], a["w"], a["o1"],
+                               a["o2"], a["lse"], a["dy"], a["dq1"], a["dk1"], a["dq2"], a["dk2"],
+                               a["dv"], a["dlam"], a["dw"], a["B"], a["T"], a["H"], a["d"],
+                               a["dvd"], a["lam"], a["li"], a["eps"], a["causal"], a["dt"],
+                               a["ws"], a["wsb"], a["stream"])
+
+
+def test_v1_backward_rejects_bad_arguments(lib):
+    assert v1b(lib, dy=None) == E_INVALID
+    assert v1b(lib, dk2=None) == E_INVALID
+    assert v1b(lib, lse=None) == E_INVALID
+    assert v1b(lib, dlam=None, T=0) == E_INVALID  # dlambda is written even with no rows
+    assert v1b(lib, dw=None) == E_INVALID
+    assert v1b(lib, causal=2) == E_INVALID
+    assert v1b(lib, lam=float("inf")) == E_INVALID
+    assert v1b(lib, eps=-1.0) == E_INVALID
+    assert v1b(lib, dt=F32) == E_UNSUPPORTED
+    assert v1b(lib, d=96, dvd=192) == E_UNSUPPORTED
+    assert v1b(lib, dq1=P + 4) == E_ALIGN
+    assert v1b(lib, dlam=P + 1) == E_ALIGN
+    assert v1b(lib, w=P + 2) == E_ALIGN
+    assert v1b(lib, ws=None) == E_WORKSPACE
+    assert v1b(lib, wsb=64) == E_WORKSPACE
+    assert b"workspace" in lib.diffattn_last_error()
+
+
+def test_v1_backward_workspace_query(lib):
+    # bf16 dz [B,T,H,dv], fp32 stats [B][H][4][T rounded up to 64], then the
+    # preprocessing grid's partial sums (at most 1024 blocks of dv + 4 floats)
+    assert lib.diffattn_v1_bwd_workspace_bytes(4, 4096, 12, 128, 256) == (
+        4 * 4096 * 12 * 256 * 2 + 4 * 12 * 4 * 4096 * 4 + 1024 * 260 * 4)
+    assert lib.diffattn_v1_bwd_workspace_bytes(1, 1, 1, 64, 128) == (
+        256 + 4 * 64 * 4 + 16 * 132 * 4)  # one wave per row of the 64 padded rows
+    assert lib.diffattn_v1_bwd_workspace_bytes(1, 64, 1, 96, 192) == 0
+    assert lib.diffattn_v1_bwd_workspace_bytes(0, 64, 1, 128, 256) == 0

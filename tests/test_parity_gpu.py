@@ -464,6 +464,215 @@ def test_v2_backward_full_workload_sampled(gpu):
 
 
 # ---------------------------------------------------------------------------
+# V1 training forward and backward (same gradient bounds as V2; dz and the
+# per-map P and dS enter the products rounded to bf16)
+# ---------------------------------------------------------------------------
+
+def run_v1_train(x, dy, lam, li, eps, weight=None, causal=True):
+    out, o1, o2, lse = da.v1_fwd_train(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, li, eps,
+                                       weight=weight, causal=causal)
+    grads = da.v1_bwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], o1, o2, lse, dy, lam, li, eps,
+                      weight=weight, causal=causal)
+    torch.cuda.synchronize()
+    return out, o1, o2, lse, grads
+
+
+V1_GRAD_NAMES = ("dq1", "dk1", "dq2", "dk2", "dv", "dlambda", "dweight")
+
+
+def v1_oracle_state(x, causal=True):
+    """The forward state the backward reads (per-map O and lse), from the oracle, fp32."""
+    O1, L1 = oracle.v2_forward_stats(x["q1"], x["k1"], x["v"], causal=causal)
+    O2, L2 = oracle.v2_forward_stats(x["q2"], x["k2"], x["v"], causal=causal)
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).float()
+    return f(O1), f(O2), f(np.stack([L1, L2], axis=-1)), O1, O2
+
+
+def dlambda_terms(O1, O2, dy, lam, li, eps, weight=None):
+    """Terms -dz_ic O2_ic of dlambda (fp64, from the oracle's O), [..., dv]: the
+    scale its rounding error is measured against, since the terms nearly cancel
+    (<dz_i, z_i> = 0 by the norm's scale invariance, and O1 ~ O2 when the two
+    maps are close; one token makes the sum vanish in closed form)."""
+    dy = np.asarray(dy, dtype=np.float64)
+    w = 1.0 if weight is None else np.asarray(weight, dtype=np.float64)
+    z = O1 - lam * O2
+    r = np.sqrt(np.mean(z * z, axis=-1, keepdims=True) + eps)
+    g = (1.0 - li) * w * dy
+    dz = g / r - z * np.sum(g * z, axis=-1, keepdims=True) / (z.shape[-1] * r ** 3)
+    return -dz * O2
+
+
+def check_dlambda(got, ref, terms, what, end_to_end=False):
+    """dlambda, a cancelling sum, against its terms: on the oracle's forward
+    state |err| <= 2e-2 |ref| + 1e-5 sum|terms| (fp32 rounding, ~2^-24 per
+    term, with margin); end to end the kernel forward's O (fp16 P, bf16-rounded
+    scaled q) enters every row term, and 2e-2 |ref| may rise to 2e-2 times the
+    sum over rows of |row term|."""
+    got, ref = float(np.asarray(got).reshape(())), float(ref)
+    err = abs(got - ref)
+    scale = float(np.sum(np.abs(terms)))
+    bound = 2e-2 * abs(ref) + 1e-5 * scale
+    if end_to_end:
+        bound = max(bound, 2e-2 * float(np.sum(np.abs(np.sum(terms, axis=-1)))) + 1e-5 * scale)
+    note(f"{what} dlambda: got={got:.6g} ref={ref:.6g} err={err:.3e} scale={scale:.3e} "
+         f"bound={bound:.3e} ({err / bound:.3f}x)")
+    assert err <= bound, f"{what} dlambda: |err| {err:.3e} > {bound:.3e}"
+
+
+def check_v1_grads(grads, refs, what, dlam_terms, end_to_end=False):
+    for name, g, r in zip(V1_GRAD_NAMES, grads, refs):
+        got = g.cpu().numpy().reshape(np.shape(r))
+        if name == "dlambda":
+            check_dlambda(got, r, dlam_terms, what, end_to_end)
+        else:
+            compare_grad(got, r, f"{what} {name}")
+
+
+@pytest.mark.parametrize("B,T,H,d,dv,causal,layer,weighted,std", [
+    (1, 64, 2, 64, 128, True, 1, False, None), (2, 37, 2, 64, 128, True, 3, True, None),
+    (1, 200, 2, 128, 256, True, 12, False, None), (1, 130, 2, 128, 256, False, 5, True, 1.0),
+    (2, 97, 1, 64, 128, False, 28, False, None), (1, 1, 2, 128, 256, True, 2, False, None),
+    (1, 257, 1, 128, 256, True, 7, True, 1.0), (2, 129, 2, 64, 128, True, 20, False, 0.5)])
+def test_v1_backward_small_all_elements(gpu, B, T, H, d, dv, causal, layer, weighted, std):
+    w = inp.V1_BF16.with_shape(B=B, T=T, H=H, d=d, dv=dv, std=std or 1.0 / math.sqrt(d))
+    x = inp.v1_inputs(w)
+    dy = inp.v1_dy(w)
+    lam = li = oracle.lambda_init(layer)
+    weight = (1.0 + 0.25 * torch.randn(dv, generator=torch.Generator().manual_seed(7))
+              if weighted else None)
+    wg = None if weight is None else weight.to(gpu)
+    xg = cuda(x, gpu)
+    refs = oracle.v1_backward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, li, w.eps, dy,
+                              weight=weight, causal=causal)
+    what = f"v1 bwd B={B} T={T} H={H} d={d} causal={causal} layer={layer} std={w.std:.3g}"
+    # (1) the backward on the oracle's forward state: every gradient, dlambda included
+    o1, o2, lse, O1, O2 = v1_oracle_state(x, causal)
+    grads = da.v1_bwd(xg["q1"], xg["k1"], xg["q2"], xg["k2"], xg["v"], o1.to(gpu), o2.to(gpu),
+                      lse.to(gpu), dy.to(gpu), lam, li, w.eps, weight=wg, causal=causal)
+    torch.cuda.synchronize()
+    terms = dlambda_terms(O1, O2, dy.numpy(), lam, li, w.eps, weight)
+    check_v1_grads(grads, refs, what + " [oracle state]", terms)
+    # (2) end to end: the kernel's training forward feeding the backward
+    *_, grads = run_v1_train(xg, dy.to(gpu), lam, li, w.eps, wg, causal)
+    check_v1_grads(grads, refs, what, terms, end_to_end=True)
+
+
+def test_v1_backward_grid_stride_rows(gpu):
+    # more rows than the preprocessing grid has waves, so its loop and the
+    # fixed-order partial sums of dlambda and dweight run as at full size
+    w = inp.V1_BF16.with_shape(B=2, T=1024, H=4)
+    x = inp.v1_inputs(w)
+    dy = inp.v1_dy(w)
+    lam = li = oracle.lambda_init(9)
+    xg = cuda(x, gpu)
+    refs = oracle.v1_backward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, li, w.eps, dy)
+    o1, o2, lse, O1, O2 = v1_oracle_state(x)
+    grads = da.v1_bwd(xg["q1"], xg["k1"], xg["q2"], xg["k2"], xg["v"], o1.to(gpu), o2.to(gpu),
+                      lse.to(gpu), dy.to(gpu), lam, li, w.eps)
+    torch.cuda.synchronize()
+    terms = dlambda_terms(O1, O2, dy.numpy(), lam, li, w.eps)
+    check_v1_grads(grads, refs, "v1 bwd B2 T1024 H4 [oracle state]", terms)
+    *_, grads = run_v1_train(xg, dy.to(gpu), lam, li, w.eps)
+    check_v1_grads(grads, refs, "v1 bwd B2 T1024 H4", terms, end_to_end=True)
+
+
+def test_v1_train_forward_outputs(gpu):
+    # out matches the inference forward exactly; per-map O and lse match the oracle
+    w = inp.V1_BF16.with_shape(B=2, T=150, H=2)
+    x = inp.v1_inputs(w)
+    xg = cuda(x, gpu)
+    lam = li = oracle.lambda_init(4)
+    out, o1, o2, lse = da.v1_fwd_train(xg["q1"], xg["k1"], xg["q2"], xg["k2"], xg["v"], lam, li,
+                                       w.eps)
+    assert torch.equal(out, run_v1(xg, lam, li, w.eps))
+    rv = rms(x["v"])
+    for k, (o, l) in enumerate(((o1, lse[..., 0]), (o2, lse[..., 1])), start=1):
+        O, L = oracle.v2_forward_stats(x[f"q{k}"], x[f"k{k}"], x["v"])
+        compare(o.cpu().numpy(), O, rv, TOL_BF16, REL_L2_BF16, what=f"v1 train o{k}")
+        err = float(np.max(np.abs(l.cpu().numpy() - L)))
+        note(f"v1 train lse map {k}: max|err|={err:.3e}")
+        assert err <= 1e-2
+
+
+def test_v1_backward_zero_upstream_empty_and_determinism(gpu):
+    w = inp.V1_BF16.with_shape(B=1, T=190, H=2)
+    xg = cuda(inp.v1_inputs(w), gpu)
+    lam = li = oracle.lambda_init(6)
+    zero = torch.zeros((1, 190, 2, 256), dtype=torch.float32, device=gpu)
+    *_, grads = run_v1_train(xg, zero, lam, li, w.eps)
+    for g in grads:
+        assert torch.count_nonzero(g).item() == 0
+    dy = inp.v1_dy(w).to(gpu)
+    *_, g1 = run_v1_train(xg, dy, lam, li, w.eps)
+    *_, g2 = run_v1_train(xg, dy, lam, li, w.eps)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)  # fixed-order reductions: bitwise repeatable
+    # no rows: the parameter gradients are empty sums (written as zeros)
+    e = {k: v[:, :0] for k, v in xg.items()}
+    o = zero[:, :0]
+    ge = da.v1_bwd(e["q1"], e["k1"], e["q2"], e["k2"], e["v"], o, o, o[..., :2], o, lam, li,
+                   w.eps)
+    torch.cuda.synchronize()
+    assert ge[0].numel() == 0
+    assert torch.count_nonzero(ge[5]).item() == 0 and torch.count_nonzero(ge[6]).item() == 0
+
+
+def test_v1_backward_full_workload_sampled(gpu):
+    # B4 T4096 H12 d128 dv256, launched as the benchmark does.  (1) The random
+    # upstream gradient: the tensor gradients of two sampled heads against the
+    # oracle on those heads, and the key gradients' zero sum over all heads.
+    # (2) The same gradient kept on the two sampled heads only: elsewhere dz is
+    # exactly zero, so dlambda and dweight are the sampled heads' oracle sums
+    # and every other head's gradients vanish.
+    w = inp.V1_BF16
+    x = inp.v1_inputs(w)
+    dy = inp.v1_dy(w)
+    lam = li = oracle.lambda_init(14)
+    xg = cuda(x, gpu)
+    note("v1 bwd full workload: launching")
+    *fwd, grads = run_v1_train(xg, dy.to(gpu), lam, li, w.eps)
+    heads = [(0, 0), (3, 7)]
+    refs = {}
+    for b, h in heads:
+        sl = {k: x[k][b:b + 1, :, h:h + 1] for k in x}
+        note(f"v1 bwd full workload: oracle head b={b} h={h}")
+        refs[(b, h)] = oracle.v1_backward(sl["q1"], sl["k1"], sl["q2"], sl["k2"], sl["v"], lam,
+                                          li, w.eps, dy[b:b + 1, :, h:h + 1])
+        for i, name in enumerate(V1_GRAD_NAMES[:5]):
+            compare_grad(grads[i][b:b + 1, :, h:h + 1].cpu().numpy(), refs[(b, h)][i],
+                         f"v1 bwd full {name} b={b} h={h}")
+    for i in (1, 3):
+        ksum = grads[i].double().sum(dim=1)
+        rel = float((ksum.abs() / grads[i].double().abs().sum(dim=1)).max())
+        note(f"v1 bwd full {V1_GRAD_NAMES[i]} zero-sum: max |sum| / sum|.| = {rel:.3e}")
+        assert rel <= 1e-2
+    # (2): dz vanishes outside the sampled heads; there the backward reads the
+    # oracle's forward state, so dlambda and dweight are checked as strictly as
+    # in the small cases
+    mask = torch.zeros_like(dy)
+    o1, o2, lse = (t.clone() for t in fwd[1:4])
+    terms = []
+    for b, h in heads:
+        mask[b, :, h] = 1.0
+        sl = {k: x[k][b:b + 1, :, h:h + 1] for k in x}
+        so1, so2, slse, O1, O2 = v1_oracle_state(sl)
+        o1[b, :, h] = so1[0, :, 0].to(gpu)
+        o2[b, :, h] = so2[0, :, 0].to(gpu)
+        lse[b, :, h] = slse[0, :, 0].to(gpu)
+        terms.append(dlambda_terms(O1, O2, dy[b:b + 1, :, h:h + 1].numpy(), lam, li, w.eps))
+    gm = da.v1_bwd(xg["q1"], xg["k1"], xg["q2"], xg["k2"], xg["v"], o1, o2, lse,
+                   (dy * mask).to(gpu), lam, li, w.eps)
+    torch.cuda.synchronize()
+    check_dlambda(gm[5].cpu().numpy(), sum(refs[k][5] for k in refs), np.concatenate(terms),
+                  "v1 bwd full (sampled heads)")
+    compare_grad(gm[6].cpu().numpy(), sum(refs[k][6] for k in refs),
+                 "v1 bwd full dweight (sampled heads)")
+    keep = mask[..., :1].to(gpu).bool()
+    for i in range(5):
+        assert torch.count_nonzero(gm[i].masked_fill(keep, 0.0)).item() == 0
+
+
+# ---------------------------------------------------------------------------
 # V1 decode
 # ---------------------------------------------------------------------------
 
