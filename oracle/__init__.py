@@ -15,6 +15,7 @@ from .diffattn_oracle import (  # noqa: F401
     v1_head,
     v1_head_backward,
     v1_norm,
+    v1_norm_backward,
     v2_backward,
     v2_backward_query_rows,
     v2_combine,

@@ -154,6 +154,25 @@ def v1_norm(z, lam_init: float, eps: float, weight=None) -> np.ndarray:
     return (1.0 - lam_init) * y
 
 
+def v1_norm_backward(z, dy, lam_init: float, eps: float, weight=None):
+    """Backward of ``v1_norm``: gradients of sum(dy * y) with respect to z and the weight.
+
+    The chain rule through y = s w z / r (V2 summary §1, the V1 recap), with
+    s = 1 - lam_init, r = sqrt(mean(z^2) + eps) over the dv channels and g = s w dy:
+        dz = g / r - z <g, z> / (dv r^3),   dw = sum over rows of s dy z / r.
+    z, dy: [..., dv].  Returns (dz [..., dv], dw [dv]).
+    """
+    z, dy = _f64(z), _f64(dy)
+    dvw = z.shape[-1]
+    w = np.ones(dvw) if weight is None else _f64(weight)
+    r = np.sqrt(np.mean(z * z, axis=-1, keepdims=True) + eps)
+    s = 1.0 - lam_init
+    g = s * w * dy
+    dz = g / r - z * np.sum(g * z, axis=-1, keepdims=True) / (dvw * r ** 3)
+    dw = np.sum((s * dy * z / r).reshape(-1, dvw), axis=0)
+    return dz, dw
+
+
 def v1_attention(q1, k1, q2, k2, v, lam: float, causal: bool = True, rows=None) -> np.ndarray:
     """z for every (batch, head): inputs [B, T, H, d] / [B, T, H, dv] -> [B, R, H, dv]."""
     q1, k1, q2, k2, v = (_f64(a) for a in (q1, k1, q2, k2, v))
@@ -190,19 +209,13 @@ def v1_head_backward(q1, k1, q2, k2, v, lam: float, lam_init: float, eps: float,
     """
     q1, k1, q2, k2, v, dy = (_f64(a) for a in (q1, k1, q2, k2, v, dy))
     T, d = q1.shape
-    dvw = v.shape[1]
-    w = np.ones(dvw) if weight is None else _f64(weight)
     rows = np.arange(T)
     scale = 1.0 / math.sqrt(d)
     p1 = _attention_map(q1, k1, rows, scale, causal)
     p2 = _attention_map(q2, k2, rows, scale, causal)
     o1, o2 = p1 @ v, p2 @ v
     z = o1 - lam * o2
-    r = np.sqrt(np.mean(z * z, axis=-1, keepdims=True) + eps)
-    s = 1.0 - lam_init
-    g = s * w * dy
-    dz = g / r - z * np.sum(g * z, axis=-1, keepdims=True) / (dvw * r ** 3)
-    dw = np.sum(s * dy * z / r, axis=0)
+    dz, dw = v1_norm_backward(z, dy, lam_init, eps, weight)
     dlam = -float(np.sum(dz * o2))
     grads = []
     dv = np.zeros_like(v)

@@ -127,6 +127,43 @@ def test_v1_uniform_attention_gain_matches_page_figure():
     assert 1.0 / math.sqrt(n) < math.sqrt(np.mean(ms)) * 1.05  # lower end of [1/sqrt(n), 1)
 
 
+def test_v1_norm_backward_amplifies_by_page_figure():
+    # V2 summary §3: at length 8192 with uniform attention the per-head norm
+    # scales its input up ~90.5x, and the gradient through it grows by the same
+    # factor: dz = (g - zhat <g, zhat> / dv) / r with zhat = z / r of mean
+    # square ~1, so for random g, |dz|^2 ~ |g|^2 (1 - 1/dv) / r^2.
+    fig = GOLDEN["uniform_attention_norm_gain_n8192"]
+    n, dv, heads = fig["n"], 64, 256
+    r = rng(15)
+    zq = np.zeros((n, 4))
+    num = den = 0.0
+    for _ in range(heads):
+        v = r.standard_normal((n, dv))
+        z = oracle.v1_head(zq, zq, zq, zq, v, lam=0.0, rows=[n - 1])
+        dy = r.standard_normal(z.shape)
+        dz, _ = oracle.v1_norm_backward(z, dy, lam_init=0.0, eps=1e-12)
+        num += float(np.sum(dz ** 2))
+        den += float(np.sum(dy ** 2)) * (1.0 - 1.0 / dv)
+    gain = math.sqrt(num / den)
+    assert abs(gain - fig["value"]) / fig["value"] < fig["tolerance_rel"]
+
+
+def test_v1_norm_backward_is_orthogonal_to_z_and_scale_invariant():
+    # the norm output does not change when z is scaled (eps -> 0), so dz has no
+    # component along z and scaling z by c scales dz by 1/c; dw sums s dy z / r
+    r = rng(16)
+    z = r.standard_normal((5, 7, 32))
+    dy = r.standard_normal(z.shape)
+    w = 1.0 + 0.1 * r.standard_normal(32)
+    dz, dw = oracle.v1_norm_backward(z, dy, 0.3, 0.0, w)
+    np.testing.assert_allclose(np.sum(dz * z, axis=-1), 0.0, atol=1e-12)
+    dz3, dw3 = oracle.v1_norm_backward(3.0 * z, dy, 0.3, 0.0, w)
+    np.testing.assert_allclose(dz3, dz / 3.0, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dw3, dw, rtol=1e-12, atol=1e-13)
+    y = oracle.v1_norm(z, 0.3, 0.0, w)
+    np.testing.assert_allclose(dw, np.sum((dy * y / w).reshape(-1, 32), axis=0), rtol=1e-12)
+
+
 def test_v1_one_hot_maps_select_values():
     # make stream 1 of row i look only at key a, stream 2 only at key b
     T, d, dv, i, a, b = 12, 8, 16, 9, 2, 6
