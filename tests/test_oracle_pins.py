@@ -131,7 +131,9 @@ def test_v1_norm_backward_amplifies_by_page_figure():
     # V2 summary §3: at length 8192 with uniform attention the per-head norm
     # scales its input up ~90.5x, and the gradient through it grows by the same
     # factor: dz = (g - zhat <g, zhat> / dv) / r with zhat = z / r of mean
-    # square ~1, so for random g, |dz|^2 ~ |g|^2 (1 - 1/dv) / r^2.
+    # square ~1, so for random g, |dz|^2 ~ |g|^2 (1 - 1/dv) / r^2.  Averaging
+    # 1/r^2 rather than r^2 adds the chi-square factor E[dv / chi2_dv] =
+    # dv / (dv - 2) to the page's 1/RMS figure.
     fig = GOLDEN["uniform_attention_norm_gain_n8192"]
     n, dv, heads = fig["n"], 64, 256
     r = rng(15)
@@ -145,7 +147,8 @@ def test_v1_norm_backward_amplifies_by_page_figure():
         num += float(np.sum(dz ** 2))
         den += float(np.sum(dy ** 2)) * (1.0 - 1.0 / dv)
     gain = math.sqrt(num / den)
-    assert abs(gain - fig["value"]) / fig["value"] < fig["tolerance_rel"]
+    expect = fig["value"] * math.sqrt(dv / (dv - 2.0))
+    assert abs(gain - expect) / expect < fig["tolerance_rel"]
 
 
 def test_v1_norm_backward_is_orthogonal_to_z_and_scale_invariant():
