@@ -11,13 +11,14 @@ The other hot-path kernels are timed in the same run (``secondary``):
 V2 GQA causal prefill (B2, Hq64/Hkv8, T8192, d128), V2 packed varlen prefill
 (65536 tokens), the V2 decode step (B64, 32768-entry cache, Hq64/Hkv8,
 d128, metric HBM GB/s), the V1 decode step (B32, 32768-entry cache, H12,
-d128/dv256, GB/s) and the V2 backward on the prefill workload (2.5x the
-forward's FLOP).  Inputs are synthetic, seeded, already resident in HBM when
+d128/dv256, GB/s), the V2 backward on the prefill workload (2x the
+forward's FLOP: dP and dV are formed once per head pair) and the V1 backward
+on the headline workload.  Inputs are synthetic, seeded, already resident in HBM when
 timing starts.  The fp64 CPU oracle is timed on a bounded sample of the
 headline workload on this host (``cpu_baseline``).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
-       [--no-cpu-baseline] [--only v1|v2|varlen|decode|v1dec|bwd]
+       [--no-cpu-baseline] [--only v1|v2|varlen|decode|v1dec|bwd|v1bwd]
 """
 from __future__ import annotations
 
@@ -39,8 +40,9 @@ SOURCES = {
     "v2": ("v2_prefill.hip", "device_common.h", "kernels.h"),
     "varlen": ("v2_prefill.hip", "device_common.h", "kernels.h"),
     "decode": ("v2_decode.hip", "device_common.h", "kernels.h"),
-    "bwd": ("v2_backward.hip", "device_common.h", "kernels.h"),
+    "bwd": ("v2_backward.hip", "bwd_common.h", "device_common.h", "kernels.h"),
     "v1dec": ("v1_decode.hip", "device_common.h", "kernels.h"),
+    "v1bwd": ("v1_backward.hip", "bwd_common.h", "device_common.h", "kernels.h"),
 }
 
 
@@ -89,6 +91,19 @@ def v2_flops_seq(n, Hq, d):
     return 2.0 * d * n * (n + 1) * Hq
 
 
+def v2_bwd_flops_seq(n, Hq, d):
+    # per (query, key) pair and pair of heads: S_e, S_o, dP (shared: the odd
+    # head's is -sigma times it), dV (one product of P_e - sigma P_o), dQ_e,
+    # dQ_o, dK_e, dK_o: 8 products of 2d = 2x the forward's 2 per head
+    return 2.0 * v2_flops_seq(n, Hq, d)
+
+
+def v1_bwd_flops(B, T, H, d, dv):
+    # per (query, key) pair and head: S1, S2, dQ1, dQ2, dK1, dK2 (2d each) and
+    # dP = dz V^T, dV = (P1 - lambda P2)^T dz (2dv each), causal lower triangle
+    return (12.0 * d + 4.0 * dv) * T * (T + 1) / 2 * B * H
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -114,7 +129,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["v1", "v2", "varlen", "decode", "v1dec", "bwd"],
+    ap.add_argument("--only", choices=["v1", "v2", "varlen", "decode", "v1dec", "bwd", "v1bwd"],
                     default=None)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -287,13 +302,38 @@ def main():
             for _ in range(args.warmup):
                 f()
             ms = time_calls(f, iters, stream)
-            # five products per (query, key) pair and head against the forward's two
-            flop = 2.5 * w.B * v2_flops_seq(w.T, w.Hq, w.d)
+            flop = w.B * v2_bwd_flops_seq(w.T, w.Hq, w.d)
             tf = flop / (ms * 1e-3) / 1e12
             secondary["v2_backward"] = {"workload": name, "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
                                         "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flop": flop,
                                         "traffic": hbm_traffic("bwd", name)}
             del x, dout, oh, lse, wsb
+            torch.cuda.empty_cache()
+        if args.only in (None, "v1bwd"):
+            # V1 backward on the headline workload (one layer's lambda): the
+            # preprocessing, reduction, dQ and dK/dV kernels of one
+            # diffattn_v1_bwd call; the training forward runs once, untimed
+            w = inp.V1_BF16
+            name = w.name.replace("v1_bf16", "v1_backward_bf16")
+            log(f"[bench] {name}")
+            x = inp.v1_inputs(w, device=dev)
+            dy = inp.v1_dy(w, device=dev)
+            li = da.lambda_init(14)
+            _, o1, o2, lse = da.v1_fwd_train(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], li, li,
+                                             w.eps)
+            wsb = torch.empty(da.v1_bwd_workspace_bytes(w.B, w.T, w.H, w.d, w.dv),
+                              dtype=torch.uint8, device=dev)
+            f = lambda: da.v1_bwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], o1, o2, lse, dy, li,
+                                  li, w.eps, workspace=wsb)
+            for _ in range(args.warmup):
+                f()
+            ms = time_calls(f, iters, stream)
+            flop = v1_bwd_flops(w.B, w.T, w.H, w.d, w.dv)
+            tf = flop / (ms * 1e-3) / 1e12
+            secondary["v1_backward"] = {"workload": name, "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
+                                        "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flop": flop,
+                                        "traffic": hbm_traffic("v1bwd", name)}
+            del x, dy, o1, o2, lse, wsb
             torch.cuda.empty_cache()
     if secondary:
         result["secondary"] = secondary

@@ -33,18 +33,20 @@ __device__ __forceinline__ int trans_offset(int row, int byte_in_row) {
   return row * BTile<D>::kRowBytes + ((c32 ^ (row & (n32 - 1))) << 5) + (byte_in_row & 31);
 }
 
-// Direct-to-LDS load of a 64-row tile: rows r0 .. r0+63 of a bf16 matrix whose
-// consecutive rows are `stride` elements apart, rows >= n_valid clamped to the
-// last valid row (their values are masked by the caller).  TRANS selects the
-// layout.  Each wave issues kInstr / NW loads of 1 KiB.
-template <int D, bool TRANS, int NW = kWaves>
+// Direct-to-LDS load of a ROWS-row tile: rows r0 .. r0+ROWS-1 of a bf16 matrix
+// whose consecutive rows are `stride` elements apart, rows >= n_valid clamped
+// to the last valid row (their values are masked by the caller).  TRANS
+// selects the layout.  The tile is ROWS * D * 2 / 1024 loads of 1 KiB, dealt
+// round-robin to the NW waves.
+template <int D, bool TRANS, int NW = kWaves, int ROWS = 64>
 __device__ __forceinline__ void load_tile(const uint16_t* base, size_t stride, int n_valid,
                                           uint8_t* lds, int wave, int lane) {
   using TL = BTile<D>;
+  constexpr int kInstr = ROWS * TL::kRowBytes / 1024;
 #pragma unroll
-  for (int j = 0; j < (TL::kInstr + NW - 1) / NW; ++j) {
+  for (int j = 0; j < (kInstr + NW - 1) / NW; ++j) {
     const int blk = wave + j * NW;
-    if (TL::kInstr % NW != 0 && blk >= TL::kInstr) break;
+    if (kInstr % NW != 0 && blk >= kInstr) break;
     const int off = blk * 1024 + lane * 16;  // LDS byte this lane fills
     const int r = off / TL::kRowBytes;
     const int pos = (off % TL::kRowBytes) >> 4;

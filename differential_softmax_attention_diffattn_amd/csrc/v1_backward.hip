@@ -21,13 +21,13 @@
 //  * v1_bwd_dq_kernel: a wave owns 16 query rows of one (batch, head) and both
 //    maps, lanes own query columns; K1, K2 and V tiles of 64 keys stream
 //    through LDS: S1^T, S2^T, dP^T = V dz^T, dS^T, dQ_k^T += K_k^T dS_k^T.
-//  * v1_bwd_dkdv_kernel: a workgroup of 4 waves owns 64 keys of one (batch,
-//    head), a wave 16 keys with their K1, K2 and V fragments in registers
-//    (lanes own key columns); Q1, Q2 and dz tiles of 64 rows stream through
-//    LDS: S1, S2, dP = dz V^T, dS, dV += (P1 - lambda P2)^T dz,
-//    dK_k += dS_k^T Q_k.
-// MFMA work is 16x16x32 bf16 with fp32 accumulation; P, dS and dz are rounded
-// to bf16 as operands.
+//  * v1_bwd_dkdv_kernel: a workgroup of 4 waves owns 128 keys of one (batch,
+//    head), a wave 32 keys with their K1 and K2 fragments in registers
+//    (lanes own key columns) and V in LDS; Q1, Q2 and dz tiles of 32 rows
+//    stream through LDS: S1, S2, dP = dz V^T, dS, dV += (P1 - lambda P2)^T dz,
+//    dK_k += dS_k^T Q_k, as 32x32x16 MFMAs.
+// MFMA work is bf16 with fp32 accumulation (16x16x32 in the dQ kernel); P, dS
+// and dz are rounded to bf16 as operands.
 #include <math.h>
 
 #include "bwd_common.h"
@@ -153,24 +153,31 @@ __global__ __launch_bounds__(256) void v1_bwd_pre_kernel(V1BwdArgs a, int Tp, ui
   if (threadIdx.x == 0) pb[0] = redl[0] + redl[1] + redl[2] + redl[3];
 }
 
-// Fixed-order sums of the per-block partials into dlambda and dw.
+// Fixed-order sums of the per-block partials into dlambda and dw: a workgroup
+// per 64 partial columns (column 0 is dlambda, 4.. are dw), 16 waves each
+// summing every 16th partial row, then the 16 wave sums in order.
+constexpr int kRedWaves = 16;
 template <int DV>
-__global__ __launch_bounds__(256) void v1_bwd_reduce_kernel(V1BwdArgs a, const float* part,
-                                                            int nblk) {
-  if (a.dnorm_weight != nullptr) {
-    for (int c = threadIdx.x; c < DV; c += blockDim.x) {
-      float acc = 0.f;
-      for (int k = 0; k < nblk; ++k) acc += part[(size_t)k * (DV + 4) + 4 + c];
-      a.dnorm_weight[c] = acc;
-    }
+__global__ __launch_bounds__(kRedWaves * kWave) void v1_bwd_reduce_kernel(V1BwdArgs a,
+                                                                         const float* part,
+                                                                         int nblk) {
+  __shared__ float acc_s[kRedWaves][kWave];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = blockIdx.x * kWave + lane;
+  float acc = 0.f;
+  if (col < DV + 4) {
+#pragma unroll 8
+    for (int k = wave; k < nblk; k += kRedWaves) acc += part[(size_t)k * (DV + 4) + col];
   }
-  if (a.dlambda != nullptr && threadIdx.x < kWave) {
-    float acc = 0.f;
-    for (int k = threadIdx.x; k < nblk; k += kWave) acc += part[(size_t)k * (DV + 4)];
+  acc_s[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  float t = 0.f;
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-    if (threadIdx.x == 0) a.dlambda[0] = acc;
-  }
+  for (int w = 0; w < kRedWaves; ++w) t += acc_s[w][lane];
+  if (col == 0 && a.dlambda != nullptr) a.dlambda[0] = t;
+  if (col >= 4 && col < DV + 4 && a.dnorm_weight != nullptr) a.dnorm_weight[col - 4] = t;
 }
 
 // ---------------------------------------------------------------------------
@@ -369,158 +376,195 @@ __global__ __launch_bounds__(kDqWaves * kWave, 1) void v1_bwd_dq_kernel(V1BwdArg
 }
 
 // ---------------------------------------------------------------------------
-// dK1, dK2 and dV: a workgroup of 4 waves owns 64 keys of one (batch, head).
+// dK1, dK2 and dV: a workgroup of 4 waves owns 128 keys of one (batch, head),
+// a wave 32 keys (32x32x16 MFMAs: each staged operand read feeds twice the
+// work of a 16-wide tile).  Per wave: dK1, dK2 [32 keys x D] and dV [32 keys
+// x DV] accumulators, K1 and K2 fragments in registers; V of the 128 keys
+// stays in LDS for the whole kernel; Q1, Q2 and dz stream by 32-row tiles.
 // ---------------------------------------------------------------------------
+constexpr int kKvRows = 32;  // query rows per staged tile (dK/dV)
+
 template <int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kKvWaves * kWave, 1) void v1_bwd_dkdv_kernel(V1BwdArgs a, int Tp,
                                                                          const uint16_t* dz,
                                                                          const float* stats) {
   using TK = BTile<D>;
   using TV = BTile<DV>;
-  constexpr int NC = D / 32;
-  constexpr int NCV = DV / 32;
-  constexpr int NDB = D / 16;
-  constexpr int NDBV = DV / 16;
-  constexpr int kKvKeys = kKvWaves * 16;
-  // per stage: Q1, Q2 (transposing layout, read both ways), dz (same), then the
-  // rows' log2 lse of both maps and D1, D2 (fp32 x 64 each)
-  constexpr int kVec = 4 * kQRows * 4;
-  constexpr int kStage = 2 * TK::kBytes + TV::kBytes + kVec;
+  constexpr int NK = D / 16;    // k-steps of the products over d
+  constexpr int NKV = DV / 16;  // k-steps over dv
+  constexpr int NDB = D / 32;   // 32-column blocks of dK
+  constexpr int NVB = DV / 32;  // 32-column blocks of dV
+  constexpr int kKvKeys = kKvWaves * 32;
+  // per stage: 32-row Q1, Q2 and dz tiles (transposing layout, read both
+  // ways), then the rows' log2 lse of both maps and D1, D2 (fp32 x 32 each)
+  constexpr int kQB = kKvRows * TK::kRowBytes;
+  constexpr int kZB = kKvRows * TV::kRowBytes;
+  constexpr int kStage = 2 * kQB + kZB + 4 * kKvRows * 4;
+  __shared__ __align__(16) uint8_t vtile[kKvKeys * TV::kRowBytes];
   __shared__ __align__(16) uint8_t st0[kStage];
   __shared__ __align__(16) uint8_t st1[kStage];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4;
-  const int c16 = lane & 15;
+  const int hf = lane >> 5;   // k group of the operands, row group of the results
+  const int c32 = lane & 31;  // operand row / result column
+  const int j16 = lane & 15;
+  const int hi16 = (lane >> 4) & 1;
   const int T = a.T;
   const int BH = a.B * a.H;
-  const int n_qt = (T + kQRows - 1) / kQRows;
+  const int n_qt = (T + kKvRows - 1) / kKvRows;
   const int kt = blockIdx.x / BH;  // key tiles with the most query tiles first
   const int bh = blockIdx.x - kt * BH;
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const int key0 = kt * kKvKeys;
-  const int qt0 = CAUSAL ? key0 / kQRows : 0;
+  const int key_w = key0 + wave * 32;
+  const int qt0 = CAUSAL ? key0 / kKvRows : 0;
   const int n_items = n_qt - qt0;  // query tiles, last first
 
-  const int key = key0 + wave * 16 + c16;  // this lane's key column
+  const int key = key_w + c32;  // this lane's key column
   const int keyc = min(key, T - 1);
   const size_t rk = ((size_t)b * T + keyc) * a.H + h;
-  u32x4 k1f[NC], k2f[NC], vf[NCV];
+  u32x4 k1f[NK], k2f[NK];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    k1f[c] = ldg128(a.k1 + rk * D + c * 32 + g * 8);
-    k2f[c] = ldg128(a.k2 + rk * D + c * 32 + g * 8);
+  for (int c = 0; c < NK; ++c) {
+    k1f[c] = ldg128(a.k1 + rk * D + c * 16 + hf * 8);
+    k2f[c] = ldg128(a.k2 + rk * D + c * 16 + hf * 8);
   }
-#pragma unroll
-  for (int c = 0; c < NCV; ++c) vf[c] = ldg128(a.v + rk * DV + c * 32 + g * 8);
   const float cs = kLog2e / sqrtf((float)D);
-  const int wave_key_lo = key0 + wave * 16;
 
   const size_t qstr = (size_t)a.H * D, zstr = (size_t)a.H * DV;
+  {
+    const size_t rv = ((size_t)b * T + key0) * a.H + h;
+    load_tile<DV, false, kKvWaves, kKvKeys>(a.v + rv * DV, zstr, T - key0, vtile, wave, lane);
+  }
   auto load = [&](int item, uint8_t* st) {
-    const int r0 = (n_qt - 1 - item) * kQRows;
+    const int r0 = (n_qt - 1 - item) * kKvRows;
     const size_t rr = ((size_t)b * T + r0) * a.H + h;
-    load_tile<D, true, kKvWaves>(a.q1 + rr * D, qstr, T - r0, st, wave, lane);
-    load_tile<D, true, kKvWaves>(a.q2 + rr * D, qstr, T - r0, st + TK::kBytes, wave, lane);
-    load_tile<DV, true, kKvWaves>(dz + rr * DV, zstr, T - r0, st + 2 * TK::kBytes, wave, lane);
-    if (lane < 16)  // wave k loads row vector k (256 bytes)
+    load_tile<D, true, kKvWaves, kKvRows>(a.q1 + rr * D, qstr, T - r0, st, wave, lane);
+    load_tile<D, true, kKvWaves, kKvRows>(a.q2 + rr * D, qstr, T - r0, st + kQB, wave, lane);
+    load_tile<DV, true, kKvWaves, kKvRows>(dz + rr * DV, zstr, T - r0, st + 2 * kQB, wave, lane);
+    if (lane < kKvRows / 4)  // wave k loads row vector k (128 bytes)
       dma16(stats + ((size_t)bh * 4 + wave) * Tp + r0, (uint32_t)(lane * 16),
-            st + 2 * TK::kBytes + TV::kBytes + wave * 256);
+            st + 2 * kQB + kZB + wave * kKvRows * 4);
   };
 
-  f32x4 dk1[NDB], dk2[NDB], dvv[NDBV];
+  f32x16 dk1[NDB], dk2[NDB], dvv[NVB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    dk1[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dk2[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 16; ++i) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      dk1[db][i] = 0.f;
+      dk2[db][i] = 0.f;
+    }
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) dvv[vb][i] = 0.f;
   }
-#pragma unroll
-  for (int db = 0; db < NDBV; ++db) dvv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int tr_row = 4 * g + (c16 >> 2);
-  const int tr_byte = 8 * (c16 & 3);
+  // transposing reads (B operands of dV and dK): lane j16 of each 16-lane group
+  // addresses row tr_row (+8 for the second read) and the 4-column chunk
+  // tr_col of a 32-column block; the group receives columns 16 hi16 .. +15
+  const int tr_row = 4 * hf + (j16 >> 2);
+  const int tr_col = 16 * hi16 + 4 * (j16 & 3);
+  const uint8_t* vrow = vtile + (wave * 32 + c32) * TV::kRowBytes;
+  const int vsw = (wave * 32 + c32) & (TV::kChunks - 1);
 
   auto work = [&](auto masked, int item, const uint8_t* st) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
-    const int r0 = (n_qt - 1 - item) * kQRows;
-    if (CAUSAL && r0 + kQRows <= wave_key_lo) return;  // every key of the wave is above the rows
+    const int r0 = (n_qt - 1 - item) * kKvRows;
+    if (CAUSAL && r0 + kKvRows - 1 < key_w) return;  // every key of the wave is above the rows
     const uint8_t* q1l = st;
-    const uint8_t* q2l = st + TK::kBytes;
-    const uint8_t* zl = st + 2 * TK::kBytes;
-    const float* vec = reinterpret_cast<const float*>(st + 2 * TK::kBytes + TV::kBytes);
+    const uint8_t* q2l = st + kQB;
+    const uint8_t* zl = st + 2 * kQB;
+    const float* vec = reinterpret_cast<const float*>(st + 2 * kQB + kZB);
+    f32x16 s1, s2, dp;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {  // 32-query halves: one k-step of the dV / dK products
-      float pc[2][4], d1[2][4], d2[2][4];
+    for (int i = 0; i < 16; ++i) s1[i] = s2[i] = dp[i] = 0.f;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int qb = 2 * s + j;
-        f32x4 s1 = f32x4{0.f, 0.f, 0.f, 0.f}, s2 = s1, dp = s1;
+    for (int c = 0; c < NK; ++c) {
+      const int off = trans_offset<D>(c32, c * 32 + hf * 16);
+      s1 = mfma32_bf16(*reinterpret_cast<const u32x4*>(q1l + off), k1f[c], s1);
+      s2 = mfma32_bf16(*reinterpret_cast<const u32x4*>(q2l + off), k2f[c], s2);
+      if ((c & 1) == 1) __builtin_amdgcn_sched_barrier(0);  // bounds the reads in flight
+    }
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const int off = trans_offset<D>(qb * 16 + c16, (c * 4 + g) * 16);
-          s1 = mfma_bf16(*reinterpret_cast<const u32x4*>(q1l + off), k1f[c], s1);
-          s2 = mfma_bf16(*reinterpret_cast<const u32x4*>(q2l + off), k2f[c], s2);
-        }
+    for (int c = 0; c < NKV; ++c) {
+      const u32x4 vb = *reinterpret_cast<const u32x4*>(vrow + (((2 * c + hf) ^ vsw) << 4));
+      dp = mfma32_bf16(*reinterpret_cast<const u32x4*>(zl + trans_offset<DV>(c32, c * 32 + hf * 16)),
+                       vb, dp);
+      if ((c & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+    // result element i: query row r0 + 8 (i / 4) + 4 hf + i % 4, key column c32
+    u32x4 pa[2], sa1[2], sa2[2];
 #pragma unroll
-        for (int c = 0; c < NCV; ++c)
-          dp = mfma_bf16(*reinterpret_cast<const u32x4*>(zl + trans_offset<DV>(qb * 16 + c16, (c * 4 + g) * 16)),
-                         vf[c], dp);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(vec + qb * 16 + 4 * g);
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(vec + kQRows + qb * 16 + 4 * g);
-        const f32x4 e1 = *reinterpret_cast<const f32x4*>(vec + 2 * kQRows + qb * 16 + 4 * g);
-        const f32x4 e2 = *reinterpret_cast<const f32x4*>(vec + 3 * kQRows + qb * 16 + 4 * g);
+    for (int ks = 0; ks < 2; ++ks) {
+      float pc[8], x1[8], x2[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int q = r0 + qb * 16 + 4 * g + i;
-          float p1 = fast_exp2(fmaf(s1[i], cs, -l1[i]));
-          float p2 = fast_exp2(fmaf(s2[i], cs, -l2[i]));
-          if (MASKED && (q >= T || key >= T || (CAUSAL && key > q))) {
-            p1 = 0.f;
-            p2 = 0.f;
+      for (int gq = 0; gq < 2; ++gq) {
+        const int rb = 16 * ks + 8 * gq + 4 * hf;  // tile row of element 4 (2 ks + gq)
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(vec + rb);
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(vec + kKvRows + rb);
+        const f32x4 e1 = *reinterpret_cast<const f32x4*>(vec + 2 * kKvRows + rb);
+        const f32x4 e2 = *reinterpret_cast<const f32x4*>(vec + 3 * kKvRows + rb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 8 * ks + 4 * gq + e;
+          const int q = r0 + rb + e;
+          float p1 = fast_exp2(fmaf(s1[i], cs, -l1[e]));
+          float p2 = fast_exp2(fmaf(s2[i], cs, -l2[e]));
+          if (MASKED) {  // a select, not a branch: every lane takes the same path
+            const bool ok = (q < T) & (key < T) & (!CAUSAL | (key <= q));
+            p1 = ok ? p1 : 0.f;
+            p2 = ok ? p2 : 0.f;
           }
-          pc[j][i] = fmaf(-a.lambda, p2, p1);
-          d1[j][i] = p1 * (dp[i] - e1[i]);
-          d2[j][i] = p2 * fmaf(-a.lambda, dp[i], -e2[i]);
+          pc[4 * gq + e] = fmaf(-a.lambda, p2, p1);
+          x1[4 * gq + e] = p1 * (dp[i] - e1[e]);
+          x2[4 * gq + e] = p2 * fmaf(-a.lambda, dp[i], -e2[e]);
         }
       }
-      auto pack = [](const float (&x)[2][4]) {
-        return u32x4{pack_bf16x2(x[0][0], x[0][1]), pack_bf16x2(x[0][2], x[0][3]),
-                     pack_bf16x2(x[1][0], x[1][1]), pack_bf16x2(x[1][2], x[1][3])};
+      auto pack = [](const float (&x)[8]) {
+        return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                     pack_bf16x2(x[6], x[7])};
       };
-      const u32x4 pa = pack(pc), sa1 = pack(d1), sa2 = pack(d2);
+      pa[ks] = pack(pc);
+      sa1[ks] = pack(x1);
+      sa2[ks] = pack(x2);
+    }
+    // dV += (P1 - lambda P2)^T dz, dK_k += dS_k^T Q_k: k = the 32 query rows
 #pragma unroll
-      for (int db = 0; db < NDBV; ++db) {
-        const int off = trans_offset<DV>(s * 32 + tr_row, db * 32 + tr_byte);
-        const u32x2 lo = lds_read_tr16(zl + off), hi = lds_read_tr16(zl + off + 16 * TV::kRowBytes);
-        dvv[db] = mfma_bf16(pa, u32x4{lo[0], lo[1], hi[0], hi[1]}, dvv[db]);
+    for (int ks = 0; ks < 2; ++ks) {
+      const int row = 16 * ks + tr_row;
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb) {
+        // rows r and r + 8 can sit in different swizzle classes: two offsets
+        const int col = 2 * (vb * 32 + tr_col);
+        const u32x2 lo = lds_read_tr16(zl + trans_offset<DV>(row, col));
+        const u32x2 hi = lds_read_tr16(zl + trans_offset<DV>(row + 8, col));
+        dvv[vb] = mfma32_bf16(pa[ks], u32x4{lo[0], lo[1], hi[0], hi[1]}, dvv[vb]);
+        if ((vb & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int off = trans_offset<D>(s * 32 + tr_row, db * 32 + tr_byte);
-        const u32x2 a1 = lds_read_tr16(q1l + off), b1 = lds_read_tr16(q1l + off + 16 * TK::kRowBytes);
-        const u32x2 a2 = lds_read_tr16(q2l + off), b2 = lds_read_tr16(q2l + off + 16 * TK::kRowBytes);
-        dk1[db] = mfma_bf16(sa1, u32x4{a1[0], a1[1], b1[0], b1[1]}, dk1[db]);
-        dk2[db] = mfma_bf16(sa2, u32x4{a2[0], a2[1], b2[0], b2[1]}, dk2[db]);
+        const int col = 2 * (db * 32 + tr_col);
+        const int off0 = trans_offset<D>(row, col), off1 = trans_offset<D>(row + 8, col);
+        const u32x2 a1 = lds_read_tr16(q1l + off0), b1 = lds_read_tr16(q1l + off1);
+        const u32x2 a2 = lds_read_tr16(q2l + off0), b2 = lds_read_tr16(q2l + off1);
+        dk1[db] = mfma32_bf16(sa1[ks], u32x4{a1[0], a1[1], b1[0], b1[1]}, dk1[db]);
+        dk2[db] = mfma32_bf16(sa2[ks], u32x4{a2[0], a2[1], b2[0], b2[1]}, dk2[db]);
+        if ((db & 1) == 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
   auto item_masked = [&](int item) {
-    const int r0 = (n_qt - 1 - item) * kQRows;
-    return (CAUSAL && r0 < key0 + kKvKeys) || r0 + kQRows > T || key0 + kKvKeys > T;
+    const int r0 = (n_qt - 1 - item) * kKvRows;
+    return (CAUSAL && r0 < key0 + kKvKeys) || r0 + kKvRows > T || key0 + kKvKeys > T;
   };
   auto run = [&](int item, const uint8_t* st) __attribute__((always_inline)) {
-    if (!CAUSAL || item_masked(item))
-      work(BoolTag<true>{}, item, st);
-    else
-      work(BoolTag<false>{}, item, st);
+    work(BoolTag<true>{}, item, st);
   };
 
-  if (n_items > 0) {
-    load(0, st0);
-    __builtin_amdgcn_s_waitcnt(0x0f70);
-    __syncthreads();
-  }
+  if (n_items > 0) load(0, st0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
   int it = 0;
   for (; it + 2 <= n_items; it += 2) {  // unrolled by two: each stage a fixed LDS object
     load(it + 1, st1);
@@ -534,20 +578,20 @@ __global__ __launch_bounds__(kKvWaves * kWave, 1) void v1_bwd_dkdv_kernel(V1BwdA
   }
   if (it < n_items) run(it, st0);
 
-  // C layout: lane column = channel (16 db + c16), rows = keys 4 g + i of the wave's 16
+  // result element i: key row key_w + 8 (i / 4) + 4 hf + i % 4, column c32 of the block
   const float scale = 1.0f / sqrtf((float)D);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int kk = key0 + wave * 16 + 4 * g + i;
+  for (int i = 0; i < 16; ++i) {
+    const int kk = key_w + 8 * (i / 4) + 4 * hf + (i % 4);
     if (kk >= T) continue;
     const size_t r = ((size_t)b * T + kk) * a.H + h;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      a.dk1[r * D + db * 16 + c16] = dk1[db][i] * scale;
-      a.dk2[r * D + db * 16 + c16] = dk2[db][i] * scale;
+      a.dk1[r * D + db * 32 + c32] = dk1[db][i] * scale;
+      a.dk2[r * D + db * 32 + c32] = dk2[db][i] * scale;
     }
 #pragma unroll
-    for (int db = 0; db < NDBV; ++db) a.dvg[r * DV + db * 16 + c16] = dvv[db][i];
+    for (int vb = 0; vb < NVB; ++vb) a.dvg[r * DV + vb * 32 + c32] = dvv[vb][i];
   }
 }
 
@@ -574,8 +618,8 @@ Layout<D, DV> layout(int B, int T, int H) {
 template <int D, int DV>
 hipError_t launch_typed(const V1BwdArgs& a, hipStream_t stream) {
   if ((long long)a.B * a.T * a.H == 0) {  // no rows: dlambda and dw are empty sums
-    hipLaunchKernelGGL((v1_bwd_reduce_kernel<DV>), dim3(1), dim3(256), 0, stream, a,
-                       (const float*)nullptr, 0);
+    hipLaunchKernelGGL((v1_bwd_reduce_kernel<DV>), dim3((DV + 4 + kWave - 1) / kWave),
+                       dim3(kRedWaves * kWave), 0, stream, a, (const float*)nullptr, 0);
     return hipGetLastError();
   }
   const auto L = layout<D, DV>(a.B, a.T, a.H);
@@ -585,11 +629,11 @@ hipError_t launch_typed(const V1BwdArgs& a, hipStream_t stream) {
   float* part = reinterpret_cast<float*>(ws + L.part);
   hipLaunchKernelGGL((v1_bwd_pre_kernel<DV>), dim3(L.nblk), dim3(256), 0, stream, a, L.Tp, dz,
                      stats, part);
-  hipLaunchKernelGGL((v1_bwd_reduce_kernel<DV>), dim3(1), dim3(256), 0, stream, a,
-                     (const float*)part, L.nblk);
+  hipLaunchKernelGGL((v1_bwd_reduce_kernel<DV>), dim3((DV + 4 + kWave - 1) / kWave),
+                     dim3(kRedWaves * kWave), 0, stream, a, (const float*)part, L.nblk);
   const long long BH = (long long)a.B * a.H;
   const long long dq_blocks = (long long)((a.T + kDqWaves * kRows - 1) / (kDqWaves * kRows)) * BH;
-  const long long kv_blocks = (long long)((a.T + kKvWaves * 16 - 1) / (kKvWaves * 16)) * BH;
+  const long long kv_blocks = (long long)((a.T + kKvWaves * 32 - 1) / (kKvWaves * 32)) * BH;
   if (dq_blocks > 0x7fffffffLL || kv_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.causal) {
     hipLaunchKernelGGL((v1_bwd_dq_kernel<D, DV, true>), dim3((unsigned)dq_blocks),
