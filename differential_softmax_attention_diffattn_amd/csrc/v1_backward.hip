@@ -21,13 +21,13 @@
 //  * v1_bwd_dq_kernel: a wave owns 16 query rows of one (batch, head) and both
 //    maps, lanes own query columns; K1, K2 and V tiles of 64 keys stream
 //    through LDS: S1^T, S2^T, dP^T = V dz^T, dS^T, dQ_k^T += K_k^T dS_k^T.
-//  * v1_bwd_dkdv_kernel: a workgroup of 4 waves owns 128 keys of one (batch,
-//    head), a wave 32 keys with their K1 and K2 fragments in registers
+//  * v1_bwd_dkdv_kernel: a workgroup of 8 waves owns 128 keys of one (batch,
+//    head), a wave 16 keys with their K1 and K2 fragments in registers
 //    (lanes own key columns) and V in LDS; Q1, Q2 and dz tiles of 32 rows
 //    stream through LDS: S1, S2, dP = dz V^T, dS, dV += (P1 - lambda P2)^T dz,
-//    dK_k += dS_k^T Q_k, as 32x32x16 MFMAs.
-// MFMA work is bf16 with fp32 accumulation (16x16x32 in the dQ kernel); P, dS
-// and dz are rounded to bf16 as operands.
+//    dK_k += dS_k^T Q_k.
+// MFMA work is 16x16x32 bf16 with fp32 accumulation; P, dS and dz are rounded
+// to bf16 as operands.
 #include <math.h>
 
 #include "bwd_common.h"
@@ -46,7 +46,6 @@ constexpr int kKeys = 64;     // keys per staged tile (dq)
 constexpr int kQRows = 64;    // query rows per staged tile (dkdv)
 constexpr int kRows = 16;     // query rows per wave (dq)
 constexpr int kDqWaves = 8;   // dq: 128 query rows per workgroup
-constexpr int kKvWaves = 4;   // dkdv: 64 keys per workgroup, one wave per SIMD
 constexpr int kPreBlocks = 1024;
 
 template <bool B>
@@ -376,25 +375,26 @@ __global__ __launch_bounds__(kDqWaves * kWave, 1) void v1_bwd_dq_kernel(V1BwdArg
 }
 
 // ---------------------------------------------------------------------------
-// dK1, dK2 and dV: a workgroup of 4 waves owns 128 keys of one (batch, head),
-// a wave 32 keys (32x32x16 MFMAs: each staged operand read feeds twice the
-// work of a 16-wide tile).  Per wave: dK1, dK2 [32 keys x D] and dV [32 keys
-// x DV] accumulators, K1 and K2 fragments in registers; V of the 128 keys
-// stays in LDS for the whole kernel; Q1, Q2 and dz stream by 32-row tiles.
+// dK1, dK2 and dV: a workgroup of 8 waves (two per SIMD, so one wave's MFMAs
+// overlap the other's softmax work) owns 128 keys of one (batch, head), a
+// wave 16 keys.  Per wave: dK1, dK2 [16 keys x D] and dV [16 keys x DV]
+// accumulators and the K1, K2 fragments in registers; V of the 128 keys stays
+// in LDS for the whole kernel; Q1, Q2 and dz stream by 32-row tiles.
 // ---------------------------------------------------------------------------
-constexpr int kKvRows = 32;  // query rows per staged tile (dK/dV)
+constexpr int kKvRows = 32;   // query rows per staged tile (dK/dV)
+constexpr int kKvWaves8 = 8;  // waves of the dK/dV workgroup
 
 template <int D, int DV, bool CAUSAL>
-__global__ __launch_bounds__(kKvWaves * kWave, 1) void v1_bwd_dkdv_kernel(V1BwdArgs a, int Tp,
-                                                                         const uint16_t* dz,
-                                                                         const float* stats) {
+__global__ __launch_bounds__(kKvWaves8 * kWave) void v1_bwd_dkdv_kernel(V1BwdArgs a, int Tp,
+                                                                       const uint16_t* dz,
+                                                                       const float* stats) {
   using TK = BTile<D>;
   using TV = BTile<DV>;
-  constexpr int NK = D / 16;    // k-steps of the products over d
-  constexpr int NKV = DV / 16;  // k-steps over dv
-  constexpr int NDB = D / 32;   // 32-column blocks of dK
-  constexpr int NVB = DV / 32;  // 32-column blocks of dV
-  constexpr int kKvKeys = kKvWaves * 32;
+  constexpr int NC = D / 32;     // k-steps of the products over d
+  constexpr int NCV = DV / 32;   // k-steps over dv
+  constexpr int NDB = D / 16;    // 16-column blocks of dK
+  constexpr int NDBV = DV / 16;  // 16-column blocks of dV
+  constexpr int kKvKeys = kKvWaves8 * 16;
   // per stage: 32-row Q1, Q2 and dz tiles (transposing layout, read both
   // ways), then the rows' log2 lse of both maps and D1, D2 (fp32 x 32 each)
   constexpr int kQB = kKvRows * TK::kRowBytes;
@@ -406,10 +406,8 @@ __global__ __launch_bounds__(kKvWaves * kWave, 1) void v1_bwd_dkdv_kernel(V1BwdA
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hf = lane >> 5;   // k group of the operands, row group of the results
-  const int c32 = lane & 31;  // operand row / result column
-  const int j16 = lane & 15;
-  const int hi16 = (lane >> 4) & 1;
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
   const int T = a.T;
   const int BH = a.B * a.H;
   const int n_qt = (T + kKvRows - 1) / kKvRows;
@@ -418,148 +416,122 @@ __global__ __launch_bounds__(kKvWaves * kWave, 1) void v1_bwd_dkdv_kernel(V1BwdA
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const int key0 = kt * kKvKeys;
-  const int key_w = key0 + wave * 32;
+  const int key_w = key0 + wave * 16;
   const int qt0 = CAUSAL ? key0 / kKvRows : 0;
   const int n_items = n_qt - qt0;  // query tiles, last first
 
-  const int key = key_w + c32;  // this lane's key column
+  const int key = key_w + c16;  // this lane's key column
   const int keyc = min(key, T - 1);
   const size_t rk = ((size_t)b * T + keyc) * a.H + h;
-  u32x4 k1f[NK], k2f[NK];
+  u32x4 k1f[NC], k2f[NC];
 #pragma unroll
-  for (int c = 0; c < NK; ++c) {
-    k1f[c] = ldg128(a.k1 + rk * D + c * 16 + hf * 8);
-    k2f[c] = ldg128(a.k2 + rk * D + c * 16 + hf * 8);
+  for (int c = 0; c < NC; ++c) {
+    k1f[c] = ldg128(a.k1 + rk * D + c * 32 + g * 8);
+    k2f[c] = ldg128(a.k2 + rk * D + c * 32 + g * 8);
   }
   const float cs = kLog2e / sqrtf((float)D);
 
   const size_t qstr = (size_t)a.H * D, zstr = (size_t)a.H * DV;
   {
     const size_t rv = ((size_t)b * T + key0) * a.H + h;
-    load_tile<DV, false, kKvWaves, kKvKeys>(a.v + rv * DV, zstr, T - key0, vtile, wave, lane);
+    load_tile<DV, false, kKvWaves8, kKvKeys>(a.v + rv * DV, zstr, T - key0, vtile, wave, lane);
   }
   auto load = [&](int item, uint8_t* st) {
     const int r0 = (n_qt - 1 - item) * kKvRows;
     const size_t rr = ((size_t)b * T + r0) * a.H + h;
-    load_tile<D, true, kKvWaves, kKvRows>(a.q1 + rr * D, qstr, T - r0, st, wave, lane);
-    load_tile<D, true, kKvWaves, kKvRows>(a.q2 + rr * D, qstr, T - r0, st + kQB, wave, lane);
-    load_tile<DV, true, kKvWaves, kKvRows>(dz + rr * DV, zstr, T - r0, st + 2 * kQB, wave, lane);
-    if (lane < kKvRows / 4)  // wave k loads row vector k (128 bytes)
+    load_tile<D, true, kKvWaves8, kKvRows>(a.q1 + rr * D, qstr, T - r0, st, wave, lane);
+    load_tile<D, true, kKvWaves8, kKvRows>(a.q2 + rr * D, qstr, T - r0, st + kQB, wave, lane);
+    load_tile<DV, true, kKvWaves8, kKvRows>(dz + rr * DV, zstr, T - r0, st + 2 * kQB, wave, lane);
+    if (wave < 4 && lane < kKvRows / 4)  // wave k < 4 loads row vector k (128 bytes)
       dma16(stats + ((size_t)bh * 4 + wave) * Tp + r0, (uint32_t)(lane * 16),
             st + 2 * kQB + kZB + wave * kKvRows * 4);
   };
 
-  f32x16 dk1[NDB], dk2[NDB], dvv[NVB];
+  f32x4 dk1[NDB], dk2[NDB], dvv[NDBV];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      dk1[db][i] = 0.f;
-      dk2[db][i] = 0.f;
-    }
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) dvv[vb][i] = 0.f;
+  for (int db = 0; db < NDB; ++db) {
+    dk1[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dk2[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // transposing reads (B operands of dV and dK): lane j16 of each 16-lane group
-  // addresses row tr_row (+8 for the second read) and the 4-column chunk
-  // tr_col of a 32-column block; the group receives columns 16 hi16 .. +15
-  const int tr_row = 4 * hf + (j16 >> 2);
-  const int tr_col = 16 * hi16 + 4 * (j16 & 3);
-  const uint8_t* vrow = vtile + (wave * 32 + c32) * TV::kRowBytes;
-  const int vsw = (wave * 32 + c32) & (TV::kChunks - 1);
+#pragma unroll
+  for (int db = 0; db < NDBV; ++db) dvv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // transposing reads (B operands of dV and dK): lane (g, c16) addresses row
+  // tr_row (+16 for the second read) and the 4-column chunk tr_byte / 2
+  const int tr_row = 4 * g + (c16 >> 2);
+  const int tr_byte = 8 * (c16 & 3);
+  const int vrow = wave * 16 + c16;
 
-  auto work = [&](auto masked, int item, const uint8_t* st) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked)::value;
+  auto work = [&](int item, const uint8_t* st) __attribute__((always_inline)) {
     const int r0 = (n_qt - 1 - item) * kKvRows;
     if (CAUSAL && r0 + kKvRows - 1 < key_w) return;  // every key of the wave is above the rows
     const uint8_t* q1l = st;
     const uint8_t* q2l = st + kQB;
     const uint8_t* zl = st + 2 * kQB;
     const float* vec = reinterpret_cast<const float*>(st + 2 * kQB + kZB);
-    f32x16 s1, s2, dp;
+    // the lane's rows, made opaque here so that the swizzled offsets derived
+    // from them are formed next to their use instead of being kept live
+    // across the loop (dozens of registers)
+    int rr = c16, tr = tr_row, vr = vrow;
+    asm volatile("" : "+v"(rr), "+v"(tr), "+v"(vr));
+    float pc[2][4], x1[2][4], x2[2][4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s1[i] = s2[i] = dp[i] = 0.f;
+    for (int j = 0; j < 2; ++j) {  // 16-row blocks of the tile
+      f32x4 s1 = f32x4{0.f, 0.f, 0.f, 0.f}, s2 = s1, dp = s1;
 #pragma unroll
-    for (int c = 0; c < NK; ++c) {
-      const int off = trans_offset<D>(c32, c * 32 + hf * 16);
-      s1 = mfma32_bf16(*reinterpret_cast<const u32x4*>(q1l + off), k1f[c], s1);
-      s2 = mfma32_bf16(*reinterpret_cast<const u32x4*>(q2l + off), k2f[c], s2);
-      if ((c & 1) == 1) __builtin_amdgcn_sched_barrier(0);  // bounds the reads in flight
-    }
-#pragma unroll
-    for (int c = 0; c < NKV; ++c) {
-      const u32x4 vb = *reinterpret_cast<const u32x4*>(vrow + (((2 * c + hf) ^ vsw) << 4));
-      dp = mfma32_bf16(*reinterpret_cast<const u32x4*>(zl + trans_offset<DV>(c32, c * 32 + hf * 16)),
-                       vb, dp);
-      if ((c & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-    }
-    // result element i: query row r0 + 8 (i / 4) + 4 hf + i % 4, key column c32
-    u32x4 pa[2], sa1[2], sa2[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      float pc[8], x1[8], x2[8];
-#pragma unroll
-      for (int gq = 0; gq < 2; ++gq) {
-        const int rb = 16 * ks + 8 * gq + 4 * hf;  // tile row of element 4 (2 ks + gq)
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(vec + rb);
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(vec + kKvRows + rb);
-        const f32x4 e1 = *reinterpret_cast<const f32x4*>(vec + 2 * kKvRows + rb);
-        const f32x4 e2 = *reinterpret_cast<const f32x4*>(vec + 3 * kKvRows + rb);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 8 * ks + 4 * gq + e;
-          const int q = r0 + rb + e;
-          float p1 = fast_exp2(fmaf(s1[i], cs, -l1[e]));
-          float p2 = fast_exp2(fmaf(s2[i], cs, -l2[e]));
-          if (MASKED) {  // a select, not a branch: every lane takes the same path
-            const bool ok = (q < T) & (key < T) & (!CAUSAL | (key <= q));
-            p1 = ok ? p1 : 0.f;
-            p2 = ok ? p2 : 0.f;
-          }
-          pc[4 * gq + e] = fmaf(-a.lambda, p2, p1);
-          x1[4 * gq + e] = p1 * (dp[i] - e1[e]);
-          x2[4 * gq + e] = p2 * fmaf(-a.lambda, dp[i], -e2[e]);
-        }
-      }
-      auto pack = [](const float (&x)[8]) {
-        return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                     pack_bf16x2(x[6], x[7])};
-      };
-      pa[ks] = pack(pc);
-      sa1[ks] = pack(x1);
-      sa2[ks] = pack(x2);
-    }
-    // dV += (P1 - lambda P2)^T dz, dK_k += dS_k^T Q_k: k = the 32 query rows
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int row = 16 * ks + tr_row;
-#pragma unroll
-      for (int vb = 0; vb < NVB; ++vb) {
-        // rows r and r + 8 can sit in different swizzle classes: two offsets
-        const int col = 2 * (vb * 32 + tr_col);
-        const u32x2 lo = lds_read_tr16(zl + trans_offset<DV>(row, col));
-        const u32x2 hi = lds_read_tr16(zl + trans_offset<DV>(row + 8, col));
-        dvv[vb] = mfma32_bf16(pa[ks], u32x4{lo[0], lo[1], hi[0], hi[1]}, dvv[vb]);
-        if ((vb & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      for (int c = 0; c < NC; ++c) {
+        const int off = trans_offset<D>(j * 16 + rr, (c * 4 + g) * 16);
+        s1 = mfma_bf16(*reinterpret_cast<const u32x4*>(q1l + off), k1f[c], s1);
+        s2 = mfma_bf16(*reinterpret_cast<const u32x4*>(q2l + off), k2f[c], s2);
       }
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int col = 2 * (db * 32 + tr_col);
-        const int off0 = trans_offset<D>(row, col), off1 = trans_offset<D>(row + 8, col);
-        const u32x2 a1 = lds_read_tr16(q1l + off0), b1 = lds_read_tr16(q1l + off1);
-        const u32x2 a2 = lds_read_tr16(q2l + off0), b2 = lds_read_tr16(q2l + off1);
-        dk1[db] = mfma32_bf16(sa1[ks], u32x4{a1[0], a1[1], b1[0], b1[1]}, dk1[db]);
-        dk2[db] = mfma32_bf16(sa2[ks], u32x4{a2[0], a2[1], b2[0], b2[1]}, dk2[db]);
-        if ((db & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+      for (int c = 0; c < NCV; ++c) {
+        const u32x4 vb = *reinterpret_cast<const u32x4*>(vtile + rows_offset<DV>(vr, c * 4 + g));
+        dp = mfma_bf16(
+            *reinterpret_cast<const u32x4*>(zl + trans_offset<DV>(j * 16 + rr, (c * 4 + g) * 16)),
+            vb, dp);
+      }
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(vec + j * 16 + 4 * g);
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(vec + kKvRows + j * 16 + 4 * g);
+      const f32x4 e1 = *reinterpret_cast<const f32x4*>(vec + 2 * kKvRows + j * 16 + 4 * g);
+      const f32x4 e2 = *reinterpret_cast<const f32x4*>(vec + 3 * kKvRows + j * 16 + 4 * g);
+      // result element i: query row r0 + 16 j + 4 g + i, key column c16
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = r0 + j * 16 + 4 * g + i;
+        float p1 = fast_exp2(fmaf(s1[i], cs, -l1[i]));
+        float p2 = fast_exp2(fmaf(s2[i], cs, -l2[i]));
+        // a select, not a branch: every lane takes the same path
+        const bool ok = (q < T) & (key < T) & (!CAUSAL | (key <= q));
+        p1 = ok ? p1 : 0.f;
+        p2 = ok ? p2 : 0.f;
+        pc[j][i] = fmaf(-a.lambda, p2, p1);
+        x1[j][i] = p1 * (dp[i] - e1[i]);
+        x2[j][i] = p2 * fmaf(-a.lambda, dp[i], -e2[i]);
       }
     }
-  };
-  auto item_masked = [&](int item) {
-    const int r0 = (n_qt - 1 - item) * kKvRows;
-    return (CAUSAL && r0 < key0 + kKvKeys) || r0 + kKvRows > T || key0 + kKvKeys > T;
-  };
-  auto run = [&](int item, const uint8_t* st) __attribute__((always_inline)) {
-    work(BoolTag<true>{}, item, st);
+    auto pack = [](const float (&x)[2][4]) {
+      return u32x4{pack_bf16x2(x[0][0], x[0][1]), pack_bf16x2(x[0][2], x[0][3]),
+                   pack_bf16x2(x[1][0], x[1][1]), pack_bf16x2(x[1][2], x[1][3])};
+    };
+    // dV += (P1 - lambda P2)^T dz, dK_k += dS_k^T Q_k over the 32 rows; the
+    // A operands' eight k slots are rows {4g..4g+3, 16+4g..16+4g+3}, matched by
+    // the transposing reads at rows tr_row and tr_row + 16
+    const u32x4 pa = pack(pc), sa1 = pack(x1), sa2 = pack(x2);
+#pragma unroll
+    for (int db = 0; db < NDBV; ++db) {
+      const u32x2 lo = lds_read_tr16(zl + trans_offset<DV>(tr, db * 32 + tr_byte));
+      const u32x2 hi = lds_read_tr16(zl + trans_offset<DV>(tr + 16, db * 32 + tr_byte));
+      dvv[db] = mfma_bf16(pa, u32x4{lo[0], lo[1], hi[0], hi[1]}, dvv[db]);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int off0 = trans_offset<D>(tr, db * 32 + tr_byte);
+      const int off1 = trans_offset<D>(tr + 16, db * 32 + tr_byte);
+      const u32x2 a1 = lds_read_tr16(q1l + off0), b1 = lds_read_tr16(q1l + off1);
+      const u32x2 a2 = lds_read_tr16(q2l + off0), b2 = lds_read_tr16(q2l + off1);
+      dk1[db] = mfma_bf16(sa1, u32x4{a1[0], a1[1], b1[0], b1[1]}, dk1[db]);
+      dk2[db] = mfma_bf16(sa2, u32x4{a2[0], a2[1], b2[0], b2[1]}, dk2[db]);
+    }
   };
 
   if (n_items > 0) load(0, st0);
@@ -568,30 +540,30 @@ __global__ __launch_bounds__(kKvWaves * kWave, 1) void v1_bwd_dkdv_kernel(V1BwdA
   int it = 0;
   for (; it + 2 <= n_items; it += 2) {  // unrolled by two: each stage a fixed LDS object
     load(it + 1, st1);
-    run(it, st0);
+    work(it, st0);
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
     if (it + 2 < n_items) load(it + 2, st0);
-    run(it + 1, st1);
+    work(it + 1, st1);
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
   }
-  if (it < n_items) run(it, st0);
+  if (it < n_items) work(it, st0);
 
-  // result element i: key row key_w + 8 (i / 4) + 4 hf + i % 4, column c32 of the block
+  // result element i: key row key_w + 4 g + i, column 16 db + c16
   const float scale = 1.0f / sqrtf((float)D);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int kk = key_w + 8 * (i / 4) + 4 * hf + (i % 4);
+  for (int i = 0; i < 4; ++i) {
+    const int kk = key_w + 4 * g + i;
     if (kk >= T) continue;
     const size_t r = ((size_t)b * T + kk) * a.H + h;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      a.dk1[r * D + db * 32 + c32] = dk1[db][i] * scale;
-      a.dk2[r * D + db * 32 + c32] = dk2[db][i] * scale;
+      a.dk1[r * D + db * 16 + c16] = dk1[db][i] * scale;
+      a.dk2[r * D + db * 16 + c16] = dk2[db][i] * scale;
     }
 #pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) a.dvg[r * DV + vb * 32 + c32] = dvv[vb][i];
+    for (int db = 0; db < NDBV; ++db) a.dvg[r * DV + db * 16 + c16] = dvv[db][i];
   }
 }
 
@@ -633,21 +605,21 @@ hipError_t launch_typed(const V1BwdArgs& a, hipStream_t stream) {
                      dim3(kRedWaves * kWave), 0, stream, a, (const float*)part, L.nblk);
   const long long BH = (long long)a.B * a.H;
   const long long dq_blocks = (long long)((a.T + kDqWaves * kRows - 1) / (kDqWaves * kRows)) * BH;
-  const long long kv_blocks = (long long)((a.T + kKvWaves * 32 - 1) / (kKvWaves * 32)) * BH;
+  const long long kv_blocks = (long long)((a.T + kKvWaves8 * 16 - 1) / (kKvWaves8 * 16)) * BH;
   if (dq_blocks > 0x7fffffffLL || kv_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.causal) {
     hipLaunchKernelGGL((v1_bwd_dq_kernel<D, DV, true>), dim3((unsigned)dq_blocks),
                        dim3(kDqWaves * kWave), 0, stream, a, L.Tp, (const uint16_t*)dz,
                        (const float*)stats);
     hipLaunchKernelGGL((v1_bwd_dkdv_kernel<D, DV, true>), dim3((unsigned)kv_blocks),
-                       dim3(kKvWaves * kWave), 0, stream, a, L.Tp, (const uint16_t*)dz,
+                       dim3(kKvWaves8 * kWave), 0, stream, a, L.Tp, (const uint16_t*)dz,
                        (const float*)stats);
   } else {
     hipLaunchKernelGGL((v1_bwd_dq_kernel<D, DV, false>), dim3((unsigned)dq_blocks),
                        dim3(kDqWaves * kWave), 0, stream, a, L.Tp, (const uint16_t*)dz,
                        (const float*)stats);
     hipLaunchKernelGGL((v1_bwd_dkdv_kernel<D, DV, false>), dim3((unsigned)kv_blocks),
-                       dim3(kKvWaves * kWave), 0, stream, a, L.Tp, (const uint16_t*)dz,
+                       dim3(kKvWaves8 * kWave), 0, stream, a, L.Tp, (const uint16_t*)dz,
                        (const float*)stats);
   }
   return hipGetLastError();
