@@ -263,13 +263,17 @@ __global__ __launch_bounds__(kDqWaves * kWave, 1) void v1_bwd_dq_kernel(V1BwdArg
   auto step = [&](auto masked, const uint8_t* l1, const uint8_t* l2, const uint8_t* lv, int cc,
                   int k0) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
+    // the lane's rows, made opaque here so that the swizzled offsets derived
+    // from them are formed next to their use instead of being kept live
+    int rr = c16, tk = tr_key;
+    asm volatile("" : "+v"(rr), "+v"(tk));
     f32x4 s1[2], s2[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s1[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
       s2[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
       dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int key = cc * 32 + kb * 16 + c16;
+      const int key = cc * 32 + kb * 16 + rr;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const int off = trans_offset<D>(key, (c * 4 + g) * 16);
@@ -289,9 +293,10 @@ __global__ __launch_bounds__(kDqWaves * kWave, 1) void v1_bwd_dq_kernel(V1BwdArg
         const int key = k0 + kb * 16 + 4 * g + i;
         float p1 = fast_exp2(fmaf(s1[kb][i], cs, -l21));
         float p2 = fast_exp2(fmaf(s2[kb][i], cs, -l22));
-        if (MASKED && (key >= T || (CAUSAL && key > row))) {
-          p1 = 0.f;
-          p2 = 0.f;
+        if (MASKED) {  // a select, not a branch: every lane takes the same path
+          const bool ok = (key < T) & (!CAUSAL | (key <= row));
+          p1 = ok ? p1 : 0.f;
+          p2 = ok ? p2 : 0.f;
         }
         x1[kb * 4 + i] = p1 * (dp[kb][i] - dd1);
         x2[kb * 4 + i] = p2 * fmaf(-a.lambda, dp[kb][i], -dd2);
@@ -299,9 +304,10 @@ __global__ __launch_bounds__(kDqWaves * kWave, 1) void v1_bwd_dq_kernel(V1BwdArg
     const u32x4 ds1 = pack8(x1), ds2 = pack8(x2);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int off = trans_offset<D>(cc * 32 + tr_key, db * 32 + tr_byte);
-      const u32x2 a1 = lds_read_tr16(l1 + off), b1 = lds_read_tr16(l1 + off + 16 * TK::kRowBytes);
-      const u32x2 a2 = lds_read_tr16(l2 + off), b2 = lds_read_tr16(l2 + off + 16 * TK::kRowBytes);
+      const int off0 = trans_offset<D>(cc * 32 + tk, db * 32 + tr_byte);
+      const int off1 = trans_offset<D>(cc * 32 + tk + 16, db * 32 + tr_byte);
+      const u32x2 a1 = lds_read_tr16(l1 + off0), b1 = lds_read_tr16(l1 + off1);
+      const u32x2 a2 = lds_read_tr16(l2 + off0), b2 = lds_read_tr16(l2 + off1);
       dq1[db] = mfma_bf16(u32x4{a1[0], a1[1], b1[0], b1[1]}, ds1, dq1[db]);
       dq2[db] = mfma_bf16(u32x4{a2[0], a2[1], b2[0], b2[1]}, ds2, dq2[db]);
     }

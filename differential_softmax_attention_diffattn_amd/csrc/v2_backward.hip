@@ -443,9 +443,10 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
         const int q = r0 + qb * 16 + 4 * g + i;
         float pe = fast_exp2(fmaf(se[qb][i], cs, -l2e[i]));
         float po = fast_exp2(fmaf(so[qb][i], cs, -l2o[i]));
-        if (MASKED && (q >= T || key >= T || (CAUSAL && key > q))) {
-          pe = 0.f;
-          po = 0.f;
+        if (MASKED) {  // a select, not a branch: every lane takes the same path
+          const bool ok = (q < T) & (key < T) & (!CAUSAL | (key <= q));
+          pe = ok ? pe : 0.f;
+          po = ok ? po : 0.f;
         }
         pv[qb][i] = fmaf(-sg[i], po, pe);
         dse[qb][i] = pe * (dpa[qb][i] - dle[i]);
