@@ -6,6 +6,7 @@ never by the library itself.
 from .diffattn_oracle import (  # noqa: F401
     gqa_kv_head,
     lambda_init,
+    out_projection,
     sigmoid,
     softmax_rows,
     v1_attention,
@@ -17,12 +18,14 @@ from .diffattn_oracle import (  # noqa: F401
     v1_norm,
     v1_norm_backward,
     v2_backward,
+    v2_attention_param_counts,
     v2_backward_query_rows,
     v2_combine,
     v2_decode,
     v2_forward,
     v2_forward_stats,
     v2_heads,
+    v2_lambda_logits,
     v2_sequence,
     v2_sequence_backward,
     v2_varlen_forward,

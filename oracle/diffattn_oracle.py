@@ -504,3 +504,50 @@ def v2_backward_query_rows(q, k, v, logit, dout, rows, causal: bool = True,
         ds = p * (dp - np.sum(do * o, axis=-1, keepdims=True))
         dq[:, j] = scale * (ds @ k[:, kv])
     return dq, dlogit
+
+
+# ---------------------------------------------------------------------------
+# The projections on either side of the V2 attention
+# ---------------------------------------------------------------------------
+
+def v2_lambda_logits(x, w_lambda) -> np.ndarray:
+    """Per-token, per-pair coefficients projected from the layer input.
+
+    V2 summary §1: the coefficient that scales the second head of a pair comes
+    from a projection of X, one per token and pair, and passes through a
+    sigmoid where it is used.  This returns the projection (the logits):
+    x [N, d_model], w_lambda [h, d_model] (one weight row per pair) -> [N, h].
+    """
+    return _f64(x) @ _f64(w_lambda).T
+
+
+def out_projection(attn_out, w_o) -> np.ndarray:
+    """Output projection of the attention output: attn_out [N, K] @ w_o^T.
+
+    V2 summary §1 and §7: after the subtraction each token carries h*d
+    columns, so the output projection has the baseline's shape (h*d in,
+    d_model out).  w_o [d_model, K] (one row per output feature) -> [N, d_model].
+    """
+    return _f64(attn_out) @ _f64(w_o).T
+
+
+def v2_attention_param_counts(d_model: int, h: int, hkv: int, d: int) -> dict:
+    """Weight counts of one attention module, V2 against a 2h-head GQA baseline.
+
+    V2 summary §1, §7: V2 has 2h query heads of dim d (as the baseline with the
+    same 2h*d query width), hkv shared key/value heads, a per-pair coefficient
+    projection (d_model -> h), and an output projection from h*d columns (the
+    difference is taken before it); the baseline projects all 2h*d columns.
+    Returns the counts per projection and the saving as a fraction of the
+    baseline module.
+    """
+    q = d_model * 2 * h * d
+    kv = 2 * d_model * hkv * d
+    lam = d_model * h
+    o_v2 = h * d * d_model
+    o_base = 2 * h * d * d_model
+    v2 = q + kv + lam + o_v2
+    base = q + kv + o_base
+    return {"q": q, "kv": kv, "lambda": lam, "o_v2": o_v2, "o_base": o_base, "v2": v2,
+            "base": base, "o_saving": o_base - o_v2,
+            "o_saving_frac_of_base": (o_base - o_v2) / base}

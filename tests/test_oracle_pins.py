@@ -622,3 +622,69 @@ def test_v1_backward_zero_upstream_gives_zero():
     g = oracle.v1_backward(q, q, q, q, v, 0.2, 0.2, 1e-6, np.zeros_like(v))
     for x in g:
         np.testing.assert_array_equal(x, 0.0)
+
+
+# ---------------------------------------------------------------------------
+# Projections either side of the V2 attention
+# ---------------------------------------------------------------------------
+
+def test_projections_match_brute_force_loops():
+    r = rng(21)
+    x = r.standard_normal((5, 12))
+    w = r.standard_normal((3, 12))
+    got = oracle.v2_lambda_logits(x, w)
+    for n in range(5):
+        for p in range(3):
+            assert abs(got[n, p] - math.fsum(x[n, c] * w[p, c] for c in range(12))) < 1e-12
+    a = r.standard_normal((4, 16))
+    wo = r.standard_normal((6, 16))
+    y = oracle.out_projection(a, wo)
+    for n in range(4):
+        for j in range(6):
+            assert abs(y[n, j] - math.fsum(a[n, c] * wo[j, c] for c in range(16))) < 1e-12
+
+
+def test_difference_before_projection_equals_negated_pair_weights():
+    # V2 summary §7: a 2h-head model could express the difference by giving the
+    # two heads of a pair exactly opposite output weights.  With sigma = 1 the
+    # V2 output projected by W equals the 2h-head outputs projected by
+    # [W_p, -W_p] per pair (sigma < 1 scales the odd head's block instead).
+    r = rng(22)
+    T, Hq, Hkv, d, dm = 9, 8, 2, 4, 5
+    q = r.standard_normal((1, T, Hq, d))
+    k = r.standard_normal((1, T, Hkv, d))
+    v = r.standard_normal((1, T, Hkv, d))
+    h = Hq // 2
+    for logit_val, sig in ((60.0, 1.0), (0.3, float(expit(0.3)))):
+        logit = np.full((1, T, h), logit_val)
+        out = oracle.v2_forward(q, k, v, logit).reshape(T, h * d)
+        heads = oracle.v2_heads(q[0], k[0], v[0]).reshape(T, Hq * d)
+        w = r.standard_normal((dm, h * d))
+        w_base = np.zeros((dm, Hq * d))
+        for p in range(h):
+            w_base[:, (2 * p) * d:(2 * p + 1) * d] = w[:, p * d:(p + 1) * d]
+            w_base[:, (2 * p + 1) * d:(2 * p + 2) * d] = -sig * w[:, p * d:(p + 1) * d]
+        np.testing.assert_allclose(oracle.out_projection(out, w),
+                                   oracle.out_projection(heads, w_base), rtol=1e-12, atol=1e-12)
+
+
+def test_output_projection_saving_matches_page_figures():
+    # count weights by building the projections as torch modules (independent of
+    # the oracle's arithmetic), then compare with the page's half and ~25 %
+    fig = GOLDEN["v2_output_projection_saving"]
+    for d_model, h, hkv, d in ((4096, 32, 8, 128), (4096, 32, 4, 128), (8192, 64, 8, 128)):
+        c = oracle.v2_attention_param_counts(d_model, h, hkv, d)
+        mods = {"q": torch.nn.Linear(d_model, 2 * h * d, bias=False, device="meta"),
+                "k": torch.nn.Linear(d_model, hkv * d, bias=False, device="meta"),
+                "v": torch.nn.Linear(d_model, hkv * d, bias=False, device="meta"),
+                "lam": torch.nn.Linear(d_model, h, bias=False, device="meta"),
+                "o_v2": torch.nn.Linear(h * d, d_model, bias=False, device="meta"),
+                "o_base": torch.nn.Linear(2 * h * d, d_model, bias=False, device="meta")}
+        n = {k: m.weight.numel() for k, m in mods.items()}
+        assert c["v2"] == n["q"] + n["k"] + n["v"] + n["lam"] + n["o_v2"]
+        assert c["base"] == n["q"] + n["k"] + n["v"] + n["o_base"]
+        assert c["o_v2"] / c["o_base"] == fig["o_projection_fraction_kept"]
+        # the query and output projections dominate when the KV heads are few
+        assert abs(c["o_saving_frac_of_base"] - fig["attention_params_saved_frac"]) <= fig["tolerance_abs"] + 2 * hkv / (4 * h)
+    small_kv = oracle.v2_attention_param_counts(4096, 32, 1, 128)
+    assert abs(small_kv["o_saving_frac_of_base"] - fig["attention_params_saved_frac"]) < fig["tolerance_abs"]
