@@ -13,12 +13,14 @@ V2 GQA causal prefill (B2, Hq64/Hkv8, T8192, d128), V2 packed varlen prefill
 d128, metric HBM GB/s), the V1 decode step (B32, 32768-entry cache, H12,
 d128/dv256, GB/s), the V2 backward on the prefill workload (2x the
 forward's FLOP: dP and dV are formed once per head pair) and the V1 backward
-on the headline workload.  Inputs are synthetic, seeded, already resident in HBM when
+on the headline workload, and the two projections either side of the V2
+attention on its tokens (coefficient logits, GB/s; output projection,
+TFLOP/s).  Inputs are synthetic, seeded, already resident in HBM when
 timing starts.  The fp64 CPU oracle is timed on a bounded sample of the
 headline workload on this host (``cpu_baseline``).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
-       [--no-cpu-baseline] [--only v1|v2|varlen|decode|v1dec|bwd|v1bwd]
+       [--no-cpu-baseline] [--only v1|v2|varlen|decode|v1dec|bwd|v1bwd|lproj|proj]
 """
 from __future__ import annotations
 
@@ -43,6 +45,8 @@ SOURCES = {
     "bwd": ("v2_backward.hip", "bwd_common.h", "device_common.h", "kernels.h"),
     "v1dec": ("v1_decode.hip", "device_common.h", "kernels.h"),
     "v1bwd": ("v1_backward.hip", "bwd_common.h", "device_common.h", "kernels.h"),
+    "proj": ("proj.hip", "device_common.h", "kernels.h"),
+    "lproj": ("proj.hip", "device_common.h", "kernels.h"),
 }
 
 
@@ -129,7 +133,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["v1", "v2", "varlen", "decode", "v1dec", "bwd", "v1bwd"],
+    ap.add_argument("--only", choices=["v1", "v2", "varlen", "decode", "v1dec", "bwd", "v1bwd",
+                                       "lproj", "proj"],
                     default=None)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -334,6 +339,38 @@ def main():
                                         "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flop": flop,
                                         "traffic": hbm_traffic("v1bwd", name)}
             del x, dy, o1, o2, lse, wsb
+            torch.cuda.empty_cache()
+        if args.only in (None, "lproj", "proj"):
+            w = inp.V2_PROJ
+            log(f"[bench] {w.name}")
+            x = inp.proj_inputs(w, device=dev)
+            if args.only in (None, "lproj"):
+                lg = torch.empty((w.N, w.h), dtype=torch.float32, device=dev)
+                f = lambda: da.v2_lambda_proj(x["x"], x["w_lambda"], out=lg)
+                for _ in range(args.warmup):
+                    f()
+                ms = time_calls(f, iters, stream)
+                byts = 2.0 * w.N * w.d_model + 2.0 * w.h * w.d_model + 4.0 * w.N * w.h
+                gbs = byts / (ms * 1e-3) / 1e9
+                name = w.name.replace("v2_proj", "v2_lambda_proj")
+                secondary["v2_lambda_proj"] = {"workload": name, "ms": round(ms, 4), "GB/s": round(gbs, 1),
+                                               "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": byts,
+                                               "traffic": hbm_traffic("lproj", name)}
+                del lg
+            if args.only in (None, "proj"):
+                y = torch.empty((w.N, w.d_model), dtype=torch.bfloat16, device=dev)
+                f = lambda: da.out_proj(x["attn_out"], x["w_o"], out=y)
+                for _ in range(args.warmup):
+                    f()
+                ms = time_calls(f, iters, stream)
+                flop = 2.0 * w.N * w.d_model * w.h * w.d
+                tf = flop / (ms * 1e-3) / 1e12
+                name = w.name.replace("v2_proj", "out_proj")
+                secondary["out_proj"] = {"workload": name, "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
+                                         "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flop": flop,
+                                         "traffic": hbm_traffic("proj", name)}
+                del y
+            del x
             torch.cuda.empty_cache()
     if secondary:
         result["secondary"] = secondary

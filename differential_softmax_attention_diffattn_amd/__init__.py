@@ -19,6 +19,10 @@ arithmetic runs in the library's kernels; there is no fallback path.
                 V1 training forward (also keeps per-map O and log-sum-exp) and
                 the backward through the norm: gradients of q1, k1, q2, k2, v,
                 lambda and the norm weight
+    v2_lambda_proj / out_proj
+                the projections either side of the V2 attention: coefficient
+                logits from the layer input, and the output projection of the
+                h*d columns left after the subtraction
     lambda_init 0.8 - 0.6 exp(-0.3 (l - 1))
 """
 from __future__ import annotations
@@ -35,6 +39,8 @@ __all__ = [
     "v2_bwd",
     "v1_fwd_train",
     "v1_bwd",
+    "v2_lambda_proj",
+    "out_proj",
     "lambda_init",
     "v1_workspace_bytes",
     "v2_decode_workspace_bytes",
@@ -463,4 +469,48 @@ def v1_decode(q1, q2, k1_cache, k2_cache, v_cache, lam: float, lambda_init: floa
             _ptr(weight), _ptr(out), _ptr(workspace), ws_bytes, B, S_max, H, d, dv, float(lam),
             float(lambda_init), float(eps), DIFFATTN_BF16, _stream(dev))
     _lib.check("diffattn_v1_decode", rc)
+    return out
+
+
+def v2_lambda_proj(x, w_lambda, out=None):
+    """Coefficient logits of V2: x [N, d_model] bf16, w_lambda [h, d_model] bf16 -> [N, h] fp32."""
+    torch = _torch()
+    dev = x.device
+    _check_tensor("x", x, dtype=torch.bfloat16, dim=2)
+    _check_tensor("w_lambda", w_lambda, dtype=torch.bfloat16, dim=2, device=dev)
+    N, dm = x.shape
+    h = w_lambda.shape[0]
+    if w_lambda.shape[1] != dm:
+        raise ValueError("w_lambda must be [h, d_model]")
+    if out is None:
+        out = torch.empty((N, h), dtype=torch.float32, device=dev)
+    _check_tensor("out", out, dtype=torch.float32, dim=2, device=dev)
+    if tuple(out.shape) != (N, h):
+        raise ValueError("out has the wrong shape")
+    with torch.cuda.device(dev):
+        rc = _lib.load().diffattn_v2_lambda_proj(_ptr(x), _ptr(w_lambda), _ptr(out), N, dm, h,
+                                                 DIFFATTN_BF16, _stream(dev))
+    _lib.check("diffattn_v2_lambda_proj", rc)
+    return out
+
+
+def out_proj(attn_out, w_o, out=None):
+    """Output projection: attn_out [M, K] bf16, w_o [N, K] bf16 -> [M, N] bf16 (fp32 accumulation)."""
+    torch = _torch()
+    dev = attn_out.device
+    _check_tensor("attn_out", attn_out, dtype=torch.bfloat16, dim=2)
+    _check_tensor("w_o", w_o, dtype=torch.bfloat16, dim=2, device=dev)
+    M, K = attn_out.shape
+    N = w_o.shape[0]
+    if w_o.shape[1] != K:
+        raise ValueError("w_o must be [N, K]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _check_tensor("out", out, dtype=torch.bfloat16, dim=2, device=dev)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out has the wrong shape")
+    with torch.cuda.device(dev):
+        rc = _lib.load().diffattn_out_proj(_ptr(attn_out), _ptr(w_o), _ptr(out), M, K, N,
+                                           DIFFATTN_BF16, _stream(dev))
+    _lib.check("diffattn_out_proj", rc)
     return out

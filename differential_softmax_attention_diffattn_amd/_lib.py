@@ -27,7 +27,7 @@ ERRORS = {
 }
 
 _c = ctypes
-_vp, _sz, _i, _f = _c.c_void_p, _c.c_size_t, _c.c_int, _c.c_float
+_vp, _sz, _i, _f, _ll = _c.c_void_p, _c.c_size_t, _c.c_int, _c.c_float, _c.c_longlong
 
 SIGNATURES = {
     "diffattn_v1_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _f, _i,
@@ -52,6 +52,8 @@ SIGNATURES = {
     "diffattn_v1_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _i,
                                 _i, _f, _f, _f, _i, _vp]),
     "diffattn_v1_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "diffattn_v2_lambda_proj": (_i, [_vp, _vp, _vp, _ll, _i, _i, _i, _vp]),
+    "diffattn_out_proj": (_i, [_vp, _vp, _vp, _ll, _ll, _ll, _i, _vp]),
     "diffattn_lambda_init": (_f, [_i]),
     "diffattn_last_error": (_c.c_char_p, []),
     "diffattn_version": (_i, []),

@@ -520,4 +520,49 @@ int diffattn_v2_decode(const void* q, const void* k_cache, const void* v_cache,
   return from_hip(diffattn::launch_v2_decode(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+int diffattn_v2_lambda_proj(const void* x, const void* w_lambda, float* logits, long long N,
+                            int d_model, int h, diffattn_dtype dtype, void* stream) {
+  const char* fn = "diffattn_v2_lambda_proj";
+  if (N < 0 || d_model <= 0 || h <= 0)
+    return fail(DIFFATTN_E_INVALID, "%s: bad sizes N=%lld d_model=%d h=%d", fn, N, d_model, h);
+  if (dtype != DIFFATTN_BF16)
+    return fail(dtype == DIFFATTN_F32 ? DIFFATTN_E_UNSUPPORTED : DIFFATTN_E_INVALID,
+                "%s: only bf16 is supported", fn);
+  if (h % 16 || h > 64)
+    return fail(DIFFATTN_E_UNSUPPORTED, "%s: h=%d must be 16, 32, 48 or 64", fn, h);
+  if (d_model % 256)
+    return fail(DIFFATTN_E_UNSUPPORTED, "%s: d_model=%d must be a multiple of 256", fn, d_model);
+  if (prod({N, d_model}) < 0 || prod({N, d_model}) > (1LL << 40))
+    return fail(DIFFATTN_E_INVALID, "%s: problem too large", fn);
+  if (N == 0) return ok();
+  if (!x || !w_lambda || !logits) return fail(DIFFATTN_E_INVALID, "%s: null tensor pointer", fn);
+  if (!aligned16(x) || !aligned16(w_lambda) || !aligned4(logits))
+    return fail(DIFFATTN_E_ALIGN, "%s: x and w_lambda must be 16-byte, logits 4-byte aligned", fn);
+  diffattn::LambdaProjArgs a{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_lambda),
+                             logits, N, d_model, h};
+  return from_hip(diffattn::launch_lambda_proj(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int diffattn_out_proj(const void* attn_out, const void* w_o, void* y, long long M, long long K,
+                      long long N, diffattn_dtype dtype, void* stream) {
+  const char* fn = "diffattn_out_proj";
+  if (M < 0 || K <= 0 || N <= 0)
+    return fail(DIFFATTN_E_INVALID, "%s: bad sizes M=%lld K=%lld N=%lld", fn, M, K, N);
+  if (dtype != DIFFATTN_BF16)
+    return fail(dtype == DIFFATTN_F32 ? DIFFATTN_E_UNSUPPORTED : DIFFATTN_E_INVALID,
+                "%s: only bf16 is supported", fn);
+  if (K % 64) return fail(DIFFATTN_E_UNSUPPORTED, "%s: K=%lld must be a multiple of 64", fn, K);
+  if (N % 4) return fail(DIFFATTN_E_UNSUPPORTED, "%s: N=%lld must be a multiple of 4", fn, N);
+  if (prod({M, K}) < 0 || prod({M, N}) < 0 || prod({N, K}) < 0 || prod({M, K}) > (1LL << 40) ||
+      prod({M, N}) > (1LL << 40) || K * 256 > 0xffffffffLL)
+    return fail(DIFFATTN_E_INVALID, "%s: problem too large", fn);
+  if (M == 0) return ok();
+  if (!attn_out || !w_o || !y) return fail(DIFFATTN_E_INVALID, "%s: null tensor pointer", fn);
+  if (!aligned16(attn_out) || !aligned16(w_o) || !aligned16(y))
+    return fail(DIFFATTN_E_ALIGN, "%s: tensor pointers must be 16-byte aligned", fn);
+  diffattn::GemmArgs a{static_cast<const uint16_t*>(attn_out), static_cast<const uint16_t*>(w_o),
+                       static_cast<uint16_t*>(y), M, N, K};
+  return from_hip(diffattn::launch_gemm_tn(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 }  // extern "C"

@@ -99,6 +99,23 @@ struct DecodeArgs {
   float scale;
 };
 
+// Coefficient logits of V2: logits[n, p] = sum_c x[n, c] w[p, c].
+struct LambdaProjArgs {
+  const uint16_t* x;  // bf16 [N, d_model]
+  const uint16_t* w;  // bf16 [h, d_model]
+  float* logits;      // fp32 [N, h]
+  long long N;
+  int d_model, h;     // d_model % 256 == 0, h in {16, 32, 48, 64}
+};
+
+// Output projection: y[m, n] = sum_k a[m, k] w[n, k], bf16 out.
+struct GemmArgs {
+  const uint16_t* a;  // bf16 [M, K]
+  const uint16_t* w;  // bf16 [N, K]
+  uint16_t* y;        // bf16 [M, N]
+  long long M, N, K;  // K % 64 == 0
+};
+
 struct V1DecodeArgs {
   const uint16_t* q1;        // bf16 [B, H, d]
   const uint16_t* q2;        // bf16 [B, H, d]
@@ -133,5 +150,7 @@ hipError_t launch_v2_prefill(const V2Args& a, hipStream_t stream);
 size_t v2_bwd_workspace_bytes(int B, int T, int Hq);
 hipError_t launch_v2_backward(const V2BwdArgs& a, hipStream_t stream);
 hipError_t launch_v2_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_lambda_proj(const LambdaProjArgs& a, hipStream_t stream);
+hipError_t launch_gemm_tn(const GemmArgs& a, hipStream_t stream);
 
 }  // namespace diffattn

@@ -259,6 +259,44 @@ def v2_inputs(w: V2Workload, device=None) -> dict:
     )
 
 
+@dataclass(frozen=True)
+class ProjWorkload:
+    """The projections either side of the V2 attention: N tokens, model width
+    d_model (= h * d, the baseline's attention width), h pairs, h * d columns
+    after the subtraction."""
+    name: str
+    N: int
+    d_model: int
+    h: int
+    d: int
+    seeds: tuple  # x, w_lambda, attn_out, w_o
+
+
+# the V2 prefill workload's tokens (B2 x T8192), 32 pairs of d = 128
+V2_PROJ = ProjWorkload(name="v2_proj_bf16_n16384_dmodel4096_h32_d128", N=16384, d_model=4096,
+                       h=32, d=128, seeds=(701, 702, 703, 704))
+
+
+def _rows(n_rows: int, n_cols: int, seed: int, std: float, device=None) -> torch.Tensor:
+    """[n_rows, n_cols] bf16 drawn in blocks of 256 rows (one derived seed per block)."""
+    nb = (n_rows + 255) // 256
+    t = normal((nb, 256, n_cols), seed, std, device=device)
+    return t.reshape(nb * 256, n_cols)[:n_rows].contiguous()
+
+
+def proj_inputs(w: ProjWorkload, device=None) -> dict:
+    """x [N, d_model] N(0,1); w_lambda [h, d_model] and w_o [d_model, h*d] N(0, 1/fan_in);
+    attn_out [N, h*d] N(0,1); all bf16."""
+    sx, sl, sa, so = w.seeds
+    hd = w.h * w.d
+    return dict(
+        x=_rows(w.N, w.d_model, sx, 1.0, device),
+        w_lambda=_rows(w.h, w.d_model, sl, 1.0 / math.sqrt(w.d_model), device),
+        attn_out=_rows(w.N, hd, sa, 1.0, device),
+        w_o=_rows(w.d_model, hd, so, 1.0 / math.sqrt(hd), device),
+    )
+
+
 DOUT_SEED = 305  # upstream gradient of the V2 backward workload (B2 T8192 Hq64 Hkv8 d128)
 
 

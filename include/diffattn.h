@@ -290,6 +290,43 @@ DIFFATTN_API int diffattn_v2_decode(const void* q, const void* k_cache, const vo
 /* Workspace bytes diffattn_v2_decode needs (0 for sizes it would reject). */
 DIFFATTN_API size_t diffattn_v2_decode_workspace_bytes(int B, int S_max, int Hq, int Hkv, int d);
 
+/*
+ * V2 coefficient logits [P2 §1]: the coefficient that scales the second
+ * head of each pair is projected from the layer input, one per token and
+ * pair, and passes through a sigmoid where it is used (diffattn_v2_fwd and
+ * diffattn_v2_decode apply it).  This computes the projection:
+ *
+ *   logits[n, p] = sum_c x[n, c] * w_lambda[p, c]     (fp32 accumulation)
+ *
+ *   x        : [N, d_model] bf16, the layer input (N tokens)
+ *   w_lambda : [h, d_model] bf16, one weight row per pair
+ *   logits   : [N, h] fp32 (written), the lambda_logit input of the V2 calls
+ *
+ * Supported: dtype DIFFATTN_BF16, h in {16, 32, 48, 64}, d_model a multiple of
+ * 256.  x and w_lambda 16-byte aligned, logits 4-byte aligned.  N = 0 is a
+ * no-op (pointers are then not read).
+ */
+DIFFATTN_API int diffattn_v2_lambda_proj(const void* x, const void* w_lambda, float* logits,
+                            long long N, int d_model, int h, diffattn_dtype dtype,
+                            void* stream);
+
+/*
+ * Output projection [P2 §1, §7]: after the subtraction each token carries
+ * h*d columns, so the projection back to d_model has the baseline's shape
+ * (half the input width of a 2h-head model with the same query heads):
+ *
+ *   y[m, n] = sum_k attn_out[m, k] * w_o[n, k]        (fp32 accumulation)
+ *
+ *   attn_out : [M, K] bf16 (e.g. the V2 output [tokens, h*d], or V1's z)
+ *   w_o      : [N, K] bf16, one weight row per output feature
+ *   y        : [M, N] bf16 (written)
+ *
+ * Supported: dtype DIFFATTN_BF16, K a multiple of 64 (and below 2^24), N a
+ * multiple of 4; all pointers 16-byte aligned.  M = 0 is a no-op.
+ */
+DIFFATTN_API int diffattn_out_proj(const void* attn_out, const void* w_o, void* y, long long M,
+                      long long K, long long N, diffattn_dtype dtype, void* stream);
+
 /* Initial lambda of 1-based layer `layer` [P1 "λ의 역할과 학습"]:
  * 0.8 - 0.6 * exp(-0.3 * (layer - 1)) in fp32.  Returns NaN (and sets the last
  * error) for layer < 1. */

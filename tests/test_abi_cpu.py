@@ -266,3 +266,33 @@ def test_v1_backward_workspace_query(lib):
         256 + 4 * 64 * 4 + 16 * 132 * 4)  # one wave per row of the 64 padded rows
     assert lib.diffattn_v1_bwd_workspace_bytes(1, 64, 1, 96, 192) == 0
     assert lib.diffattn_v1_bwd_workspace_bytes(0, 64, 1, 128, 256) == 0
+
+
+def test_lambda_proj_rejects_bad_arguments(lib):
+    f = lambda x=P, w=P, o=P, N=64, dm=4096, h=32, dt=BF16: lib.diffattn_v2_lambda_proj(
+        x, w, o, N, dm, h, dt, None)
+    assert f(N=-1) == E_INVALID
+    assert f(h=0) == E_INVALID
+    assert f(dt=F32) == E_UNSUPPORTED
+    assert f(dt=5) == E_INVALID
+    assert f(h=24) == E_UNSUPPORTED
+    assert f(h=80) == E_UNSUPPORTED
+    assert f(dm=4000) == E_UNSUPPORTED
+    assert f(x=None) == E_INVALID
+    assert f(w=P + 8) == E_ALIGN
+    assert f(o=P + 2) == E_ALIGN
+    assert f(N=0, x=None, w=None, o=None) == 0
+
+
+def test_out_proj_rejects_bad_arguments(lib):
+    f = lambda a=P, w=P, y=P, M=64, K=4096, N=4096, dt=BF16: lib.diffattn_out_proj(
+        a, w, y, M, K, N, dt, None)
+    assert f(M=-1) == E_INVALID
+    assert f(K=0) == E_INVALID
+    assert f(dt=F32) == E_UNSUPPORTED
+    assert f(K=100) == E_UNSUPPORTED
+    assert f(N=6) == E_UNSUPPORTED
+    assert f(K=1 << 25) == E_INVALID
+    assert f(y=None) == E_INVALID
+    assert f(a=P + 8) == E_ALIGN
+    assert f(M=0, a=None, w=None, y=None) == 0

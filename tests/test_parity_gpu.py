@@ -732,3 +732,63 @@ def test_v1_decode_full_workload_sampled_batches(gpu):
     got = out[sel].cpu().numpy()
     ratio = compare(got, ref, rms(x["v_cache"][:1]), TOL_BF16, REL_L2_BF16, what="v1 decode full")
     note(f"v1 decode full: error ratio {ratio:.3f}")
+
+
+# ---------------------------------------------------------------------------
+# Projections either side of the V2 attention.  Bounds from the arithmetic:
+# bf16 products are exact in fp32 and the fp32 sums of K terms err by at most
+# ~K 2^-24 sum|a w| (1e-5 sum|a w| leaves margin); the bf16 output of the
+# output projection adds half an ulp, 2^-9 |ref| (2^-8 with margin).
+# ---------------------------------------------------------------------------
+
+def check_proj(got, ref, absref, what, out_bf16=False):
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape and np.all(np.isfinite(got)), what
+    bound = 1e-5 * absref + (2.0 ** -8) * np.abs(ref) * out_bf16 + 1e-30
+    ratio = float(np.max(np.abs(got - ref) / bound))
+    note(f"{what}: max |err| / bound = {ratio:.3f}")
+    assert ratio <= 1.0, f"{what}: error exceeds the bound ({ratio:.3f}x)"
+
+
+@pytest.mark.parametrize("N,dm,h", [(1, 256, 16), (37, 256, 32), (100, 1024, 48), (1000, 512, 64),
+                                    (257, 4096, 32)])
+def test_lambda_proj_small(gpu, N, dm, h):
+    w = inp.V2_PROJ.__class__(name="t", N=N, d_model=dm, h=h, d=128, seeds=(711, 712, 713, 714))
+    x = inp.proj_inputs(w)
+    got = da.v2_lambda_proj(x["x"].to(gpu), x["w_lambda"].to(gpu))
+    torch.cuda.synchronize()
+    xf, wf = x["x"].double().numpy(), x["w_lambda"].double().numpy()
+    check_proj(got.cpu().numpy(), oracle.v2_lambda_logits(xf, wf), np.abs(xf) @ np.abs(wf).T,
+               f"lambda proj N={N} d_model={dm} h={h}")
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 64, 4), (100, 128, 100), (129, 1024, 128), (300, 512, 260),
+                                   (256, 4096, 256)])
+def test_out_proj_small(gpu, M, K, N):
+    g = torch.Generator().manual_seed(M * 131 + K * 7 + N)
+    a = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    wo = (torch.randn(N, K, generator=g) / math.sqrt(K)).to(torch.bfloat16)
+    got = da.out_proj(a.to(gpu), wo.to(gpu))
+    torch.cuda.synchronize()
+    af, wf = a.double().numpy(), wo.double().numpy()
+    check_proj(got.float().cpu().numpy(), oracle.out_projection(af, wf), np.abs(af) @ np.abs(wf).T,
+               f"out proj M={M} K={K} N={N}", out_bf16=True)
+
+
+def test_projections_full_workload_sampled(gpu):
+    # N16384 tokens, d_model 4096, h 32, h*d 4096, launched as the benchmark does;
+    # sampled token rows (all outputs of each) against the oracle
+    w = inp.V2_PROJ
+    x = inp.proj_inputs(w, device=gpu)
+    logits = da.v2_lambda_proj(x["x"], x["w_lambda"])
+    y = da.out_proj(x["attn_out"], x["w_o"])
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 5000, 8191, 8192, 16383])
+    xf = x["x"][rows].double().cpu().numpy()
+    wl = x["w_lambda"].double().cpu().numpy()
+    check_proj(logits[rows].cpu().numpy(), oracle.v2_lambda_logits(xf, wl), np.abs(xf) @ np.abs(wl).T,
+               "lambda proj full")
+    af = x["attn_out"][rows].double().cpu().numpy()
+    wo = x["w_o"].double().cpu().numpy()
+    check_proj(y[rows].float().cpu().numpy(), oracle.out_projection(af, wo), np.abs(af) @ np.abs(wo).T,
+               "out proj full", out_bf16=True)
