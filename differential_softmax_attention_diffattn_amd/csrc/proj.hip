@@ -99,27 +99,33 @@ __global__ __launch_bounds__(kProjWaves * kWave) void lambda_proj_kernel(LambdaP
 }
 
 // ---------------------------------------------------------------------------
-// Output projection: C[M, N] = A[M, K] * W[N, K]^T.  A workgroup of 4 waves
-// owns a 128 x 128 tile of C, a wave 64 x 64 (4 x 4 MFMA blocks); A and W
-// tiles of 128 rows x 64 k (16 KB each) go global -> LDS by direct loads,
+// Output projection: C[M, N] = A[M, K] * W[N, K]^T.  A workgroup of 8 waves
+// owns a 256 x 256 tile of C, a wave 128 x 64 (8 x 4 MFMA blocks); A and W
+// tiles of 256 rows x 64 k (32 KB each) go global -> LDS by direct loads,
 // double-buffered.  LDS rows are 128 bytes; the 16-byte chunk c of row r sits
 // at position c ^ ((r >> 1) & 7), so the 16 rows an MFMA operand read touches
 // (two rows per 256-byte bank window) land in 16 distinct bank groups.
+// Tiles are numbered so that each XCD (workgroups are dealt to the 8 XCDs
+// round-robin) works on a band of 8 row tiles across all column tiles: the
+// band's A rows and the W tiles are shared in that XCD's L2.
 // ---------------------------------------------------------------------------
-constexpr int kGemmTile = 128;
+constexpr int kGemmTile = 256;
 constexpr int kGemmK = 64;
-constexpr int kGemmWaves = 4;
+constexpr int kGemmWaves = 8;
 constexpr int kGemmTileBytes = kGemmTile * kGemmK * 2;
+constexpr int kGemmGroupM = 8;
+constexpr int kXcds = 8;
 
 __device__ __forceinline__ int gemm_lds_offset(int row, int chunk) {
   return row * (kGemmK * 2) + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
-// rows r0 .. r0+127 of a [rows, K] bf16 matrix (rows >= n_valid clamped), k
-// columns k0 .. k0+63, into the swizzled tile: 16 loads of 1 KiB, 4 per wave.
+// rows r0 .. r0+255 of a [rows, K] bf16 matrix (rows >= n_valid clamped), k
+// columns k0 .. k0+63, into the swizzled tile: 32 loads of 1 KiB, 4 per wave.
 __device__ __forceinline__ void gemm_load_tile(const uint16_t* base, long long K, long long r0,
                                                long long n_valid, int k0, uint8_t* lds, int wave,
                                                int lane) {
+  const long long rb = min(r0, n_valid - 1);  // wave-uniform base row
 #pragma unroll
   for (int j = 0; j < kGemmTileBytes / 1024 / kGemmWaves; ++j) {
     const int blk = wave + j * kGemmWaves;
@@ -127,13 +133,12 @@ __device__ __forceinline__ void gemm_load_tile(const uint16_t* base, long long K
     const int r = off >> 7;                  // 128-byte rows
     const int pos = (off & 127) >> 4;
     const int lc = pos ^ ((r >> 1) & 7);  // logical chunk stored at that position
-    const long long rb = min(r0, n_valid - 1);  // wave-uniform base row
     const long long row = min(r0 + r, n_valid - 1);
     dma16(base + rb * K + k0, (uint32_t)(((row - rb) * K + lc * 8) * 2), lds + blk * 1024);
   }
 }
 
-__global__ __launch_bounds__(kGemmWaves * kWave, 2) void gemm_tn_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kGemmWaves * kWave, 1) void gemm_tn_kernel(GemmArgs a) {
   __shared__ __align__(16) uint8_t sa0[kGemmTileBytes];
   __shared__ __align__(16) uint8_t sb0[kGemmTileBytes];
   __shared__ __align__(16) uint8_t sa1[kGemmTileBytes];
@@ -142,17 +147,26 @@ __global__ __launch_bounds__(kGemmWaves * kWave, 2) void gemm_tn_kernel(GemmArgs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int c16 = lane & 15;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int tiles_n = (a.N + kGemmTile - 1) / kGemmTile;
-  const int tm = blockIdx.x / tiles_n;
-  const int tn = blockIdx.x - tm * tiles_n;
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves of 128 x 64
+  const int tiles_m = (int)((a.M + kGemmTile - 1) / kGemmTile);
+  const int tiles_n = (int)((a.N + kGemmTile - 1) / kGemmTile);
+  const int ntiles = tiles_m * tiles_n;
+  // workgroup -> tile: consecutive tile numbers on one XCD, grouped by 8 row tiles
+  int pid = blockIdx.x;
+  if (ntiles % kXcds == 0) pid = (blockIdx.x % kXcds) * (ntiles / kXcds) + blockIdx.x / kXcds;
+  const int per_group = kGemmGroupM * tiles_n;
+  const int group = pid / per_group;
+  const int first_m = group * kGemmGroupM;
+  const int gm = min(tiles_m - first_m, kGemmGroupM);
+  const int tm = first_m + (pid % per_group) % gm;
+  const int tn = (pid % per_group) / gm;
   const long long m0 = (long long)tm * kGemmTile;
   const long long n0 = (long long)tn * kGemmTile;
-  const int nk = a.K / kGemmK;
+  const int nk = (int)(a.K / kGemmK);
 
-  f32x4 acc[4][4];
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -163,17 +177,17 @@ __global__ __launch_bounds__(kGemmWaves * kWave, 2) void gemm_tn_kernel(GemmArgs
   auto compute = [&](const uint8_t* la, const uint8_t* lb) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < kGemmK / 32; ++ks) {
-      u32x4 fa[4], fb[4];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        fa[mb] = *reinterpret_cast<const u32x4*>(la + gemm_lds_offset(wm * 64 + mb * 16 + c16, ks * 4 + g));
+      u32x4 fb[4];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
         fb[nb] = *reinterpret_cast<const u32x4*>(lb + gemm_lds_offset(wn * 64 + nb * 16 + c16, ks * 4 + g));
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 8; ++mb) {
+        const u32x4 fa =
+            *reinterpret_cast<const u32x4*>(la + gemm_lds_offset(wm * 128 + mb * 16 + c16, ks * 4 + g));
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma_bf16(fb[nb], fa[mb], acc[mb][nb]);
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma_bf16(fb[nb], fa, acc[mb][nb]);
+      }
     }
   };
 
@@ -197,8 +211,8 @@ __global__ __launch_bounds__(kGemmWaves * kWave, 2) void gemm_tn_kernel(GemmArgs
   // (of the wave's 64) for token 16 mb + c16; four consecutive features per lane
   // are stored as one 8-byte bf16 group
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const long long m = m0 + wm * 64 + mb * 16 + c16;
+  for (int mb = 0; mb < 8; ++mb) {
+    const long long m = m0 + wm * 128 + mb * 16 + c16;
     if (m >= a.M) continue;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
