@@ -20,7 +20,7 @@ timing starts.  The fp64 CPU oracle is timed on a bounded sample of the
 headline workload on this host (``cpu_baseline``).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
-       [--no-cpu-baseline] [--only v1|v2|varlen|decode|v1dec|bwd|v1bwd|lproj|proj]
+       [--no-cpu-baseline] [--only v1|v2|varlen|decode|v1dec|bwd|vbwd|v1bwd|lproj|proj]
 """
 from __future__ import annotations
 
@@ -46,6 +46,7 @@ SOURCES = {
     "v1dec": ("v1_decode.hip", "device_common.h", "kernels.h"),
     "v1bwd": ("v1_backward.hip", "bwd_common.h", "device_common.h", "kernels.h"),
     "proj": ("proj.hip", "device_common.h", "kernels.h"),
+    "vbwd": ("v2_backward.hip", "bwd_common.h", "device_common.h", "kernels.h"),
     "lproj": ("proj.hip", "device_common.h", "kernels.h"),
 }
 
@@ -133,8 +134,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["v1", "v2", "varlen", "decode", "v1dec", "bwd", "v1bwd",
-                                       "lproj", "proj"],
+    ap.add_argument("--only", choices=["v1", "v2", "varlen", "decode", "v1dec", "bwd", "vbwd",
+                                       "v1bwd", "lproj", "proj"],
                     default=None)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -312,6 +313,31 @@ def main():
             secondary["v2_backward"] = {"workload": name, "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
                                         "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flop": flop,
                                         "traffic": hbm_traffic("bwd", name)}
+            del x, dout, oh, lse, wsb
+            torch.cuda.empty_cache()
+        if args.only in (None, "vbwd"):
+            # V2 backward of the packed prefill workload (65536 tokens, 8 sequences)
+            w = inp.V2_VARLEN
+            name = w.name.replace("v2_varlen", "v2_varlen_backward")
+            log(f"[bench] {name}")
+            x = inp.v2_inputs(w, device=dev)
+            dout = inp.v2_varlen_dout(w, device=dev)
+            mx = max(w.lengths)
+            _, oh, lse = da.v2_varlen_fwd_train(x["q"], x["k"], x["v"], x["logit"], x["cu_seqlens"], mx)
+            N = sum(w.lengths)
+            wsb = torch.empty(da._lib.load().diffattn_v2_varlen_bwd_workspace_bytes(
+                N, len(w.lengths), w.Hq, w.Hkv, w.d), dtype=torch.uint8, device=dev)
+            f = lambda: da.v2_varlen_bwd(x["q"], x["k"], x["v"], x["logit"], x["cu_seqlens"], oh, lse,
+                                         dout, workspace=wsb)
+            for _ in range(args.warmup):
+                f()
+            ms = time_calls(f, iters, stream)
+            flop = sum(v2_bwd_flops_seq(n, w.Hq, w.d) for n in w.lengths)
+            tf = flop / (ms * 1e-3) / 1e12
+            secondary["v2_varlen_backward"] = {"workload": name, "ms": round(ms, 4),
+                                               "TFLOP/s": round(tf, 2),
+                                               "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                                               "flop": flop, "traffic": hbm_traffic("vbwd", name)}
             del x, dout, oh, lse, wsb
             torch.cuda.empty_cache()
         if args.only in (None, "v1bwd"):

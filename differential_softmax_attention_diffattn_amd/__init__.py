@@ -15,6 +15,8 @@ arithmetic runs in the library's kernels; there is no fallback path.
     v2_fwd_train / v2_bwd
                 V2 training forward (also keeps per-head O and log-sum-exp) and
                 the backward: gradients of q, k, v and the lambda logits
+    v2_varlen_fwd_train / v2_varlen_bwd
+                the same for packed (varlen) batches
     v1_fwd_train / v1_bwd
                 V1 training forward (also keeps per-map O and log-sum-exp) and
                 the backward through the norm: gradients of q1, k1, q2, k2, v,
@@ -39,6 +41,8 @@ __all__ = [
     "v2_bwd",
     "v1_fwd_train",
     "v1_bwd",
+    "v2_varlen_fwd_train",
+    "v2_varlen_bwd",
     "v2_lambda_proj",
     "out_proj",
     "lambda_init",
@@ -417,6 +421,82 @@ def v2_bwd(q, k, v, logit, o_heads, lse, dout, causal: bool = True, scale: float
             _ptr(dk), _ptr(dv), _ptr(dlogit), _ptr(workspace), ws_bytes, B, T, Hq, Hkv, d,
             float(scale or 0.0), 1 if causal else 0, DIFFATTN_BF16, _stream(dev))
     _lib.check("diffattn_v2_bwd", rc)
+    return dq, dk, dv, dlogit
+
+
+def _v2_packed_check(q, k, v, logit, cu_seqlens):
+    torch = _torch()
+    dev = q.device
+    _check_tensor("q", q, dtype=torch.bfloat16, dim=3)
+    _check_tensor("k", k, dtype=torch.bfloat16, dim=3, device=dev)
+    _check_tensor("v", v, dtype=torch.bfloat16, dim=3, device=dev)
+    _check_tensor("logit", logit, dtype=torch.float32, dim=2, device=dev)
+    _check_tensor("cu_seqlens", cu_seqlens, dtype=torch.int32, dim=1, device=dev)
+    N, Hq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != N or k.shape[2] != d:
+        raise ValueError("k/v shape does not match q")
+    if Hq % 2 or tuple(logit.shape) != (N, Hq // 2):
+        raise ValueError(f"logit must have shape {(N, Hq // 2)} and Hq must be even")
+    return N, Hq, k.shape[1], d, cu_seqlens.shape[0] - 1
+
+
+def v2_varlen_fwd_train(q, k, v, logit, cu_seqlens, max_seqlen: int, causal: bool = True,
+                        scale: float | None = None):
+    """DIFF V2 training forward of a packed batch.
+
+    q [N,Hq,d], k/v [N,Hkv,d] bf16, logit [N,Hq/2] fp32, cu_seqlens int32 [nseq+1] ->
+    (out [N,Hq/2,d] bf16, o_heads [N,Hq,d] bf16, lse [N,Hq] fp32).
+    """
+    torch = _torch()
+    dev = q.device
+    N, Hq, Hkv, d, nseq = _v2_packed_check(q, k, v, logit, cu_seqlens)
+    out = torch.empty((N, Hq // 2, d), dtype=torch.bfloat16, device=dev)
+    o_heads = torch.empty((N, Hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((N, Hq), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        rc = _lib.load().diffattn_v2_varlen_fwd_train(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(logit), _ptr(cu_seqlens), nseq, int(max_seqlen),
+            _ptr(out), _ptr(o_heads), _ptr(lse), Hq, Hkv, d, float(scale or 0.0),
+            1 if causal else 0, DIFFATTN_BF16, _stream(dev))
+    _lib.check("diffattn_v2_varlen_fwd_train", rc)
+    return out, o_heads, lse
+
+
+def v2_varlen_bwd(q, k, v, logit, cu_seqlens, o_heads, lse, dout, causal: bool = True,
+                  scale: float | None = None, workspace=None):
+    """DIFF V2 backward of a packed batch: gradients of sum(dout * out).
+
+    o_heads, lse from v2_varlen_fwd_train; dout [N,Hq/2,d] bf16 ->
+    (dq [N,Hq,d], dk [N,Hkv,d], dv [N,Hkv,d], dlogit [N,Hq/2]), all fp32.
+    """
+    torch = _torch()
+    dev = q.device
+    N, Hq, Hkv, d, nseq = _v2_packed_check(q, k, v, logit, cu_seqlens)
+    _check_tensor("o_heads", o_heads, dtype=torch.bfloat16, dim=3, device=dev)
+    _check_tensor("lse", lse, dtype=torch.float32, dim=2, device=dev)
+    _check_tensor("dout", dout, dtype=torch.bfloat16, dim=3, device=dev)
+    if tuple(o_heads.shape) != (N, Hq, d) or tuple(lse.shape) != (N, Hq):
+        raise ValueError("o_heads / lse shapes do not match q")
+    if tuple(dout.shape) != (N, Hq // 2, d):
+        raise ValueError("dout must have shape [N, Hq/2, d]")
+    dq = torch.empty((N, Hq, d), dtype=torch.float32, device=dev)
+    dk = torch.empty((N, Hkv, d), dtype=torch.float32, device=dev)
+    dv = torch.empty((N, Hkv, d), dtype=torch.float32, device=dev)
+    dlogit = torch.empty((N, Hq // 2), dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    need = int(lib.diffattn_v2_varlen_bwd_workspace_bytes(N, nseq, Hq, Hkv, d))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _check_tensor("workspace", workspace, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        rc = lib.diffattn_v2_varlen_bwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(logit), _ptr(cu_seqlens), nseq, _ptr(o_heads),
+            _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dlogit), _ptr(workspace),
+            ws_bytes, N, Hq, Hkv, d, float(scale or 0.0), 1 if causal else 0, DIFFATTN_BF16,
+            _stream(dev))
+    _lib.check("diffattn_v2_varlen_bwd", rc)
     return dq, dk, dv, dlogit
 
 

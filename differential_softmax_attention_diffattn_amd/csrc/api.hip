@@ -388,6 +388,108 @@ int diffattn_v2_bwd(const void* q, const void* k, const void* v, const float* la
   a.d = d;
   a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
   a.causal = causal;
+  a.cu_seqlens = nullptr;
+  a.nseq = B;
+  a.N = (long long)B * T;
+  a.Np = diffattn::v2_bwd_rows(B, T);
+  return from_hip(diffattn::launch_v2_backward(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int diffattn_v2_varlen_fwd_train(const void* q, const void* k, const void* v,
+                                 const float* lambda_logit, const int* cu_seqlens, int nseq,
+                                 int max_seqlen, void* out, void* o_heads, float* lse, int Hq,
+                                 int Hkv, int d, float scale, int causal, diffattn_dtype dtype,
+                                 void* stream) {
+  const char* fn = "diffattn_v2_varlen_fwd_train";
+  if (!q || !k || !v || !lambda_logit || !out || !o_heads || !lse || !cu_seqlens)
+    return fail(DIFFATTN_E_INVALID, "%s: null tensor pointer", fn);
+  const int rc = v2_heads_check(fn, Hq, Hkv, d, scale, causal, dtype);
+  if (rc != DIFFATTN_OK) return rc;
+  if (nseq < 0 || max_seqlen < 0)
+    return fail(DIFFATTN_E_INVALID, "%s: nseq=%d max_seqlen=%d must be >= 0", fn, nseq, max_seqlen);
+  const void* ptrs[] = {q, k, v, out, o_heads};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(DIFFATTN_E_ALIGN, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (!aligned4(lambda_logit) || !aligned4(lse) || !aligned4(cu_seqlens))
+    return fail(DIFFATTN_E_ALIGN, "%s: lambda_logit, lse and cu_seqlens must be 4-byte aligned", fn);
+  if (nseq == 0 || max_seqlen == 0) return ok();
+  diffattn::V2Args a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.logit = lambda_logit;
+  a.out = static_cast<uint16_t*>(out);
+  a.cu_seqlens = cu_seqlens;
+  a.nseq = nseq;
+  a.max_seqlen = max_seqlen;
+  a.T = 0;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+  a.causal = causal;
+  a.o_heads = static_cast<uint16_t*>(o_heads);
+  a.lse = lse;
+  return from_hip(diffattn::launch_v2_prefill(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+size_t diffattn_v2_varlen_bwd_workspace_bytes(long long N, int nseq, int Hq, int Hkv, int d) {
+  if (N < 0 || nseq < 0 || Hq <= 0 || Hkv <= 0 || Hq % 2 || Hq % Hkv || (Hq / Hkv) % 2) return 0;
+  if (d != 64 && d != 128) return 0;
+  if (prod({N, Hq, d}) < 0 || prod({N, Hq, d}) > (1LL << 40)) return 0;
+  if (N == 0 || nseq == 0) return 0;
+  return diffattn::v2_bwd_workspace_bytes_rows(diffattn::v2_bwd_varlen_rows(N, nseq), Hq);
+}
+
+int diffattn_v2_varlen_bwd(const void* q, const void* k, const void* v, const float* lambda_logit,
+                           const int* cu_seqlens, int nseq, const void* o_heads, const float* lse,
+                           const void* dout, float* dq, float* dk, float* dv,
+                           float* dlambda_logit, void* workspace, size_t workspace_bytes,
+                           long long N, int Hq, int Hkv, int d, float scale, int causal,
+                           diffattn_dtype dtype, void* stream) {
+  const char* fn = "diffattn_v2_varlen_bwd";
+  const int rc = v2_heads_check(fn, Hq, Hkv, d, scale, causal, dtype);
+  if (rc != DIFFATTN_OK) return rc;
+  if (N < 0 || nseq < 0) return fail(DIFFATTN_E_INVALID, "%s: N=%lld nseq=%d must be >= 0", fn, N, nseq);
+  if (prod({N, Hq, d}) > (1LL << 40)) return fail(DIFFATTN_E_INVALID, "%s: problem too large", fn);
+  if (N == 0 || nseq == 0) return ok();
+  if (!q || !k || !v || !lambda_logit || !cu_seqlens || !o_heads || !lse || !dout || !dq || !dk ||
+      !dv || !dlambda_logit)
+    return fail(DIFFATTN_E_INVALID, "%s: null tensor pointer", fn);
+  const void* ptrs[] = {q, k, v, o_heads, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(DIFFATTN_E_ALIGN, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (!aligned4(lambda_logit) || !aligned4(lse) || !aligned4(dlambda_logit) || !aligned4(cu_seqlens))
+    return fail(DIFFATTN_E_ALIGN, "%s: lambda_logit, lse, dlambda_logit and cu_seqlens must be 4-byte aligned", fn);
+  const size_t need = diffattn_v2_varlen_bwd_workspace_bytes(N, nseq, Hq, Hkv, d);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DIFFATTN_E_WORKSPACE, "%s: workspace of %zu bytes required (got %zu%s)", fn, need,
+                workspace_bytes, workspace ? "" : ", NULL");
+  if (!aligned16(workspace)) return fail(DIFFATTN_E_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  diffattn::V2BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.logit = lambda_logit;
+  a.o_heads = static_cast<const uint16_t*>(o_heads);
+  a.lse = lse;
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dlogit = dlambda_logit;
+  a.delta = static_cast<float*>(workspace);
+  a.B = 0;
+  a.T = 0;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
+  a.causal = causal;
+  a.cu_seqlens = cu_seqlens;
+  a.nseq = nseq;
+  a.N = N;
+  a.Np = diffattn::v2_bwd_varlen_rows(N, nseq);
   return from_hip(diffattn::launch_v2_backward(a, static_cast<hipStream_t>(stream)), fn);
 }
 

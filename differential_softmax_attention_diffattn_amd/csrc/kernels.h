@@ -80,10 +80,16 @@ struct V2BwdArgs {
   float* dk;                // fp32 [B, T, Hkv, d]
   float* dv;                // fp32 [B, T, Hkv, d]
   float* dlogit;            // fp32 [B, T, Hq/2]
-  float* delta;             // fp32 workspace [B, T, Hq]: rowsum(dO_j o O_j)
+  float* delta;             // fp32 workspace: per-row values, [head][Np] (see v2_backward.hip)
   int B, T, Hq, Hkv, d;
   float scale;
   int causal;
+  // packed (varlen) batches: tensors are [N, ...] and sequence s owns tokens
+  // cu_seqlens[s] .. cu_seqlens[s+1]-1; nullptr for padded batches (B x T)
+  const int* cu_seqlens;
+  int nseq;
+  long long N;   // packed tokens (varlen)
+  long long Np;  // rows per head in the workspace
 };
 
 struct DecodeArgs {
@@ -148,6 +154,11 @@ hipError_t launch_v1_backward(const V1BwdArgs& a, hipStream_t stream);
 hipError_t launch_v2_prefill(const V2Args& a, hipStream_t stream);
 // V2 backward workspace: per-row delta, log2 lse and sigmoid (see v2_backward.hip).
 size_t v2_bwd_workspace_bytes(int B, int T, int Hq);
+// Rows per head of that workspace: B * T rounded up per sequence to 64, or for
+// packed batches the bound N + 64 * nseq (each sequence padded to 64 rows).
+long long v2_bwd_rows(int B, int T);
+long long v2_bwd_varlen_rows(long long N, int nseq);
+size_t v2_bwd_workspace_bytes_rows(long long Np, int Hq);
 hipError_t launch_v2_backward(const V2BwdArgs& a, hipStream_t stream);
 hipError_t launch_v2_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_lambda_proj(const LambdaProjArgs& a, hipStream_t stream);

@@ -1,5 +1,5 @@
-// DIFF V2 backward on gfx950 (padded batches): gradients of sum(dout * out) of
-// the V2 forward
+// DIFF V2 backward on gfx950 (padded and packed/varlen batches): gradients of
+// sum(dout * out) of the V2 forward
 //     O_j[t]   = softmax_k(q_{t,j} . k_{k,kv(j)} * scale) v_{k,kv(j)}    (causal: k <= t)
 //     out[t,p] = O_2p[t] - sigmoid(logit[t,p]) * O_2p+1[t]
 // ("Differential Transformer V2" summary (pogovet.com), 상세 정리 §1 and §4).
@@ -14,8 +14,9 @@
 //
 // Three kernels:
 //  * v2_bwd_pre_kernel: per (token, pair) D_2p, D_2p+1, s, dlogit, and the
-//    log-sum-exp in log2 units, stored [B][head][T rounded up to 64] so that a
-//    query tile's row values are contiguous;
+//    log-sum-exp in log2 units, stored [head][Np]: every sequence's rows start
+//    at a multiple of 64 and are padded to one (zeros), so a query tile's row
+//    values are one contiguous 256-byte run;
 //  * v2_bwd_dq_kernel: the forward's decomposition (a wave owns one pair and
 //    16 query rows, lanes own query columns; K and V tiles stream through LDS):
 //    S^T = K Q^T, dP^T = V dout^T, dS^T, dQ^T += K^T dS^T;
@@ -51,34 +52,78 @@ struct BoolTag {
   static constexpr bool value = B;
 };
 
+// One sequence of the batch: its first token, length and first workspace row.
+struct SeqView {
+  long long tok0;
+  int L;
+  long long ws0;
+};
+
+__host__ __device__ __forceinline__ long long pad64(long long x) { return (x + 63) / 64 * 64; }
+
+// Tile t (of `rows`-row tiles, numbered sequence by sequence, a sequence's
+// tiles consecutive) -> its sequence and the tile's index inside it.  Returns
+// false past the last tile.  Padded batches divide; packed ones scan
+// cu_seqlens (as the forward does).
+__device__ __forceinline__ bool tile_of(const V2BwdArgs& a, long long t, int rows, SeqView& sv,
+                                        int& tile) {
+  if (a.cu_seqlens == nullptr) {
+    const int nt = (a.T + rows - 1) / rows;
+    const long long b = t / nt;
+    if (b >= a.B) return false;
+    tile = (int)(t - b * nt);
+    sv.tok0 = b * a.T;
+    sv.L = a.T;
+    sv.ws0 = b * pad64(a.T);
+    return true;
+  }
+  long long ws = 0;
+  for (int s = 0; s < a.nseq; ++s) {
+    const int c0 = a.cu_seqlens[s];
+    const int len = a.cu_seqlens[s + 1] - c0;
+    const int nt = (len + rows - 1) / rows;
+    if (t < nt) {
+      tile = (int)t;
+      sv.tok0 = c0;
+      sv.L = len;
+      sv.ws0 = ws;
+      return true;
+    }
+    t -= nt;
+    ws += pad64(len);
+  }
+  return false;
+}
+
 // ---------------------------------------------------------------------------
-// Preprocessing: one wave per (token, pair).
+// Preprocessing: one wave per (workspace row, pair).
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void v2_bwd_pre_kernel(V2BwdArgs a, int Tp, float* lse2,
-                                                         float* sig) {
+__global__ __launch_bounds__(256) void v2_bwd_pre_kernel(V2BwdArgs a, float* lse2, float* sig) {
   const int h = a.Hq / 2;
   const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const long long n_items = (long long)a.B * Tp * h;
-  if (item >= n_items) return;
+  const long long Np = a.Np;
+  if (item >= Np * h) return;
   const int p = (int)(item % h);
-  const long long bt = item / h;
-  const int t = (int)(bt % Tp);
-  const int b = (int)(bt / Tp);
-  const size_t ws = ((size_t)b * a.Hq + 2 * p) * Tp + t;  // [b][2p][t]
-  const size_t wsig = ((size_t)b * h + p) * Tp + t;
-  if (t >= a.T) {  // padding rows: finite zeros (the tiles read them and mask them)
+  const long long prow = item / h;  // workspace row: 64-row tile prow / 64
+  SeqView sv;
+  int tile;
+  if (!tile_of(a, prow / 64, 64, sv, tile)) return;  // rows past the last sequence: unused
+  const int t = tile * 64 + (int)(prow % 64);
+  const size_t ws = (size_t)(2 * p) * Np + sv.ws0 + t;  // [2p][row]
+  const size_t wsig = (size_t)p * Np + sv.ws0 + t;
+  if (t >= sv.L) {  // padding rows: finite zeros (the tiles read them and mask them)
     if (lane == 0) {
       a.delta[ws] = 0.f;
-      a.delta[ws + Tp] = 0.f;
+      a.delta[ws + Np] = 0.f;
       lse2[ws] = 0.f;
-      lse2[ws + Tp] = 0.f;
+      lse2[ws + Np] = 0.f;
       sig[wsig] = 0.f;
     }
     return;
   }
-  const size_t tok = (size_t)b * a.T + t;
+  const size_t tok = (size_t)(sv.tok0 + t);
   constexpr int E = D / 64;  // elements per lane
   float de = 0.f, dod = 0.f;
 #pragma unroll
@@ -96,10 +141,10 @@ __global__ __launch_bounds__(256) void v2_bwd_pre_kernel(V2BwdArgs a, int Tp, fl
   if (lane == 0) {
     const float s = sigmoid_f32(a.logit[tok * h + p]);
     a.delta[ws] = de;             // <dO_2p, O_2p> with dO_2p = dout_p
-    a.delta[ws + Tp] = -s * dod;  // <dO_2p+1, O_2p+1> with dO_2p+1 = -s dout_p
+    a.delta[ws + Np] = -s * dod;  // <dO_2p+1, O_2p+1> with dO_2p+1 = -s dout_p
     a.dlogit[tok * h + p] = -s * (1.f - s) * dod;
     lse2[ws] = a.lse[tok * a.Hq + 2 * p] * kLog2e;
-    lse2[ws + Tp] = a.lse[tok * a.Hq + 2 * p + 1] * kLog2e;
+    lse2[ws + Np] = a.lse[tok * a.Hq + 2 * p + 1] * kLog2e;
     sig[wsig] = s;
   }
 }
@@ -109,8 +154,7 @@ __global__ __launch_bounds__(256) void v2_bwd_pre_kernel(V2BwdArgs a, int Tp, fl
 // through LDS (K in the transposing layout: it is read both ways).
 // ---------------------------------------------------------------------------
 template <int D, int PW, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, int Tp,
-                                                                const float* lse2,
+__global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, const float* lse2,
                                                                 const float* sig) {
   using TL = BTile<D>;
   constexpr int QSUB = kWaves / PW;
@@ -129,11 +173,12 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, int
 
   const int n_hg = a.Hq / (2 * PW);
   const int hg = blockIdx.x % n_hg;
-  const int t = blockIdx.x / n_hg;
-  const int nt = (a.T + QTILE - 1) / QTILE;
-  const int b = t / nt;
-  const int qt = nt - 1 - (t - b * nt);  // longest first
-  const int T = a.T;
+  SeqView sv;
+  int qt;
+  if (!tile_of(a, blockIdx.x / n_hg, QTILE, sv, qt)) return;  // uniform over the block
+  qt = (sv.L + QTILE - 1) / QTILE - 1 - qt;  // a sequence's longest (last) tile first
+  const int T = sv.L;
+  const long long Np = a.Np;
   const int hpairs = a.Hq / 2;
   const int group = a.Hq / a.Hkv;
   const int p = hg * PW + (wave % PW);
@@ -147,7 +192,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, int
   const float cs = a.scale * kLog2e;
   const int row = q_lo + c16;  // this lane's query column
   const int rowc = min(row, T - 1);
-  const size_t tok = (size_t)b * T + rowc;
+  const size_t tok = (size_t)(sv.tok0 + rowc);
   // B operands: Q^T of both heads and dout^T of the pair
   u32x4 qf[2][NC], of[NC];
 #pragma unroll
@@ -160,15 +205,15 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, int
   float l2[2], dl[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const size_t w = ((size_t)b * a.Hq + 2 * p + nb) * Tp + rowc;
+    const size_t w = (size_t)(2 * p + nb) * Np + sv.ws0 + rowc;
     l2[nb] = lse2[w];
     dl[nb] = a.delta[w];
   }
-  const float sg = sig[((size_t)b * hpairs + p) * Tp + rowc];
+  const float sg = sig[(size_t)p * Np + sv.ws0 + rowc];
 
   const size_t kv_stride = (size_t)a.Hkv * D;
-  const uint16_t* kbase_g = a.k + ((size_t)b * T * a.Hkv + kv) * D;
-  const uint16_t* vbase_g = a.v + ((size_t)b * T * a.Hkv + kv) * D;
+  const uint16_t* kbase_g = a.k + ((size_t)sv.tok0 * a.Hkv + kv) * D;
+  const uint16_t* vbase_g = a.v + ((size_t)sv.tok0 * a.Hkv + kv) * D;
   auto load_k = [&](int kt, uint8_t* kl) {
     const int r0 = kt * kKeys;
     load_tile<D, true>(kbase_g + (size_t)r0 * kv_stride, kv_stride, T - r0, kl, wave, lane);
@@ -296,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, int
   if (!wave_active || row >= T) return;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    float* dst = a.dq + (((size_t)b * T + row) * a.Hq + 2 * p + nb) * D + g * 4;
+    float* dst = a.dq + (((size_t)sv.tok0 + row) * a.Hq + 2 * p + nb) * D + g * 4;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       f32x4 r;
@@ -317,8 +362,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, int
 constexpr int kDkvKeys = kWaves * 16;
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, int Tp,
-                                                                  const float* lse2,
+__global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, const float* lse2,
                                                                   const float* sig) {
   using TL = BTile<D>;
   constexpr int NC = D / 32;
@@ -335,14 +379,26 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
   const int g = lane >> 4;
   const int c16 = lane & 15;
 
-  const int T = a.T;
+  // blocks: padded batches take the key tiles with the most query tiles first,
+  // then (batch, KV head); packed batches go sequence by sequence
+  SeqView sv;
+  int kt, kvh;
+  if (a.cu_seqlens == nullptr) {
+    const int nbg = a.B * a.Hkv;
+    kt = blockIdx.x / nbg;
+    const int bg = blockIdx.x - kt * nbg;
+    const int b = bg / a.Hkv;
+    kvh = bg - b * a.Hkv;
+    sv.tok0 = (long long)b * a.T;
+    sv.L = a.T;
+    sv.ws0 = (long long)b * pad64(a.T);
+  } else {
+    kvh = blockIdx.x % a.Hkv;
+    if (!tile_of(a, blockIdx.x / a.Hkv, kDkvKeys, sv, kt)) return;  // uniform over the block
+  }
+  const int T = sv.L;
+  const long long Np = a.Np;
   const int n_qt = (T + kQRows - 1) / kQRows;
-  // blocks: key tiles with the most query tiles first, then (batch, KV head)
-  const int nbg = a.B * a.Hkv;
-  const int kt = blockIdx.x / nbg;
-  const int bg = blockIdx.x - kt * nbg;
-  const int b = bg / a.Hkv;
-  const int kvh = bg - b * a.Hkv;
   const int group = a.Hq / a.Hkv;
   const int npairs = group / 2;
   const int hpairs = a.Hq / 2;
@@ -356,7 +412,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
   // this wave's 16 keys: K^T and V^T B operands (lane column = key)
   const int key = key0 + wave * 16 + c16;
   const int keyc = min(key, T - 1);
-  const size_t kvrow = ((size_t)b * T + keyc) * a.Hkv + kvh;
+  const size_t kvrow = ((size_t)sv.tok0 + keyc) * a.Hkv + kvh;
   u32x4 kf[NC], vf[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -374,20 +430,20 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
     const int je = kvh * group + 2 * pp;  // even head of the pair
     const int pair = je / 2;
     const size_t q_stride = (size_t)a.Hq * D;
-    const uint16_t* qe = a.q + (((size_t)b * T + r0) * a.Hq + je) * D;
+    const uint16_t* qe = a.q + (((size_t)sv.tok0 + r0) * a.Hq + je) * D;
     load_tile<D, true>(qe, q_stride, T - r0, st, wave, lane);
     load_tile<D, true>(qe + D, q_stride, T - r0, st + TL::kBytes, wave, lane);
-    const uint16_t* dsrc = a.dout + (((size_t)b * T + r0) * hpairs + pair) * D;
+    const uint16_t* dsrc = a.dout + (((size_t)sv.tok0 + r0) * hpairs + pair) * D;
     load_tile<D, true>(dsrc, (size_t)hpairs * D, T - r0, st + 2 * TL::kBytes, wave, lane);
     // row vectors (64 floats each, padded rows included): 5 x 256 bytes
     if (wave < 5 && lane < 16) {
       const float* src;
       if (wave < 2)
-        src = lse2 + ((size_t)b * a.Hq + je + wave) * Tp + r0;
+        src = lse2 + (size_t)(je + wave) * Np + sv.ws0 + r0;
       else if (wave < 4)
-        src = a.delta + ((size_t)b * a.Hq + je + wave - 2) * Tp + r0;
+        src = a.delta + (size_t)(je + wave - 2) * Np + sv.ws0 + r0;
       else
-        src = sig + ((size_t)b * hpairs + pair) * Tp + r0;
+        src = sig + (size_t)pair * Np + sv.ws0 + r0;
       dma16(src, (uint32_t)(lane * 16), st + 3 * TL::kBytes + wave * 256);
     }
   };
@@ -519,7 +575,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
     for (int i = 0; i < 4; ++i) {
       const int kk = key0 + wave * 16 + 4 * g + i;
       if (kk < T) {
-        const size_t o = (((size_t)b * T + kk) * a.Hkv + kvh) * D + db * 16 + c16;
+        const size_t o = (((size_t)sv.tok0 + kk) * a.Hkv + kvh) * D + db * 16 + c16;
         a.dk[o] = dk[db][i] * a.scale;
         a.dv[o] = dv[db][i];
       }
@@ -528,35 +584,41 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, i
 
 template <int D>
 hipError_t launch_d(const V2BwdArgs& a, hipStream_t stream) {
-  const int Tp = (a.T + 63) / 64 * 64;
-  float* lse2 = a.delta + (size_t)a.B * a.Hq * Tp;
-  float* sig = lse2 + (size_t)a.B * a.Hq * Tp;
-  const long long pre_items = (long long)a.B * Tp * (a.Hq / 2);
+  const long long Np = a.Np;
+  float* lse2 = a.delta + (size_t)a.Hq * Np;
+  float* sig = lse2 + (size_t)a.Hq * Np;
+  const long long pre_items = Np * (a.Hq / 2);
   const long long pre_blocks = (pre_items + 3) / 4;
   if (pre_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((v2_bwd_pre_kernel<D>), dim3((unsigned)pre_blocks), dim3(256), 0, stream, a,
-                     Tp, lse2, sig);
+                     lse2, sig);
   const int pairs_per_group = (a.Hq / a.Hkv) / 2;
   const int PW = pairs_per_group % 4 == 0 ? 4 : pairs_per_group % 2 == 0 ? 2 : 1;
   const int qtile = kRows * (kWaves / PW);
-  const long long dq_blocks = (long long)((a.T + qtile - 1) / qtile) * a.B * (a.Hq / (2 * PW));
-  const long long kv_blocks = (long long)((a.T + kDkvKeys - 1) / kDkvKeys) * a.B * a.Hkv;
+  // tiles over all sequences: padded B * ceil(T / tile); packed at most
+  // ceil(N / tile) + nseq (blocks past the last tile exit)
+  auto tiles = [&](int rows) -> long long {
+    if (a.cu_seqlens == nullptr) return (long long)((a.T + rows - 1) / rows) * a.B;
+    return (a.N + rows - 1) / rows + a.nseq;
+  };
+  const long long dq_blocks = tiles(qtile) * (a.Hq / (2 * PW));
+  const long long kv_blocks = tiles(kDkvKeys) * a.Hkv;
   if (dq_blocks > 0x7fffffffLL || kv_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
 #define DQ(PWV, C)                                                                               \
   hipLaunchKernelGGL((v2_bwd_dq_kernel<D, PWV, C>), dim3((unsigned)dq_blocks), dim3(kThreads), 0, \
-                     stream, a, Tp, (const float*)lse2, (const float*)sig)
+                     stream, a, (const float*)lse2, (const float*)sig)
   if (a.causal) {
     if (PW == 4) DQ(4, true);
     else if (PW == 2) DQ(2, true);
     else DQ(1, true);
     hipLaunchKernelGGL((v2_bwd_dkdv_kernel<D, true>), dim3((unsigned)kv_blocks), dim3(kThreads), 0,
-                       stream, a, Tp, (const float*)lse2, (const float*)sig);
+                       stream, a, (const float*)lse2, (const float*)sig);
   } else {
     if (PW == 4) DQ(4, false);
     else if (PW == 2) DQ(2, false);
     else DQ(1, false);
     hipLaunchKernelGGL((v2_bwd_dkdv_kernel<D, false>), dim3((unsigned)kv_blocks), dim3(kThreads),
-                       0, stream, a, Tp, (const float*)lse2, (const float*)sig);
+                       0, stream, a, (const float*)lse2, (const float*)sig);
   }
 #undef DQ
   return hipGetLastError();
@@ -564,10 +626,17 @@ hipError_t launch_d(const V2BwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+long long v2_bwd_rows(int B, int T) { return (long long)B * pad64(T); }
+
+long long v2_bwd_varlen_rows(long long N, int nseq) { return pad64(N) + 64LL * nseq; }
+
+size_t v2_bwd_workspace_bytes_rows(long long Np, int Hq) {
+  // delta and lse2 [Hq][Np], sigmoid [Hq/2][Np], fp32
+  return ((size_t)Hq * Np * 2 + (size_t)(Hq / 2) * Np) * sizeof(float);
+}
+
 size_t v2_bwd_workspace_bytes(int B, int T, int Hq) {
-  const size_t Tp = (size_t)(T + 63) / 64 * 64;
-  // delta and lse2 [B][Hq][Tp], sigmoid [B][Hq/2][Tp], fp32
-  return ((size_t)B * Hq * Tp * 2 + (size_t)B * (Hq / 2) * Tp) * sizeof(float);
+  return v2_bwd_workspace_bytes_rows(v2_bwd_rows(B, T), Hq);
 }
 
 hipError_t launch_v2_backward(const V2BwdArgs& a, hipStream_t stream) {

@@ -300,6 +300,15 @@ def proj_inputs(w: ProjWorkload, device=None) -> dict:
 DOUT_SEED = 305  # upstream gradient of the V2 backward workload (B2 T8192 Hq64 Hkv8 d128)
 
 
+def v2_varlen_dout(w: V2Workload, seed: int = DOUT_SEED, device=None) -> torch.Tensor:
+    """Upstream gradient [N,Hq/2,d] bf16 of a packed batch, iid N(0,1), drawn in
+    blocks of 1024 tokens like the packed inputs."""
+    total = int(sum(w.lengths))
+    nb = (total + 1023) // 1024
+    t = normal((nb, 1024, w.Hq // 2, w.d), seed, 1.0, device=device)
+    return t.reshape(nb * 1024, w.Hq // 2, w.d)[:total].contiguous()
+
+
 def v2_dout(w: V2Workload, seed: int = DOUT_SEED, device=None) -> torch.Tensor:
     """Upstream gradient dL/dout [B,T,Hq/2,d] bf16, iid N(0,1) (padded batches)."""
     return normal((w.B, w.T, w.Hq // 2, w.d), seed, 1.0, device=device)

@@ -235,6 +235,37 @@ DIFFATTN_API int diffattn_v2_bwd(const void* q, const void* k, const void* v,
 DIFFATTN_API size_t diffattn_v2_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int d);
 
 /*
+ * V2 training forward and backward of packed (varlen) batches: as
+ * diffattn_v2_fwd_train and diffattn_v2_bwd, with the tensors packed [N, ...]
+ * and sequence s owning tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 (attention
+ * never crosses a sequence), as in diffattn_v2_fwd's packed form.
+ *
+ *   cu_seqlens : device int32 [nseq + 1], cu_seqlens[0] = 0, non-decreasing,
+ *                cu_seqlens[nseq] = N (not checked: it lives on the device);
+ *                every token's gradients are written once by its sequence
+ *   max_seqlen : the longest sequence (forward only; an upper bound is fine)
+ *   q, o_heads, dq : [N, Hq, d];  k, v, dk, dv : [N, Hkv, d];
+ *   lambda_logit, dlambda_logit : [N, Hq/2];  lse : [N, Hq];  out, dout : [N, Hq/2, d]
+ *   workspace  : at least diffattn_v2_varlen_bwd_workspace_bytes(N, nseq, ...)
+ *                bytes (per-row values of every sequence padded to 64 rows).
+ * Supported shapes and dtypes as for the padded calls.  N = 0 or nseq = 0 is
+ * a no-op.
+ */
+DIFFATTN_API int diffattn_v2_varlen_fwd_train(const void* q, const void* k, const void* v,
+                                 const float* lambda_logit, const int* cu_seqlens, int nseq,
+                                 int max_seqlen, void* out, void* o_heads, float* lse, int Hq,
+                                 int Hkv, int d, float scale, int causal, diffattn_dtype dtype,
+                                 void* stream);
+DIFFATTN_API int diffattn_v2_varlen_bwd(const void* q, const void* k, const void* v,
+                           const float* lambda_logit, const int* cu_seqlens, int nseq,
+                           const void* o_heads, const float* lse, const void* dout, float* dq,
+                           float* dk, float* dv, float* dlambda_logit, void* workspace,
+                           size_t workspace_bytes, long long N, int Hq, int Hkv, int d,
+                           float scale, int causal, diffattn_dtype dtype, void* stream);
+DIFFATTN_API size_t diffattn_v2_varlen_bwd_workspace_bytes(long long N, int nseq, int Hq, int Hkv,
+                                              int d);
+
+/*
  * V1 decode step [P1 "Differential Attention: 빼기의 힘"; norm and factor: P2
  * §1]: one new query row per (batch entry, head) against the cached K1, K2
  * and V.  The cache already holds the new token; entry b attends to positions

@@ -296,3 +296,46 @@ def test_out_proj_rejects_bad_arguments(lib):
     assert f(y=None) == E_INVALID
     assert f(a=P + 8) == E_ALIGN
     assert f(M=0, a=None, w=None, y=None) == 0
+
+
+def vbwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, lg=P, cu=P, nseq=2, oh=P, lse=P, dout=P, dq=P, dk=P, dv=P, dlg=P, ws=P,
+             wsb=1 << 30, N=100, Hq=16, Hkv=2, d=128, scale=0.0, causal=1, dt=BF16, stream=None)
+    a.update(kw)
+    return lib.diffattn_v2_varlen_bwd(a["q"], a["k"], a["v"], a["lg"], a["cu"], a["nseq"], a["oh"],
+                                      a["lse"], a["dout"], a["dq"], a["dk"], a["dv"], a["dlg"],
+                                      a["ws"], a["wsb"], a["N"], a["Hq"], a["Hkv"], a["d"],
+                                      a["scale"], a["causal"], a["dt"], a["stream"])
+
+
+def test_v2_varlen_backward_rejects_bad_arguments(lib):
+    assert vbwd(lib, cu=None) == E_INVALID
+    assert vbwd(lib, dq=None) == E_INVALID
+    assert vbwd(lib, N=-1) == E_INVALID
+    assert vbwd(lib, Hq=6, Hkv=2) == E_INVALID
+    assert vbwd(lib, d=96) == E_UNSUPPORTED
+    assert vbwd(lib, cu=P + 2) == E_ALIGN
+    assert vbwd(lib, dk=P + 4) == E_ALIGN
+    assert vbwd(lib, ws=None) == E_WORKSPACE
+    assert vbwd(lib, wsb=128) == E_WORKSPACE
+    assert vbwd(lib, N=0) == 0
+    assert vbwd(lib, nseq=0) == 0
+
+
+def test_v2_varlen_backward_workspace_query(lib):
+    # per-row values of every sequence padded to 64 rows: rows <= N rounded up + 64 per sequence
+    Np = (65536 + 63) // 64 * 64 + 64 * 8
+    assert lib.diffattn_v2_varlen_bwd_workspace_bytes(65536, 8, 64, 8, 128) == 4 * Np * (64 * 2 + 32)
+    assert lib.diffattn_v2_varlen_bwd_workspace_bytes(100, 3, 16, 2, 128) == 4 * (128 + 192) * (16 * 2 + 8)
+    assert lib.diffattn_v2_varlen_bwd_workspace_bytes(100, 3, 16, 2, 96) == 0
+    assert lib.diffattn_v2_varlen_bwd_workspace_bytes(0, 3, 16, 2, 128) == 0
+
+
+def test_v2_varlen_train_forward_rejects_bad_arguments(lib):
+    f = lambda **kw: lib.diffattn_v2_varlen_fwd_train(*[{**dict(q=P, k=P, v=P, lg=P, cu=P, nseq=2, ms=64, out=P, oh=P, lse=P, Hq=16, Hkv=2, d=128, scale=0.0, causal=1, dt=BF16, st=None), **kw}[n] for n in ("q", "k", "v", "lg", "cu", "nseq", "ms", "out", "oh", "lse", "Hq", "Hkv", "d", "scale", "causal", "dt", "st")])
+    assert f(cu=None) == E_INVALID
+    assert f(oh=None) == E_INVALID
+    assert f(nseq=-1) == E_INVALID
+    assert f(Hq=6) == E_INVALID
+    assert f(oh=P + 8) == E_ALIGN
+    assert f(nseq=0) == 0

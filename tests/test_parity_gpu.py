@@ -463,6 +463,67 @@ def test_v2_backward_full_workload_sampled(gpu):
 
 
 
+def run_varlen_train(x, dout, causal=True):
+    mx = int((x["cu_seqlens"][1:] - x["cu_seqlens"][:-1]).max().item())
+    out, oh, lse = da.v2_varlen_fwd_train(x["q"], x["k"], x["v"], x["logit"], x["cu_seqlens"], mx,
+                                          causal=causal)
+    grads = da.v2_varlen_bwd(x["q"], x["k"], x["v"], x["logit"], x["cu_seqlens"], oh, lse, dout,
+                             causal=causal)
+    torch.cuda.synchronize()
+    return out, grads
+
+
+@pytest.mark.parametrize("lengths,Hq,Hkv,d,causal", [
+    ((37, 64, 1, 130), 16, 2, 128, True), ((200, 0, 65, 5), 8, 2, 128, False),
+    ((97, 128, 31), 16, 4, 64, True), ((129,), 8, 1, 128, True)])
+def test_v2_varlen_backward_small_all_elements(gpu, lengths, Hq, Hkv, d, causal):
+    w = inp.V2_VARLEN.with_shape(Hq=Hq, Hkv=Hkv, d=d, lengths=lengths, causal=causal)
+    x = inp.v2_inputs(w)
+    dout = inp.v2_varlen_dout(w)
+    out, grads = run_varlen_train(cuda(x, gpu), dout.to(gpu), causal)
+    # the training forward's output is the inference forward's
+    ref_out = da.v2_fwd(*(t.to(gpu) for t in (x["q"], x["k"], x["v"], x["logit"])),
+                        cu_seqlens=x["cu_seqlens"].to(gpu), max_seqlen=max(lengths), causal=causal)
+    assert torch.equal(out, ref_out)
+    cu = [int(c) for c in x["cu_seqlens"].tolist()]
+    refs = [np.zeros(g.shape) for g in grads]
+    for s in range(len(lengths)):
+        a, e = cu[s], cu[s + 1]
+        if e == a:
+            continue
+        r = oracle.v2_sequence_backward(x["q"][a:e], x["k"][a:e], x["v"][a:e], x["logit"][a:e],
+                                        dout[a:e], causal=causal)
+        for i in range(4):
+            refs[i][a:e] = r[i]
+    for name, g, r in zip(("dq", "dk", "dv", "dlogit"), grads, refs):
+        compare_grad(g.cpu().numpy(), r, f"v2 varlen bwd {name} lengths={lengths} causal={causal}")
+
+
+def test_v2_varlen_backward_full_workload_sampled(gpu):
+    # the packed prefill workload (65536 tokens, 8 sequences), launched as the
+    # benchmark launches the forward; dq and dlogit on sampled rows of three
+    # sequences against the row-restricted oracle, and the key gradients' zero
+    # sum per sequence and KV head
+    w = inp.V2_VARLEN
+    x = inp.v2_inputs(w)
+    dout = inp.v2_varlen_dout(w)
+    note("v2 varlen bwd full workload: launching")
+    _, (dq, dk, dv, dlogit) = run_varlen_train(cuda(x, gpu), dout.to(gpu))
+    cu = [int(c) for c in x["cu_seqlens"].tolist()]
+    for s in (0, 3, 7):
+        a, e = cu[s], cu[s + 1]
+        rows = np.unique(np.array([0, 1, 63, 64, (e - a) // 2, e - a - 2, e - a - 1]).clip(0, e - a - 1))
+        rq, rl = oracle.v2_backward_query_rows(x["q"][a:e], x["k"][a:e], x["v"][a:e], x["logit"][a:e],
+                                               dout[a:e], rows)
+        compare_grad(dq[a + rows].cpu().numpy(), rq, f"v2 varlen bwd full dq seq={s}")
+        compare_grad(dlogit[a + rows].cpu().numpy(), rl, f"v2 varlen bwd full dlogit seq={s}")
+        ksum = dk[a:e].double().sum(dim=0)
+        rel = float((ksum.abs() / dk[a:e].double().abs().sum(dim=0)).max())
+        note(f"v2 varlen bwd full dk zero-sum seq={s}: {rel:.3e}")
+        assert rel <= 1e-2
+    assert torch.isfinite(dv).all()
+
+
 # ---------------------------------------------------------------------------
 # V1 training forward and backward (same gradient bounds as V2; dz and the
 # per-map P and dS enter the products rounded to bf16)
