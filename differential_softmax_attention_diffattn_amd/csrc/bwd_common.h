@@ -33,6 +33,19 @@ __device__ __forceinline__ int trans_offset(int row, int byte_in_row) {
   return row * BTile<D>::kRowBytes + ((c32 ^ (row & (n32 - 1))) << 5) + (byte_in_row & 31);
 }
 
+// The same offsets as one base per (row, byte) XORed with the chunk index:
+// trans_offset<D>(row, 32 c + b) == trans_base<D>(row, b) ^ (c << 5) and
+// rows_offset<D>(row, c) == rows_base<D>(row) ^ (c << 4) (the row's bits sit
+// above the chunk bits), so a loop over chunks costs one XOR per read.
+template <int D>
+__device__ __forceinline__ int trans_base(int row, int byte_in_chunk) {
+  return row * BTile<D>::kRowBytes | ((row & (D / 16 - 1)) << 5) | byte_in_chunk;
+}
+template <int D>
+__device__ __forceinline__ int rows_base(int row) {
+  return row * BTile<D>::kRowBytes | ((row & (BTile<D>::kChunks - 1)) << 4);
+}
+
 // Direct-to-LDS load of a ROWS-row tile: rows r0 .. r0+ROWS-1 of a bf16 matrix
 // whose consecutive rows are `stride` elements apart, rows >= n_valid clamped
 // to the last valid row (their values are masked by the caller).  TRANS

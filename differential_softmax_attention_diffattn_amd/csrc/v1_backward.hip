@@ -39,7 +39,9 @@ namespace {
 
 using bwd::BTile;
 using bwd::load_tile;
+using bwd::rows_base;
 using bwd::rows_offset;
+using bwd::trans_base;
 using bwd::trans_offset;
 
 constexpr int kKeys = 64;     // keys per staged tile (dq)
@@ -263,27 +265,35 @@ __global__ __launch_bounds__(kDqWaves * kWave, 1) void v1_bwd_dq_kernel(V1BwdArg
   auto step = [&](auto masked, const uint8_t* l1, const uint8_t* l2, const uint8_t* lv, int cc,
                   int k0) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
-    // the lane's rows, made opaque here so that the swizzled offsets derived
-    // from them are formed next to their use instead of being kept live
-    int rr = c16, tk = tr_key;
-    asm volatile("" : "+v"(rr), "+v"(tk));
+    // the lane's swizzled row bases, made opaque here so that the offsets
+    // derived from them (one XOR each) are formed next to their use instead of
+    // being kept live across the loop.  K A reads: 32-byte chunk 2c + (g >> 1),
+    // byte 16 (g & 1); V A reads: 16-byte chunk 4c + g (the row layout's
+    // swizzle class changes with the 16-key block, hence two bases).
+    int bk = trans_base<D>(c16, (g & 1) * 16) ^ ((g >> 1) << 5);
+    int bv0 = rows_base<DV>(c16) ^ (g << 4);
+    int bv1 = rows_base<DV>(16 + c16) ^ (g << 4);
+    int tk = trans_base<D>(tr_key, tr_byte);
+    asm volatile("" : "+v"(bk), "+v"(bv0), "+v"(bv1), "+v"(tk));
     f32x4 s1[2], s2[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s1[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
       s2[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
       dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int key = cc * 32 + kb * 16 + rr;
+      const int rk = (cc * 32 + kb * 16) * TK::kRowBytes;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const int off = trans_offset<D>(key, (c * 4 + g) * 16);
+        const int off = (bk ^ (c << 6)) + rk;
         s1[kb] = mfma_bf16(*reinterpret_cast<const u32x4*>(l1 + off), q1f[c], s1[kb]);
         s2[kb] = mfma_bf16(*reinterpret_cast<const u32x4*>(l2 + off), q2f[c], s2[kb]);
       }
+      const int bv = kb ? bv1 : bv0;
 #pragma unroll
       for (int c = 0; c < NCV; ++c)
-        dp[kb] = mfma_bf16(*reinterpret_cast<const u32x4*>(lv + rows_offset<DV>(key, c * 4 + g)),
-                           dzf[c], dp[kb]);
+        dp[kb] = mfma_bf16(
+            *reinterpret_cast<const u32x4*>(lv + (bv ^ (c << 6)) + cc * 32 * TV::kRowBytes),
+            dzf[c], dp[kb]);
     }
     float x1[8], x2[8];
 #pragma unroll
@@ -304,8 +314,9 @@ __global__ __launch_bounds__(kDqWaves * kWave, 1) void v1_bwd_dq_kernel(V1BwdArg
     const u32x4 ds1 = pack8(x1), ds2 = pack8(x2);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int off0 = trans_offset<D>(cc * 32 + tk, db * 32 + tr_byte);
-      const int off1 = trans_offset<D>(cc * 32 + tk + 16, db * 32 + tr_byte);
+      // rows tr_key and tr_key + 16 share a swizzle class: the second read is +16 rows
+      const int off0 = (tk ^ (db << 5)) + cc * 32 * TK::kRowBytes;
+      const int off1 = off0 + 16 * TK::kRowBytes;
       const u32x2 a1 = lds_read_tr16(l1 + off0), b1 = lds_read_tr16(l1 + off1);
       const u32x2 a2 = lds_read_tr16(l2 + off0), b2 = lds_read_tr16(l2 + off1);
       dq1[db] = mfma_bf16(u32x4{a1[0], a1[1], b1[0], b1[1]}, ds1, dq1[db]);
@@ -474,27 +485,31 @@ __global__ __launch_bounds__(kKvWaves8 * kWave) void v1_bwd_dkdv_kernel(V1BwdArg
     const uint8_t* q2l = st + kQB;
     const uint8_t* zl = st + 2 * kQB;
     const float* vec = reinterpret_cast<const float*>(st + 2 * kQB + kZB);
-    // the lane's rows, made opaque here so that the swizzled offsets derived
-    // from them are formed next to their use instead of being kept live
-    // across the loop (dozens of registers)
-    int rr = c16, tr = tr_row, vr = vrow;
-    asm volatile("" : "+v"(rr), "+v"(tr), "+v"(vr));
+    // the lane's swizzled row bases, made opaque here so that the offsets
+    // derived from them (one XOR each) are formed next to their use instead of
+    // being kept live across the loop (dozens of registers).  S and dP A reads:
+    // 32-byte chunk 2c + (g >> 1), byte 16 (g & 1); V reads: 16-byte chunk 4c + g.
+    int bq = trans_base<D>(c16, (g & 1) * 16) ^ ((g >> 1) << 5);
+    int bz = trans_base<DV>(c16, (g & 1) * 16) ^ ((g >> 1) << 5);
+    int bv = rows_base<DV>(vrow) ^ (g << 4);
+    int tz = trans_base<DV>(tr_row, tr_byte);
+    int tk = trans_base<D>(tr_row, tr_byte);
+    asm volatile("" : "+v"(bq), "+v"(bz), "+v"(bv), "+v"(tz), "+v"(tk));
     float pc[2][4], x1[2][4], x2[2][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {  // 16-row blocks of the tile
       f32x4 s1 = f32x4{0.f, 0.f, 0.f, 0.f}, s2 = s1, dp = s1;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const int off = trans_offset<D>(j * 16 + rr, (c * 4 + g) * 16);
+        const int off = (bq ^ (c << 6)) + j * 16 * TK::kRowBytes;
         s1 = mfma_bf16(*reinterpret_cast<const u32x4*>(q1l + off), k1f[c], s1);
         s2 = mfma_bf16(*reinterpret_cast<const u32x4*>(q2l + off), k2f[c], s2);
       }
 #pragma unroll
       for (int c = 0; c < NCV; ++c) {
-        const u32x4 vb = *reinterpret_cast<const u32x4*>(vtile + rows_offset<DV>(vr, c * 4 + g));
+        const u32x4 vb = *reinterpret_cast<const u32x4*>(vtile + (bv ^ (c << 6)));
         dp = mfma_bf16(
-            *reinterpret_cast<const u32x4*>(zl + trans_offset<DV>(j * 16 + rr, (c * 4 + g) * 16)),
-            vb, dp);
+            *reinterpret_cast<const u32x4*>(zl + (bz ^ (c << 6)) + j * 16 * TV::kRowBytes), vb, dp);
       }
       const f32x4 l1 = *reinterpret_cast<const f32x4*>(vec + j * 16 + 4 * g);
       const f32x4 l2 = *reinterpret_cast<const f32x4*>(vec + kKvRows + j * 16 + 4 * g);
@@ -525,14 +540,16 @@ __global__ __launch_bounds__(kKvWaves8 * kWave) void v1_bwd_dkdv_kernel(V1BwdArg
     const u32x4 pa = pack(pc), sa1 = pack(x1), sa2 = pack(x2);
 #pragma unroll
     for (int db = 0; db < NDBV; ++db) {
-      const u32x2 lo = lds_read_tr16(zl + trans_offset<DV>(tr, db * 32 + tr_byte));
-      const u32x2 hi = lds_read_tr16(zl + trans_offset<DV>(tr + 16, db * 32 + tr_byte));
+      // rows tr_row and tr_row + 16 share a swizzle class: the second read is +16 rows
+      const int off = tz ^ (db << 5);
+      const u32x2 lo = lds_read_tr16(zl + off);
+      const u32x2 hi = lds_read_tr16(zl + off + 16 * TV::kRowBytes);
       dvv[db] = mfma_bf16(pa, u32x4{lo[0], lo[1], hi[0], hi[1]}, dvv[db]);
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int off0 = trans_offset<D>(tr, db * 32 + tr_byte);
-      const int off1 = trans_offset<D>(tr + 16, db * 32 + tr_byte);
+      const int off0 = tk ^ (db << 5);
+      const int off1 = off0 + 16 * TK::kRowBytes;
       const u32x2 a1 = lds_read_tr16(q1l + off0), b1 = lds_read_tr16(q1l + off1);
       const u32x2 a2 = lds_read_tr16(q2l + off0), b2 = lds_read_tr16(q2l + off1);
       dk1[db] = mfma_bf16(sa1, u32x4{a1[0], a1[1], b1[0], b1[1]}, dk1[db]);

@@ -38,7 +38,9 @@ namespace {
 
 using bwd::BTile;
 using bwd::load_tile;
+using bwd::rows_base;
 using bwd::rows_offset;
+using bwd::trans_base;
 using bwd::trans_offset;
 
 constexpr int kWaves = 8;
@@ -238,6 +240,13 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, con
   auto step = [&](auto masked, const uint8_t* kl, const uint8_t* vl, int cc, int k0)
                   __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
+    // the lane's swizzled row bases (see the dK/dV kernel): K A reads at
+    // 32-byte chunk 2c + (g >> 1), V A reads at 16-byte chunk 4c + g,
+    // transposing K reads at row tr_key
+    int bk = trans_base<D>(c16, (g & 1) * 16) ^ ((g >> 1) << 5);
+    int bv = rows_base<D>(c16) ^ (g << 4);
+    int bt = trans_base<D>(tr_key, tr_byte);
+    asm volatile("" : "+v"(bk), "+v"(bv), "+v"(bt));
     f32x4 sacc[2][2], dpa[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -249,9 +258,10 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, con
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int key = cc * 32 + kb * 16 + c16;
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(kl + trans_offset<D>(key, (c * 4 + g) * 16));
-        const u32x4 vf = *reinterpret_cast<const u32x4*>(vl + rows_offset<D>(key, c * 4 + g));
+        // rows cc 32 + kb 16 + c16: the same swizzle class as c16 in both layouts (D >= 64)
+        const int rk = (cc * 32 + kb * 16) * TL::kRowBytes;
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(kl + (bk ^ (c << 6)) + rk);
+        const u32x4 vf = *reinterpret_cast<const u32x4*>(vl + (bv ^ (c << 6)) + rk);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = mfma_bf16(kf, qf[nb][c], sacc[kb][nb]);
         dpa[kb] = mfma_bf16(vf, of[c], dpa[kb]);
@@ -276,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, con
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const uint8_t* kp = kl + trans_offset<D>(cc * 32 + tr_key, db * 32 + tr_byte);
+      const uint8_t* kp = kl + (bt ^ (db << 5)) + cc * 32 * TL::kRowBytes;
       const u32x2 lo = lds_read_tr16(kp);
       const u32x2 hi = lds_read_tr16(kp + 16 * TL::kRowBytes);
       const u32x4 kt_f = u32x4{lo[0], lo[1], hi[0], hi[1]};
@@ -467,6 +477,12 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
     const uint8_t* qlo = st + TL::kBytes;
     const uint8_t* dl = st + 2 * TL::kBytes;
     const float* vec = reinterpret_cast<const float*>(st + 3 * TL::kBytes);
+    // the lane's swizzled row bases, opaque here so that the offsets derived
+    // from them (one XOR each) are formed next to their use: A reads at 32-byte
+    // chunk 2c + (g >> 1), byte 16 (g & 1); transposing reads at row tr_row
+    int ba = trans_base<D>(c16, (g & 1) * 16) ^ ((g >> 1) << 5);
+    int bt = trans_base<D>(tr_row, tr_byte);
+    asm volatile("" : "+v"(ba), "+v"(bt));
     // S_e, S_o = Q K^T and dP = dout V^T: 4 query blocks x this wave's 16 keys
     f32x4 se[4], so[4], dpa[4];
 #pragma unroll
@@ -476,7 +492,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
       dpa[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const int off = trans_offset<D>(qb * 16 + c16, (c * 4 + g) * 16);
+        const int off = (ba ^ (c << 6)) + qb * 16 * TL::kRowBytes;
         const u32x4 qa = *reinterpret_cast<const u32x4*>(qle + off);
         const u32x4 qb_ = *reinterpret_cast<const u32x4*>(qlo + off);
         const u32x4 da = *reinterpret_cast<const u32x4*>(dl + off);
@@ -524,7 +540,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
       const u32x4 sao = pack8(dso, s);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int off = trans_offset<D>(s * 32 + tr_row, db * 32 + tr_byte);
+        const int off = (bt ^ (db << 5)) + s * 32 * TL::kRowBytes;
         const u32x2 dlo_ = lds_read_tr16(dl + off);
         const u32x2 dhi_ = lds_read_tr16(dl + off + 16 * TL::kRowBytes);
         const u32x2 elo = lds_read_tr16(qle + off);
