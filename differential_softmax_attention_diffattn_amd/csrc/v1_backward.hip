@@ -45,7 +45,6 @@ using bwd::trans_base;
 using bwd::trans_offset;
 
 constexpr int kKeys = 64;     // keys per staged tile (dq)
-constexpr int kQRows = 64;    // query rows per staged tile (dkdv)
 constexpr int kRows = 16;     // query rows per wave (dq)
 constexpr int kDqWaves = 8;   // dq: 128 query rows per workgroup
 constexpr int kPreBlocks = 1024;
