@@ -618,6 +618,25 @@ def test_v1_backward_small_all_elements(gpu, B, T, H, d, dv, causal, layer, weig
     check_v1_grads(grads, refs, what, terms, end_to_end=True)
 
 
+@pytest.mark.parametrize("lam,li", [(1.3, 0.5), (-0.5, 0.3)])
+def test_v1_backward_lambda_outside_init_range(gpu, lam, li):
+    # the API takes any finite lambda (the pages allow lambda > 1); lambda and
+    # lambda_init are independent arguments
+    w = inp.V1_BF16.with_shape(B=1, T=150, H=2, d=64, dv=128, std=0.5)
+    x = inp.v1_inputs(w)
+    dy = inp.v1_dy(w)
+    xg = cuda(x, gpu)
+    refs = oracle.v1_backward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, li, w.eps, dy)
+    o1, o2, lse, O1, O2 = v1_oracle_state(x)
+    grads = da.v1_bwd(xg["q1"], xg["k1"], xg["q2"], xg["k2"], xg["v"], o1.to(gpu), o2.to(gpu),
+                      lse.to(gpu), dy.to(gpu), lam, li, w.eps)
+    torch.cuda.synchronize()
+    terms = dlambda_terms(O1, O2, dy.numpy(), lam, li, w.eps)
+    check_v1_grads(grads, refs, f"v1 bwd lambda={lam} li={li} [oracle state]", terms)
+    *_, grads = run_v1_train(xg, dy.to(gpu), lam, li, w.eps)
+    check_v1_grads(grads, refs, f"v1 bwd lambda={lam} li={li}", terms, end_to_end=True)
+
+
 def test_v1_backward_grid_stride_rows(gpu):
     # more rows than the preprocessing grid has waves, so its loop and the
     # fixed-order partial sums of dlambda and dweight run as at full size
