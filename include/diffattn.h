@@ -1,12 +1,14 @@
 /*
  * diffattn.h -- C ABI of the MI355X (gfx950) differential-attention library.
  *
- * The library computes differential attention (the forward pass, and the V2
- * backward for training) as described on two web pages:
+ * The library computes differential attention -- prefill and decode forward
+ * passes, the training backward of V1 (through its norm) and V2, and the two
+ * projections on either side of the V2 attention -- as described on two web
+ * pages:
  *   [P1] "Differential Transformer | ICLR 2025 Oral" (dainus.ai blog),
  *        sections "Differential Attention: 빼기의 힘", "λ의 역할과 학습",
  *        "파라미터 효율성";
- *   [P2] "Differential Transformer V2" (pogovet.com summary), 상세 정리 §1-§4.
+ *   [P2] "Differential Transformer V2" (pogovet.com summary), 상세 정리 §1-§4, §7.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -27,7 +29,8 @@
  *    failed launch (message from the HIP runtime).
  *  - "bf16" is bfloat16 stored as 16-bit words; "fp32" is IEEE binary32.
  *  - Empty problems (a zero batch or length) return DIFFATTN_OK and launch
- *    nothing.
+ *    nothing, except diffattn_v1_bwd, which still writes its two parameter
+ *    gradients (empty sums: zeros).
  */
 #ifndef DIFFATTN_H_
 #define DIFFATTN_H_
