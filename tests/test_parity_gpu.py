@@ -58,6 +58,24 @@ def compare(got, ref, rms_v, tol, rel_l2=None, what=""):
     return err / bound
 
 
+def compare_buckets(got, ref, rows, edges=(64, 1024), rel_l2=REL_L2_BF16, what=""):
+    """Relative L2 of got vs ref within row-length buckets (row index < 64,
+    64..1023, >= 1024): long rows average many keys and have small outputs, so
+    a whole-tensor norm could hide an error confined to them."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rows = np.asarray(rows)
+    lo = 0
+    for hi in (*edges, None):
+        sel = (rows >= lo) if hi is None else (rows >= lo) & (rows < hi)
+        if sel.any():
+            g, r = got[:, sel], ref[:, sel]
+            rel = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300))
+            note(f"{what} rows [{lo}, {hi}): relL2={rel:.3e}")
+            assert rel <= rel_l2, f"{what}: rows [{lo}, {hi}) relative L2 {rel:.3e} > {rel_l2}"
+        lo = hi if hi is not None else lo
+
+
 def cuda(d, dev):
     return {k: (None if v is None else v.to(dev)) for k, v in d.items()}
 
@@ -162,6 +180,31 @@ def test_v1_bf16_causal_rows_ignore_future(gpu):
     assert torch.equal(a[:, :cut], b[:, :cut])
 
 
+# Needles: key j of one map is set to alpha times the query of row i, so row i's
+# map puts nearly all its weight on key j (logit ~ alpha / sqrt(d) above the
+# rest).  The two maps pick different keys, so z ~ v_j - lambda v_j' is far from
+# the near-uniform regime; the kernel's running maximum jumps mid-row, which
+# takes the rescale path.
+V1_NEEDLES = ((250, 200, 17), (299, 0, 298), (64, 64, 63), (130, 5, 129), (7, 3, 7))
+
+
+@pytest.mark.parametrize("alpha", [40.0, 400.0])
+def test_v1_bf16_needles(gpu, alpha):
+    w = inp.V1_BF16.with_shape(B=1, T=300, H=2)
+    x = inp.v1_inputs(w)
+    for h in range(2):
+        for i, j1, j2 in V1_NEEDLES:
+            x["k1"][0, j1, h] = (alpha * x["q1"][0, i, h].float()).to(torch.bfloat16)
+            x["k2"][0, j2, h] = (alpha * x["q2"][0, i, h].float()).to(torch.bfloat16)
+    lam = li = oracle.lambda_init(4)
+    ref = oracle.v1_forward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, li, w.eps)
+    out = run_v1(cuda(x, gpu), lam, li, w.eps)
+    rows = [i for i, _, _ in V1_NEEDLES]
+    compare(out.cpu().numpy(), ref, rms(x["v"]), TOL_BF16, REL_L2_BF16, what=f"v1 needles a={alpha}")
+    compare(out[:, rows].cpu().numpy(), ref[:, rows], rms(x["v"]), TOL_BF16, REL_L2_BF16,
+            what=f"v1 needle rows a={alpha}")
+
+
 def test_v1_bf16_full_workload_sampled_rows(gpu):
     w = inp.V1_BF16
     note(f"generating {w.name} on the GPU")
@@ -181,6 +224,7 @@ def test_v1_bf16_full_workload_sampled_rows(gpu):
             got = out[b, rows, h].cpu().numpy()[None, :, None]
             worst = max(worst, compare(got, ref, rv, TOL_BF16, REL_L2_BF16,
                                        what=f"v1 full layer={layer} b={b} h={h}"))
+            compare_buckets(got, ref, rows, what=f"v1 full layer={layer} b={b} h={h}")
     note(f"v1 full workload: worst error / bound = {worst:.3f}")
 
 
@@ -274,6 +318,28 @@ def test_v2_deterministic(gpu):
     assert torch.equal(a, b)
 
 
+# Needles for V2: key j of a KV head is alpha times the query of one head of a
+# pair at row i, so that head's map is nearly one-hot on key j while its partner
+# stays diffuse (even and odd heads take turns).
+V2_NEEDLES = ((180, 150, 0), (181, 3, 1), (64, 64, 4), (100, 99, 7), (5, 0, 2))
+
+
+@pytest.mark.parametrize("alpha", [40.0, 400.0])
+def test_v2_needles(gpu, alpha):
+    w = inp.V2_PREFILL.with_shape(B=1, T=190, Hq=16, Hkv=2)
+    x = inp.v2_inputs(w)
+    g = w.Hq // w.Hkv
+    for i, j, head in V2_NEEDLES:
+        x["k"][0, j, head // g] = (alpha * x["q"][0, i, head].float()).to(torch.bfloat16)
+    ref = oracle.v2_forward(x["q"], x["k"], x["v"], x["logit"])
+    out = run_v2(cuda(x, gpu))
+    rows = [i for i, _, _ in V2_NEEDLES]
+    compare(out.float().cpu().numpy(), ref, rms(x["v"]), TOL_BF16, REL_L2_BF16,
+            what=f"v2 needles a={alpha}")
+    compare(out[:, rows].float().cpu().numpy(), ref[:, rows], rms(x["v"]), TOL_BF16, REL_L2_BF16,
+            what=f"v2 needle rows a={alpha}")
+
+
 def test_v2_full_workload_sampled_rows(gpu):
     w = inp.V2_PREFILL
     note(f"generating {w.name} on the GPU")
@@ -286,6 +352,7 @@ def test_v2_full_workload_sampled_rows(gpu):
         ref = oracle.v2_forward(sl["q"], sl["k"], sl["v"], sl["logit"], rows=rows)
         got = out[b:b + 1, rows].float().cpu().numpy()
         compare(got, ref, rv, TOL_BF16, REL_L2_BF16, what=f"v2 full b={b}")
+        compare_buckets(got, ref, rows, what=f"v2 full b={b}")
 
 
 def test_v2_varlen_full_workload_sampled_tokens(gpu):
@@ -333,6 +400,29 @@ def test_decode_small(gpu, B, S, Hq, Hkv, d, lens):
         for b, n in enumerate(lens):
             if n == 0:
                 assert np.all(got[b] == 0.0)
+
+
+def test_decode_needles(gpu):
+    # the random decode output is tiny (~RMS(V)/sqrt(S)), so the absolute bound
+    # barely tests it; a needle key per (batch, head) makes the output ~v_s
+    w = inp.V2_DECODE.with_shape(B=3, S=3000, Hq=16, Hkv=2, d=128, cache_lens=(3000, 1777, 65))
+    x = inp.decode_inputs(w)
+    g = w.Hq // w.Hkv
+    picks = ((0, 0, 2999), (0, 5, 0), (0, 9, 1500), (1, 1, 1776), (1, 14, 31), (2, 3, 64),
+             (2, 12, 0))
+    for b, j, s_ in picks:
+        x["k_cache"][b, s_, j // g] = (400.0 * x["q"][b, j].float()).to(torch.bfloat16)
+    lens = np.array(w.cache_lens)
+    ref = oracle.v2_decode(x["q"], x["k_cache"], x["v_cache"], x["logit"], cache_len=lens)
+    out = run_decode(cuda(x, gpu))
+    got = out.float().cpu().numpy()
+    compare(got, ref, rms(x["v_cache"]), TOL_BF16, REL_L2_BF16, what="decode needles")
+    sel = [(b, j // 2) for b, j, _ in picks]
+    g_sel = np.array([got[b, p] for b, p in sel])
+    r_sel = np.array([ref[b, p] for b, p in sel])
+    compare(g_sel, r_sel, rms(x["v_cache"]), TOL_BF16, REL_L2_BF16, what="decode needle pairs")
+    # the picked pairs are dominated by their needle value: far from the diffuse output
+    assert float(np.sqrt(np.mean(r_sel ** 2))) > 0.2 * rms(x["v_cache"])
 
 
 def test_decode_full_workload_sampled_batches(gpu):
