@@ -75,5 +75,52 @@ __device__ __forceinline__ void load_tile(const uint16_t* base, size_t stride, i
   }
 }
 
+// Loader of ROWS-row tiles of one layout and row stride that keeps, per lane,
+// one 32-bit byte offset per load of a full tile (computed once), so a full
+// tile costs no address arithmetic: the tile base moves in scalar registers.
+// Only a ragged tile (fewer than ROWS valid rows, the last of a sequence)
+// takes the clamping load_tile path, from a lane index made opaque there so
+// that path's offsets are not hoisted and kept live across the caller's loop.
+template <int D, bool TRANS, int NW = kWaves, int ROWS = 64>
+struct TileLoader {
+  static constexpr int kInstr = ROWS * BTile<D>::kRowBytes / 1024;
+  static constexpr int kJ = (kInstr + NW - 1) / NW;
+  uint32_t off[kJ];
+  size_t stride;
+
+  __device__ __forceinline__ TileLoader(size_t stride_, int wave, int lane) : stride(stride_) {
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int o = (wave + j * NW) * 1024 + lane * 16;  // LDS byte this lane fills
+      const int r = o / BTile<D>::kRowBytes;
+      const int pos = (o % BTile<D>::kRowBytes) >> 4;
+      int lc;
+      if (TRANS) {
+        constexpr int n32 = D / 16;
+        lc = (((pos >> 1) ^ (r & (n32 - 1))) << 1) | (pos & 1);
+      } else {
+        lc = pos ^ (r & (BTile<D>::kChunks - 1));
+      }
+      off[j] = (uint32_t)((r * stride + lc * 8) * 2);
+    }
+  }
+  // rows 0 .. ROWS-1 of the tile at `base`, of which n_valid are valid
+  __device__ __forceinline__ void load(const uint16_t* base, int n_valid, uint8_t* lds, int wave,
+                                       int lane) const {
+    if (n_valid >= ROWS) {
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        const int blk = wave + j * NW;
+        if (kInstr % NW != 0 && blk >= kInstr) break;
+        dma16(base, off[j], lds + blk * 1024);
+      }
+    } else {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      load_tile<D, TRANS, NW, ROWS>(base, stride, n_valid, lds, wave, ln);
+    }
+  }
+};
+
 }  // namespace bwd
 }  // namespace diffattn

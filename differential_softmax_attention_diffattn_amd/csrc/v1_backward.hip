@@ -39,6 +39,7 @@ namespace {
 
 using bwd::BTile;
 using bwd::load_tile;
+using bwd::TileLoader;
 using bwd::rows_base;
 using bwd::rows_offset;
 using bwd::trans_base;
@@ -237,14 +238,16 @@ __global__ __launch_bounds__(kDqWaves * kWave, 1) void v1_bwd_dq_kernel(V1BwdArg
   const uint16_t* k1g = a.k1 + ((size_t)b * T * a.H + h) * D;
   const uint16_t* k2g = a.k2 + ((size_t)b * T * a.H + h) * D;
   const uint16_t* vg = a.v + ((size_t)b * T * a.H + h) * DV;
+  const TileLoader<D, true> k_ld(kstr, wave, lane);  // K1 and K2: same layout and stride
+  const TileLoader<DV, false> v_ld(vstr, wave, lane);
   auto load_k = [&](int kt, uint8_t* l1, uint8_t* l2) {
     const int r0 = kt * kKeys;
-    load_tile<D, true>(k1g + (size_t)r0 * kstr, kstr, T - r0, l1, wave, lane);
-    load_tile<D, true>(k2g + (size_t)r0 * kstr, kstr, T - r0, l2, wave, lane);
+    k_ld.load(k1g + (size_t)r0 * kstr, T - r0, l1, wave, lane);
+    k_ld.load(k2g + (size_t)r0 * kstr, T - r0, l2, wave, lane);
   };
   auto load_v = [&](int kt, uint8_t* lv) {
     const int r0 = kt * kKeys;
-    load_tile<DV, false>(vg + (size_t)r0 * vstr, vstr, T - r0, lv, wave, lane);
+    v_ld.load(vg + (size_t)r0 * vstr, T - r0, lv, wave, lane);
   };
 
   f32x4 dq1[NDB], dq2[NDB];
@@ -452,12 +455,15 @@ __global__ __launch_bounds__(kKvWaves8 * kWave) void v1_bwd_dkdv_kernel(V1BwdArg
     const size_t rv = ((size_t)b * T + key0) * a.H + h;
     load_tile<DV, false, kKvWaves8, kKvKeys>(a.v + rv * DV, zstr, T - key0, vtile, wave, lane);
   }
+  // Q1 and Q2 share layout and row stride, so one loader serves both
+  const TileLoader<D, true, kKvWaves8, kKvRows> q_ld(qstr, wave, lane);
+  const TileLoader<DV, true, kKvWaves8, kKvRows> z_ld(zstr, wave, lane);
   auto load = [&](int item, uint8_t* st) {
     const int r0 = (n_qt - 1 - item) * kKvRows;
     const size_t rr = ((size_t)b * T + r0) * a.H + h;
-    load_tile<D, true, kKvWaves8, kKvRows>(a.q1 + rr * D, qstr, T - r0, st, wave, lane);
-    load_tile<D, true, kKvWaves8, kKvRows>(a.q2 + rr * D, qstr, T - r0, st + kQB, wave, lane);
-    load_tile<DV, true, kKvWaves8, kKvRows>(dz + rr * DV, zstr, T - r0, st + 2 * kQB, wave, lane);
+    q_ld.load(a.q1 + rr * D, T - r0, st, wave, lane);
+    q_ld.load(a.q2 + rr * D, T - r0, st + kQB, wave, lane);
+    z_ld.load(dz + rr * DV, T - r0, st + 2 * kQB, wave, lane);
     if (wave < 4 && lane < kKvRows / 4)  // wave k < 4 loads row vector k (128 bytes)
       dma16(stats + ((size_t)bh * 4 + wave) * Tp + r0, (uint32_t)(lane * 16),
             st + 2 * kQB + kZB + wave * kKvRows * 4);

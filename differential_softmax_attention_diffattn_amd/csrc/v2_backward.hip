@@ -38,6 +38,7 @@ namespace {
 
 using bwd::BTile;
 using bwd::load_tile;
+using bwd::TileLoader;
 using bwd::rows_base;
 using bwd::rows_offset;
 using bwd::trans_base;
@@ -216,13 +217,15 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, con
   const size_t kv_stride = (size_t)a.Hkv * D;
   const uint16_t* kbase_g = a.k + ((size_t)sv.tok0 * a.Hkv + kv) * D;
   const uint16_t* vbase_g = a.v + ((size_t)sv.tok0 * a.Hkv + kv) * D;
+  const TileLoader<D, true> k_ld(kv_stride, wave, lane);
+  const TileLoader<D, false> v_ld(kv_stride, wave, lane);
   auto load_k = [&](int kt, uint8_t* kl) {
     const int r0 = kt * kKeys;
-    load_tile<D, true>(kbase_g + (size_t)r0 * kv_stride, kv_stride, T - r0, kl, wave, lane);
+    k_ld.load(kbase_g + (size_t)r0 * kv_stride, T - r0, kl, wave, lane);
   };
   auto load_v = [&](int kt, uint8_t* vl) {
     const int r0 = kt * kKeys;
-    load_tile<D, false>(vbase_g + (size_t)r0 * kv_stride, kv_stride, T - r0, vl, wave, lane);
+    v_ld.load(vbase_g + (size_t)r0 * kv_stride, T - r0, vl, wave, lane);
   };
 
   f32x4 dq[NDB][2];
@@ -433,18 +436,19 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
   // the last query row this wave's keys can see is below the tile start: skip
   const int wave_key_lo = key0 + wave * 16;
 
+  const TileLoader<D, true> q_ld((size_t)a.Hq * D, wave, lane);  // Q_e and Q_o
+  const TileLoader<D, true> o_ld((size_t)hpairs * D, wave, lane);  // dout
   auto load = [&](int item, uint8_t* st) {
     const int pp = item % npairs;
     const int qt = n_qt - 1 - item / npairs;
     const int r0 = qt * kQRows;
     const int je = kvh * group + 2 * pp;  // even head of the pair
     const int pair = je / 2;
-    const size_t q_stride = (size_t)a.Hq * D;
     const uint16_t* qe = a.q + (((size_t)sv.tok0 + r0) * a.Hq + je) * D;
-    load_tile<D, true>(qe, q_stride, T - r0, st, wave, lane);
-    load_tile<D, true>(qe + D, q_stride, T - r0, st + TL::kBytes, wave, lane);
+    q_ld.load(qe, T - r0, st, wave, lane);
+    q_ld.load(qe + D, T - r0, st + TL::kBytes, wave, lane);
     const uint16_t* dsrc = a.dout + (((size_t)sv.tok0 + r0) * hpairs + pair) * D;
-    load_tile<D, true>(dsrc, (size_t)hpairs * D, T - r0, st + 2 * TL::kBytes, wave, lane);
+    o_ld.load(dsrc, T - r0, st + 2 * TL::kBytes, wave, lane);
     // row vectors (64 floats each, padded rows included): 5 x 256 bytes
     if (wave < 5 && lane < 16) {
       const float* src;
