@@ -139,8 +139,9 @@ def main():
                     default=None)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the kernels would shard)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path; "
+              "the kernels would shard by head (V1) or KV head (V2) with no communication",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

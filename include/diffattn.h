@@ -52,7 +52,7 @@ typedef enum { DIFFATTN_F32 = 0, DIFFATTN_BF16 = 1 } diffattn_dtype;
 enum {
   DIFFATTN_OK = 0,
   DIFFATTN_E_INVALID = -1,     /* bad shape, null pointer, non-finite scalar */
-  DIFFATTN_E_UNSUPPORTED = -2, /* well-formed, but not a shape/dtype this build runs */
+  DIFFATTN_E_UNSUPPORTED = -2, /* well-formed, but not a shape/dtype this library runs */
   DIFFATTN_E_ALIGN = -3,       /* a pointer is not 16-byte aligned */
   DIFFATTN_E_WORKSPACE = -4,   /* workspace missing or smaller than the query says */
   DIFFATTN_E_HIP = -5          /* the HIP runtime reported an error at launch */
