@@ -461,6 +461,17 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
   __syncthreads();
   if (stream != 0 || !wave_active) return;
   const float post = 1.0f - a.lambda_init;
+  // The lane's weights (channels db*16 + 4g .. +3), all loaded before the first
+  // output store: the memory counter also counts stores, so a weight load issued
+  // after a store would make its wait cover that store too.
+  const bool weighted = a.norm_weight != nullptr;
+  f32x4 wv[NDB];
+  if (weighted) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[db][i] = a.norm_weight[db * 16 + g * 4 + i];
+  }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const float* src = xch + (rg * kRows + nb * 16 + c16) * XSTRIDE + g * 4;
@@ -484,10 +495,7 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
       for (int db = 0; db < NDB; ++db) {
         f32x4 y;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float w = a.norm_weight ? a.norm_weight[db * 16 + g * 4 + i] : 1.0f;
-          y[i] = o[db][nb][i] * r * w;
-        }
+        for (int i = 0; i < 4; ++i) y[i] = o[db][nb][i] * r * (weighted ? wv[db][i] : 1.0f);
         *reinterpret_cast<f32x4*>(dst + db * 16) = y;
       }
     }
