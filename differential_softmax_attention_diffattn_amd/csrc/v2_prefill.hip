@@ -145,6 +145,10 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
                                          cs)
                           : u32x4{0, 0, 0, 0};
 
+  // the pair's coefficient logit for this lane's row, fetched now so its load
+  // latency is not paid at the end of the key loop
+  const float lgv = row < L ? a.logit[(size_t)(tok0 + row) * hpairs + p] : 0.f;
+
   // ---- direct-to-LDS tile loads (K and V rows, swizzled) ----
   // Each lane's chunks inside a tile are fixed; keep them as 32-bit element
   // offsets from the tile's first key and move the tile base in scalar
@@ -424,7 +428,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   }
   if (row < L) {
     const size_t tok = (size_t)(tok0 + row);
-    const float sg = sigmoid_f32(a.logit[tok * hpairs + p]);
+    const float sg = sigmoid_f32(lgv);
     uint16_t* dst = a.out + (tok * hpairs + p) * D + g * 4;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
