@@ -88,6 +88,22 @@ __device__ __forceinline__ float sum_across_rows(float x) {
   auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+// Sum over each row of 16 lanes with DPP lane permutations (VALU only, no LDS
+// round trip): lane ^ 1, lane ^ 2, then the mirrored quad of each half-row and
+// the mirrored half of the row.  Every lane of the row gets the row's sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<0xb1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_mov<0x4e>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_mov<0x141>(x);  // row_half_mirror
+  x += dpp_mov<0x140>(x);  // row_mirror
+  return x;
+}
+// Sum over all 64 lanes (every lane gets it), in a fixed order.
+__device__ __forceinline__ float wave_sum(float x) { return sum_across_rows(row16_sum(x)); }
 __device__ __forceinline__ float sum_within_row16(float x) {
   x += __shfl_xor(x, 1);
   x += __shfl_xor(x, 2);

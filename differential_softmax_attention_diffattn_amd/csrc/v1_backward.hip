@@ -13,7 +13,7 @@
 // dV = (P1 - lambda P2)^T dz are formed once.
 //
 // Kernels:
-//  * v1_bwd_pre_kernel (one wave per row): z from the forward's per-map O, dz
+//  * v1_bwd_pre_kernel (16 lanes per row): z from the forward's per-map O, dz
 //    (stored bf16 as the MFMA operand), D_k = rowsum(dO_k o O_k) from the
 //    rounded dz, log2-unit log-sum-exp, per-block partial sums of dlambda and
 //    dw; stats stored [B][H][4][T rounded up to 64] so a tile's row values
@@ -48,7 +48,7 @@ using bwd::trans_offset;
 constexpr int kKeys = 64;     // keys per staged tile (dq)
 constexpr int kRows = 16;     // query rows per wave (dq)
 constexpr int kDqWaves = 8;   // dq: 128 query rows per workgroup
-constexpr int kPreBlocks = 1024;
+constexpr int kPreBlocks = 2048;  // preprocessing workgroups at most (grid-stride beyond)
 
 template <bool B>
 struct BoolTag {
@@ -58,48 +58,59 @@ struct BoolTag {
 int pad64(int T) { return (T + 63) / 64 * 64; }
 
 // ---------------------------------------------------------------------------
-// Preprocessing: one wave per (row, head), grid-stride; per-block partials.
+// Preprocessing: 16 lanes per (row, head), grid-stride; per-block partials.
 // ---------------------------------------------------------------------------
+constexpr int kPreGroups = 16;  // 16-lane groups per 256-thread workgroup
 template <int DV>
 __global__ __launch_bounds__(256) void v1_bwd_pre_kernel(V1BwdArgs a, int Tp, uint16_t* dz,
                                                          float* stats, float* part) {
-  constexpr int E = DV / 64;  // channels per lane
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // A 16-lane group owns one (row, head) at a time; lane l16 holds channels
+  // l16*E .. l16*E + E-1, so the group reads each fp32 row as one contiguous
+  // run and its dot products are row-of-16 DPP sums (four rows per wave are in
+  // flight, no cross-lane traffic through LDS).
+  constexpr int E = DV / 16;
+  static_assert(E % 4 == 0, "channels per lane in 16-byte vectors");
+  const int l16 = threadIdx.x & 15;
+  const int grp = threadIdx.x >> 4;
   const float s = 1.0f - a.lambda_init;
   float w[E], dw_acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    w[e] = a.norm_weight ? a.norm_weight[lane * E + e] : 1.0f;
+    w[e] = a.norm_weight ? a.norm_weight[l16 * E + e] : 1.0f;
     dw_acc[e] = 0.f;
   }
   float dl_acc = 0.f;
   const long long n_items = (long long)a.B * a.H * Tp;
-  for (long long item = (long long)blockIdx.x * 4 + wave; item < n_items;
-       item += (long long)gridDim.x * 4) {
+  for (long long item = (long long)blockIdx.x * kPreGroups + grp; item < n_items;
+       item += (long long)gridDim.x * kPreGroups) {
     const int t = (int)(item % Tp);
     const long long bh = item / Tp;
     const int h = (int)(bh % a.H);
     const int b = (int)(bh / a.H);
     float* st = stats + (size_t)bh * 4 * Tp + t;  // [b][h][k][t] at st[k * Tp]
     if (t >= a.T) {  // padding rows: finite zeros (tiles read and mask them)
-      if (lane == 0) st[0] = st[Tp] = st[2 * Tp] = st[3 * Tp] = 0.f;
+      if (l16 == 0) st[0] = st[Tp] = st[2 * Tp] = st[3 * Tp] = 0.f;
       continue;
     }
     const size_t r = ((size_t)b * a.T + t) * a.H + h;
+    const float lse1 = a.lse[r * 2], lse2 = a.lse[r * 2 + 1];
     float dy[E], o1[E], o2[E], z[E];
+    const size_t c0 = r * DV + l16 * E;
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const f32x4 y4 = *reinterpret_cast<const f32x4*>(a.dy + c0 + e);
+      const f32x4 p4 = *reinterpret_cast<const f32x4*>(a.o1 + c0 + e);
+      const f32x4 q4 = *reinterpret_cast<const f32x4*>(a.o2 + c0 + e);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dy[e + i] = y4[i], o1[e + i] = p4[i], o2[e + i] = q4[i];
+    }
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const size_t c = r * DV + lane * E + e;
-      dy[e] = a.dy[c];
-      o1[e] = a.o1[c];
-      o2[e] = a.o2[c];
       z[e] = fmaf(-a.lambda, o2[e], o1[e]);  // as the forward forms it
       ss = fmaf(z[e], z[e], ss);
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+    ss = row16_sum(ss);
     const float rr = sqrtf(ss * (1.0f / DV) + a.eps);
     const float ir = 1.0f / rr;
     float g[E], gz = 0.f;
@@ -108,50 +119,60 @@ __global__ __launch_bounds__(256) void v1_bwd_pre_kernel(V1BwdArgs a, int Tp, ui
       g[e] = s * w[e] * dy[e];
       gz = fmaf(g[e], z[e], gz);
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) gz += __shfl_xor(gz, m);
+    gz = row16_sum(gz);
     const float cz = gz * ir * ir * ir * (1.0f / DV);
     float d1 = 0.f, d2 = 0.f, dl = 0.f;
-    uint16_t zb[E];
+    uint32_t zb[E / 2];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float dzv = fmaf(g[e], ir, -z[e] * cz);
-      zb[e] = f32_to_bf16(dzv);
-      const float dzr = bf16_to_f32(zb[e]);  // the operand the MFMAs see
-      d1 = fmaf(dzr, o1[e], d1);
-      d2 = fmaf(dzr, o2[e], d2);
-      dl = fmaf(-dzv, o2[e], dl);
+    for (int e = 0; e < E; e += 2) {
+      const float dz0 = fmaf(g[e], ir, -z[e] * cz);
+      const float dz1 = fmaf(g[e + 1], ir, -z[e + 1] * cz);
+      zb[e / 2] = pack_bf16x2(dz0, dz1);
+      const float r0 = bf16lo_to_f32(zb[e / 2]), r1 = bf16hi_to_f32(zb[e / 2]);  // as the MFMAs see dz
+      d1 = fmaf(r0, o1[e], d1);
+      d1 = fmaf(r1, o1[e + 1], d1);
+      d2 = fmaf(r0, o2[e], d2);
+      d2 = fmaf(r1, o2[e + 1], d2);
+      dl = fmaf(-dz0, o2[e], dl);
+      dl = fmaf(-dz1, o2[e + 1], dl);
       dw_acc[e] = fmaf(s * dy[e] * z[e], ir, dw_acc[e]);
+      dw_acc[e + 1] = fmaf(s * dy[e + 1] * z[e + 1], ir, dw_acc[e + 1]);
     }
     dl_acc += dl;
+    d1 = row16_sum(d1);
+    d2 = row16_sum(d2);
+    uint32_t* dzr = reinterpret_cast<uint32_t*>(dz + r * DV + l16 * E);
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      d1 += __shfl_xor(d1, m);
-      d2 += __shfl_xor(d2, m);
-    }
-    uint16_t* dzr = dz + r * DV + lane * E;
-#pragma unroll
-    for (int e = 0; e < E; ++e) dzr[e] = zb[e];
-    if (lane == 0) {
-      st[0] = a.lse[r * 2] * kLog2e;
-      st[Tp] = a.lse[r * 2 + 1] * kLog2e;
+    for (int e = 0; e < E / 2; e += 4)
+      *reinterpret_cast<u32x4*>(dzr + e) = u32x4{zb[e], zb[e + 1], zb[e + 2], zb[e + 3]};
+    if (l16 == 0) {
+      st[0] = lse1 * kLog2e;
+      st[Tp] = lse2 * kLog2e;
       st[2 * Tp] = d1;
       st[3 * Tp] = -a.lambda * d2;
     }
   }
-  // block partials: [dlambda, pad x3, dw[DV]]
-  __shared__ float red[4][DV];
-  __shared__ float redl[4];
+  // block partials: [dlambda, pad x3, dw[DV]], summed over the groups in order
+  __shared__ float red[kPreGroups][DV];
+  __shared__ float redl[kPreGroups];
 #pragma unroll
-  for (int e = 0; e < E; ++e) red[wave][lane * E + e] = dw_acc[e];
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) dl_acc += __shfl_xor(dl_acc, m);
-  if (lane == 0) redl[wave] = dl_acc;
+  for (int e = 0; e < E; ++e) red[grp][l16 * E + e] = dw_acc[e];
+  dl_acc = row16_sum(dl_acc);
+  if (l16 == 0) redl[grp] = dl_acc;
   __syncthreads();
   float* pb = part + (size_t)blockIdx.x * (DV + 4);
-  for (int c = threadIdx.x; c < DV; c += blockDim.x)
-    pb[4 + c] = red[0][c] + red[1][c] + red[2][c] + red[3][c];
-  if (threadIdx.x == 0) pb[0] = redl[0] + redl[1] + redl[2] + redl[3];
+  for (int c = threadIdx.x; c < DV; c += blockDim.x) {
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < kPreGroups; ++k) acc += red[k][c];
+    pb[4 + c] = acc;
+  }
+  if (threadIdx.x == 0) {
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < kPreGroups; ++k) acc += redl[k];
+    pb[0] = acc;
+  }
 }
 
 // Fixed-order sums of the per-block partials into dlambda and dw: a workgroup
@@ -607,7 +628,7 @@ Layout<D, DV> layout(int B, int T, int H) {
   Layout<D, DV> L;
   L.Tp = pad64(T);
   const long long items = (long long)B * H * L.Tp;
-  L.nblk = (int)std::min<long long>(kPreBlocks, (items + 3) / 4);
+  L.nblk = (int)std::min<long long>(kPreBlocks, (items + kPreGroups - 1) / kPreGroups);
   L.dz = 0;
   L.stats = ((size_t)B * T * H * DV * 2 + 255) / 256 * 256;
   L.part = L.stats + ((size_t)B * H * 4 * L.Tp * 4 + 255) / 256 * 256;

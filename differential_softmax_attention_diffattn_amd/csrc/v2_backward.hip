@@ -99,15 +99,20 @@ __device__ __forceinline__ bool tile_of(const V2BwdArgs& a, long long t, int row
 }
 
 // ---------------------------------------------------------------------------
-// Preprocessing: one wave per (workspace row, pair).
+// Preprocessing: 16 lanes per (workspace row, pair).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void v2_bwd_pre_kernel(V2BwdArgs a, float* lse2, float* sig) {
+  // 16 lanes per (row, pair) item, four items per wave: each lane reads D/16
+  // consecutive elements (16 bytes at D = 128) of dout and of both heads' O,
+  // and the dot products are summed over the 16-lane row by DPP.
+  constexpr int EPL = D / 16;
+  static_assert(EPL == 8 || EPL == 4, "head dim 128 or 64");
   const int h = a.Hq / 2;
-  const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  const long long item = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int l16 = threadIdx.x & 15;
   const long long Np = a.Np;
-  if (item >= Np * h) return;
+  if (item >= Np * h) return;  // uniform over the item's 16 lanes
   const int p = (int)(item % h);
   const long long prow = item / h;  // workspace row: 64-row tile prow / 64
   SeqView sv;
@@ -117,7 +122,7 @@ __global__ __launch_bounds__(256) void v2_bwd_pre_kernel(V2BwdArgs a, float* lse
   const size_t ws = (size_t)(2 * p) * Np + sv.ws0 + t;  // [2p][row]
   const size_t wsig = (size_t)p * Np + sv.ws0 + t;
   if (t >= sv.L) {  // padding rows: finite zeros (the tiles read them and mask them)
-    if (lane == 0) {
+    if (l16 == 0) {
       a.delta[ws] = 0.f;
       a.delta[ws + Np] = 0.f;
       lse2[ws] = 0.f;
@@ -127,27 +132,41 @@ __global__ __launch_bounds__(256) void v2_bwd_pre_kernel(V2BwdArgs a, float* lse
     return;
   }
   const size_t tok = (size_t)(sv.tok0 + t);
-  constexpr int E = D / 64;  // elements per lane
+  // the row's scalars go out with the vector loads
+  const float lg = a.logit[tok * h + p];
+  const float lse_e = a.lse[tok * a.Hq + 2 * p];
+  const float lse_o = a.lse[tok * a.Hq + 2 * p + 1];
+  const uint16_t* gp = a.dout + (tok * h + p) * D + l16 * EPL;
+  const uint16_t* ep = a.o_heads + (tok * a.Hq + 2 * p) * D + l16 * EPL;
+  uint32_t gw[EPL / 2], ew[EPL / 2], ow[EPL / 2];
+  if constexpr (EPL == 8) {
+    const u32x4 g4 = ldg128(gp), e4 = ldg128(ep), o4 = ldg128(ep + D);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gw[j] = g4[j], ew[j] = e4[j], ow[j] = o4[j];
+  } else {
+    const u32x2 g2 = *reinterpret_cast<const u32x2*>(gp);
+    const u32x2 e2 = *reinterpret_cast<const u32x2*>(ep);
+    const u32x2 o2 = *reinterpret_cast<const u32x2*>(ep + D);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) gw[j] = g2[j], ew[j] = e2[j], ow[j] = o2[j];
+  }
   float de = 0.f, dod = 0.f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int c = lane * E + e;
-    const float g = bf16_to_f32(a.dout[(tok * h + p) * D + c]);
-    de = fmaf(g, bf16_to_f32(a.o_heads[(tok * a.Hq + 2 * p) * D + c]), de);
-    dod = fmaf(g, bf16_to_f32(a.o_heads[(tok * a.Hq + 2 * p + 1) * D + c]), dod);
+  for (int j = 0; j < EPL / 2; ++j) {
+    de = fmaf(bf16lo_to_f32(gw[j]), bf16lo_to_f32(ew[j]), de);
+    de = fmaf(bf16hi_to_f32(gw[j]), bf16hi_to_f32(ew[j]), de);
+    dod = fmaf(bf16lo_to_f32(gw[j]), bf16lo_to_f32(ow[j]), dod);
+    dod = fmaf(bf16hi_to_f32(gw[j]), bf16hi_to_f32(ow[j]), dod);
   }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    de += __shfl_xor(de, m);
-    dod += __shfl_xor(dod, m);
-  }
-  if (lane == 0) {
-    const float s = sigmoid_f32(a.logit[tok * h + p]);
+  de = row16_sum(de);
+  dod = row16_sum(dod);
+  if (l16 == 0) {
+    const float s = sigmoid_f32(lg);
     a.delta[ws] = de;             // <dO_2p, O_2p> with dO_2p = dout_p
     a.delta[ws + Np] = -s * dod;  // <dO_2p+1, O_2p+1> with dO_2p+1 = -s dout_p
     a.dlogit[tok * h + p] = -s * (1.f - s) * dod;
-    lse2[ws] = a.lse[tok * a.Hq + 2 * p] * kLog2e;
-    lse2[ws + Np] = a.lse[tok * a.Hq + 2 * p + 1] * kLog2e;
+    lse2[ws] = lse_e * kLog2e;
+    lse2[ws + Np] = lse_o * kLog2e;
     sig[wsig] = s;
   }
 }
@@ -608,7 +627,7 @@ hipError_t launch_d(const V2BwdArgs& a, hipStream_t stream) {
   float* lse2 = a.delta + (size_t)a.Hq * Np;
   float* sig = lse2 + (size_t)a.Hq * Np;
   const long long pre_items = Np * (a.Hq / 2);
-  const long long pre_blocks = (pre_items + 3) / 4;
+  const long long pre_blocks = (pre_items + 15) / 16;  // 16 items per workgroup
   if (pre_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((v2_bwd_pre_kernel<D>), dim3((unsigned)pre_blocks), dim3(256), 0, stream, a,
                      lse2, sig);
