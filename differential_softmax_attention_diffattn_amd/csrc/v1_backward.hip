@@ -318,6 +318,24 @@ __global__ __launch_bounds__(kDqWaves * kWave, 1) void v1_bwd_dq_kernel(V1BwdArg
             *reinterpret_cast<const u32x4*>(lv + (bv ^ (c << 6)) + cc * 32 * TV::kRowBytes),
             dzf[c], dp[kb]);
     }
+    // K1^T and K2^T fragments of the dQ products (transposing reads), kKtRing
+    // blocks ahead of their MFMAs; the first ones go out before dS is formed,
+    // and the scheduling fences keep each read where it is issued.  Rows
+    // tr_key and tr_key + 16 share a swizzle class: the second read is +16 rows.
+    auto fetch_kt = [&](const uint8_t* kl, int db) {
+      const int off0 = (tk ^ (db << 5)) + cc * 32 * TK::kRowBytes;
+      const u32x2 lo = lds_read_tr16(kl + off0);
+      const u32x2 hi = lds_read_tr16(kl + off0 + 16 * TK::kRowBytes);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    constexpr int kKtRing = 2;
+    u32x4 k1r[kKtRing], k2r[kKtRing];
+#pragma unroll
+    for (int i = 0; i < kKtRing; ++i) {
+      k1r[i] = fetch_kt(l1, i);
+      k2r[i] = fetch_kt(l2, i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float x1[8], x2[8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -337,13 +355,13 @@ __global__ __launch_bounds__(kDqWaves * kWave, 1) void v1_bwd_dq_kernel(V1BwdArg
     const u32x4 ds1 = pack8(x1), ds2 = pack8(x2);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      // rows tr_key and tr_key + 16 share a swizzle class: the second read is +16 rows
-      const int off0 = (tk ^ (db << 5)) + cc * 32 * TK::kRowBytes;
-      const int off1 = off0 + 16 * TK::kRowBytes;
-      const u32x2 a1 = lds_read_tr16(l1 + off0), b1 = lds_read_tr16(l1 + off1);
-      const u32x2 a2 = lds_read_tr16(l2 + off0), b2 = lds_read_tr16(l2 + off1);
-      dq1[db] = mfma_bf16(u32x4{a1[0], a1[1], b1[0], b1[1]}, ds1, dq1[db]);
-      dq2[db] = mfma_bf16(u32x4{a2[0], a2[1], b2[0], b2[1]}, ds2, dq2[db]);
+      dq1[db] = mfma_bf16(k1r[db % kKtRing], ds1, dq1[db]);
+      dq2[db] = mfma_bf16(k2r[db % kKtRing], ds2, dq2[db]);
+      if (db + kKtRing < NDB) {
+        k1r[db % kKtRing] = fetch_kt(l1, db + kKtRing);
+        k2r[db % kKtRing] = fetch_kt(l2, db + kKtRing);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 

@@ -288,6 +288,20 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, con
         for (int nb = 0; nb < 2; ++nb) sacc[kb][nb] = mfma_bf16(kf, qf[nb][c], sacc[kb][nb]);
         dpa[kb] = mfma_bf16(vf, of[c], dpa[kb]);
       }
+    // K^T fragments of the dQ product (transposing reads), kKtRing blocks ahead
+    // of their MFMAs; the first ones go out before dS is formed, and the
+    // scheduling fences keep each read where it is issued
+    auto fetch_kt = [&](int db) {
+      const uint8_t* kp = kl + (bt ^ (db << 5)) + cc * 32 * TL::kRowBytes;
+      const u32x2 lo = lds_read_tr16(kp);
+      const u32x2 hi = lds_read_tr16(kp + 16 * TL::kRowBytes);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    constexpr int kKtRing = 2;
+    u32x4 ktr[kKtRing];
+#pragma unroll
+    for (int i = 0; i < kKtRing; ++i) ktr[i] = fetch_kt(i);
+    __builtin_amdgcn_sched_barrier(0);
     // dS^T per head, packed as the B operand of dQ^T += K^T dS^T
     u32x4 dsf[2];
 #pragma unroll
@@ -308,12 +322,10 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, con
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const uint8_t* kp = kl + (bt ^ (db << 5)) + cc * 32 * TL::kRowBytes;
-      const u32x2 lo = lds_read_tr16(kp);
-      const u32x2 hi = lds_read_tr16(kp + 16 * TL::kRowBytes);
-      const u32x4 kt_f = u32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) dq[db][nb] = mfma_bf16(kt_f, dsf[nb], dq[db][nb]);
+      for (int nb = 0; nb < 2; ++nb) dq[db][nb] = mfma_bf16(ktr[db % kKtRing], dsf[nb], dq[db][nb]);
+      if (db + kKtRing < NDB) ktr[db % kKtRing] = fetch_kt(db + kKtRing);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
