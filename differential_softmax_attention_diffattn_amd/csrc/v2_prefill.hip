@@ -135,19 +135,20 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   // yields log2-domain logits directly.
   const float cs = a.scale * kLog2e;
   const int row = q_lo + c16;
+  // Every load of the prologue goes out before any of its results is used:
+  // rows past the sequence end read its last row (L >= 1 here) and are zeroed
+  // when scaled, after the first tile's loads have been issued.  (Loading and
+  // scaling row by row under `row < L` made each load wait for the one before.)
+  const int rowc = min(row, L - 1);
   u32x4 qf[2][NC];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      qf[nb][c] = row < L ? scale_bf16x8(ldg128(a.q + ((size_t)(tok0 + row) * a.Hq + 2 * p + nb) * D +
-                                                c * 32 + g * 8),
-                                         cs)
-                          : u32x4{0, 0, 0, 0};
-
+      qf[nb][c] = ldg128(a.q + ((size_t)(tok0 + rowc) * a.Hq + 2 * p + nb) * D + c * 32 + g * 8);
   // the pair's coefficient logit for this lane's row, fetched now so its load
   // latency is not paid at the end of the key loop
-  const float lgv = row < L ? a.logit[(size_t)(tok0 + row) * hpairs + p] : 0.f;
+  const float lgv = a.logit[(size_t)(tok0 + rowc) * hpairs + p];
 
   // ---- direct-to-LDS tile loads (K and V rows, swizzled) ----
   // Each lane's chunks inside a tile are fixed; keep them as 32-bit element
@@ -202,6 +203,12 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   };
 
   load_tiles(0, smem0);
+  // Q pre-multiplied by scale * log2(e) (rounded to bf16); rows past the end zeroed
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      qf[nb][c] = row < L ? scale_bf16x8(qf[nb][c], cs) : u32x4{0, 0, 0, 0};
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): direct-to-LDS loads landed
   __syncthreads();
 
