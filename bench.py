@@ -19,6 +19,10 @@ TFLOP/s).  Inputs are synthetic, seeded, already resident in HBM when
 timing starts.  The fp64 CPU oracle is timed on a bounded sample of the
 headline workload on this host (``cpu_baseline``).
 
+Every leg's untimed warm-up is its W calls (steps for the headline) and then
+more until 100 ms of wall time have passed, so the timed calls run at the
+clocks of sustained load; the headline then times exactly K steps.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
        [--no-cpu-baseline] [--only v1|v2|varlen|decode|v1dec|bwd|vbwd|v1bwd|lproj|proj]
 """
@@ -113,6 +117,22 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def warm_up(fn, calls, min_ms=100.0):
+    """Untimed warm-up: ``calls`` calls of ``fn``, then more until at least
+    ``min_ms`` of wall time has passed since the start, so the timed calls that
+    follow run at the clocks of sustained load (the first tens of milliseconds
+    on an idle GPU run measurably slower)."""
+    import torch
+
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        fn()
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        fn()
+        torch.cuda.synchronize()
+
+
 def time_calls(fn, iters, stream):
     """Average milliseconds per call of ``fn`` with HIP events on ``stream``."""
     import torch
@@ -175,9 +195,7 @@ def main():
             for li in lams:
                 v1_call(li)
 
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
+        warm_up(step, args.warmup)
         log(f"[bench] timing {args.steps} steps x {len(lams)} layer calls")
         t0 = time.perf_counter()
         ms_step = time_calls(step, args.steps, stream)
@@ -224,8 +242,7 @@ def main():
             x = inp.v2_inputs(w, device=dev)
             o = torch.empty((w.B, w.T, w.Hq // 2, w.d), dtype=torch.bfloat16, device=dev)
             f = lambda: da.v2_fwd(x["q"], x["k"], x["v"], x["logit"], out=o)
-            for _ in range(args.warmup):
-                f()
+            warm_up(f, args.warmup)
             ms = time_calls(f, iters, stream)
             flop = w.B * v2_flops_seq(w.T, w.Hq, w.d)
             tf = flop / (ms * 1e-3) / 1e12
@@ -243,8 +260,7 @@ def main():
             mx = max(w.lengths)
             f = lambda: da.v2_fwd(x["q"], x["k"], x["v"], x["logit"], cu_seqlens=x["cu_seqlens"],
                                   max_seqlen=mx, out=o)
-            for _ in range(args.warmup):
-                f()
+            warm_up(f, args.warmup)
             ms = time_calls(f, iters, stream)
             flop = sum(v2_flops_seq(n, w.Hq, w.d) for n in w.lengths)
             tf = flop / (ms * 1e-3) / 1e12
@@ -263,8 +279,7 @@ def main():
                               dtype=torch.uint8, device=dev)
             f = lambda: da.v2_decode(x["q"], x["k_cache"], x["v_cache"], x["logit"], out=o,
                                      workspace=wsd)
-            for _ in range(args.warmup):
-                f()
+            warm_up(f, args.warmup)
             ms = time_calls(f, iters, stream)
             byts = 2.0 * w.B * w.S * w.Hkv * w.d * 2
             gbs = byts / (ms * 1e-3) / 1e9
@@ -283,8 +298,7 @@ def main():
             li = da.lambda_init(w.layer)
             f = lambda: da.v1_decode(x["q1"], x["q2"], x["k1_cache"], x["k2_cache"], x["v_cache"],
                                      li, li, w.eps, out=o, workspace=wsd)
-            for _ in range(args.warmup):
-                f()
+            warm_up(f, args.warmup)
             ms = time_calls(f, iters, stream)
             byts = 2.0 * w.B * w.S * w.H * (2 * w.d + w.dv)  # K1, K2 and V once, bf16
             gbs = byts / (ms * 1e-3) / 1e9
@@ -306,8 +320,7 @@ def main():
             wsb = torch.empty(da.v2_bwd_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.d),
                               dtype=torch.uint8, device=dev)
             f = lambda: da.v2_bwd(x["q"], x["k"], x["v"], x["logit"], oh, lse, dout, workspace=wsb)
-            for _ in range(args.warmup):
-                f()
+            warm_up(f, args.warmup)
             ms = time_calls(f, iters, stream)
             flop = w.B * v2_bwd_flops_seq(w.T, w.Hq, w.d)
             tf = flop / (ms * 1e-3) / 1e12
@@ -330,8 +343,7 @@ def main():
                 N, len(w.lengths), w.Hq, w.Hkv, w.d), dtype=torch.uint8, device=dev)
             f = lambda: da.v2_varlen_bwd(x["q"], x["k"], x["v"], x["logit"], x["cu_seqlens"], oh, lse,
                                          dout, workspace=wsb)
-            for _ in range(args.warmup):
-                f()
+            warm_up(f, args.warmup)
             ms = time_calls(f, iters, stream)
             flop = sum(v2_bwd_flops_seq(n, w.Hq, w.d) for n in w.lengths)
             tf = flop / (ms * 1e-3) / 1e12
@@ -357,8 +369,7 @@ def main():
                               dtype=torch.uint8, device=dev)
             f = lambda: da.v1_bwd(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], o1, o2, lse, dy, li,
                                   li, w.eps, workspace=wsb)
-            for _ in range(args.warmup):
-                f()
+            warm_up(f, args.warmup)
             ms = time_calls(f, iters, stream)
             flop = v1_bwd_flops(w.B, w.T, w.H, w.d, w.dv)
             tf = flop / (ms * 1e-3) / 1e12
@@ -374,8 +385,7 @@ def main():
             if args.only in (None, "lproj"):
                 lg = torch.empty((w.N, w.h), dtype=torch.float32, device=dev)
                 f = lambda: da.v2_lambda_proj(x["x"], x["w_lambda"], out=lg)
-                for _ in range(args.warmup):
-                    f()
+                warm_up(f, args.warmup)
                 ms = time_calls(f, iters, stream)
                 byts = 2.0 * w.N * w.d_model + 2.0 * w.h * w.d_model + 4.0 * w.N * w.h
                 gbs = byts / (ms * 1e-3) / 1e9
@@ -387,8 +397,7 @@ def main():
             if args.only in (None, "proj"):
                 y = torch.empty((w.N, w.d_model), dtype=torch.bfloat16, device=dev)
                 f = lambda: da.out_proj(x["attn_out"], x["w_o"], out=y)
-                for _ in range(args.warmup):
-                    f()
+                warm_up(f, args.warmup)
                 ms = time_calls(f, iters, stream)
                 flop = 2.0 * w.N * w.d_model * w.h * w.d
                 tf = flop / (ms * 1e-3) / 1e12
