@@ -19,6 +19,7 @@ from .diffattn_oracle import (  # noqa: F401
     v1_norm_backward,
     v2_backward,
     v2_attention_param_counts,
+    v2_backward_key_rows,
     v2_backward_query_rows,
     v2_combine,
     v2_decode,

@@ -506,6 +506,51 @@ def v2_backward_query_rows(q, k, v, logit, dout, rows, causal: bool = True,
     return dq, dlogit
 
 
+def v2_backward_key_rows(q, k, v, logit, dout, keys, kv_heads=None, causal: bool = True,
+                         scale: float | None = None, row_block: int = 1024):
+    """dk and dv of one sequence at the key positions ``keys`` only.
+
+    Same chain rule as ``v2_sequence_backward``, restricted to the columns
+    ``keys`` of every attention map: dk[t] = scale * sum_i dS[i, t] q_i and
+    dv[t] = sum_i P[i, t] dO_i, summed over the query heads of the KV head.
+    Each query row still needs its whole softmax row (for P's normaliser) and
+    its output O_i (for rowsum(dO o O)), so the cost is that of the forward
+    over the rows that can see the keys (i >= min(keys) when causal); rows are
+    taken ``row_block`` at a time to bound memory.  ``kv_heads`` (default all)
+    selects the KV heads to compute.
+    q [T, 2h, d], k/v [T, Hkv, d], logit [T, h], dout [T, h, d] ->
+    (dk [K, len(kv_heads), d], dv [K, len(kv_heads), d]).
+    """
+    q, k, v, logit, dout = (_f64(a) for a in (q, k, v, logit, dout))
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv or Hq % 2:
+        raise ValueError("Hq must be even and a multiple of Hkv")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    keys = np.asarray(keys, dtype=np.int64)
+    kv_heads = list(range(Hkv)) if kv_heads is None else [int(x) for x in kv_heads]
+    sig = sigmoid(logit)                                     # [T, h]
+    dk = np.zeros((keys.size, len(kv_heads), d))
+    dv = np.zeros((keys.size, len(kv_heads), v.shape[-1]))
+    first = int(keys.min()) if causal and keys.size else 0
+    for slot, kv in enumerate(kv_heads):
+        for j in (j for j in range(Hq) if gqa_kv_head(j, Hq, Hkv) == kv):
+            for r0 in range(first, T, row_block):
+                rows = np.arange(r0, min(r0 + row_block, T))
+                p = _attention_map(q[rows, j], k[:, kv], rows, scale, causal)   # [R, T]
+                o = p @ v[:, kv]                                             # O_j of the rows
+                if j % 2 == 0:
+                    do = dout[rows, j // 2]
+                else:
+                    do = -sig[rows, j // 2, None] * dout[rows, j // 2]
+                pk = p[:, keys]                                              # P at the keys
+                dpk = do @ v[keys, kv].T                                     # dP at the keys
+                dsk = pk * (dpk - np.sum(do * o, axis=-1, keepdims=True))    # dS at the keys
+                dk[:, slot] += scale * (dsk.T @ q[rows, j])
+                dv[:, slot] += pk.T @ do
+    return dk, dv
+
+
 # ---------------------------------------------------------------------------
 # The projections on either side of the V2 attention
 # ---------------------------------------------------------------------------

@@ -509,6 +509,31 @@ def test_v2_backward_query_rows_matches_central_differences(causal):
                 assert abs(g[(ridx,) + idx] - fd) <= 2e-8, (which, r, idx)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_v2_backward_key_rows_matches_central_differences(causal):
+    # dk and dv of selected keys (all KV heads, and one KV head alone) against
+    # central differences of the forward oracle; small row blocks make the
+    # row loop run several times
+    (q, k, v, logit, dout), loss = _v2_loss_and_grads(45, 7, 8, 2, 3, causal)
+    keys = np.array([0, 2, 6])
+    h = 1e-5
+    for kv_heads in (None, [1]):
+        dk, dv = oracle.v2_backward_key_rows(q[0], k[0], v[0], logit[0], dout[0], keys,
+                                             kv_heads=kv_heads, causal=causal, row_block=3)
+        heads = [0, 1] if kv_heads is None else kv_heads
+        for which, g in ((1, dk), (2, dv)):
+            for kidx, t in enumerate(keys):
+                for slot, kv in enumerate(heads):
+                    for c in range(g.shape[-1]):
+                        args = [q, k, v, logit]
+                        plus = [a.copy() for a in args]
+                        minus = [a.copy() for a in args]
+                        plus[which][0, t, kv, c] += h
+                        minus[which][0, t, kv, c] -= h
+                        fd = (loss(*plus) - loss(*minus)) / (2 * h)
+                        assert abs(g[kidx, slot, c] - fd) <= 2e-8, (which, t, kv, c)
+
+
 
 # ---------------------------------------------------------------------------
 # V1 decode
