@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import oracle
+import dlambda_check as dlc
 import differential_softmax_attention_diffattn_amd as da
 from differential_softmax_attention_diffattn_amd import inputs as inp
 
@@ -550,6 +551,15 @@ def test_v2_backward_full_workload_sampled(gpu):
     note(f"v2 bwd full dk zero-sum: max |sum| / sum|.| = {rel:.3e}")
     assert rel <= 1e-2
     assert torch.isfinite(dv).all()
+    # dk and dv element by element at sampled keys (tile edges and the last key),
+    # one KV head per sequence, against the key-restricted oracle
+    keys = np.array([0, 63, 64, 127, 128, 4096, w.T - 1])
+    for b, kv in ((0, 0), (1, w.Hkv - 1)):
+        note(f"v2 bwd full workload: key-row oracle b={b} kv={kv}")
+        rk, rv = oracle.v2_backward_key_rows(x["q"][b], x["k"][b], x["v"][b], x["logit"][b],
+                                             dout[b], keys, kv_heads=[kv])
+        compare_grad(dk[b, keys, kv:kv + 1].cpu().numpy(), rk, f"v2 bwd full dk b={b} kv={kv}")
+        compare_grad(dv[b, keys, kv:kv + 1].cpu().numpy(), rv, f"v2 bwd full dv b={b} kv={kv}")
 
 
 
@@ -612,6 +622,24 @@ def test_v2_varlen_backward_full_workload_sampled(gpu):
         note(f"v2 varlen bwd full dk zero-sum seq={s}: {rel:.3e}")
         assert rel <= 1e-2
     assert torch.isfinite(dv).all()
+    # dk and dv element by element at sampled keys against the key-restricted
+    # oracle: the last key of every sequence (all KV heads), and the first keys
+    # and the tile edges of the three shortest sequences (one KV head each; their
+    # first keys see every row of the sequence)
+    lens = [cu[s + 1] - cu[s] for s in range(len(cu) - 1)]
+    shortest = sorted(range(len(lens)), key=lambda s: lens[s])[:3]
+    for s in range(len(lens)):
+        a, e = cu[s], cu[s + 1]
+        if s in shortest:
+            keys = np.unique(np.array([0, 63, 64, 127, 128, lens[s] - 1]).clip(0, lens[s] - 1))
+            heads = [s % w.Hkv]
+        else:
+            keys, heads = np.array([lens[s] - 1]), list(range(w.Hkv))
+        note(f"v2 varlen bwd full workload: key-row oracle seq={s} keys={keys.tolist()}")
+        rk, rv = oracle.v2_backward_key_rows(x["q"][a:e], x["k"][a:e], x["v"][a:e],
+                                             x["logit"][a:e], dout[a:e], keys, kv_heads=heads)
+        compare_grad(dk[a + keys][:, heads].cpu().numpy(), rk, f"v2 varlen bwd full dk seq={s}")
+        compare_grad(dv[a + keys][:, heads].cpu().numpy(), rv, f"v2 varlen bwd full dv seq={s}")
 
 
 # ---------------------------------------------------------------------------
@@ -639,44 +667,63 @@ def v1_oracle_state(x, causal=True):
     return f(O1), f(O2), f(np.stack([L1, L2], axis=-1)), O1, O2
 
 
-def dlambda_terms(O1, O2, dy, lam, li, eps, weight=None):
-    """Terms -dz_ic O2_ic of dlambda (fp64, from the oracle's O), [..., dv]: the
-    scale its rounding error is measured against, since the terms nearly cancel
-    (<dz_i, z_i> = 0 by the norm's scale invariance, and O1 ~ O2 when the two
-    maps are close; one token makes the sum vanish in closed form)."""
-    dy = np.asarray(dy, dtype=np.float64)
-    w = 1.0 if weight is None else np.asarray(weight, dtype=np.float64)
-    z = O1 - lam * O2
-    r = np.sqrt(np.mean(z * z, axis=-1, keepdims=True) + eps)
-    g = (1.0 - li) * w * dy
-    dz = g / r - z * np.sum(g * z, axis=-1, keepdims=True) / (z.shape[-1] * r ** 3)
-    return -dz * O2
+def check_dlambda(got, ref, terms, what, e2e=None):
+    """dlambda, a cancelling sum (tests/dlambda_check.py states the bounds).
 
-
-def check_dlambda(got, ref, terms, what, end_to_end=False):
-    """dlambda, a cancelling sum, against its terms: on the oracle's forward
-    state |err| <= 2e-2 |ref| + 1e-5 sum|terms| (fp32 rounding, ~2^-24 per
-    term, with margin); end to end the kernel forward's O (fp16 P, bf16-rounded
-    scaled q) enters every row term, and 2e-2 |ref| may rise to 2e-2 times the
-    sum over rows of |row term|."""
+    Without ``e2e`` the backward ran on the oracle's forward state: |err| <=
+    2e-3 |ref| + 2^-24 sum|terms|.  With ``e2e = (G1, G2, dO1, dO2)`` it ran on
+    the kernel's training forward, whose measured O error dO moves dlambda by
+    about <G, dO>; the bound adds 6 standard deviations of that change."""
     got, ref = float(np.asarray(got).reshape(())), float(ref)
     err = abs(got - ref)
-    scale = float(np.sum(np.abs(terms)))
-    bound = 2e-2 * abs(ref) + 1e-5 * scale
-    if end_to_end:
-        bound = max(bound, 2e-2 * float(np.sum(np.abs(np.sum(terms, axis=-1)))) + 1e-5 * scale)
-    note(f"{what} dlambda: got={got:.6g} ref={ref:.6g} err={err:.3e} scale={scale:.3e} "
-         f"bound={bound:.3e} ({err / bound:.3f}x)")
+    if e2e is None:
+        bound = dlc.oracle_state_bound(ref, terms)
+        extra = ""
+    else:
+        bound, sigma = dlc.end_to_end_bound(ref, terms, *e2e)
+        extra = f" sigma(fwd)={sigma:.3e}"
+    tag = "decisive" if dlc.decisive(bound, ref) else "NOT decisive (|ref| too small against it)"
+    note(f"{what} dlambda: got={got:.6g} ref={ref:.6g} err={err:.3e} bound={bound:.3e} "
+         f"({err / bound:.3f}x, {bound / max(abs(ref), 1e-300):.3f}|ref|, {tag}){extra}")
     assert err <= bound, f"{what} dlambda: |err| {err:.3e} > {bound:.3e}"
+    return dlc.decisive(bound, ref)
 
 
-def check_v1_grads(grads, refs, what, dlam_terms, end_to_end=False):
+def check_v1_grads(grads, refs, what, dlam_terms, e2e=None):
+    decisive = None
     for name, g, r in zip(V1_GRAD_NAMES, grads, refs):
         got = g.cpu().numpy().reshape(np.shape(r))
         if name == "dlambda":
-            check_dlambda(got, r, dlam_terms, what, end_to_end)
+            decisive = check_dlambda(got, r, dlam_terms, what, e2e)
         else:
             compare_grad(got, r, f"{what} {name}")
+    return decisive
+
+
+def v1_dlambda_e2e(O1, O2, o1, o2, dy, lam, li, eps, weight=None):
+    """(G1, G2, dO1, dO2) for the end-to-end dlambda bound: the oracle's
+    sensitivity and the kernel forward's measured O error."""
+    G1, G2 = dlc.dlambda_sensitivity(O1, O2, dy, lam, li, eps, weight)
+    return G1, G2, o1.cpu().double().numpy() - O1, o2.cpu().double().numpy() - O2
+
+
+def check_v1_backward_both_ways(xg, x, dy, lam, li, eps, weight, causal, refs, what,
+                                require_decisive_e2e=True):
+    """The backward on the oracle's forward state (strict, always decisive unless
+    dlambda is zero in closed form), then end to end."""
+    o1, o2, lse, O1, O2 = v1_oracle_state(x, causal)
+    wg = None if weight is None else weight.to(xg["v"].device)
+    dev = xg["v"].device
+    grads = da.v1_bwd(xg["q1"], xg["k1"], xg["q2"], xg["k2"], xg["v"], o1.to(dev), o2.to(dev),
+                      lse.to(dev), dy.to(dev), lam, li, eps, weight=wg, causal=causal)
+    torch.cuda.synchronize()
+    terms = dlc.dlambda_terms(O1, O2, dy.numpy(), lam, li, eps, weight)
+    assert check_v1_grads(grads, refs, what + " [oracle state]", terms) or abs(refs[5]) < 1e-6
+    _, ko1, ko2, _, grads = run_v1_train(xg, dy.to(dev), lam, li, eps, wg, causal)
+    e2e = v1_dlambda_e2e(O1, O2, ko1, ko2, dy.numpy(), lam, li, eps, weight)
+    decisive = check_v1_grads(grads, refs, what, terms, e2e)
+    if require_decisive_e2e:
+        assert decisive or abs(refs[5]) < 1e-6, f"{what}: end-to-end dlambda bound not decisive"
 
 
 @pytest.mark.parametrize("B,T,H,d,dv,causal,layer,weighted,std", [
@@ -696,16 +743,12 @@ def test_v1_backward_small_all_elements(gpu, B, T, H, d, dv, causal, layer, weig
     refs = oracle.v1_backward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, li, w.eps, dy,
                               weight=weight, causal=causal)
     what = f"v1 bwd B={B} T={T} H={H} d={d} causal={causal} layer={layer} std={w.std:.3g}"
-    # (1) the backward on the oracle's forward state: every gradient, dlambda included
-    o1, o2, lse, O1, O2 = v1_oracle_state(x, causal)
-    grads = da.v1_bwd(xg["q1"], xg["k1"], xg["q2"], xg["k2"], xg["v"], o1.to(gpu), o2.to(gpu),
-                      lse.to(gpu), dy.to(gpu), lam, li, w.eps, weight=wg, causal=causal)
-    torch.cuda.synchronize()
-    terms = dlambda_terms(O1, O2, dy.numpy(), lam, li, w.eps, weight)
-    check_v1_grads(grads, refs, what + " [oracle state]", terms)
-    # (2) end to end: the kernel's training forward feeding the backward
-    *_, grads = run_v1_train(xg, dy.to(gpu), lam, li, w.eps, wg, causal)
-    check_v1_grads(grads, refs, what, terms, end_to_end=True)
+    # (1) on the oracle's forward state, then (2) end to end.  At T200 / layer 12
+    # the fp16 P of the forward moves dlambda by ~0.12 |ref| (sigma ~0.1 |ref|,
+    # also in a CPU emulation of the rounding), so its end-to-end bound cannot
+    # tell dlambda from zero and the oracle-state check decides there.
+    check_v1_backward_both_ways(xg, x, dy, lam, li, w.eps, weight, causal, refs, what,
+                                require_decisive_e2e=(T, layer) != (200, 12))
 
 
 @pytest.mark.parametrize("lam,li", [(1.3, 0.5), (-0.5, 0.3)])
@@ -717,14 +760,8 @@ def test_v1_backward_lambda_outside_init_range(gpu, lam, li):
     dy = inp.v1_dy(w)
     xg = cuda(x, gpu)
     refs = oracle.v1_backward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, li, w.eps, dy)
-    o1, o2, lse, O1, O2 = v1_oracle_state(x)
-    grads = da.v1_bwd(xg["q1"], xg["k1"], xg["q2"], xg["k2"], xg["v"], o1.to(gpu), o2.to(gpu),
-                      lse.to(gpu), dy.to(gpu), lam, li, w.eps)
-    torch.cuda.synchronize()
-    terms = dlambda_terms(O1, O2, dy.numpy(), lam, li, w.eps)
-    check_v1_grads(grads, refs, f"v1 bwd lambda={lam} li={li} [oracle state]", terms)
-    *_, grads = run_v1_train(xg, dy.to(gpu), lam, li, w.eps)
-    check_v1_grads(grads, refs, f"v1 bwd lambda={lam} li={li}", terms, end_to_end=True)
+    check_v1_backward_both_ways(xg, x, dy, lam, li, w.eps, None, True, refs,
+                                f"v1 bwd lambda={lam} li={li}")
 
 
 def test_v1_backward_grid_stride_rows(gpu):
@@ -736,14 +773,7 @@ def test_v1_backward_grid_stride_rows(gpu):
     lam = li = oracle.lambda_init(9)
     xg = cuda(x, gpu)
     refs = oracle.v1_backward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, li, w.eps, dy)
-    o1, o2, lse, O1, O2 = v1_oracle_state(x)
-    grads = da.v1_bwd(xg["q1"], xg["k1"], xg["q2"], xg["k2"], xg["v"], o1.to(gpu), o2.to(gpu),
-                      lse.to(gpu), dy.to(gpu), lam, li, w.eps)
-    torch.cuda.synchronize()
-    terms = dlambda_terms(O1, O2, dy.numpy(), lam, li, w.eps)
-    check_v1_grads(grads, refs, "v1 bwd B2 T1024 H4 [oracle state]", terms)
-    *_, grads = run_v1_train(xg, dy.to(gpu), lam, li, w.eps)
-    check_v1_grads(grads, refs, "v1 bwd B2 T1024 H4", terms, end_to_end=True)
+    check_v1_backward_both_ways(xg, x, dy, lam, li, w.eps, None, True, refs, "v1 bwd B2 T1024 H4")
 
 
 def test_v1_train_forward_outputs(gpu):
@@ -829,11 +859,11 @@ def test_v1_backward_full_workload_sampled(gpu):
         o1[b, :, h] = so1[0, :, 0].to(gpu)
         o2[b, :, h] = so2[0, :, 0].to(gpu)
         lse[b, :, h] = slse[0, :, 0].to(gpu)
-        terms.append(dlambda_terms(O1, O2, dy[b:b + 1, :, h:h + 1].numpy(), lam, li, w.eps))
+        terms.append(dlc.dlambda_terms(O1, O2, dy[b:b + 1, :, h:h + 1].numpy(), lam, li, w.eps))
     gm = da.v1_bwd(xg["q1"], xg["k1"], xg["q2"], xg["k2"], xg["v"], o1, o2, lse,
                    (dy * mask).to(gpu), lam, li, w.eps)
     torch.cuda.synchronize()
-    check_dlambda(gm[5].cpu().numpy(), sum(refs[k][5] for k in refs), np.concatenate(terms),
+    assert check_dlambda(gm[5].cpu().numpy(), sum(refs[k][5] for k in refs), np.concatenate(terms),
                   "v1 bwd full (sampled heads)")
     compare_grad(gm[6].cpu().numpy(), sum(refs[k][6] for k in refs),
                  "v1 bwd full dweight (sampled heads)")
