@@ -95,6 +95,22 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _outputs(fn, outs, specs, dev):
+    """Output tensors of ``fn``: the caller's ``outs`` (checked against ``specs``,
+    a list of (name, shape, dtype)) or new ones."""
+    torch = _torch()
+    if outs is None:
+        return [torch.empty(shape, dtype=dt, device=dev) for _, shape, dt in specs]
+    outs = list(outs)
+    if len(outs) != len(specs):
+        raise ValueError(f"{fn}: outs must hold {len(specs)} tensors ({', '.join(n for n, _, _ in specs)})")
+    for t, (name, shape, dt) in zip(outs, specs):
+        _check_tensor(name, t, dtype=dt, dim=len(shape), device=dev)
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{fn}: {name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return outs
+
+
 def lambda_init(layer: int) -> float:
     """Initial lambda of 1-based layer ``layer`` (computed by the library, fp32)."""
     v = _lib.load().diffattn_lambda_init(int(layer))
@@ -170,19 +186,20 @@ def _v1_bf16_check(q1, k1, q2, k2, v, weight):
 
 
 def v1_fwd_train(q1, k1, q2, k2, v, lam: float, lambda_init: float, eps: float = 1e-12,
-                 weight=None, causal: bool = True, workspace=None):
+                 weight=None, causal: bool = True, workspace=None, outs=None):
     """DIFF V1 training forward (bf16 inputs).
 
     Returns (out [B,T,H,dv], o1 [B,T,H,dv], o2 [B,T,H,dv], lse [B,T,H,2]), all
     fp32: o1, o2 are the per-map normalised outputs, lse their log-sum-exp.
+    ``outs``: the same four tensors, preallocated (optional).
     """
     torch = _torch()
     dev = q1.device
     B, T, H, d, dv = _v1_bf16_check(q1, k1, q2, k2, v, weight)
-    out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
-    o1 = torch.empty_like(out)
-    o2 = torch.empty_like(out)
-    lse = torch.empty((B, T, H, 2), dtype=torch.float32, device=dev)
+    f32 = torch.float32
+    out, o1, o2, lse = _outputs("v1_fwd_train", outs, [
+        ("out", (B, T, H, dv), f32), ("o1", (B, T, H, dv), f32), ("o2", (B, T, H, dv), f32),
+        ("lse", (B, T, H, 2), f32)], dev)
     lib = _lib.load()
     need = int(lib.diffattn_v1_workspace_bytes(B, T, H, d, dv, DIFFATTN_BF16))
     if need and workspace is None:
@@ -204,12 +221,13 @@ def v1_bwd_workspace_bytes(B, T, H, d, dv) -> int:
 
 
 def v1_bwd(q1, k1, q2, k2, v, o1, o2, lse, dy, lam: float, lambda_init: float,
-           eps: float = 1e-12, weight=None, causal: bool = True, workspace=None):
+           eps: float = 1e-12, weight=None, causal: bool = True, workspace=None, outs=None):
     """DIFF V1 backward (bf16 inputs): gradients of sum(dy * y).
 
     o1, o2, lse from v1_fwd_train on the same inputs; dy [B,T,H,dv] fp32 ->
     (dq1, dk1, dq2, dk2 [B,T,H,d], dv [B,T,H,dv], dlambda [1], dweight [dv]),
     all fp32.  dweight is the gradient of the norm weight (ones when weight is None).
+    ``outs``: the same seven tensors, preallocated (optional).
     """
     torch = _torch()
     dev = q1.device
@@ -221,13 +239,11 @@ def v1_bwd(q1, k1, q2, k2, v, o1, o2, lse, dy, lam: float, lambda_init: float,
     _check_tensor("lse", lse, dtype=torch.float32, dim=4, device=dev)
     if tuple(lse.shape) != (B, T, H, 2):
         raise ValueError(f"lse must have shape {(B, T, H, 2)}")
-    dq1 = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
-    dk1 = torch.empty_like(dq1)
-    dq2 = torch.empty_like(dq1)
-    dk2 = torch.empty_like(dq1)
-    dvv = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
-    dlam = torch.empty(1, dtype=torch.float32, device=dev)
-    dw = torch.empty(dv, dtype=torch.float32, device=dev)
+    f32 = torch.float32
+    dq1, dk1, dq2, dk2, dvv, dlam, dw = _outputs("v1_bwd", outs, [
+        ("dq1", (B, T, H, d), f32), ("dk1", (B, T, H, d), f32), ("dq2", (B, T, H, d), f32),
+        ("dk2", (B, T, H, d), f32), ("dv", (B, T, H, dv), f32), ("dlambda", (1,), f32),
+        ("dweight", (dv,), f32)], dev)
     lib = _lib.load()
     need = int(lib.diffattn_v1_bwd_workspace_bytes(B, T, H, d, dv))
     if workspace is None and need:
@@ -282,7 +298,7 @@ def v2_fwd(q, k, v, logit, cu_seqlens=None, max_seqlen=None, causal: bool = True
         if max_seqlen is None:
             raise ValueError("max_seqlen (a host int) is required with cu_seqlens")
         nseq = cu_seqlens.shape[0] - 1
-        B, T = 0, 0
+        B, T = 0, lead[0]  # packed: T carries the token count N
     else:
         nseq, max_seqlen = 0, 0
         B, T = lead
@@ -327,6 +343,8 @@ def v2_decode(q, k_cache, v_cache, logit, cache_len=None, scale: float | None = 
     if out is None:
         out = torch.empty((B, Hq // 2, d), dtype=torch.bfloat16, device=dev)
     _check_tensor("out", out, dtype=torch.bfloat16, dim=3, device=dev)
+    if tuple(out.shape) != (B, Hq // 2, d):
+        raise ValueError("out has the wrong shape")
     lib = _lib.load()
     need = int(lib.diffattn_v2_decode_workspace_bytes(B, S_max, Hq, Hkv, d))
     if workspace is None and need:
@@ -362,18 +380,19 @@ def _v2_padded_check(q, k, v, logit):
     return B, T, Hq, k.shape[2], d
 
 
-def v2_fwd_train(q, k, v, logit, causal: bool = True, scale: float | None = None):
+def v2_fwd_train(q, k, v, logit, causal: bool = True, scale: float | None = None, outs=None):
     """DIFF V2 training forward (padded batch).
 
     q [B,T,Hq,d], k/v [B,T,Hkv,d] bf16, logit [B,T,Hq/2] fp32 ->
     (out [B,T,Hq/2,d] bf16, o_heads [B,T,Hq,d] bf16, lse [B,T,Hq] fp32).
+    ``outs``: the same three tensors, preallocated (optional).
     """
     torch = _torch()
     dev = q.device
     B, T, Hq, Hkv, d = _v2_padded_check(q, k, v, logit)
-    out = torch.empty((B, T, Hq // 2, d), dtype=torch.bfloat16, device=dev)
-    o_heads = torch.empty((B, T, Hq, d), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
+    out, o_heads, lse = _outputs("v2_fwd_train", outs, [
+        ("out", (B, T, Hq // 2, d), torch.bfloat16), ("o_heads", (B, T, Hq, d), torch.bfloat16),
+        ("lse", (B, T, Hq), torch.float32)], dev)
     lib = _lib.load()
     with torch.cuda.device(dev):
         rc = lib.diffattn_v2_fwd_train(
@@ -388,11 +407,12 @@ def v2_bwd_workspace_bytes(B, T, Hq, Hkv, d) -> int:
 
 
 def v2_bwd(q, k, v, logit, o_heads, lse, dout, causal: bool = True, scale: float | None = None,
-           workspace=None):
+           workspace=None, outs=None):
     """DIFF V2 backward (padded batch): gradients of sum(dout * out).
 
     o_heads, lse from v2_fwd_train on the same inputs; dout [B,T,Hq/2,d] bf16 ->
     (dq [B,T,Hq,d], dk [B,T,Hkv,d], dv [B,T,Hkv,d], dlogit [B,T,Hq/2]), all fp32.
+    ``outs``: the same four tensors, preallocated (optional).
     """
     torch = _torch()
     dev = q.device
@@ -404,10 +424,10 @@ def v2_bwd(q, k, v, logit, o_heads, lse, dout, causal: bool = True, scale: float
         raise ValueError("o_heads / lse shapes do not match q")
     if tuple(dout.shape) != (B, T, Hq // 2, d):
         raise ValueError("dout must have shape [B, T, Hq/2, d]")
-    dq = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
-    dk = torch.empty((B, T, Hkv, d), dtype=torch.float32, device=dev)
-    dv = torch.empty((B, T, Hkv, d), dtype=torch.float32, device=dev)
-    dlogit = torch.empty((B, T, Hq // 2), dtype=torch.float32, device=dev)
+    f32 = torch.float32
+    dq, dk, dv, dlogit = _outputs("v2_bwd", outs, [
+        ("dq", (B, T, Hq, d), f32), ("dk", (B, T, Hkv, d), f32), ("dv", (B, T, Hkv, d), f32),
+        ("dlogit", (B, T, Hq // 2), f32)], dev)
     lib = _lib.load()
     need = int(lib.diffattn_v2_bwd_workspace_bytes(B, T, Hq, Hkv, d))
     if workspace is None and need:
@@ -441,21 +461,22 @@ def _v2_packed_check(q, k, v, logit, cu_seqlens):
 
 
 def v2_varlen_fwd_train(q, k, v, logit, cu_seqlens, max_seqlen: int, causal: bool = True,
-                        scale: float | None = None):
+                        scale: float | None = None, outs=None):
     """DIFF V2 training forward of a packed batch.
 
     q [N,Hq,d], k/v [N,Hkv,d] bf16, logit [N,Hq/2] fp32, cu_seqlens int32 [nseq+1] ->
     (out [N,Hq/2,d] bf16, o_heads [N,Hq,d] bf16, lse [N,Hq] fp32).
+    ``outs``: the same three tensors, preallocated (optional).
     """
     torch = _torch()
     dev = q.device
     N, Hq, Hkv, d, nseq = _v2_packed_check(q, k, v, logit, cu_seqlens)
-    out = torch.empty((N, Hq // 2, d), dtype=torch.bfloat16, device=dev)
-    o_heads = torch.empty((N, Hq, d), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((N, Hq), dtype=torch.float32, device=dev)
+    out, o_heads, lse = _outputs("v2_varlen_fwd_train", outs, [
+        ("out", (N, Hq // 2, d), torch.bfloat16), ("o_heads", (N, Hq, d), torch.bfloat16),
+        ("lse", (N, Hq), torch.float32)], dev)
     with torch.cuda.device(dev):
         rc = _lib.load().diffattn_v2_varlen_fwd_train(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(logit), _ptr(cu_seqlens), nseq, int(max_seqlen),
+            _ptr(q), _ptr(k), _ptr(v), _ptr(logit), _ptr(cu_seqlens), nseq, int(max_seqlen), N,
             _ptr(out), _ptr(o_heads), _ptr(lse), Hq, Hkv, d, float(scale or 0.0),
             1 if causal else 0, DIFFATTN_BF16, _stream(dev))
     _lib.check("diffattn_v2_varlen_fwd_train", rc)
@@ -463,11 +484,12 @@ def v2_varlen_fwd_train(q, k, v, logit, cu_seqlens, max_seqlen: int, causal: boo
 
 
 def v2_varlen_bwd(q, k, v, logit, cu_seqlens, o_heads, lse, dout, causal: bool = True,
-                  scale: float | None = None, workspace=None):
+                  scale: float | None = None, workspace=None, outs=None):
     """DIFF V2 backward of a packed batch: gradients of sum(dout * out).
 
     o_heads, lse from v2_varlen_fwd_train; dout [N,Hq/2,d] bf16 ->
     (dq [N,Hq,d], dk [N,Hkv,d], dv [N,Hkv,d], dlogit [N,Hq/2]), all fp32.
+    ``outs``: the same four tensors, preallocated (optional).
     """
     torch = _torch()
     dev = q.device
@@ -479,10 +501,10 @@ def v2_varlen_bwd(q, k, v, logit, cu_seqlens, o_heads, lse, dout, causal: bool =
         raise ValueError("o_heads / lse shapes do not match q")
     if tuple(dout.shape) != (N, Hq // 2, d):
         raise ValueError("dout must have shape [N, Hq/2, d]")
-    dq = torch.empty((N, Hq, d), dtype=torch.float32, device=dev)
-    dk = torch.empty((N, Hkv, d), dtype=torch.float32, device=dev)
-    dv = torch.empty((N, Hkv, d), dtype=torch.float32, device=dev)
-    dlogit = torch.empty((N, Hq // 2), dtype=torch.float32, device=dev)
+    f32 = torch.float32
+    dq, dk, dv, dlogit = _outputs("v2_varlen_bwd", outs, [
+        ("dq", (N, Hq, d), f32), ("dk", (N, Hkv, d), f32), ("dv", (N, Hkv, d), f32),
+        ("dlogit", (N, Hq // 2), f32)], dev)
     lib = _lib.load()
     need = int(lib.diffattn_v2_varlen_bwd_workspace_bytes(N, nseq, Hq, Hkv, d))
     if workspace is None and need:
