@@ -46,8 +46,8 @@ SIGNATURES = {
     "diffattn_v2_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i,
                              _i, _i, _i, _i, _f, _i, _i, _vp]),
     "diffattn_v2_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
-    "diffattn_v2_varlen_fwd_train": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _i, _i, _i,
-                                          _f, _i, _i, _vp]),
+    "diffattn_v2_varlen_fwd_train": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _vp, _vp, _vp, _i,
+                                          _i, _i, _f, _i, _i, _vp]),
     "diffattn_v2_varlen_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _sz, _ll, _i, _i, _i, _f, _i, _i, _vp]),
     "diffattn_v2_varlen_bwd_workspace_bytes": (_sz, [_ll, _i, _i, _i, _i]),

@@ -267,8 +267,10 @@ int diffattn_v2_fwd(const void* q, const void* k, const void* v, const float* la
   if (rc != DIFFATTN_OK) return rc;
   int nseq_eff, maxlen;
   if (cu_seqlens) {
-    if (nseq < 0 || max_seqlen < 0)
-      return fail(DIFFATTN_E_INVALID, "%s: nseq=%d max_seqlen=%d must be >= 0", fn, nseq, max_seqlen);
+    if (nseq < 0 || max_seqlen < 0 || T < 0)
+      return fail(DIFFATTN_E_INVALID, "%s: nseq=%d max_seqlen=%d T=%d must be >= 0", fn, nseq,
+                  max_seqlen, T);
+    if (prod({T, Hq, d}) > (1LL << 40)) return fail(DIFFATTN_E_INVALID, "%s: problem too large", fn);
     nseq_eff = nseq;
     maxlen = max_seqlen;
   } else {
@@ -293,6 +295,7 @@ int diffattn_v2_fwd(const void* q, const void* k, const void* v, const float* la
   a.nseq = nseq_eff;
   a.max_seqlen = maxlen;
   a.T = T;
+  a.N = (cu_seqlens && T > 0) ? (long long)T : -1;  // packed: T is the token count, if known
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.d = d;
@@ -327,6 +330,7 @@ int diffattn_v2_fwd_train(const void* q, const void* k, const void* v, const flo
   a.nseq = B;
   a.max_seqlen = T;
   a.T = T;
+  a.N = -1;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.d = d;
@@ -397,22 +401,24 @@ int diffattn_v2_bwd(const void* q, const void* k, const void* v, const float* la
 
 int diffattn_v2_varlen_fwd_train(const void* q, const void* k, const void* v,
                                  const float* lambda_logit, const int* cu_seqlens, int nseq,
-                                 int max_seqlen, void* out, void* o_heads, float* lse, int Hq,
-                                 int Hkv, int d, float scale, int causal, diffattn_dtype dtype,
-                                 void* stream) {
+                                 int max_seqlen, long long N, void* out, void* o_heads, float* lse,
+                                 int Hq, int Hkv, int d, float scale, int causal,
+                                 diffattn_dtype dtype, void* stream) {
   const char* fn = "diffattn_v2_varlen_fwd_train";
   if (!q || !k || !v || !lambda_logit || !out || !o_heads || !lse || !cu_seqlens)
     return fail(DIFFATTN_E_INVALID, "%s: null tensor pointer", fn);
   const int rc = v2_heads_check(fn, Hq, Hkv, d, scale, causal, dtype);
   if (rc != DIFFATTN_OK) return rc;
-  if (nseq < 0 || max_seqlen < 0)
-    return fail(DIFFATTN_E_INVALID, "%s: nseq=%d max_seqlen=%d must be >= 0", fn, nseq, max_seqlen);
+  if (nseq < 0 || max_seqlen < 0 || N < 0)
+    return fail(DIFFATTN_E_INVALID, "%s: nseq=%d max_seqlen=%d N=%lld must be >= 0", fn, nseq,
+                max_seqlen, N);
+  if (prod({N, Hq, d}) > (1LL << 40)) return fail(DIFFATTN_E_INVALID, "%s: problem too large", fn);
   const void* ptrs[] = {q, k, v, out, o_heads};
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail(DIFFATTN_E_ALIGN, "%s: tensor pointers must be 16-byte aligned", fn);
   if (!aligned4(lambda_logit) || !aligned4(lse) || !aligned4(cu_seqlens))
     return fail(DIFFATTN_E_ALIGN, "%s: lambda_logit, lse and cu_seqlens must be 4-byte aligned", fn);
-  if (nseq == 0 || max_seqlen == 0) return ok();
+  if (nseq == 0 || max_seqlen == 0 || N == 0) return ok();
   diffattn::V2Args a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -423,6 +429,7 @@ int diffattn_v2_varlen_fwd_train(const void* q, const void* k, const void* v,
   a.nseq = nseq;
   a.max_seqlen = max_seqlen;
   a.T = 0;
+  a.N = N;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.d = d;

@@ -60,6 +60,7 @@ struct V2Args {
   int nseq;                 // number of sequences (B when padded)
   int max_seqlen;           // longest sequence (T when padded)
   int T;                    // padded sequence length (unused when cu_seqlens != nullptr)
+  long long N;              // packed batches: total tokens cu_seqlens[nseq], or -1 if unknown
   int Hq, Hkv, d;
   float scale;              // softmax scale (> 0)
   int causal;
@@ -136,6 +137,9 @@ struct V1DecodeArgs {
   int split_len, nsplit;     // cache slices of split_len keys
   float lambda, lambda_init, eps, scale;
 };
+
+// Compute units of the current device (queried once per device; 256 without one).
+int device_cu_count();
 
 // V1 decode split rule shared by the workspace query and the launcher.
 void v1_decode_split(int B, int S_max, int H, int* split_len, int* nsplit);

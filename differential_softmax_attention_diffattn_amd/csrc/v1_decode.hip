@@ -311,11 +311,15 @@ hipError_t launch_dv(const V1DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// Slices of 256..4096 keys, aiming for >= 1024 workgroups, at most 512 per entry.
+// Slices of 64..4096 keys, aiming for at least four rounds of workgroups over
+// the compute units (a workgroup's 128 KB of LDS keeps it alone on its CU;
+// one round of long slices measured slower here: 2.27 vs 2.07 ms on B32
+// S32768 H12), at most 512 per entry.
 void v1_decode_split(int B, int S_max, int H, int* split_len, int* nsplit) {
   const long long units = (long long)B * (H / v1_heads_per_block(H));
+  const long long target = 4LL * device_cu_count();
   int len = 4096;
-  while (len > 256 && units * ((S_max + len - 1) / len) < 1024) len /= 2;
+  while (len > 64 && units * ((S_max + len - 1) / len) < target) len /= 2;
   int ns = S_max > 0 ? (S_max + len - 1) / len : 1;
   while (ns > 512) {
     len *= 2;

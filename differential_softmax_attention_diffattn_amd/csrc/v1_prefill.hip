@@ -193,14 +193,16 @@ __global__ __launch_bounds__(kThreads, 1) void v1_prefill_kernel(V1Args a, const
       for (int j = 0; j < TL::kKInstrPerWave; ++j)
         dma16(tile + (size_t)j * kJRows * krow_stride, k_lane_off,
               base + (rg + kRowGroups * j) * 1024);
-    } else {  // ragged last tile: clamp rows past T (they are masked)
+    } else {  // ragged last tile: clamp rows past T (they are masked); offsets
+              // relative to the tile's first key stay within 32 bits
+      const int last = T - 1 - kt * kKeys;
 #pragma unroll
       for (int j = 0; j < TL::kKInstrPerWave; ++j) {
         const int blk = rg + kRowGroups * j;
         int row, chunk;
         k_lane_chunk(blk, row, chunk);
-        const size_t e = (size_t)min(kt * kKeys + row, T - 1) * krow_stride + chunk * 8;
-        dma16(k_head, (uint32_t)(e * 2), base + blk * 1024);
+        const size_t e = (size_t)min(row, last) * krow_stride + chunk * 8;
+        dma16(tile, (uint32_t)(e * 2), base + blk * 1024);
       }
     }
   };

@@ -32,6 +32,7 @@
 #include "bwd_common.h"
 #include "device_common.h"
 #include "kernels.h"
+#include "varlen.h"
 
 namespace diffattn {
 namespace {
@@ -66,8 +67,10 @@ __host__ __device__ __forceinline__ long long pad64(long long x) { return (x + 6
 
 // Tile t (of `rows`-row tiles, numbered sequence by sequence, a sequence's
 // tiles consecutive) -> its sequence and the tile's index inside it.  Returns
-// false past the last tile.  Padded batches divide; packed ones scan
-// cu_seqlens (as the forward does).
+// false for a tile that does not exist.  Padded batches divide; packed ones
+// number the tiles by slots (varlen.h) and find the sequence by binary search.
+// A packed sequence's workspace rows start at its 64-row slot: 64 * (
+// floor(cu[s] / 64) + s), so they fit in floor(N / 64) * 64 + 64 nseq rows.
 __device__ __forceinline__ bool tile_of(const V2BwdArgs& a, long long t, int rows, SeqView& sv,
                                         int& tile) {
   if (a.cu_seqlens == nullptr) {
@@ -80,22 +83,16 @@ __device__ __forceinline__ bool tile_of(const V2BwdArgs& a, long long t, int row
     sv.ws0 = b * pad64(a.T);
     return true;
   }
-  long long ws = 0;
-  for (int s = 0; s < a.nseq; ++s) {
-    const int c0 = a.cu_seqlens[s];
-    const int len = a.cu_seqlens[s + 1] - c0;
-    const int nt = (len + rows - 1) / rows;
-    if (t < nt) {
-      tile = (int)t;
-      sv.tok0 = c0;
-      sv.L = len;
-      sv.ws0 = ws;
-      return true;
-    }
-    t -= nt;
-    ws += pad64(len);
-  }
-  return false;
+  const int s = slot_sequence(a.cu_seqlens, a.nseq, t, rows);
+  const int c0 = a.cu_seqlens[s];
+  const int len = a.cu_seqlens[s + 1] - c0;
+  const long long k = t - slot_start(a.cu_seqlens, s, rows);
+  if (k >= (len + rows - 1) / rows) return false;
+  tile = (int)k;
+  sv.tok0 = c0;
+  sv.L = len;
+  sv.ws0 = 64 * slot_start(a.cu_seqlens, s, 64);
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -646,11 +643,11 @@ hipError_t launch_d(const V2BwdArgs& a, hipStream_t stream) {
   const int pairs_per_group = (a.Hq / a.Hkv) / 2;
   const int PW = pairs_per_group % 4 == 0 ? 4 : pairs_per_group % 2 == 0 ? 2 : 1;
   const int qtile = kRows * (kWaves / PW);
-  // tiles over all sequences: padded B * ceil(T / tile); packed at most
-  // ceil(N / tile) + nseq (blocks past the last tile exit)
+  // tiles over all sequences: padded B * ceil(T / tile); packed the tile slots
+  // of varlen.h (blocks of empty slots exit)
   auto tiles = [&](int rows) -> long long {
     if (a.cu_seqlens == nullptr) return (long long)((a.T + rows - 1) / rows) * a.B;
-    return (a.N + rows - 1) / rows + a.nseq;
+    return slot_count(a.N, a.nseq, 0, rows);
   };
   const long long dq_blocks = tiles(qtile) * (a.Hq / (2 * PW));
   const long long kv_blocks = tiles(kDkvKeys) * a.Hkv;

@@ -296,19 +296,43 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// The longest power-of-two slices (256..65536 keys) that still give one
-// workgroup per compute unit (256 on gfx950; a workgroup's 128 KB of LDS keeps
-// it alone on its CU): the whole cache then streams in one round of
-// workgroups, with no round boundaries and the fewest partials (measured on
-// B64 S32768 Hkv8: 8192-key slices 6.15 TB/s, 2048 6.06, 1024 5.91, 512
-// 5.46).  The partial count per (batch, query head) is
+// Compute units of the current device (256 on MI355X), queried once per
+// device; 256 when no device can be queried (workspace queries on a host
+// without a GPU).
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static int cached[kMaxDevices] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// The longest power-of-two slices (64..65536 keys) that still give one
+// workgroup per compute unit (a workgroup's 128 KB of LDS keeps it alone on
+// its CU): the whole cache then streams in one round of workgroups, with no
+// round boundaries and the fewest partials (measured on B64 S32768 Hkv8:
+// 8192-key slices 6.15 TB/s, 2048 6.06, 1024 5.91, 512 5.46).  Small batches
+// get slices down to 64 keys (two 32-key chunks per wave) so that they still
+// fill the device.  The partial count per (batch, query head) is
 // nsplit * (8 / KV heads per workgroup) and stays <= 512.
-constexpr int kDecodeCUs = 256;
 void decode_split(int B, int S_max, int Hkv, int* split_len, int* nsplit, int* nparts) {
   const int kvw = kv_heads_per_block(Hkv);
   const long long units = (long long)B * (Hkv / kvw);
+  const int cus = device_cu_count();
   int len = 65536;
-  while (len > 256 && units * ((S_max + len - 1) / len) < kDecodeCUs) len /= 2;
+  while (len > 64 && units * ((S_max + len - 1) / len) < cus) len /= 2;
   int ns = S_max > 0 ? (S_max + len - 1) / len : 1;
   const int sub = kWaves / kvw;
   while (ns * sub > 512) {  // bound the partial count (combine kernel weight table)

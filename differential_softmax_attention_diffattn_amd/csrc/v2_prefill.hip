@@ -28,6 +28,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "varlen.h"
 
 namespace diffattn {
 namespace {
@@ -92,25 +93,21 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   // longest (last) tile first, and the pair groups of a tile are adjacent.  With
   // one pair group per KV head and 8 of them, blocks of one KV head land on one
   // XCD and that XCD's CUs work through the tiles of one sequence together,
-  // sharing its K/V tiles in L2.  Blocks past the last tile exit.
+  // sharing its K/V tiles in L2.  Packed batches number the tiles by slots
+  // (varlen.h): a binary search over cu_seqlens finds the sequence, and the
+  // blocks of empty slots exit.
   const int n_hg = a.Hq / (2 * PW);
   const int hg = blockIdx.x % n_hg;
-  int t = blockIdx.x / n_hg;
+  const int t = blockIdx.x / n_hg;
   int tok0, L, qt;
   if (a.cu_seqlens != nullptr) {
-    int seq = 0;
-    for (; seq < a.nseq; ++seq) {
-      const int len = a.cu_seqlens[seq + 1] - a.cu_seqlens[seq];
-      const int nt = (len + QTILE - 1) / QTILE;
-      if (t < nt) {
-        qt = nt - 1 - t;
-        break;
-      }
-      t -= nt;
-    }
-    if (seq == a.nseq) return;  // uniform over the block
+    const int seq = slot_sequence(a.cu_seqlens, a.nseq, t, QTILE);
     tok0 = a.cu_seqlens[seq];
     L = a.cu_seqlens[seq + 1] - tok0;
+    const int nt = (L + QTILE - 1) / QTILE;
+    const int tile = (int)(t - slot_start(a.cu_seqlens, seq, QTILE));
+    if (tile >= nt) return;  // an empty slot: uniform over the block
+    qt = nt - 1 - tile;
   } else {
     const int nt = (a.T + QTILE - 1) / QTILE;
     const int seq = t / nt;
@@ -190,14 +187,18 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
         dma16(vbase_g + jrow, v_lane_off, base + TL::kTileBytes + blk * 1024);
       }
     } else {  // ragged last tile: clamp rows past the sequence end (they are masked)
+      // (offsets relative to the tile's first key, so they stay within 32 bits
+      // for any sequence length)
+      const int last = L - 1 - kt * kKeys;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int blk = wave + j * kWaves;
         int r, kc, vc;
         lane_chunks(j, r, kc, vc);
-        const size_t key = (size_t)min(kt * kKeys + r, L - 1);
-        dma16(kbase_g, (uint32_t)((key * kv_stride + kc * 8) * 2), base + blk * 1024);
-        dma16(vbase_g, (uint32_t)((key * kv_stride + vc * 8) * 2), base + TL::kTileBytes + blk * 1024);
+        const size_t rr = (size_t)min(r, last);
+        dma16(kbase_g + tile, (uint32_t)((rr * kv_stride + kc * 8) * 2), base + blk * 1024);
+        dma16(vbase_g + tile, (uint32_t)((rr * kv_stride + vc * 8) * 2),
+              base + TL::kTileBytes + blk * 1024);
       }
     }
   };
@@ -455,9 +456,12 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
 template <int D, int PW>
 hipError_t launch_typed(const V2Args& a, hipStream_t stream) {
   constexpr int QTILE = kRows * (kWaves / PW);
-  // an upper bound on the query tiles of all sequences (exact for padded batches)
-  const int n_qt_max = (a.max_seqlen + QTILE - 1) / QTILE;
-  const long long blocks = (long long)n_qt_max * a.nseq * (a.Hq / (2 * PW));
+  // query tiles: B x ceil(T / QTILE) for padded batches, the tile slots of
+  // varlen.h for packed ones
+  const long long tiles = a.cu_seqlens != nullptr
+                              ? slot_count(a.N, a.nseq, a.max_seqlen, QTILE)
+                              : (long long)((a.T + QTILE - 1) / QTILE) * a.nseq;
+  const long long blocks = tiles * (a.Hq / (2 * PW));
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.causal)

@@ -201,8 +201,15 @@ V2_VARLEN = V2Workload(
     d=128, std=INV_SQRT_128, seeds=(502, 503, 504, 505), logit_mean=2.0, logit_std=1.0,
     lengths=tuple(varlen_lengths(VARLEN_TOTAL, VARLEN_LO, VARLEN_HI, VARLEN_SEED)))
 
+# One sequence decoding against the full 32768-entry cache (a small-batch decode step).
+V2_DECODE_B1 = V2_DECODE.with_shape(name="v2_decode_bf16_b1_s32768_hq64_hkv8_d128", B=1)
+
+# A packed batch of many short sequences: 2048 x 32 tokens (65536 in all).
+V2_VARLEN_SHORT = V2_VARLEN.with_shape(name="v2_varlen_bf16_causal_2048x32_hq64_hkv8_d128",
+                                       lengths=(32,) * 2048)
+
 WORKLOADS = {w.name: w for w in (V1_FP32_SMALL, V1_BF16, V2_PREFILL, V2_DECODE, V2_VARLEN,
-                                  V1_DECODE)}
+                                  V1_DECODE, V2_DECODE_B1, V2_VARLEN_SHORT)}
 
 
 # ---------------------------------------------------------------------------

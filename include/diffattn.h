@@ -174,9 +174,10 @@ DIFFATTN_API size_t diffattn_v1_bwd_workspace_bytes(int B, int T, int H, int d, 
  * Packed batch (cu_seqlens != NULL): nseq sequences; sequence s owns tokens
  *   cu_seqlens[s] .. cu_seqlens[s+1]-1 of the packed tensors and attends only
  *   within itself.  cu_seqlens is a DEVICE int32 array [nseq + 1], non-
- *   decreasing, starting at 0; max_seqlen must be >= every sequence length
- *   (rows beyond it are not computed).  Shapes as above with [B, T] replaced
- *   by [total tokens]; B and T are ignored.
+ *   decreasing, starting at 0.  Shapes as above with [B, T] replaced by
+ *   [N total tokens]; B is ignored and T is N = cu_seqlens[nseq] (it sizes the
+ *   launch), or 0 when the caller does not know N; then nseq * max_seqlen
+ *   bounds the tokens, and max_seqlen must be >= every sequence length.
  *
  *   scale : softmax scale; <= 0 selects 1/sqrt(d).
  * Supported: dtype DIFFATTN_BF16, d in {64, 128}.
@@ -247,6 +248,7 @@ DIFFATTN_API size_t diffattn_v2_bwd_workspace_bytes(int B, int T, int Hq, int Hk
  *                cu_seqlens[nseq] = N (not checked: it lives on the device);
  *                every token's gradients are written once by its sequence
  *   max_seqlen : the longest sequence (forward only; an upper bound is fine)
+ *   N          : the packed token count cu_seqlens[nseq] (sizes the launches)
  *   q, o_heads, dq : [N, Hq, d];  k, v, dk, dv : [N, Hkv, d];
  *   lambda_logit, dlambda_logit : [N, Hq/2];  lse : [N, Hq];  out, dout : [N, Hq/2, d]
  *   workspace  : at least diffattn_v2_varlen_bwd_workspace_bytes(N, nseq, ...)
@@ -256,9 +258,9 @@ DIFFATTN_API size_t diffattn_v2_bwd_workspace_bytes(int B, int T, int Hq, int Hk
  */
 DIFFATTN_API int diffattn_v2_varlen_fwd_train(const void* q, const void* k, const void* v,
                                  const float* lambda_logit, const int* cu_seqlens, int nseq,
-                                 int max_seqlen, void* out, void* o_heads, float* lse, int Hq,
-                                 int Hkv, int d, float scale, int causal, diffattn_dtype dtype,
-                                 void* stream);
+                                 int max_seqlen, long long N, void* out, void* o_heads,
+                                 float* lse, int Hq, int Hkv, int d, float scale, int causal,
+                                 diffattn_dtype dtype, void* stream);
 DIFFATTN_API int diffattn_v2_varlen_bwd(const void* q, const void* k, const void* v,
                            const float* lambda_logit, const int* cu_seqlens, int nseq,
                            const void* o_heads, const float* lse, const void* dout, float* dq,

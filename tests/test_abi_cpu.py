@@ -332,7 +332,7 @@ def test_v2_varlen_backward_workspace_query(lib):
 
 
 def test_v2_varlen_train_forward_rejects_bad_arguments(lib):
-    f = lambda **kw: lib.diffattn_v2_varlen_fwd_train(*[{**dict(q=P, k=P, v=P, lg=P, cu=P, nseq=2, ms=64, out=P, oh=P, lse=P, Hq=16, Hkv=2, d=128, scale=0.0, causal=1, dt=BF16, st=None), **kw}[n] for n in ("q", "k", "v", "lg", "cu", "nseq", "ms", "out", "oh", "lse", "Hq", "Hkv", "d", "scale", "causal", "dt", "st")])
+    f = lambda **kw: lib.diffattn_v2_varlen_fwd_train(*[{**dict(q=P, k=P, v=P, lg=P, cu=P, nseq=2, ms=64, N=100, out=P, oh=P, lse=P, Hq=16, Hkv=2, d=128, scale=0.0, causal=1, dt=BF16, st=None), **kw}[n] for n in ("q", "k", "v", "lg", "cu", "nseq", "ms", "N", "out", "oh", "lse", "Hq", "Hkv", "d", "scale", "causal", "dt", "st")])
     assert f(cu=None) == E_INVALID
     assert f(oh=None) == E_INVALID
     assert f(nseq=-1) == E_INVALID
