@@ -11,6 +11,8 @@ arithmetic runs in the library's kernels; there is no fallback path.
     v2_fwd      V2: GQA attention over 2h query heads, O_even - sigmoid(logit) O_odd
                 (padded or packed/varlen batches)
     v2_decode   V2 decode step against a KV cache
+    v2_decode_noalloc
+                the same without a workspace (partials in a library-owned array)
     v1_decode   V1 decode step against cached K1, K2 and V (with the norm)
     v2_fwd_train / v2_bwd
                 V2 training forward (also keeps per-head O and log-sum-exp) and
@@ -36,6 +38,7 @@ __all__ = [
     "v1_fwd",
     "v2_fwd",
     "v2_decode",
+    "v2_decode_noalloc",
     "v1_decode",
     "v2_fwd_train",
     "v2_bwd",
@@ -358,6 +361,42 @@ def v2_decode(q, k_cache, v_cache, logit, cache_len=None, scale: float | None = 
             _ptr(workspace), ws_bytes, B, S_max, Hq, Hkv, d, float(scale or 0.0), DIFFATTN_BF16,
             _stream(dev))
     _lib.check("diffattn_v2_decode", rc)
+    return out
+
+
+def v2_decode_noalloc(q, k_cache, v_cache, logit, cache_len=None, scale: float | None = None,
+                      out=None):
+    """v2_decode with the partial results in the library's own device array (no
+    workspace; for callers that cannot allocate).  ``out`` may be preallocated;
+    calls that overlap on one GPU race (they share the array)."""
+    torch = _torch()
+    dev = q.device
+    _check_tensor("q", q, dtype=torch.bfloat16, dim=3)
+    _check_tensor("k_cache", k_cache, dtype=torch.bfloat16, dim=4, device=dev)
+    _check_tensor("v_cache", v_cache, dtype=torch.bfloat16, dim=4, device=dev)
+    _check_tensor("logit", logit, dtype=torch.float32, dim=2, device=dev)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    B, Hq, d = q.shape
+    _, S_max, Hkv, dk = k_cache.shape
+    if k_cache.shape[0] != B or dk != d:
+        raise ValueError("cache shape does not match q")
+    if Hq % 2 or tuple(logit.shape) != (B, Hq // 2):
+        raise ValueError("Hq must be even and logit must have shape [B, Hq/2]")
+    if cache_len is not None:
+        _check_tensor("cache_len", cache_len, dtype=torch.int32, dim=1, device=dev)
+        if cache_len.shape[0] != B:
+            raise ValueError("cache_len must have B entries")
+    if out is None:
+        out = torch.empty((B, Hq // 2, d), dtype=torch.bfloat16, device=dev)
+    _check_tensor("out", out, dtype=torch.bfloat16, dim=3, device=dev)
+    if tuple(out.shape) != (B, Hq // 2, d):
+        raise ValueError("out has the wrong shape")
+    with torch.cuda.device(dev):
+        rc = _lib.load().diffattn_v2_decode_noalloc(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(logit), _ptr(out), B,
+            S_max, Hq, Hkv, d, float(scale or 0.0), DIFFATTN_BF16, _stream(dev))
+    _lib.check("diffattn_v2_decode_noalloc", rc)
     return out
 
 

@@ -54,6 +54,8 @@ SIGNATURES = {
     "diffattn_v2_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _i, _i, _f, _i,
                                 _vp]),
     "diffattn_v2_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "diffattn_v2_decode_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
+                                        _vp]),
     "diffattn_v1_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _i,
                                 _i, _f, _f, _f, _i, _vp]),
     "diffattn_v1_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),

@@ -573,11 +573,14 @@ size_t diffattn_v2_decode_workspace_bytes(int B, int S_max, int Hq, int Hkv, int
   return n < 0 ? 0 : (size_t)n * sizeof(float);
 }
 
-int diffattn_v2_decode(const void* q, const void* k_cache, const void* v_cache,
-                       const int* cache_len, const float* lambda_logit, void* out,
-                       void* workspace, size_t workspace_bytes, int B, int S_max, int Hq,
-                       int Hkv, int d, float scale, diffattn_dtype dtype, void* stream) {
-  const char* fn = "diffattn_v2_decode";
+}  // extern "C"
+
+namespace {
+
+// Checks of the V2 decode entry points, before any launch; DIFFATTN_OK or a code.
+int v2_decode_check(const char* fn, const void* q, const void* k_cache, const void* v_cache,
+                    const int* cache_len, const float* lambda_logit, const void* out, int B,
+                    int S_max, int Hq, int Hkv, int d, float scale, diffattn_dtype dtype) {
   if (!q || !k_cache || !v_cache || !lambda_logit || !out)
     return fail(DIFFATTN_E_INVALID, "%s: null tensor pointer", fn);
   if (B < 0 || S_max < 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
@@ -604,12 +607,12 @@ int diffattn_v2_decode(const void* q, const void* k_cache, const void* v_cache,
     if (!aligned16(p)) return fail(DIFFATTN_E_ALIGN, "%s: tensor pointers must be 16-byte aligned", fn);
   if (!aligned4(lambda_logit) || (cache_len && !aligned4(cache_len)))
     return fail(DIFFATTN_E_ALIGN, "%s: lambda_logit and cache_len must be 4-byte aligned", fn);
-  if (B == 0) return ok();
-  const size_t need = diffattn_v2_decode_workspace_bytes(B, S_max, Hq, Hkv, d);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(DIFFATTN_E_WORKSPACE, "%s: workspace of %zu bytes required (got %zu%s)", fn, need,
-                workspace_bytes, workspace ? "" : ", NULL");
-  if (!aligned16(workspace)) return fail(DIFFATTN_E_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  return DIFFATTN_OK;
+}
+
+int v2_decode_launch(const char* fn, const void* q, const void* k_cache, const void* v_cache,
+                     const int* cache_len, const float* lambda_logit, void* out, void* partial,
+                     int B, int S_max, int Hq, int Hkv, int d, float scale, void* stream) {
   diffattn::DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k_cache = static_cast<const uint16_t*>(k_cache);
@@ -617,7 +620,7 @@ int diffattn_v2_decode(const void* q, const void* k_cache, const void* v_cache,
   a.cache_len = cache_len;
   a.logit = lambda_logit;
   a.out = static_cast<uint16_t*>(out);
-  a.partial = static_cast<float*>(workspace);
+  a.partial = static_cast<float*>(partial);
   a.B = B;
   a.S_max = S_max;
   a.Hq = Hq;
@@ -627,6 +630,53 @@ int diffattn_v2_decode(const void* q, const void* k_cache, const void* v_cache,
   diffattn::decode_split(B, S_max, Hkv, &a.split_len, &a.nsplit, &nparts);
   a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
   return from_hip(diffattn::launch_v2_decode(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int diffattn_v2_decode(const void* q, const void* k_cache, const void* v_cache,
+                       const int* cache_len, const float* lambda_logit, void* out,
+                       void* workspace, size_t workspace_bytes, int B, int S_max, int Hq,
+                       int Hkv, int d, float scale, diffattn_dtype dtype, void* stream) {
+  const char* fn = "diffattn_v2_decode";
+  const int rc = v2_decode_check(fn, q, k_cache, v_cache, cache_len, lambda_logit, out, B, S_max,
+                                 Hq, Hkv, d, scale, dtype);
+  if (rc != DIFFATTN_OK) return rc;
+  if (B == 0) return ok();
+  const size_t need = diffattn_v2_decode_workspace_bytes(B, S_max, Hq, Hkv, d);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DIFFATTN_E_WORKSPACE, "%s: workspace of %zu bytes required (got %zu%s)", fn, need,
+                workspace_bytes, workspace ? "" : ", NULL");
+  if (!aligned16(workspace)) return fail(DIFFATTN_E_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  return v2_decode_launch(fn, q, k_cache, v_cache, cache_len, lambda_logit, out, workspace, B,
+                          S_max, Hq, Hkv, d, scale, stream);
+}
+
+int diffattn_v2_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                               const int* cache_len, const float* lambda_logit, void* out, int B,
+                               int S_max, int Hq, int Hkv, int d, float scale,
+                               diffattn_dtype dtype, void* stream) {
+  const char* fn = "diffattn_v2_decode_noalloc";
+  const int rc = v2_decode_check(fn, q, k_cache, v_cache, cache_len, lambda_logit, out, B, S_max,
+                                 Hq, Hkv, d, scale, dtype);
+  if (rc != DIFFATTN_OK) return rc;
+  if (B == 0) return ok();
+  const size_t need = diffattn_v2_decode_workspace_bytes(B, S_max, Hq, Hkv, d);
+  const size_t limit = diffattn::decode_noalloc_scratch_bytes();
+  static_assert(DIFFATTN_V2_DECODE_NOALLOC_MAX_BYTES == (size_t(32) << 20),
+                "the header's limit is the array's size");
+  if (need > limit)
+    return fail(DIFFATTN_E_UNSUPPORTED,
+                "%s: these sizes need %zu bytes of partial results, above the %zu-byte array of "
+                "this entry point; use diffattn_v2_decode with a workspace",
+                fn, need, limit);
+  hipError_t e = hipSuccess;
+  void* scratch = diffattn::decode_noalloc_scratch(&e);
+  if (scratch == nullptr) return from_hip(e == hipSuccess ? hipErrorInvalidSymbol : e, fn);
+  return v2_decode_launch(fn, q, k_cache, v_cache, cache_len, lambda_logit, out, scratch, B,
+                          S_max, Hq, Hkv, d, scale, stream);
 }
 
 int diffattn_v2_lambda_proj(const void* x, const void* w_lambda, float* logits, long long N,

@@ -165,6 +165,11 @@ long long v2_bwd_varlen_rows(long long N, int nseq);
 size_t v2_bwd_workspace_bytes_rows(long long Np, int Hq);
 hipError_t launch_v2_backward(const V2BwdArgs& a, hipStream_t stream);
 hipError_t launch_v2_decode(const DecodeArgs& a, hipStream_t stream);
+// The V2 decode's library-owned partials (for callers that cannot allocate):
+// its size, and its device address on the current device (looked up once per
+// device; nullptr and the HIP error in *err on failure).
+size_t decode_noalloc_scratch_bytes();
+void* decode_noalloc_scratch(hipError_t* err);
 hipError_t launch_lambda_proj(const LambdaProjArgs& a, hipStream_t stream);
 hipError_t launch_gemm_tn(const GemmArgs& a, hipStream_t stream);
 

@@ -18,6 +18,8 @@
 // the partials with log-sum-exp weights and applies the pair subtraction.
 #include <math.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -348,6 +350,48 @@ hipError_t launch_v2_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.d == 128) return launch_d<128>(a, stream);
   if (a.d == 64) return launch_d<64>(a, stream);
   return hipErrorInvalidValue;
+}
+
+// Partial results of the decode entry point that allocates nothing
+// (diffattn_v2_decode_noalloc).  Every GPU the library runs on holds its own
+// copy until the process ends, and every such call on that GPU uses it, so
+// calls that overlap on one GPU race.  The split kernel writes every record
+// the combine kernel reads (empty slices included), so nothing in it needs to
+// start at zero.  Host code never uses the array's name, which is only a
+// host-side stand-in: it uses the device address looked up below.
+namespace {
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+}  // namespace
+
+size_t decode_noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+void* decode_noalloc_scratch(hipError_t* err) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with this device current
+    if (e != hipSuccess || p == nullptr) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    ptrs[dev] = p;
+  }
+  *err = hipSuccess;
+  return ptrs[dev];
 }
 
 }  // namespace diffattn

@@ -327,6 +327,28 @@ DIFFATTN_API int diffattn_v2_decode(const void* q, const void* k_cache, const vo
 DIFFATTN_API size_t diffattn_v2_decode_workspace_bytes(int B, int S_max, int Hq, int Hkv, int d);
 
 /*
+ * diffattn_v2_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and errors as diffattn_v2_decode, minus
+ * the workspace: the per-slice partial results go to an array the library
+ * owns, DIFFATTN_V2_DECODE_NOALLOC_MAX_BYTES on each GPU it runs on, held
+ * until the process ends.  Sizes whose diffattn_v2_decode_workspace_bytes()
+ * exceeds that limit are rejected with DIFFATTN_E_UNSUPPORTED (at Hq 64, d 128
+ * that is above roughly B = 990 unsplit sequences; a split cache needs at most
+ * about 34 KB per workgroup of the launch).  The call allocates nothing (no
+ * hipMalloc, no allocating library routine); its first call on a device looks
+ * up that device's array.  All calls on one GPU share the array, so calls
+ * that overlap on one GPU (different streams, or threads) race: serialise
+ * them.  Nothing in the array needs clearing between calls.
+ */
+#define DIFFATTN_V2_DECODE_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+DIFFATTN_API int diffattn_v2_decode_noalloc(const void* q, const void* k_cache,
+                                            const void* v_cache, const int* cache_len,
+                                            const float* lambda_logit, void* out, int B,
+                                            int S_max, int Hq, int Hkv, int d, float scale,
+                                            diffattn_dtype dtype, void* stream);
+
+/*
  * V2 coefficient logits [P2 §1]: the coefficient that scales the second
  * head of each pair is projected from the layer input, one per token and
  * pair, and passes through a sigmoid where it is used (diffattn_v2_fwd and

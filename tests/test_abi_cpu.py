@@ -339,3 +339,20 @@ def test_v2_varlen_train_forward_rejects_bad_arguments(lib):
     assert f(Hq=6) == E_INVALID
     assert f(oh=P + 8) == E_ALIGN
     assert f(nseq=0) == 0
+
+
+def test_v2_decode_noalloc_rejects_bad_and_oversize_arguments(lib):
+    # the checks run before the library's array is looked up or anything launches
+    f = lambda **kw: lib.diffattn_v2_decode_noalloc(*[{**dict(
+        q=P, k=P, v=P, cl=None, lg=P, out=P, B=4, S=4096, Hq=64, Hkv=8, d=128, scale=0.0, dt=BF16,
+        st=None), **kw}[n] for n in ("q", "k", "v", "cl", "lg", "out", "B", "S", "Hq", "Hkv", "d",
+                                     "scale", "dt", "st")])
+    assert f(q=None) == E_INVALID
+    assert f(Hq=6, Hkv=2) == E_INVALID
+    assert f(d=96) == E_UNSUPPORTED
+    assert f(out=P + 8) == E_ALIGN
+    assert f(B=0) == 0
+    # partials beyond the library's 32 MiB array: rejected with a message
+    assert lib.diffattn_v2_decode_workspace_bytes(2048, 4096, 64, 8, 128) > 32 << 20
+    assert f(B=2048) == E_UNSUPPORTED
+    assert b"diffattn_v2_decode with a workspace" in lib.diffattn_last_error()
