@@ -4,6 +4,11 @@ Imported by the tests, the smoke check and the benchmark's CPU-baseline leg;
 never by the library itself.
 """
 from .diffattn_oracle import (  # noqa: F401
+    gda_combine,
+    gda_decode,
+    gda_forward,
+    gda_heads,
+    gda_sequence,
     gqa_kv_head,
     lambda_init,
     out_projection,

@@ -552,6 +552,85 @@ def v2_backward_key_rows(q, k, v, logit, dout, keys, kv_heads=None, causal: bool
 
 
 # ---------------------------------------------------------------------------
+# Grouped Differential Attention (unequal signal : noise head counts)
+# ---------------------------------------------------------------------------
+#
+# The blog "Differential Transformer | ICLR 2025 Oral" (section "같은 문제,
+# 다른 접근") names Grouped Differential Attention as the follow-up that splits
+# the heads unevenly, r signal heads per noise head (3:1 or 4:1), and gives no
+# formula.  Reading (the V2 form of the subtraction, which the V2 summary §1
+# gives for r = 1): the query heads form blocks of r + 1 consecutive heads, r
+# signal heads then one noise head, every block inside one GQA group (so its
+# heads share K and V, as V2 requires of a pair); each signal head subtracts
+# its block's noise head, scaled by the sigmoid of its own per-token
+# coefficient.  r = 1 is V2.
+
+def gda_heads(Hq: int, ratio: int):
+    """(signal head, noise head) query-head indices of each output head s."""
+    if ratio < 1 or Hq % (ratio + 1):
+        raise ValueError("Hq must be a multiple of ratio + 1")
+    nout = Hq // (ratio + 1) * ratio
+    sig = [(s // ratio) * (ratio + 1) + s % ratio for s in range(nout)]
+    noise = [(s // ratio) * (ratio + 1) + ratio for s in range(nout)]
+    return sig, noise
+
+
+def gda_combine(O, logit, ratio: int) -> np.ndarray:
+    """out[:, s] = O[:, sig(s)] - sigmoid(logit[:, s]) * O[:, noise(s)].
+
+    O: [R, Hq, d]; logit: [R, Hq r / (r + 1)].  Returns [R, Hq r / (r + 1), d].
+    """
+    O, logit = _f64(O), _f64(logit)
+    sig, noise = gda_heads(O.shape[1], ratio)
+    return O[:, sig] - sigmoid(logit)[..., None] * O[:, noise]
+
+
+def gda_sequence(q, k, v, logit, ratio: int, rows=None, causal: bool = True,
+                 scale: float | None = None) -> np.ndarray:
+    """One sequence: q [T, Hq, d], k/v [T, Hkv, d], logit [T, Hq r / (r + 1)]."""
+    q = _f64(q)
+    Hq, Hkv = q.shape[1], _f64(k).shape[1]
+    if (Hq // Hkv) % (ratio + 1):
+        raise ValueError("each block of ratio + 1 heads must lie in one GQA group")
+    logit = _f64(logit)
+    rows = np.arange(logit.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    O = v2_heads(q, k, v, rows, causal, scale)
+    return gda_combine(O, logit[rows], ratio)
+
+
+def gda_forward(q, k, v, logit, ratio: int, causal: bool = True, scale: float | None = None,
+                rows=None) -> np.ndarray:
+    """Padded batch: q [B, T, Hq, d], k/v [B, T, Hkv, d], logit [B, T, nout] -> [B, R, nout, d]."""
+    q, k, v, logit = _f64(q), _f64(k), _f64(v), _f64(logit)
+    B, T = q.shape[:2]
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    return np.stack([gda_sequence(q[b], k[b], v[b], logit[b], ratio, rows, causal, scale)
+                     for b in range(B)])
+
+
+def gda_decode(q, k_cache, v_cache, logit, ratio: int, cache_len=None,
+               scale: float | None = None) -> np.ndarray:
+    """One decode step: q [B, Hq, d], caches [B, S, Hkv, d], logit [B, nout] -> [B, nout, d].
+
+    Entry b attends to cache positions 0 .. cache_len[b]-1 (all S when None);
+    an entry with no cached positions gives zeros.
+    """
+    q, logit = _f64(q), _f64(logit)
+    B, Hq = q.shape[:2]
+    S = k_cache.shape[1]
+    nout = Hq // (ratio + 1) * ratio
+    out = np.zeros((B, nout, v_cache.shape[-1]))
+    for b in range(B):
+        n = S if cache_len is None else int(np.asarray(cache_len)[b])
+        if n <= 0:
+            continue
+        O = v2_heads(q[b][None], _f64(k_cache[b, :n]), _f64(v_cache[b, :n]), rows=np.array([0]),
+                     causal=False, scale=scale)
+        out[b] = gda_combine(O, logit[b][None], ratio)[0]
+    return out
+
+
+# ---------------------------------------------------------------------------
 # The projections on either side of the V2 attention
 # ---------------------------------------------------------------------------
 

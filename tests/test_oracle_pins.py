@@ -713,3 +713,91 @@ def test_output_projection_saving_matches_page_figures():
         assert abs(c["o_saving_frac_of_base"] - fig["attention_params_saved_frac"]) <= fig["tolerance_abs"] + 2 * hkv / (4 * h)
     small_kv = oracle.v2_attention_param_counts(4096, 32, 1, 128)
     assert abs(small_kv["o_saving_frac_of_base"] - fig["attention_params_saved_frac"]) < fig["tolerance_abs"]
+
+
+# ---------------------------------------------------------------------------
+# Grouped Differential Attention (the reading in the oracle: blocks of r
+# signal heads and one noise head inside a GQA group)
+# ---------------------------------------------------------------------------
+
+def _gda_brute_row(q, k, v, logit, i, g, r, scale):
+    """Scalar loops with math.exp for query row i of one sequence."""
+    Hq = len(q[0])
+    d = len(q[0][0])
+    O = []
+    for j in range(Hq):
+        kv = j // g
+        s = [sum(q[i][j][c] * k[t][kv][c] for c in range(d)) * scale for t in range(i + 1)]
+        e = [math.exp(x - max(s)) for x in s]
+        O.append([sum(e[t] / sum(e) * v[t][kv][c] for t in range(i + 1)) for c in range(d)])
+    res = []
+    for s_ in range(Hq // (r + 1) * r):
+        blk, pos = divmod(s_, r)
+        sg = 1.0 / (1.0 + math.exp(-logit[i][s_]))
+        res.append([O[blk * (r + 1) + pos][c] - sg * O[blk * (r + 1) + r][c] for c in range(d)])
+    return res
+
+
+@pytest.mark.parametrize("ratio,Hq,Hkv", [(3, 8, 2), (4, 10, 2), (3, 8, 1)])
+def test_gda_brute_force_tiny(ratio, Hq, Hkv):
+    r = rng(60 + ratio + Hq)
+    T, d = 5, 3
+    q, k, v = r.normal(size=(1, T, Hq, d)), r.normal(size=(1, T, Hkv, d)), r.normal(size=(1, T, Hkv, d))
+    nout = Hq // (ratio + 1) * ratio
+    logit = r.normal(size=(1, T, nout))
+    out = oracle.gda_forward(q, k, v, logit, ratio)
+    assert out.shape == (1, T, nout, d)
+    for i in range(T):
+        ref = _gda_brute_row(q[0].tolist(), k[0].tolist(), v[0].tolist(), logit[0].tolist(), i,
+                             Hq // Hkv, ratio, 1.0 / math.sqrt(d))
+        np.testing.assert_allclose(out[0, i], np.array(ref), rtol=1e-11, atol=1e-12)
+
+
+def test_gda_one_to_one_is_v2():
+    q, k, v, logit = v2_rand(61, T=17, Hq=8, Hkv=2)
+    np.testing.assert_array_equal(oracle.gda_forward(q, k, v, logit, 1), oracle.v2_forward(q, k, v, logit))
+
+
+def test_gda_sigmoid_zero_is_gqa_attention_of_the_signal_heads():
+    # logit -800: sigmoid is 0 to double precision, so every output head is the
+    # plain GQA attention of its signal head (torch SDPA, float64, enable_gqa)
+    r = rng(62)
+    T, Hq, Hkv, d, ratio = 19, 8, 2, 8, 3
+    q, k, v = r.normal(size=(1, T, Hq, d)), r.normal(size=(1, T, Hkv, d)), r.normal(size=(1, T, Hkv, d))
+    logit = np.full((1, T, 6), -800.0)
+    out = oracle.gda_forward(q, k, v, logit, ratio)
+    ref = sdpa(q[0], k[0], v[0], True, gqa=True)          # [T, Hq, d]
+    sig, _ = oracle.gda_heads(Hq, ratio)
+    assert sig == [0, 1, 2, 4, 5, 6]
+    np.testing.assert_allclose(out[0], ref[:, sig], rtol=0, atol=1e-13)
+
+
+def test_gda_identical_signal_and_noise_heads_give_zero():
+    # every head of a block carries the same query and sigmoid(40) = 1 - 4e-18:
+    # the subtraction cancels (to rounding of the sigmoid)
+    r = rng(63)
+    T, Hkv, d, ratio = 12, 2, 4, 4
+    q1 = r.normal(size=(1, T, Hkv * 2, 1, d))
+    q = np.repeat(q1, ratio + 1, axis=3).reshape(1, T, Hkv * 2 * (ratio + 1), d)
+    k, v = r.normal(size=(1, T, Hkv, d)), r.normal(size=(1, T, Hkv, d))
+    logit = np.full((1, T, Hkv * 2 * ratio), 40.0)
+    out = oracle.gda_forward(q, k, v, logit, ratio)
+    assert np.abs(out).max() <= 1e-15 * np.abs(v).max() * 10
+
+
+def test_gda_decode_is_the_last_prefill_row():
+    r = rng(64)
+    T, Hq, Hkv, d, ratio = 23, 8, 2, 8, 3
+    q, k, v = r.normal(size=(1, T, Hq, d)), r.normal(size=(1, T, Hkv, d)), r.normal(size=(1, T, Hkv, d))
+    logit = r.normal(size=(1, T, 6))
+    pre = oracle.gda_forward(q, k, v, logit, ratio)
+    dec = oracle.gda_decode(q[:, -1], k, v, logit[:, -1], ratio)
+    np.testing.assert_allclose(dec[0], pre[0, -1], rtol=0, atol=1e-13)
+    # an empty cache gives zeros
+    assert np.all(oracle.gda_decode(q[:, -1], k, v, logit[:, -1], ratio, cache_len=np.array([0])) == 0)
+
+
+def test_gda_rejects_blocks_across_gqa_groups():
+    q, k, v, logit = v2_rand(65, T=4, Hq=8, Hkv=4)   # groups of 2 heads: a 4-head block cannot fit
+    with pytest.raises(ValueError):
+        oracle.gda_forward(q, k, v, np.zeros((1, 4, 6)), 3)
