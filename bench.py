@@ -44,7 +44,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
 LEGS = ["v1", "v2", "varlen", "varlen_short", "decode", "decode_b1", "v1dec", "bwd", "vbwd",
-        "v1bwd", "lproj", "proj"]
+        "v1bwd", "lproj", "proj", "gda", "gda_dec"]
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "differential_softmax_attention_diffattn_amd", "csrc")
@@ -58,6 +58,8 @@ SOURCES = {
     "varlen_short": _V2P,
     "decode": ("v2_decode.hip", "device_common.h", "kernels.h"),
     "decode_b1": ("v2_decode.hip", "device_common.h", "kernels.h"),
+    "gda": _V2P,
+    "gda_dec": ("v2_decode.hip", "device_common.h", "kernels.h"),
     "bwd": _V2B,
     "vbwd": _V2B,
     "v1dec": ("v1_decode.hip", "device_common.h", "kernels.h"),
@@ -341,6 +343,34 @@ def main():
         torch.cuda.empty_cache()
         if cpu and leg == "decode":
             secondary[key]["cpu_baseline"] = cpu_baseline_decode(w)
+    if want("gda"):
+        # grouped variant, 3 signal heads per noise head: the algorithmic count
+        # attends each of the Hq query heads once; the kernel recomputes a
+        # block's noise head for each of its signal heads (2 Hs head passes)
+        w = inp.GDA_PREFILL_R3
+        log(f"[bench] {w.name}")
+        x = inp.v2_inputs(w, device=dev)
+        o = torch.empty((w.B, w.T, w.n_out, w.d), dtype=torch.bfloat16, device=dev)
+        mfma_leg("gda_prefill", w.name,
+                 lambda: da.gda_fwd(x["q"], x["k"], x["v"], x["logit"], w.ratio, out=o),
+                 w.B * v2_flops_seq(w.T, w.Hq, w.d),
+                 {"ratio": w.ratio, "executed_flop": w.B * v2_flops_seq(w.T, 2 * w.n_out, w.d),
+                  "traffic": hbm_traffic("gda", w.name)})
+        del x, o
+        torch.cuda.empty_cache()
+    if want("gda_dec"):
+        w = inp.GDA_DECODE_R3
+        log(f"[bench] {w.name}")
+        x = inp.decode_inputs(w, device=dev)
+        o = torch.empty((w.B, w.n_out, w.d), dtype=torch.bfloat16, device=dev)
+        wsd = torch.empty(da.gda_decode_workspace_bytes(w.B, w.S, w.Hq, w.Hkv, w.d, w.ratio),
+                          dtype=torch.uint8, device=dev)
+        f = lambda: da.gda_decode(x["q"], x["k_cache"], x["v_cache"], x["logit"], w.ratio, out=o,
+                                  workspace=wsd)
+        hbm_leg("gda_decode", w.name, f, decode_bytes(w.B, w.S, w.Hkv, w.d),
+                {"ratio": w.ratio, "traffic": hbm_traffic("gda_dec", w.name)})
+        del x, o, wsd
+        torch.cuda.empty_cache()
     if want("v1dec"):
         w = inp.V1_DECODE
         log(f"[bench] {w.name}")

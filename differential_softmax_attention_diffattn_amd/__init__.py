@@ -39,6 +39,8 @@ __all__ = [
     "v2_fwd",
     "v2_decode",
     "v2_decode_noalloc",
+    "gda_fwd",
+    "gda_decode",
     "v1_decode",
     "v2_fwd_train",
     "v2_bwd",
@@ -51,6 +53,7 @@ __all__ = [
     "lambda_init",
     "v1_workspace_bytes",
     "v2_decode_workspace_bytes",
+    "gda_decode_workspace_bytes",
     "v1_decode_workspace_bytes",
     "v2_bwd_workspace_bytes",
     "v1_bwd_workspace_bytes",
@@ -264,14 +267,14 @@ def v1_bwd(q1, k1, q2, k2, v, o1, o2, lse, dy, lam: float, lambda_init: float,
     return dq1, dk1, dq2, dk2, dvv, dlam, dw
 
 
-def v2_fwd(q, k, v, logit, cu_seqlens=None, max_seqlen=None, causal: bool = True,
-           scale: float | None = None, out=None):
-    """DIFF V2 forward.
+def _signal_heads(Hq: int, ratio: int) -> int:
+    """Output heads of blocks of ``ratio`` signal heads and one noise head."""
+    if ratio < 1 or Hq % (ratio + 1):
+        raise ValueError(f"Hq={Hq} must be a multiple of ratio + 1 = {ratio + 1}")
+    return Hq // (ratio + 1) * ratio
 
-    Padded: q [B,T,Hq,d], k/v [B,T,Hkv,d] bf16, logit [B,T,Hq/2] fp32 -> out [B,T,Hq/2,d] bf16.
-    Packed: q [N,Hq,d], k/v [N,Hkv,d], logit [N,Hq/2], cu_seqlens int32 [nseq+1] on the GPU and
-    ``max_seqlen`` (host int, >= every sequence length) -> out [N,Hq/2,d].
-    """
+
+def _prefill(fn, ratio, q, k, v, logit, cu_seqlens, max_seqlen, causal, scale, out):
     torch = _torch()
     dev = q.device
     packed = cu_seqlens is not None
@@ -287,14 +290,13 @@ def v2_fwd(q, k, v, logit, cu_seqlens=None, max_seqlen=None, causal: bool = True
     Hkv = k.shape[-2]
     if tuple(k.shape[:nd - 2]) != lead or k.shape[-1] != d:
         raise ValueError("k/v shape does not match q")
-    if Hq % 2:
-        raise ValueError("Hq must be even")
-    if tuple(logit.shape) != lead + (Hq // 2,):
-        raise ValueError(f"logit must have shape {lead + (Hq // 2,)}")
+    Hs = _signal_heads(Hq, ratio)
+    if tuple(logit.shape) != lead + (Hs,):
+        raise ValueError(f"logit must have shape {lead + (Hs,)}")
     if out is None:
-        out = torch.empty(lead + (Hq // 2, d), dtype=torch.bfloat16, device=dev)
+        out = torch.empty(lead + (Hs, d), dtype=torch.bfloat16, device=dev)
     _check_tensor("out", out, dtype=torch.bfloat16, dim=nd, device=dev)
-    if tuple(out.shape) != lead + (Hq // 2, d):
+    if tuple(out.shape) != lead + (Hs, d):
         raise ValueError("out has the wrong shape")
     if packed:
         _check_tensor("cu_seqlens", cu_seqlens, dtype=torch.int32, dim=1, device=dev)
@@ -306,23 +308,43 @@ def v2_fwd(q, k, v, logit, cu_seqlens=None, max_seqlen=None, causal: bool = True
         nseq, max_seqlen = 0, 0
         B, T = lead
     lib = _lib.load()
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(logit), _ptr(out), _ptr(cu_seqlens), nseq,
+            int(max_seqlen), B, T, Hq, Hkv, d]
+    if fn == "diffattn_gda_fwd":
+        args.append(int(ratio))
     with torch.cuda.device(dev):
-        rc = lib.diffattn_v2_fwd(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(logit), _ptr(out), _ptr(cu_seqlens), nseq,
-            int(max_seqlen), B, T, Hq, Hkv, d, float(scale or 0.0), 1 if causal else 0,
-            DIFFATTN_BF16, _stream(dev))
-    _lib.check("diffattn_v2_fwd", rc)
+        rc = getattr(lib, fn)(*args, float(scale or 0.0), 1 if causal else 0, DIFFATTN_BF16,
+                              _stream(dev))
+    _lib.check(fn, rc)
     return out
+
+
+def v2_fwd(q, k, v, logit, cu_seqlens=None, max_seqlen=None, causal: bool = True,
+           scale: float | None = None, out=None):
+    """DIFF V2 forward.
+
+    Padded: q [B,T,Hq,d], k/v [B,T,Hkv,d] bf16, logit [B,T,Hq/2] fp32 -> out [B,T,Hq/2,d] bf16.
+    Packed: q [N,Hq,d], k/v [N,Hkv,d], logit [N,Hq/2], cu_seqlens int32 [nseq+1] on the GPU and
+    ``max_seqlen`` (host int, >= every sequence length) -> out [N,Hq/2,d].
+    """
+    return _prefill("diffattn_v2_fwd", 1, q, k, v, logit, cu_seqlens, max_seqlen, causal, scale,
+                    out)
+
+
+def gda_fwd(q, k, v, logit, ratio: int, cu_seqlens=None, max_seqlen=None, causal: bool = True,
+            scale: float | None = None, out=None):
+    """Grouped differential attention forward: blocks of ``ratio`` signal heads
+    and one noise head (ratio 1 is V2).  Shapes as v2_fwd with Hs = Hq/(ratio+1)*ratio
+    output heads: logit [..., Hs] fp32 -> out [..., Hs, d] bf16."""
+    return _prefill("diffattn_gda_fwd", ratio, q, k, v, logit, cu_seqlens, max_seqlen, causal,
+                    scale, out)
 
 
 def v2_decode_workspace_bytes(B, S_max, Hq, Hkv, d) -> int:
     return int(_lib.load().diffattn_v2_decode_workspace_bytes(B, S_max, Hq, Hkv, d))
 
 
-def v2_decode(q, k_cache, v_cache, logit, cache_len=None, scale: float | None = None, out=None,
-              workspace=None):
-    """DIFF V2 decode step.  q [B,Hq,d], caches [B,S_max,Hkv,d] bf16, logit [B,Hq/2] fp32,
-    cache_len int32 [B] on the GPU or None -> out [B,Hq/2,d] bf16."""
+def _decode(fn, ratio, q, k_cache, v_cache, logit, cache_len, scale, out, workspace):
     torch = _torch()
     dev = q.device
     _check_tensor("q", q, dtype=torch.bfloat16, dim=3)
@@ -335,33 +357,54 @@ def v2_decode(q, k_cache, v_cache, logit, cache_len=None, scale: float | None = 
     _, S_max, Hkv, dk = k_cache.shape
     if k_cache.shape[0] != B or dk != d:
         raise ValueError("cache shape does not match q")
-    if Hq % 2:
-        raise ValueError("Hq must be even")
-    if tuple(logit.shape) != (B, Hq // 2):
-        raise ValueError("logit must have shape [B, Hq/2]")
+    Hs = _signal_heads(Hq, ratio)
+    if tuple(logit.shape) != (B, Hs):
+        raise ValueError(f"logit must have shape {(B, Hs)}")
     if cache_len is not None:
         _check_tensor("cache_len", cache_len, dtype=torch.int32, dim=1, device=dev)
         if cache_len.shape[0] != B:
             raise ValueError("cache_len must have B entries")
     if out is None:
-        out = torch.empty((B, Hq // 2, d), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((B, Hs, d), dtype=torch.bfloat16, device=dev)
     _check_tensor("out", out, dtype=torch.bfloat16, dim=3, device=dev)
-    if tuple(out.shape) != (B, Hq // 2, d):
+    if tuple(out.shape) != (B, Hs, d):
         raise ValueError("out has the wrong shape")
     lib = _lib.load()
-    need = int(lib.diffattn_v2_decode_workspace_bytes(B, S_max, Hq, Hkv, d))
+    need = int(lib.diffattn_gda_decode_workspace_bytes(B, S_max, Hq, Hkv, d, ratio))
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace is not None:
         _check_tensor("workspace", workspace, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = [_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(logit), _ptr(out),
+            _ptr(workspace), ws_bytes, B, S_max, Hq, Hkv, d]
+    if fn == "diffattn_gda_decode":
+        args.append(int(ratio))
     with torch.cuda.device(dev):
-        rc = lib.diffattn_v2_decode(
-            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(logit), _ptr(out),
-            _ptr(workspace), ws_bytes, B, S_max, Hq, Hkv, d, float(scale or 0.0), DIFFATTN_BF16,
-            _stream(dev))
-    _lib.check("diffattn_v2_decode", rc)
+        rc = getattr(lib, fn)(*args, float(scale or 0.0), DIFFATTN_BF16, _stream(dev))
+    _lib.check(fn, rc)
     return out
+
+
+def v2_decode(q, k_cache, v_cache, logit, cache_len=None, scale: float | None = None, out=None,
+              workspace=None):
+    """DIFF V2 decode step.  q [B,Hq,d], caches [B,S_max,Hkv,d] bf16, logit [B,Hq/2] fp32,
+    cache_len int32 [B] on the GPU or None -> out [B,Hq/2,d] bf16."""
+    return _decode("diffattn_v2_decode", 1, q, k_cache, v_cache, logit, cache_len, scale, out,
+                   workspace)
+
+
+def gda_decode_workspace_bytes(B, S_max, Hq, Hkv, d, ratio) -> int:
+    return int(_lib.load().diffattn_gda_decode_workspace_bytes(B, S_max, Hq, Hkv, d, ratio))
+
+
+def gda_decode(q, k_cache, v_cache, logit, ratio: int, cache_len=None,
+               scale: float | None = None, out=None, workspace=None):
+    """Grouped differential attention decode step: as v2_decode with blocks of
+    ``ratio`` signal heads and one noise head; logit [B,Hs] -> out [B,Hs,d],
+    Hs = Hq/(ratio+1)*ratio."""
+    return _decode("diffattn_gda_decode", ratio, q, k_cache, v_cache, logit, cache_len, scale,
+                   out, workspace)
 
 
 def v2_decode_noalloc(q, k_cache, v_cache, logit, cache_len=None, scale: float | None = None,

@@ -41,6 +41,8 @@ SIGNATURES = {
     "diffattn_v1_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "diffattn_v2_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i,
                              _vp]),
+    "diffattn_gda_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i,
+                              _i, _vp]),
     "diffattn_v2_fwd_train": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
                                    _i, _vp]),
     "diffattn_v2_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i,
@@ -56,6 +58,9 @@ SIGNATURES = {
     "diffattn_v2_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "diffattn_v2_decode_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
                                         _vp]),
+    "diffattn_gda_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _i, _i, _i,
+                                 _f, _i, _vp]),
+    "diffattn_gda_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "diffattn_v1_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _i, _i, _i,
                                 _i, _f, _f, _f, _i, _vp]),
     "diffattn_v1_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),

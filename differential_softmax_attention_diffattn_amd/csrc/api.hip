@@ -51,19 +51,27 @@ long long prod(std::initializer_list<long long> xs) {
   return r;
 }
 
-// Head-layout and dtype checks shared by the V2 prefill, training-forward and
-// backward entry points; returns DIFFATTN_OK or a failure code.
+// Head-layout and dtype checks shared by the V2 (ratio 1) and grouped
+// (ratio r) prefill, training-forward and backward entry points; returns
+// DIFFATTN_OK or a failure code.
 int v2_heads_check(const char* fn, int Hq, int Hkv, int d, float scale, int causal,
-                   diffattn_dtype dtype) {
+                   diffattn_dtype dtype, int ratio = 1) {
   if (Hq <= 0 || Hkv <= 0 || d <= 0)
     return fail(DIFFATTN_E_INVALID, "%s: bad head sizes Hq=%d Hkv=%d d=%d", fn, Hq, Hkv, d);
-  if (Hq % 2) return fail(DIFFATTN_E_INVALID, "%s: Hq=%d must be even (pairs of heads)", fn, Hq);
+  if (ratio < 1 || ratio > 15)
+    return fail(DIFFATTN_E_INVALID, "%s: ratio=%d must be in 1..15", fn, ratio);
+  if (ratio == 1 && Hq % 2)
+    return fail(DIFFATTN_E_INVALID, "%s: Hq=%d must be even (pairs of heads)", fn, Hq);
   if (Hq % Hkv)
     return fail(DIFFATTN_E_INVALID, "%s: Hq=%d must be a multiple of Hkv=%d", fn, Hq, Hkv);
-  if ((Hq / Hkv) % 2)
+  if (ratio == 1 && (Hq / Hkv) % 2)
     return fail(DIFFATTN_E_INVALID,
                 "%s: Hq/Hkv=%d must be even so both heads of a pair share one KV head", fn,
                 Hq / Hkv);
+  if ((Hq / Hkv) % (ratio + 1))
+    return fail(DIFFATTN_E_INVALID,
+                "%s: Hq/Hkv=%d must be a multiple of ratio + 1 = %d so every block of signal "
+                "heads and its noise head share one KV head", fn, Hq / Hkv, ratio + 1);
   if (causal != 0 && causal != 1) return fail(DIFFATTN_E_INVALID, "%s: causal must be 0 or 1", fn);
   if (!isfinite(scale)) return fail(DIFFATTN_E_INVALID, "%s: scale must be finite", fn);
   if (dtype != DIFFATTN_BF16)
@@ -256,14 +264,18 @@ int diffattn_v1_bwd(const void* q1, const void* k1, const void* q2, const void* 
   return from_hip(diffattn::launch_v1_backward(a, static_cast<hipStream_t>(stream)), fn);
 }
 
-int diffattn_v2_fwd(const void* q, const void* k, const void* v, const float* lambda_logit,
-                    void* out, const int* cu_seqlens, int nseq, int max_seqlen, int B, int T,
-                    int Hq, int Hkv, int d, float scale, int causal, diffattn_dtype dtype,
-                    void* stream) {
-  const char* fn = "diffattn_v2_fwd";
+}  // extern "C"
+
+namespace {
+
+// The V2 (ratio 1) and grouped (ratio r) prefill: checks, then one launch.
+int prefill_call(const char* fn, const void* q, const void* k, const void* v,
+                 const float* lambda_logit, void* out, const int* cu_seqlens, int nseq,
+                 int max_seqlen, int B, int T, int Hq, int Hkv, int d, int ratio, float scale,
+                 int causal, diffattn_dtype dtype, void* stream) {
   if (!q || !k || !v || !lambda_logit || !out)
     return fail(DIFFATTN_E_INVALID, "%s: null tensor pointer", fn);
-  const int rc = v2_heads_check(fn, Hq, Hkv, d, scale, causal, dtype);
+  const int rc = v2_heads_check(fn, Hq, Hkv, d, scale, causal, dtype, ratio);
   if (rc != DIFFATTN_OK) return rc;
   int nseq_eff, maxlen;
   if (cu_seqlens) {
@@ -297,11 +309,33 @@ int diffattn_v2_fwd(const void* q, const void* k, const void* v, const float* la
   a.T = T;
   a.N = (cu_seqlens && T > 0) ? (long long)T : -1;  // packed: T is the token count, if known
   a.Hq = Hq;
+  a.ratio = ratio;
+  a.nout = Hq / (ratio + 1) * ratio;
   a.Hkv = Hkv;
   a.d = d;
   a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
   a.causal = causal;
   return from_hip(diffattn::launch_v2_prefill(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int diffattn_v2_fwd(const void* q, const void* k, const void* v, const float* lambda_logit,
+                    void* out, const int* cu_seqlens, int nseq, int max_seqlen, int B, int T,
+                    int Hq, int Hkv, int d, float scale, int causal, diffattn_dtype dtype,
+                    void* stream) {
+  return prefill_call("diffattn_v2_fwd", q, k, v, lambda_logit, out, cu_seqlens, nseq,
+                      max_seqlen, B, T, Hq, Hkv, d, 1, scale, causal, dtype, stream);
+}
+
+int diffattn_gda_fwd(const void* q, const void* k, const void* v, const float* lambda_logit,
+                     void* out, const int* cu_seqlens, int nseq, int max_seqlen, int B, int T,
+                     int Hq, int Hkv, int d, int ratio, float scale, int causal,
+                     diffattn_dtype dtype, void* stream) {
+  return prefill_call("diffattn_gda_fwd", q, k, v, lambda_logit, out, cu_seqlens, nseq,
+                      max_seqlen, B, T, Hq, Hkv, d, ratio, scale, causal, dtype, stream);
 }
 
 int diffattn_v2_fwd_train(const void* q, const void* k, const void* v, const float* lambda_logit,
@@ -332,6 +366,7 @@ int diffattn_v2_fwd_train(const void* q, const void* k, const void* v, const flo
   a.T = T;
   a.N = -1;
   a.Hq = Hq;
+  a.nout = Hq / 2;
   a.Hkv = Hkv;
   a.d = d;
   a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
@@ -431,6 +466,7 @@ int diffattn_v2_varlen_fwd_train(const void* q, const void* k, const void* v,
   a.T = 0;
   a.N = N;
   a.Hq = Hq;
+  a.nout = Hq / 2;
   a.Hkv = Hkv;
   a.d = d;
   a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
@@ -564,8 +600,14 @@ int diffattn_v1_decode(const void* q1, const void* q2, const void* k1_cache, con
 }
 
 size_t diffattn_v2_decode_workspace_bytes(int B, int S_max, int Hq, int Hkv, int d) {
-  if (B < 0 || S_max < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || (Hq / Hkv) % 2 || Hq / Hkv > 16)
-    return 0;
+  return diffattn_gda_decode_workspace_bytes(B, S_max, Hq, Hkv, d, 1);
+}
+
+// The partials hold every query head's (m, l, o) per slice of the cache, so the
+// size does not depend on how the heads are grouped into blocks.
+size_t diffattn_gda_decode_workspace_bytes(int B, int S_max, int Hq, int Hkv, int d, int ratio) {
+  if (B < 0 || S_max < 0 || Hq <= 0 || Hkv <= 0 || ratio < 1 || ratio > 15) return 0;
+  if (Hq % Hkv || (Hq / Hkv) % (ratio + 1) || Hq / Hkv > 16) return 0;
   if (d != 64 && d != 128) return 0;
   int split_len, nsplit, nparts;
   diffattn::decode_split(B, S_max, Hkv, &split_len, &nsplit, &nparts);
@@ -580,24 +622,15 @@ namespace {
 // Checks of the V2 decode entry points, before any launch; DIFFATTN_OK or a code.
 int v2_decode_check(const char* fn, const void* q, const void* k_cache, const void* v_cache,
                     const int* cache_len, const float* lambda_logit, const void* out, int B,
-                    int S_max, int Hq, int Hkv, int d, float scale, diffattn_dtype dtype) {
+                    int S_max, int Hq, int Hkv, int d, float scale, diffattn_dtype dtype,
+                    int ratio = 1) {
   if (!q || !k_cache || !v_cache || !lambda_logit || !out)
     return fail(DIFFATTN_E_INVALID, "%s: null tensor pointer", fn);
   if (B < 0 || S_max < 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
     return fail(DIFFATTN_E_INVALID, "%s: bad sizes B=%d S_max=%d Hq=%d Hkv=%d d=%d", fn, B, S_max,
                 Hq, Hkv, d);
-  if (Hq % 2) return fail(DIFFATTN_E_INVALID, "%s: Hq=%d must be even (pairs of heads)", fn, Hq);
-  if (Hq % Hkv)
-    return fail(DIFFATTN_E_INVALID, "%s: Hq=%d must be a multiple of Hkv=%d", fn, Hq, Hkv);
-  if ((Hq / Hkv) % 2)
-    return fail(DIFFATTN_E_INVALID,
-                "%s: Hq/Hkv=%d must be even so both heads of a pair share one KV head", fn,
-                Hq / Hkv);
-  if (!isfinite(scale)) return fail(DIFFATTN_E_INVALID, "%s: scale must be finite", fn);
-  if (dtype != DIFFATTN_BF16)
-    return fail(dtype == DIFFATTN_F32 ? DIFFATTN_E_UNSUPPORTED : DIFFATTN_E_INVALID,
-                "%s: only bf16 is supported", fn);
-  if (d != 64 && d != 128) return fail(DIFFATTN_E_UNSUPPORTED, "%s: d=%d not in {64, 128}", fn, d);
+  const int rc = v2_heads_check(fn, Hq, Hkv, d, scale, 0, dtype, ratio);
+  if (rc != DIFFATTN_OK) return rc;
   if (Hq / Hkv > 16)
     return fail(DIFFATTN_E_UNSUPPORTED, "%s: Hq/Hkv=%d above 16 query heads per KV head", fn,
                 Hq / Hkv);
@@ -612,7 +645,8 @@ int v2_decode_check(const char* fn, const void* q, const void* k_cache, const vo
 
 int v2_decode_launch(const char* fn, const void* q, const void* k_cache, const void* v_cache,
                      const int* cache_len, const float* lambda_logit, void* out, void* partial,
-                     int B, int S_max, int Hq, int Hkv, int d, float scale, void* stream) {
+                     int B, int S_max, int Hq, int Hkv, int d, float scale, void* stream,
+                     int ratio = 1) {
   diffattn::DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k_cache = static_cast<const uint16_t*>(k_cache);
@@ -624,6 +658,8 @@ int v2_decode_launch(const char* fn, const void* q, const void* k_cache, const v
   a.B = B;
   a.S_max = S_max;
   a.Hq = Hq;
+  a.ratio = ratio;
+  a.nout = Hq / (ratio + 1) * ratio;
   a.Hkv = Hkv;
   a.d = d;
   int nparts;
@@ -652,6 +688,25 @@ int diffattn_v2_decode(const void* q, const void* k_cache, const void* v_cache,
   if (!aligned16(workspace)) return fail(DIFFATTN_E_ALIGN, "%s: workspace must be 16-byte aligned", fn);
   return v2_decode_launch(fn, q, k_cache, v_cache, cache_len, lambda_logit, out, workspace, B,
                           S_max, Hq, Hkv, d, scale, stream);
+}
+
+int diffattn_gda_decode(const void* q, const void* k_cache, const void* v_cache,
+                        const int* cache_len, const float* lambda_logit, void* out,
+                        void* workspace, size_t workspace_bytes, int B, int S_max, int Hq,
+                        int Hkv, int d, int ratio, float scale, diffattn_dtype dtype,
+                        void* stream) {
+  const char* fn = "diffattn_gda_decode";
+  const int rc = v2_decode_check(fn, q, k_cache, v_cache, cache_len, lambda_logit, out, B, S_max,
+                                 Hq, Hkv, d, scale, dtype, ratio);
+  if (rc != DIFFATTN_OK) return rc;
+  if (B == 0) return ok();
+  const size_t need = diffattn_gda_decode_workspace_bytes(B, S_max, Hq, Hkv, d, ratio);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DIFFATTN_E_WORKSPACE, "%s: workspace of %zu bytes required (got %zu%s)", fn, need,
+                workspace_bytes, workspace ? "" : ", NULL");
+  if (!aligned16(workspace)) return fail(DIFFATTN_E_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  return v2_decode_launch(fn, q, k_cache, v_cache, cache_len, lambda_logit, out, workspace, B,
+                          S_max, Hq, Hkv, d, scale, stream, ratio);
 }
 
 int diffattn_v2_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,

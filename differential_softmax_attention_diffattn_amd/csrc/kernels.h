@@ -66,6 +66,11 @@ struct V2Args {
   int causal;
   uint16_t* o_heads;        // bf16 [tokens, Hq, d] per-head outputs, or nullptr (training forward)
   float* lse;               // fp32 [tokens, Hq] natural-log log-sum-exp, or nullptr
+  // Heads subtracted: blocks of `ratio` signal heads and one noise head (V2:
+  // ratio 1, pairs); output head s subtracts noise head (s / ratio) *
+  // (ratio + 1) + ratio from signal head (s / ratio) * (ratio + 1) + s % ratio.
+  int ratio = 1;
+  int nout = 0;             // output heads: Hq / (ratio + 1) * ratio
 };
 
 // V2 backward (padded batches).  Gradients of sum(dout * out) of the V2 forward.
@@ -104,6 +109,8 @@ struct DecodeArgs {
   int B, S_max, Hq, Hkv, d;
   int split_len, nsplit;    // cache slices of split_len keys; nparts = partials per head
   float scale;
+  int ratio = 1;            // signal heads per noise head (as V2Args)
+  int nout = 0;             // output heads
 };
 
 // Coefficient logits of V2: logits[n, p] = sum_c x[n, c] w[p, c].

@@ -228,20 +228,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   }
 }
 
-// Merge the partials of both heads of a pair with log-sum-exp weights, then
-// out_p = O_2p - sigmoid(logit_p) * O_2p+1.
+// Merge the partials of the two heads an output head subtracts (V2: a pair)
+// with log-sum-exp weights, then
+// out_p = O_signal(p) - sigmoid(logit_p) * O_noise(p).
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, int nparts) {
   __shared__ float wts[2][512];
   __shared__ float inv_l[2];
-  const int hp = a.Hq / 2;
+  // output head p: its block's signal head minus sigmoid-weighted noise head
+  // (V2: the pair 2p, 2p + 1)
+  const int hp = a.nout;
   const int p = blockIdx.x % hp;
   const int b = blockIdx.x / hp;
+  const int R = a.ratio;
+  const int heads[2] = {(p / R) * (R + 1) + p % R, (p / R) * (R + 1) + R};
   const int t = threadIdx.x;
   const float* src[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e)
-    src[e] = a.partial + (((size_t)b * a.Hq + 2 * p + e) * nparts) * kPartStride<D>;
+    src[e] = a.partial + (((size_t)b * a.Hq + heads[e]) * nparts) * kPartStride<D>;
   // weights 2^(m_s - M) / L per part, computed once per head by one wave each
   if (t < 2 * kWave) {
     const int e = t / kWave, ln = t % kWave;
@@ -281,7 +286,7 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((decode_split_kernel<D, KVW>), dim3((unsigned)blocks), dim3(kThreads), 0,
                      stream, a);
   const int nparts = a.nsplit * (kWaves / KVW);
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.B * (a.Hq / 2))), dim3(256), 0,
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.B * a.nout)), dim3(256), 0,
                      stream, a, nparts);
   return hipGetLastError();
 }

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   // sharing its K/V tiles in L2.  Packed batches number the tiles by slots
   // (varlen.h): a binary search over cu_seqlens finds the sequence, and the
   // blocks of empty slots exit.
-  const int n_hg = a.Hq / (2 * PW);
+  const int n_hg = a.nout / PW;
   const int hg = blockIdx.x % n_hg;
   const int t = blockIdx.x / n_hg;
   int tok0, L, qt;
@@ -116,10 +116,16 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
     L = a.T;
   }
 
-  const int hpairs = a.Hq / 2;
+  // output head p subtracts its block's noise head from its signal head (V2:
+  // blocks of two, the pair 2p, 2p + 1); the PW output heads of a workgroup
+  // lie in one GQA group (the launch picks PW so)
+  const int nout = a.nout;
   const int group = a.Hq / a.Hkv;
+  const int R = a.ratio;
   const int p = hg * PW + (wave % PW);
-  const int kv = (hg * PW * 2) / group;
+  const int head_sig = (p / R) * (R + 1) + p % R;
+  const int head_noise = (p / R) * (R + 1) + R;
+  const int kv = (((hg * PW) / R) * (R + 1)) / group;
   const int q_lo = qt * QTILE + (wave / PW) * kRows;
   const bool wave_active = q_lo < L;
 
@@ -142,10 +148,11 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      qf[nb][c] = ldg128(a.q + ((size_t)(tok0 + rowc) * a.Hq + 2 * p + nb) * D + c * 32 + g * 8);
+      qf[nb][c] = ldg128(a.q + ((size_t)(tok0 + rowc) * a.Hq + (nb ? head_noise : head_sig)) * D +
+                         c * 32 + g * 8);
   // the pair's coefficient logit for this lane's row, fetched now so its load
   // latency is not paid at the end of the key loop
-  const float lgv = a.logit[(size_t)(tok0 + rowc) * hpairs + p];
+  const float lgv = a.logit[(size_t)(tok0 + rowc) * nout + p];
 
   // ---- direct-to-LDS tile loads (K and V rows, swizzled) ----
   // Each lane's chunks inside a tile are fixed; keep them as 32-bit element
@@ -420,13 +427,13 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
     // scaled scores (the accumulators hold log2-domain values minus mb)
     const size_t tok = (size_t)(tok0 + row);
     if (g == 0) {
-      a.lse[tok * a.Hq + 2 * p] = (mb[0] + log2f(l_e)) * 0.69314718055994531f;
-      a.lse[tok * a.Hq + 2 * p + 1] = (mb[1] + log2f(l_o)) * 0.69314718055994531f;
+      a.lse[tok * a.Hq + head_sig] = (mb[0] + log2f(l_e)) * 0.69314718055994531f;
+      a.lse[tok * a.Hq + head_noise] = (mb[1] + log2f(l_o)) * 0.69314718055994531f;
     }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const float inv = nb ? inv_o : inv_e;
-      uint16_t* dst = a.o_heads + (tok * a.Hq + 2 * p + nb) * D + g * 4;
+      uint16_t* dst = a.o_heads + (tok * a.Hq + (nb ? head_noise : head_sig)) * D + g * 4;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
         *reinterpret_cast<u32x2*>(dst + db * 16) =
@@ -437,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   if (row < L) {
     const size_t tok = (size_t)(tok0 + row);
     const float sg = sigmoid_f32(lgv);
-    uint16_t* dst = a.out + (tok * hpairs + p) * D + g * 4;
+    uint16_t* dst = a.out + (tok * nout + p) * D + g * 4;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       float r[4];
@@ -461,7 +468,7 @@ hipError_t launch_typed(const V2Args& a, hipStream_t stream) {
   const long long tiles = a.cu_seqlens != nullptr
                               ? slot_count(a.N, a.nseq, a.max_seqlen, QTILE)
                               : (long long)((a.T + QTILE - 1) / QTILE) * a.nseq;
-  const long long blocks = tiles * (a.Hq / (2 * PW));
+  const long long blocks = tiles * (a.nout / PW);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.causal)
@@ -475,9 +482,10 @@ hipError_t launch_typed(const V2Args& a, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_d(const V2Args& a, hipStream_t stream) {
-  const int pairs_per_group = (a.Hq / a.Hkv) / 2;
-  if (pairs_per_group % 4 == 0) return launch_typed<D, 4>(a, stream);
-  if (pairs_per_group % 2 == 0) return launch_typed<D, 2>(a, stream);
+  // output heads per GQA group: a workgroup's PW output heads must share one
+  const int out_per_group = (a.Hq / a.Hkv) / (a.ratio + 1) * a.ratio;
+  if (out_per_group % 4 == 0) return launch_typed<D, 4>(a, stream);
+  if (out_per_group % 2 == 0) return launch_typed<D, 2>(a, stream);
   return launch_typed<D, 1>(a, stream);
 }
 

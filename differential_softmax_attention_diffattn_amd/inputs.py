@@ -122,6 +122,12 @@ class V2Workload:
     logit_std: float = 1.0
     lengths: tuple | None = None
     causal: bool = True
+    ratio: int = 1  # signal heads per noise head (grouped variant; 1 = pairs)
+
+    @property
+    def n_out(self) -> int:
+        """Output heads (and logits per token): blocks of ratio + 1 query heads give ratio each."""
+        return self.Hq // (self.ratio + 1) * self.ratio
 
     def with_shape(self, **kw) -> "V2Workload":
         d = dict(self.__dict__)
@@ -141,6 +147,11 @@ class DecodeWorkload:
     std: float
     seeds: tuple  # q, k_cache, v_cache, logit
     cache_lens: tuple | None = None
+    ratio: int = 1  # signal heads per noise head (grouped variant; 1 = pairs)
+
+    @property
+    def n_out(self) -> int:
+        return self.Hq // (self.ratio + 1) * self.ratio
 
     def with_shape(self, **kw) -> "DecodeWorkload":
         d = dict(self.__dict__)
@@ -208,8 +219,19 @@ V2_DECODE_B1 = V2_DECODE.with_shape(name="v2_decode_bf16_b1_s32768_hq64_hkv8_d12
 V2_VARLEN_SHORT = V2_VARLEN.with_shape(name="v2_varlen_bf16_causal_2048x32_hq64_hkv8_d128",
                                        lengths=(32,) * 2048)
 
+# Grouped variant at the V2 prefill's and decode's shapes: in each GQA group of 8
+# query heads, two blocks of 3 signal heads and 1 noise head (48 output heads);
+# and 4:1 with 80 query heads over the same 8 KV heads (two blocks of 5 per group,
+# 64 output heads).
+GDA_PREFILL_R3 = V2_PREFILL.with_shape(name="gda_prefill_bf16_causal_b2_t8192_hq64_hkv8_d128_r3",
+                                       ratio=3)
+GDA_PREFILL_R4 = V2_PREFILL.with_shape(name="gda_prefill_bf16_causal_b2_t8192_hq80_hkv8_d128_r4",
+                                       Hq=80, ratio=4)
+GDA_DECODE_R3 = V2_DECODE.with_shape(name="gda_decode_bf16_b64_s32768_hq64_hkv8_d128_r3", ratio=3)
+
 WORKLOADS = {w.name: w for w in (V1_FP32_SMALL, V1_BF16, V2_PREFILL, V2_DECODE, V2_VARLEN,
-                                  V1_DECODE, V2_DECODE_B1, V2_VARLEN_SHORT)}
+                                  V1_DECODE, V2_DECODE_B1, V2_VARLEN_SHORT, GDA_PREFILL_R3,
+                                  GDA_PREFILL_R4, GDA_DECODE_R3)}
 
 
 # ---------------------------------------------------------------------------
@@ -239,7 +261,7 @@ def v1_dy(w: V1Workload, seed: int = V1_DY_SEED, device=None) -> torch.Tensor:
 def v2_inputs(w: V2Workload, device=None) -> dict:
     """Padded: q [B,T,Hq,d] ...; packed (``w.lengths`` set): q [total,Hq,d], plus cu_seqlens."""
     sq, sk, sv, sl = w.seeds
-    h = w.Hq // 2
+    h = w.n_out
     if w.lengths is None:
         lead = (w.B, w.T)
         return dict(
@@ -324,7 +346,7 @@ def v2_dout(w: V2Workload, seed: int = DOUT_SEED, device=None) -> torch.Tensor:
 def decode_small_inputs(w: DecodeWorkload, device=None) -> dict:
     """Decode inputs for the query, logits and lengths (the caches come from :func:`decode_cache_slice`)."""
     sq, sk, sv, sl = w.seeds
-    h = w.Hq // 2
+    h = w.n_out
     lens = None if w.cache_lens is None else torch.tensor(w.cache_lens, dtype=torch.int32,
                                                           device=device)
     return dict(

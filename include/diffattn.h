@@ -188,6 +188,32 @@ DIFFATTN_API int diffattn_v2_fwd(const void* q, const void* k, const void* v, co
                     void* stream);
 
 /*
+ * Grouped differential attention forward (prefill) [P1 "같은 문제, 다른 접근":
+ * the follow-up that splits heads into signal and noise heads at 3:1 or 4:1].
+ * The page gives the ratio only; the rule here is this reading of it, the V2
+ * subtraction with one noise head serving a block of `ratio` signal heads:
+ * query heads come in blocks of ratio + 1 inside a GQA group, heads
+ * (ratio + 1) m .. (ratio + 1) m + ratio - 1 are the signal heads of block m
+ * and head (ratio + 1) m + ratio its noise head.  Output head s (block
+ * m = s / ratio, position r = s % ratio) is
+ *
+ *   out[i,s] = O_{(ratio+1) m + r}[i] - sigmoid(lambda_logit[i,s]) * O_{(ratio+1) m + ratio}[i],
+ *
+ * with O_j as in diffattn_v2_fwd.  ratio == 1 is diffattn_v2_fwd exactly.
+ * Hs = Hq / (ratio + 1) * ratio output heads; lambda_logit is [.., Hs] fp32
+ * and out [.., Hs, d] bf16; q, k, v, cu_seqlens, nseq, max_seqlen, B, T, scale,
+ * causal and dtype as diffattn_v2_fwd.  Hq / Hkv must be a multiple of
+ * ratio + 1 (a block never spans two KV heads); ratio in 1..15.  Each signal
+ * head's workgroup recomputes its block's noise head, so the attention work
+ * is 2 Hs head-passes, not Hq.
+ */
+DIFFATTN_API int diffattn_gda_fwd(const void* q, const void* k, const void* v,
+                                  const float* lambda_logit, void* out, const int* cu_seqlens,
+                                  int nseq, int max_seqlen, int B, int T, int Hq, int Hkv, int d,
+                                  int ratio, float scale, int causal, diffattn_dtype dtype,
+                                  void* stream);
+
+/*
  * V2 training forward (padded batches) [P2 §1, §4]: diffattn_v2_fwd's output,
  * plus what diffattn_v2_bwd needs from the forward:
  *
@@ -325,6 +351,25 @@ DIFFATTN_API int diffattn_v2_decode(const void* q, const void* k_cache, const vo
 
 /* Workspace bytes diffattn_v2_decode needs (0 for sizes it would reject). */
 DIFFATTN_API size_t diffattn_v2_decode_workspace_bytes(int B, int S_max, int Hq, int Hkv, int d);
+
+/*
+ * Grouped differential attention decode step [P1 "같은 문제, 다른 접근"; rule
+ * as diffattn_gda_fwd]: diffattn_v2_decode with blocks of `ratio` signal heads
+ * and one noise head.  lambda_logit : [B, Hs] fp32; out : [B, Hs, d] bf16 with
+ * Hs = Hq / (ratio + 1) * ratio; the other arguments as diffattn_v2_decode.
+ * Every query head is attended once, so the noise head is not recomputed.
+ * Supported: dtype DIFFATTN_BF16, d in {64, 128}, Hq / Hkv a multiple of
+ * ratio + 1 and <= 16, ratio in 1..15.
+ */
+DIFFATTN_API int diffattn_gda_decode(const void* q, const void* k_cache, const void* v_cache,
+                                     const int* cache_len, const float* lambda_logit, void* out,
+                                     void* workspace, size_t workspace_bytes, int B, int S_max,
+                                     int Hq, int Hkv, int d, int ratio, float scale,
+                                     diffattn_dtype dtype, void* stream);
+
+/* Workspace bytes diffattn_gda_decode needs (0 for sizes it would reject). */
+DIFFATTN_API size_t diffattn_gda_decode_workspace_bytes(int B, int S_max, int Hq, int Hkv, int d,
+                                                        int ratio);
 
 /*
  * diffattn_v2_decode for callers that cannot allocate device memory: code

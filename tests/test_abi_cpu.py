@@ -356,3 +356,53 @@ def test_v2_decode_noalloc_rejects_bad_and_oversize_arguments(lib):
     assert lib.diffattn_v2_decode_workspace_bytes(2048, 4096, 64, 8, 128) > 32 << 20
     assert f(B=2048) == E_UNSUPPORTED
     assert b"diffattn_v2_decode with a workspace" in lib.diffattn_last_error()
+
+
+def gda(lib, **kw):
+    a = dict(q=P, k=P, v=P, lg=P, out=P, cu=None, nseq=0, maxlen=0, B=2, T=64, Hq=16, Hkv=2,
+             d=128, ratio=3, scale=0.0, causal=1, dt=BF16, stream=None)
+    a.update(kw)
+    return lib.diffattn_gda_fwd(a["q"], a["k"], a["v"], a["lg"], a["out"], a["cu"], a["nseq"],
+                                a["maxlen"], a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], a["ratio"],
+                                a["scale"], a["causal"], a["dt"], a["stream"])
+
+
+def test_gda_forward_rejects_bad_arguments(lib):
+    assert gda(lib, ratio=0) == E_INVALID
+    assert gda(lib, ratio=16) == E_INVALID
+    # groups of 8 query heads: blocks of 4 (ratio 3) fit, blocks of 5 (ratio 4) do not
+    assert gda(lib, ratio=4) == E_INVALID
+    assert b"ratio + 1" in lib.diffattn_last_error()
+    assert gda(lib, Hq=15, Hkv=5, ratio=4) == E_INVALID     # groups of 3 cannot hold 5
+    assert gda(lib, Hq=15, Hkv=3, ratio=4, B=0) == 0          # odd Hq: one block per group
+    assert gda(lib, Hq=10, Hkv=2, ratio=4, B=0) == 0
+    assert gda(lib, Hq=10, Hkv=2, ratio=4, T=0) == 0
+    assert gda(lib, d=96) == E_UNSUPPORTED
+    assert gda(lib, dt=F32) == E_UNSUPPORTED
+    assert gda(lib, out=P + 2) == E_ALIGN
+    assert gda(lib, cu=P, nseq=-1, maxlen=5) == E_INVALID
+    assert gda(lib, cu=P, nseq=0, maxlen=0) == 0
+
+
+def gdec(lib, **kw):
+    a = dict(q=P, k=P, v=P, lens=None, lg=P, out=P, ws=P, wsb=1 << 30, B=4, S=1024, Hq=16, Hkv=2,
+             d=128, ratio=3, scale=0.0, dt=BF16, stream=None)
+    a.update(kw)
+    return lib.diffattn_gda_decode(a["q"], a["k"], a["v"], a["lens"], a["lg"], a["out"], a["ws"],
+                                   a["wsb"], a["B"], a["S"], a["Hq"], a["Hkv"], a["d"], a["ratio"],
+                                   a["scale"], a["dt"], a["stream"])
+
+
+def test_gda_decode_rejects_bad_arguments_and_sizes_its_workspace(lib):
+    assert gdec(lib, ratio=4) == E_INVALID
+    assert gdec(lib, Hq=64, Hkv=2, ratio=3) == E_UNSUPPORTED   # 32 query heads per KV head
+    assert gdec(lib, ws=None) == E_WORKSPACE
+    assert gdec(lib, wsb=8) == E_WORKSPACE
+    assert gdec(lib, B=0) == 0
+    # partials are kept per query head, whatever the blocks: the V2 size
+    for B, S in ((1, 32768), (64, 4096)):
+        assert (lib.diffattn_gda_decode_workspace_bytes(B, S, 16, 2, 128, 3)
+                == lib.diffattn_gda_decode_workspace_bytes(B, S, 16, 2, 128, 1)
+                == lib.diffattn_v2_decode_workspace_bytes(B, S, 16, 2, 128) > 0)
+    assert lib.diffattn_gda_decode_workspace_bytes(4, 1024, 16, 2, 128, 4) == 0
+    assert lib.diffattn_gda_decode_workspace_bytes(4, 1024, 10, 2, 128, 4) > 0
