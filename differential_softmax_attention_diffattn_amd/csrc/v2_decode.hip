@@ -231,15 +231,24 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
 // Merge the partials of the two heads an output head subtracts (V2: a pair)
 // with log-sum-exp weights, then
 // out_p = O_signal(p) - sigmoid(logit_p) * O_noise(p).
-template <int D>
+// A workgroup owns COLS of the D channels of one output head (D, or a slice of
+// 32 when there are many partials, so that a small batch still spreads over
+// the device); its 256 threads are COLS columns x 256 / COLS part groups, each
+// group summing every (256 / COLS)-th partial, then the groups are added in a
+// fixed order.
+template <int D, int COLS>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, int nparts) {
+  constexpr int NG = 256 / COLS;
+  constexpr int kSlices = D / COLS;
   __shared__ float wts[2][512];
   __shared__ float inv_l[2];
+  __shared__ float red[2][NG][COLS];
   // output head p: its block's signal head minus sigmoid-weighted noise head
   // (V2: the pair 2p, 2p + 1)
   const int hp = a.nout;
-  const int p = blockIdx.x % hp;
-  const int b = blockIdx.x / hp;
+  const int slice = blockIdx.x % kSlices;
+  const int p = (blockIdx.x / kSlices) % hp;
+  const int b = blockIdx.x / kSlices / hp;
   const int R = a.ratio;
   const int heads[2] = {(p / R) * (R + 1) + p % R, (p / R) * (R + 1) + R};
   const int t = threadIdx.x;
@@ -247,35 +256,69 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, int n
 #pragma unroll
   for (int e = 0; e < 2; ++e)
     src[e] = a.partial + (((size_t)b * a.Hq + heads[e]) * nparts) * kPartStride<D>;
-  // weights 2^(m_s - M) / L per part, computed once per head by one wave each
+  // weights 2^(m_s - M) / L per part, computed once per head by one wave each;
+  // a lane's (m, l) pairs (parts ln + 64 k, at most 512 parts) are all loaded
+  // before any is used, so their latencies overlap
   if (t < 2 * kWave) {
     const int e = t / kWave, ln = t % kWave;
+    float ms[8], ls[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int s = ln + k * kWave;
+      ms[k] = -INFINITY;
+      ls[k] = 0.f;
+      if (s < nparts) {
+        const f32x2 ml = *reinterpret_cast<const f32x2*>(src[e] + s * kPartStride<D> + D);
+        ms[k] = ml[0];
+        ls[k] = ml[1];
+      }
+    }
     float M = -INFINITY;
-    for (int s = ln; s < nparts; s += kWave) M = fmaxf(M, src[e][s * kPartStride<D> + D]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) M = fmaxf(M, ms[k]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     float L = 0.f;
-    for (int s = ln; s < nparts; s += kWave) {
-      const float ms = src[e][s * kPartStride<D> + D];
-      const float w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
-      wts[e][s] = w;
-      L = fmaf(src[e][s * kPartStride<D> + D + 1], w, L);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int s = ln + k * kWave;
+      const float w = (ms[k] == -INFINITY) ? 0.f : fast_exp2(ms[k] - M);
+      if (s < nparts) wts[e][s] = w;
+      L = fmaf(ls[k], w, L);
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
     if (ln == 0) inv_l[e] = L > 0.f ? 1.0f / L : 0.f;
   }
   __syncthreads();
-  if (t >= D) return;
+  const int col = t % COLS;
+  const int grp = t / COLS;
+  const int ch = slice * COLS + col;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    // four independent chains per thread: the loads overlap
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int s = grp;
+    for (; s + 3 * NG < nparts; s += 4 * NG) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        acc[u] = fmaf(src[e][(s + u * NG) * kPartStride<D> + ch], wts[e][s + u * NG], acc[u]);
+    }
+    for (; s < nparts; s += NG) acc[0] = fmaf(src[e][s * kPartStride<D> + ch], wts[e][s], acc[0]);
+    red[e][grp][col] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  }
+  __syncthreads();
+  if (t >= COLS) return;
   float res[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     float O = 0.f;
-    for (int s = 0; s < nparts; ++s) O = fmaf(src[e][s * kPartStride<D> + t], wts[e][s], O);
+#pragma unroll
+    for (int k = 0; k < NG; ++k) O += red[e][k][t];
     res[e] = __fmul_rn(O, inv_l[e]);
   }
   const float sg = sigmoid_f32(a.logit[(size_t)b * hp + p]);
-  a.out[((size_t)b * hp + p) * D + t] = f32_to_bf16(fmaf(-sg, res[1], res[0]));
+  a.out[((size_t)b * hp + p) * D + slice * COLS + t] = f32_to_bf16(fmaf(-sg, res[1], res[0]));
 }
 
 template <int D, int KVW>
@@ -286,8 +329,12 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((decode_split_kernel<D, KVW>), dim3((unsigned)blocks), dim3(kThreads), 0,
                      stream, a);
   const int nparts = a.nsplit * (kWaves / KVW);
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(a.B * a.nout)), dim3(256), 0,
-                     stream, a, nparts);
+  if (nparts >= 32)
+    hipLaunchKernelGGL((decode_combine_kernel<D, 32>), dim3((unsigned)(a.B * a.nout * (D / 32))),
+                       dim3(256), 0, stream, a, nparts);
+  else
+    hipLaunchKernelGGL((decode_combine_kernel<D, D>), dim3((unsigned)(a.B * a.nout)), dim3(256), 0,
+                       stream, a, nparts);
   return hipGetLastError();
 }
 
