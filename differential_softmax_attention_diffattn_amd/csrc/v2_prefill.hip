@@ -68,7 +68,13 @@ __device__ __forceinline__ int v_offset(int row, int byte_in_row) {
   return row * Tile<D>::kRowBytes + ((c32 ^ (row & (n32 - 1))) << 5) + (byte_in_row & 31);
 }
 
-template <int D, int PW, bool CAUSAL>
+// SHARED (grouped variant with ratio + 1 dividing 2 PW): each wave computes
+// the two consecutive query heads 2pp, 2pp + 1 once, as for V2, and the
+// subtraction happens in the epilogue: waves holding a noise head publish its
+// normalised output through LDS, and every signal head subtracts its block's
+// noise head from there or from its own registers.  Otherwise each wave
+// computes an output head's signal and noise head itself (V2: the pair).
+template <int D, int PW, bool CAUSAL, bool SHARED>
 __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   using TL = Tile<D>;
   constexpr int QSUB = kWaves / PW;  // 16-row groups per workgroup
@@ -96,7 +102,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   // sharing its K/V tiles in L2.  Packed batches number the tiles by slots
   // (varlen.h): a binary search over cu_seqlens finds the sequence, and the
   // blocks of empty slots exit.
-  const int n_hg = a.nout / PW;
+  const int n_hg = SHARED ? a.Hq / 2 / PW : a.nout / PW;
   const int hg = blockIdx.x % n_hg;
   const int t = blockIdx.x / n_hg;
   int tok0, L, qt;
@@ -123,9 +129,15 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   const int group = a.Hq / a.Hkv;
   const int R = a.ratio;
   const int p = hg * PW + (wave % PW);
-  const int head_sig = (p / R) * (R + 1) + p % R;
-  const int head_noise = (p / R) * (R + 1) + R;
-  const int kv = (((hg * PW) / R) * (R + 1)) / group;
+  // the wave's two query heads: SHARED, the pair 2p, 2p + 1 (2p is a signal
+  // head: blocks start at even heads and end with their noise head); else the
+  // signal and noise head of output head p
+  const int head_sig = SHARED ? 2 * p : (p / R) * (R + 1) + p % R;
+  const int head_noise = SHARED ? 2 * p + 1 : (p / R) * (R + 1) + R;
+  const int kv = SHARED ? (hg * PW * 2) / group : (((hg * PW) / R) * (R + 1)) / group;
+  // output-head index of a signal query head j
+  auto out_index = [&](int j) { return (j / (R + 1)) * R + j % (R + 1); };
+  const bool odd_is_noise = SHARED && (head_noise % (R + 1) == R);
   const int q_lo = qt * QTILE + (wave / PW) * kRows;
   const bool wave_active = q_lo < L;
 
@@ -152,7 +164,9 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
                          c * 32 + g * 8);
   // the pair's coefficient logit for this lane's row, fetched now so its load
   // latency is not paid at the end of the key loop
-  const float lgv = a.logit[(size_t)(tok0 + rowc) * nout + p];
+  const float lgv = a.logit[(size_t)(tok0 + rowc) * nout + (SHARED ? out_index(head_sig) : p)];
+  const float lgv_odd =
+      (SHARED && !odd_is_noise) ? a.logit[(size_t)(tok0 + rowc) * nout + out_index(head_noise)] : 0.f;
 
   // ---- direct-to-LDS tile loads (K and V rows, swizzled) ----
   // Each lane's chunks inside a tile are fixed; keep them as 32-bit element
@@ -355,6 +369,76 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
     }
   };
 
+  // SHARED epilogue.  xch holds, per row group and block of the workgroup,
+  // the block's normalised noise-head output [16 rows][D] (fp32, padded rows).
+  auto shared_epilogue = [&]() __attribute__((always_inline)) {
+    constexpr int XS = D + 4;
+    constexpr int kBlocks = 2 * PW / 4 > 0 ? 2 * PW / 4 : 1;  // blocks (>= 4 heads) in 2 PW heads
+    __shared__ __align__(16) float xch[QSUB][kBlocks][kRows * XS];
+    const int rg = wave / PW;
+    const int head0 = 2 * hg * PW;  // first query head of the workgroup
+    const float l_e = sum_across_rows(l_part[0]);
+    const float l_o = sum_across_rows(l_part[1]);
+    const float inv_e = 1.0f / l_e;
+    const float inv_o = 1.0f / l_o;
+    if (wave_active && odd_is_noise) {
+      float* dst = &xch[rg][(head_noise - head0) / (R + 1)][c16 * XS + g * 4];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        f32x4 t;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] = __fmul_rn(o[db][1][i], inv_o);
+        *reinterpret_cast<f32x4*>(dst + db * 16) = t;
+      }
+    }
+    __syncthreads();
+    if (!wave_active || row >= L) return;
+    const size_t tok = (size_t)(tok0 + row);
+    if (a.o_heads != nullptr) {  // training forward: every head once
+      if (g == 0) {
+        a.lse[tok * a.Hq + head_sig] = (mb[0] + log2f(l_e)) * 0.69314718055994531f;
+        a.lse[tok * a.Hq + head_noise] = (mb[1] + log2f(l_o)) * 0.69314718055994531f;
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const float inv = nb ? inv_o : inv_e;
+        uint16_t* dst = a.o_heads + (tok * a.Hq + (nb ? head_noise : head_sig)) * D + g * 4;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          *reinterpret_cast<u32x2*>(dst + db * 16) =
+              u32x2{pack_bf16x2(o[db][nb][0] * inv, o[db][nb][1] * inv),
+                    pack_bf16x2(o[db][nb][2] * inv, o[db][nb][3] * inv)};
+      }
+    }
+    // the even head always subtracts its block's noise head: the odd head of
+    // this wave, or published by another wave
+    const int noise_e = (head_sig / (R + 1)) * (R + 1) + R;
+    const float* xn = &xch[rg][(noise_e - head0) / (R + 1)][c16 * XS + g * 4];
+    const float sg_e = sigmoid_f32(lgv);
+    const float sg_o = sigmoid_f32(lgv_odd);
+    uint16_t* dst_e = a.out + (tok * nout + out_index(head_sig)) * D + g * 4;
+    uint16_t* dst_o = a.out + (tok * nout + out_index(head_noise)) * D + g * 4;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      f32x4 n4;
+      if (odd_is_noise) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) n4[i] = __fmul_rn(o[db][1][i], inv_o);
+      } else {
+        n4 = *reinterpret_cast<const f32x4*>(xn + db * 16);
+      }
+      float r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = fmaf(-sg_e, n4[i], __fmul_rn(o[db][0][i], inv_e));
+      *reinterpret_cast<u32x2*>(dst_e + db * 16) = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+      if (!odd_is_noise) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = fmaf(-sg_o, n4[i], __fmul_rn(o[db][1][i], inv_o));
+        *reinterpret_cast<u32x2*>(dst_o + db * 16) = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+      }
+    }
+  };
+
   // Key tiles [0, n_int) are fully valid and visible to every row of the
   // workgroup: they take the unmasked step in a branch-free loop, unrolled by
   // two so each stage is a fixed LDS object.  The remaining (diagonal and
@@ -415,6 +499,10 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
     __syncthreads();
   }
 
+  if constexpr (SHARED) {
+    shared_epilogue();
+    return;
+  }
   if (!wave_active) return;
 
   // ---- epilogue: normalise, pair subtraction, bf16 store ----
@@ -460,7 +548,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   }
 }
 
-template <int D, int PW>
+template <int D, int PW, bool SHARED>
 hipError_t launch_typed(const V2Args& a, hipStream_t stream) {
   constexpr int QTILE = kRows * (kWaves / PW);
   // query tiles: B x ceil(T / QTILE) for padded batches, the tile slots of
@@ -468,25 +556,34 @@ hipError_t launch_typed(const V2Args& a, hipStream_t stream) {
   const long long tiles = a.cu_seqlens != nullptr
                               ? slot_count(a.N, a.nseq, a.max_seqlen, QTILE)
                               : (long long)((a.T + QTILE - 1) / QTILE) * a.nseq;
-  const long long blocks = tiles * (a.nout / PW);
+  const long long blocks = tiles * (SHARED ? a.Hq / 2 / PW : a.nout / PW);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.causal)
-    hipLaunchKernelGGL((v2_prefill_kernel<D, PW, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((v2_prefill_kernel<D, PW, true, SHARED>), dim3((unsigned)blocks),
+                       dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((v2_prefill_kernel<D, PW, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((v2_prefill_kernel<D, PW, false, SHARED>), dim3((unsigned)blocks),
+                       dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const V2Args& a, hipStream_t stream) {
-  // output heads per GQA group: a workgroup's PW output heads must share one
-  const int out_per_group = (a.Hq / a.Hkv) / (a.ratio + 1) * a.ratio;
-  if (out_per_group % 4 == 0) return launch_typed<D, 4>(a, stream);
-  if (out_per_group % 2 == 0) return launch_typed<D, 2>(a, stream);
-  return launch_typed<D, 1>(a, stream);
+  const int group = a.Hq / a.Hkv;
+  const int R = a.ratio;
+  // grouped variant whose blocks of ratio + 1 heads tile a workgroup's 2 PW
+  // query heads: every head computed once (SHARED)
+  if (R > 1 && (R + 1) % 2 == 0 && a.o_heads == nullptr) {
+    const int pairs_per_group = group / 2;
+    if (pairs_per_group % 4 == 0 && 8 % (R + 1) == 0) return launch_typed<D, 4, true>(a, stream);
+    if (pairs_per_group % 2 == 0 && 4 % (R + 1) == 0) return launch_typed<D, 2, true>(a, stream);
+  }
+  // otherwise a workgroup's PW output heads must share one GQA group
+  const int out_per_group = group / (R + 1) * R;
+  if (out_per_group % 4 == 0) return launch_typed<D, 4, false>(a, stream);
+  if (out_per_group % 2 == 0) return launch_typed<D, 2, false>(a, stream);
+  return launch_typed<D, 1, false>(a, stream);
 }
 
 }  // namespace

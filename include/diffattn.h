@@ -203,9 +203,11 @@ DIFFATTN_API int diffattn_v2_fwd(const void* q, const void* k, const void* v, co
  * Hs = Hq / (ratio + 1) * ratio output heads; lambda_logit is [.., Hs] fp32
  * and out [.., Hs, d] bf16; q, k, v, cu_seqlens, nseq, max_seqlen, B, T, scale,
  * causal and dtype as diffattn_v2_fwd.  Hq / Hkv must be a multiple of
- * ratio + 1 (a block never spans two KV heads); ratio in 1..15.  Each signal
- * head's workgroup recomputes its block's noise head, so the attention work
- * is 2 Hs head-passes, not Hq.
+ * ratio + 1 (a block never spans two KV heads); ratio in 1..15.  With ratio
+ * 3 or 7 and Hq / Hkv a multiple of 4 (ratio 3) or 8 (ratio 7), every query
+ * head is attended once and the noise head is shared through on-chip memory;
+ * for other ratios each signal head's workgroup recomputes its block's noise
+ * head (2 Hs head-passes instead of Hq).
  */
 DIFFATTN_API int diffattn_gda_fwd(const void* q, const void* k, const void* v,
                                   const float* lambda_logit, void* out, const int* cu_seqlens,
