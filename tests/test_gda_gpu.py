@@ -3,8 +3,8 @@ and one noise head inside a GQA group) through the C ABI, against the oracle's
 gda_* functions.
 
 Bounds as the V2 tests: max|err| <= 2e-2 * RMS(V) and relative L2 <= 1e-2.
-Small cases run every row (ratios 1, 3 and 4; blocks of one, two and several
-per group; ragged tails; causal and not; d 64 and 128); the full-size
+Small cases run every row (ratios 1, 2, 3, 4 and 7; blocks of one, two and
+several per group; ragged tails; causal and not; d 64 and 128); the full-size
 workloads run as the benchmark launches them and are checked on sampled rows.
 Needle keys make single heads' outputs large, so a signal or noise head taken
 from the wrong block shows at once.
@@ -59,9 +59,11 @@ def on(x, dev):
     return {k: (None if v is None else v.to(dev)) for k, v in x.items()}
 
 
-# (Hq, Hkv, ratio): blocks per GQA group 2, 1, 2, 1, 4; output heads per
-# group 6, 3, 8, 4, 4 (so one, two and four output heads share a workgroup)
-SHAPES = [(16, 2, 3), (12, 3, 3), (20, 2, 4), (10, 2, 4), (16, 2, 1)]
+# (Hq, Hkv, ratio): blocks per GQA group 2, 1, 2, 1, 4, 1, 2; output heads per
+# group 6, 3, 8, 4, 4, 7, 4 (so one, two and four output heads share a
+# workgroup).  Ratios 3 and 7 take the path that attends every head once and
+# shares the noise head on chip; 2 and 4 recompute it per signal head.
+SHAPES = [(16, 2, 3), (12, 3, 3), (20, 2, 4), (10, 2, 4), (16, 2, 1), (16, 2, 7), (12, 2, 2)]
 
 
 @pytest.mark.parametrize("Hq,Hkv,ratio", SHAPES)
@@ -117,21 +119,25 @@ def test_gda_non_default_scale(gpu):
     compare(out.float().cpu().numpy(), ref, rms(x["v"]), "gda scale 0.3")
 
 
-def test_gda_needle_heads(gpu):
+@pytest.mark.parametrize("Hq,Hkv,ratio,heads", [
+    (20, 2, 4, (0, 4, 5, 9, 13, 14, 19)),       # per-signal-head recompute
+    (16, 2, 3, (0, 3, 5, 7, 10, 11, 15)),       # noise heads shared on chip
+])
+def test_gda_needle_heads(gpu, Hq, Hkv, ratio, heads):
     # one needle key per chosen query head: that head's output becomes ~v of
     # the needle, so each output head's result names the signal and noise
     # heads it used
-    w = inp.V2_PREFILL.with_shape(B=1, T=256, Hq=20, Hkv=2, ratio=4)
+    w = inp.V2_PREFILL.with_shape(B=1, T=256, Hq=Hq, Hkv=Hkv, ratio=ratio)
     x = inp.v2_inputs(w)
     g = w.Hq // w.Hkv
     row = 255
-    for j, t in ((0, 10), (4, 20), (5, 30), (9, 40), (13, 50), (14, 60), (19, 70)):
-        x["k"][0, t, j // g] = (300.0 * x["q"][0, row, j].float()).to(torch.bfloat16)
-    ref = oracle.gda_forward(x["q"], x["k"], x["v"], x["logit"], 4)
+    for n, j in enumerate(heads):
+        x["k"][0, 10 * (n + 1), j // g] = (300.0 * x["q"][0, row, j].float()).to(torch.bfloat16)
+    ref = oracle.gda_forward(x["q"], x["k"], x["v"], x["logit"], ratio)
     xg = on(x, gpu)
-    out = da.gda_fwd(xg["q"], xg["k"], xg["v"], xg["logit"], 4)
+    out = da.gda_fwd(xg["q"], xg["k"], xg["v"], xg["logit"], ratio)
     torch.cuda.synchronize()
-    compare(out.float().cpu().numpy(), ref, rms(x["v"]), "gda needles r=4")
+    compare(out.float().cpu().numpy(), ref, rms(x["v"]), f"gda needles r={ratio}")
 
 
 @pytest.mark.parametrize("w", [inp.GDA_PREFILL_R3, inp.GDA_PREFILL_R4], ids=lambda w: w.name)
