@@ -404,7 +404,7 @@ constexpr int kDkvKeys = kWaves * 16;
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, const float* lse2,
-                                                                  const float* sig) {
+                                                                  const float* sig, int cohort) {
   using TL = BTile<D>;
   constexpr int NC = D / 32;
   constexpr int NDB = D / 16;
@@ -421,13 +421,26 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
   const int c16 = lane & 15;
 
   // blocks: padded batches take the key tiles with the most query tiles first,
-  // then (batch, KV head); packed batches go sequence by sequence
+  // then (batch, KV head); packed batches go sequence by sequence.  When the
+  // (batch, KV head) pairs split evenly over the 8 XCDs (workgroups go to
+  // XCDs round robin), each XCD instead works through its pairs one at a
+  // time, key tiles in order, so that the workgroups running together on it
+  // read the same Q and dout tiles.
   SeqView sv;
   int kt, kvh;
   if (a.cu_seqlens == nullptr) {
     const int nbg = a.B * a.Hkv;
-    kt = blockIdx.x / nbg;
-    const int bg = blockIdx.x - kt * nbg;
+    int bg;
+    if (nbg % 8 == 0) {
+      const int nkt = (a.T + kDkvKeys - 1) / kDkvKeys;
+      const int xcd = blockIdx.x % 8;
+      const int local = blockIdx.x / 8;
+      kt = local % nkt;
+      bg = xcd + 8 * (local / nkt);
+    } else {
+      kt = blockIdx.x / nbg;
+      bg = blockIdx.x - kt * nbg;
+    }
     const int b = bg / a.Hkv;
     kvh = bg - b * a.Hkv;
     sv.tok0 = (long long)b * a.T;
@@ -445,10 +458,16 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
   const int hpairs = a.Hq / 2;
   const int key0 = kt * kDkvKeys;
   const int qt0 = CAUSAL ? key0 / kQRows : 0;
-  // (pair, query tile) items, last query tile first: the workgroups of one KV
-  // head (on one XCD) then walk the same Q / dout tiles at the same time and
-  // share them in L2
+  // (pair, query tile) items.  The workgroups that start together on an XCD
+  // (its first `cohort` key tiles of a (batch, KV head) pair) walk the query
+  // tiles last first, so they read the same Q / dout tiles at the same time
+  // and share them in L2.  The later ones start one by one as those finish,
+  // each when the others have reached (about) its first query tile; they walk
+  // upwards from there, so they too stay on the same tile.  The order changes
+  // nothing but the memory traffic: dK and dV sum over all items.
   const int n_items = npairs * (n_qt - qt0);
+  const bool ascending = kt >= cohort;
+  auto qt_of = [&](int item) { return ascending ? qt0 + item / npairs : n_qt - 1 - item / npairs; };
 
   // this wave's 16 keys: K^T and V^T B operands (lane column = key)
   const int key = key0 + wave * 16 + c16;
@@ -468,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
   const TileLoader<D, true> o_ld((size_t)hpairs * D, wave, lane);  // dout
   auto load = [&](int item, uint8_t* st) {
     const int pp = item % npairs;
-    const int qt = n_qt - 1 - item / npairs;
+    const int qt = qt_of(item);
     const int r0 = qt * kQRows;
     const int je = kvh * group + 2 * pp;  // even head of the pair
     const int pair = je / 2;
@@ -502,7 +521,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
   // MASKED: the item's query tile touches the diagonal or a ragged end
   auto work = [&](auto masked, int item, const uint8_t* st) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
-    const int qt = n_qt - 1 - item / npairs;
+    const int qt = qt_of(item);
     const int r0 = qt * kQRows;
     if (CAUSAL && r0 + kQRows <= wave_key_lo) return;  // every key of the wave is above the rows
     const uint8_t* qle = st;
@@ -592,7 +611,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
     __syncthreads();
   }
   auto item_masked = [&](int item) {
-    const int r0 = (n_qt - 1 - item / npairs) * kQRows;
+    const int r0 = qt_of(item) * kQRows;
     return (CAUSAL && r0 < key0 + kDkvKeys) || r0 + kQRows > T || key0 + kDkvKeys > T;
   };
   auto run = [&](int item, const uint8_t* st) __attribute__((always_inline)) {
@@ -651,6 +670,11 @@ hipError_t launch_d(const V2BwdArgs& a, hipStream_t stream) {
   };
   const long long dq_blocks = tiles(qtile) * (a.Hq / (2 * PW));
   const long long kv_blocks = tiles(kDkvKeys) * a.Hkv;
+  // dK/dV workgroups that start together on one XCD (one per CU; padded
+  // batches whose (batch, KV head) pairs split evenly over the 8 XCDs)
+  const int cohort = (a.cu_seqlens == nullptr && (a.B * a.Hkv) % 8 == 0 && a.causal)
+                         ? device_cu_count() / 8
+                         : 0x7fffffff;
   if (dq_blocks > 0x7fffffffLL || kv_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
 #define DQ(PWV, C)                                                                               \
   hipLaunchKernelGGL((v2_bwd_dq_kernel<D, PWV, C>), dim3((unsigned)dq_blocks), dim3(kThreads), 0, \
@@ -660,13 +684,13 @@ hipError_t launch_d(const V2BwdArgs& a, hipStream_t stream) {
     else if (PW == 2) DQ(2, true);
     else DQ(1, true);
     hipLaunchKernelGGL((v2_bwd_dkdv_kernel<D, true>), dim3((unsigned)kv_blocks), dim3(kThreads), 0,
-                       stream, a, (const float*)lse2, (const float*)sig);
+                       stream, a, (const float*)lse2, (const float*)sig, cohort);
   } else {
     if (PW == 4) DQ(4, false);
     else if (PW == 2) DQ(2, false);
     else DQ(1, false);
     hipLaunchKernelGGL((v2_bwd_dkdv_kernel<D, false>), dim3((unsigned)kv_blocks), dim3(kThreads),
-                       0, stream, a, (const float*)lse2, (const float*)sig);
+                       0, stream, a, (const float*)lse2, (const float*)sig, cohort);
   }
 #undef DQ
   return hipGetLastError();
