@@ -445,7 +445,8 @@ constexpr int kKvWaves8 = 8;  // waves of the dK/dV workgroup
 template <int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kKvWaves8 * kWave) void v1_bwd_dkdv_kernel(V1BwdArgs a, int Tp,
                                                                        const uint16_t* dz,
-                                                                       const float* stats) {
+                                                                       const float* stats,
+                                                                       int cohort) {
   using TK = BTile<D>;
   using TV = BTile<DV>;
   constexpr int NC = D / 32;     // k-steps of the products over d
@@ -469,14 +470,35 @@ __global__ __launch_bounds__(kKvWaves8 * kWave) void v1_bwd_dkdv_kernel(V1BwdArg
   const int T = a.T;
   const int BH = a.B * a.H;
   const int n_qt = (T + kKvRows - 1) / kKvRows;
-  const int kt = blockIdx.x / BH;  // key tiles with the most query tiles first
-  const int bh = blockIdx.x - kt * BH;
+  // key tiles with the most query tiles first.  When the (batch, head) pairs
+  // split evenly over the 8 XCDs (workgroups go to XCDs round robin), each
+  // XCD works through its pairs one at a time, key tiles in order, in rounds
+  // of `cohort` workgroups (one per CU): see the item order below.
+  int kt, bh, local = -1;
+  if (BH % 8 == 0) {
+    const int xcd = blockIdx.x % 8;
+    local = blockIdx.x / 8;
+    const int nkt = (T + kKvKeys - 1) / kKvKeys;
+    kt = local % nkt;
+    bh = xcd + 8 * (local / nkt);
+  } else {
+    kt = blockIdx.x / BH;
+    bh = blockIdx.x - kt * BH;
+  }
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const int key0 = kt * kKvKeys;
   const int key_w = key0 + wave * 16;
   const int qt0 = CAUSAL ? key0 / kKvRows : 0;
-  const int n_items = n_qt - qt0;  // query tiles, last first
+  // Query tiles.  A round of workgroups that starts together walks them last
+  // first (they read the same Q / dz tiles at the same time and share them in
+  // L2) and ends one after another; the next round starts one by one, the
+  // longest first, each when the others have reached about its first tile,
+  // so it walks upwards and stays on their tile.  Only the memory traffic
+  // depends on the order.
+  const int n_items = n_qt - qt0;
+  const bool ascending = local >= 0 && ((local / cohort) & 1);
+  auto qt_of = [&](int item) { return ascending ? qt0 + item : n_qt - 1 - item; };
 
   const int key = key_w + c16;  // this lane's key column
   const int keyc = min(key, T - 1);
@@ -498,7 +520,7 @@ __global__ __launch_bounds__(kKvWaves8 * kWave) void v1_bwd_dkdv_kernel(V1BwdArg
   const TileLoader<D, true, kKvWaves8, kKvRows> q_ld(qstr, wave, lane);
   const TileLoader<DV, true, kKvWaves8, kKvRows> z_ld(zstr, wave, lane);
   auto load = [&](int item, uint8_t* st) {
-    const int r0 = (n_qt - 1 - item) * kKvRows;
+    const int r0 = qt_of(item) * kKvRows;
     const size_t rr = ((size_t)b * T + r0) * a.H + h;
     q_ld.load(a.q1 + rr * D, T - r0, st, wave, lane);
     q_ld.load(a.q2 + rr * D, T - r0, st + kQB, wave, lane);
@@ -523,7 +545,7 @@ __global__ __launch_bounds__(kKvWaves8 * kWave) void v1_bwd_dkdv_kernel(V1BwdArg
   const int vrow = wave * 16 + c16;
 
   auto work = [&](int item, const uint8_t* st) __attribute__((always_inline)) {
-    const int r0 = (n_qt - 1 - item) * kKvRows;
+    const int r0 = qt_of(item) * kKvRows;
     if (CAUSAL && r0 + kKvRows - 1 < key_w) return;  // every key of the wave is above the rows
     const uint8_t* q1l = st;
     const uint8_t* q2l = st + kQB;
@@ -674,20 +696,23 @@ hipError_t launch_typed(const V1BwdArgs& a, hipStream_t stream) {
   const long long dq_blocks = (long long)((a.T + kDqWaves * kRows - 1) / (kDqWaves * kRows)) * BH;
   const long long kv_blocks = (long long)((a.T + kKvWaves8 * 16 - 1) / (kKvWaves8 * 16)) * BH;
   if (dq_blocks > 0x7fffffffLL || kv_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // dK/dV workgroups that run together on one XCD (one per CU), causal only:
+  // without the mask every workgroup has the same work and rounds stay whole
+  const int cohort = a.causal ? device_cu_count() / 8 : 0x7fffffff;
   if (a.causal) {
     hipLaunchKernelGGL((v1_bwd_dq_kernel<D, DV, true>), dim3((unsigned)dq_blocks),
                        dim3(kDqWaves * kWave), 0, stream, a, L.Tp, (const uint16_t*)dz,
                        (const float*)stats);
     hipLaunchKernelGGL((v1_bwd_dkdv_kernel<D, DV, true>), dim3((unsigned)kv_blocks),
                        dim3(kKvWaves8 * kWave), 0, stream, a, L.Tp, (const uint16_t*)dz,
-                       (const float*)stats);
+                       (const float*)stats, cohort);
   } else {
     hipLaunchKernelGGL((v1_bwd_dq_kernel<D, DV, false>), dim3((unsigned)dq_blocks),
                        dim3(kDqWaves * kWave), 0, stream, a, L.Tp, (const uint16_t*)dz,
                        (const float*)stats);
     hipLaunchKernelGGL((v1_bwd_dkdv_kernel<D, DV, false>), dim3((unsigned)kv_blocks),
                        dim3(kKvWaves8 * kWave), 0, stream, a, L.Tp, (const uint16_t*)dz,
-                       (const float*)stats);
+                       (const float*)stats, cohort);
   }
   return hipGetLastError();
 }

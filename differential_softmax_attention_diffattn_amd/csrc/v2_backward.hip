@@ -428,13 +428,14 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
   // read the same Q and dout tiles.
   SeqView sv;
   int kt, kvh;
+  int local = -1;  // position in its XCD's sequence of workgroups, when ordered so
   if (a.cu_seqlens == nullptr) {
     const int nbg = a.B * a.Hkv;
     int bg;
     if (nbg % 8 == 0) {
       const int nkt = (a.T + kDkvKeys - 1) / kDkvKeys;
       const int xcd = blockIdx.x % 8;
-      const int local = blockIdx.x / 8;
+      local = blockIdx.x / 8;
       kt = local % nkt;
       bg = xcd + 8 * (local / nkt);
     } else {
@@ -458,15 +459,17 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
   const int hpairs = a.Hq / 2;
   const int key0 = kt * kDkvKeys;
   const int qt0 = CAUSAL ? key0 / kQRows : 0;
-  // (pair, query tile) items.  The workgroups that start together on an XCD
-  // (its first `cohort` key tiles of a (batch, KV head) pair) walk the query
-  // tiles last first, so they read the same Q / dout tiles at the same time
-  // and share them in L2.  The later ones start one by one as those finish,
-  // each when the others have reached (about) its first query tile; they walk
-  // upwards from there, so they too stay on the same tile.  The order changes
-  // nothing but the memory traffic: dK and dV sum over all items.
+  // (pair, query tile) items.  An XCD runs `cohort` workgroups at a time (one
+  // per CU), in rounds of its sequence: a round that starts together (key
+  // tiles in order, so item counts falling) walks the query tiles last first
+  // -- its workgroups read the same Q / dout tiles at the same time and share
+  // them in L2 -- and ends one workgroup after another; the next round then
+  // starts one by one, the longest first, each when the others have reached
+  // about its first query tile, so it walks upwards and stays on their tile,
+  // and ends together; and so on.  The order changes nothing but the memory
+  // traffic: dK and dV sum over all items.
   const int n_items = npairs * (n_qt - qt0);
-  const bool ascending = kt >= cohort;
+  const bool ascending = local >= 0 && ((local / cohort) & 1);
   auto qt_of = [&](int item) { return ascending ? qt0 + item / npairs : n_qt - 1 - item / npairs; };
 
   // this wave's 16 keys: K^T and V^T B operands (lane column = key)
