@@ -321,7 +321,16 @@ def main():
         extra = {"nseq": len(w.lengths), "traffic": hbm_traffic(leg, w.name)}
         if len(w.lengths) <= 16:
             extra["lengths"] = list(w.lengths)
-        mfma_leg(key, w.name, f, sum(v2_flops_seq(n, w.Hq, w.d) for n in w.lengths), extra)
+        flop = sum(v2_flops_seq(n, w.Hq, w.d) for n in w.lengths)
+        # bytes the call must move: q, k, v and the logits in, out back
+        byts = float(N * (w.Hq * w.d + 2 * w.Hkv * w.d) * 2 + N * (w.Hq // 2) * 4
+                     + N * (w.Hq // 2) * w.d * 2)
+        if max(w.lengths) <= 256:
+            # short sequences: a few FLOP per byte, so the HBM roofline bounds it
+            hbm_leg(key, w.name, f, byts, {**extra, "flop": flop, "bound": "hbm"})
+            secondary[key]["TFLOP/s"] = round(flop / (secondary[key]["ms"] * 1e-3) / 1e12, 2)
+        else:
+            mfma_leg(key, w.name, f, flop, {**extra, "bytes": byts})
         del x, o
         torch.cuda.empty_cache()
         if cpu and leg == "varlen":

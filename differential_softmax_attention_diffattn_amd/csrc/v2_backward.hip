@@ -68,9 +68,11 @@ __host__ __device__ __forceinline__ long long pad64(long long x) { return (x + 6
 // Tile t (of `rows`-row tiles, numbered sequence by sequence, a sequence's
 // tiles consecutive) -> its sequence and the tile's index inside it.  Returns
 // false for a tile that does not exist.  Padded batches divide; packed ones
-// number the tiles by slots (varlen.h) and find the sequence by binary search.
+// number the tiles by slots (varlen.h) and find the sequence by a search over cu_seqlens.
 // A packed sequence's workspace rows start at its 64-row slot: 64 * (
 // floor(cu[s] / 64) + s), so they fit in floor(N / 64) * 64 + 64 nseq rows.
+// WAVE: the whole wave searches together (every lane active, t uniform).
+template <bool WAVE>
 __device__ __forceinline__ bool tile_of(const V2BwdArgs& a, long long t, int rows, SeqView& sv,
                                         int& tile) {
   if (a.cu_seqlens == nullptr) {
@@ -83,7 +85,8 @@ __device__ __forceinline__ bool tile_of(const V2BwdArgs& a, long long t, int row
     sv.ws0 = b * pad64(a.T);
     return true;
   }
-  const int s = slot_sequence(a.cu_seqlens, a.nseq, t, rows);
+  const int s = WAVE ? slot_sequence_wave(a.cu_seqlens, a.nseq, t, rows)
+                     : slot_sequence(a.cu_seqlens, a.nseq, t, rows);
   const int c0 = a.cu_seqlens[s];
   const int len = a.cu_seqlens[s + 1] - c0;
   const long long k = t - slot_start(a.cu_seqlens, s, rows);
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(256) void v2_bwd_pre_kernel(V2BwdArgs a, float* lse
   const long long prow = item / h;  // workspace row: 64-row tile prow / 64
   SeqView sv;
   int tile;
-  if (!tile_of(a, prow / 64, 64, sv, tile)) return;  // rows past the last sequence: unused
+  if (!tile_of<false>(a, prow / 64, 64, sv, tile)) return;  // rows past the last sequence: unused
   const int t = tile * 64 + (int)(prow % 64);
   const size_t ws = (size_t)(2 * p) * Np + sv.ws0 + t;  // [2p][row]
   const size_t wsig = (size_t)p * Np + sv.ws0 + t;
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, con
   const int hg = blockIdx.x % n_hg;
   SeqView sv;
   int qt;
-  if (!tile_of(a, blockIdx.x / n_hg, QTILE, sv, qt)) return;  // uniform over the block
+  if (!tile_of<true>(a, blockIdx.x / n_hg, QTILE, sv, qt)) return;  // uniform over the block
   qt = (sv.L + QTILE - 1) / QTILE - 1 - qt;  // a sequence's longest (last) tile first
   const int T = sv.L;
   const long long Np = a.Np;
@@ -449,7 +452,7 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
     sv.ws0 = (long long)b * pad64(a.T);
   } else {
     kvh = blockIdx.x % a.Hkv;
-    if (!tile_of(a, blockIdx.x / a.Hkv, kDkvKeys, sv, kt)) return;  // uniform over the block
+    if (!tile_of<true>(a, blockIdx.x / a.Hkv, kDkvKeys, sv, kt)) return;  // uniform over the block
   }
   const int T = sv.L;
   const long long Np = a.Np;

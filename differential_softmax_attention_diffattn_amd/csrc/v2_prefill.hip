@@ -100,14 +100,14 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   // one pair group per KV head and 8 of them, blocks of one KV head land on one
   // XCD and that XCD's CUs work through the tiles of one sequence together,
   // sharing its K/V tiles in L2.  Packed batches number the tiles by slots
-  // (varlen.h): a binary search over cu_seqlens finds the sequence, and the
+  // (varlen.h): a search over cu_seqlens by the whole wave finds the sequence, and the
   // blocks of empty slots exit.
   const int n_hg = SHARED ? a.Hq / 2 / PW : a.nout / PW;
   const int hg = blockIdx.x % n_hg;
   const int t = blockIdx.x / n_hg;
   int tok0, L, qt;
   if (a.cu_seqlens != nullptr) {
-    const int seq = slot_sequence(a.cu_seqlens, a.nseq, t, QTILE);
+    const int seq = slot_sequence_wave(a.cu_seqlens, a.nseq, t, QTILE);
     tok0 = a.cu_seqlens[seq];
     L = a.cu_seqlens[seq + 1] - tok0;
     const int nt = (L + QTILE - 1) / QTILE;
