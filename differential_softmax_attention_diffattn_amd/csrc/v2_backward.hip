@@ -620,26 +620,42 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
     const int r0 = qt_of(item) * kQRows;
     return (CAUSAL && r0 < key0 + kDkvKeys) || r0 + kQRows > T || key0 + kDkvKeys > T;
   };
-  auto run = [&](int item, const uint8_t* st) __attribute__((always_inline)) {
-    // (without the causal mask a single instance is kept: two of them make the
-    // register allocator spill)
-    if (!CAUSAL || item_masked(item))
-      work(BoolTag<true>{}, item, st);
-    else
-      work(BoolTag<false>{}, item, st);
+  // One item with the stage chosen at run time: the next item's loads, the
+  // work, the wait.  (Reads from a stage chosen at run time wait for every
+  // load in flight; only the few masked items take this path.)
+  auto one_dynamic = [&](int it) __attribute__((always_inline)) {
+    if (it + 1 < n_items) load(it + 1, ((it + 1) & 1) ? st1 : st0);
+    work(BoolTag<true>{}, it, (it & 1) ? st1 : st0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
   };
-  int it = 0;
-  for (; it + 2 <= n_items; it += 2) {  // unrolled by two: each stage a fixed LDS object
+  // Masked items (the diagonal query tiles and a ragged last one) lie at the
+  // two ends of the item order; the unmasked run between them takes the
+  // mask-free work in a loop unrolled by two, each stage a fixed LDS object.
+  // Separate loops keep each work instance in one register assignment (one
+  // loop choosing between a masked and an unmasked instance per item made
+  // the compiler copy the dK/dV accumulators between them at every item).
+  int m0 = 0, m1 = n_items;
+  if (CAUSAL) {
+    while (m0 < n_items && item_masked(m0)) ++m0;
+    while (m1 > m0 && item_masked(m1 - 1)) --m1;
+  } else {
+    m0 = m1 = n_items;  // one instance (two make the register allocator spill)
+  }
+  const int main_b = min(m1, (m0 + 1) & ~1);  // the unrolled run starts at an even item
+  const int main_e = main_b + ((m1 - main_b) & ~1);
+  for (int it = 0; it < main_b; ++it) one_dynamic(it);
+  for (int it = main_b; it < main_e; it += 2) {
     load(it + 1, st1);
-    run(it, st0);
+    work(BoolTag<false>{}, it, st0);
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
     if (it + 2 < n_items) load(it + 2, st0);
-    run(it + 1, st1);
+    work(BoolTag<false>{}, it + 1, st1);
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
   }
-  if (it < n_items) run(it, st0);
+  for (int it = main_e; it < n_items; ++it) one_dynamic(it);
 
   // C layout: lane column = d (16 db + c16), rows = keys 4 g + i of the wave's 16
 #pragma unroll
