@@ -107,11 +107,13 @@ __global__ __launch_bounds__(kThreads, 1) void v2_prefill_kernel(V2Args a) {
   const int t = blockIdx.x / n_hg;
   int tok0, L, qt;
   if (a.cu_seqlens != nullptr) {
-    const int seq = slot_sequence_wave(a.cu_seqlens, a.nseq, t, QTILE);
+    // every sequence within one query tile: tile t is sequence t (no slots)
+    const bool one_tile = a.max_seqlen <= QTILE;
+    const int seq = one_tile ? t : slot_sequence_wave(a.cu_seqlens, a.nseq, t, QTILE);
     tok0 = a.cu_seqlens[seq];
     L = a.cu_seqlens[seq + 1] - tok0;
     const int nt = (L + QTILE - 1) / QTILE;
-    const int tile = (int)(t - slot_start(a.cu_seqlens, seq, QTILE));
+    const int tile = one_tile ? 0 : (int)(t - slot_start(a.cu_seqlens, seq, QTILE));
     if (tile >= nt) return;  // an empty slot: uniform over the block
     qt = nt - 1 - tile;
   } else {
@@ -553,9 +555,9 @@ hipError_t launch_typed(const V2Args& a, hipStream_t stream) {
   constexpr int QTILE = kRows * (kWaves / PW);
   // query tiles: B x ceil(T / QTILE) for padded batches, the tile slots of
   // varlen.h for packed ones
-  const long long tiles = a.cu_seqlens != nullptr
-                              ? slot_count(a.N, a.nseq, a.max_seqlen, QTILE)
-                              : (long long)((a.T + QTILE - 1) / QTILE) * a.nseq;
+  const long long tiles = a.cu_seqlens == nullptr ? (long long)((a.T + QTILE - 1) / QTILE) * a.nseq
+                          : a.max_seqlen <= QTILE ? (long long)a.nseq
+                                                  : slot_count(a.N, a.nseq, a.max_seqlen, QTILE);
   const long long blocks = tiles * (SHARED ? a.Hq / 2 / PW : a.nout / PW);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;

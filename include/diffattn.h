@@ -176,8 +176,10 @@ DIFFATTN_API size_t diffattn_v1_bwd_workspace_bytes(int B, int T, int H, int d, 
  *   within itself.  cu_seqlens is a DEVICE int32 array [nseq + 1], non-
  *   decreasing, starting at 0.  Shapes as above with [B, T] replaced by
  *   [N total tokens]; B is ignored and T is N = cu_seqlens[nseq] (it sizes the
- *   launch), or 0 when the caller does not know N; then nseq * max_seqlen
- *   bounds the tokens, and max_seqlen must be >= every sequence length.
+ *   launch), or 0 when the caller does not know N (then nseq * max_seqlen
+ *   bounds the tokens).  max_seqlen must be >= every sequence length: it also
+ *   sizes the launch (one workgroup row per sequence when every sequence fits
+ *   one query tile).
  *
  *   scale : softmax scale; <= 0 selects 1/sqrt(d).
  * Supported: dtype DIFFATTN_BF16, d in {64, 128}.

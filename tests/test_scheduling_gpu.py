@@ -140,3 +140,22 @@ def test_decode_single_sequence_full_cache(gpu):
     ref1 = oracle.v1_decode(y["q1"], y["q2"], y["k1_cache"], y["k2_cache"], y["v_cache"], lam, li,
                             w1.eps)
     compare(out1.cpu().numpy(), ref1, rms(y["v_cache"]), "v1 decode B1 S32768")
+
+
+@pytest.mark.parametrize("lengths,Hq,Hkv,max_seqlen", [
+    ((1, 32, 0, 17, 31, 5, 32, 2) * 40, 64, 8, 32),    # 32-row query tiles: one per sequence
+    ((64, 1, 0, 33, 63, 2) * 30, 8, 2, 64),            # 64-row query tiles (two pairs per KV head)
+    ((5, 9, 1) * 50, 16, 2, 20),                       # max_seqlen above every length
+])
+def test_packed_forward_every_sequence_in_one_tile(gpu, lengths, Hq, Hkv, max_seqlen):
+    # when max_seqlen fits one query tile the launch has one tile per sequence
+    # and no search over cu_seqlens
+    w = inp.V2_VARLEN.with_shape(lengths=tuple(lengths), Hq=Hq, Hkv=Hkv)
+    x = inp.v2_inputs(w)
+    xg = {k: v.to(gpu) for k, v in x.items()}
+    out = da.v2_fwd(xg["q"], xg["k"], xg["v"], xg["logit"], cu_seqlens=xg["cu_seqlens"],
+                    max_seqlen=max_seqlen)
+    torch.cuda.synchronize()
+    ref = oracle.v2_varlen_forward(x["q"], x["k"], x["v"], x["logit"], x["cu_seqlens"])
+    compare(out.float().cpu().numpy(), ref, rms(x["v"]),
+            f"v2 packed one tile per sequence nseq={len(lengths)} Hq={Hq} max_seqlen={max_seqlen}")
