@@ -279,6 +279,13 @@ __global__ __launch_bounds__(kDqWaves * kWave, 1) void v1_bwd_dq_kernel(V1BwdArg
   }
   const int tr_key = 4 * g + (c16 >> 2);
   const int tr_byte = 8 * (c16 & 3);
+  // the V A-read offsets (16-byte chunk 4c + g of rows c16 and 16 + c16): the
+  // most numerous reads of a step, so formed once here and kept in registers
+  int vo[2][NCV];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int c = 0; c < NCV; ++c) vo[kb][c] = rows_base<DV>(kb * 16 + c16) ^ (g << 4) ^ (c << 6);
 
   auto pack8 = [](const float (&x)[8]) {
     return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
@@ -294,10 +301,8 @@ __global__ __launch_bounds__(kDqWaves * kWave, 1) void v1_bwd_dq_kernel(V1BwdArg
     // byte 16 (g & 1); V A reads: 16-byte chunk 4c + g (the row layout's
     // swizzle class changes with the 16-key block, hence two bases).
     int bk = trans_base<D>(c16, (g & 1) * 16) ^ ((g >> 1) << 5);
-    int bv0 = rows_base<DV>(c16) ^ (g << 4);
-    int bv1 = rows_base<DV>(16 + c16) ^ (g << 4);
     int tk = trans_base<D>(tr_key, tr_byte);
-    asm volatile("" : "+v"(bk), "+v"(bv0), "+v"(bv1), "+v"(tk));
+    asm volatile("" : "+v"(bk), "+v"(tk));
     f32x4 s1[2], s2[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -311,11 +316,10 @@ __global__ __launch_bounds__(kDqWaves * kWave, 1) void v1_bwd_dq_kernel(V1BwdArg
         s1[kb] = mfma_bf16(*reinterpret_cast<const u32x4*>(l1 + off), q1f[c], s1[kb]);
         s2[kb] = mfma_bf16(*reinterpret_cast<const u32x4*>(l2 + off), q2f[c], s2[kb]);
       }
-      const int bv = kb ? bv1 : bv0;
 #pragma unroll
       for (int c = 0; c < NCV; ++c)
         dp[kb] = mfma_bf16(
-            *reinterpret_cast<const u32x4*>(lv + (bv ^ (c << 6)) + cc * 32 * TV::kRowBytes),
+            *reinterpret_cast<const u32x4*>(lv + vo[kb][c] + cc * 32 * TV::kRowBytes),
             dzf[c], dp[kb]);
     }
     // K1^T and K2^T fragments of the dQ products (transposing reads), kKtRing
