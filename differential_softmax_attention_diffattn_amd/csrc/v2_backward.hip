@@ -171,6 +171,98 @@ __global__ __launch_bounds__(256) void v2_bwd_pre_kernel(V2BwdArgs a, float* lse
   }
 }
 
+// The same preprocessing for Hq / 2 a multiple of 16, by tiles of 16 workspace
+// rows x 16 pairs: a workgroup's 16 lane groups take the 16 pairs of one row
+// per pass (so the per-token reads of dout, O, lse and logits stay contiguous,
+// as above), and the per-row values collect in LDS and go out as 64-byte runs
+// of 16 rows per head (the per-item layout above writes each 4-byte value to a
+// different cache line).  All 16 rows lie in one 64-row workspace tile, so the
+// sequence is found once; workspace row = 16 * row tile + pass.
+template <int D>
+__global__ __launch_bounds__(256) void v2_bwd_pre_tiled_kernel(V2BwdArgs a, float* lse2, float* sig) {
+  constexpr int EPL = D / 16;
+  static_assert(EPL == 8 || EPL == 4, "head dim 128 or 64");
+  constexpr int kPass = 16;   // rows per tile, one per pass
+  constexpr int kGroup = 4;   // passes whose loads are in flight together
+  __shared__ float sd[32][kPass + 1], sl[32][kPass + 1], ss[16][kPass + 1];
+  const int h = a.Hq / 2;
+  const int n_pt = h / 16;
+  const long long rt = blockIdx.x / n_pt;
+  const int p0 = (int)(blockIdx.x % n_pt) * 16;
+  const int j = threadIdx.x >> 4;  // pair p0 + j
+  const int l16 = threadIdx.x & 15;
+  const int p = p0 + j;
+  const long long Np = a.Np;
+  const long long row0 = rt * kPass;
+  if (row0 >= Np) return;
+  SeqView sv;
+  int tile;
+  if (!tile_of<false>(a, row0 / 64, 64, sv, tile)) return;  // rows past the last sequence: unused
+  const int t0 = tile * 64 + (int)(row0 % 64);  // the first pass's row inside its sequence
+#pragma unroll
+  for (int i0 = 0; i0 < kPass; i0 += kGroup) {
+    uint32_t gw[kGroup][EPL / 2], ew[kGroup][EPL / 2], ow[kGroup][EPL / 2];
+    float lg[kGroup], le[kGroup], lo[kGroup];
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {  // loads of kGroup passes first (padding rows read row 0)
+      const int t = t0 + i0 + u;
+      const size_t tok = (size_t)(sv.tok0 + (t < sv.L ? t : 0));
+      lg[u] = a.logit[tok * h + p];
+      le[u] = a.lse[tok * a.Hq + 2 * p];
+      lo[u] = a.lse[tok * a.Hq + 2 * p + 1];
+      const uint16_t* gp = a.dout + (tok * h + p) * D + l16 * EPL;
+      const uint16_t* ep = a.o_heads + (tok * a.Hq + 2 * p) * D + l16 * EPL;
+      if constexpr (EPL == 8) {
+        const u32x4 g4 = ldg128(gp), e4 = ldg128(ep), o4 = ldg128(ep + D);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) gw[u][q] = g4[q], ew[u][q] = e4[q], ow[u][q] = o4[q];
+      } else {
+        const u32x2 g2 = *reinterpret_cast<const u32x2*>(gp);
+        const u32x2 e2 = *reinterpret_cast<const u32x2*>(ep);
+        const u32x2 o2 = *reinterpret_cast<const u32x2*>(ep + D);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) gw[u][q] = g2[q], ew[u][q] = e2[q], ow[u][q] = o2[q];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u) {
+      const int i = i0 + u;
+      const int t = t0 + i;
+      float de = 0.f, dod = 0.f;
+#pragma unroll
+      for (int q = 0; q < EPL / 2; ++q) {
+        de = fmaf(bf16lo_to_f32(gw[u][q]), bf16lo_to_f32(ew[u][q]), de);
+        de = fmaf(bf16hi_to_f32(gw[u][q]), bf16hi_to_f32(ew[u][q]), de);
+        dod = fmaf(bf16lo_to_f32(gw[u][q]), bf16lo_to_f32(ow[u][q]), dod);
+        dod = fmaf(bf16hi_to_f32(gw[u][q]), bf16hi_to_f32(ow[u][q]), dod);
+      }
+      de = row16_sum(de);
+      dod = row16_sum(dod);
+      if (l16 == 0) {
+        const bool valid = t < sv.L;  // padding rows: finite zeros (the tiles read and mask them)
+        const float s = sigmoid_f32(lg[u]);
+        sd[2 * j][i] = valid ? de : 0.f;            // <dO_2p, O_2p> with dO_2p = dout_p
+        sd[2 * j + 1][i] = valid ? -s * dod : 0.f;  // <dO_2p+1, O_2p+1>, dO_2p+1 = -s dout_p
+        sl[2 * j][i] = valid ? le[u] * kLog2e : 0.f;
+        sl[2 * j + 1][i] = valid ? lo[u] * kLog2e : 0.f;
+        ss[j][i] = valid ? s : 0.f;
+        if (valid) a.dlogit[(size_t)(sv.tok0 + t) * h + p] = -s * (1.f - s) * dod;
+      }
+    }
+  }
+  __syncthreads();
+  // 16 consecutive lanes write one head's 16 rows (64 bytes)
+  const int r = threadIdx.x & 15;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int hh = (threadIdx.x >> 4) + 16 * k;  // head 2 p0 + hh
+    const size_t w = (size_t)(2 * p0 + hh) * Np + row0 + r;
+    a.delta[w] = sd[hh][r];
+    lse2[w] = sl[hh][r];
+  }
+  sig[(size_t)(p0 + (threadIdx.x >> 4)) * Np + row0 + r] = ss[threadIdx.x >> 4][r];
+}
+
 // ---------------------------------------------------------------------------
 // dQ: a wave owns one pair and 16 query rows; K and V tiles of 64 keys stream
 // through LDS (K in the transposing layout: it is read both ways).
@@ -677,10 +769,17 @@ hipError_t launch_d(const V2BwdArgs& a, hipStream_t stream) {
   float* lse2 = a.delta + (size_t)a.Hq * Np;
   float* sig = lse2 + (size_t)a.Hq * Np;
   const long long pre_items = Np * (a.Hq / 2);
-  const long long pre_blocks = (pre_items + 15) / 16;  // 16 items per workgroup
-  if (pre_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((v2_bwd_pre_kernel<D>), dim3((unsigned)pre_blocks), dim3(256), 0, stream, a,
-                     lse2, sig);
+  if ((a.Hq / 2) % 16 == 0) {  // tiles of 16 rows x 16 pairs (Np is a multiple of 64)
+    const long long blocks = Np / 16 * (a.Hq / 2 / 16);
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((v2_bwd_pre_tiled_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       a, lse2, sig);
+  } else {
+    const long long pre_blocks = (pre_items + 15) / 16;  // 16 items per workgroup
+    if (pre_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((v2_bwd_pre_kernel<D>), dim3((unsigned)pre_blocks), dim3(256), 0, stream,
+                       a, lse2, sig);
+  }
   const int pairs_per_group = (a.Hq / a.Hkv) / 2;
   const int PW = pairs_per_group % 4 == 0 ? 4 : pairs_per_group % 2 == 0 ? 2 : 1;
   const int qtile = kRows * (kWaves / PW);
