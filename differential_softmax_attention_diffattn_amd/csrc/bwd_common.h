@@ -20,17 +20,30 @@ struct BTile {
 // Two LDS layouts of a 64-row bf16 tile (row-major, swizzled):
 //  * rows: 16-byte chunk c of row r at position c ^ (r mod nchunks), for
 //    16-byte row reads (an MFMA operand whose k index runs along a row);
-//  * trans: 32-byte chunk c of row r at position c ^ (r mod D/16), for the
+//  * trans: 32-byte chunk c of row r at position c ^ trans_swz(r), for the
 //    transposing read (an operand whose k index runs down the rows).
+// trans_swz is a permutation of the D/16 chunk positions over rows r mod
+// D/16.  For D = 128 (256-byte rows, one row per pass over the 64 banks) it
+// is r mod 8 with its bits rotated, (r mod 4) * 2 + (r / 4 mod 2): then any 8
+// consecutive rows fall on 8 different positions (the 16x16 transposing reads
+// of 8 rows, the 16-byte row reads), and so do two adjacent chunks of any 4
+// rows 4h .. 4h+3 (the 32x32 transposing reads, whose first 32 lanes take
+// 4 rows x 64 bytes); with the plain r mod 8 those two chunks of 4 rows
+// cover only 4 positions, a two-way bank conflict.  For D = 64 (two rows per
+// pass) r mod 4 already keeps both patterns apart.
+template <int D>
+__device__ __forceinline__ int trans_swz(int row) {
+  if constexpr (D / 16 == 8) return ((row & 3) << 1) | ((row >> 2) & 1);
+  return row & (D / 16 - 1);
+}
 template <int D>
 __device__ __forceinline__ int rows_offset(int row, int chunk) {
   return row * BTile<D>::kRowBytes + ((chunk ^ (row & (BTile<D>::kChunks - 1))) << 4);
 }
 template <int D>
 __device__ __forceinline__ int trans_offset(int row, int byte_in_row) {
-  constexpr int n32 = D / 16;
   const int c32 = byte_in_row >> 5;
-  return row * BTile<D>::kRowBytes + ((c32 ^ (row & (n32 - 1))) << 5) + (byte_in_row & 31);
+  return row * BTile<D>::kRowBytes + ((c32 ^ trans_swz<D>(row)) << 5) + (byte_in_row & 31);
 }
 
 // The same offsets as one base per (row, byte) XORed with the chunk index:
@@ -39,7 +52,7 @@ __device__ __forceinline__ int trans_offset(int row, int byte_in_row) {
 // above the chunk bits), so a loop over chunks costs one XOR per read.
 template <int D>
 __device__ __forceinline__ int trans_base(int row, int byte_in_chunk) {
-  return row * BTile<D>::kRowBytes | ((row & (D / 16 - 1)) << 5) | byte_in_chunk;
+  return row * BTile<D>::kRowBytes | (trans_swz<D>(row) << 5) | byte_in_chunk;
 }
 template <int D>
 __device__ __forceinline__ int rows_base(int row) {
@@ -65,8 +78,7 @@ __device__ __forceinline__ void load_tile(const uint16_t* base, size_t stride, i
     const int pos = (off % TL::kRowBytes) >> 4;
     int lc;  // logical 16-byte chunk stored at that position
     if (TRANS) {
-      constexpr int n32 = D / 16;
-      lc = (((pos >> 1) ^ (r & (n32 - 1))) << 1) | (pos & 1);
+      lc = (((pos >> 1) ^ trans_swz<D>(r)) << 1) | (pos & 1);
     } else {
       lc = pos ^ (r & (TL::kChunks - 1));
     }
@@ -96,8 +108,7 @@ struct TileLoader {
       const int pos = (o % BTile<D>::kRowBytes) >> 4;
       int lc;
       if (TRANS) {
-        constexpr int n32 = D / 16;
-        lc = (((pos >> 1) ^ (r & (n32 - 1))) << 1) | (pos & 1);
+        lc = (((pos >> 1) ^ trans_swz<D>(r)) << 1) | (pos & 1);
       } else {
         lc = pos ^ (r & (BTile<D>::kChunks - 1));
       }

@@ -20,13 +20,14 @@
 //  * v2_bwd_dq_kernel: the forward's decomposition (a wave owns one pair and
 //    16 query rows, lanes own query columns; K and V tiles stream through LDS):
 //    S^T = K Q^T, dP^T = V dout^T, dS^T, dQ^T += K^T dS^T;
-//  * v2_bwd_dkdv_kernel: a workgroup owns 128 keys of one KV head; a wave
-//    keeps its 16 keys' K and V fragments in registers (lanes own key
-//    columns) and handles both heads of every pair, so dout V^T and the dV
-//    product are formed once per pair; the Q and dout tiles of every pair and
-//    query tile stream through LDS.
-// All MFMA work is 16x16x32 bf16 with fp32 accumulation; P and dS are rounded
-// to bf16 for the second product of each pair, as in the forward.
+//  * v2_bwd_dkdv_kernel: a workgroup owns 256 keys of one KV head; a wave
+//    keeps its 32 keys' K fragments in registers (lanes own key columns), V
+//    of the workgroup's keys sits in LDS, and the wave handles both heads of
+//    every pair, so dout V^T and the dV product are formed once per pair; the
+//    Q and dout tiles of every pair and query tile stream through LDS.
+// MFMA work is bf16 with fp32 accumulation (16x16x32 in dQ, 32x32x16 in
+// dK/dV); P and dS are rounded to bf16 for the second product of each pair,
+// as in the forward.
 #include <math.h>
 
 #include "bwd_common.h"
@@ -48,7 +49,6 @@ using bwd::trans_offset;
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kKeys = 64;   // keys per staged tile (dq)
-constexpr int kQRows = 64;  // query rows per staged tile (dkdv)
 constexpr int kRows = 16;   // query rows per wave (dq)
 
 template <bool B>
@@ -489,31 +489,39 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, con
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV: a workgroup owns 128 keys of one KV head, a wave 16 of them and
-// both heads of every pair.  Per (pair, query tile of 64 rows):
+// dK and dV: a workgroup owns 256 keys of one KV head, a wave 32 of them and
+// both heads of every pair.  Per (pair, query tile of 32 rows):
 //   S_e, S_o = Q_{e,o} K^T, dP = dout V^T (shared: dP_o = -s dP),
 //   dS_e = P_e o (dP - D_e), dS_o = P_o o (-s dP - D_o),
 //   dV += (P_e - s P_o)^T dout,  dK += dS_e^T Q_e + dS_o^T Q_o.
+// All products are 32x32x16 MFMAs: each LDS operand read (1 KiB per wave)
+// feeds 32 x 32 x 16 multiply-adds, half the LDS bytes per FLOP of the
+// 16x16x32 form, whose operand reads (the transposing ones above all) held
+// the kernel below half its MFMA rate.  The lanes own key columns (32 keys);
+// K stays in registers, V of the workgroup's keys in LDS.
 // ---------------------------------------------------------------------------
-constexpr int kDkvKeys = kWaves * 16;
+constexpr int kKvRows = 32;               // query rows per staged tile
+constexpr int kDkvKeys = kWaves * 32;     // keys per workgroup
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, const float* lse2,
                                                                   const float* sig, int cohort) {
   using TL = BTile<D>;
-  constexpr int NC = D / 32;
-  constexpr int NDB = D / 16;
+  constexpr int NK = D / 16;  // k-steps over d
+  constexpr int NB = D / 32;  // 32-column blocks of dK and dV
+  constexpr int kTile = kKvRows * TL::kRowBytes;
   // per stage: Q of the even and odd head and dout of the pair (transposing
   // layout, read both ways), then the rows' lse2 and delta of both heads and s
-  constexpr int kVec = 5 * kQRows * 4;
-  constexpr int kStage = 3 * TL::kBytes + kVec;
+  constexpr int kVec = 5 * kKvRows * 4;
+  constexpr int kStage = 3 * kTile + kVec;
+  __shared__ __align__(16) uint8_t vt[kDkvKeys * TL::kRowBytes];
   __shared__ __align__(16) uint8_t st0[kStage];
   __shared__ __align__(16) uint8_t st1[kStage];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4;
-  const int c16 = lane & 15;
+  const int hf = lane >> 5;  // half of the wave: k group of the MFMA operands
+  const int c32 = lane & 31;
 
   // blocks: padded batches take the key tiles with the most query tiles first,
   // then (batch, KV head); packed batches go sequence by sequence.  When the
@@ -548,12 +556,12 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
   }
   const int T = sv.L;
   const long long Np = a.Np;
-  const int n_qt = (T + kQRows - 1) / kQRows;
+  const int n_qt = (T + kKvRows - 1) / kKvRows;
   const int group = a.Hq / a.Hkv;
   const int npairs = group / 2;
   const int hpairs = a.Hq / 2;
   const int key0 = kt * kDkvKeys;
-  const int qt0 = CAUSAL ? key0 / kQRows : 0;
+  const int qt0 = CAUSAL ? key0 / kKvRows : 0;
   // (pair, query tile) items.  An XCD runs `cohort` workgroups at a time (one
   // per CU), in rounds of its sequence: a round that starts together (key
   // tiles in order, so item counts falling) walks the query tiles last first
@@ -567,35 +575,34 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
   const bool ascending = local >= 0 && ((local / cohort) & 1);
   auto qt_of = [&](int item) { return ascending ? qt0 + item / npairs : n_qt - 1 - item / npairs; };
 
-  // this wave's 16 keys: K^T and V^T B operands (lane column = key)
-  const int key = key0 + wave * 16 + c16;
+  // V of the workgroup's keys, once (rows past the end clamped; masked below)
+  load_tile<D, true, kWaves, kDkvKeys>(a.v + (((size_t)sv.tok0 + key0) * a.Hkv + kvh) * D,
+                                       (size_t)a.Hkv * D, T - key0, vt, wave, lane);
+  // this lane's key: K^T B operands (column = key, k group hf: d 16 ks + 8 hf .. + 7)
+  const int key = key0 + wave * 32 + c32;
   const int keyc = min(key, T - 1);
   const size_t kvrow = ((size_t)sv.tok0 + keyc) * a.Hkv + kvh;
-  u32x4 kf[NC], vf[NC];
+  u32x4 kf[NK];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    kf[c] = ldg128(a.k + kvrow * D + c * 32 + g * 8);
-    vf[c] = ldg128(a.v + kvrow * D + c * 32 + g * 8);
-  }
+  for (int ks = 0; ks < NK; ++ks) kf[ks] = ldg128(a.k + kvrow * D + ks * 16 + hf * 8);
   const float cs = a.scale * kLog2e;
-  // the last query row this wave's keys can see is below the tile start: skip
-  const int wave_key_lo = key0 + wave * 16;
+  const int wave_key_lo = key0 + wave * 32;
 
-  const TileLoader<D, true> q_ld((size_t)a.Hq * D, wave, lane);  // Q_e and Q_o
-  const TileLoader<D, true> o_ld((size_t)hpairs * D, wave, lane);  // dout
+  const TileLoader<D, true, kWaves, kKvRows> q_ld((size_t)a.Hq * D, wave, lane);   // Q_e and Q_o
+  const TileLoader<D, true, kWaves, kKvRows> o_ld((size_t)hpairs * D, wave, lane);  // dout
   auto load = [&](int item, uint8_t* st) {
     const int pp = item % npairs;
     const int qt = qt_of(item);
-    const int r0 = qt * kQRows;
+    const int r0 = qt * kKvRows;
     const int je = kvh * group + 2 * pp;  // even head of the pair
     const int pair = je / 2;
     const uint16_t* qe = a.q + (((size_t)sv.tok0 + r0) * a.Hq + je) * D;
     q_ld.load(qe, T - r0, st, wave, lane);
-    q_ld.load(qe + D, T - r0, st + TL::kBytes, wave, lane);
+    q_ld.load(qe + D, T - r0, st + kTile, wave, lane);
     const uint16_t* dsrc = a.dout + (((size_t)sv.tok0 + r0) * hpairs + pair) * D;
-    o_ld.load(dsrc, T - r0, st + 2 * TL::kBytes, wave, lane);
-    // row vectors (64 floats each, padded rows included): 5 x 256 bytes
-    if (wave < 5 && lane < 16) {
+    o_ld.load(dsrc, T - r0, st + 2 * kTile, wave, lane);
+    // row vectors (32 floats each, padded rows included): 5 x 128 bytes
+    if (wave < 5 && lane < 8) {
       const float* src;
       if (wave < 2)
         src = lse2 + (size_t)(je + wave) * Np + sv.ws0 + r0;
@@ -603,84 +610,91 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
         src = a.delta + (size_t)(je + wave - 2) * Np + sv.ws0 + r0;
       else
         src = sig + (size_t)pair * Np + sv.ws0 + r0;
-      dma16(src, (uint32_t)(lane * 16), st + 3 * TL::kBytes + wave * 256);
+      dma16(src, (uint32_t)(lane * 16), st + 3 * kTile + wave * 128);
     }
   };
 
-  f32x4 dk[NDB], dv[NDB];
+  f32x16 dk[NB], dv[NB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    dk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const int tr_row = 4 * g + (c16 >> 2);
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dk[nb][e] = dv[nb][e] = 0.f;
+  // transposing reads (B operands of dV and dK, k = query rows): the lane's
+  // 16-lane group g4 reads rows 4 hf + (c16 >> 2) (+ 8) of the 16-column
+  // block g4 & 1 of each 32-column block; lane c16 gets that block's column
+  // c16 down the four rows
+  const int c16 = lane & 15;
+  const int tr_row = 4 * hf + (c16 >> 2);
   const int tr_byte = 8 * (c16 & 3);
+  const int tr_half = ((lane >> 4) & 1) << 5;
 
   // MASKED: the item's query tile touches the diagonal or a ragged end
   auto work = [&](auto masked, int item, const uint8_t* st) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
     const int qt = qt_of(item);
-    const int r0 = qt * kQRows;
-    if (CAUSAL && r0 + kQRows <= wave_key_lo) return;  // every key of the wave is above the rows
+    const int r0 = qt * kKvRows;
+    if (CAUSAL && r0 + kKvRows <= wave_key_lo) return;  // every key of the wave is above the rows
     const uint8_t* qle = st;
-    const uint8_t* qlo = st + TL::kBytes;
-    const uint8_t* dl = st + 2 * TL::kBytes;
-    const float* vec = reinterpret_cast<const float*>(st + 3 * TL::kBytes);
-    // the lane's swizzled row bases, opaque here so that the offsets derived
-    // from them (one XOR each) are formed next to their use: A reads at 32-byte
-    // chunk 2c + (g >> 1), byte 16 (g & 1); transposing reads at row tr_row
-    int ba = trans_base<D>(c16, (g & 1) * 16) ^ ((g >> 1) << 5);
-    int bt = trans_base<D>(tr_row, tr_byte);
-    asm volatile("" : "+v"(ba), "+v"(bt));
-    // S_e, S_o = Q K^T and dP = dout V^T: 4 query blocks x this wave's 16 keys
-    f32x4 se[4], so[4], dpa[4];
+    const uint8_t* qlo = st + kTile;
+    const uint8_t* dl = st + 2 * kTile;
+    const float* vec = reinterpret_cast<const float*>(st + 3 * kTile);
+    // the lane's swizzled bases, opaque here so that the offsets derived from
+    // them (one XOR each) are formed next to their use: A reads at row c32,
+    // 32-byte chunk ks, byte 16 hf; V reads the same in the wave's V rows;
+    // transposing reads at row tr_row
+    int ba = trans_base<D>(c32, hf * 16);
+    int bv = ba + wave * 32 * TL::kRowBytes;
+    int bt = trans_base<D>(tr_row, tr_byte) ^ tr_half;
+    asm volatile("" : "+v"(ba), "+v"(bv), "+v"(bt));
+    // S_e, S_o = Q K^T and dP = dout V^T: 32 queries x the wave's 32 keys
+    f32x16 se, so, dp;
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      se[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      so[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dpa[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 16; ++e) se[e] = so[e] = dp[e] = 0.f;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int off = (ba ^ (c << 6)) + qb * 16 * TL::kRowBytes;
-        const u32x4 qa = *reinterpret_cast<const u32x4*>(qle + off);
-        const u32x4 qb_ = *reinterpret_cast<const u32x4*>(qlo + off);
-        const u32x4 da = *reinterpret_cast<const u32x4*>(dl + off);
-        se[qb] = mfma_bf16(qa, kf[c], se[qb]);
-        so[qb] = mfma_bf16(qb_, kf[c], so[qb]);
-        dpa[qb] = mfma_bf16(da, vf[c], dpa[qb]);
-      }
+    for (int ks = 0; ks < NK; ++ks) {
+      const int off = ba ^ (ks << 5);
+      const u32x4 qa = *reinterpret_cast<const u32x4*>(qle + off);
+      const u32x4 qb = *reinterpret_cast<const u32x4*>(qlo + off);
+      const u32x4 da = *reinterpret_cast<const u32x4*>(dl + off);
+      const u32x4 vb = *reinterpret_cast<const u32x4*>(vt + (bv ^ (ks << 5)));
+      se = mfma32_bf16(qa, kf[ks], se);
+      so = mfma32_bf16(qb, kf[ks], so);
+      dp = mfma32_bf16(da, vb, dp);
     }
-    // P, dS of both heads and P'' = P_e - s P_o; rows are queries 16 qb + 4 g + i
-    float pv[4][4], dse[4][4], dso[4][4];
+    // P, dS of both heads and P'' = P_e - s P_o; element 4 j + i is query
+    // r0 + 8 j + 4 hf + i
+    float pv[16], dse[16], dso[16];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      const f32x4 l2e = *reinterpret_cast<const f32x4*>(vec + qb * 16 + 4 * g);
-      const f32x4 l2o = *reinterpret_cast<const f32x4*>(vec + kQRows + qb * 16 + 4 * g);
-      const f32x4 dle = *reinterpret_cast<const f32x4*>(vec + 2 * kQRows + qb * 16 + 4 * g);
-      const f32x4 dlo = *reinterpret_cast<const f32x4*>(vec + 3 * kQRows + qb * 16 + 4 * g);
-      const f32x4 sg = *reinterpret_cast<const f32x4*>(vec + 4 * kQRows + qb * 16 + 4 * g);
+    for (int j = 0; j < 4; ++j) {
+      const int rv = 8 * j + 4 * hf;
+      const f32x4 l2e = *reinterpret_cast<const f32x4*>(vec + rv);
+      const f32x4 l2o = *reinterpret_cast<const f32x4*>(vec + kKvRows + rv);
+      const f32x4 dle = *reinterpret_cast<const f32x4*>(vec + 2 * kKvRows + rv);
+      const f32x4 dlo = *reinterpret_cast<const f32x4*>(vec + 3 * kKvRows + rv);
+      const f32x4 sg = *reinterpret_cast<const f32x4*>(vec + 4 * kKvRows + rv);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int q = r0 + qb * 16 + 4 * g + i;
-        float pe = fast_exp2(fmaf(se[qb][i], cs, -l2e[i]));
-        float po = fast_exp2(fmaf(so[qb][i], cs, -l2o[i]));
+        const int e = 4 * j + i;
+        float pe = fast_exp2(fmaf(se[e], cs, -l2e[i]));
+        float po = fast_exp2(fmaf(so[e], cs, -l2o[i]));
         if (MASKED) {  // a select, not a branch: every lane takes the same path
+          const int q = r0 + rv + i;
           const bool ok = (q < T) & (key < T) & (!CAUSAL | (key <= q));
           pe = ok ? pe : 0.f;
           po = ok ? po : 0.f;
         }
-        pv[qb][i] = fmaf(-sg[i], po, pe);
-        dse[qb][i] = pe * (dpa[qb][i] - dle[i]);
-        dso[qb][i] = po * fmaf(-sg[i], dpa[qb][i], -dlo[i]);
+        pv[e] = fmaf(-sg[i], po, pe);
+        dse[e] = pe * (dp[e] - dle[i]);
+        dso[e] = po * fmaf(-sg[i], dp[e], -dlo[i]);
       }
     }
-    // dV += P''^T dout and dK += dS_e^T Q_e + dS_o^T Q_o over two 32-query
-    // k-steps; A operands from the registers above (key = row, queries
-    // 32 s + {4 g + i, 16 + 4 g + i}), B operands by transposing reads.
-    auto pack8 = [&](const float (&x)[4][4], int s) {
-      return u32x4{pack_bf16x2(x[2 * s][0], x[2 * s][1]), pack_bf16x2(x[2 * s][2], x[2 * s][3]),
-                   pack_bf16x2(x[2 * s + 1][0], x[2 * s + 1][1]),
-                   pack_bf16x2(x[2 * s + 1][2], x[2 * s + 1][3])};
+    // dV += P''^T dout and dK += dS_e^T Q_e + dS_o^T Q_o over two 16-query
+    // k-steps.  A operands from the registers above (row = key; k slots 0-3
+    // are queries 16 s + 4 hf + 0..3, slots 4-7 queries 16 s + 8 + 4 hf +
+    // 0..3), B operands by transposing reads of the same rows.
+    auto pack8 = [&](const float (&x)[16], int s) {
+      return u32x4{pack_bf16x2(x[8 * s + 0], x[8 * s + 1]), pack_bf16x2(x[8 * s + 2], x[8 * s + 3]),
+                   pack_bf16x2(x[8 * s + 4], x[8 * s + 5]), pack_bf16x2(x[8 * s + 6], x[8 * s + 7])};
     };
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -688,29 +702,27 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
       const u32x4 sae = pack8(dse, s);
       const u32x4 sao = pack8(dso, s);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int off = (bt ^ (db << 5)) + s * 32 * TL::kRowBytes;
+      for (int nb = 0; nb < NB; ++nb) {
+        const int off = (bt ^ (nb << 6)) + s * 16 * TL::kRowBytes;
         const u32x2 dlo_ = lds_read_tr16(dl + off);
-        const u32x2 dhi_ = lds_read_tr16(dl + off + 16 * TL::kRowBytes);
+        const u32x2 dhi_ = lds_read_tr16(dl + off + 8 * TL::kRowBytes);
         const u32x2 elo = lds_read_tr16(qle + off);
-        const u32x2 ehi = lds_read_tr16(qle + off + 16 * TL::kRowBytes);
+        const u32x2 ehi = lds_read_tr16(qle + off + 8 * TL::kRowBytes);
         const u32x2 olo = lds_read_tr16(qlo + off);
-        const u32x2 ohi = lds_read_tr16(qlo + off + 16 * TL::kRowBytes);
-        dv[db] = mfma_bf16(pa, u32x4{dlo_[0], dlo_[1], dhi_[0], dhi_[1]}, dv[db]);
-        dk[db] = mfma_bf16(sae, u32x4{elo[0], elo[1], ehi[0], ehi[1]}, dk[db]);
-        dk[db] = mfma_bf16(sao, u32x4{olo[0], olo[1], ohi[0], ohi[1]}, dk[db]);
+        const u32x2 ohi = lds_read_tr16(qlo + off + 8 * TL::kRowBytes);
+        dv[nb] = mfma32_bf16(pa, u32x4{dlo_[0], dlo_[1], dhi_[0], dhi_[1]}, dv[nb]);
+        dk[nb] = mfma32_bf16(sae, u32x4{elo[0], elo[1], ehi[0], ehi[1]}, dk[nb]);
+        dk[nb] = mfma32_bf16(sao, u32x4{olo[0], olo[1], ohi[0], ohi[1]}, dk[nb]);
       }
     }
   };
 
-  if (n_items > 0) {
-    load(0, st0);
-    __builtin_amdgcn_s_waitcnt(0x0f70);
-    __syncthreads();
-  }
+  if (n_items > 0) load(0, st0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
   auto item_masked = [&](int item) {
-    const int r0 = qt_of(item) * kQRows;
-    return (CAUSAL && r0 < key0 + kDkvKeys) || r0 + kQRows > T || key0 + kDkvKeys > T;
+    const int r0 = qt_of(item) * kKvRows;
+    return (CAUSAL && r0 < key0 + kDkvKeys) || r0 + kKvRows > T || key0 + kDkvKeys > T;
   };
   // One item with the stage chosen at run time: the next item's loads, the
   // work, the wait.  (Reads from a stage chosen at run time wait for every
@@ -749,16 +761,16 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
   }
   for (int it = main_e; it < n_items; ++it) one_dynamic(it);
 
-  // C layout: lane column = d (16 db + c16), rows = keys 4 g + i of the wave's 16
+  // C layout: lane column = d (32 nb + c32), element 4 j + i = key 8 j + 4 hf + i of the wave's 32
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kk = key0 + wave * 16 + 4 * g + i;
+    for (int e = 0; e < 16; ++e) {
+      const int kk = key0 + wave * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
       if (kk < T) {
-        const size_t o = (((size_t)sv.tok0 + kk) * a.Hkv + kvh) * D + db * 16 + c16;
-        a.dk[o] = dk[db][i] * a.scale;
-        a.dv[o] = dv[db][i];
+        const size_t o = (((size_t)sv.tok0 + kk) * a.Hkv + kvh) * D + nb * 32 + c32;
+        a.dk[o] = dk[nb][e] * a.scale;
+        a.dv[o] = dv[nb][e];
       }
     }
 }
