@@ -588,29 +588,35 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
   const float cs = a.scale * kLog2e;
   const int wave_key_lo = key0 + wave * 32;
 
-  const TileLoader<D, true, kWaves, kKvRows> q_ld((size_t)a.Hq * D, wave, lane);   // Q_e and Q_o
-  const TileLoader<D, true, kWaves, kKvRows> o_ld((size_t)hpairs * D, wave, lane);  // dout
+  // The stage loads are issued by waves 4-7 only.  Issued by all eight right
+  // after the barrier, the direct-to-LDS loads stalled every wave for 600-1000
+  // cycles at issue (the CU's address unit takes them one after another) with
+  // the MFMA pipes idle; now waves 0-3 start their score MFMAs at once and the
+  // two waves of each SIMD run out of step, one's MFMAs under the other's
+  // issue stall and softmax.
+  constexpr int kLoadWaves = kWaves / 2;
+  const int lw = wave - kLoadWaves;  // loading wave index, valid for waves 4-7
+  const TileLoader<D, true, kLoadWaves, kKvRows> q_ld((size_t)a.Hq * D, lw, lane);   // Q_e and Q_o
+  const TileLoader<D, true, kLoadWaves, kKvRows> o_ld((size_t)hpairs * D, lw, lane);  // dout
   auto load = [&](int item, uint8_t* st) {
+    if (wave < kLoadWaves) return;
     const int pp = item % npairs;
     const int qt = qt_of(item);
     const int r0 = qt * kKvRows;
     const int je = kvh * group + 2 * pp;  // even head of the pair
     const int pair = je / 2;
     const uint16_t* qe = a.q + (((size_t)sv.tok0 + r0) * a.Hq + je) * D;
-    q_ld.load(qe, T - r0, st, wave, lane);
-    q_ld.load(qe + D, T - r0, st + kTile, wave, lane);
+    q_ld.load(qe, T - r0, st, lw, lane);
+    q_ld.load(qe + D, T - r0, st + kTile, lw, lane);
     const uint16_t* dsrc = a.dout + (((size_t)sv.tok0 + r0) * hpairs + pair) * D;
-    o_ld.load(dsrc, T - r0, st + 2 * kTile, wave, lane);
-    // row vectors (32 floats each, padded rows included): 5 x 128 bytes
-    if (wave < 5 && lane < 8) {
-      const float* src;
-      if (wave < 2)
-        src = lse2 + (size_t)(je + wave) * Np + sv.ws0 + r0;
-      else if (wave < 4)
-        src = a.delta + (size_t)(je + wave - 2) * Np + sv.ws0 + r0;
-      else
-        src = sig + (size_t)pair * Np + sv.ws0 + r0;
-      dma16(src, (uint32_t)(lane * 16), st + 3 * kTile + wave * 128);
+    o_ld.load(dsrc, T - r0, st + 2 * kTile, lw, lane);
+    // row vectors (32 floats each, padded rows included): 5 x 128 bytes, the
+    // lse2 and delta pairs by waves 4-7, s by wave 4
+    if (lane < 8) {
+      const float* src = lw < 2 ? lse2 + (size_t)(je + lw) * Np : a.delta + (size_t)(je + lw - 2) * Np;
+      dma16(src + sv.ws0 + r0, (uint32_t)(lane * 16), st + 3 * kTile + lw * 128);
+      if (lw == 0)
+        dma16(sig + (size_t)pair * Np + sv.ws0 + r0, (uint32_t)(lane * 16), st + 3 * kTile + 4 * 128);
     }
   };
 
