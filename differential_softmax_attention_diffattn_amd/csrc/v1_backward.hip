@@ -229,8 +229,20 @@ __global__ __launch_bounds__(kDqWaves * kWave, 1) void v1_bwd_dq_kernel(V1BwdArg
   const int T = a.T;
   const int BH = a.B * a.H;
   const int n_qt = (T + QTILE - 1) / QTILE;
-  const int jr = blockIdx.x / BH;  // longest query tiles first over all (batch, head)
-  const int bh = blockIdx.x - jr * BH;
+  // Longest query tiles first.  When the (batch, head) pairs split evenly
+  // over the 8 XCDs (workgroups go to XCDs round robin), each XCD works
+  // through its pairs one at a time, all query tiles of a pair together, so
+  // that the workgroups running together on it stream the same K1, K2 and V
+  // tiles and share them in L2; otherwise longest first over all pairs.
+  int jr, bh;
+  if (BH % 8 == 0) {
+    const int local = blockIdx.x / 8;
+    jr = local % n_qt;
+    bh = blockIdx.x % 8 + 8 * (local / n_qt);
+  } else {
+    jr = blockIdx.x / BH;
+    bh = blockIdx.x - jr * BH;
+  }
   const int qt = n_qt - 1 - jr;
   const int b = bh / a.H;
   const int h = bh - b * a.H;
