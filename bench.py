@@ -394,7 +394,7 @@ def main():
         del x, o, wsd
         torch.cuda.empty_cache()
     if want("bwd"):
-        # V2 backward on the prefill workload: the preprocessing, dQ and dK/dV
+        # V2 backward on the prefill workload: the dQ (with the row values) and dK/dV
         # kernels of one diffattn_v2_bwd call; the training forward that
         # produces o_heads / lse runs once, outside the timed region
         w = inp.V2_PREFILL

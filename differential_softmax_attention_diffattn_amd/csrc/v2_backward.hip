@@ -12,14 +12,14 @@
 // with P recomputed from the forward's log-sum-exp.  Both heads of a pair
 // share dout_p, so dout_p V^T is formed once per pair.
 //
-// Three kernels:
-//  * v2_bwd_pre_kernel: per (token, pair) D_2p, D_2p+1, s, dlogit, and the
-//    log-sum-exp in log2 units, stored [head][Np]: every sequence's rows start
-//    at a multiple of 64 and are padded to one (zeros), so a query tile's row
-//    values are one contiguous 256-byte run;
+// Two kernels:
 //  * v2_bwd_dq_kernel: the forward's decomposition (a wave owns one pair and
 //    16 query rows, lanes own query columns; K and V tiles stream through LDS):
-//    S^T = K Q^T, dP^T = V dout^T, dS^T, dQ^T += K^T dS^T;
+//    S^T = K Q^T, dP^T = V dout^T, dS^T, dQ^T += K^T dS^T.  It first forms its
+//    rows' D_2p, D_2p+1, s, dlogit and the log-sum-exp in log2 units and
+//    stores them [head][Np] for the next kernel: every sequence's rows start at
+//    a multiple of 64, so a 32-row query tile's values are one contiguous
+//    128-byte run;
 //  * v2_bwd_dkdv_kernel: a workgroup owns 256 keys of one KV head; a wave
 //    keeps its 32 keys' K fragments in registers (lanes own key columns), V
 //    of the workgroup's keys sits in LDS, and the wave handles both heads of
@@ -99,177 +99,12 @@ __device__ __forceinline__ bool tile_of(const V2BwdArgs& a, long long t, int row
 }
 
 // ---------------------------------------------------------------------------
-// Preprocessing: 16 lanes per (workspace row, pair).
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void v2_bwd_pre_kernel(V2BwdArgs a, float* lse2, float* sig) {
-  // 16 lanes per (row, pair) item, four items per wave: each lane reads D/16
-  // consecutive elements (16 bytes at D = 128) of dout and of both heads' O,
-  // and the dot products are summed over the 16-lane row by DPP.
-  constexpr int EPL = D / 16;
-  static_assert(EPL == 8 || EPL == 4, "head dim 128 or 64");
-  const int h = a.Hq / 2;
-  const long long item = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int l16 = threadIdx.x & 15;
-  const long long Np = a.Np;
-  if (item >= Np * h) return;  // uniform over the item's 16 lanes
-  const int p = (int)(item % h);
-  const long long prow = item / h;  // workspace row: 64-row tile prow / 64
-  SeqView sv;
-  int tile;
-  if (!tile_of<false>(a, prow / 64, 64, sv, tile)) return;  // rows past the last sequence: unused
-  const int t = tile * 64 + (int)(prow % 64);
-  const size_t ws = (size_t)(2 * p) * Np + sv.ws0 + t;  // [2p][row]
-  const size_t wsig = (size_t)p * Np + sv.ws0 + t;
-  if (t >= sv.L) {  // padding rows: finite zeros (the tiles read them and mask them)
-    if (l16 == 0) {
-      a.delta[ws] = 0.f;
-      a.delta[ws + Np] = 0.f;
-      lse2[ws] = 0.f;
-      lse2[ws + Np] = 0.f;
-      sig[wsig] = 0.f;
-    }
-    return;
-  }
-  const size_t tok = (size_t)(sv.tok0 + t);
-  // the row's scalars go out with the vector loads
-  const float lg = a.logit[tok * h + p];
-  const float lse_e = a.lse[tok * a.Hq + 2 * p];
-  const float lse_o = a.lse[tok * a.Hq + 2 * p + 1];
-  const uint16_t* gp = a.dout + (tok * h + p) * D + l16 * EPL;
-  const uint16_t* ep = a.o_heads + (tok * a.Hq + 2 * p) * D + l16 * EPL;
-  uint32_t gw[EPL / 2], ew[EPL / 2], ow[EPL / 2];
-  if constexpr (EPL == 8) {
-    const u32x4 g4 = ldg128(gp), e4 = ldg128(ep), o4 = ldg128(ep + D);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) gw[j] = g4[j], ew[j] = e4[j], ow[j] = o4[j];
-  } else {
-    const u32x2 g2 = *reinterpret_cast<const u32x2*>(gp);
-    const u32x2 e2 = *reinterpret_cast<const u32x2*>(ep);
-    const u32x2 o2 = *reinterpret_cast<const u32x2*>(ep + D);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) gw[j] = g2[j], ew[j] = e2[j], ow[j] = o2[j];
-  }
-  float de = 0.f, dod = 0.f;
-#pragma unroll
-  for (int j = 0; j < EPL / 2; ++j) {
-    de = fmaf(bf16lo_to_f32(gw[j]), bf16lo_to_f32(ew[j]), de);
-    de = fmaf(bf16hi_to_f32(gw[j]), bf16hi_to_f32(ew[j]), de);
-    dod = fmaf(bf16lo_to_f32(gw[j]), bf16lo_to_f32(ow[j]), dod);
-    dod = fmaf(bf16hi_to_f32(gw[j]), bf16hi_to_f32(ow[j]), dod);
-  }
-  de = row16_sum(de);
-  dod = row16_sum(dod);
-  if (l16 == 0) {
-    const float s = sigmoid_f32(lg);
-    a.delta[ws] = de;             // <dO_2p, O_2p> with dO_2p = dout_p
-    a.delta[ws + Np] = -s * dod;  // <dO_2p+1, O_2p+1> with dO_2p+1 = -s dout_p
-    a.dlogit[tok * h + p] = -s * (1.f - s) * dod;
-    lse2[ws] = lse_e * kLog2e;
-    lse2[ws + Np] = lse_o * kLog2e;
-    sig[wsig] = s;
-  }
-}
-
-// The same preprocessing for Hq / 2 a multiple of 16, by tiles of 16 workspace
-// rows x 16 pairs: a workgroup's 16 lane groups take the 16 pairs of one row
-// per pass (so the per-token reads of dout, O, lse and logits stay contiguous,
-// as above), and the per-row values collect in LDS and go out as 64-byte runs
-// of 16 rows per head (the per-item layout above writes each 4-byte value to a
-// different cache line).  All 16 rows lie in one 64-row workspace tile, so the
-// sequence is found once; workspace row = 16 * row tile + pass.
-template <int D>
-__global__ __launch_bounds__(256) void v2_bwd_pre_tiled_kernel(V2BwdArgs a, float* lse2, float* sig) {
-  constexpr int EPL = D / 16;
-  static_assert(EPL == 8 || EPL == 4, "head dim 128 or 64");
-  constexpr int kPass = 16;   // rows per tile, one per pass
-  constexpr int kGroup = 4;   // passes whose loads are in flight together
-  __shared__ float sd[32][kPass + 1], sl[32][kPass + 1], ss[16][kPass + 1];
-  const int h = a.Hq / 2;
-  const int n_pt = h / 16;
-  const long long rt = blockIdx.x / n_pt;
-  const int p0 = (int)(blockIdx.x % n_pt) * 16;
-  const int j = threadIdx.x >> 4;  // pair p0 + j
-  const int l16 = threadIdx.x & 15;
-  const int p = p0 + j;
-  const long long Np = a.Np;
-  const long long row0 = rt * kPass;
-  if (row0 >= Np) return;
-  SeqView sv;
-  int tile;
-  if (!tile_of<false>(a, row0 / 64, 64, sv, tile)) return;  // rows past the last sequence: unused
-  const int t0 = tile * 64 + (int)(row0 % 64);  // the first pass's row inside its sequence
-#pragma unroll
-  for (int i0 = 0; i0 < kPass; i0 += kGroup) {
-    uint32_t gw[kGroup][EPL / 2], ew[kGroup][EPL / 2], ow[kGroup][EPL / 2];
-    float lg[kGroup], le[kGroup], lo[kGroup];
-#pragma unroll
-    for (int u = 0; u < kGroup; ++u) {  // loads of kGroup passes first (padding rows read row 0)
-      const int t = t0 + i0 + u;
-      const size_t tok = (size_t)(sv.tok0 + (t < sv.L ? t : 0));
-      lg[u] = a.logit[tok * h + p];
-      le[u] = a.lse[tok * a.Hq + 2 * p];
-      lo[u] = a.lse[tok * a.Hq + 2 * p + 1];
-      const uint16_t* gp = a.dout + (tok * h + p) * D + l16 * EPL;
-      const uint16_t* ep = a.o_heads + (tok * a.Hq + 2 * p) * D + l16 * EPL;
-      if constexpr (EPL == 8) {
-        const u32x4 g4 = ldg128(gp), e4 = ldg128(ep), o4 = ldg128(ep + D);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) gw[u][q] = g4[q], ew[u][q] = e4[q], ow[u][q] = o4[q];
-      } else {
-        const u32x2 g2 = *reinterpret_cast<const u32x2*>(gp);
-        const u32x2 e2 = *reinterpret_cast<const u32x2*>(ep);
-        const u32x2 o2 = *reinterpret_cast<const u32x2*>(ep + D);
-#pragma unroll
-        for (int q = 0; q < 2; ++q) gw[u][q] = g2[q], ew[u][q] = e2[q], ow[u][q] = o2[q];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kGroup; ++u) {
-      const int i = i0 + u;
-      const int t = t0 + i;
-      float de = 0.f, dod = 0.f;
-#pragma unroll
-      for (int q = 0; q < EPL / 2; ++q) {
-        de = fmaf(bf16lo_to_f32(gw[u][q]), bf16lo_to_f32(ew[u][q]), de);
-        de = fmaf(bf16hi_to_f32(gw[u][q]), bf16hi_to_f32(ew[u][q]), de);
-        dod = fmaf(bf16lo_to_f32(gw[u][q]), bf16lo_to_f32(ow[u][q]), dod);
-        dod = fmaf(bf16hi_to_f32(gw[u][q]), bf16hi_to_f32(ow[u][q]), dod);
-      }
-      de = row16_sum(de);
-      dod = row16_sum(dod);
-      if (l16 == 0) {
-        const bool valid = t < sv.L;  // padding rows: finite zeros (the tiles read and mask them)
-        const float s = sigmoid_f32(lg[u]);
-        sd[2 * j][i] = valid ? de : 0.f;            // <dO_2p, O_2p> with dO_2p = dout_p
-        sd[2 * j + 1][i] = valid ? -s * dod : 0.f;  // <dO_2p+1, O_2p+1>, dO_2p+1 = -s dout_p
-        sl[2 * j][i] = valid ? le[u] * kLog2e : 0.f;
-        sl[2 * j + 1][i] = valid ? lo[u] * kLog2e : 0.f;
-        ss[j][i] = valid ? s : 0.f;
-        if (valid) a.dlogit[(size_t)(sv.tok0 + t) * h + p] = -s * (1.f - s) * dod;
-      }
-    }
-  }
-  __syncthreads();
-  // 16 consecutive lanes write one head's 16 rows (64 bytes)
-  const int r = threadIdx.x & 15;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int hh = (threadIdx.x >> 4) + 16 * k;  // head 2 p0 + hh
-    const size_t w = (size_t)(2 * p0 + hh) * Np + row0 + r;
-    a.delta[w] = sd[hh][r];
-    lse2[w] = sl[hh][r];
-  }
-  sig[(size_t)(p0 + (threadIdx.x >> 4)) * Np + row0 + r] = ss[threadIdx.x >> 4][r];
-}
-
-// ---------------------------------------------------------------------------
 // dQ: a wave owns one pair and 16 query rows; K and V tiles of 64 keys stream
 // through LDS (K in the transposing layout: it is read both ways).
 // ---------------------------------------------------------------------------
 template <int D, int PW, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, const float* lse2,
-                                                                const float* sig) {
+__global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, float* lse2,
+                                                                float* sig) {
   using TL = BTile<D>;
   constexpr int QSUB = kWaves / PW;
   constexpr int QTILE = kRows * QSUB;
@@ -316,14 +151,54 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, con
       qf[nb][c] = ldg128(a.q + (tok * a.Hq + 2 * p + nb) * D + c * 32 + g * 8);
     of[c] = ldg128(a.dout + (tok * hpairs + p) * D + c * 32 + g * 8);
   }
-  float l2[2], dl[2];
+  // The row's values, formed here from the row's O of both heads (read in
+  // dout's fragment layout), lse and logit: D_2p = <dout_p, O_2p>,
+  // D_2p+1 = -s <dout_p, O_2p+1> (the odd head's output gradient is -s dout_p),
+  // dlogit_p = -s (1 - s) <dout_p, O_2p+1> and lse log2(e), with s the pair's
+  // sigmoid.  The four lanes of a row (g) each sum 32 of the D products.
+  float l2[2], dl[2], sg;
+  {
+    u32x4 oh[2][NC];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const size_t w = (size_t)(2 * p + nb) * Np + sv.ws0 + rowc;
-    l2[nb] = lse2[w];
-    dl[nb] = a.delta[w];
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        oh[nb][c] = ldg128(a.o_heads + (tok * a.Hq + 2 * p + nb) * D + c * 32 + g * 8);
+    const float lg = a.logit[tok * hpairs + p];
+    const float le = a.lse[tok * a.Hq + 2 * p];
+    const float lo = a.lse[tok * a.Hq + 2 * p + 1];
+    float de = 0.f, dod = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t gw = of[c][j], ew = oh[0][c][j], ow = oh[1][c][j];
+        de = fmaf(bf16lo_to_f32(gw), bf16lo_to_f32(ew), de);
+        de = fmaf(bf16hi_to_f32(gw), bf16hi_to_f32(ew), de);
+        dod = fmaf(bf16lo_to_f32(gw), bf16lo_to_f32(ow), dod);
+        dod = fmaf(bf16hi_to_f32(gw), bf16hi_to_f32(ow), dod);
+      }
+    de = sum_across_rows(de);
+    dod = sum_across_rows(dod);
+    sg = sigmoid_f32(lg);
+    l2[0] = le * kLog2e;
+    l2[1] = lo * kLog2e;
+    dl[0] = de;
+    dl[1] = -sg * dod;
+    // publish them for the dK/dV kernel, whose 32-row query tiles read every
+    // row of this tile below the sequence's 32-row bound (rows past the end:
+    // finite zeros, which its masks discard)
+    if (g == 0 && row < (T + 31) / 32 * 32) {
+      const bool valid = row < T;
+      const size_t w = (size_t)(2 * p) * Np + sv.ws0 + row;
+      a.delta[w] = valid ? dl[0] : 0.f;
+      a.delta[w + Np] = valid ? dl[1] : 0.f;
+      lse2[w] = valid ? l2[0] : 0.f;
+      lse2[w + Np] = valid ? l2[1] : 0.f;
+      sig[(size_t)p * Np + sv.ws0 + row] = valid ? sg : 0.f;
+      if (valid) a.dlogit[tok * hpairs + p] = -sg * (1.f - sg) * dod;
+    }
   }
-  const float sg = sig[(size_t)p * Np + sv.ws0 + rowc];
 
   const size_t kv_stride = (size_t)a.Hkv * D;
   const uint16_t* kbase_g = a.k + ((size_t)sv.tok0 * a.Hkv + kv) * D;
@@ -786,18 +661,6 @@ hipError_t launch_d(const V2BwdArgs& a, hipStream_t stream) {
   const long long Np = a.Np;
   float* lse2 = a.delta + (size_t)a.Hq * Np;
   float* sig = lse2 + (size_t)a.Hq * Np;
-  const long long pre_items = Np * (a.Hq / 2);
-  if ((a.Hq / 2) % 16 == 0) {  // tiles of 16 rows x 16 pairs (Np is a multiple of 64)
-    const long long blocks = Np / 16 * (a.Hq / 2 / 16);
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((v2_bwd_pre_tiled_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       a, lse2, sig);
-  } else {
-    const long long pre_blocks = (pre_items + 15) / 16;  // 16 items per workgroup
-    if (pre_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((v2_bwd_pre_kernel<D>), dim3((unsigned)pre_blocks), dim3(256), 0, stream,
-                       a, lse2, sig);
-  }
   const int pairs_per_group = (a.Hq / a.Hkv) / 2;
   const int PW = pairs_per_group % 4 == 0 ? 4 : pairs_per_group % 2 == 0 ? 2 : 1;
   const int qtile = kRows * (kWaves / PW);
@@ -817,7 +680,7 @@ hipError_t launch_d(const V2BwdArgs& a, hipStream_t stream) {
   if (dq_blocks > 0x7fffffffLL || kv_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
 #define DQ(PWV, C)                                                                               \
   hipLaunchKernelGGL((v2_bwd_dq_kernel<D, PWV, C>), dim3((unsigned)dq_blocks), dim3(kThreads), 0, \
-                     stream, a, (const float*)lse2, (const float*)sig)
+                     stream, a, lse2, sig)
   if (a.causal) {
     if (PW == 4) DQ(4, true);
     else if (PW == 2) DQ(2, true);
