@@ -709,8 +709,13 @@ def test_output_projection_saving_matches_page_figures():
         assert c["v2"] == n["q"] + n["k"] + n["v"] + n["lam"] + n["o_v2"]
         assert c["base"] == n["q"] + n["k"] + n["v"] + n["o_base"]
         assert c["o_v2"] / c["o_base"] == fig["o_projection_fraction_kept"]
-        # the query and output projections dominate when the KV heads are few
-        assert abs(c["o_saving_frac_of_base"] - fig["attention_params_saved_frac"]) <= fig["tolerance_abs"] + 2 * hkv / (4 * h)
+        base = n["q"] + n["k"] + n["v"] + n["o_base"]
+        assert c["o_saving_frac_of_base"] == (n["o_base"] - n["o_v2"]) / base
+        # The page's ~25 % holds when the query and output projections hold the
+        # module's weights; the K and V projections (2 hkv d of the 4 h d + 2 hkv d
+        # base columns) move the exact saving h / (4h + 2hkv) below 1/4 by
+        # (2hkv/h) / (4 (4 + 2hkv/h)) <= hkv / (8h).
+        assert abs(c["o_saving_frac_of_base"] - fig["attention_params_saved_frac"]) <= fig["tolerance_abs"] + hkv / (8 * h)
     small_kv = oracle.v2_attention_param_counts(4096, 32, 1, 128)
     assert abs(small_kv["o_saving_frac_of_base"] - fig["attention_params_saved_frac"]) < fig["tolerance_abs"]
 
