@@ -83,7 +83,9 @@ enum {
  * Supported: in_dtype DIFFATTN_F32 with d in 16..128 and dv in 16..256, both
  * multiples of 16; in_dtype DIFFATTN_BF16 with (d, dv) = (128, 256) or
  * (64, 128).  The bf16 path forms P.V in fp16 (11-bit significand), so V
- * entries must lie within the fp16 range (|v| <= 65504).
+ * entries must lie within the fp16 range (|v| <= 65504; the largest bf16
+ * value inside it is 65280).  Larger entries are not supported: they become
+ * inf in the fp16 operand and the output is then not finite.
  */
 DIFFATTN_API int diffattn_v1_fwd(const void* q1, const void* k1, const void* q2, const void* k2,
                     const void* v, const float* norm_weight, float* out, int B, int T, int H,

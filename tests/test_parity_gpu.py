@@ -181,6 +181,27 @@ def test_v1_bf16_causal_rows_ignore_future(gpu):
     assert torch.equal(a[:, :cut], b[:, :cut])
 
 
+def test_v1_bf16_values_at_the_fp16_limit(gpu):
+    # The bf16 path forms P.V in fp16, so V must lie within the fp16 range; the
+    # largest bf16 value inside it is 65280 (255 * 2^8).  V is the workload's
+    # draw times 2^17 (exact in bf16) with a few entries set to +-65280, so the
+    # packed fp16 operand holds the range's edge; the output (RMS-normalised,
+    # hence nearly scale-free) must still match the oracle on every row.
+    w = inp.V1_BF16.with_shape(B=1, T=200, H=2)
+    x = inp.v1_inputs(w)
+    v0 = x["v"].clone()
+    edge = 65280.0 / 2.0 ** 17
+    for t, h, c, sgn in ((0, 0, 0, 1), (17, 1, 255, -1), (64, 0, 100, 1), (199, 1, 7, -1), (120, 0, 31, -1)):
+        v0[0, t, h, c] = sgn * edge
+    x["v"] = (v0.float() * 2.0 ** 17).to(torch.bfloat16)
+    assert torch.equal(x["v"].float(), v0.float() * 2.0 ** 17)  # the scaling is exact
+    assert float(x["v"].float().abs().max()) == 65280.0
+    lam = li = oracle.lambda_init(5)
+    ref = oracle.v1_forward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, li, w.eps)
+    out = run_v1(cuda(x, gpu), lam, li, w.eps)
+    compare(out.cpu().numpy(), ref, rms(v0), TOL_BF16, REL_L2_BF16, what="v1 bf16 V at the fp16 limit")
+
+
 # Needles: key j of one map is set to alpha times the query of row i, so row i's
 # map puts nearly all its weight on key j (logit ~ alpha / sqrt(d) above the
 # rest).  The two maps pick different keys, so z ~ v_j - lambda v_j' is far from
