@@ -256,6 +256,25 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, int n
 #pragma unroll
   for (int e = 0; e < 2; ++e)
     src[e] = a.partial + (((size_t)b * a.Hq + heads[e]) * nparts) * kPartStride<D>;
+  // this thread's channel of parts grp + NG j, up to kPer per head at a time
+  // (whole-head workgroups have fewer than 32 parts, a few per thread); the
+  // first batch is loaded before the weights are known, so its latency
+  // overlaps that of the (m, l) loads
+  const int col = t % COLS;
+  const int grp = t / COLS;
+  const int ch = slice * COLS + col;
+  constexpr int kPer = COLS == D ? 4 : 32;
+  float ov[2][kPer];
+  auto load_batch = [&](int j0) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int s = grp + NG * (j0 + j);
+        ov[e][j] = s < nparts ? src[e][(size_t)s * kPartStride<D> + ch] : 0.f;
+      }
+  };
+  load_batch(0);
   // weights 2^(m_s - M) / L per part, computed once per head by one wave each;
   // a lane's (m, l) pairs (parts ln + 64 k, at most 512 parts) are all loaded
   // before any is used, so their latencies overlap
@@ -291,22 +310,20 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, int n
     if (ln == 0) inv_l[e] = L > 0.f ? 1.0f / L : 0.f;
   }
   __syncthreads();
-  const int col = t % COLS;
-  const int grp = t / COLS;
-  const int ch = slice * COLS + col;
+  // four chains per head: part grp + NG j goes to chain j mod 4
+  float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  for (int j0 = 0; grp + NG * j0 < nparts; j0 += kPer) {
+    if (j0 > 0) load_batch(j0);
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    // four independent chains per thread: the loads overlap
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    int s = grp;
-    for (; s + 3 * NG < nparts; s += 4 * NG) {
+    for (int e = 0; e < 2; ++e)
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        acc[u] = fmaf(src[e][(s + u * NG) * kPartStride<D> + ch], wts[e][s + u * NG], acc[u]);
-    }
-    for (; s < nparts; s += NG) acc[0] = fmaf(src[e][s * kPartStride<D> + ch], wts[e][s], acc[0]);
-    red[e][grp][col] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      for (int j = 0; j < kPer; ++j) {
+        const int s = grp + NG * (j0 + j);
+        if (s < nparts) acc[e][j & 3] = fmaf(ov[e][j], wts[e][s], acc[e][j & 3]);
+      }
   }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) red[e][grp][col] = (acc[e][0] + acc[e][1]) + (acc[e][2] + acc[e][3]);
   __syncthreads();
   if (t >= COLS) return;
   float res[2];
