@@ -48,7 +48,7 @@ using bwd::trans_offset;
 constexpr int kKeys = 64;     // keys per staged tile (dq)
 constexpr int kRows = 16;     // query rows per wave (dq)
 constexpr int kDqWaves = 8;   // dq: 128 query rows per workgroup
-constexpr int kPreBlocks = 2048;  // preprocessing workgroups at most (grid-stride beyond)
+constexpr int kPreBlocks = 1024;  // preprocessing workgroups at most (grid-stride beyond)
 
 template <bool B>
 struct BoolTag {
