@@ -259,9 +259,9 @@ def test_v1_backward_rejects_bad_arguments(lib):
 
 def test_v1_backward_workspace_query(lib):
     # bf16 dz [B,T,H,dv], fp32 stats [B][H][4][T rounded up to 64], then the
-    # preprocessing grid's partial sums (at most 2048 blocks of dv + 4 floats)
+    # preprocessing grid's partial sums (at most 1024 blocks of dv + 4 floats)
     assert lib.diffattn_v1_bwd_workspace_bytes(4, 4096, 12, 128, 256) == (
-        4 * 4096 * 12 * 256 * 2 + 4 * 12 * 4 * 4096 * 4 + 2048 * 260 * 4)
+        4 * 4096 * 12 * 256 * 2 + 4 * 12 * 4 * 4096 * 4 + 1024 * 260 * 4)
     assert lib.diffattn_v1_bwd_workspace_bytes(1, 1, 1, 64, 128) == (
         256 + 4 * 64 * 4 + 4 * 132 * 4)  # 16 rows per workgroup: 4 for the 64 padded rows
     assert lib.diffattn_v1_bwd_workspace_bytes(1, 64, 1, 96, 192) == 0

@@ -786,15 +786,16 @@ def test_v1_backward_lambda_outside_init_range(gpu, lam, li):
 
 
 def test_v1_backward_grid_stride_rows(gpu):
-    # more rows than the preprocessing grid has waves, so its loop and the
-    # fixed-order partial sums of dlambda and dweight run as at full size
-    w = inp.V1_BF16.with_shape(B=2, T=1024, H=4)
+    # more (row, head) items than the preprocessing grid's 1024 x 16 lane
+    # groups (3 x 5 x 1152 padded rows = 17280), so its grid-stride loop and
+    # the fixed-order partial sums of dlambda and dweight run as at full size
+    w = inp.V1_BF16.with_shape(B=3, T=1100, H=5, d=64, dv=128)
     x = inp.v1_inputs(w)
     dy = inp.v1_dy(w)
     lam = li = oracle.lambda_init(9)
     xg = cuda(x, gpu)
     refs = oracle.v1_backward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, li, w.eps, dy)
-    check_v1_backward_both_ways(xg, x, dy, lam, li, w.eps, None, True, refs, "v1 bwd B2 T1024 H4")
+    check_v1_backward_both_ways(xg, x, dy, lam, li, w.eps, None, True, refs, "v1 bwd B3 T1100 H5 d64")
 
 
 def test_v1_train_forward_outputs(gpu):
