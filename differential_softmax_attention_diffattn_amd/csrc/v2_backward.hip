@@ -103,8 +103,7 @@ __device__ __forceinline__ bool tile_of(const V2BwdArgs& a, long long t, int row
 // through LDS (K in the transposing layout: it is read both ways).
 // ---------------------------------------------------------------------------
 template <int D, int PW, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, float* lse2,
-                                                                float* sig) {
+__global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, float* lse2) {
   using TL = BTile<D>;
   constexpr int QSUB = kWaves / PW;
   constexpr int QTILE = kRows * QSUB;
@@ -187,15 +186,17 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dq_kernel(V2BwdArgs a, flo
     dl[1] = -sg * dod;
     // publish them for the dK/dV kernel, whose 32-row query tiles read every
     // row of this tile below the sequence's 32-row bound (rows past the end:
-    // finite zeros, which its masks discard)
+    // finite zeros, which its masks discard).  The odd head's values carry s:
+    // its lse in log2 units minus log2(s), so that the dK/dV kernel's
+    // exponential gives s P_o directly (0 when s is 0), and <dout_p, O_2p+1>
+    // itself, so that dS_o = s P_o (<dout_p, O_2p+1> - dP) needs no s.
     if (g == 0 && row < (T + 31) / 32 * 32) {
       const bool valid = row < T;
       const size_t w = (size_t)(2 * p) * Np + sv.ws0 + row;
       a.delta[w] = valid ? dl[0] : 0.f;
-      a.delta[w + Np] = valid ? dl[1] : 0.f;
+      a.delta[w + Np] = valid ? dod : 0.f;
       lse2[w] = valid ? l2[0] : 0.f;
-      lse2[w + Np] = valid ? l2[1] : 0.f;
-      sig[(size_t)p * Np + sv.ws0 + row] = valid ? sg : 0.f;
+      lse2[w + Np] = valid ? l2[1] - log2f(sg) : 0.f;
       if (valid) a.dlogit[tok * hpairs + p] = -sg * (1.f - sg) * dod;
     }
   }
@@ -380,14 +381,14 @@ constexpr int kDkvKeys = kWaves * 32;     // keys per workgroup
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, const float* lse2,
-                                                                  const float* sig, int cohort) {
+                                                                  int cohort) {
   using TL = BTile<D>;
   constexpr int NK = D / 16;  // k-steps over d
   constexpr int NB = D / 32;  // 32-column blocks of dK and dV
   constexpr int kTile = kKvRows * TL::kRowBytes;
   // per stage: Q of the even and odd head and dout of the pair (transposing
-  // layout, read both ways), then the rows' lse2 and delta of both heads and s
-  constexpr int kVec = 5 * kKvRows * 4;
+  // layout, read both ways), then the rows' lse2 and delta values of both heads
+  constexpr int kVec = 4 * kKvRows * 4;
   constexpr int kStage = 3 * kTile + kVec;
   __shared__ __align__(16) uint8_t vt[kDkvKeys * TL::kRowBytes];
   __shared__ __align__(16) uint8_t st0[kStage];
@@ -485,13 +486,11 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
     q_ld.load(qe + D, T - r0, st + kTile, lw, lane);
     const uint16_t* dsrc = a.dout + (((size_t)sv.tok0 + r0) * hpairs + pair) * D;
     o_ld.load(dsrc, T - r0, st + 2 * kTile, lw, lane);
-    // row vectors (32 floats each, padded rows included): 5 x 128 bytes, the
-    // lse2 and delta pairs by waves 4-7, s by wave 4
+    // row vectors (32 floats each, padded rows included): 4 x 128 bytes, the
+    // lse2 and delta pairs, one by each of waves 4-7
     if (lane < 8) {
       const float* src = lw < 2 ? lse2 + (size_t)(je + lw) * Np : a.delta + (size_t)(je + lw - 2) * Np;
       dma16(src + sv.ws0 + r0, (uint32_t)(lane * 16), st + 3 * kTile + lw * 128);
-      if (lw == 0)
-        dma16(sig + (size_t)pair * Np + sv.ws0 + r0, (uint32_t)(lane * 16), st + 3 * kTile + 4 * 128);
     }
   };
 
@@ -542,8 +541,11 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
       so = mfma32_bf16(qb, kf[ks], so);
       dp = mfma32_bf16(da, vb, dp);
     }
-    // P, dS of both heads and P'' = P_e - s P_o; element 4 j + i is query
-    // r0 + 8 j + 4 hf + i
+    // P_e, s P_o, their difference P'' = P_e - s P_o and dS of both heads:
+    // dS_e = P_e (dP - D_e), dS_o = P_o (-s dP - D_o) = s P_o (g_o - dP) with
+    // D_o = -s g_o, g_o = <dout, O_o> (the row values arrive with s folded in:
+    // lse2 of the odd head minus log2 s, and g_o).  Element 4 j + i is query
+    // r0 + 8 j + 4 hf + i.
     float pv[16], dse[16], dso[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -551,22 +553,21 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
       const f32x4 l2e = *reinterpret_cast<const f32x4*>(vec + rv);
       const f32x4 l2o = *reinterpret_cast<const f32x4*>(vec + kKvRows + rv);
       const f32x4 dle = *reinterpret_cast<const f32x4*>(vec + 2 * kKvRows + rv);
-      const f32x4 dlo = *reinterpret_cast<const f32x4*>(vec + 3 * kKvRows + rv);
-      const f32x4 sg = *reinterpret_cast<const f32x4*>(vec + 4 * kKvRows + rv);
+      const f32x4 go = *reinterpret_cast<const f32x4*>(vec + 3 * kKvRows + rv);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * j + i;
         float pe = fast_exp2(fmaf(se[e], cs, -l2e[i]));
-        float po = fast_exp2(fmaf(so[e], cs, -l2o[i]));
+        float po = fast_exp2(fmaf(so[e], cs, -l2o[i]));  // s P_o
         if (MASKED) {  // a select, not a branch: every lane takes the same path
           const int q = r0 + rv + i;
           const bool ok = (q < T) & (key < T) & (!CAUSAL | (key <= q));
           pe = ok ? pe : 0.f;
           po = ok ? po : 0.f;
         }
-        pv[e] = fmaf(-sg[i], po, pe);
+        pv[e] = pe - po;
         dse[e] = pe * (dp[e] - dle[i]);
-        dso[e] = po * fmaf(-sg[i], dp[e], -dlo[i]);
+        dso[e] = po * (go[i] - dp[e]);
       }
     }
     // dV += P''^T dout and dK += dS_e^T Q_e + dS_o^T Q_o over two 16-query
@@ -660,7 +661,6 @@ template <int D>
 hipError_t launch_d(const V2BwdArgs& a, hipStream_t stream) {
   const long long Np = a.Np;
   float* lse2 = a.delta + (size_t)a.Hq * Np;
-  float* sig = lse2 + (size_t)a.Hq * Np;
   const int pairs_per_group = (a.Hq / a.Hkv) / 2;
   const int PW = pairs_per_group % 4 == 0 ? 4 : pairs_per_group % 2 == 0 ? 2 : 1;
   const int qtile = kRows * (kWaves / PW);
@@ -680,19 +680,19 @@ hipError_t launch_d(const V2BwdArgs& a, hipStream_t stream) {
   if (dq_blocks > 0x7fffffffLL || kv_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
 #define DQ(PWV, C)                                                                               \
   hipLaunchKernelGGL((v2_bwd_dq_kernel<D, PWV, C>), dim3((unsigned)dq_blocks), dim3(kThreads), 0, \
-                     stream, a, lse2, sig)
+                     stream, a, lse2)
   if (a.causal) {
     if (PW == 4) DQ(4, true);
     else if (PW == 2) DQ(2, true);
     else DQ(1, true);
     hipLaunchKernelGGL((v2_bwd_dkdv_kernel<D, true>), dim3((unsigned)kv_blocks), dim3(kThreads), 0,
-                       stream, a, (const float*)lse2, (const float*)sig, cohort);
+                       stream, a, (const float*)lse2, cohort);
   } else {
     if (PW == 4) DQ(4, false);
     else if (PW == 2) DQ(2, false);
     else DQ(1, false);
     hipLaunchKernelGGL((v2_bwd_dkdv_kernel<D, false>), dim3((unsigned)kv_blocks), dim3(kThreads),
-                       0, stream, a, (const float*)lse2, (const float*)sig, cohort);
+                       0, stream, a, (const float*)lse2, cohort);
   }
 #undef DQ
   return hipGetLastError();
@@ -705,8 +705,8 @@ long long v2_bwd_rows(int B, int T) { return (long long)B * pad64(T); }
 long long v2_bwd_varlen_rows(long long N, int nseq) { return pad64(N) + 64LL * nseq; }
 
 size_t v2_bwd_workspace_bytes_rows(long long Np, int Hq) {
-  // delta and lse2 [Hq][Np], sigmoid [Hq/2][Np], fp32
-  return ((size_t)Hq * Np * 2 + (size_t)(Hq / 2) * Np) * sizeof(float);
+  // delta and lse2 [Hq][Np], fp32
+  return (size_t)Hq * Np * 2 * sizeof(float);
 }
 
 size_t v2_bwd_workspace_bytes(int B, int T, int Hq) {

@@ -199,9 +199,9 @@ def test_v2_backward_rejects_bad_arguments(lib):
 
 
 def test_v2_backward_workspace_query(lib):
-    # fp32 delta and log2-lse [B][Hq][T rounded up to 64], sigmoid [B][Hq/2][same]
-    assert lib.diffattn_v2_bwd_workspace_bytes(2, 8192, 64, 8, 128) == 4 * 2 * 8192 * (64 * 2 + 32)
-    assert lib.diffattn_v2_bwd_workspace_bytes(1, 65, 16, 2, 128) == 4 * 128 * (16 * 2 + 8)
+    # fp32 delta and log2-lse values [B][Hq][T rounded up to 64]
+    assert lib.diffattn_v2_bwd_workspace_bytes(2, 8192, 64, 8, 128) == 4 * 2 * 8192 * 64 * 2
+    assert lib.diffattn_v2_bwd_workspace_bytes(1, 65, 16, 2, 128) == 4 * 128 * 16 * 2
     assert lib.diffattn_v2_bwd_workspace_bytes(1, 64, 6, 2, 128) == 0
     assert lib.diffattn_v2_bwd_workspace_bytes(1, 64, 16, 2, 96) == 0
 
@@ -325,8 +325,8 @@ def test_v2_varlen_backward_rejects_bad_arguments(lib):
 def test_v2_varlen_backward_workspace_query(lib):
     # per-row values of every sequence padded to 64 rows: rows <= N rounded up + 64 per sequence
     Np = (65536 + 63) // 64 * 64 + 64 * 8
-    assert lib.diffattn_v2_varlen_bwd_workspace_bytes(65536, 8, 64, 8, 128) == 4 * Np * (64 * 2 + 32)
-    assert lib.diffattn_v2_varlen_bwd_workspace_bytes(100, 3, 16, 2, 128) == 4 * (128 + 192) * (16 * 2 + 8)
+    assert lib.diffattn_v2_varlen_bwd_workspace_bytes(65536, 8, 64, 8, 128) == 4 * Np * 64 * 2
+    assert lib.diffattn_v2_varlen_bwd_workspace_bytes(100, 3, 16, 2, 128) == 4 * (128 + 192) * 16 * 2
     assert lib.diffattn_v2_varlen_bwd_workspace_bytes(100, 3, 16, 2, 96) == 0
     assert lib.diffattn_v2_varlen_bwd_workspace_bytes(0, 3, 16, 2, 128) == 0
 
