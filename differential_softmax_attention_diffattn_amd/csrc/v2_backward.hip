@@ -56,6 +56,35 @@ struct BoolTag {
   static constexpr bool value = B;
 };
 
+// Lane n of each 16-lane row of x, in every lane of that row (DPP
+// row_newbcast; n a constant once the caller's loops are unrolled).  Used as
+// the first operand of a VOP2 subtraction the compiler folds the broadcast
+// into that instruction.
+template <int N>
+__device__ __forceinline__ float row_bcast_n(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + N, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row_bcast(float x, int n) {
+  switch (n) {
+    case 0: return row_bcast_n<0>(x);
+    case 1: return row_bcast_n<1>(x);
+    case 2: return row_bcast_n<2>(x);
+    case 3: return row_bcast_n<3>(x);
+    case 4: return row_bcast_n<4>(x);
+    case 5: return row_bcast_n<5>(x);
+    case 6: return row_bcast_n<6>(x);
+    case 7: return row_bcast_n<7>(x);
+    case 8: return row_bcast_n<8>(x);
+    case 9: return row_bcast_n<9>(x);
+    case 10: return row_bcast_n<10>(x);
+    case 11: return row_bcast_n<11>(x);
+    case 12: return row_bcast_n<12>(x);
+    case 13: return row_bcast_n<13>(x);
+    case 14: return row_bcast_n<14>(x);
+    default: return row_bcast_n<15>(x);
+  }
+}
+
 // One sequence of the batch: its first token, length and first workspace row.
 struct SeqView {
   long long tok0;
@@ -507,6 +536,8 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
   const int tr_row = 4 * hf + (c16 >> 2);
   const int tr_byte = 8 * (c16 & 3);
   const int tr_half = ((lane >> 4) & 1) << 5;
+  // the query row whose D_e and g_o this lane reads (see the softmax below)
+  const int row_lane = 8 * ((lane >> 2) & 3) + 4 * hf + (lane & 3);
 
   // MASKED: the item's query tile touches the diagonal or a ragged end
   auto work = [&](auto masked, int item, const uint8_t* st) __attribute__((always_inline)) {
@@ -546,14 +577,21 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
     // D_o = -s g_o, g_o = <dout, O_o> (the row values arrive with s folded in:
     // lse2 of the odd head minus log2 s, and g_o).  Element 4 j + i is query
     // r0 + 8 j + 4 hf + i.
+    // D_e and g_o: one 4-byte read each, lane 16 r + n holding row
+    // 8 (n >> 2) + 4 (r >> 1) + (n & 3), so that lane n = 4 j + i of each
+    // 16-lane row holds the row that element 4 j + i of that row's lanes
+    // needs; a row broadcast hands it over inside the subtraction (16-byte
+    // reads of every lane's 16 rows took 8 KB of LDS reads per item; the
+    // log-sum-exp rows stay 16-byte reads, since their broadcast cannot fold
+    // into the fused multiply-add of the exponent and costs a move each).
+    const float dle_l = vec[2 * kKvRows + row_lane];
+    const float go_l = vec[3 * kKvRows + row_lane];
     float pv[16], dse[16], dso[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rv = 8 * j + 4 * hf;
       const f32x4 l2e = *reinterpret_cast<const f32x4*>(vec + rv);
       const f32x4 l2o = *reinterpret_cast<const f32x4*>(vec + kKvRows + rv);
-      const f32x4 dle = *reinterpret_cast<const f32x4*>(vec + 2 * kKvRows + rv);
-      const f32x4 go = *reinterpret_cast<const f32x4*>(vec + 3 * kKvRows + rv);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * j + i;
@@ -566,8 +604,8 @@ __global__ __launch_bounds__(kThreads, 1) void v2_bwd_dkdv_kernel(V2BwdArgs a, c
           po = ok ? po : 0.f;
         }
         pv[e] = pe - po;
-        dse[e] = pe * (dp[e] - dle[i]);
-        dso[e] = po * (go[i] - dp[e]);
+        dse[e] = pe * -(row_bcast(dle_l, e) - dp[e]);  // dP - D_e, broadcast operand first
+        dso[e] = po * (row_bcast(go_l, e) - dp[e]);
       }
     }
     // dV += P''^T dout and dK += dS_e^T Q_e + dS_o^T Q_o over two 16-query
