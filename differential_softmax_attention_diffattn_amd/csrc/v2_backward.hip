@@ -16,10 +16,11 @@
 //  * v2_bwd_dq_kernel: the forward's decomposition (a wave owns one pair and
 //    16 query rows, lanes own query columns; K and V tiles stream through LDS):
 //    S^T = K Q^T, dP^T = V dout^T, dS^T, dQ^T += K^T dS^T.  It first forms its
-//    rows' D_2p, D_2p+1, s, dlogit and the log-sum-exp in log2 units and
-//    stores them [head][Np] for the next kernel: every sequence's rows start at
-//    a multiple of 64, so a 32-row query tile's values are one contiguous
-//    128-byte run;
+//    rows' D_2p, D_2p+1, s, dlogit and the log-sum-exp in log2 units, writes
+//    dlogit, and stores per head a log-sum-exp and a D value [head][Np] for
+//    the next kernel (the odd head's with s folded in): every sequence's rows
+//    start at a multiple of 64, so a 32-row query tile's values are one
+//    contiguous 128-byte run;
 //  * v2_bwd_dkdv_kernel: a workgroup owns 256 keys of one KV head; a wave
 //    keeps its 32 keys' K fragments in registers (lanes own key columns), V
 //    of the workgroup's keys sits in LDS, and the wave handles both heads of
