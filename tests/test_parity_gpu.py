@@ -520,6 +520,29 @@ def test_v2_backward_small_all_elements(gpu, Hq, Hkv, d, T, causal):
         compare_grad(g.cpu().numpy(), r, f"v2 bwd {name} Hq={Hq} Hkv={Hkv} d={d} T={T} causal={causal}")
 
 
+def test_v2_backward_saturated_coefficients(gpu):
+    # Coefficient logits at the ends of the sigmoid: -200 gives s = 0 exactly in
+    # fp32 (the odd head drops out: its dq is zero and it adds nothing to dk,
+    # dv), +40 gives s = 1 exactly; other pairs and tokens mix both with
+    # ordinary logits.  Every element against the oracle (whose fp64 s is 1e-87,
+    # not 0, at -200).
+    w = inp.V2_PREFILL.with_shape(B=2, T=130, Hq=8, Hkv=2)
+    x = inp.v2_inputs(w)
+    lg = x["logit"]
+    lg[:, :, 0] = -200.0
+    lg[:, :, 1] = 40.0
+    lg[:, ::3, 2] = -200.0
+    lg[:, 1::3, 3] = 40.0
+    dout = inp.v2_dout(w)
+    _, _, _, grads = run_train(cuda(x, gpu), dout.to(gpu))
+    refs = oracle.v2_backward(x["q"], x["k"], x["v"], x["logit"], dout)
+    for name, g, r in zip(("dq", "dk", "dv", "dlogit"), grads, refs):
+        compare_grad(g.cpu().numpy(), r, f"v2 bwd saturated logits {name}")
+    dq = grads[0].cpu()
+    assert torch.count_nonzero(dq[:, :, 1]).item() == 0  # head 1: the noise head of pair 0
+    assert torch.count_nonzero(grads[3].cpu()[:, :, :2]).item() == 0  # s (1 - s) = 0
+
+
 def test_v2_train_forward_outputs(gpu):
     # out matches the inference forward exactly; per-head O and lse match the oracle
     w = inp.V2_PREFILL.with_shape(B=2, T=150, Hq=16, Hkv=2)
