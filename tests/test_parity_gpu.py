@@ -543,6 +543,26 @@ def test_v2_backward_saturated_coefficients(gpu):
     assert torch.count_nonzero(grads[3].cpu()[:, :, :2]).item() == 0  # s (1 - s) = 0
 
 
+@pytest.mark.parametrize("T", [40, 130])
+def test_v2_backward_ignores_workspace_contents(gpu, T):
+    # The workspace's contents on entry are ignored: all-NaN bits (0xFF) and
+    # zeros give identical gradients (T = 40 and 130 leave rows past the end
+    # of the last query tile that no workgroup writes)
+    w = inp.V2_PREFILL.with_shape(B=2, T=T, Hq=8, Hkv=2)
+    xg = cuda(inp.v2_inputs(w), gpu)
+    dout = inp.v2_dout(w).to(gpu)
+    _, oh, lse = da.v2_fwd_train(xg["q"], xg["k"], xg["v"], xg["logit"])
+    nbytes = da.v2_bwd_workspace_bytes(w.B, T, w.Hq, w.Hkv, w.d)
+    res = []
+    for fill in (0xFF, 0x00):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=gpu)
+        res.append(da.v2_bwd(xg["q"], xg["k"], xg["v"], xg["logit"], oh, lse, dout, workspace=ws))
+        torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv", "dlogit"), *res):
+        assert torch.isfinite(a).all(), f"T={T} {name}: non-finite with a NaN-filled workspace"
+        assert torch.equal(a, b), f"T={T} {name} depends on the workspace contents"
+
+
 def test_v2_train_forward_outputs(gpu):
     # out matches the inference forward exactly; per-head O and lse match the oracle
     w = inp.V2_PREFILL.with_shape(B=2, T=150, Hq=16, Hkv=2)
