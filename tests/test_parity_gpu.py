@@ -1057,3 +1057,50 @@ def test_projections_full_workload_sampled(gpu):
     wo = x["w_o"].double().cpu().numpy()
     check_proj(y[rows].float().cpu().numpy(), oracle.out_projection(af, wo), np.abs(af) @ np.abs(wo).T,
                "out proj full", out_bf16=True)
+
+
+# ---------------------------------------------------------------------------
+# Workspaces: their contents on entry are ignored
+# ---------------------------------------------------------------------------
+
+def test_workspace_contents_ignored_by_every_call(gpu):
+    # Each call that takes a workspace gives the same bits with a NaN-filled
+    # (0xFF bytes) and a zeroed workspace: V1 forward (V pack), V1 backward
+    # (dz, row values, partial sums), V2 decode and V1 decode (partials), on
+    # ragged shapes.
+    def both(nbytes, call):
+        res = []
+        for fill in (0xFF, 0x00):
+            ws = torch.full((max(1, nbytes),), fill, dtype=torch.uint8, device=gpu)
+            r = call(ws)
+            torch.cuda.synchronize()
+            res.append(r if isinstance(r, (tuple, list)) else (r,))
+        for i, (a, b) in enumerate(zip(*res)):
+            assert torch.isfinite(a).all(), f"output {i}: non-finite with a NaN-filled workspace"
+            assert torch.equal(a, b), f"output {i} depends on the workspace contents"
+
+    w1 = inp.V1_BF16.with_shape(B=2, T=150, H=2)
+    x1 = cuda(inp.v1_inputs(w1), gpu)
+    li = oracle.lambda_init(6)
+    note("v1_fwd")
+    both(da.v1_workspace_bytes(w1.B, w1.T, w1.H, w1.d, w1.dv, torch.bfloat16),
+         lambda ws: da.v1_fwd(x1["q1"], x1["k1"], x1["q2"], x1["k2"], x1["v"], li, li, w1.eps,
+                              workspace=ws))
+    note("v1_bwd")
+    _, o1, o2, lse = da.v1_fwd_train(x1["q1"], x1["k1"], x1["q2"], x1["k2"], x1["v"], li, li, w1.eps)
+    dy = inp.v1_dy(w1).to(gpu)
+    both(da.v1_bwd_workspace_bytes(w1.B, w1.T, w1.H, w1.d, w1.dv),
+         lambda ws: da.v1_bwd(x1["q1"], x1["k1"], x1["q2"], x1["k2"], x1["v"], o1, o2, lse, dy, li,
+                              li, w1.eps, workspace=ws))
+    note("v2_decode")
+    wd = inp.V2_DECODE.with_shape(B=3, S=700, Hq=16, Hkv=2, cache_lens=(700, 1, 333))
+    xd = cuda(inp.decode_inputs(wd), gpu)
+    both(da.v2_decode_workspace_bytes(wd.B, wd.S, wd.Hq, wd.Hkv, wd.d),
+         lambda ws: da.v2_decode(xd["q"], xd["k_cache"], xd["v_cache"], xd["logit"],
+                                 cache_len=xd["cache_len"], workspace=ws))
+    note("v1_decode")
+    wv = inp.V1_DECODE.with_shape(B=2, S=900, H=4, cache_lens=(900, 17))
+    xv = cuda(inp.v1_decode_inputs(wv), gpu)
+    both(da.v1_decode_workspace_bytes(wv.B, wv.S, wv.H, wv.d, wv.dv),
+         lambda ws: da.v1_decode(xv["q1"], xv["q2"], xv["k1_cache"], xv["k2_cache"], xv["v_cache"],
+                                 li, li, wv.eps, cache_len=xv["cache_len"], workspace=ws))
