@@ -563,6 +563,25 @@ def test_v2_backward_ignores_workspace_contents(gpu, T):
         assert torch.equal(a, b), f"T={T} {name} depends on the workspace contents"
 
 
+@pytest.mark.parametrize("alpha", [40.0, 400.0])
+def test_v2_backward_needles(gpu, alpha):
+    # Peaked maps (the V2 needles: one head of a pair nearly one-hot on a key,
+    # its partner diffuse): the backward recomputes P from the unscaled q
+    # against the forward's log-sum-exp, which the forward formed from q
+    # scaled and rounded to bf16; at these logits the two must still agree
+    # to the gradient tolerance, every element against the oracle.
+    w = inp.V2_PREFILL.with_shape(B=1, T=190, Hq=16, Hkv=2)
+    x = inp.v2_inputs(w)
+    g = w.Hq // w.Hkv
+    for i, j, head in V2_NEEDLES:
+        x["k"][0, j, head // g] = (alpha * x["q"][0, i, head].float()).to(torch.bfloat16)
+    dout = inp.v2_dout(w)
+    _, _, _, grads = run_train(cuda(x, gpu), dout.to(gpu))
+    refs = oracle.v2_backward(x["q"], x["k"], x["v"], x["logit"], dout)
+    for name, gr, r in zip(("dq", "dk", "dv", "dlogit"), grads, refs):
+        compare_grad(gr.cpu().numpy(), r, f"v2 bwd needles a={alpha} {name}")
+
+
 def test_v2_train_forward_outputs(gpu):
     # out matches the inference forward exactly; per-head O and lse match the oracle
     w = inp.V2_PREFILL.with_shape(B=2, T=150, Hq=16, Hkv=2)
