@@ -834,6 +834,26 @@ def test_v1_backward_small_all_elements(gpu, B, T, H, d, dv, causal, layer, weig
                                 require_decisive_e2e=(T, layer) != (200, 12))
 
 
+@pytest.mark.parametrize("alpha", [40.0, 400.0])
+def test_v1_backward_needles(gpu, alpha):
+    # Peaked maps (the V1 needles: each map of some rows nearly one-hot on a
+    # key, the two maps on different keys), every element against the oracle,
+    # on the oracle's forward state and end to end; the forward's fp16 P moves
+    # dlambda most on peaked rows, so the end-to-end dlambda bound need not be
+    # decisive here and the oracle-state check decides.
+    w = inp.V1_BF16.with_shape(B=1, T=300, H=2)
+    x = inp.v1_inputs(w)
+    for h in range(2):
+        for i, j1, j2 in V1_NEEDLES:
+            x["k1"][0, j1, h] = (alpha * x["q1"][0, i, h].float()).to(torch.bfloat16)
+            x["k2"][0, j2, h] = (alpha * x["q2"][0, i, h].float()).to(torch.bfloat16)
+    dy = inp.v1_dy(w)
+    lam = li = oracle.lambda_init(4)
+    refs = oracle.v1_backward(x["q1"], x["k1"], x["q2"], x["k2"], x["v"], lam, li, w.eps, dy)
+    check_v1_backward_both_ways(cuda(x, gpu), x, dy, lam, li, w.eps, None, True, refs,
+                                f"v1 bwd needles a={alpha}", require_decisive_e2e=False)
+
+
 @pytest.mark.parametrize("lam,li", [(1.3, 0.5), (-0.5, 0.3)])
 def test_v1_backward_lambda_outside_init_range(gpu, lam, li):
     # the API takes any finite lambda (the pages allow lambda > 1); lambda and
